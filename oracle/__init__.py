@@ -1,0 +1,213 @@
+"""CPU oracle of the BlockFFN layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never loads it and
+shares no code with it.
+
+The arithmetic lives in ``blockffn_oracle.c`` (plain C, double accumulation,
+OpenMP over tokens); this module only builds it with gcc and marshals numpy
+arrays.  Arrays are float32 (an fp32 layer) or uint16 bfloat16 bit patterns
+(a bf16 layer); the C code widens them itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "blockffn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+F32, BF16 = 0, 1
+MAX_HIST = 129
+
+
+class OracleStats(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
+        ("n_experts", ctypes.c_int64), ("chunk_len", ctypes.c_int64),
+        ("active_pairs", ctypes.c_int64), ("union_sum", ctypes.c_int64),
+        ("reuse_num", ctypes.c_int64), ("reuse_den", ctypes.c_int64),
+        ("hist", ctypes.c_int64 * MAX_HIST),
+    ]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (plain -O2, no fast-math, no FMA contraction)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            # BLOCKFFN_ORACLE_LIB points the tests at a deliberately broken
+            # copy of the oracle (mutation tests); normally it is unset.
+            path = os.environ.get("BLOCKFFN_ORACLE_LIB")
+            if not path:
+                build(force=False)
+                path = _LIB
+            lib = ctypes.CDLL(path)
+            vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+            lib.oracle_route.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp, dbl, vp, vp, vp]
+            lib.oracle_expert.argtypes = [i32, i32, i32, vp, i64, vp, vp, i32, vp]
+            lib.oracle_forward_tokens.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp]
+            lib.oracle_forward_chunks.argtypes = [i32, i32, i32, i32, vp, i64, i32, vp, vp, vp, vp, vp, vp]
+            lib.oracle_forward_dense.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, vp]
+            lib.oracle_union.argtypes = [i32, vp, i64, i32, vp, vp, vp]
+            lib.oracle_stats.argtypes = [i32, vp, i64, i32, ctypes.POINTER(OracleStats)]
+            lib.oracle_num_threads.argtypes = []
+            for name in ("oracle_route", "oracle_expert", "oracle_forward_tokens",
+                         "oracle_forward_chunks", "oracle_forward_dense", "oracle_union",
+                         "oracle_stats", "oracle_num_threads"):
+                getattr(lib, name).restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle inputs must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=dtype) if dtype is not None else np.ascontiguousarray(a)
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        raise RuntimeError(f"{name} failed with code {rc}")
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def mask_words(n_experts: int) -> int:
+    return (n_experts + 63) // 64
+
+
+def route(x, w_router, b_router=None, rms_scale=None, eps: float = 1e-6):
+    """Router: returns (z[T][E] f64, g[T][E] f64, mask[T][W] u64)."""
+    x, w_router = _c(x), _c(w_router)
+    code = _dtype_code(x)
+    assert _dtype_code(w_router) == code, "x and w_router must share a dtype"
+    T, d = x.shape
+    E = w_router.shape[0]
+    assert w_router.shape == (E, d)
+    b = _c(b_router, np.float32)
+    s = _c(rms_scale, np.float32)
+    z = np.empty((T, E), np.float64)
+    g = np.empty((T, E), np.float64)
+    m = np.empty((T, mask_words(E)), np.uint64)
+    _check(_load().oracle_route(d, E, code, _p(x), T, _p(w_router), _p(b), _p(s), float(eps),
+                                _p(z), _p(g), _p(m)), "oracle_route")
+    return z, g, m
+
+
+def expert(x, t: int, w_in, w_out, i: int):
+    """E_i(x_t) as a float64 vector of length d."""
+    x, w_in, w_out = _c(x), _c(w_in), _c(w_out)
+    code = _dtype_code(x)
+    E, de, d = w_in.shape
+    e = np.empty(d, np.float64)
+    _check(_load().oracle_expert(d, de, code, _p(x), int(t), _p(w_in), _p(w_out), int(i), _p(e)),
+           "oracle_expert")
+    return e
+
+
+def _fwd_common(x, w_in, w_out, g):
+    x, w_in, w_out = _c(x), _c(w_in), _c(w_out)
+    code = _dtype_code(x)
+    assert _dtype_code(w_in) == code and _dtype_code(w_out) == code
+    T, d = x.shape
+    E, de, d2 = w_in.shape
+    assert d2 == d and w_out.shape == (E, d, de)
+    g = _c(g, np.float64)
+    assert g.shape == (T, E)
+    return x, w_in, w_out, g, code, T, d, E, de
+
+
+def forward_tokens(x, w_in, w_out, g, mask):
+    x, w_in, w_out, g, code, T, d, E, de = _fwd_common(x, w_in, w_out, g)
+    mask = _c(mask, np.uint64)
+    y = np.empty((T, d), np.float64)
+    _check(_load().oracle_forward_tokens(d, E, de, code, _p(x), T, _p(w_in), _p(w_out), _p(g),
+                                         _p(mask), _p(y)), "oracle_forward_tokens")
+    return y
+
+
+def forward_chunks(x, w_in, w_out, g, chunk_len: int, count, lst):
+    x, w_in, w_out, g, code, T, d, E, de = _fwd_common(x, w_in, w_out, g)
+    count = _c(count, np.int32)
+    lst = _c(lst, np.int32)
+    y = np.empty((T, d), np.float64)
+    _check(_load().oracle_forward_chunks(d, E, de, code, _p(x), T, int(chunk_len), _p(w_in),
+                                         _p(w_out), _p(g), _p(count), _p(lst), _p(y)),
+           "oracle_forward_chunks")
+    return y
+
+
+def forward_dense(x, w_in, w_out, g):
+    x, w_in, w_out, g, code, T, d, E, de = _fwd_common(x, w_in, w_out, g)
+    y = np.empty((T, d), np.float64)
+    _check(_load().oracle_forward_dense(d, E, de, code, _p(x), T, _p(w_in), _p(w_out), _p(g), _p(y)),
+           "oracle_forward_dense")
+    return y
+
+
+def chunk_union(mask, n_experts: int, chunk_len: int):
+    """Returns (umask[C][W] u64, count[C] i32, list[C][E] i32 with -1 tail)."""
+    mask = _c(mask, np.uint64)
+    T = mask.shape[0]
+    W = mask_words(n_experts)
+    C = T // chunk_len
+    um = np.empty((C, W), np.uint64)
+    cnt = np.empty(C, np.int32)
+    lst = np.empty((C, n_experts), np.int32)
+    _check(_load().oracle_union(n_experts, _p(mask), T, int(chunk_len), _p(um), _p(cnt), _p(lst)),
+           "oracle_union")
+    return um, cnt, lst
+
+
+def stats(mask, n_experts: int, chunk_len: int) -> dict:
+    mask = _c(mask, np.uint64)
+    T = mask.shape[0]
+    st = OracleStats()
+    _check(_load().oracle_stats(n_experts, _p(mask), T, int(chunk_len), ctypes.byref(st)), "oracle_stats")
+    out = {f: getattr(st, f) for f, _ in OracleStats._fields_ if f != "hist"}
+    out["hist"] = np.array(st.hist[: n_experts + 1], dtype=np.int64)
+    out["tls"] = 1.0 - st.active_pairs / (T * n_experts) if T else 0.0
+    out["cls"] = 1.0 - st.union_sum / (st.n_chunks * n_experts) if st.n_chunks else 0.0
+    out["reuse"] = st.reuse_num / st.reuse_den if st.reuse_den else 0.0
+    return out
+
+
+def layer_forward(layer, x, chunk_len: int):
+    """Full oracle pass on one layer: route, union, per-token forward, stats."""
+    z, g, m = route(x, layer.w_router, layer.b_router, layer.rms_scale, layer.rms_eps)
+    um, cnt, lst = chunk_union(m, layer.n_experts, chunk_len)
+    y = forward_tokens(x, layer.w_in, layer.w_out, g, m)
+    return dict(z=z, g=g, mask=m, umask=um, count=cnt, list=lst, y=y)

@@ -1,0 +1,315 @@
+/*
+ * blockffn_oracle.c -- plain, slow CPU oracle of the BlockFFN layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It includes no HIP header and shares no code, table
+ * or helper with the GPU library.
+ *
+ * What it computes (sources: the BlockFFN write-up on lsdiaocha.cn, §2 core
+ * design and §4 acceleration kernel; the abstract of "BlockFFN: Towards
+ * End-Side Acceleration-Friendly Mixture-of-Experts with Chunk-Level
+ * Activation Sparsity", arXiv 2507.08771):
+ *
+ *   router   z_i = sum_k W_r[i][k] x_k + b_i
+ *            a_i = max(z_i, 0)                      (ReLU; expert i active iff z_i > 0)
+ *            g_i = s_i a_i / sqrt(mean_i(a_i^2) + eps)   (RMSNorm over the E outputs)
+ *   expert   E_i(x) = W_out[i] Swish(W_in[i] x),  Swish(u) = u / (1 + e^-u)
+ *   layer    y = sum over active i, ascending, of g_i E_i(x)
+ *   chunk    U_c = union of the active sets of the L tokens of chunk c
+ *   stats    token-level sparsity, chunk-level sparsity, experts-per-token
+ *            histogram, consecutive-token expert reuse
+ *
+ * Every sum is accumulated in double, in the plain index order written
+ * below, with no blocking or reordering.  Inputs are read in their stored
+ * precision (IEEE binary32, or bfloat16 = the upper 16 bits of a binary32)
+ * and widened here.  Every function is pinned by CPU tests against brute
+ * force, closed forms, invariants and special cases that reduce to library
+ * routines; none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+#define ORACLE_MAX_HIST 129
+
+typedef struct oracle_stats {
+  int64_t n_tokens, n_chunks, n_experts, chunk_len;
+  int64_t active_pairs; /* sum over tokens of |M_t| */
+  int64_t union_sum;    /* sum over chunks of |U_c| */
+  int64_t reuse_num;    /* sum over t >= 1 of |M_t and M_{t-1}| */
+  int64_t reuse_den;    /* sum over t >= 1 of |M_{t-1}| */
+  int64_t hist[ORACLE_MAX_HIST]; /* hist[k] = number of tokens with k active experts */
+} oracle_stats_t;
+
+/* Element idx of a stored array, widened to double. */
+static double widen(const void *base, int64_t idx, int dtype) {
+  if (dtype == ORACLE_F32) return (double)((const float *)base)[idx];
+  uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static int mask_words(int E) { return (E + 63) / 64; }
+
+static int mask_bit(const uint64_t *m, int i) { return (int)((m[i / 64] >> (i % 64)) & 1u); }
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * Router (write-up §2: ReLU then RMSNorm; abstract: "a router integrating ReLU
+ * activation and RMSNorm").  For each token t writes the pre-activations
+ * z[t][E], the gates g[t][E] and the activation pattern mask[t][W] (bit i of
+ * word i/64 set iff z_i > 0).  The RMS is taken over all E router outputs,
+ * inactive ones included.  rms_scale may be NULL (unit scale), b_router NULL
+ * (no bias).
+ */
+int oracle_route(int32_t d, int32_t E, int32_t dtype, const void *x, int64_t T,
+                 const void *w_router, const float *b_router, const float *rms_scale,
+                 double eps, double *z_out, double *g_out, uint64_t *mask_out) {
+  if (d <= 0 || E <= 0 || T < 0) return -1;
+  const int W = mask_words(E);
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double *z = z_out + t * E;
+    double *g = g_out + t * E;
+    uint64_t *m = mask_out + t * W;
+    for (int w = 0; w < W; ++w) m[w] = 0;
+    for (int i = 0; i < E; ++i) {
+      double acc = 0.0;
+      for (int k = 0; k < d; ++k)
+        acc += widen(w_router, (int64_t)i * d + k, dtype) * widen(x, t * d + k, dtype);
+      if (b_router) acc += (double)b_router[i];
+      z[i] = acc;
+      if (acc > 0.0) m[i / 64] |= (uint64_t)1 << (i % 64);
+    }
+    double ms = 0.0;
+    for (int i = 0; i < E; ++i) {
+      double a = z[i] > 0.0 ? z[i] : 0.0;
+      ms += a * a;
+    }
+    ms /= (double)E;
+    const double denom = sqrt(ms + eps);
+    for (int i = 0; i < E; ++i) {
+      double a = z[i] > 0.0 ? z[i] : 0.0;
+      double s = rms_scale ? (double)rms_scale[i] : 1.0;
+      g[i] = s * a / denom;
+    }
+  }
+  return 0;
+}
+
+/*
+ * One expert on one token (write-up §2: a non-gated MLP with Swish):
+ * u = W_in[i] x (d_e values), h = Swish(u), e = W_out[i] h (d values).
+ * w_in_i points at W_in[i] ([d_e][d]) and w_out_i at W_out[i] ([d][d_e]);
+ * x_off is the element offset of the token in x.
+ */
+static void expert_eval(int d, int de, int dtype, const void *x, int64_t x_off,
+                        const void *w_in, int64_t w_in_off, const void *w_out, int64_t w_out_off,
+                        double *h, double *e) {
+  for (int j = 0; j < de; ++j) {
+    double u = 0.0;
+    for (int k = 0; k < d; ++k)
+      u += widen(w_in, w_in_off + (int64_t)j * d + k, dtype) * widen(x, x_off + k, dtype);
+    h[j] = u / (1.0 + exp(-u));
+  }
+  for (int k = 0; k < d; ++k) {
+    double acc = 0.0;
+    for (int j = 0; j < de; ++j) acc += widen(w_out, w_out_off + (int64_t)k * de + j, dtype) * h[j];
+    e[k] = acc;
+  }
+}
+
+/* Exported for the expert special-case pins: e[d] = E_i(x_t). */
+int oracle_expert(int32_t d, int32_t de, int32_t dtype, const void *x, int64_t t,
+                  const void *w_in, const void *w_out, int32_t i, double *e_out) {
+  double *h = (double *)malloc(sizeof(double) * (size_t)de);
+  if (!h) return -2;
+  expert_eval(d, de, dtype, x, t * d, w_in, (int64_t)i * de * d, w_out, (int64_t)i * d * de, h, e_out);
+  free(h);
+  return 0;
+}
+
+/*
+ * Per-token layer output: y_t = sum over i in M_t, ascending, of g[t][i] E_i(x_t).
+ * Experts outside the pattern are skipped (their gate is exactly zero).
+ */
+int oracle_forward_tokens(int32_t d, int32_t E, int32_t de, int32_t dtype, const void *x, int64_t T,
+                          const void *w_in, const void *w_out, const double *g,
+                          const uint64_t *mask, double *y) {
+  const int W = mask_words(E);
+  int err = 0;
+#pragma omp parallel
+  {
+    double *h = (double *)malloc(sizeof(double) * (size_t)de);
+    double *e = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!h || !e) {
+#pragma omp atomic write
+      err = -2;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      double *yt = y + t * d;
+      for (int k = 0; k < d; ++k) yt[k] = 0.0;
+      if (!h || !e) continue;
+      for (int i = 0; i < E; ++i) {
+        if (!mask_bit(mask + t * W, i)) continue;
+        expert_eval(d, de, dtype, x, t * d, w_in, (int64_t)i * de * d, w_out, (int64_t)i * d * de, h, e);
+        for (int k = 0; k < d; ++k) yt[k] += g[t * E + i] * e[k];
+      }
+    }
+    free(h);
+    free(e);
+  }
+  return err;
+}
+
+/*
+ * Chunk evaluation (write-up §4): for every chunk, run every expert of the
+ * chunk's union list on every token of the chunk and weight it by the token's
+ * own gate, which masks out the pairs the token did not activate:
+ * y_t = sum over s < count[c] of g[t][list[c][s]] E_{list[c][s]}(x_t).
+ */
+int oracle_forward_chunks(int32_t d, int32_t E, int32_t de, int32_t dtype, const void *x, int64_t T,
+                          int32_t L, const void *w_in, const void *w_out, const double *g,
+                          const int32_t *count, const int32_t *list, double *y) {
+  if (L <= 0 || T % L != 0) return -1;
+  int err = 0;
+#pragma omp parallel
+  {
+    double *h = (double *)malloc(sizeof(double) * (size_t)de);
+    double *e = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!h || !e) {
+#pragma omp atomic write
+      err = -2;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t c = t / L;
+      double *yt = y + t * d;
+      for (int k = 0; k < d; ++k) yt[k] = 0.0;
+      if (!h || !e) continue;
+      for (int s = 0; s < count[c]; ++s) {
+        const int i = list[c * E + s];
+        expert_eval(d, de, dtype, x, t * d, w_in, (int64_t)i * de * d, w_out, (int64_t)i * d * de, h, e);
+        for (int k = 0; k < d; ++k) yt[k] += g[t * E + i] * e[k];
+      }
+    }
+    free(h);
+    free(e);
+  }
+  return err;
+}
+
+/* Dense evaluation: every expert on every token, y_t = sum over all i of g[t][i] E_i(x_t). */
+int oracle_forward_dense(int32_t d, int32_t E, int32_t de, int32_t dtype, const void *x, int64_t T,
+                         const void *w_in, const void *w_out, const double *g, double *y) {
+  int err = 0;
+#pragma omp parallel
+  {
+    double *h = (double *)malloc(sizeof(double) * (size_t)de);
+    double *e = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!h || !e) {
+#pragma omp atomic write
+      err = -2;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      double *yt = y + t * d;
+      for (int k = 0; k < d; ++k) yt[k] = 0.0;
+      if (!h || !e) continue;
+      for (int i = 0; i < E; ++i) {
+        expert_eval(d, de, dtype, x, t * d, w_in, (int64_t)i * de * d, w_out, (int64_t)i * d * de, h, e);
+        for (int k = 0; k < d; ++k) yt[k] += g[t * E + i] * e[k];
+      }
+    }
+    free(h);
+    free(e);
+  }
+  return err;
+}
+
+/*
+ * Chunk union (write-up §4; abstract: chunk-level sparsity is about the union
+ * of the parameters several consecutive tokens activate).  Chunks are the
+ * aligned, non-overlapping runs of L tokens.  umask[c] is the OR of the
+ * chunk's token masks, count[c] its number of set bits, list[c][0..count)
+ * the set bits in ascending order and list[c][count..E) = -1.
+ */
+int oracle_union(int32_t E, const uint64_t *mask, int64_t T, int32_t L, uint64_t *umask,
+                 int32_t *count, int32_t *list) {
+  if (E <= 0 || L <= 0 || T % L != 0) return -1;
+  const int W = mask_words(E);
+  const int64_t C = T / L;
+  for (int64_t c = 0; c < C; ++c) {
+    for (int w = 0; w < W; ++w) {
+      uint64_t u = 0;
+      for (int64_t t = c * L; t < (c + 1) * L; ++t) u |= mask[t * W + w];
+      umask[c * W + w] = u;
+    }
+    int n = 0;
+    for (int i = 0; i < E; ++i)
+      if (mask_bit(umask + c * W, i)) list[c * E + n++] = i;
+    count[c] = n;
+    for (int s = n; s < E; ++s) list[c * E + s] = -1;
+  }
+  return 0;
+}
+
+static int64_t count_bits(const uint64_t *m, int E) {
+  int64_t n = 0;
+  for (int i = 0; i < E; ++i) n += mask_bit(m, i);
+  return n;
+}
+
+/*
+ * Sparsity statistics (abstract and write-up §3: token-level and 8-token
+ * chunk-level sparsity; write-up §5: expert reuse between consecutive tokens
+ * and the distribution of experts per token).  TLS = 1 - active_pairs/(T E),
+ * CLS_L = 1 - union_sum/(C E), reuse = reuse_num/reuse_den.
+ */
+int oracle_stats(int32_t E, const uint64_t *mask, int64_t T, int32_t L, oracle_stats_t *out) {
+  if (E <= 0 || E >= ORACLE_MAX_HIST || L <= 0 || T % L != 0) return -1;
+  const int W = mask_words(E);
+  const int64_t C = T / L;
+  memset(out, 0, sizeof *out);
+  out->n_tokens = T;
+  out->n_chunks = C;
+  out->n_experts = E;
+  out->chunk_len = L;
+  uint64_t *u = (uint64_t *)calloc((size_t)W, sizeof(uint64_t));
+  if (!u) return -2;
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t n = count_bits(mask + t * W, E);
+    out->active_pairs += n;
+    out->hist[n] += 1;
+    if (t >= 1) {
+      int64_t both = 0;
+      for (int i = 0; i < E; ++i) both += mask_bit(mask + t * W, i) & mask_bit(mask + (t - 1) * W, i);
+      out->reuse_num += both;
+      out->reuse_den += count_bits(mask + (t - 1) * W, E);
+    }
+  }
+  for (int64_t c = 0; c < C; ++c) {
+    for (int w = 0; w < W; ++w) u[w] = 0;
+    for (int64_t t = c * L; t < (c + 1) * L; ++t)
+      for (int w = 0; w < W; ++w) u[w] |= mask[t * W + w];
+    out->union_sum += count_bits(u, E);
+  }
+  free(u);
+  return 0;
+}

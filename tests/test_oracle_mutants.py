@@ -1,0 +1,56 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU,
+in a temporary directory), builds it, and runs the pin suite against it; the
+suite must fail.  The mistakes are the ones a reader of the pages could make:
+a non-strict ReLU threshold, a wrong RMS denominator, epsilon outside the
+root, a different activation, a transposed matrix, a dropped gate, AND
+instead of OR for the union, a chunk boundary off by one, a wrong bf16
+widening, a wrong reuse denominator, a flipped bias sign.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "blockffn_oracle.c")
+
+MUTANTS = {
+    "relu_not_strict": ("if (acc > 0.0) m[i / 64]", "if (acc >= 0.0) m[i / 64]"),
+    "rms_denominator": ("ms /= (double)E;", "ms /= (double)(E + 1);"),
+    "eps_outside_root": ("sqrt(ms + eps)", "(sqrt(ms) + eps)"),
+    "relu_instead_of_swish": ("h[j] = u / (1.0 + exp(-u));", "h[j] = u > 0.0 ? u : 0.0;"),
+    "w_out_transposed": ("widen(w_out, w_out_off + (int64_t)k * de + j, dtype)",
+                         "widen(w_out, w_out_off + (int64_t)j * d + k, dtype)"),
+    "gate_dropped": ("if (!mask_bit(mask + t * W, i)) continue;\n        expert_eval(d, de, dtype, x, t * d, w_in, (int64_t)i * de * d, w_out, (int64_t)i * d * de, h, e);\n        for (int k = 0; k < d; ++k) yt[k] += g[t * E + i] * e[k];",
+                     "if (!mask_bit(mask + t * W, i)) continue;\n        expert_eval(d, de, dtype, x, t * d, w_in, (int64_t)i * de * d, w_out, (int64_t)i * d * de, h, e);\n        for (int k = 0; k < d; ++k) yt[k] += e[k];"),
+    "union_and": ("for (int64_t t = c * L; t < (c + 1) * L; ++t) u |= mask[t * W + w];",
+                  "for (int64_t t = c * L; t < (c + 1) * L; ++t) u &= mask[t * W + w];"),
+    "chunk_boundary": ("for (int64_t t = c * L; t < (c + 1) * L; ++t) u |= mask[t * W + w];",
+                       "for (int64_t t = c * L + 1; t < (c + 1) * L; ++t) u |= mask[t * W + w];"),
+    "bf16_widening": ("[idx]) << 16;", "[idx]) << 15;"),
+    "reuse_denominator": ("out->reuse_den += count_bits(mask + (t - 1) * W, E);",
+                          "out->reuse_den += count_bits(mask + t * W, E);"),
+    "bias_sign": ("if (b_router) acc += (double)b_router[i];", "if (b_router) acc -= (double)b_router[i];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as tmp:
+        c = os.path.join(tmp, "mutant.c")
+        so = os.path.join(tmp, "libmutant.so")
+        open(c, "w").write(src.replace(old, new))
+        subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
+                        "-o", so, c, "-lm"], check=True)
+        env = dict(os.environ, BLOCKFFN_ORACLE_LIB=so)
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+        assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"

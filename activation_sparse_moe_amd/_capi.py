@@ -1,0 +1,94 @@
+"""ctypes declarations of libblockffn's C ABI (include/blockffn.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Loading fails loudly if the library has not been built; there is no
+fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libblockffn.so")
+
+F32, BF16 = 0, 1
+MODE_AUTO, MODE_GEMV, MODE_CHUNK_MFMA, MODE_GROUPED, MODE_DENSE = 0, 1, 2, 3, 4
+MODES = {"auto": MODE_AUTO, "gemv": MODE_GEMV, "chunk_mfma": MODE_CHUNK_MFMA, "grouped": MODE_GROUPED,
+         "dense": MODE_DENSE}
+
+OK = 0
+ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_CHUNK, ERR_WORKSPACE = -1, -2, -3, -4, -5
+ERR_MODE, ERR_ALIGN, ERR_LAYERS, ERR_HIP = -6, -7, -8, -9
+
+# Every symbol include/blockffn.h declares.
+EXPORTS = ("blockffn_route", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats",
+           "blockffn_set_stage_events", "blockffn_workspace_size", "blockffn_status_string",
+           "blockffn_last_error", "blockffn_version")
+
+
+class BlockffnLayer(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("d_expert", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("layer_stride", ctypes.c_int64),
+        ("w_router", ctypes.c_void_p), ("b_router", ctypes.c_void_p), ("rms_scale", ctypes.c_void_p),
+        ("w_in", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
+    ]
+
+
+class BlockffnStats(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64), ("n_chunks", ctypes.c_int64), ("n_experts", ctypes.c_int64),
+        ("chunk_len", ctypes.c_int64), ("active_pairs", ctypes.c_int64), ("union_sum", ctypes.c_int64),
+        ("reuse_num", ctypes.c_int64), ("reuse_den", ctypes.c_int64), ("hist", ctypes.c_int64 * 129),
+    ]
+
+
+class BlockFFNError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where} failed ({status}): {message}")
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libblockffn.so (built by `python -m activation_sparse_moe_amd.build`)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m activation_sparse_moe_amd.build` "
+                               "(the BlockFFN path has no fallback)")
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lp = ctypes.POINTER(BlockffnLayer)
+        lib.blockffn_route.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, vp]
+        lib.blockffn_chunk_union.argtypes = [i32, vp, i64, i32, vp, vp, vp, vp]
+        lib.blockffn_forward.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, i32, vp, sz, vp, vp]
+        lib.blockffn_sparsity_stats.argtypes = [i32, vp, i64, i32, vp, vp]
+        for f in ("blockffn_route", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats"):
+            getattr(lib, f).restype = ctypes.c_int
+        lib.blockffn_set_stage_events.argtypes = [vp, i32]
+        lib.blockffn_set_stage_events.restype = ctypes.c_int
+        lib.blockffn_workspace_size.argtypes = [lp, i64, i32, i32]
+        lib.blockffn_workspace_size.restype = sz
+        lib.blockffn_status_string.argtypes = [ctypes.c_int]
+        lib.blockffn_status_string.restype = ctypes.c_char_p
+        lib.blockffn_last_error.argtypes = []
+        lib.blockffn_last_error.restype = ctypes.c_char_p
+        lib.blockffn_version.argtypes = []
+        lib.blockffn_version.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def check(status: int, where: str) -> None:
+    if status != OK:
+        lib = load()
+        raise BlockFFNError(status, where, lib.blockffn_last_error().decode(errors="replace"))

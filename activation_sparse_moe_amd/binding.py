@@ -1,0 +1,237 @@
+"""Python binding of libblockffn with the C ABI's names.
+
+PyTorch supplies device memory and streams only; each function marshals its
+arguments into one call of the C ABI, which enqueues HIP kernels on the
+current torch stream (or the stream given).  Output tensors are allocated
+here when the caller passes none.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _capi
+from ._capi import BF16, F32, MODES, BlockffnLayer, check, load
+
+_ALIGN = 256
+_STATS_WORDS = 8 + 129
+
+
+def _torch_dtype(dtype: int) -> torch.dtype:
+    return torch.float32 if dtype == F32 else torch.bfloat16
+
+
+def _elem(dtype: int) -> int:
+    return 4 if dtype == F32 else 2
+
+
+def _round(v: int, a: int = _ALIGN) -> int:
+    return (v + a - 1) // a * a
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _to_device(a, dtype: int, device) -> torch.Tensor:
+    """numpy float32 / uint16-bf16-bits (or a torch tensor) -> device tensor of the layer dtype."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device=device, dtype=_torch_dtype(dtype)).contiguous()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        assert dtype == BF16, "bf16 bit patterns given for an fp32 layer"
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    assert a.dtype == np.float32, f"expected float32 or uint16 bf16 bits, got {a.dtype}"
+    return torch.from_numpy(a).to(device=device, dtype=_torch_dtype(dtype))
+
+
+class DeviceLayer:
+    """`replicas` copies of one BlockFFN layer in a single device buffer.
+
+    Every copy has the same internal layout, so copy r's tensors sit at
+    replica 0's addresses plus r * stride bytes, which is the stacked-layer
+    convention of the C ABI (chunk c uses copy c % n_layers).  The copies are
+    distinct memory, so a stack of them streams from HBM like a stack of
+    distinct layers.
+    """
+
+    def __init__(self, d: int, n_experts: int, d_expert: int, dtype: int, rms_eps: float = 1e-6,
+                 device="cuda", replicas: int = 1, has_bias: bool = True, has_scale: bool = False):
+        assert dtype in (F32, BF16)
+        self.d, self.n_experts, self.d_expert, self.dtype = d, n_experts, d_expert, dtype
+        self.rms_eps, self.replicas, self.device = float(rms_eps), int(replicas), torch.device(device)
+        es = _elem(dtype)
+        E, de = n_experts, d_expert
+        sizes = [("w_router", E * d * es), ("b_router", 4 * E if has_bias else 0),
+                 ("rms_scale", 4 * E if has_scale else 0), ("w_in", E * de * d * es), ("w_out", E * d * de * es)]
+        self._off = {}
+        off = 0
+        for name, nbytes in sizes:
+            self._off[name] = (off, nbytes) if nbytes else None
+            off = _round(off + nbytes)
+        self.stride = _round(off, 4096)
+        self.buffer = torch.empty(self.stride * self.replicas, dtype=torch.uint8, device=self.device)
+
+    # views into copy r
+    def _view(self, name: str, r: int, shape, dtype: torch.dtype) -> Optional[torch.Tensor]:
+        slot = self._off[name]
+        if slot is None:
+            return None
+        off, nbytes = slot
+        base = r * self.stride + off
+        return self.buffer[base:base + nbytes].view(dtype).view(*shape)
+
+    def tensors(self, r: int = 0) -> dict:
+        td = _torch_dtype(self.dtype)
+        E, d, de = self.n_experts, self.d, self.d_expert
+        return dict(w_router=self._view("w_router", r, (E, d), td),
+                    b_router=self._view("b_router", r, (E,), torch.float32),
+                    rms_scale=self._view("rms_scale", r, (E,), torch.float32),
+                    w_in=self._view("w_in", r, (E, de, d), td),
+                    w_out=self._view("w_out", r, (E, d, de), td))
+
+    @classmethod
+    def from_arrays(cls, w_router, b_router, rms_scale, w_in, w_out, dtype: int, rms_eps: float = 1e-6,
+                    device="cuda", replicas: int = 1) -> "DeviceLayer":
+        E, d = w_router.shape
+        de = w_in.shape[1]
+        self = cls(d, E, de, dtype, rms_eps, device, replicas, has_bias=b_router is not None,
+                   has_scale=rms_scale is not None)
+        t = self.tensors(0)
+        t["w_router"].copy_(_to_device(w_router, dtype, self.device))
+        t["w_in"].copy_(_to_device(w_in, dtype, self.device))
+        t["w_out"].copy_(_to_device(w_out, dtype, self.device))
+        if b_router is not None:
+            t["b_router"].copy_(torch.as_tensor(np.asarray(b_router, np.float32)).to(self.device))
+        if rms_scale is not None:
+            t["rms_scale"].copy_(torch.as_tensor(np.asarray(rms_scale, np.float32)).to(self.device))
+        for r in range(1, replicas):
+            self.buffer[r * self.stride:(r + 1) * self.stride].copy_(self.buffer[:self.stride])
+        return self
+
+    @classmethod
+    def from_workload(cls, layer, device="cuda", replicas: int = 1) -> "DeviceLayer":
+        return cls.from_arrays(layer.w_router, layer.b_router, layer.rms_scale, layer.w_in, layer.w_out,
+                               F32 if layer.dtype == "f32" else BF16, layer.rms_eps, device, replicas)
+
+    def descriptor(self) -> BlockffnLayer:
+        t = self.tensors(0)
+        return BlockffnLayer(self.d, self.n_experts, self.d_expert, self.dtype, self.rms_eps, 0,
+                             self.stride, t["w_router"].data_ptr(),
+                             t["b_router"].data_ptr() if t["b_router"] is not None else None,
+                             t["rms_scale"].data_ptr() if t["rms_scale"] is not None else None,
+                             t["w_in"].data_ptr(), t["w_out"].data_ptr())
+
+    @property
+    def mask_words(self) -> int:
+        return (self.n_experts + 63) // 64
+
+
+def tokens_to_device(x, dtype: int, device="cuda") -> torch.Tensor:
+    return _to_device(x, dtype, device)
+
+
+def blockffn_route(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, n_layers: Optional[int] = None,
+                   gates: Optional[torch.Tensor] = None, token_masks: Optional[torch.Tensor] = None,
+                   preact: Optional[torch.Tensor] = None, want_preact: bool = False, stream=None):
+    """Router (ReLU + RMSNorm) -> (gates [T][E] f32, token_masks [T][W] int64 bit patterns, preact or None)."""
+    T = x.shape[0]
+    E = layer.n_experts
+    if gates is None:
+        gates = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    if token_masks is None:
+        token_masks = torch.empty((T, layer.mask_words), dtype=torch.int64, device=x.device)
+    if want_preact and preact is None:
+        preact = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    desc = layer.descriptor()
+    nl = layer.replicas if n_layers is None else n_layers
+    check(load().blockffn_route(ctypes.byref(desc), nl, _ptr(x), T, chunk_len, _ptr(gates), _ptr(token_masks),
+                                _ptr(preact), _stream(stream)), "blockffn_route")
+    return gates, token_masks, preact
+
+
+def blockffn_chunk_union(n_experts: int, token_masks: torch.Tensor, chunk_len: int,
+                         chunk_masks: Optional[torch.Tensor] = None, active_count: Optional[torch.Tensor] = None,
+                         active_list: Optional[torch.Tensor] = None, stream=None):
+    """Chunk union -> (chunk_masks [C][W] int64, active_count [C] int32, active_list [C][E] int32)."""
+    T, W = token_masks.shape
+    C = T // chunk_len if chunk_len > 0 else 0
+    dev = token_masks.device
+    if chunk_masks is None:
+        chunk_masks = torch.empty((C, W), dtype=torch.int64, device=dev)
+    if active_count is None:
+        active_count = torch.empty((C,), dtype=torch.int32, device=dev)
+    if active_list is None:
+        active_list = torch.empty((C, n_experts), dtype=torch.int32, device=dev)
+    check(load().blockffn_chunk_union(n_experts, _ptr(token_masks), T, chunk_len, _ptr(chunk_masks),
+                                      _ptr(active_count), _ptr(active_list), _stream(stream)),
+          "blockffn_chunk_union")
+    return chunk_masks, active_count, active_list
+
+
+def blockffn_workspace_size(layer: DeviceLayer, n_tokens: int, chunk_len: int, mode="auto") -> int:
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    desc = layer.descriptor()
+    return int(load().blockffn_workspace_size(ctypes.byref(desc), n_tokens, chunk_len, m))
+
+
+def alloc_workspace(layer: DeviceLayer, n_tokens: int, chunk_len: int, mode="auto") -> torch.Tensor:
+    nbytes = blockffn_workspace_size(layer, n_tokens, chunk_len, mode)
+    # torch's caching allocator returns 256-byte aligned blocks
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=layer.device)
+
+
+def blockffn_forward(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, gates: torch.Tensor,
+                     active_count: Optional[torch.Tensor], active_list: Optional[torch.Tensor], mode="auto",
+                     n_layers: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                     y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Expert evaluation over each chunk's union -> y [T][d] fp32."""
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(layer, T, chunk_len, m)
+    desc = layer.descriptor()
+    nl = layer.replicas if n_layers is None else n_layers
+    check(load().blockffn_forward(ctypes.byref(desc), nl, _ptr(x), T, chunk_len, _ptr(gates), _ptr(active_count),
+                                  _ptr(active_list), m, _ptr(workspace), workspace.numel(), _ptr(y),
+                                  _stream(stream)), "blockffn_forward")
+    return y
+
+
+def blockffn_sparsity_stats(n_experts: int, token_masks: torch.Tensor, chunk_len: int,
+                            stats_dev: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Sparsity statistics into a device int64 tensor laid out as blockffn_stats."""
+    if stats_dev is None:
+        stats_dev = torch.empty((_STATS_WORDS,), dtype=torch.int64, device=token_masks.device)
+    T = token_masks.shape[0]
+    check(load().blockffn_sparsity_stats(n_experts, _ptr(token_masks), T, chunk_len, _ptr(stats_dev),
+                                         _stream(stream)), "blockffn_sparsity_stats")
+    return stats_dev
+
+
+def stats_dict(stats_dev: torch.Tensor) -> dict:
+    v = stats_dev.cpu().numpy()
+    keys = ("n_tokens", "n_chunks", "n_experts", "chunk_len", "active_pairs", "union_sum", "reuse_num", "reuse_den")
+    out = {k: int(v[i]) for i, k in enumerate(keys)}
+    E = out["n_experts"]
+    out["hist"] = v[8:8 + E + 1].astype(np.int64)
+    T, C = out["n_tokens"], out["n_chunks"]
+    out["tls"] = 1.0 - out["active_pairs"] / (T * E) if T else 0.0
+    out["cls"] = 1.0 - out["union_sum"] / (C * E) if C else 0.0
+    out["reuse"] = out["reuse_num"] / out["reuse_den"] if out["reuse_den"] else 0.0
+    return out
+
+
+def masks_to_u64(token_masks: torch.Tensor) -> np.ndarray:
+    return token_masks.cpu().numpy().view(np.uint64)

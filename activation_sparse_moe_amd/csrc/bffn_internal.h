@@ -1,0 +1,97 @@
+// Internal declarations shared by the gfx950 kernels of libblockffn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "blockffn.h"
+
+namespace bffn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // four waves
+constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, each with its own L2
+
+// Kernel-side view of a (stack of) layer(s).  Layer l's tensors sit at
+// ptr + l * stride bytes; chunk c uses layer c % n_layers.
+struct LayerArgs {
+  const void* w_router;
+  const float* b_router;
+  const float* rms_scale;
+  const void* w_in;
+  const void* w_out;
+  int64_t stride;
+  int32_t n_layers;
+  int32_t d, E, de;
+  float eps;
+};
+
+template <typename P>
+__device__ __forceinline__ P layer_ptr(P p, int64_t stride, int64_t unit, int n_layers) {
+  if (p == nullptr || n_layers == 1) return p;
+  return reinterpret_cast<P>(reinterpret_cast<const char*>(p) + stride * (unit % n_layers));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Swish with beta = 1 (SiLU): u * logistic(u).
+__device__ __forceinline__ float swish(float u) { return u / (1.0f + __expf(-u)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Blocks of one launch are handed to the 8 XCDs round-robin.  Renumber them
+// so that each XCD works through one contiguous range of logical blocks:
+// blocks of the same unit then share that XCD's L2 for their common operand.
+// The grid is padded to a multiple of 8; returns -1 for padding blocks.
+__device__ __forceinline__ int64_t xcd_logical_block(int64_t bid, int64_t n_logical) {
+  const int64_t per = (n_logical + kXcds - 1) / kXcds;
+  const int64_t logical = (bid % kXcds) * per + bid / kXcds;
+  return logical < n_logical ? logical : -1;
+}
+inline int64_t xcd_grid(int64_t n_logical) { return ((n_logical + kXcds - 1) / kXcds) * kXcds; }
+
+// Caller-provided events recorded around the forward's kernels (may be empty).
+struct StageEvents {
+  hipEvent_t* ev = nullptr;
+  int n = 0;
+  void record(int k, hipStream_t s) const {
+    if (ev != nullptr && k < n) (void)hipEventRecord(ev[k], s);
+  }
+};
+
+// ---- launchers (host side, enqueue only; arguments already validated) ----
+hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len, int dtype,
+                        float* gates, uint64_t* masks, float* preact, hipStream_t s);
+hipError_t launch_chunk_union(int E, const uint64_t* masks, int64_t n_tokens, int chunk_len,
+                              uint64_t* chunk_masks, int32_t* count, int32_t* list, hipStream_t s);
+hipError_t launch_stats(int E, const uint64_t* masks, int64_t n_tokens, int chunk_len,
+                        blockffn_stats* out, hipStream_t s);
+hipError_t launch_forward_gemv(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len,
+                               int dtype, const float* gates, const int32_t* count, const int32_t* list,
+                               bool dense, float* hbuf, float* y, const StageEvents& se, hipStream_t s);
+hipError_t launch_forward_mfma(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len,
+                               const float* gates, const int32_t* count, const int32_t* list, bool dense,
+                               uint16_t* hbuf, float* y, const StageEvents& se, hipStream_t s);
+
+bool route_uses_mfma(int d, int E, int chunk_len, int dtype);
+bool forward_mfma_supported(int d, int de, int dtype);
+
+}  // namespace bffn

@@ -1,0 +1,240 @@
+// C ABI of libblockffn: host-side validation, mode selection and dispatch to
+// the gfx950 kernels.  Validation never touches the HIP runtime, so a call
+// that fails it enqueues nothing (and works on a machine without a GPU).
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "bffn_internal.h"
+
+#define BFFN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512];
+thread_local bffn::StageEvents g_stage_events;
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Largest number of units one call accepts: keeps every grid below 2^31 blocks.
+constexpr int64_t kMaxUnits = int64_t(1) << 20;
+
+int check_chunking(int64_t n_tokens, int32_t chunk_len) {
+  if (chunk_len < 1 || chunk_len > 32) return fail(BLOCKFFN_ERR_CHUNK, "chunk_len %d outside [1, 32]", chunk_len);
+  if (n_tokens < 0) return fail(BLOCKFFN_ERR_CHUNK, "n_tokens %lld is negative", (long long)n_tokens);
+  if (n_tokens % chunk_len != 0)
+    return fail(BLOCKFFN_ERR_CHUNK, "n_tokens %lld is not a multiple of chunk_len %d", (long long)n_tokens,
+                chunk_len);
+  if (n_tokens / chunk_len > kMaxUnits)
+    return fail(BLOCKFFN_ERR_CHUNK, "%lld chunks exceed the per-call limit of %lld; split the call",
+                (long long)(n_tokens / chunk_len), (long long)kMaxUnits);
+  return BLOCKFFN_OK;
+}
+
+int check_experts(int32_t E) {
+  if (E < 1 || E > 128) return fail(BLOCKFFN_ERR_SHAPE, "n_experts %d outside [1, 128]", E);
+  return BLOCKFFN_OK;
+}
+
+int check_layer(const blockffn_layer* ly, int32_t n_layers) {
+  if (!ly) return fail(BLOCKFFN_ERR_NULL, "layer descriptor is NULL");
+  if (ly->dtype != BLOCKFFN_F32 && ly->dtype != BLOCKFFN_BF16)
+    return fail(BLOCKFFN_ERR_DTYPE, "unknown dtype %d", ly->dtype);
+  if (int r = check_experts(ly->n_experts)) return r;
+  if (ly->d < 64 || ly->d % 64 != 0 || ly->d > (1 << 16))
+    return fail(BLOCKFFN_ERR_SHAPE, "d %d must be a positive multiple of 64 (at most 65536)", ly->d);
+  if (ly->d_expert < 16 || ly->d_expert % 16 != 0 || ly->d_expert > 1024)
+    return fail(BLOCKFFN_ERR_SHAPE, "d_expert %d must be a multiple of 16 in [16, 1024]", ly->d_expert);
+  if (!std::isfinite(ly->rms_eps) || ly->rms_eps < 0.f)
+    return fail(BLOCKFFN_ERR_SHAPE, "rms_eps must be finite and >= 0");
+  if (ly->reserved != 0) return fail(BLOCKFFN_ERR_SHAPE, "reserved field must be 0");
+  if (n_layers < 1) return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d < 1", n_layers);
+  if (n_layers > 1 && ly->layer_stride <= 0)
+    return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d > 1 needs a positive layer_stride", n_layers);
+  if (n_layers > 1 && ly->layer_stride % 256 != 0)
+    return fail(BLOCKFFN_ERR_ALIGN, "layer_stride %lld is not a multiple of 256", (long long)ly->layer_stride);
+  if (!ly->w_router || !ly->w_in || !ly->w_out)
+    return fail(BLOCKFFN_ERR_NULL, "w_router, w_in and w_out must all be non-NULL");
+  if (!aligned(ly->w_router, 16) || !aligned(ly->w_in, 16) || !aligned(ly->w_out, 16))
+    return fail(BLOCKFFN_ERR_ALIGN, "weight pointers must be 16-byte aligned");
+  if (!aligned(ly->b_router, 4) || !aligned(ly->rms_scale, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "b_router and rms_scale must be 4-byte aligned");
+  return BLOCKFFN_OK;
+}
+
+bffn::LayerArgs layer_args(const blockffn_layer* ly, int32_t n_layers) {
+  bffn::LayerArgs la;
+  la.w_router = ly->w_router;
+  la.b_router = ly->b_router;
+  la.rms_scale = ly->rms_scale;
+  la.w_in = ly->w_in;
+  la.w_out = ly->w_out;
+  la.stride = n_layers > 1 ? ly->layer_stride : 0;
+  la.n_layers = n_layers;
+  la.d = ly->d;
+  la.E = ly->n_experts;
+  la.de = ly->d_expert;
+  la.eps = ly->rms_eps;
+  return la;
+}
+
+enum class Path { kGemv, kMfma };
+
+// Resolves `mode` to a kernel family; returns a status code.
+int resolve_mode(const blockffn_layer* ly, int32_t chunk_len, int32_t mode, Path* path, bool* dense) {
+  const bool mfma_ok = bffn::forward_mfma_supported(ly->d, ly->d_expert, ly->dtype);
+  const bool auto_mfma = mfma_ok && chunk_len >= 8;
+  *dense = false;
+  switch (mode) {
+    case BLOCKFFN_MODE_AUTO:
+      *path = auto_mfma ? Path::kMfma : Path::kGemv;
+      return BLOCKFFN_OK;
+    case BLOCKFFN_MODE_GEMV:
+      *path = Path::kGemv;
+      return BLOCKFFN_OK;
+    case BLOCKFFN_MODE_CHUNK_MFMA:
+      if (!mfma_ok)
+        return fail(BLOCKFFN_ERR_MODE, "CHUNK_MFMA needs bf16 with d and d_expert multiples of 128");
+      *path = Path::kMfma;
+      return BLOCKFFN_OK;
+    case BLOCKFFN_MODE_DENSE:
+      *path = auto_mfma ? Path::kMfma : Path::kGemv;
+      *dense = true;
+      return BLOCKFFN_OK;
+    case BLOCKFFN_MODE_GROUPED:
+      return fail(BLOCKFFN_ERR_MODE, "GROUPED mode is not available in this build");
+    default:
+      return fail(BLOCKFFN_ERR_MODE, "unknown mode %d", mode);
+  }
+}
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t hbuf_bytes(const blockffn_layer* ly, int64_t n_tokens, Path path) {
+  const size_t elem = path == Path::kMfma ? 2 : 4;
+  return round256((size_t)n_tokens * (size_t)ly->n_experts * (size_t)ly->d_expert * elem);
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BLOCKFFN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return BLOCKFFN_OK;
+}
+
+}  // namespace
+
+BFFN_EXPORT int blockffn_route(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+                               int32_t chunk_len, float* gates, uint64_t* token_masks, float* preact,
+                               hipStream_t stream) {
+  if (int r = check_layer(layer, n_layers)) return r;
+  if (int r = check_chunking(n_tokens, chunk_len)) return r;
+  if (n_tokens == 0) return BLOCKFFN_OK;  // nothing is read or written; buffers may be NULL
+  if (!x || !gates || !token_masks) return fail(BLOCKFFN_ERR_NULL, "x, gates and token_masks must be non-NULL");
+  if (!aligned(x, 16) || !aligned(gates, 4) || !aligned(token_masks, 8) || !aligned(preact, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "x must be 16-byte, gates/preact 4-byte and token_masks 8-byte aligned");
+  const bffn::LayerArgs la = layer_args(layer, n_layers);
+  return hip_status(bffn::launch_route(la, x, n_tokens, chunk_len, layer->dtype, gates, token_masks, preact, stream),
+                    "router launch");
+}
+
+BFFN_EXPORT int blockffn_chunk_union(int32_t n_experts, const uint64_t* token_masks, int64_t n_tokens,
+                                     int32_t chunk_len, uint64_t* chunk_masks, int32_t* active_count,
+                                     int32_t* active_list, hipStream_t stream) {
+  if (int r = check_experts(n_experts)) return r;
+  if (int r = check_chunking(n_tokens, chunk_len)) return r;
+  if (n_tokens == 0) return BLOCKFFN_OK;
+  if (!token_masks || !chunk_masks || !active_count || !active_list)
+    return fail(BLOCKFFN_ERR_NULL, "token_masks, chunk_masks, active_count and active_list must be non-NULL");
+  if (!aligned(token_masks, 8) || !aligned(chunk_masks, 8) || !aligned(active_count, 4) || !aligned(active_list, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "mask arrays must be 8-byte and count/list 4-byte aligned");
+  return hip_status(bffn::launch_chunk_union(n_experts, token_masks, n_tokens, chunk_len, chunk_masks, active_count,
+                                             active_list, stream),
+                    "chunk-union launch");
+}
+
+BFFN_EXPORT size_t blockffn_workspace_size(const blockffn_layer* layer, int64_t n_tokens, int32_t chunk_len,
+                                           int32_t mode) {
+  if (check_layer(layer, 1) != BLOCKFFN_OK || check_chunking(n_tokens, chunk_len) != BLOCKFFN_OK) return 0;
+  Path path;
+  bool dense;
+  if (resolve_mode(layer, chunk_len, mode, &path, &dense) != BLOCKFFN_OK) return 0;
+  return hbuf_bytes(layer, n_tokens, path);
+}
+
+BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+                                 int32_t chunk_len, const float* gates, const int32_t* active_count,
+                                 const int32_t* active_list, int32_t mode, void* workspace, size_t workspace_bytes,
+                                 float* y, hipStream_t stream) {
+  if (int r = check_layer(layer, n_layers)) return r;
+  if (int r = check_chunking(n_tokens, chunk_len)) return r;
+  Path path;
+  bool dense;
+  if (int r = resolve_mode(layer, chunk_len, mode, &path, &dense)) return r;
+  if (n_tokens == 0) return BLOCKFFN_OK;
+  if (!x || !gates || !y) return fail(BLOCKFFN_ERR_NULL, "x, gates and y must be non-NULL");
+  if (!dense && (!active_count || !active_list))
+    return fail(BLOCKFFN_ERR_NULL, "active_count and active_list must be non-NULL outside DENSE mode");
+  if (!aligned(x, 16) || !aligned(gates, 4) || !aligned(y, 16) || !aligned(active_count, 4) ||
+      !aligned(active_list, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "x and y must be 16-byte aligned, gates/count/list 4-byte aligned");
+  const size_t need = hbuf_bytes(layer, n_tokens, path);
+  if (need > 0 && !workspace) return fail(BLOCKFFN_ERR_NULL, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned(workspace, 256)) return fail(BLOCKFFN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  const bffn::LayerArgs la = layer_args(layer, n_layers);
+  hipError_t e;
+  if (path == Path::kMfma)
+    e = bffn::launch_forward_mfma(la, static_cast<const uint16_t*>(x), n_tokens, chunk_len, gates, active_count,
+                                  active_list, dense, static_cast<uint16_t*>(workspace), y, g_stage_events, stream);
+  else
+    e = bffn::launch_forward_gemv(la, x, n_tokens, chunk_len, layer->dtype, gates, active_count, active_list, dense,
+                                  static_cast<float*>(workspace), y, g_stage_events, stream);
+  return hip_status(e, "forward launch");
+}
+
+BFFN_EXPORT int blockffn_sparsity_stats(int32_t n_experts, const uint64_t* token_masks, int64_t n_tokens,
+                                        int32_t chunk_len, blockffn_stats* stats_dev, hipStream_t stream) {
+  if (int r = check_experts(n_experts)) return r;
+  if (int r = check_chunking(n_tokens, chunk_len)) return r;
+  if (!token_masks || !stats_dev) return fail(BLOCKFFN_ERR_NULL, "token_masks and stats_dev must be non-NULL");
+  if (!aligned(token_masks, 8) || !aligned(stats_dev, 8))
+    return fail(BLOCKFFN_ERR_ALIGN, "token_masks and stats_dev must be 8-byte aligned");
+  return hip_status(bffn::launch_stats(n_experts, token_masks, n_tokens, chunk_len, stats_dev, stream),
+                    "stats launch");
+}
+
+BFFN_EXPORT int blockffn_set_stage_events(hipEvent_t* events, int32_t n_events) {
+  if (events != nullptr && n_events < 1) return fail(BLOCKFFN_ERR_SHAPE, "n_events %d < 1", n_events);
+  g_stage_events.ev = events;
+  g_stage_events.n = events != nullptr ? n_events : 0;
+  return BLOCKFFN_OK;
+}
+
+BFFN_EXPORT const char* blockffn_status_string(int status) {
+  switch (status) {
+    case BLOCKFFN_OK: return "ok";
+    case BLOCKFFN_ERR_NULL: return "a required pointer is NULL";
+    case BLOCKFFN_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case BLOCKFFN_ERR_DTYPE: return "unknown dtype";
+    case BLOCKFFN_ERR_CHUNK: return "bad chunk_len or n_tokens";
+    case BLOCKFFN_ERR_WORKSPACE: return "workspace too small";
+    case BLOCKFFN_ERR_MODE: return "unknown or unsupported mode";
+    case BLOCKFFN_ERR_ALIGN: return "misaligned pointer or stride";
+    case BLOCKFFN_ERR_LAYERS: return "bad layer count or stride";
+    case BLOCKFFN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+BFFN_EXPORT const char* blockffn_last_error(void) { return g_err; }
+
+BFFN_EXPORT int blockffn_version(void) { return BLOCKFFN_VERSION; }

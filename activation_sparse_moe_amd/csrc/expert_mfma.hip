@@ -1,0 +1,235 @@
+// Expert streaming on the matrix cores: the chunk path (bf16, L >= 8).
+// (BlockFFN write-up, lsdiaocha.cn, §4 acceleration kernel: multiply only by
+// the experts in the union of the chunk's activations, batching the chunk's
+// tokens, then mask the irrelevant activations; §7: an outer loop over the
+// active experts with a batched product inside.)
+//
+// Up:   H'[unit][slot] (L x d_e) = g[:, i] * Swish(X_chunk W_in[i]^T), stored bf16
+// Down: Y_chunk (L x d) = sum over the union's slots, in list order, of
+//       H'[unit][slot] W_out[i]^T, accumulated in fp32 registers
+//
+// Both are tall-skinny products (L <= 32 tokens against 128..4096 weight
+// rows), so weights are the streamed MFMA operand A (16 rows per tile) and
+// tokens the small operand B (16 columns per tile, padded with zeros past L).
+// Every weight element is used by exactly one lane, so A goes from HBM
+// straight into registers with no LDS round trip: per 128-element step lane
+// (m = lane % 16, g = lane / 16) loads 64 contiguous bytes of its row at
+// element offset 32 g (four lanes cover 256 contiguous bytes of the row), and
+// MFMA q of the step contracts elements [32 g + 8 q, 32 g + 8 q + 8) of each
+// lane group; B is loaded with the same permutation of k, so the product is
+// exact whatever order the k's are visited in.  Each wave owns four 16-row
+// stripes (64 rows) and double-buffers the next step's loads.
+#include "bffn_internal.h"
+
+namespace bffn {
+namespace {
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int NT>
+struct Step {
+  u32x4 a[4][4];   // [stripe][q]
+  u32x4 b[NT][4];  // [token tile][q]
+};
+
+// A rows: a_row0 points at element 32 g of row m of stripe 0; stripes are
+// `a_stripe` elements apart.  B: b_row[tl] points at element 32 g of token
+// m + 16 tl's row (nullptr past L).
+template <int NT>
+__device__ __forceinline__ void load_step(Step<NT>& st, const uint16_t* a_row0, int64_t a_stripe,
+                                          const uint16_t* const (&b_row)[NT], int k0) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(a_row0 + s * a_stripe + k0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st.a[s][q] = p[q];
+  }
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) {
+    if (b_row[tl] != nullptr) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(b_row[tl] + k0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) st.b[tl][q] = p[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) st.b[tl][q] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void mfma_step(f32x4 (&acc)[4][NT], const Step<NT>& st) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl)
+        acc[s][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[s][q]), as_bf16x8(st.b[tl][q]),
+                                                             acc[s][tl], 0, 0, 0);
+}
+
+template <int NT>
+__global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
+                                                         int64_t n_units, int L, const float* __restrict__ gates,
+                                                         const int32_t* __restrict__ count,
+                                                         const int32_t* __restrict__ list, int dense,
+                                                         int64_t blocks_per_unit, uint16_t* __restrict__ hbuf) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int64_t lb = xcd_logical_block(blockIdx.x, n_units * blocks_per_unit);
+  if (lb < 0) return;
+  const int64_t unit = lb / blocks_per_unit;
+  const int wave_in_unit = (int)(lb % blocks_per_unit) * 4 + w;
+  const int d = la.d, de = la.de, E = la.E;
+  const int rbs = de >> 6;
+  const int slot = wave_in_unit / rbs, rb = wave_in_unit % rbs;
+  const int n_active = dense ? E : count[unit];
+  if (slot >= n_active) return;
+  const int i = dense ? slot : list[unit * E + slot];
+  const uint16_t* wi = layer_ptr(static_cast<const uint16_t*>(la.w_in), la.stride, unit, la.n_layers);
+  const uint16_t* a_row0 = wi + ((int64_t)i * de + rb * 64 + m) * d + g * 32;
+  const int64_t a_stripe = 16 * (int64_t)d;
+  const int64_t t0 = unit * L;
+  const uint16_t* b_row[NT];
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) {
+    const int n = m + 16 * tl;
+    b_row[tl] = n < L ? x + (t0 + n) * d + g * 32 : nullptr;
+  }
+  f32x4 acc[4][NT];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int tl = 0; tl < NT; ++tl) acc[s][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Step<NT> s0, s1;
+  load_step<NT>(s0, a_row0, a_stripe, b_row, 0);
+  for (int k0 = 0; k0 < d; k0 += 256) {
+    if (k0 + 128 < d) load_step<NT>(s1, a_row0, a_stripe, b_row, k0 + 128);
+    mfma_step<NT>(acc, s0);
+    if (k0 + 128 >= d) break;
+    if (k0 + 256 < d) load_step<NT>(s0, a_row0, a_stripe, b_row, k0 + 256);
+    mfma_step<NT>(acc, s1);
+  }
+
+  // D layout: lane (m, g) holds rows 4 g + r (r < 4), column m of each tile.
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) {
+    const int n = m + 16 * tl;
+    if (n >= L) continue;
+    const float gv = gates[(t0 + n) * E + i];
+    uint16_t* hrow = hbuf + ((unit * E + slot) * L + n) * (int64_t)de + rb * 64 + 4 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f32x4 v = acc[s][tl];
+      const uint32_t lo = f32_to_bf16(gv * swish(v[0])) | (f32_to_bf16(gv * swish(v[1])) << 16);
+      const uint32_t hi = f32_to_bf16(gv * swish(v[2])) | (f32_to_bf16(gv * swish(v[3])) << 16);
+      *reinterpret_cast<u32x2*>(hrow + s * 16) = u32x2{lo, hi};
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t n_units, int L,
+                                                           const int32_t* __restrict__ count,
+                                                           const int32_t* __restrict__ list, int dense,
+                                                           int64_t blocks_per_unit,
+                                                           const uint16_t* __restrict__ hbuf,
+                                                           float* __restrict__ y) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int64_t lb = xcd_logical_block(blockIdx.x, n_units * blocks_per_unit);
+  if (lb < 0) return;
+  const int64_t unit = lb / blocks_per_unit;
+  const int wave_in_unit = (int)(lb % blocks_per_unit) * 4 + w;
+  const int d = la.d, de = la.de, E = la.E;
+  const int kb = wave_in_unit * 64;
+  if (kb >= d) return;
+  const int n_active = dense ? E : count[unit];
+  const uint16_t* wo = layer_ptr(static_cast<const uint16_t*>(la.w_out), la.stride, unit, la.n_layers);
+  const int64_t a_stripe = 16 * (int64_t)de;
+  const int64_t t0 = unit * L;
+  const int spe = de >> 7;  // 128-element steps per expert
+  const int n_steps = n_active * spe;
+
+  f32x4 acc[4][NT];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int tl = 0; tl < NT; ++tl) acc[s][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Step p covers slot p / spe, elements [128 (p % spe), +128) of that expert.
+  auto load = [&](Step<NT>& st, int p) {
+    const int slot = p / spe, j0 = (p % spe) * 128;
+    const int i = dense ? slot : list[unit * E + slot];
+    const uint16_t* a_row0 = wo + ((int64_t)i * d + kb + m) * de + g * 32;
+    const uint16_t* b_row[NT];
+#pragma unroll
+    for (int tl = 0; tl < NT; ++tl) {
+      const int n = m + 16 * tl;
+      b_row[tl] = n < L ? hbuf + ((unit * E + slot) * L + n) * (int64_t)de + g * 32 : nullptr;
+    }
+    load_step<NT>(st, a_row0, a_stripe, b_row, j0);
+  };
+
+  Step<NT> s0, s1;
+  if (n_steps > 0) load(s0, 0);
+  for (int p = 0; p < n_steps; p += 2) {
+    if (p + 1 < n_steps) load(s1, p + 1);
+    mfma_step<NT>(acc, s0);
+    if (p + 1 >= n_steps) break;
+    if (p + 2 < n_steps) load(s0, p + 2);
+    mfma_step<NT>(acc, s1);
+  }
+
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) {
+    const int n = m + 16 * tl;
+    if (n >= L) continue;
+    float* yrow = y + (t0 + n) * d + kb + 4 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4*>(yrow + s * 16) = acc[s][tl];
+  }
+}
+
+template <int NT>
+hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int L, const float* gates,
+                     const int32_t* count, const int32_t* list, bool dense, uint16_t* hbuf, float* y,
+                     const StageEvents& se, hipStream_t s) {
+  se.record(0, s);
+  {
+    const int waves = la.E * (la.de >> 6);
+    const int64_t bpu = (waves + 3) / 4;
+    const int64_t nlog = units * bpu;
+    up_mfma_kernel<NT><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(la, x, units, L, gates, count, list,
+                                                                                dense ? 1 : 0, bpu, hbuf);
+  }
+  se.record(1, s);
+  {
+    const int waves = la.d >> 6;
+    const int64_t bpu = (waves + 3) / 4;
+    const int64_t nlog = units * bpu;
+    down_mfma_kernel<NT><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(la, units, L, count, list,
+                                                                                  dense ? 1 : 0, bpu, hbuf, y);
+  }
+  se.record(2, s);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool forward_mfma_supported(int d, int de, int dtype) {
+  return dtype == BLOCKFFN_BF16 && d % 128 == 0 && de % 128 == 0;
+}
+
+hipError_t launch_forward_mfma(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len,
+                               const float* gates, const int32_t* count, const int32_t* list, bool dense,
+                               uint16_t* hbuf, float* y, const StageEvents& se, hipStream_t s) {
+  const int64_t units = n_tokens / chunk_len;
+  if (units == 0) return hipSuccess;
+  if (chunk_len <= 16) return launch_nt<1>(la, x, units, chunk_len, gates, count, list, dense, hbuf, y, se, s);
+  return launch_nt<2>(la, x, units, chunk_len, gates, count, list, dense, hbuf, y, se, s);
+}
+
+}  // namespace bffn

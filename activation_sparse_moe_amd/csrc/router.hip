@@ -1,0 +1,238 @@
+// Router: z = W_r x + b, a = ReLU(z), g = s * a / sqrt(mean_E(a^2) + eps),
+// activation pattern bit i = [z_i > 0].
+// (BlockFFN write-up, lsdiaocha.cn, §2 core design: a ReLU router followed by
+// RMSNorm, which separates the activation pattern from its strength; BlockFFN
+// abstract, arXiv 2507.08771: a router integrating ReLU and RMSNorm.)
+//
+// One workgroup per unit (a chunk of L tokens, or one token when L == 1)
+// computes the unit's E x L pre-activations into LDS, then a fused epilogue
+// applies ReLU + RMSNorm and builds the 64-bit activation words with wave64
+// ballots.  Two producers of the pre-activations:
+//   * route_mfma_kernel (bf16, L >= 8): the router is a genuine E x d x L
+//     contraction; each wave streams a quarter of d for every expert row
+//     through v_mfma_f32_16x16x32_bf16 and the four partial sums are added in
+//     a fixed order in the epilogue (deterministic).
+//   * route_valu_kernel (fp32, or L < 8): a bandwidth-bound GEMV; lane groups
+//     stride over d with 16-byte loads and reduce with cross-lane shuffles.
+#include "bffn_internal.h"
+
+namespace bffn {
+namespace {
+
+// Partial sums zp[part][e][n] (n < L) in LDS -> gates, masks, optional z.
+// Wave w handles tokens n = w, w + 4, ...; lane l handles experts l, l + 64.
+__device__ void router_epilogue(const float* zp, int nparts, int E, int L, int64_t t0,
+                                const float* __restrict__ b, const float* __restrict__ s, float eps,
+                                float* __restrict__ gates, uint64_t* __restrict__ masks,
+                                float* __restrict__ preact) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int W = (E + 63) >> 6;
+  const bool v0 = lane < E, v1 = lane + 64 < E;
+  const float b0 = (v0 && b) ? b[lane] : 0.f, b1 = (v1 && b) ? b[lane + 64] : 0.f;
+  const float s0 = (v0 && s) ? s[lane] : 1.f, s1 = (v1 && s) ? s[lane + 64] : 1.f;
+  for (int n = w; n < L; n += 4) {
+    float z0 = 0.f, z1 = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+      if (v0) z0 += zp[(p * E + lane) * L + n];
+      if (v1) z1 += zp[(p * E + lane + 64) * L + n];
+    }
+    z0 += b0;
+    z1 += b1;
+    const bool on0 = v0 && z0 > 0.f, on1 = v1 && z1 > 0.f;
+    const float a0 = on0 ? z0 : 0.f, a1 = on1 ? z1 : 0.f;
+    // mean over all E outputs, inactive ones included
+    const float ms = wave_sum(a0 * a0 + a1 * a1) / (float)E;
+    const float inv = 1.0f / sqrtf(ms + eps);
+    const int64_t t = t0 + n;
+    if (v0) gates[t * E + lane] = s0 * a0 * inv;
+    if (v1) gates[t * E + lane + 64] = s1 * a1 * inv;
+    if (preact) {
+      if (v0) preact[t * E + lane] = z0;
+      if (v1) preact[t * E + lane + 64] = z1;
+    }
+    const uint64_t m0 = __ballot(on0);
+    const uint64_t m1 = __ballot(on1);
+    if (lane == 0) {
+      masks[t * W] = m0;
+      if (W > 1) masks[t * W + 1] = m1;
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float dot16(const T* a, const T* b);
+
+template <>
+__device__ __forceinline__ float dot16<float>(const float* a, const float* b) {
+  const f32x4 va = *reinterpret_cast<const f32x4*>(a);
+  const f32x4 vb = *reinterpret_cast<const f32x4*>(b);
+  return va.x * vb.x + va.y * vb.y + va.z * vb.z + va.w * vb.w;
+}
+
+template <>
+__device__ __forceinline__ float dot16<uint16_t>(const uint16_t* a, const uint16_t* b) {
+  const u32x4 va = *reinterpret_cast<const u32x4*>(a);
+  const u32x4 vb = *reinterpret_cast<const u32x4*>(b);
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc += bf16_lo(va[q]) * bf16_lo(vb[q]) + bf16_hi(va[q]) * bf16_hi(vb[q]);
+  return acc;
+}
+
+// lpr lanes per router row (a power of two dividing 64); each lane covers nv
+// 16-byte vectors of the row.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const T* __restrict__ x, int L,
+                                                            int lpr, int nv, float* __restrict__ gates,
+                                                            uint64_t* __restrict__ masks,
+                                                            float* __restrict__ preact) {
+  extern __shared__ float zp[];  // [E][L]
+  const int64_t unit = blockIdx.x;
+  const T* wr = layer_ptr(static_cast<const T*>(la.w_router), la.stride, unit, la.n_layers);
+  const float* b = layer_ptr(la.b_router, la.stride, unit, la.n_layers);
+  const float* s = layer_ptr(la.rms_scale, la.stride, unit, la.n_layers);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int d = la.d, E = la.E;
+  constexpr int VEC = 16 / sizeof(T);
+  const int rpp = 64 / lpr, lg = lane / lpr, li = lane % lpr;
+  const int64_t t0 = unit * L;
+  for (int r0 = w * rpp; r0 < E; r0 += 4 * rpp) {
+    const int r = r0 + lg;
+    const bool rv = r < E;
+    for (int n = 0; n < L; ++n) {
+      float acc = 0.f;
+      if (rv) {
+        const T* wrow = wr + (int64_t)r * d;
+        const T* xrow = x + (t0 + n) * d;
+        for (int mm = 0; mm < nv; ++mm) {
+          const int k = (li + mm * lpr) * VEC;
+          acc += dot16<T>(wrow + k, xrow + k);
+        }
+      }
+      for (int off = lpr >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+      if (rv && li == 0) zp[r * L + n] = acc;
+    }
+  }
+  __syncthreads();
+  router_epilogue(zp, 1, E, L, t0, b, s, la.eps, gates, masks, preact);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// MFMA router.  Wave w owns d-range [w d/4, (w+1) d/4) for every expert row,
+// in blocks of four 16-row stripes.  Per 128-element step, lane (m, g)
+// (m = lane % 16, g = lane / 16) loads 64 contiguous bytes of row m at
+// element offset 32 g, and the same offset of token m's x; MFMA q of the
+// step contracts elements [32 g + 8 q, 32 g + 8 q + 8) of every lane group,
+// so A and B see one consistent permutation of the 128 k's.
+template <int NT>
+__global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
+                                                            int L, float* __restrict__ gates,
+                                                            uint64_t* __restrict__ masks,
+                                                            float* __restrict__ preact) {
+  extern __shared__ float zp[];  // [4][E][L]
+  const int64_t unit = blockIdx.x;
+  const uint16_t* wr = layer_ptr(static_cast<const uint16_t*>(la.w_router), la.stride, unit, la.n_layers);
+  const float* b = layer_ptr(la.b_router, la.stride, unit, la.n_layers);
+  const float* s = layer_ptr(la.rms_scale, la.stride, unit, la.n_layers);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int d = la.d, E = la.E;
+  const int kw = d >> 2;
+  const int64_t t0 = unit * L;
+  const int nstripes = E >> 4;
+  for (int sb = 0; sb < nstripes; sb += 4) {
+    f32x4 acc[4][NT];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl) acc[st][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = w * kw; k0 < (w + 1) * kw; k0 += 128) {
+      u32x4 bv[NT][4];
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl) {
+        const int n = m + 16 * tl;
+        if (n < L) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(x + (t0 + n) * d + k0 + g * 32);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bv[tl][q] = p[q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bv[tl][q] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      u32x4 av[4][4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (sb + st < nstripes) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(wr + (int64_t)((sb + st) * 16 + m) * d + k0 + g * 32);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) av[st][q] = p[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          if (sb + st < nstripes)
+#pragma unroll
+            for (int tl = 0; tl < NT; ++tl)
+              acc[st][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[st][q]), as_bf16x8(bv[tl][q]),
+                                                                    acc[st][tl], 0, 0, 0);
+    }
+    // D layout: lane (m, g) holds rows 4 g + r, column m of each 16 x 16 tile.
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (sb + st < nstripes) {
+#pragma unroll
+        for (int tl = 0; tl < NT; ++tl) {
+          const int n = m + 16 * tl;
+          if (n < L) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) zp[(w * E + (sb + st) * 16 + 4 * g + r) * L + n] = acc[st][tl][r];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  router_epilogue(zp, 4, E, L, t0, b, s, la.eps, gates, masks, preact);
+}
+
+}  // namespace
+
+bool route_uses_mfma(int d, int E, int chunk_len, int dtype) {
+  return dtype == BLOCKFFN_BF16 && chunk_len >= 8 && E % 16 == 0 && d % 512 == 0;
+}
+
+hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len, int dtype,
+                        float* gates, uint64_t* masks, float* preact, hipStream_t s) {
+  const int64_t units = n_tokens / chunk_len;
+  if (units == 0) return hipSuccess;
+  const int L = chunk_len;
+  if (route_uses_mfma(la.d, la.E, L, dtype)) {
+    const size_t lds = sizeof(float) * 4 * la.E * L;
+    if (L <= 16)
+      route_mfma_kernel<1><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
+          la, static_cast<const uint16_t*>(x), L, gates, masks, preact);
+    else
+      route_mfma_kernel<2><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
+          la, static_cast<const uint16_t*>(x), L, gates, masks, preact);
+  } else {
+    const size_t lds = sizeof(float) * la.E * L;
+    const int vec = dtype == BLOCKFFN_F32 ? 4 : 8;
+    const int nvec = la.d / vec;
+    int lpr = 64;
+    while (nvec % lpr) lpr >>= 1;
+    const int nv = nvec / lpr;
+    if (dtype == BLOCKFFN_F32)
+      route_valu_kernel<float><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
+          la, static_cast<const float*>(x), L, lpr, nv, gates, masks, preact);
+    else
+      route_valu_kernel<uint16_t><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
+          la, static_cast<const uint16_t*>(x), L, lpr, nv, gates, masks, preact);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bffn

@@ -1,0 +1,209 @@
+/*
+ * blockffn.h -- C ABI of the BlockFFN layer forward on MI355X (gfx950).
+ *
+ * The layer (BlockFFN write-up, lsdiaocha.cn, §2 core design; abstract of
+ * "BlockFFN: Towards End-Side Acceleration-Friendly Mixture-of-Experts with
+ * Chunk-Level Activation Sparsity", arXiv 2507.08771):
+ *
+ *   router   z = W_r x + b;  a = ReLU(z);  g = s * a / sqrt(mean_E(a^2) + eps)
+ *            expert i is active for the token iff z_i > 0
+ *   experts  E_i(x) = W_out[i] Swish(W_in[i] x), a non-gated MLP d -> d_e -> d
+ *   output   y = sum over the active experts of g_i E_i(x)
+ *
+ * and the chunk-level evaluation of write-up §4: for a chunk of L consecutive
+ * tokens, the union of their active experts is found and only those experts
+ * run, over every token of the chunk, each pair weighted by the token's own
+ * gate (zero for the experts the token did not activate).
+ *
+ * One export per stage of that pipeline: blockffn_route (router),
+ * blockffn_chunk_union (union + compacted expert list),
+ * blockffn_forward (expert streaming, gate scaling and sum) and
+ * blockffn_sparsity_stats (token- and chunk-level sparsity).
+ *
+ * General rules for every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *     the `layer` descriptor itself, which is a host struct read during the
+ *     call.  Buffers must stay valid until the queued work has completed;
+ *     the library keeps no reference after the call returns.
+ *   - No entry point allocates memory.  Scratch space for blockffn_forward is
+ *     a caller-provided workspace of at least blockffn_workspace_size() bytes.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); no
+ *     entry point synchronises.  Apart from the optional per-thread stage
+ *     timing events (blockffn_set_stage_events), calls carry no hidden state
+ *     and may be made from several threads at once on different buffers.
+ *   - Every entry point returns BLOCKFFN_OK (0) or a negative BLOCKFFN_ERR_*
+ *     code.  Arguments are validated on the host before anything is
+ *     enqueued: a call that fails validation enqueues nothing.
+ *     blockffn_last_error() gives a message for the calling thread's last
+ *     failure.  Nothing aborts and no C++ exception crosses the ABI.
+ *   - Layout: every matrix is row-major in the [out][in] convention, so each
+ *     expert's rows are contiguous: w_router[E][d], w_in[E][d_e][d],
+ *     w_out[E][d][d_e], x[T][d], gates[T][E], y[T][d].
+ *   - Chunks are the aligned, non-overlapping runs of chunk_len consecutive
+ *     tokens; n_tokens must be a multiple of chunk_len.  Chunk c covers
+ *     tokens [c*chunk_len, (c+1)*chunk_len).
+ *   - Token masks: token t's activation pattern is W = ceil(E/64) 64-bit
+ *     words at token_masks[t*W]; expert i is bit (i % 64) of word i / 64.
+ *   - A call with n_tokens == 0 validates its other arguments and enqueues
+ *     nothing; its token-sized buffers may then be NULL.
+ *
+ * Supported shapes: 1 <= E <= 128, d a multiple of 64, d_e a multiple of 16
+ * (at most 1024), 1 <= chunk_len <= 32.  The MFMA forward additionally needs
+ * bf16, d a multiple of 128 and d_e a multiple of 128.
+ */
+#ifndef BLOCKFFN_H_
+#define BLOCKFFN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BLOCKFFN_VERSION 1
+
+/* Element type of x and of every weight matrix. */
+#define BLOCKFFN_F32 0  /* IEEE binary32 */
+#define BLOCKFFN_BF16 1 /* bfloat16: the upper 16 bits of a binary32 */
+
+/* blockffn_forward modes. */
+#define BLOCKFFN_MODE_AUTO 0       /* bf16 with chunk_len >= 8 -> CHUNK_MFMA, else GEMV */
+#define BLOCKFFN_MODE_GEMV 1       /* vector-ALU streaming of the active experts (any dtype) */
+#define BLOCKFFN_MODE_CHUNK_MFMA 2 /* matrix-core tiles over each chunk's union (bf16) */
+#define BLOCKFFN_MODE_GROUPED 3    /* token-expert pairs grouped by expert (bf16, one layer) */
+#define BLOCKFFN_MODE_DENSE 4      /* every expert on every token (the comparison path) */
+
+/* Status codes. */
+#define BLOCKFFN_OK 0
+#define BLOCKFFN_ERR_NULL (-1)      /* a required pointer is NULL */
+#define BLOCKFFN_ERR_SHAPE (-2)     /* unsupported or inconsistent d / E / d_e */
+#define BLOCKFFN_ERR_DTYPE (-3)     /* unknown dtype */
+#define BLOCKFFN_ERR_CHUNK (-4)     /* chunk_len out of range or n_tokens % chunk_len != 0 */
+#define BLOCKFFN_ERR_WORKSPACE (-5) /* workspace smaller than blockffn_workspace_size() */
+#define BLOCKFFN_ERR_MODE (-6)      /* unknown mode, or a mode the layer's dtype/shape cannot use */
+#define BLOCKFFN_ERR_ALIGN (-7)     /* a pointer or the layer stride is misaligned */
+#define BLOCKFFN_ERR_LAYERS (-8)    /* n_layers < 1, or n_layers > 1 without a layer stride */
+#define BLOCKFFN_ERR_HIP (-9)       /* a HIP launch failed (see blockffn_last_error) */
+
+/*
+ * One BlockFFN layer (plain data; the library takes no ownership).
+ *
+ * With n_layers > 1 the entry points see a stack of layers of identical
+ * shape: layer l's tensors live at (char*)ptr + l * layer_stride for every
+ * pointer below (NULL pointers stay NULL), and chunk c uses layer
+ * c % n_layers.  layer_stride is ignored when n_layers == 1.
+ */
+typedef struct blockffn_layer {
+  int32_t d;          /* hidden size */
+  int32_t n_experts;  /* E */
+  int32_t d_expert;   /* d_e, hidden width of one expert MLP */
+  int32_t dtype;      /* BLOCKFFN_F32 or BLOCKFFN_BF16, for x and every weight */
+  float rms_eps;      /* RMSNorm epsilon, inside the square root (1e-6 typical) */
+  int32_t reserved;   /* must be 0 */
+  int64_t layer_stride;     /* bytes between consecutive layers (multiple of 256) */
+  const void* w_router;     /* [E][d], dtype */
+  const float* b_router;    /* [E] fp32 router bias, or NULL for none */
+  const float* rms_scale;   /* [E] fp32 RMSNorm scale, or NULL for ones */
+  const void* w_in;         /* [E][d_e][d], dtype */
+  const void* w_out;        /* [E][d][d_e], dtype */
+} blockffn_layer;
+
+/* Sparsity statistics (BlockFFN abstract; write-up §3 and §5). */
+typedef struct blockffn_stats {
+  int64_t n_tokens, n_chunks, n_experts, chunk_len;
+  int64_t active_pairs; /* sum over tokens of |M_t|; TLS = 1 - active_pairs / (T E) */
+  int64_t union_sum;    /* sum over chunks of |U_c|; CLS = 1 - union_sum / (C E) */
+  int64_t reuse_num;    /* sum over t >= 1 of |M_t and M_{t-1}| */
+  int64_t reuse_den;    /* sum over t >= 1 of |M_{t-1}|; reuse = reuse_num / reuse_den */
+  int64_t hist[129];    /* hist[k] = tokens with exactly k active experts, k <= E */
+} blockffn_stats;
+
+/*
+ * Router: pre-activations, ReLU, RMSNorm over the E outputs, activation
+ * pattern (write-up §2; abstract).
+ *   x            [n_tokens][d] in the layer's dtype
+ *   gates        [n_tokens][E] fp32 out: g = s * ReLU(z) / sqrt(mean_E(ReLU(z)^2) + eps),
+ *                exactly 0 for inactive experts
+ *   token_masks  [n_tokens][W] u64 out: bit i set iff z_i > 0
+ *   preact       [n_tokens][E] fp32 out (z), or NULL
+ *   chunk_len    maps tokens to chunks, and so to layers when n_layers > 1
+ * z is accumulated in fp32.  Errors: NULL, SHAPE, DTYPE, CHUNK, ALIGN, LAYERS, HIP.
+ */
+int blockffn_route(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+                   int32_t chunk_len, float* gates, uint64_t* token_masks, float* preact,
+                   hipStream_t stream);
+
+/*
+ * Chunk union and compaction (write-up §4; abstract: the union of the
+ * parameters several consecutive tokens activate).
+ *   token_masks   [n_tokens][W] u64 in
+ *   chunk_masks   [C][W] u64 out: OR of the chunk's token masks
+ *   active_count  [C] i32 out: number of experts in the union
+ *   active_list   [C][E] i32 out: the union's experts in ascending order,
+ *                 entries [active_count[c], E) set to -1
+ * Errors: NULL, SHAPE, CHUNK, ALIGN, HIP.
+ */
+int blockffn_chunk_union(int32_t n_experts, const uint64_t* token_masks, int64_t n_tokens,
+                         int32_t chunk_len, uint64_t* chunk_masks, int32_t* active_count,
+                         int32_t* active_list, hipStream_t stream);
+
+/*
+ * Expert evaluation over each chunk's union (write-up §4 acceleration
+ * kernel: multiply only by the union's experts, batch the chunk's tokens,
+ * mask the irrelevant activations with the gates; §7: outer loop over the
+ * active experts).
+ *   gates, active_count, active_list   as written by the two calls above
+ *                                      (active_* are ignored in DENSE mode)
+ *   y          [n_tokens][d] fp32 out, overwritten:
+ *              y_t = sum over i in the chunk's union of g[t][i] E_i(x_t)
+ *   workspace  device scratch of at least blockffn_workspace_size() bytes,
+ *              256-byte aligned; its contents need no initialisation
+ * GROUPED mode needs n_layers == 1.  Errors: NULL, SHAPE, DTYPE, CHUNK,
+ * WORKSPACE, MODE, ALIGN, LAYERS, HIP.
+ */
+int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+                     int32_t chunk_len, const float* gates, const int32_t* active_count,
+                     const int32_t* active_list, int32_t mode, void* workspace,
+                     size_t workspace_bytes, float* y, hipStream_t stream);
+
+/*
+ * Sparsity statistics of a mask stream (abstract: TLS and 8-token CLS;
+ * write-up §5: consecutive-token expert reuse, experts-per-token histogram).
+ *   stats_dev  one blockffn_stats in device memory, fully overwritten
+ * Errors: NULL, SHAPE, CHUNK, ALIGN, HIP.
+ */
+int blockffn_sparsity_stats(int32_t n_experts, const uint64_t* token_masks, int64_t n_tokens,
+                            int32_t chunk_len, blockffn_stats* stats_dev, hipStream_t stream);
+
+/*
+ * Stage timing (instrumentation for profilers and benchmarks).  While set,
+ * every blockffn_forward call of the calling thread records events[0] on its
+ * stream before its first kernel and events[k] right after its k-th kernel,
+ * for k < n_events.  The forward enqueues two kernels on the GEMV, MFMA and
+ * DENSE paths (expert up-projection, then down-projection).  `events` are
+ * caller-created hipEvents in caller memory that must stay valid while set;
+ * pass NULL to stop.  Errors: SHAPE (n_events < 1 with non-NULL events).
+ */
+int blockffn_set_stage_events(hipEvent_t* events, int32_t n_events);
+
+/* Workspace bytes blockffn_forward needs for these arguments (0 on invalid input). */
+size_t blockffn_workspace_size(const blockffn_layer* layer, int64_t n_tokens, int32_t chunk_len,
+                               int32_t mode);
+
+/* Static description of a status code. */
+const char* blockffn_status_string(int status);
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+const char* blockffn_last_error(void);
+
+/* BLOCKFFN_VERSION of the built library. */
+int blockffn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKFFN_H_ */

@@ -1,0 +1,187 @@
+"""The C-ABI library loads, exports what include/blockffn.h declares, matches
+the header's struct layout, and rejects bad arguments on the host.
+
+No test here runs GPU work: every call below fails host-side validation,
+which runs before any HIP call.  Calls that use placeholder device pointers
+are skipped on a machine that shows a GPU, so that no placeholder can ever
+reach a kernel.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from activation_sparse_moe_amd import _capi
+from activation_sparse_moe_amd._capi import BlockffnLayer, BlockffnStats
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "blockffn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _capi.load()
+
+
+def _no_gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+cpu_only = pytest.mark.skipif(not _no_gpu_visible(), reason="placeholder pointers are only used without a GPU")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(blockffn_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_capi.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _capi.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(declared) <= exported
+    # internal symbols stay hidden
+    assert not any(s.startswith("_ZN4bffn") for s in exported)
+
+
+def test_struct_layout_matches_header():
+    prog = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "blockffn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu\n", sizeof(blockffn_layer), offsetof(blockffn_layer, layer_stride),
+         offsetof(blockffn_layer, w_router), offsetof(blockffn_layer, w_out), sizeof(blockffn_stats));
+  printf("%zu %zu\n", offsetof(blockffn_stats, active_pairs), offsetof(blockffn_stats, hist));
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "layout.c")
+        exe = os.path.join(tmp, "layout")
+        open(src, "w").write(prog)
+        subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I",
+                        "/opt/rocm/include", src, "-o", exe], check=True)
+        lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    a = [int(v) for v in lines[0].split()]
+    b = [int(v) for v in lines[1].split()]
+    assert a == [ctypes.sizeof(BlockffnLayer), BlockffnLayer.layer_stride.offset, BlockffnLayer.w_router.offset,
+                 BlockffnLayer.w_out.offset, ctypes.sizeof(BlockffnStats)]
+    assert b == [BlockffnStats.active_pairs.offset, BlockffnStats.hist.offset]
+
+
+def test_version_and_status_strings(lib):
+    assert lib.blockffn_version() == 1
+    assert lib.blockffn_status_string(0) == b"ok"
+    for code in range(-9, 0):
+        s = lib.blockffn_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.blockffn_status_string(-100) == b"unknown status"
+
+
+P = 0x10000  # placeholder, 64 KiB aligned; never dereferenced (every call fails validation)
+
+
+def _layer(**kw):
+    f = dict(d=256, n_experts=16, d_expert=128, dtype=1, rms_eps=1e-6, reserved=0, layer_stride=0,
+             w_router=P, b_router=P, rms_scale=None, w_in=P, w_out=P)
+    f.update(kw)
+    return BlockffnLayer(**f)
+
+
+def _route(lib, layer, n_layers=1, x=P, T=16, L=8, gates=P, masks=P, preact=None):
+    return lib.blockffn_route(ctypes.byref(layer) if layer is not None else None, n_layers, x, T, L, gates, masks,
+                              preact, None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _capi.ERR_DTYPE),
+    (dict(n_experts=0), _capi.ERR_SHAPE),
+    (dict(n_experts=129), _capi.ERR_SHAPE),
+    (dict(d=100), _capi.ERR_SHAPE),
+    (dict(d=0), _capi.ERR_SHAPE),
+    (dict(d_expert=24), _capi.ERR_SHAPE),
+    (dict(d_expert=2048), _capi.ERR_SHAPE),
+    (dict(rms_eps=-1.0), _capi.ERR_SHAPE),
+    (dict(rms_eps=float("nan")), _capi.ERR_SHAPE),
+    (dict(reserved=1), _capi.ERR_SHAPE),
+    (dict(w_in=None), _capi.ERR_NULL),
+    (dict(w_router=P + 8), _capi.ERR_ALIGN),
+    (dict(b_router=P + 2), _capi.ERR_ALIGN),
+])
+def test_route_rejects_bad_layer(lib, kw, code):
+    assert _route(lib, _layer(**kw)) == code
+    assert lib.blockffn_last_error()
+
+
+@cpu_only
+def test_route_rejects_bad_arguments(lib):
+    assert _route(lib, None) == _capi.ERR_NULL
+    assert _route(lib, _layer(), n_layers=0) == _capi.ERR_LAYERS
+    assert _route(lib, _layer(), n_layers=2) == _capi.ERR_LAYERS            # no stride
+    assert _route(lib, _layer(layer_stride=1000), n_layers=2) == _capi.ERR_ALIGN
+    assert _route(lib, _layer(), L=0) == _capi.ERR_CHUNK
+    assert _route(lib, _layer(), L=33) == _capi.ERR_CHUNK
+    assert _route(lib, _layer(), T=12, L=8) == _capi.ERR_CHUNK             # ragged tail
+    assert _route(lib, _layer(), T=-8) == _capi.ERR_CHUNK
+    assert _route(lib, _layer(), x=None) == _capi.ERR_NULL
+    assert _route(lib, _layer(), gates=None) == _capi.ERR_NULL
+    assert _route(lib, _layer(), x=P + 4) == _capi.ERR_ALIGN
+    assert _route(lib, _layer(), masks=P + 4) == _capi.ERR_ALIGN
+    assert b"multiple of chunk_len" in (lib.blockffn_route(ctypes.byref(_layer()), 1, P, 12, 8, P, P, None, None)
+                                        and lib.blockffn_last_error())
+
+
+@cpu_only
+def test_union_and_stats_reject_bad_arguments(lib):
+    u = lib.blockffn_chunk_union
+    assert u(0, P, 16, 8, P, P, P, None) == _capi.ERR_SHAPE
+    assert u(200, P, 16, 8, P, P, P, None) == _capi.ERR_SHAPE
+    assert u(64, P, 16, 3, P, P, P, None) == _capi.ERR_CHUNK
+    assert u(64, None, 16, 8, P, P, P, None) == _capi.ERR_NULL
+    assert u(64, P, 16, 8, P, P, None, None) == _capi.ERR_NULL
+    assert u(64, P + 4, 16, 8, P, P, P, None) == _capi.ERR_ALIGN
+    s = lib.blockffn_sparsity_stats
+    assert s(0, P, 16, 8, P, None) == _capi.ERR_SHAPE
+    assert s(64, P, 16, 5, P, None) == _capi.ERR_CHUNK
+    assert s(64, P, 16, 8, None, None) == _capi.ERR_NULL
+    assert s(64, P, 16, 8, P + 4, None) == _capi.ERR_ALIGN
+
+
+def _forward(lib, layer, mode=0, T=16, L=8, ws=P, ws_bytes=1 << 40, y=P, count=P, lst=P, n_layers=1):
+    return lib.blockffn_forward(ctypes.byref(layer), n_layers, P, T, L, P, count, lst, mode, ws, ws_bytes, y, None)
+
+
+@cpu_only
+def test_forward_rejects_bad_arguments(lib):
+    assert _forward(lib, _layer(), mode=9) == _capi.ERR_MODE
+    assert _forward(lib, _layer(dtype=0), mode=_capi.MODE_CHUNK_MFMA) == _capi.ERR_MODE  # MFMA needs bf16
+    assert _forward(lib, _layer(d=192), mode=_capi.MODE_CHUNK_MFMA) == _capi.ERR_MODE    # d % 128
+    assert _forward(lib, _layer(), ws_bytes=1024) == _capi.ERR_WORKSPACE
+    assert _forward(lib, _layer(), ws=None) == _capi.ERR_NULL
+    assert _forward(lib, _layer(), ws=P + 64) == _capi.ERR_ALIGN
+    assert _forward(lib, _layer(), y=P + 4) == _capi.ERR_ALIGN
+    assert _forward(lib, _layer(), count=None) == _capi.ERR_NULL
+    assert _forward(lib, _layer(), T=20) == _capi.ERR_CHUNK
+
+
+def test_workspace_size(lib):
+    lay = _layer(d=2048, n_experts=64, d_expert=128)
+    T = 4096
+    # chunk path (bf16 hidden activations) and GEMV path (fp32)
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, _capi.MODE_CHUNK_MFMA) == T * 64 * 128 * 2
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 1, _capi.MODE_AUTO) == T * 64 * 128 * 4
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 3, _capi.MODE_AUTO) == 0   # ragged
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, 99) == 0

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case draws its inputs from the seeded generator, runs router -> chunk
+union -> expert forward -> stats on the GPU, runs the oracle on the same
+inputs, and compares element by element (bars in gpu_parity_util).  Shapes
+span several tiles and ragged tails: E not a multiple of 64 (and of 16),
+an odd number of 128-element steps, chunk lengths that pad a 16-token tile,
+single tokens, fp32 and bf16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_moe_amd import binding as B
+from activation_sparse_moe_amd._capi import BF16, F32
+from gpu_parity_util import (bits, check_route, check_union, check_y, oracle_full, run_gpu, say)
+from workload import CONFIGS, make_layer, make_tokens, make_workload
+
+pytestmark = pytest.mark.gpu
+
+# name: (d, E, d_e, dtype, L, chunks, bias_k, alpha, seed)
+CASES = {
+    "bf16_d512_E80_de256_L8": (512, 80, 256, "bf16", 8, 12, 0.9, 0.8, 101),     # MFMA router, 2 mask words
+    "bf16_d640_E70_de128_L8": (640, 70, 128, "bf16", 8, 10, 0.9, 0.8, 102),     # VALU router, 5 MFMA steps
+    "bf16_d512_E64_de128_L32": (512, 64, 128, "bf16", 32, 4, 1.0, 0.65, 103),   # two token tiles
+    "bf16_d512_E48_de128_L17": (512, 48, 128, "bf16", 17, 3, 0.9, 0.7, 104),    # second tile padded
+    "bf16_d1024_E64_de128_L1": (1024, 64, 128, "bf16", 1, 40, 0.887, 0.0, 105), # single-token GEMV
+    "bf16_d256_E128_de64_L3": (256, 128, 64, "bf16", 3, 9, 1.0, 0.6, 106),      # short chunk GEMV, E = 128
+    "f32_d128_E24_de32_L8": (128, 24, 32, "f32", 8, 6, 0.8, 0.7, 107),          # fp32 chunk -> GEMV
+}
+
+
+def _case(name):
+    d, E, de, dt, L, C, k, a, seed = CASES[name]
+    rng = np.random.default_rng(seed)
+    layer = make_layer(d, E, de, dt, k, rng)
+    tok = make_tokens(d, C, L, a, dt, rng)
+    return layer, tok.x, L
+
+
+def _compare_all(layer, x, L, gpu, name, check_stats=True):
+    E, dt = layer.n_experts, layer.dtype
+    z, g, m, um, cnt, lst = oracle_full(layer, x, L)
+    flipped, keep = check_route(gpu, z, g, m, E, dt)
+    nflip_u = check_union(gpu, um, z, E, L)
+    y_ref = oracle.forward_tokens(x, layer.w_in, layer.w_out, g, m)
+    rel = check_y(gpu["y"], y_ref, keep, dt, name)
+    if check_stats and not flipped:
+        st = oracle.stats(m, E, L)
+        for key in ("active_pairs", "union_sum", "reuse_num", "reuse_den"):
+            assert gpu["stats"][key] == st[key], key
+        np.testing.assert_array_equal(gpu["stats"]["hist"], st["hist"])
+    say(f"  {name}: max|dy|/rms {rel:.2e}, band flips {len(flipped)} tokens / {nflip_u} union bits")
+    return y_ref, keep
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_layer_parity(name):
+    layer, x, L = _case(name)
+    say(f"[gpu] layer parity {name} T={x.shape[0]}")
+    dl = B.DeviceLayer.from_workload(layer)
+    xd = B.tokens_to_device(x, dl.dtype)
+    gpu = run_gpu(dl, xd, L)
+    _compare_all(layer, x, L, gpu, name)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_every_mode_matches_oracle(name):
+    layer, x, L = _case(name)
+    dl = B.DeviceLayer.from_workload(layer)
+    xd = B.tokens_to_device(x, dl.dtype)
+    modes = ["gemv", "dense"]
+    if layer.dtype == "bf16" and layer.d % 128 == 0 and layer.d_expert % 128 == 0:
+        modes.append("chunk_mfma")
+    z, g, m, um, cnt, lst = oracle_full(layer, x, L)
+    y_ref = oracle.forward_dense(x, layer.w_in, layer.w_out, g)
+    for mode in modes:
+        say(f"[gpu] mode {mode} {name}")
+        gpu = run_gpu(dl, xd, L, mode=mode, stats=False)
+        flipped, keep = check_route(gpu, z, g, m, layer.n_experts, layer.dtype)
+        check_y(gpu["y"], y_ref, keep, layer.dtype, f"{name}/{mode}")
+
+
+def test_stacked_distinct_layers():
+    # chunk c must use layer c % n_layers: three different layers in one call
+    d, E, de, L, C = 512, 64, 128, 8, 9
+    rngs = [np.random.default_rng(200 + r) for r in range(3)]
+    layers = [make_layer(d, E, de, "bf16", 0.9, rg) for rg in rngs]
+    x = make_tokens(d, C, L, 0.8, "bf16", np.random.default_rng(210)).x
+    dl = B.DeviceLayer.from_workload(layers[0], replicas=3)
+    for r in (1, 2):
+        t = dl.tensors(r)
+        src = B.DeviceLayer.from_workload(layers[r]).tensors(0)
+        for key in ("w_router", "b_router", "w_in", "w_out"):
+            t[key].copy_(src[key])
+    xd = B.tokens_to_device(x, BF16)
+    for mode in ("auto", "gemv"):
+        say(f"[gpu] stacked layers mode {mode}")
+        gpu = run_gpu(dl, xd, L, mode=mode, n_layers=3)
+        for r in range(3):
+            chunks = np.arange(r, C, 3)
+            tok = (chunks[:, None] * L + np.arange(L)[None, :]).ravel()
+            ly = layers[r]
+            z, g, m = oracle.route(x[tok], ly.w_router, ly.b_router, None, ly.rms_eps)
+            flipped, keep = check_route(gpu, z, g, m, E, "bf16", t_idx=tok)
+            y_ref = oracle.forward_tokens(x[tok], ly.w_in, ly.w_out, g, m)
+            check_y(gpu["y"][tok], y_ref, keep, "bf16", f"stacked layer {r}/{mode}")
+
+
+def test_edge_cases_empty_none_and_all_active():
+    d, E, de, L = 512, 64, 128, 8
+    rng = np.random.default_rng(300)
+    layer = make_layer(d, E, de, "bf16", 0.9, rng)
+    x = make_tokens(d, 4, L, 0.8, "bf16", rng).x
+    dl = B.DeviceLayer.from_workload(layer)
+    # zero tokens: every entry point returns OK and enqueues nothing
+    say("[gpu] edge: zero tokens")
+    x0 = torch.empty((0, d), dtype=torch.bfloat16, device="cuda")
+    g0, m0, _ = B.blockffn_route(dl, x0, L)
+    _, c0, l0 = B.blockffn_chunk_union(E, m0, L)
+    y0 = B.blockffn_forward(dl, x0, L, g0, c0, l0)
+    torch.cuda.synchronize()
+    assert y0.shape == (0, d)
+    # no expert active anywhere: gates, masks, unions and outputs are exactly zero
+    for name, bias in (("none active", -1e4), ("all active", 1e4)):
+        say(f"[gpu] edge: {name}")
+        t = dl.tensors(0)
+        t["b_router"].fill_(bias)
+        layer.b_router = np.full(E, bias, np.float32)
+        xd = B.tokens_to_device(x, BF16)
+        for mode in ("auto", "gemv"):
+            gpu = run_gpu(dl, xd, L, mode=mode)
+            if bias < 0:
+                assert (gpu["mask"] == 0).all() and (gpu["g"] == 0).all()
+                assert (gpu["count"] == 0).all() and (gpu["list"] == -1).all()
+                assert (gpu["y"] == 0).all()
+                assert gpu["stats"]["active_pairs"] == 0 and gpu["stats"]["hist"][0] == x.shape[0]
+            else:
+                assert (gpu["count"] == E).all()
+                np.testing.assert_array_equal(gpu["list"], np.tile(np.arange(E), (4, 1)))
+            _compare_all(layer, x, L, gpu, f"{name}/{mode}")
+
+
+def test_union_and_stats_kernels_on_seeded_masks():
+    # masks straight from a seeded generator (not from the router), so the
+    # union and statistics kernels are compared bit for bit
+    rng = np.random.default_rng(400)
+    for E, L, C, p in ((8, 4, 16, 0.2), (64, 8, 512, 0.19), (70, 3, 33, 0.3), (128, 32, 20, 0.15),
+                       (128, 1, 100, 0.5), (1, 2, 7, 0.5)):
+        say(f"[gpu] union/stats E={E} L={L} C={C}")
+        T = L * C
+        act = rng.random((T, E)) < p
+        W = (E + 63) // 64
+        m = np.zeros((T, W), np.uint64)
+        for w in range(W):
+            for b in range(min(64, E - 64 * w)):
+                m[:, w] |= act[:, 64 * w + b].astype(np.uint64) << np.uint64(b)
+        md = torch.from_numpy(m.view(np.int64)).cuda()
+        um, cnt, lst = B.blockffn_chunk_union(E, md, L)
+        st = B.stats_dict(B.blockffn_sparsity_stats(E, md, L))
+        torch.cuda.synchronize()
+        o_um, o_cnt, o_lst = oracle.chunk_union(m, E, L)
+        np.testing.assert_array_equal(B.masks_to_u64(um), o_um)
+        np.testing.assert_array_equal(cnt.cpu().numpy(), o_cnt)
+        np.testing.assert_array_equal(lst.cpu().numpy(), o_lst)
+        o_st = oracle.stats(m, E, L)
+        for key in ("n_tokens", "n_chunks", "active_pairs", "union_sum", "reuse_num", "reuse_den"):
+            assert st[key] == o_st[key], key
+        np.testing.assert_array_equal(st["hist"], o_st["hist"])
+
+
+def test_tiny_fp32_config_full():
+    cfg = CONFIGS["tiny_f32_L4"]
+    layer, tok = make_workload(cfg)
+    say(f"[gpu] {cfg.name} full")
+    dl = B.DeviceLayer.from_workload(layer)
+    gpu = run_gpu(dl, B.tokens_to_device(tok.x, F32), cfg.chunk_len)
+    _compare_all(layer, tok.x, cfg.chunk_len, gpu, cfg.name)
+    # the oracle's dense evaluation agrees too (zero-gate experts add nothing)
+    z, g, m = oracle.route(tok.x, layer.w_router, layer.b_router, None, layer.rms_eps)
+    np.testing.assert_array_equal(oracle.forward_dense(tok.x, layer.w_in, layer.w_out, g),
+                                  oracle.forward_tokens(tok.x, layer.w_in, layer.w_out, g, m))
+
+
+@pytest.mark.parametrize("name", ["decode_L1_d2048_E64", "chunk8_d2048_E64", "large_L8_d4096_E128",
+                                  "large_L32_d4096_E128"])
+def test_full_size_sampled(name):
+    """Full workload in the benchmark's launch configuration (one layer copy
+    per chunk where it fits); the oracle checks every mask and the statistics,
+    and the outputs of a sample of chunks."""
+    cfg = CONFIGS[name]
+    layer, tok = make_workload(cfg)
+    L, E = cfg.chunk_len, cfg.n_experts
+    reps = cfg.replicas
+    say(f"[gpu] full size {name} T={cfg.n_tokens} replicas={reps}")
+    dl = B.DeviceLayer.from_workload(layer, replicas=reps)
+    xd = B.tokens_to_device(tok.x, dl.dtype)
+    gpu = run_gpu(dl, xd, L, n_layers=reps, want_preact=False)
+    del dl, xd
+    torch.cuda.empty_cache()
+    z, g, m, um, cnt, lst = oracle_full(layer, tok.x, L)
+    flipped, keep = check_route(gpu, z, g, m, E, cfg.dtype)
+    nflip_u = check_union(gpu, um, z, E, L)
+    if not flipped:
+        st = oracle.stats(m, E, L)
+        assert gpu["stats"]["union_sum"] == st["union_sum"]
+        assert gpu["stats"]["active_pairs"] == st["active_pairs"]
+    C = cfg.units
+    sample = np.unique(np.r_[np.linspace(0, C - 1, 6).astype(int), 1, C - 2])
+    if L == 1:
+        sample = np.unique(np.r_[np.linspace(0, C - 1, 48).astype(int)])
+    tok_idx = (sample[:, None] * L + np.arange(L)[None, :]).ravel()
+    y_ref = oracle.forward_tokens(tok.x[tok_idx], layer.w_in, layer.w_out, g[tok_idx], m[tok_idx])
+    rel = check_y(gpu["y"][tok_idx], y_ref, keep[tok_idx], cfg.dtype, name)
+    say(f"  {name}: sampled {len(sample)} units, max|dy|/rms {rel:.2e}, band flips {len(flipped)} tokens / "
+        f"{nflip_u} union bits, TLS {gpu['stats']['tls']:.4f} CLS {gpu['stats']['cls']:.4f}")

@@ -37,6 +37,12 @@ class WorkloadConfig:
     alpha: float      # chunk-base mixing weight (0 = independent tokens)
     seed: int
     mode: str = "auto"  # forward mode the workload exercises
+    # Distinct device copies of the layer used when the workload is timed:
+    # chunk c streams copy c % replicas, so no two chunks of one launch read
+    # the same weight bytes (a chunk passing through a deep stack of distinct
+    # layers).  1 for the batched workload, which runs every chunk through one
+    # layer on purpose.
+    replicas: int = 1
 
     @property
     def n_tokens(self) -> int:
@@ -70,18 +76,18 @@ CONFIGS: dict[str, WorkloadConfig] = {
         # Single-token decode: 4096 independent tokens, bandwidth-bound GEMV.
         WorkloadConfig("decode_L1_d2048_E64", d=2048, n_experts=64, d_expert=128,
                        dtype="bf16", chunk_len=1, units=4096, bias_k=_K_12_OF_64,
-                       alpha=0.0, seed=2),
+                       alpha=0.0, seed=2, replicas=520),
         # Speculative-verify chunk of 8 tokens, 512 chunks (about 19 of 64 experts per chunk).
         WorkloadConfig("chunk8_d2048_E64", d=2048, n_experts=64, d_expert=128,
                        dtype="bf16", chunk_len=8, units=512, bias_k=_K_12_OF_64,
-                       alpha=0.8, seed=3),
+                       alpha=0.8, seed=3, replicas=512),
         # Larger layer, chunks of 8 and of 32 tokens, 256 chunks each.
         WorkloadConfig("large_L8_d4096_E128", d=4096, n_experts=128, d_expert=128,
                        dtype="bf16", chunk_len=8, units=256, bias_k=_K_15PCT,
-                       alpha=0.647, seed=4),
+                       alpha=0.647, seed=4, replicas=256),
         WorkloadConfig("large_L32_d4096_E128", d=4096, n_experts=128, d_expert=128,
                        dtype="bf16", chunk_len=32, units=256, bias_k=_K_15PCT,
-                       alpha=0.647, seed=4),
+                       alpha=0.647, seed=4, replicas=256),
         # Prefill-like batch: 4096 tokens as 512 chunks of 8 through one layer,
         # token-expert pairs grouped by expert.
         WorkloadConfig("batched_L8_d4096_E128", d=4096, n_experts=128, d_expert=128,

@@ -89,7 +89,7 @@ hipError_t launch_forward_gemv(const LayerArgs& la, const void* x, int64_t n_tok
                                bool dense, float* hbuf, float* y, const StageEvents& se, hipStream_t s);
 hipError_t launch_forward_mfma(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len,
                                const float* gates, const int32_t* count, const int32_t* list, bool dense,
-                               uint16_t* hbuf, float* y, const StageEvents& se, hipStream_t s);
+                               uint16_t* hbuf, int64_t* plan, float* y, const StageEvents& se, hipStream_t s);
 
 bool route_uses_mfma(int d, int E, int chunk_len, int dtype);
 bool forward_mfma_supported(int d, int de, int dtype);

@@ -124,6 +124,15 @@ size_t hbuf_bytes(const blockffn_layer* ly, int64_t n_tokens, Path path) {
   return round256((size_t)n_tokens * (size_t)ly->n_experts * (size_t)ly->d_expert * elem);
 }
 
+// Work plan after the hidden buffer: one int64 per chunk plus a total.
+size_t plan_bytes(int64_t n_tokens, int32_t chunk_len) {
+  return round256(sizeof(int64_t) * (size_t)(n_tokens / chunk_len + 1));
+}
+
+size_t workspace_bytes_for(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, Path path) {
+  return hbuf_bytes(ly, n_tokens, path) + plan_bytes(n_tokens, chunk_len);
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(BLOCKFFN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return BLOCKFFN_OK;
@@ -166,7 +175,7 @@ BFFN_EXPORT size_t blockffn_workspace_size(const blockffn_layer* layer, int64_t 
   Path path;
   bool dense;
   if (resolve_mode(layer, chunk_len, mode, &path, &dense) != BLOCKFFN_OK) return 0;
-  return hbuf_bytes(layer, n_tokens, path);
+  return workspace_bytes_for(layer, n_tokens, chunk_len, path);
 }
 
 BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
@@ -185,7 +194,7 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, 
   if (!aligned(x, 16) || !aligned(gates, 4) || !aligned(y, 16) || !aligned(active_count, 4) ||
       !aligned(active_list, 4))
     return fail(BLOCKFFN_ERR_ALIGN, "x and y must be 16-byte aligned, gates/count/list 4-byte aligned");
-  const size_t need = hbuf_bytes(layer, n_tokens, path);
+  const size_t need = workspace_bytes_for(layer, n_tokens, chunk_len, path);
   if (need > 0 && !workspace) return fail(BLOCKFFN_ERR_NULL, "workspace is NULL (need %zu bytes)", need);
   if (!aligned(workspace, 256)) return fail(BLOCKFFN_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (workspace_bytes < need)
@@ -193,8 +202,11 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, 
   const bffn::LayerArgs la = layer_args(layer, n_layers);
   hipError_t e;
   if (path == Path::kMfma)
-    e = bffn::launch_forward_mfma(la, static_cast<const uint16_t*>(x), n_tokens, chunk_len, gates, active_count,
-                                  active_list, dense, static_cast<uint16_t*>(workspace), y, g_stage_events, stream);
+    e = bffn::launch_forward_mfma(
+        la, static_cast<const uint16_t*>(x), n_tokens, chunk_len, gates, active_count, active_list, dense,
+        static_cast<uint16_t*>(workspace),
+        reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + hbuf_bytes(layer, n_tokens, path)), y,
+        g_stage_events, stream);
   else
     e = bffn::launch_forward_gemv(la, x, n_tokens, chunk_len, layer->dtype, gates, active_count, active_list, dense,
                                   static_cast<float*>(workspace), y, g_stage_events, stream);

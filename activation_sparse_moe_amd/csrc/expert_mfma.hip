@@ -34,27 +34,61 @@ struct Step {
 
 // A rows: a_row0 points at element 32 g of row m of stripe 0; stripes are
 // `a_stripe` elements apart.  B: b_row[tl] points at element 32 g of token
-// m + 16 tl's row (nullptr past L).
+// m + 16 tl's row.  Lanes of tokens past L read a valid row of the chunk
+// instead (MFMA output columns are independent and those columns are never
+// stored), which keeps the pipelined loop free of branches so the compiler
+// can wait for exactly one step's loads.
+#ifndef BFFN_LANE_CONTIG
+#define BFFN_LANE_CONTIG 0
+#endif
+#ifndef BFFN_NT_LOADS
+#define BFFN_NT_LOADS 0
+#endif
+#ifndef BFFN_SCHED_FENCE
+#define BFFN_SCHED_FENCE 1
+#endif
+
+
+__device__ __forceinline__ u32x4 load_weights(const u32x4* p) {
+#if BFFN_NT_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+// Element offset, within a 128-element step, of the 8 k's lane group g feeds
+// to MFMA q.
+__device__ __forceinline__ int kofs(int g, int q) {
+#if BFFN_LANE_CONTIG
+  return g * 32 + q * 8;
+#else
+  return q * 32 + g * 8;
+#endif
+}
+
 template <int NT>
 __device__ __forceinline__ void load_step(Step<NT>& st, const uint16_t* a_row0, int64_t a_stripe,
-                                          const uint16_t* const (&b_row)[NT], int k0) {
+                                          const uint16_t* const (&b_row)[NT], int k0, int g) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(a_row0 + s * a_stripe + k0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st.a[s][q] = p[q];
+    for (int q = 0; q < 4; ++q)
+      st.a[s][q] = load_weights(reinterpret_cast<const u32x4*>(a_row0 + s * a_stripe + k0 + kofs(g, q)));
   }
 #pragma unroll
   for (int tl = 0; tl < NT; ++tl) {
-    if (b_row[tl] != nullptr) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(b_row[tl] + k0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) st.b[tl][q] = p[q];
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) st.b[tl][q] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int q = 0; q < 4; ++q) st.b[tl][q] = *reinterpret_cast<const u32x4*>(b_row[tl] + k0 + kofs(g, q));
   }
+}
+
+// Keeps the compiler's scheduler from moving instructions across this point,
+// so a step's loads stay issued ahead of the previous step's MFMAs.
+__device__ __forceinline__ void fence_schedule() {
+#if BFFN_SCHED_FENCE
+  __builtin_amdgcn_sched_barrier(0);
+#endif
 }
 
 template <int NT>
@@ -69,48 +103,49 @@ __device__ __forceinline__ void mfma_step(f32x4 (&acc)[4][NT], const Step<NT>& s
                                                              acc[s][tl], 0, 0, 0);
 }
 
+// One up-projection item: 64 rows (block rb) of the expert in `slot` of
+// chunk `unit`, over all of d, for every token of the chunk.
 template <int NT>
-__global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
-                                                         int64_t n_units, int L, const float* __restrict__ gates,
-                                                         const int32_t* __restrict__ count,
-                                                         const int32_t* __restrict__ list, int dense,
-                                                         int64_t blocks_per_unit, uint16_t* __restrict__ hbuf) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ void up_item(const LayerArgs& la, const uint16_t* __restrict__ x, int L,
+                                        const float* __restrict__ gates, int64_t unit, int slot, int rb, int i,
+                                        uint16_t* __restrict__ hbuf) {
+  const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
-  const int64_t lb = xcd_logical_block(blockIdx.x, n_units * blocks_per_unit);
-  if (lb < 0) return;
-  const int64_t unit = lb / blocks_per_unit;
-  const int wave_in_unit = (int)(lb % blocks_per_unit) * 4 + w;
   const int d = la.d, de = la.de, E = la.E;
-  const int rbs = de >> 6;
-  const int slot = wave_in_unit / rbs, rb = wave_in_unit % rbs;
-  const int n_active = dense ? E : count[unit];
-  if (slot >= n_active) return;
-  const int i = dense ? slot : list[unit * E + slot];
   const uint16_t* wi = layer_ptr(static_cast<const uint16_t*>(la.w_in), la.stride, unit, la.n_layers);
-  const uint16_t* a_row0 = wi + ((int64_t)i * de + rb * 64 + m) * d + g * 32;
+  const uint16_t* a_row0 = wi + ((int64_t)i * de + rb * 64 + m) * d;
   const int64_t a_stripe = 16 * (int64_t)d;
   const int64_t t0 = unit * L;
   const uint16_t* b_row[NT];
 #pragma unroll
-  for (int tl = 0; tl < NT; ++tl) {
-    const int n = m + 16 * tl;
-    b_row[tl] = n < L ? x + (t0 + n) * d + g * 32 : nullptr;
-  }
+  for (int tl = 0; tl < NT; ++tl) b_row[tl] = x + (t0 + (m + 16 * tl) % L) * d;
   f32x4 acc[4][NT];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int tl = 0; tl < NT; ++tl) acc[s][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Two-deep software pipeline over the d / 128 steps, tail peeled.
+  const int nsteps = d >> 7;
   Step<NT> s0, s1;
-  load_step<NT>(s0, a_row0, a_stripe, b_row, 0);
-  for (int k0 = 0; k0 < d; k0 += 256) {
-    if (k0 + 128 < d) load_step<NT>(s1, a_row0, a_stripe, b_row, k0 + 128);
+  load_step<NT>(s0, a_row0, a_stripe, b_row, 0, g);
+  int k = 0;
+  for (; k + 2 < nsteps; k += 2) {
+    load_step<NT>(s1, a_row0, a_stripe, b_row, (k + 1) << 7, g);
+    fence_schedule();
     mfma_step<NT>(acc, s0);
-    if (k0 + 128 >= d) break;
-    if (k0 + 256 < d) load_step<NT>(s0, a_row0, a_stripe, b_row, k0 + 256);
+    fence_schedule();
+    load_step<NT>(s0, a_row0, a_stripe, b_row, (k + 2) << 7, g);
+    fence_schedule();
     mfma_step<NT>(acc, s1);
+    fence_schedule();
+  }
+  if (k + 1 < nsteps) {
+    load_step<NT>(s1, a_row0, a_stripe, b_row, (k + 1) << 7, g);
+    mfma_step<NT>(acc, s0);
+    mfma_step<NT>(acc, s1);
+  } else {
+    mfma_step<NT>(acc, s0);
   }
 
   // D layout: lane (m, g) holds rows 4 g + r (r < 4), column m of each tile.
@@ -127,6 +162,60 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
       const uint32_t hi = f32_to_bf16(gv * swish(v[2])) | (f32_to_bf16(gv * swish(v[3])) << 16);
       *reinterpret_cast<u32x2*>(hrow + s * 16) = u32x2{lo, hi};
     }
+  }
+}
+
+// Exclusive prefix over chunks of the up-projection item counts
+// (union size x row blocks, or E x row blocks in dense mode):
+// prefix[u] = items of chunks < u, prefix[n_units] = total.  One block.
+__global__ __launch_bounds__(1024) void plan_items_kernel(const int32_t* __restrict__ count, int64_t n_units,
+                                                          int dense_E, int per_slot, int64_t* __restrict__ prefix) {
+  __shared__ int64_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (n_units + 1023) / 1024;
+  const int64_t b = tid * per, e = b + per < n_units ? b + per : n_units;
+  int64_t sum = 0;
+  for (int64_t u = b; u < e; ++u) sum += dense_E ? dense_E : count[u];
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int64_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int64_t run = part[tid] - sum;
+  for (int64_t u = b; u < e; ++u) {
+    prefix[u] = run * per_slot;
+    run += dense_E ? dense_E : count[u];
+  }
+  if (tid == 1023) prefix[n_units] = part[1023] * per_slot;
+}
+
+// Persistent up-projection: a fixed grid sized to the resident capacity; wave
+// gw takes items gw, gw + W, gw + 2W, ... of the chunk-major item list, so
+// every wave streams weights and no block is spent on inactive slots.
+template <int NT>
+__global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
+                                                         int64_t n_units, int L, const float* __restrict__ gates,
+                                                         const int32_t* __restrict__ list, int dense,
+                                                         const int64_t* __restrict__ prefix,
+                                                         uint16_t* __restrict__ hbuf) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int rbs = la.de >> 6;
+  const int64_t total = prefix[n_units];
+  for (int64_t item = (int64_t)blockIdx.x * 4 + w; item < total; item += nwaves) {
+    int64_t lo = 0, hi = n_units - 1;  // last chunk whose prefix <= item
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (prefix[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int64_t unit = lo;
+    const int r = (int)(item - prefix[unit]);
+    const int slot = r / rbs, rb = r % rbs;
+    const int i = dense ? slot : list[unit * la.E + slot];
+    up_item<NT>(la, x, L, gates, unit, slot, rb, i, hbuf);
   }
 }
 
@@ -163,24 +252,36 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   auto load = [&](Step<NT>& st, int p) {
     const int slot = p / spe, j0 = (p % spe) * 128;
     const int i = dense ? slot : list[unit * E + slot];
-    const uint16_t* a_row0 = wo + ((int64_t)i * d + kb + m) * de + g * 32;
+    const uint16_t* a_row0 = wo + ((int64_t)i * d + kb + m) * de;
     const uint16_t* b_row[NT];
 #pragma unroll
-    for (int tl = 0; tl < NT; ++tl) {
-      const int n = m + 16 * tl;
-      b_row[tl] = n < L ? hbuf + ((unit * E + slot) * L + n) * (int64_t)de + g * 32 : nullptr;
-    }
-    load_step<NT>(st, a_row0, a_stripe, b_row, j0);
+    for (int tl = 0; tl < NT; ++tl)
+      b_row[tl] = hbuf + ((unit * E + slot) * L + (m + 16 * tl) % L) * (int64_t)de;
+    load_step<NT>(st, a_row0, a_stripe, b_row, j0, g);
   };
 
+  // Two-deep software pipeline over the union's steps, tail peeled.
   Step<NT> s0, s1;
-  if (n_steps > 0) load(s0, 0);
-  for (int p = 0; p < n_steps; p += 2) {
-    if (p + 1 < n_steps) load(s1, p + 1);
-    mfma_step<NT>(acc, s0);
-    if (p + 1 >= n_steps) break;
-    if (p + 2 < n_steps) load(s0, p + 2);
-    mfma_step<NT>(acc, s1);
+  if (n_steps > 0) {
+    load(s0, 0);
+    int p = 0;
+    for (; p + 2 < n_steps; p += 2) {
+      load(s1, p + 1);
+      fence_schedule();
+      mfma_step<NT>(acc, s0);
+      fence_schedule();
+      load(s0, p + 2);
+      fence_schedule();
+      mfma_step<NT>(acc, s1);
+      fence_schedule();
+    }
+    if (p + 1 < n_steps) {
+      load(s1, p + 1);
+      mfma_step<NT>(acc, s0);
+      mfma_step<NT>(acc, s1);
+    } else {
+      mfma_step<NT>(acc, s0);
+    }
   }
 
 #pragma unroll
@@ -195,15 +296,24 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
 
 template <int NT>
 hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int L, const float* gates,
-                     const int32_t* count, const int32_t* list, bool dense, uint16_t* hbuf, float* y,
-                     const StageEvents& se, hipStream_t s) {
+                     const int32_t* count, const int32_t* list, bool dense, uint16_t* hbuf, int64_t* plan,
+                     float* y, const StageEvents& se, hipStream_t s) {
+  const int rbs = la.de >> 6;
+  plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, dense ? la.E : 0, rbs, plan);
   se.record(0, s);
   {
-    const int waves = la.E * (la.de >> 6);
-    const int64_t bpu = (waves + 3) / 4;
-    const int64_t nlog = units * bpu;
-    up_mfma_kernel<NT><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(la, x, units, L, gates, count, list,
-                                                                                dense ? 1 : 0, bpu, hbuf);
+    // resident capacity: blocks per CU at this kernel's register use, times CUs
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, up_mfma_kernel<NT>, kBlock, 0);
+    if (e != hipSuccess) return e;
+    const int64_t max_items = units * la.E * rbs;
+    int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    const int64_t need = (max_items + 3) / 4;
+    if (grid > need) grid = need;
+    up_mfma_kernel<NT><<<dim3((unsigned)grid), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list, dense ? 1 : 0,
+                                                                      plan, hbuf);
   }
   se.record(1, s);
   {
@@ -225,11 +335,11 @@ bool forward_mfma_supported(int d, int de, int dtype) {
 
 hipError_t launch_forward_mfma(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len,
                                const float* gates, const int32_t* count, const int32_t* list, bool dense,
-                               uint16_t* hbuf, float* y, const StageEvents& se, hipStream_t s) {
+                               uint16_t* hbuf, int64_t* plan, float* y, const StageEvents& se, hipStream_t s) {
   const int64_t units = n_tokens / chunk_len;
   if (units == 0) return hipSuccess;
-  if (chunk_len <= 16) return launch_nt<1>(la, x, units, chunk_len, gates, count, list, dense, hbuf, y, se, s);
-  return launch_nt<2>(la, x, units, chunk_len, gates, count, list, dense, hbuf, y, se, s);
+  if (chunk_len <= 16) return launch_nt<1>(la, x, units, chunk_len, gates, count, list, dense, hbuf, plan, y, se, s);
+  return launch_nt<2>(la, x, units, chunk_len, gates, count, list, dense, hbuf, plan, y, se, s);
 }
 
 }  // namespace bffn

@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the BlockFFN layer forward on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic
+input: router (ReLU + RMSNorm) -> chunk union -> expert forward over each
+chunk's union -> sparsity statistics, all through the C ABI.  The default
+workload is the speculative-verify chunk of 8 tokens: d = 2048, E = 64
+experts of 2048 -> 128 -> 2048, bf16, 512 chunks (4096 tokens), every chunk
+streaming its own copy of the layer so that no weight byte is served from a
+cache.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "chunk-8 BlockFFN layer tokens/s + active-weight HBM GB/s (% of peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "chunk8_d2048_E64"
+CSRC = os.path.join(ROOT, "activation_sparse_moe_amd", "csrc")
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--mode", default=None, help="forward mode (default: the workload's)")
+    p.add_argument("--dense-steps", type=int, default=5, help="steps of the dense all-experts comparison (0: skip)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
+    return p.parse_args(argv)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class StepRunner:
+    """Holds the device buffers of one workload and runs steps on the current stream."""
+
+    def __init__(self, cfg, mode: str):
+        import numpy as np
+        import torch
+        from activation_sparse_moe_amd import binding as B
+        from workload import make_workload
+
+        self.B, self.torch, self.np = B, torch, np
+        self.cfg, self.mode = cfg, mode
+        t = time.time()
+        self.layer, tok = make_workload(cfg)
+        self.x_host = tok.x
+        self.gen_s = time.time() - t
+        self.dl = B.DeviceLayer.from_workload(self.layer, replicas=cfg.replicas)
+        self.xd = B.tokens_to_device(tok.x, self.dl.dtype)
+        T, E, L = cfg.n_tokens, cfg.n_experts, cfg.chunk_len
+        dev = self.xd.device
+        self.gates = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.masks = torch.empty((T, self.dl.mask_words), dtype=torch.int64, device=dev)
+        C = T // L
+        self.umask = torch.empty((C, self.dl.mask_words), dtype=torch.int64, device=dev)
+        self.count = torch.empty((C,), dtype=torch.int32, device=dev)
+        self.lst = torch.empty((C, E), dtype=torch.int32, device=dev)
+        self.y = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
+        self.stats = torch.empty((8 + 129,), dtype=torch.int64, device=dev)
+        self.ws = {}
+        for m in {mode, "dense"}:
+            self.ws[m] = B.alloc_workspace(self.dl, T, L, m)
+        self.lib = B.load()
+
+    def step(self, mode: str, ev=None, stage_events=None):
+        """route -> union -> forward -> stats.  ev: 4 torch events recorded
+        after route, union, forward and stats; stage_events: ctypes array of 3
+        hipEvent_t recorded by the library around the forward's two kernels."""
+        B, cfg = self.B, self.cfg
+        L, E = cfg.chunk_len, cfg.n_experts
+        B.blockffn_route(self.dl, self.xd, L, gates=self.gates, token_masks=self.masks)
+        if ev is not None:
+            ev[0].record()
+        B.blockffn_chunk_union(E, self.masks, L, chunk_masks=self.umask, active_count=self.count,
+                               active_list=self.lst)
+        if ev is not None:
+            ev[1].record()
+        if stage_events is not None:
+            self.lib.blockffn_set_stage_events(ctypes.cast(stage_events, ctypes.c_void_p), 3)
+        B.blockffn_forward(self.dl, self.xd, L, self.gates, self.count, self.lst, mode=mode,
+                           workspace=self.ws[mode], y=self.y)
+        if stage_events is not None:
+            self.lib.blockffn_set_stage_events(None, 0)
+        if ev is not None:
+            ev[2].record()
+        B.blockffn_sparsity_stats(E, self.masks, L, stats_dev=self.stats)
+        if ev is not None:
+            ev[3].record()
+
+    def timed(self, mode: str, steps: int, warmup: int):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(mode)
+        torch.cuda.synchronize()
+        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        evs = [[E() for _ in range(4)] for _ in range(steps)]
+        stage = [[E() for _ in range(3)] for _ in range(steps)]
+        # record every event once so that its hipEvent exists before the
+        # library is handed the raw handles
+        for row in stage:
+            for e in row:
+                e.record()
+        torch.cuda.synchronize()
+        handles = [(ctypes.c_void_p * 3)(*[e.cuda_event for e in row]) for row in stage]
+        start, end = E(), E()
+        torch.cuda.synchronize()
+        start.record()
+        prev = start
+        starts = []
+        for k in range(steps):
+            starts.append(prev)
+            self.step(mode, ev=evs[k], stage_events=handles[k])
+            prev = evs[k][3]
+        end.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+        per = {"route": [], "union": [], "up": [], "down": [], "stats": [], "forward": []}
+        for k in range(steps):
+            s0 = starts[k]
+            per["route"].append(s0.elapsed_time(evs[k][0]))
+            per["union"].append(evs[k][0].elapsed_time(evs[k][1]))
+            per["up"].append(stage[k][0].elapsed_time(stage[k][1]))
+            per["down"].append(stage[k][1].elapsed_time(stage[k][2]))
+            per["forward"].append(evs[k][1].elapsed_time(evs[k][2]))
+            per["stats"].append(evs[k][2].elapsed_time(evs[k][3]))
+        avg = {k: sum(v) / len(v) for k, v in per.items()}
+        return total_ms / steps, avg
+
+    def byte_model(self):
+        """Algorithmic bytes per launch of each kernel (what the method must
+        move: the router, only the union's expert rows, x, gates, hidden
+        activations, y)."""
+        np, cfg = self.np, self.cfg
+        cnt = self.count.cpu().numpy().astype(np.int64)
+        es = 2 if cfg.dtype == "bf16" else 4
+        d, E, de, L, T = cfg.d, cfg.n_experts, cfg.d_expert, cfg.chunk_len, cfg.n_tokens
+        C = T // L
+        W = (E + 63) // 64
+        U = int(cnt.sum())
+        hid = 2 if self.mode in ("auto", "chunk_mfma") and cfg.dtype == "bf16" and L >= 8 else 4
+        b = {
+            "route": C * (E * d * es + E * 4) + T * d * es + T * E * 4 + T * W * 8,
+            "union": T * W * 8 + C * (W * 8 + 4 + E * 4),
+            "up": U * de * d * es + T * d * es + U * L * 4 + U * L * de * hid,
+            "down": U * d * de * es + U * L * de * hid + T * d * 4,
+            "stats": T * W * 8,
+        }
+        active_weight = C * E * d * es + U * 2 * d * de * es
+        step_alg = C * E * d * es + U * 2 * d * de * es + T * d * es + T * d * 4
+        return b, U, active_weight, step_alg
+
+def cpu_baseline(cfg, layer, x_host, target_s: float):
+    """The oracle as it stands, on the host cores, on a bounded sample of chunks."""
+    import oracle
+    L = cfg.chunk_len
+    C = cfg.n_tokens // L
+
+    def run(n_chunks):
+        x = x_host[: n_chunks * L]
+        t = time.perf_counter()
+        z, g, m = oracle.route(x, layer.w_router, layer.b_router, layer.rms_scale, layer.rms_eps)
+        oracle.chunk_union(m, layer.n_experts, L)
+        oracle.forward_tokens(x, layer.w_in, layer.w_out, g, m)
+        oracle.stats(m, layer.n_experts, L)
+        return time.perf_counter() - t
+
+    n = max(1, min(C, 8 if L > 1 else 64))
+    dt = run(n)
+    if dt < target_s and n < C:
+        n = int(min(C, max(n + 1, n * target_s / max(dt, 1e-3))))
+        dt = run(n)
+    return {"value": round(n * L / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {C} chunks ({n * L} tokens) of this workload, layer copy 0: route + union + "
+                      f"per-token forward + stats, fp64 C oracle, {dt:.1f} s"}
+
+
+def copy_calibration():
+    """A plain device copy of 1 GiB: its FETCH_SIZE / WRITE_SIZE counters
+    scale the expert kernels' counters to bytes."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from workload import get_config
+
+    cfg = get_config(args.workload)
+    mode = args.mode or cfg.mode
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+    runner = StepRunner(cfg, mode)
+    ms, avg = runner.timed(mode, args.steps, args.warmup)
+    from activation_sparse_moe_amd import binding as B
+    st = B.stats_dict(runner.stats)
+    bytes_per, U, active_weight, step_alg = runner.byte_model()
+    T = cfg.n_tokens
+    value = T / (ms / 1e3)
+
+    dense = None
+    if args.dense_steps > 0:
+        dms, davg = runner.timed("dense", args.dense_steps, 1)
+        dense = {"ms_per_step": round(dms, 4), "forward_ms": round(davg["forward"], 4),
+                 "speedup_step": round(dms / ms, 3), "speedup_forward": round(davg["forward"] / avg["forward"], 3)}
+
+    dom = "up" if avg["up"] >= avg["down"] else "down"
+    kernel_name = {"up": "expert_up", "down": "expert_down"}[dom]
+    achieved = bytes_per[dom] / (avg[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": f"{kernel_name} ({mode})", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": profiled_traffic(kernel_name, cfg.name),
+                "algorithmic_bytes_per_launch": bytes_per[dom], "avg_launch_ms": round(avg[dom], 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, runner.layer, runner.x_host, args.cpu_seconds)
+
+    step_gbs = step_alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded generator shaped to the pages' sparsity)",
+        "config": {"workload": cfg.name, "d": cfg.d, "n_experts": cfg.n_experts, "d_expert": cfg.d_expert,
+                   "chunk_len": cfg.chunk_len, "chunks": T // cfg.chunk_len, "tokens": T,
+                   "layer_copies": cfg.replicas, "mode": mode},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "active_weight_gbs": round(step_gbs, 1),
+        "active_weight_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+        "kernel_ms": {k: round(v, 5) for k, v in avg.items()},
+        "kernel_gbs": {k: round(bytes_per[k] / (avg[k] * 1e-3) / 1e9, 1) for k in bytes_per},
+        "dense": dense,
+        "sparsity": {"tls": round(st["tls"], 4), "cls": round(st["cls"], 4), "mean_union": round(U / (T // cfg.chunk_len), 2),
+                     "reuse": round(st["reuse"], 4)},
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -180,8 +180,11 @@ def test_forward_rejects_bad_arguments(lib):
 def test_workspace_size(lib):
     lay = _layer(d=2048, n_experts=64, d_expert=128)
     T = 4096
-    # chunk path (bf16 hidden activations) and GEMV path (fp32)
-    assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, _capi.MODE_CHUNK_MFMA) == T * 64 * 128 * 2
-    assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 1, _capi.MODE_AUTO) == T * 64 * 128 * 4
+    r256 = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    # hidden activations (bf16 on the chunk path, fp32 on the GEMV path) + one int64 plan entry per chunk
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, _capi.MODE_CHUNK_MFMA) == \
+        T * 64 * 128 * 2 + r256(8 * (T // 8 + 1))
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 1, _capi.MODE_AUTO) == \
+        T * 64 * 128 * 4 + r256(8 * (T + 1))
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 3, _capi.MODE_AUTO) == 0   # ragged
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, 99) == 0

@@ -52,11 +52,11 @@ struct Vec16<uint16_t> {
 // Rows are split over lane groups of `lpr` lanes (a power of two); a group
 // covers its row with `nv` 16-byte vectors per lane.  Four rows per group are
 // in flight per iteration.
-template <typename T>
+template <typename T, bool DENSE>
 __global__ __launch_bounds__(kBlock) void up_valu_kernel(LayerArgs la, const T* __restrict__ x, int64_t n_units,
                                                          int L, const float* __restrict__ gates,
                                                          const int32_t* __restrict__ count,
-                                                         const int32_t* __restrict__ list, int dense,
+                                                         const int32_t* __restrict__ list,
                                                          int rows_per_wave, int lpr, int nv,
                                                          int64_t blocks_per_unit, float* __restrict__ hbuf) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -67,9 +67,9 @@ __global__ __launch_bounds__(kBlock) void up_valu_kernel(LayerArgs la, const T* 
   const int de = la.de, d = la.d, E = la.E;
   const int rbs = de / rows_per_wave;
   const int slot = wave_in_unit / rbs, rb = wave_in_unit % rbs;
-  const int n_active = dense ? E : count[unit];
+  const int n_active = DENSE ? E : count[unit];
   if (slot >= n_active) return;
-  const int i = dense ? slot : list[unit * E + slot];
+  const int i = DENSE ? slot : list[unit * E + slot];
   const T* wi = layer_ptr(static_cast<const T*>(la.w_in), la.stride, unit, la.n_layers) + (int64_t)i * de * d;
   constexpr int VEC = Vec16<T>::kElems;
   const int rpp = 64 / lpr, lg = lane / lpr, li = lane % lpr;
@@ -103,10 +103,10 @@ __global__ __launch_bounds__(kBlock) void up_valu_kernel(LayerArgs la, const T* 
   }
 }
 
-template <typename T>
+template <typename T, bool DENSE>
 __global__ __launch_bounds__(kBlock) void down_valu_kernel(LayerArgs la, int64_t n_units, int L,
                                                            const int32_t* __restrict__ count,
-                                                           const int32_t* __restrict__ list, int dense,
+                                                           const int32_t* __restrict__ list,
                                                            int rows_per_wave, int lpr, int nv,
                                                            int64_t blocks_per_unit, const float* __restrict__ hbuf,
                                                            float* __restrict__ y) {
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kBlock) void down_valu_kernel(LayerArgs la, int64_t
   const int k0 = wave_in_unit * rows_per_wave;
   if (k0 >= d) return;
   const int k_end = min(d, k0 + rows_per_wave);
-  const int n_active = dense ? E : count[unit];
+  const int n_active = DENSE ? E : count[unit];
   const T* wo_base = layer_ptr(static_cast<const T*>(la.w_out), la.stride, unit, la.n_layers);
   constexpr int VEC = Vec16<T>::kElems;
   const int rpp = 64 / lpr, lg = lane / lpr, li = lane % lpr;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kBlock) void down_valu_kernel(LayerArgs la, int64_t
     for (int r0 = k0; r0 < k_end; r0 += 4 * rpp) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
       for (int s = 0; s < n_active; ++s) {
-        const int i = dense ? s : list[unit * E + s];
+        const int i = DENSE ? s : list[unit * E + s];
         const T* wo = wo_base + (int64_t)i * d * de;
         const float* hrow = hbuf + ((unit * E + s) * L + n) * (int64_t)de;
         for (int mm = 0; mm < nv; ++mm) {
@@ -162,9 +162,9 @@ void lane_split(int len, int vec, int* lpr, int* nv) {
   *nv = nvec / l;
 }
 
-template <typename T>
+template <typename T, bool DENSE>
 hipError_t launch_gemv_typed(const LayerArgs& la, const T* x, int64_t units, int L, const float* gates,
-                             const int32_t* count, const int32_t* list, bool dense, float* hbuf, float* y,
+                             const int32_t* count, const int32_t* list, float* hbuf, float* y,
                              const StageEvents& se, hipStream_t s) {
   constexpr int VEC = Vec16<T>::kElems;
   se.record(0, s);
@@ -176,8 +176,8 @@ hipError_t launch_gemv_typed(const LayerArgs& la, const T* x, int64_t units, int
     int lpr, nv;
     lane_split(la.d, VEC, &lpr, &nv);
     const int64_t nlog = units * bpu;
-    up_valu_kernel<T><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(
-        la, x, units, L, gates, count, list, dense ? 1 : 0, rows, lpr, nv, bpu, hbuf);
+    up_valu_kernel<T, DENSE><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(
+        la, x, units, L, gates, count, list, rows, lpr, nv, bpu, hbuf);
   }
   se.record(1, s);
   // down: one wave per 64 output rows
@@ -188,8 +188,8 @@ hipError_t launch_gemv_typed(const LayerArgs& la, const T* x, int64_t units, int
     int lpr, nv;
     lane_split(la.de, VEC, &lpr, &nv);
     const int64_t nlog = units * bpu;
-    down_valu_kernel<T><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(
-        la, units, L, count, list, dense ? 1 : 0, rows, lpr, nv, bpu, hbuf, y);
+    down_valu_kernel<T, DENSE><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(
+        la, units, L, count, list, rows, lpr, nv, bpu, hbuf, y);
   }
   se.record(2, s);
   return hipGetLastError();
@@ -202,11 +202,13 @@ hipError_t launch_forward_gemv(const LayerArgs& la, const void* x, int64_t n_tok
                                float* hbuf, float* y, const StageEvents& se, hipStream_t s) {
   const int64_t units = n_tokens / chunk_len;
   if (units == 0) return hipSuccess;
+  const float* xf = static_cast<const float*>(x);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
   if (dtype == BLOCKFFN_F32)
-    return launch_gemv_typed<float>(la, static_cast<const float*>(x), units, chunk_len, gates, count, list, dense,
-                                    hbuf, y, se, s);
-  return launch_gemv_typed<uint16_t>(la, static_cast<const uint16_t*>(x), units, chunk_len, gates, count, list,
-                                     dense, hbuf, y, se, s);
+    return dense ? launch_gemv_typed<float, true>(la, xf, units, chunk_len, gates, count, list, hbuf, y, se, s)
+                 : launch_gemv_typed<float, false>(la, xf, units, chunk_len, gates, count, list, hbuf, y, se, s);
+  return dense ? launch_gemv_typed<uint16_t, true>(la, xb, units, chunk_len, gates, count, list, hbuf, y, se, s)
+               : launch_gemv_typed<uint16_t, false>(la, xb, units, chunk_len, gates, count, list, hbuf, y, se, s);
 }
 
 }  // namespace bffn

@@ -195,10 +195,10 @@ __global__ __launch_bounds__(1024) void plan_items_kernel(const int32_t* __restr
 // Persistent up-projection: a fixed grid sized to the resident capacity; wave
 // gw takes items gw, gw + W, gw + 2W, ... of the chunk-major item list, so
 // every wave streams weights and no block is spent on inactive slots.
-template <int NT>
+template <int NT, bool DENSE>
 __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
                                                          int64_t n_units, int L, const float* __restrict__ gates,
-                                                         const int32_t* __restrict__ list, int dense,
+                                                         const int32_t* __restrict__ list,
                                                          const int64_t* __restrict__ prefix,
                                                          uint16_t* __restrict__ hbuf) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -214,15 +214,15 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
     const int64_t unit = lo;
     const int r = (int)(item - prefix[unit]);
     const int slot = r / rbs, rb = r % rbs;
-    const int i = dense ? slot : list[unit * la.E + slot];
+    const int i = DENSE ? slot : list[unit * la.E + slot];
     up_item<NT>(la, x, L, gates, unit, slot, rb, i, hbuf);
   }
 }
 
-template <int NT>
+template <int NT, bool DENSE>
 __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t n_units, int L,
                                                            const int32_t* __restrict__ count,
-                                                           const int32_t* __restrict__ list, int dense,
+                                                           const int32_t* __restrict__ list,
                                                            int64_t blocks_per_unit,
                                                            const uint16_t* __restrict__ hbuf,
                                                            float* __restrict__ y) {
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   const int d = la.d, de = la.de, E = la.E;
   const int kb = wave_in_unit * 64;
   if (kb >= d) return;
-  const int n_active = dense ? E : count[unit];
+  const int n_active = DENSE ? E : count[unit];
   const uint16_t* wo = layer_ptr(static_cast<const uint16_t*>(la.w_out), la.stride, unit, la.n_layers);
   const int64_t a_stripe = 16 * (int64_t)de;
   const int64_t t0 = unit * L;
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   // Step p covers slot p / spe, elements [128 (p % spe), +128) of that expert.
   auto load = [&](Step<NT>& st, int p) {
     const int slot = p / spe, j0 = (p % spe) * 128;
-    const int i = dense ? slot : list[unit * E + slot];
+    const int i = DENSE ? slot : list[unit * E + slot];
     const uint16_t* a_row0 = wo + ((int64_t)i * d + kb + m) * de;
     const uint16_t* b_row[NT];
 #pragma unroll
@@ -294,34 +294,35 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   }
 }
 
-template <int NT>
+template <int NT, bool DENSE>
 hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int L, const float* gates,
-                     const int32_t* count, const int32_t* list, bool dense, uint16_t* hbuf, int64_t* plan,
-                     float* y, const StageEvents& se, hipStream_t s) {
+                     const int32_t* count, const int32_t* list, uint16_t* hbuf, int64_t* plan, float* y,
+                     const StageEvents& se, hipStream_t s) {
   const int rbs = la.de >> 6;
-  plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, dense ? la.E : 0, rbs, plan);
+  plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, DENSE ? la.E : 0, rbs, plan);
   se.record(0, s);
   {
     // resident capacity: blocks per CU at this kernel's register use, times CUs
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, up_mfma_kernel<NT>, kBlock, 0);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, up_mfma_kernel<NT, DENSE>, kBlock, 0);
     if (e != hipSuccess) return e;
     const int64_t max_items = units * la.E * rbs;
     int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     const int64_t need = (max_items + 3) / 4;
     if (grid > need) grid = need;
-    up_mfma_kernel<NT><<<dim3((unsigned)grid), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list, dense ? 1 : 0,
-                                                                      plan, hbuf);
+    up_mfma_kernel<NT, DENSE><<<dim3((unsigned)grid), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list, plan,
+                                                                             hbuf);
   }
   se.record(1, s);
   {
     const int waves = la.d >> 6;
     const int64_t bpu = (waves + 3) / 4;
     const int64_t nlog = units * bpu;
-    down_mfma_kernel<NT><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(la, units, L, count, list,
-                                                                                  dense ? 1 : 0, bpu, hbuf, y);
+    down_mfma_kernel<NT, DENSE><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(la, units, L, count, list,
+                                                                                         bpu, hbuf, y);
   }
   se.record(2, s);
   return hipGetLastError();
@@ -338,8 +339,12 @@ hipError_t launch_forward_mfma(const LayerArgs& la, const uint16_t* x, int64_t n
                                uint16_t* hbuf, int64_t* plan, float* y, const StageEvents& se, hipStream_t s) {
   const int64_t units = n_tokens / chunk_len;
   if (units == 0) return hipSuccess;
-  if (chunk_len <= 16) return launch_nt<1>(la, x, units, chunk_len, gates, count, list, dense, hbuf, plan, y, se, s);
-  return launch_nt<2>(la, x, units, chunk_len, gates, count, list, dense, hbuf, plan, y, se, s);
+  if (dense) {
+    if (chunk_len <= 16) return launch_nt<1, true>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, se, s);
+    return launch_nt<2, true>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, se, s);
+  }
+  if (chunk_len <= 16) return launch_nt<1, false>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, se, s);
+  return launch_nt<2, false>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, se, s);
 }
 
 }  // namespace bffn

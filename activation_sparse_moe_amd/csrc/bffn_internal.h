@@ -91,6 +91,11 @@ hipError_t launch_forward_mfma(const LayerArgs& la, const uint16_t* x, int64_t n
                                const float* gates, const int32_t* count, const int32_t* list, bool dense,
                                uint16_t* hbuf, int64_t* plan, float* y, const StageEvents& se, hipStream_t s);
 
+hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, const float* gates,
+                                  void* workspace, float* y, const StageEvents& se, hipStream_t s);
+size_t grouped_workspace_bytes(int64_t n_tokens, int E, int d, int de);
+bool grouped_supported(int d, int de, int dtype);
+
 bool route_uses_mfma(int d, int E, int chunk_len, int dtype);
 bool forward_mfma_supported(int d, int de, int dtype);
 

@@ -87,7 +87,7 @@ bffn::LayerArgs layer_args(const blockffn_layer* ly, int32_t n_layers) {
   return la;
 }
 
-enum class Path { kGemv, kMfma };
+enum class Path { kGemv, kMfma, kGrouped };
 
 // Resolves `mode` to a kernel family; returns a status code.
 int resolve_mode(const blockffn_layer* ly, int32_t chunk_len, int32_t mode, Path* path, bool* dense) {
@@ -111,7 +111,10 @@ int resolve_mode(const blockffn_layer* ly, int32_t chunk_len, int32_t mode, Path
       *dense = true;
       return BLOCKFFN_OK;
     case BLOCKFFN_MODE_GROUPED:
-      return fail(BLOCKFFN_ERR_MODE, "GROUPED mode is not available in this build");
+      if (!bffn::grouped_supported(ly->d, ly->d_expert, ly->dtype))
+        return fail(BLOCKFFN_ERR_MODE, "GROUPED needs bf16 with d and d_expert multiples of 128");
+      *path = Path::kGrouped;
+      return BLOCKFFN_OK;
     default:
       return fail(BLOCKFFN_ERR_MODE, "unknown mode %d", mode);
   }
@@ -130,6 +133,7 @@ size_t plan_bytes(int64_t n_tokens, int32_t chunk_len) {
 }
 
 size_t workspace_bytes_for(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, Path path) {
+  if (path == Path::kGrouped) return bffn::grouped_workspace_bytes(n_tokens, ly->n_experts, ly->d, ly->d_expert);
   return hbuf_bytes(ly, n_tokens, path) + plan_bytes(n_tokens, chunk_len);
 }
 
@@ -187,10 +191,12 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, 
   Path path;
   bool dense;
   if (int r = resolve_mode(layer, chunk_len, mode, &path, &dense)) return r;
+  if (path == Path::kGrouped && n_layers != 1)
+    return fail(BLOCKFFN_ERR_LAYERS, "GROUPED runs one batch through one layer (n_layers %d)", n_layers);
   if (n_tokens == 0) return BLOCKFFN_OK;
   if (!x || !gates || !y) return fail(BLOCKFFN_ERR_NULL, "x, gates and y must be non-NULL");
-  if (!dense && (!active_count || !active_list))
-    return fail(BLOCKFFN_ERR_NULL, "active_count and active_list must be non-NULL outside DENSE mode");
+  if (!dense && path != Path::kGrouped && (!active_count || !active_list))
+    return fail(BLOCKFFN_ERR_NULL, "active_count and active_list must be non-NULL outside DENSE and GROUPED modes");
   if (!aligned(x, 16) || !aligned(gates, 4) || !aligned(y, 16) || !aligned(active_count, 4) ||
       !aligned(active_list, 4))
     return fail(BLOCKFFN_ERR_ALIGN, "x and y must be 16-byte aligned, gates/count/list 4-byte aligned");
@@ -201,7 +207,10 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, 
     return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   const bffn::LayerArgs la = layer_args(layer, n_layers);
   hipError_t e;
-  if (path == Path::kMfma)
+  if (path == Path::kGrouped)
+    e = bffn::launch_forward_grouped(la, static_cast<const uint16_t*>(x), n_tokens, gates, workspace, y,
+                                     g_stage_events, stream);
+  else if (path == Path::kMfma)
     e = bffn::launch_forward_mfma(
         la, static_cast<const uint16_t*>(x), n_tokens, chunk_len, gates, active_count, active_list, dense,
         static_cast<uint16_t*>(workspace),

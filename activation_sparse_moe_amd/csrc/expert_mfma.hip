@@ -9,99 +9,15 @@
 //       H'[unit][slot] W_out[i]^T, accumulated in fp32 registers
 //
 // Both are tall-skinny products (L <= 32 tokens against 128..4096 weight
-// rows), so weights are the streamed MFMA operand A (16 rows per tile) and
-// tokens the small operand B (16 columns per tile, padded with zeros past L).
-// Every weight element is used by exactly one lane, so A goes from HBM
-// straight into registers with no LDS round trip: per 128-element step lane
-// (m = lane % 16, g = lane / 16) loads 64 contiguous bytes of its row at
-// element offset 32 g (four lanes cover 256 contiguous bytes of the row), and
-// MFMA q of the step contracts elements [32 g + 8 q, 32 g + 8 q + 8) of each
-// lane group; B is loaded with the same permutation of k, so the product is
-// exact whatever order the k's are visited in.  Each wave owns four 16-row
-// stripes (64 rows) and double-buffers the next step's loads.
-#include "bffn_internal.h"
+// rows), so weights are the streamed MFMA operand A (16 rows per stripe, four
+// stripes per wave) and tokens the small operand B (16 columns per tile,
+// padded past L).  Every weight element is used by exactly one lane, so A goes
+// from HBM straight into registers with no LDS round trip, two steps in
+// flight (mfma_stream.h).
+#include "mfma_stream.h"
 
 namespace bffn {
 namespace {
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-template <int NT>
-struct Step {
-  u32x4 a[4][4];   // [stripe][q]
-  u32x4 b[NT][4];  // [token tile][q]
-};
-
-// A rows: a_row0 points at element 32 g of row m of stripe 0; stripes are
-// `a_stripe` elements apart.  B: b_row[tl] points at element 32 g of token
-// m + 16 tl's row.  Lanes of tokens past L read a valid row of the chunk
-// instead (MFMA output columns are independent and those columns are never
-// stored), which keeps the pipelined loop free of branches so the compiler
-// can wait for exactly one step's loads.
-#ifndef BFFN_LANE_CONTIG
-#define BFFN_LANE_CONTIG 0
-#endif
-#ifndef BFFN_NT_LOADS
-#define BFFN_NT_LOADS 0
-#endif
-#ifndef BFFN_SCHED_FENCE
-#define BFFN_SCHED_FENCE 1
-#endif
-
-
-__device__ __forceinline__ u32x4 load_weights(const u32x4* p) {
-#if BFFN_NT_LOADS
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-
-// Element offset, within a 128-element step, of the 8 k's lane group g feeds
-// to MFMA q.
-__device__ __forceinline__ int kofs(int g, int q) {
-#if BFFN_LANE_CONTIG
-  return g * 32 + q * 8;
-#else
-  return q * 32 + g * 8;
-#endif
-}
-
-template <int NT>
-__device__ __forceinline__ void load_step(Step<NT>& st, const uint16_t* a_row0, int64_t a_stripe,
-                                          const uint16_t* const (&b_row)[NT], int k0, int g) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      st.a[s][q] = load_weights(reinterpret_cast<const u32x4*>(a_row0 + s * a_stripe + k0 + kofs(g, q)));
-  }
-#pragma unroll
-  for (int tl = 0; tl < NT; ++tl) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) st.b[tl][q] = *reinterpret_cast<const u32x4*>(b_row[tl] + k0 + kofs(g, q));
-  }
-}
-
-// Keeps the compiler's scheduler from moving instructions across this point,
-// so a step's loads stay issued ahead of the previous step's MFMAs.
-__device__ __forceinline__ void fence_schedule() {
-#if BFFN_SCHED_FENCE
-  __builtin_amdgcn_sched_barrier(0);
-#endif
-}
-
-template <int NT>
-__device__ __forceinline__ void mfma_step(f32x4 (&acc)[4][NT], const Step<NT>& st) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int tl = 0; tl < NT; ++tl)
-        acc[s][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[s][q]), as_bf16x8(st.b[tl][q]),
-                                                             acc[s][tl], 0, 0, 0);
-}
 
 // One up-projection item: 64 rows (block rb) of the expert in `slot` of
 // chunk `unit`, over all of d, for every token of the chunk.
@@ -113,40 +29,16 @@ __device__ __forceinline__ void up_item(const LayerArgs& la, const uint16_t* __r
   const int m = lane & 15, g = lane >> 4;
   const int d = la.d, de = la.de, E = la.E;
   const uint16_t* wi = layer_ptr(static_cast<const uint16_t*>(la.w_in), la.stride, unit, la.n_layers);
-  const uint16_t* a_row0 = wi + ((int64_t)i * de + rb * 64 + m) * d;
-  const int64_t a_stripe = 16 * (int64_t)d;
+  const uint16_t* a_row[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) a_row[s] = wi + ((int64_t)i * de + rb * 64 + s * 16 + m) * d;
   const int64_t t0 = unit * L;
   const uint16_t* b_row[NT];
 #pragma unroll
   for (int tl = 0; tl < NT; ++tl) b_row[tl] = x + (t0 + (m + 16 * tl) % L) * d;
   f32x4 acc[4][NT];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int tl = 0; tl < NT; ++tl) acc[s][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Two-deep software pipeline over the d / 128 steps, tail peeled.
-  const int nsteps = d >> 7;
-  Step<NT> s0, s1;
-  load_step<NT>(s0, a_row0, a_stripe, b_row, 0, g);
-  int k = 0;
-  for (; k + 2 < nsteps; k += 2) {
-    load_step<NT>(s1, a_row0, a_stripe, b_row, (k + 1) << 7, g);
-    fence_schedule();
-    mfma_step<NT>(acc, s0);
-    fence_schedule();
-    load_step<NT>(s0, a_row0, a_stripe, b_row, (k + 2) << 7, g);
-    fence_schedule();
-    mfma_step<NT>(acc, s1);
-    fence_schedule();
-  }
-  if (k + 1 < nsteps) {
-    load_step<NT>(s1, a_row0, a_stripe, b_row, (k + 1) << 7, g);
-    mfma_step<NT>(acc, s0);
-    mfma_step<NT>(acc, s1);
-  } else {
-    mfma_step<NT>(acc, s0);
-  }
+  zero_acc<NT>(acc);
+  stream_contract<NT>(acc, a_row, b_row, 0, d >> 7, g);
 
   // D layout: lane (m, g) holds rows 4 g + r (r < 4), column m of each tile.
 #pragma unroll
@@ -237,27 +129,25 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   if (kb >= d) return;
   const int n_active = DENSE ? E : count[unit];
   const uint16_t* wo = layer_ptr(static_cast<const uint16_t*>(la.w_out), la.stride, unit, la.n_layers);
-  const int64_t a_stripe = 16 * (int64_t)de;
   const int64_t t0 = unit * L;
   const int spe = de >> 7;  // 128-element steps per expert
   const int n_steps = n_active * spe;
 
   f32x4 acc[4][NT];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int tl = 0; tl < NT; ++tl) acc[s][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+  zero_acc<NT>(acc);
 
   // Step p covers slot p / spe, elements [128 (p % spe), +128) of that expert.
   auto load = [&](Step<NT>& st, int p) {
     const int slot = p / spe, j0 = (p % spe) * 128;
     const int i = DENSE ? slot : list[unit * E + slot];
-    const uint16_t* a_row0 = wo + ((int64_t)i * d + kb + m) * de;
+    const uint16_t* a_row[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a_row[s] = wo + ((int64_t)i * d + kb + s * 16 + m) * de;
     const uint16_t* b_row[NT];
 #pragma unroll
     for (int tl = 0; tl < NT; ++tl)
       b_row[tl] = hbuf + ((unit * E + slot) * L + (m + 16 * tl) % L) * (int64_t)de;
-    load_step<NT>(st, a_row0, a_stripe, b_row, j0, g);
+    load_step<NT>(st, a_row, b_row, j0, g);
   };
 
   // Two-deep software pipeline over the union's steps, tail peeled.

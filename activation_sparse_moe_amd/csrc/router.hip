@@ -10,11 +10,11 @@
 // ballots.  Two producers of the pre-activations:
 //   * route_mfma_kernel (bf16, L >= 8): the router is a genuine E x d x L
 //     contraction; each wave streams a quarter of d for every expert row
-//     through v_mfma_f32_16x16x32_bf16 and the four partial sums are added in
-//     a fixed order in the epilogue (deterministic).
+//     through v_mfma_f32_16x16x32_bf16 (pipelined as in mfma_stream.h) and
+//     the four partial sums are added in a fixed order in the epilogue.
 //   * route_valu_kernel (fp32, or L < 8): a bandwidth-bound GEMV; lane groups
 //     stride over d with 16-byte loads and reduce with cross-lane shuffles.
-#include "bffn_internal.h"
+#include "mfma_stream.h"
 
 namespace bffn {
 namespace {
@@ -117,14 +117,11 @@ __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const 
   router_epilogue(zp, 1, E, L, t0, b, s, la.eps, gates, masks, preact);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
 // MFMA router.  Wave w owns d-range [w d/4, (w+1) d/4) for every expert row,
-// in blocks of four 16-row stripes.  Per 128-element step, lane (m, g)
-// (m = lane % 16, g = lane / 16) loads 64 contiguous bytes of row m at
-// element offset 32 g, and the same offset of token m's x; MFMA q of the
-// step contracts elements [32 g + 8 q, 32 g + 8 q + 8) of every lane group,
-// so A and B see one consistent permutation of the 128 k's.
+// in blocks of four 16-row stripes, streamed with the two-deep pipeline of
+// mfma_stream.h; the last block's missing stripes repeat a valid stripe and
+// are not stored.  The four per-wave partial sums meet in LDS and are added
+// in a fixed order by the epilogue (deterministic).
 template <int NT>
 __global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
                                                             int L, float* __restrict__ gates,
@@ -141,57 +138,29 @@ __global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const 
   const int kw = d >> 2;
   const int64_t t0 = unit * L;
   const int nstripes = E >> 4;
+  const uint16_t* b_row[NT];
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) b_row[tl] = x + (t0 + (m + 16 * tl) % L) * d;
   for (int sb = 0; sb < nstripes; sb += 4) {
-    f32x4 acc[4][NT];
+    const uint16_t* a_row[4];
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int tl = 0; tl < NT; ++tl) acc[st][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = w * kw; k0 < (w + 1) * kw; k0 += 128) {
-      u32x4 bv[NT][4];
-#pragma unroll
-      for (int tl = 0; tl < NT; ++tl) {
-        const int n = m + 16 * tl;
-        if (n < L) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(x + (t0 + n) * d + k0 + g * 32);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) bv[tl][q] = p[q];
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) bv[tl][q] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-      u32x4 av[4][4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        if (sb + st < nstripes) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(wr + (int64_t)((sb + st) * 16 + m) * d + k0 + g * 32);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) av[st][q] = p[q];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-          if (sb + st < nstripes)
-#pragma unroll
-            for (int tl = 0; tl < NT; ++tl)
-              acc[st][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[st][q]), as_bf16x8(bv[tl][q]),
-                                                                    acc[st][tl], 0, 0, 0);
+    for (int st = 0; st < 4; ++st) {
+      const int stripe = sb + st < nstripes ? sb + st : nstripes - 1;
+      a_row[st] = wr + (int64_t)(stripe * 16 + m) * d;
     }
+    f32x4 acc[4][NT];
+    zero_acc<NT>(acc);
+    stream_contract<NT>(acc, a_row, b_row, w * kw, kw >> 7, g);
     // D layout: lane (m, g) holds rows 4 g + r, column m of each 16 x 16 tile.
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      if (sb + st < nstripes) {
+      if (sb + st >= nstripes) continue;
 #pragma unroll
-        for (int tl = 0; tl < NT; ++tl) {
-          const int n = m + 16 * tl;
-          if (n < L) {
+      for (int tl = 0; tl < NT; ++tl) {
+        const int n = m + 16 * tl;
+        if (n >= L) continue;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) zp[(w * E + (sb + st) * 16 + 4 * g + r) * L + n] = acc[st][tl][r];
-          }
-        }
+        for (int r = 0; r < 4; ++r) zp[(w * E + (sb + st) * 16 + 4 * g + r) * L + n] = acc[st][tl][r];
       }
     }
   }

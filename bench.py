@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "chunk-8 BlockFFN layer tokens/s + active-weight HBM GB/s (% of peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 DEFAULT_WORKLOAD = "chunk8_d2048_E64"
 CSRC = os.path.join(ROOT, "activation_sparse_moe_amd", "csrc")
 
@@ -103,32 +104,45 @@ class StepRunner:
         self.lst = torch.empty((C, E), dtype=torch.int32, device=dev)
         self.y = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
         self.stats = torch.empty((8 + 129,), dtype=torch.int64, device=dev)
+        # units per call: never more than the layer copies, so no two units of
+        # one launch stream the same weights
+        self.sub_units = min(C, cfg.replicas) if cfg.replicas > 1 else C
+        sub_T = self.sub_units * L
         self.ws = {}
         for m in {mode, "dense"}:
-            self.ws[m] = B.alloc_workspace(self.dl, T, L, m)
+            self.ws[m] = B.alloc_workspace(self.dl, sub_T, L, m)
+        self.n_stage = 4 if mode == "grouped" else 3
         self.lib = B.load()
 
     def step(self, mode: str, ev=None, stage_events=None):
-        """route -> union -> forward -> stats.  ev: 4 torch events recorded
-        after route, union, forward and stats; stage_events: ctypes array of 3
-        hipEvent_t recorded by the library around the forward's two kernels."""
+        """route -> union -> forward -> stats, in sub-batches of at most one
+        unit per layer copy.  ev: 4 torch events recorded after route, union,
+        forward and stats of the last sub-batch; stage_events: ctypes array of
+        hipEvent_t the library records around the forward's timed kernels
+        (sub-batch 0 only)."""
         B, cfg = self.B, self.cfg
         L, E = cfg.chunk_len, cfg.n_experts
-        B.blockffn_route(self.dl, self.xd, L, gates=self.gates, token_masks=self.masks)
-        if ev is not None:
-            ev[0].record()
-        B.blockffn_chunk_union(E, self.masks, L, chunk_masks=self.umask, active_count=self.count,
-                               active_list=self.lst)
-        if ev is not None:
-            ev[1].record()
-        if stage_events is not None:
-            self.lib.blockffn_set_stage_events(ctypes.cast(stage_events, ctypes.c_void_p), 3)
-        B.blockffn_forward(self.dl, self.xd, L, self.gates, self.count, self.lst, mode=mode,
-                           workspace=self.ws[mode], y=self.y)
-        if stage_events is not None:
-            self.lib.blockffn_set_stage_events(None, 0)
-        if ev is not None:
-            ev[2].record()
+        C = cfg.n_tokens // L
+        nb = (C + self.sub_units - 1) // self.sub_units
+        for b in range(nb):
+            c0, c1 = b * self.sub_units, min(C, (b + 1) * self.sub_units)
+            t0, t1 = c0 * L, c1 * L
+            last = b == nb - 1
+            x, g, m, y = self.xd[t0:t1], self.gates[t0:t1], self.masks[t0:t1], self.y[t0:t1]
+            cnt, lst, um = self.count[c0:c1], self.lst[c0:c1], self.umask[c0:c1]
+            B.blockffn_route(self.dl, x, L, gates=g, token_masks=m)
+            if ev is not None and last:
+                ev[0].record()
+            B.blockffn_chunk_union(E, m, L, chunk_masks=um, active_count=cnt, active_list=lst)
+            if ev is not None and last:
+                ev[1].record()
+            if stage_events is not None and b == 0:
+                self.lib.blockffn_set_stage_events(ctypes.cast(stage_events, ctypes.c_void_p), self.n_stage)
+            B.blockffn_forward(self.dl, x, L, g, cnt, lst, mode=mode, workspace=self.ws[mode], y=y)
+            if stage_events is not None and b == 0:
+                self.lib.blockffn_set_stage_events(None, 0)
+            if ev is not None and last:
+                ev[2].record()
         B.blockffn_sparsity_stats(E, self.masks, L, stats_dev=self.stats)
         if ev is not None:
             ev[3].record()
@@ -140,14 +154,15 @@ class StepRunner:
         torch.cuda.synchronize()
         E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
         evs = [[E() for _ in range(4)] for _ in range(steps)]
-        stage = [[E() for _ in range(3)] for _ in range(steps)]
+        ns = self.n_stage if mode == self.mode else 3
+        stage = [[E() for _ in range(ns)] for _ in range(steps)]
         # record every event once so that its hipEvent exists before the
         # library is handed the raw handles
         for row in stage:
             for e in row:
                 e.record()
         torch.cuda.synchronize()
-        handles = [(ctypes.c_void_p * 3)(*[e.cuda_event for e in row]) for row in stage]
+        handles = [(ctypes.c_void_p * ns)(*[e.cuda_event for e in row]) for row in stage]
         start, end = E(), E()
         torch.cuda.synchronize()
         start.record()
@@ -155,22 +170,36 @@ class StepRunner:
         starts = []
         for k in range(steps):
             starts.append(prev)
-            self.step(mode, ev=evs[k], stage_events=handles[k])
+            self.step(mode, ev=evs[k], stage_events=handles[k]) if ns == self.n_stage else \
+                self._step_n(mode, evs[k], handles[k], ns)
             prev = evs[k][3]
         end.record()
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(end)
         per = {"route": [], "union": [], "up": [], "down": [], "stats": [], "forward": []}
+        if ns > 3:
+            per["combine"] = []
+        nb = (self.cfg.n_tokens // self.cfg.chunk_len + self.sub_units - 1) // self.sub_units
         for k in range(steps):
-            s0 = starts[k]
-            per["route"].append(s0.elapsed_time(evs[k][0]))
-            per["union"].append(evs[k][0].elapsed_time(evs[k][1]))
-            per["up"].append(stage[k][0].elapsed_time(stage[k][1]))
-            per["down"].append(stage[k][1].elapsed_time(stage[k][2]))
-            per["forward"].append(evs[k][1].elapsed_time(evs[k][2]))
-            per["stats"].append(evs[k][2].elapsed_time(evs[k][3]))
-        avg = {k: sum(v) / len(v) for k, v in per.items()}
+            per["up"].append(stage[k][0].elapsed_time(stage[k][1]) * nb)
+            per["down"].append(stage[k][1].elapsed_time(stage[k][2]) * nb)
+            if ns > 3:
+                per["combine"].append(stage[k][2].elapsed_time(stage[k][3]) * nb)
+            if nb == 1:
+                per["route"].append(starts[k].elapsed_time(evs[k][0]))
+                per["union"].append(evs[k][0].elapsed_time(evs[k][1]))
+                per["forward"].append(evs[k][1].elapsed_time(evs[k][2]))
+                per["stats"].append(evs[k][2].elapsed_time(evs[k][3]))
+        avg = {k: sum(v) / len(v) for k, v in per.items() if v}
         return total_ms / steps, avg
+
+    def _step_n(self, mode, ev, handle, ns):
+        n0 = self.n_stage
+        self.n_stage = ns
+        try:
+            self.step(mode, ev=ev, stage_events=handle)
+        finally:
+            self.n_stage = n0
 
     def byte_model(self):
         """Algorithmic bytes per launch of each kernel (what the method must
@@ -195,6 +224,17 @@ class StepRunner:
         step_alg = C * E * d * es + U * 2 * d * de * es + T * d * es + T * d * 4
         return b, U, active_weight, step_alg
 
+    def flop_model(self):
+        """Algorithmic matrix flops of the grouped kernels (token-expert pairs
+        x 2 d d_e each) and the bytes they must move."""
+        np, cfg = self.np, self.cfg
+        g = self.gates.cpu().numpy()
+        P = int((g > 0).sum())
+        d, de, E, T = cfg.d, cfg.d_expert, cfg.n_experts, cfg.n_tokens
+        return {"pairs": P, "up_flops": 2 * P * d * de, "down_flops": 2 * P * de * d,
+                "layer_bytes": 2 * (E * d + 2 * E * d * de) + 4 * E, "x_bytes": 2 * T * d, "y_bytes": 4 * T * d,
+                "partial_bytes": 2 * P * d}
+
 def cpu_baseline(cfg, layer, x_host, target_s: float):
     """The oracle as it stands, on the host cores, on a bounded sample of chunks."""
     import oracle
@@ -218,6 +258,35 @@ def cpu_baseline(cfg, layer, x_host, target_s: float):
     return {"value": round(n * L / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} of {C} chunks ({n * L} tokens) of this workload, layer copy 0: route + union + "
                       f"per-token forward + stats, fp64 C oracle, {dt:.1f} s"}
+
+
+def torch_dense_reference_ms(runner, steps: int) -> float:
+    """Dense all-experts forward of the whole batch as two vendor GEMMs
+    (torch.matmul -> hipBLASLt) over the concatenated experts, on the same
+    inputs and gates: the comparison for the grouped path."""
+    import torch
+    t = runner.dl.tensors(0)
+    E, d, de = runner.cfg.n_experts, runner.cfg.d, runner.cfg.d_expert
+    w_in_t = t["w_in"].reshape(E * de, d).t().contiguous()                      # [d][E d_e]
+    w_out_t = t["w_out"].permute(0, 2, 1).reshape(E * de, d).contiguous()      # [E d_e][d]
+    g_rep = runner.gates.repeat_interleave(de, dim=1)
+    x = runner.xd
+
+    def fwd():
+        h = torch.matmul(x, w_in_t).float()
+        h = (torch.nn.functional.silu(h) * g_rep).to(torch.bfloat16)
+        return torch.matmul(h, w_out_t)
+
+    for _ in range(2):
+        fwd()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fwd()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def copy_calibration():
@@ -261,18 +330,35 @@ def main(argv=None) -> int:
     value = T / (ms / 1e3)
 
     dense = None
-    if args.dense_steps > 0:
+    grouped = mode == "grouped"
+    if args.dense_steps > 0 and grouped:
+        dfwd = torch_dense_reference_ms(runner, args.dense_steps)
+        dense = {"kind": "torch.matmul (hipBLASLt) dense GEMMs over all experts", "forward_ms": round(dfwd, 4),
+                 "speedup_forward": round(dfwd / avg["forward"], 3) if "forward" in avg else None}
+    elif args.dense_steps > 0:
         dms, davg = runner.timed("dense", args.dense_steps, 1)
-        dense = {"ms_per_step": round(dms, 4), "forward_ms": round(davg["forward"], 4),
-                 "speedup_step": round(dms / ms, 3), "speedup_forward": round(davg["forward"] / avg["forward"], 3)}
+        dense = {"kind": "same kernels, every expert (BLOCKFFN_MODE_DENSE)", "ms_per_step": round(dms, 4),
+                 "speedup_step": round(dms / ms, 3)}
+        if "forward" in davg and "forward" in avg:
+            dense.update({"forward_ms": round(davg["forward"], 4),
+                          "speedup_forward": round(davg["forward"] / avg["forward"], 3)})
 
     dom = "up" if avg["up"] >= avg["down"] else "down"
     kernel_name = {"up": "expert_up", "down": "expert_down"}[dom]
-    achieved = bytes_per[dom] / (avg[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": f"{kernel_name} ({mode})", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": profiled_traffic(kernel_name, cfg.name),
-                "algorithmic_bytes_per_launch": bytes_per[dom], "avg_launch_ms": round(avg[dom], 5)}
+    if grouped:
+        fm = runner.flop_model()
+        fl = fm[f"{dom}_flops"]
+        achieved = fl / (avg[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": f"grouped_{dom} ({mode})", "achieved": round(achieved, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": profiled_traffic(f"grouped_{dom}", cfg.name),
+                    "algorithmic_flops_per_launch": fl, "avg_launch_ms": round(avg[dom], 5)}
+    else:
+        achieved = bytes_per[dom] / (avg[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": f"{kernel_name} ({mode})", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": profiled_traffic(kernel_name, cfg.name),
+                    "algorithmic_bytes_per_launch": bytes_per[dom], "avg_launch_ms": round(avg[dom], 5)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -291,7 +377,11 @@ def main(argv=None) -> int:
         "active_weight_gbs": round(step_gbs, 1),
         "active_weight_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
         "kernel_ms": {k: round(v, 5) for k, v in avg.items()},
-        "kernel_gbs": {k: round(bytes_per[k] / (avg[k] * 1e-3) / 1e9, 1) for k in bytes_per},
+        "kernel_gbs": ({k: round(bytes_per[k] / (avg[k] * 1e-3) / 1e9, 1) for k in bytes_per if k in avg}
+                       if not grouped else None),
+        "grouped": (dict(runner.flop_model(), up_tflops=round(runner.flop_model()["up_flops"] / avg["up"] / 1e9, 1),
+                         down_tflops=round(runner.flop_model()["down_flops"] / avg["down"] / 1e9, 1))
+                    if grouped else None),
         "dense": dense,
         "sparsity": {"tls": round(st["tls"], 4), "cls": round(st["cls"], 4), "mean_union": round(U / (T // cfg.chunk_len), 2),
                      "reuse": round(st["reuse"], 4)},

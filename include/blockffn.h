@@ -156,13 +156,17 @@ int blockffn_chunk_union(int32_t n_experts, const uint64_t* token_masks, int64_t
  * mask the irrelevant activations with the gates; §7: outer loop over the
  * active experts).
  *   gates, active_count, active_list   as written by the two calls above
- *                                      (active_* are ignored in DENSE mode)
+ *                                      (active_* are ignored, and may be NULL,
+ *                                      in DENSE and GROUPED modes)
  *   y          [n_tokens][d] fp32 out, overwritten:
  *              y_t = sum over i in the chunk's union of g[t][i] E_i(x_t)
  *   workspace  device scratch of at least blockffn_workspace_size() bytes,
  *              256-byte aligned; its contents need no initialisation
- * GROUPED mode needs n_layers == 1.  Errors: NULL, SHAPE, DTYPE, CHUNK,
- * WORKSPACE, MODE, ALIGN, LAYERS, HIP.
+ * GROUPED mode (one batch through one layer, n_layers == 1): every
+ * (token, expert) pair with a positive gate is grouped by expert, each
+ * expert's weights are read once for all of its tokens in MFMA GEMMs, and
+ * each token's per-expert partial rows are summed in ascending expert order.
+ * Errors: NULL, SHAPE, DTYPE, CHUNK, WORKSPACE, MODE, ALIGN, LAYERS, HIP.
  */
 int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
                      int32_t chunk_len, const float* gates, const int32_t* active_count,
@@ -181,9 +185,10 @@ int blockffn_sparsity_stats(int32_t n_experts, const uint64_t* token_masks, int6
 /*
  * Stage timing (instrumentation for profilers and benchmarks).  While set,
  * every blockffn_forward call of the calling thread records events[0] on its
- * stream before its first kernel and events[k] right after its k-th kernel,
- * for k < n_events.  The forward enqueues two kernels on the GEMV, MFMA and
- * DENSE paths (expert up-projection, then down-projection).  `events` are
+ * stream before its first timed kernel and events[k] right after its k-th
+ * timed kernel, for k < n_events.  The timed kernels are the expert
+ * up-projection and down-projection (GEMV, CHUNK_MFMA and DENSE modes), plus
+ * the per-token combine in GROUPED mode.  `events` are
  * caller-created hipEvents in caller memory that must stay valid while set;
  * pass NULL to stop.  Errors: SHAPE (n_events < 1 with non-NULL events).
  */

@@ -175,6 +175,10 @@ def test_forward_rejects_bad_arguments(lib):
     assert _forward(lib, _layer(), y=P + 4) == _capi.ERR_ALIGN
     assert _forward(lib, _layer(), count=None) == _capi.ERR_NULL
     assert _forward(lib, _layer(), T=20) == _capi.ERR_CHUNK
+    assert _forward(lib, _layer(dtype=0), mode=_capi.MODE_GROUPED) == _capi.ERR_MODE     # GROUPED needs bf16
+    assert _forward(lib, _layer(d_expert=64), mode=_capi.MODE_GROUPED) == _capi.ERR_MODE
+    assert _forward(lib, _layer(layer_stride=1 << 20), mode=_capi.MODE_GROUPED, n_layers=2) == _capi.ERR_LAYERS
+    assert _forward(lib, _layer(), mode=_capi.MODE_GROUPED, ws_bytes=4096) == _capi.ERR_WORKSPACE
 
 
 def test_workspace_size(lib):

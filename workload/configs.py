@@ -76,7 +76,7 @@ CONFIGS: dict[str, WorkloadConfig] = {
         # Single-token decode: 4096 independent tokens, bandwidth-bound GEMV.
         WorkloadConfig("decode_L1_d2048_E64", d=2048, n_experts=64, d_expert=128,
                        dtype="bf16", chunk_len=1, units=4096, bias_k=_K_12_OF_64,
-                       alpha=0.0, seed=2, replicas=520),
+                       alpha=0.0, seed=2, replicas=512),
         # Speculative-verify chunk of 8 tokens, 512 chunks (about 19 of 64 experts per chunk).
         WorkloadConfig("chunk8_d2048_E64", d=2048, n_experts=64, d_expert=128,
                        dtype="bf16", chunk_len=8, units=512, bias_k=_K_12_OF_64,

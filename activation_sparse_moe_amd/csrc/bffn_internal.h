@@ -98,5 +98,6 @@ bool grouped_supported(int d, int de, int dtype);
 
 bool route_uses_mfma(int d, int E, int chunk_len, int dtype);
 bool forward_mfma_supported(int d, int de, int dtype);
+size_t forward_mfma_plan_bytes(int64_t units);
 
 }  // namespace bffn

@@ -127,9 +127,10 @@ size_t hbuf_bytes(const blockffn_layer* ly, int64_t n_tokens, Path path) {
   return round256((size_t)n_tokens * (size_t)ly->n_experts * (size_t)ly->d_expert * elem);
 }
 
-// Work plan after the hidden buffer: one int64 per chunk plus a total.
+// Work plan after the hidden buffer: one int64 per chunk plus a total, and
+// two work counters.
 size_t plan_bytes(int64_t n_tokens, int32_t chunk_len) {
-  return round256(sizeof(int64_t) * (size_t)(n_tokens / chunk_len + 1));
+  return round256(bffn::forward_mfma_plan_bytes(n_tokens / chunk_len));
 }
 
 size_t workspace_bytes_for(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, Path path) {

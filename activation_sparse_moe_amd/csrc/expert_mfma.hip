@@ -9,53 +9,20 @@
 //       H'[unit][slot] W_out[i]^T, accumulated in fp32 registers
 //
 // Both are tall-skinny products (L <= 32 tokens against 128..4096 weight
-// rows), so weights are the streamed MFMA operand A (16 rows per stripe, four
-// stripes per wave) and tokens the small operand B (16 columns per tile,
-// padded past L).  Every weight element is used by exactly one lane, so A goes
-// from HBM straight into registers with no LDS round trip, two steps in
-// flight (mfma_stream.h).
-#include "mfma_stream.h"
+// rows): weights are MFMA operand A (16 rows per stripe, four stripes = 64
+// rows per work item) and tokens operand B (16 columns per tile, padded past
+// L).  Every weight byte is used once, so weights stream from HBM with the
+// non-temporal policy through a wave-private LDS ring (lds_stream.h): full
+// 128-byte lines per load instruction, two 64-element steps in flight, the
+// step stream continuing across work items.  Both kernels are persistent
+// (one block per CU); each wave takes a contiguous, statically balanced range
+// of work items (equal counts for the up items, equal step totals for the
+// variable-length down items), decoded with scalar loads only, so nothing in
+// the loop waits on a returning memory operation except the weight stream.
+#include "lds_stream.h"
 
 namespace bffn {
 namespace {
-
-// One up-projection item: 64 rows (block rb) of the expert in `slot` of
-// chunk `unit`, over all of d, for every token of the chunk.
-template <int NT>
-__device__ __forceinline__ void up_item(const LayerArgs& la, const uint16_t* __restrict__ x, int L,
-                                        const float* __restrict__ gates, int64_t unit, int slot, int rb, int i,
-                                        uint16_t* __restrict__ hbuf) {
-  const int lane = threadIdx.x & 63;
-  const int m = lane & 15, g = lane >> 4;
-  const int d = la.d, de = la.de, E = la.E;
-  const uint16_t* wi = layer_ptr(static_cast<const uint16_t*>(la.w_in), la.stride, unit, la.n_layers);
-  const uint16_t* a_row[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) a_row[s] = wi + ((int64_t)i * de + rb * 64 + s * 16 + m) * d;
-  const int64_t t0 = unit * L;
-  const uint16_t* b_row[NT];
-#pragma unroll
-  for (int tl = 0; tl < NT; ++tl) b_row[tl] = x + (t0 + (m + 16 * tl) % L) * d;
-  f32x4 acc[4][NT];
-  zero_acc<NT>(acc);
-  stream_contract<NT>(acc, a_row, b_row, 0, d >> 7, g);
-
-  // D layout: lane (m, g) holds rows 4 g + r (r < 4), column m of each tile.
-#pragma unroll
-  for (int tl = 0; tl < NT; ++tl) {
-    const int n = m + 16 * tl;
-    if (n >= L) continue;
-    const float gv = gates[(t0 + n) * E + i];
-    uint16_t* hrow = hbuf + ((unit * E + slot) * L + n) * (int64_t)de + rb * 64 + 4 * g;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f32x4 v = acc[s][tl];
-      const uint32_t lo = f32_to_bf16(gv * swish(v[0])) | (f32_to_bf16(gv * swish(v[1])) << 16);
-      const uint32_t hi = f32_to_bf16(gv * swish(v[2])) | (f32_to_bf16(gv * swish(v[3])) << 16);
-      *reinterpret_cast<u32x2*>(hrow + s * 16) = u32x2{lo, hi};
-    }
-  }
-}
 
 // Exclusive prefix over chunks of the up-projection item counts
 // (union size x row blocks, or E x row blocks in dense mode):
@@ -84,104 +51,267 @@ __global__ __launch_bounds__(1024) void plan_items_kernel(const int32_t* __restr
   if (tid == 1023) prefix[n_units] = part[1023] * per_slot;
 }
 
-// Persistent up-projection: a fixed grid sized to the resident capacity; wave
-// gw takes items gw, gw + W, gw + 2W, ... of the chunk-major item list, so
-// every wave streams weights and no block is spent on inactive slots.
+// Wave gw of nw takes the contiguous items [gw total / nw, (gw + 1) total / nw).
+__device__ __forceinline__ void wave_range(int64_t total, int64_t gw, int64_t nw, int64_t* b, int64_t* e) {
+  *b = gw * total / nw;
+  *e = (gw + 1) * total / nw;
+}
+
+struct UpItem {
+  int64_t unit;
+  int slot, rb, i;
+};
+
+// ---- up-projection: H'[unit][slot] = g * Swish(X W_in[i]^T), items of 64 rows ----
 template <int NT, bool DENSE>
 __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
                                                          int64_t n_units, int L, const float* __restrict__ gates,
                                                          const int32_t* __restrict__ list,
                                                          const int64_t* __restrict__ prefix,
                                                          uint16_t* __restrict__ hbuf) {
+  using G = RingGeom<NT, true>;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRingBufs][G::kBufBytes];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int rbs = la.de >> 6;
-  const int64_t total = prefix[n_units];
-  for (int64_t item = (int64_t)blockIdx.x * 4 + w; item < total; item += nwaves) {
-    int64_t lo = 0, hi = n_units - 1;  // last chunk whose prefix <= item
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+  const int d = la.d, de = la.de, E = la.E, rbs = de >> 6;
+  const int nsteps = d / kStepK;
+  uint8_t* bufs = &ring[w][0][0];
+  int64_t item, item_end;
+  wave_range(prefix[n_units], (int64_t)blockIdx.x * 4 + w, (int64_t)gridDim.x * 4, &item, &item_end);
+  if (item >= item_end) return;
+
+  auto decode = [&](int64_t it_idx) {
+    int64_t lo = 0, hi = n_units - 1;  // last chunk whose prefix <= it_idx
     while (lo < hi) {
       const int64_t mid = (lo + hi + 1) >> 1;
-      if (prefix[mid] <= item) lo = mid; else hi = mid - 1;
+      if (prefix[mid] <= it_idx) lo = mid; else hi = mid - 1;
     }
-    const int64_t unit = lo;
-    const int r = (int)(item - prefix[unit]);
-    const int slot = r / rbs, rb = r % rbs;
-    const int i = DENSE ? slot : list[unit * la.E + slot];
-    up_item<NT>(la, x, L, gates, unit, slot, rb, i, hbuf);
+    UpItem it;
+    it.unit = lo;
+    const int r = (int)(it_idx - prefix[lo]);
+    it.slot = r / rbs;
+    it.rb = r % rbs;
+    it.i = DENSE ? it.slot : list[lo * E + it.slot];
+    return it;
+  };
+  // this lane's DMA sources for an item (step 0)
+  const uint16_t* a_src[8];
+  const uint16_t* b_src[G::kBInstr];
+  const float* g_src;
+  auto point = [&](const UpItem& it) {
+    const uint16_t* wi = layer_ptr(static_cast<const uint16_t*>(la.w_in), la.stride, it.unit, la.n_layers);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int R = 8 * j + (lane >> 3);
+      a_src[j] = wi + ((int64_t)it.i * de + it.rb * 64 + R) * d + dma_chunk_elems(R, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < G::kBInstr; ++j) {
+      const int n = 8 * j + (lane >> 3);
+      b_src[j] = x + (it.unit * L + n % L) * d + dma_chunk_elems(n, lane);
+    }
+    g_src = gates + (it.unit * L + lane % L) * E + it.i;
+  };
+  auto issue = [&](int slot, int k) {
+    uint8_t* buf = bufs + slot * G::kBufBytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16<kPolicyStream>(a_src[j] + k * kStepK, buf + j * 1024);
+#pragma unroll
+    for (int j = 0; j < G::kBInstr; ++j) dma16<kPolicyReuse>(b_src[j] + k * kStepK, buf + kABytes + j * 1024);
+    dma4(g_src, buf + G::kGateOff);
+  };
+
+  UpItem cmp = decode(item), nxt = cmp;
+  point(cmp);
+  int64_t item_iss = item;
+  int k_iss = 0, k_last = 0;
+  bool iss_done = false, has_next = false;
+  issue(0, k_iss);
+  issue(1, ++k_iss);  // nsteps >= 2
+  ++k_iss;
+  f32x4 acc[4][NT];
+  ring_zero<NT>(acc);
+  int k_cmp = 0;
+  for (int t = 0;; ++t) {
+    // issue the step two ahead, or repeat a valid one past the end of the range
+    if (!iss_done && k_iss == nsteps) {
+      if (++item_iss < item_end) {
+        nxt = decode(item_iss);
+        has_next = true;
+        point(nxt);
+        k_iss = 0;
+      } else {
+        iss_done = true;
+      }
+    }
+    if (!iss_done) k_last = k_iss++;
+    issue((t + 2) % kRingBufs, k_last);
+    wait_vmcnt<G::kWaitAhead>();
+    const uint8_t* buf = bufs + (t % kRingBufs) * G::kBufBytes;
+    ring_mfma<NT>(acc, buf, m, g);
+    __builtin_amdgcn_sched_barrier(0);
+    if (++k_cmp < nsteps) continue;
+    // item complete: g * Swish, bf16, to the hidden buffer (gates from this step's buffer)
+    const int64_t t0 = cmp.unit * L;
+    const float* gv_lds = reinterpret_cast<const float*>(buf + G::kGateOff);
+#pragma unroll
+    for (int tl = 0; tl < NT; ++tl) {
+      const int n = m + 16 * tl;
+      if (n >= L) continue;
+      const float gv = gv_lds[n];
+      uint16_t* hrow = hbuf + ((cmp.unit * E + cmp.slot) * L + n) * (int64_t)de + cmp.rb * 64 + 4 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f32x4 v = acc[s][tl];
+        const uint32_t lo = f32_to_bf16(gv * swish(v[0])) | (f32_to_bf16(gv * swish(v[1])) << 16);
+        const uint32_t hi = f32_to_bf16(gv * swish(v[2])) | (f32_to_bf16(gv * swish(v[3])) << 16);
+        *reinterpret_cast<u32x2*>(hrow + s * 16) = u32x2{lo, hi};
+      }
+    }
+    if (!has_next) break;
+    cmp = nxt;
+    has_next = false;
+    k_cmp = 0;
+    ring_zero<NT>(acc);
   }
+  wait_vmcnt<0>();  // no LDS write may outlive the wave
 }
 
+// ---- down-projection: Y[unit][kb .. kb + 64) = sum over slots of H'[unit][slot] W_out[i]^T ----
+// Items (chunk, 64 output rows) take count[chunk] * d_e / 64 steps; each wave
+// gets the items whose first step falls in its equal share of all steps.
 template <int NT, bool DENSE>
 __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t n_units, int L,
                                                            const int32_t* __restrict__ count,
                                                            const int32_t* __restrict__ list,
-                                                           int64_t blocks_per_unit,
+                                                           const int64_t* __restrict__ prefix,
                                                            const uint16_t* __restrict__ hbuf,
                                                            float* __restrict__ y) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int m = lane & 15, g = lane >> 4;
-  const int64_t lb = xcd_logical_block(blockIdx.x, n_units * blocks_per_unit);
-  if (lb < 0) return;
-  const int64_t unit = lb / blocks_per_unit;
-  const int wave_in_unit = (int)(lb % blocks_per_unit) * 4 + w;
+  using G = RingGeom<NT, false>;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRingBufs][G::kBufBytes];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int d = la.d, de = la.de, E = la.E;
-  const int kb = wave_in_unit * 64;
-  if (kb >= d) return;
-  const int n_active = DENSE ? E : count[unit];
-  const uint16_t* wo = layer_ptr(static_cast<const uint16_t*>(la.w_out), la.stride, unit, la.n_layers);
-  const int64_t t0 = unit * L;
-  const int spe = de >> 7;  // 128-element steps per expert
-  const int n_steps = n_active * spe;
+  const int spe = de / kStepK;   // steps per expert
+  const int kbs = d >> 6;        // 64-row blocks per chunk
+  const int rbs = de >> 6;       // prefix[] counts union size x rbs
+  uint8_t* bufs = &ring[w][0][0];
+  const int64_t gw = (int64_t)blockIdx.x * 4 + w, nw = (int64_t)gridDim.x * 4;
 
-  f32x4 acc[4][NT];
-  zero_acc<NT>(acc);
+  // step index where item (u, kb) starts; union sizes before u are prefix[u] / rbs
+  auto nact = [&](int64_t u) { return (int64_t)(DENSE ? E : count[u]); };
+  auto item_start = [&](int64_t u, int kb) { return (prefix[u] / rbs * kbs + kb * nact(u)) * spe; };
+  const int64_t S = prefix[n_units] / rbs * kbs * spe;
+  const int64_t s_lo = gw * S / nw, s_hi = gw + 1 == nw ? S + 1 : (gw + 1) * S / nw;
+  // first item (in chunk-major order) whose start step is >= s_lo: it lies in
+  // the first chunk whose last item starts at or after s_lo (starts never
+  // decrease; chunks with an empty union share their start step)
+  int64_t u = 0;
+  {
+    int64_t lo = 0, hi = n_units;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (item_start(mid, kbs - 1) >= s_lo) hi = mid; else lo = mid + 1;
+    }
+    u = lo;
+  }
+  int kb = 0;
+  while (u < n_units && item_start(u, kb) < s_lo) ++kb;  // stops before kbs
+  auto in_range = [&](int64_t uu, int kk) { return uu < n_units && item_start(uu, kk) < s_hi; };
 
-  // Step p covers slot p / spe, elements [128 (p % spe), +128) of that expert.
-  auto load = [&](Step<NT>& st, int p) {
-    const int slot = p / spe, j0 = (p % spe) * 128;
-    const int i = DENSE ? slot : list[unit * E + slot];
-    const uint16_t* a_row[4];
+  struct DownItem {
+    int64_t unit;
+    int kb, nsteps;
+  };
+  auto store_y = [&](const DownItem& it, const f32x4 (&acc)[4][NT]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a_row[s] = wo + ((int64_t)i * d + kb + s * 16 + m) * de;
-    const uint16_t* b_row[NT];
+    for (int tl = 0; tl < NT; ++tl) {
+      const int n = m + 16 * tl;
+      if (n >= L) continue;
+      float* yrow = y + (it.unit * L + n) * d + it.kb * 64 + 4 * g;
 #pragma unroll
-    for (int tl = 0; tl < NT; ++tl)
-      b_row[tl] = hbuf + ((unit * E + slot) * L + (m + 16 * tl) % L) * (int64_t)de;
-    load_step<NT>(st, a_row, b_row, j0, g);
+      for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4*>(yrow + s * 16) = acc[s][tl];
+    }
+  };
+  // next item of this wave's range with at least one step; chunks with an
+  // empty union get y = 0 here
+  auto next_item = [&](DownItem& it) -> bool {
+    while (in_range(u, kb)) {
+      it.unit = u;
+      it.kb = kb;
+      it.nsteps = (int)nact(u) * spe;
+      if (++kb == kbs) {
+        kb = 0;
+        ++u;
+      }
+      if (it.nsteps > 0) return true;
+      f32x4 z[4][NT];
+      ring_zero<NT>(z);
+      store_y(it, z);
+    }
+    return false;
+  };
+  auto issue = [&](int slot_buf, const DownItem& it, int k) {
+    const int sl = k / spe, j0 = (k % spe) * kStepK;
+    const int i = DENSE ? sl : list[it.unit * E + sl];
+    const uint16_t* wo = layer_ptr(static_cast<const uint16_t*>(la.w_out), la.stride, it.unit, la.n_layers);
+    const uint16_t* wbase = wo + ((int64_t)i * d + it.kb * 64) * de + j0;
+    const uint16_t* hb = hbuf + ((it.unit * E + sl) * L) * (int64_t)de + j0;
+    uint8_t* buf = bufs + slot_buf * G::kBufBytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int R = 8 * j + (lane >> 3);
+      dma16<kPolicyStream>(wbase + (int64_t)R * de + dma_chunk_elems(R, lane), buf + j * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < G::kBInstr; ++j) {
+      const int n = 8 * j + (lane >> 3);
+      dma16<kPolicyReuse>(hb + (int64_t)(n % L) * de + dma_chunk_elems(n, lane), buf + kABytes + j * 1024);
+    }
   };
 
-  // Two-deep software pipeline over the union's steps, tail peeled.
-  Step<NT> s0, s1;
-  if (n_steps > 0) {
-    load(s0, 0);
-    int p = 0;
-    for (; p + 2 < n_steps; p += 2) {
-      load(s1, p + 1);
-      fence_schedule();
-      mfma_step<NT>(acc, s0);
-      fence_schedule();
-      load(s0, p + 2);
-      fence_schedule();
-      mfma_step<NT>(acc, s1);
-      fence_schedule();
+  DownItem cmp;
+  if (!next_item(cmp)) return;  // nothing issued
+  DownItem iss = cmp, nxt = cmp, last_it = cmp;
+  int k_iss = 0, k_last = 0;
+  bool iss_done = false, has_next = false;
+  auto advance_issue = [&]() {
+    if (!iss_done && k_iss == iss.nsteps) {
+      if (next_item(nxt)) {
+        iss = nxt;
+        has_next = true;
+        k_iss = 0;
+      } else {
+        iss_done = true;
+      }
     }
-    if (p + 1 < n_steps) {
-      load(s1, p + 1);
-      mfma_step<NT>(acc, s0);
-      mfma_step<NT>(acc, s1);
-    } else {
-      mfma_step<NT>(acc, s0);
+    if (!iss_done) {
+      last_it = iss;
+      k_last = k_iss++;
     }
+  };
+  advance_issue();
+  issue(0, last_it, k_last);
+  advance_issue();  // items have >= 2 steps
+  issue(1, last_it, k_last);
+  f32x4 acc[4][NT];
+  ring_zero<NT>(acc);
+  int k_cmp = 0;
+  for (int t = 0;; ++t) {
+    advance_issue();
+    issue((t + 2) % kRingBufs, last_it, k_last);
+    wait_vmcnt<G::kWaitAhead>();
+    ring_mfma<NT>(acc, bufs + (t % kRingBufs) * G::kBufBytes, m, g);
+    __builtin_amdgcn_sched_barrier(0);
+    if (++k_cmp < cmp.nsteps) continue;
+    store_y(cmp, acc);
+    if (!has_next) break;
+    cmp = nxt;
+    has_next = false;
+    k_cmp = 0;
+    ring_zero<NT>(acc);
   }
-
-#pragma unroll
-  for (int tl = 0; tl < NT; ++tl) {
-    const int n = m + 16 * tl;
-    if (n >= L) continue;
-    float* yrow = y + (t0 + n) * d + kb + 4 * g;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4*>(yrow + s * 16) = acc[s][tl];
-  }
+  wait_vmcnt<0>();  // no LDS write may outlive the wave
 }
 
 template <int NT, bool DENSE>
@@ -190,30 +320,22 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
                      const StageEvents& se, hipStream_t s) {
   const int rbs = la.de >> 6;
   plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, DENSE ? la.E : 0, rbs, plan);
+  // persistent grids sized to the resident capacity (one block per CU at this LDS use)
+  int dev = 0, cus = 0, up_cu = 0, dn_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&up_cu, up_mfma_kernel<NT, DENSE>, kBlock, 0);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&dn_cu, down_mfma_kernel<NT, DENSE>, kBlock, 0);
+  if (e != hipSuccess) return e;
+  const int64_t grid_up = (int64_t)cus * (up_cu > 0 ? up_cu : 1);
+  const int64_t grid_dn = (int64_t)cus * (dn_cu > 0 ? dn_cu : 1);
   se.record(0, s);
-  {
-    // resident capacity: blocks per CU at this kernel's register use, times CUs
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, up_mfma_kernel<NT, DENSE>, kBlock, 0);
-    if (e != hipSuccess) return e;
-    const int64_t max_items = units * la.E * rbs;
-    int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
-    const int64_t need = (max_items + 3) / 4;
-    if (grid > need) grid = need;
-    up_mfma_kernel<NT, DENSE><<<dim3((unsigned)grid), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list, plan,
+  up_mfma_kernel<NT, DENSE><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list, plan,
                                                                              hbuf);
-  }
   se.record(1, s);
-  {
-    const int waves = la.d >> 6;
-    const int64_t bpu = (waves + 3) / 4;
-    const int64_t nlog = units * bpu;
-    down_mfma_kernel<NT, DENSE><<<dim3((unsigned)xcd_grid(nlog)), dim3(kBlock), 0, s>>>(la, units, L, count, list,
-                                                                                         bpu, hbuf, y);
-  }
+  down_mfma_kernel<NT, DENSE><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(la, units, L, count, list, plan,
+                                                                               hbuf, y);
   se.record(2, s);
   return hipGetLastError();
 }
@@ -223,6 +345,8 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
 bool forward_mfma_supported(int d, int de, int dtype) {
   return dtype == BLOCKFFN_BF16 && d % 128 == 0 && de % 128 == 0;
 }
+
+size_t forward_mfma_plan_bytes(int64_t units) { return sizeof(int64_t) * (size_t)(units + 1); }
 
 hipError_t launch_forward_mfma(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len,
                                const float* gates, const int32_t* count, const int32_t* list, bool dense,

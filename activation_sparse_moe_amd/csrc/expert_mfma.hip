@@ -51,11 +51,6 @@ __global__ __launch_bounds__(1024) void plan_items_kernel(const int32_t* __restr
   if (tid == 1023) prefix[n_units] = part[1023] * per_slot;
 }
 
-// Wave gw of nw takes the contiguous items [gw total / nw, (gw + 1) total / nw).
-__device__ __forceinline__ void wave_range(int64_t total, int64_t gw, int64_t nw, int64_t* b, int64_t* e) {
-  *b = gw * total / nw;
-  *e = (gw + 1) * total / nw;
-}
 
 struct UpItem {
   int64_t unit;
@@ -70,14 +65,21 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
                                                          const int64_t* __restrict__ prefix,
                                                          uint16_t* __restrict__ hbuf) {
   using G = RingGeom<NT, true>;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRingBufs][G::kBufBytes];
+  // one LDS object: the four waves' rings, then the block's work counter
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRingBufs * G::kBufBytes + 16];
+  unsigned& taken = *reinterpret_cast<unsigned*>(lds + 4 * kRingBufs * G::kBufBytes);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int d = la.d, de = la.de, E = la.E, rbs = de >> 6;
   const int nsteps = d / kStepK;
-  uint8_t* bufs = &ring[w][0][0];
-  int64_t item, item_end;
-  wave_range(prefix[n_units], (int64_t)blockIdx.x * 4 + w, (int64_t)gridDim.x * 4, &item, &item_end);
+  uint8_t* bufs = lds + w * kRingBufs * G::kBufBytes;
+  // the block's items (all of equal size): an equal share of the total
+  const int64_t total = prefix[n_units];
+  const int64_t blk_lo = (int64_t)blockIdx.x * total / gridDim.x;
+  const int64_t item_end = ((int64_t)blockIdx.x + 1) * total / gridDim.x;
+  if (threadIdx.x == 0) taken = 0;
+  __syncthreads();
+  int64_t item = take_item(&taken, blk_lo, lane);
   if (item >= item_end) return;
 
   auto decode = [&](int64_t it_idx) {
@@ -123,20 +125,21 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
 
   UpItem cmp = decode(item), nxt = cmp;
   point(cmp);
-  int64_t item_iss = item;
   int k_iss = 0, k_last = 0;
   bool iss_done = false, has_next = false;
-  issue(0, k_iss);
-  issue(1, ++k_iss);  // nsteps >= 2
-  ++k_iss;
+  for (int b = 0; b < kRingBufs - 1; ++b) {  // nsteps >= kRingBufs - 1
+    issue(b, k_iss);
+    k_last = k_iss++;
+  }
   f32x4 acc[4][NT];
   ring_zero<NT>(acc);
   int k_cmp = 0;
   for (int t = 0;; ++t) {
     // issue the step two ahead, or repeat a valid one past the end of the range
     if (!iss_done && k_iss == nsteps) {
-      if (++item_iss < item_end) {
-        nxt = decode(item_iss);
+      item = take_item(&taken, blk_lo, lane);
+      if (item < item_end) {
+        nxt = decode(item);
         has_next = true;
         point(nxt);
         k_iss = 0;
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
       }
     }
     if (!iss_done) k_last = k_iss++;
-    issue((t + 2) % kRingBufs, k_last);
+    issue((t + kRingBufs - 1) % kRingBufs, k_last);
     wait_vmcnt<G::kWaitAhead>();
     const uint8_t* buf = bufs + (t % kRingBufs) * G::kBufBytes;
     ring_mfma<NT>(acc, buf, m, g);
@@ -188,36 +191,42 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
                                                            const uint16_t* __restrict__ hbuf,
                                                            float* __restrict__ y) {
   using G = RingGeom<NT, false>;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRingBufs][G::kBufBytes];
+  // one LDS object: the four waves' rings, then the block's work counter
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRingBufs * G::kBufBytes + 16];
+  unsigned& taken = *reinterpret_cast<unsigned*>(lds + 4 * kRingBufs * G::kBufBytes);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int d = la.d, de = la.de, E = la.E;
   const int spe = de / kStepK;   // steps per expert
   const int kbs = d >> 6;        // 64-row blocks per chunk
   const int rbs = de >> 6;       // prefix[] counts union size x rbs
-  uint8_t* bufs = &ring[w][0][0];
-  const int64_t gw = (int64_t)blockIdx.x * 4 + w, nw = (int64_t)gridDim.x * 4;
+  uint8_t* bufs = lds + w * kRingBufs * G::kBufBytes;
 
   // step index where item (u, kb) starts; union sizes before u are prefix[u] / rbs
   auto nact = [&](int64_t u) { return (int64_t)(DENSE ? E : count[u]); };
   auto item_start = [&](int64_t u, int kb) { return (prefix[u] / rbs * kbs + kb * nact(u)) * spe; };
-  const int64_t S = prefix[n_units] / rbs * kbs * spe;
-  const int64_t s_lo = gw * S / nw, s_hi = gw + 1 == nw ? S + 1 : (gw + 1) * S / nw;
-  // first item (in chunk-major order) whose start step is >= s_lo: it lies in
-  // the first chunk whose last item starts at or after s_lo (starts never
-  // decrease; chunks with an empty union share their start step)
-  int64_t u = 0;
-  {
+  // first item (chunk-major order) whose start step is >= s: it lies in the
+  // first chunk whose last item starts at or after s (starts never decrease;
+  // chunks with an empty union share their start step)
+  auto first_item_at = [&](int64_t s) -> int64_t {
     int64_t lo = 0, hi = n_units;
     while (lo < hi) {
       const int64_t mid = (lo + hi) >> 1;
-      if (item_start(mid, kbs - 1) >= s_lo) hi = mid; else lo = mid + 1;
+      if (item_start(mid, kbs - 1) >= s) hi = mid; else lo = mid + 1;
     }
-    u = lo;
-  }
-  int kb = 0;
-  while (u < n_units && item_start(u, kb) < s_lo) ++kb;  // stops before kbs
-  auto in_range = [&](int64_t uu, int kk) { return uu < n_units && item_start(uu, kk) < s_hi; };
+    if (lo == n_units) return n_units * kbs;
+    int kb = 0;
+    while (item_start(lo, kb) < s) ++kb;  // stops before kbs
+    return lo * kbs + kb;
+  };
+  // the block's items: those whose first step falls in its equal share of all
+  // steps (the last block also takes items starting at the very end)
+  const int64_t S = prefix[n_units] / rbs * kbs * spe;
+  const int64_t blk_lo = first_item_at((int64_t)blockIdx.x * S / gridDim.x);
+  const int64_t item_end = blockIdx.x + 1 == gridDim.x ? n_units * kbs
+                                                        : first_item_at(((int64_t)blockIdx.x + 1) * S / gridDim.x);
+  if (threadIdx.x == 0) taken = 0;
+  __syncthreads();
 
   struct DownItem {
     int64_t unit;
@@ -233,17 +242,15 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
       for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4*>(yrow + s * 16) = acc[s][tl];
     }
   };
-  // next item of this wave's range with at least one step; chunks with an
+  // next item of the block's range with at least one step; chunks with an
   // empty union get y = 0 here
   auto next_item = [&](DownItem& it) -> bool {
-    while (in_range(u, kb)) {
-      it.unit = u;
-      it.kb = kb;
-      it.nsteps = (int)nact(u) * spe;
-      if (++kb == kbs) {
-        kb = 0;
-        ++u;
-      }
+    for (;;) {
+      const int64_t item = take_item(&taken, blk_lo, lane);
+      if (item >= item_end) return false;
+      it.unit = item / kbs;
+      it.kb = (int)(item % kbs);
+      it.nsteps = (int)nact(it.unit) * spe;
       if (it.nsteps > 0) return true;
       f32x4 z[4][NT];
       ring_zero<NT>(z);
@@ -290,16 +297,16 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
       k_last = k_iss++;
     }
   };
-  advance_issue();
-  issue(0, last_it, k_last);
-  advance_issue();  // items have >= 2 steps
-  issue(1, last_it, k_last);
+  for (int b = 0; b < kRingBufs - 1; ++b) {
+    advance_issue();
+    issue(b, last_it, k_last);
+  }
   f32x4 acc[4][NT];
   ring_zero<NT>(acc);
   int k_cmp = 0;
   for (int t = 0;; ++t) {
     advance_issue();
-    issue((t + 2) % kRingBufs, last_it, k_last);
+    issue((t + kRingBufs - 1) % kRingBufs, last_it, k_last);
     wait_vmcnt<G::kWaitAhead>();
     ring_mfma<NT>(acc, bufs + (t % kRingBufs) * G::kBufBytes, m, g);
     __builtin_amdgcn_sched_barrier(0);

@@ -12,6 +12,11 @@
 // Two steps are always in flight ahead of the one being multiplied, so the
 // wait before a step is a constant vmcnt.
 //
+// Work items are shared out in two levels: each block owns a contiguous,
+// statically balanced range of items, and the block's waves take items from
+// that range through an LDS counter (an LDS atomic waits on lgkmcnt, not on
+// vmcnt, so taking work never drains the weight stream).
+//
 // Operand layout (v_mfma_f32_16x16x32_bf16, checked on gfx950): lane l
 // supplies row l % 16 of A and column l % 16 of B with k elements
 // 8 (l / 16) .. +7 of the 32-wide block, and receives rows 4 (l / 16) + r
@@ -35,11 +40,11 @@ constexpr unsigned kPolicyReuse = 0;
 // One buffer: A rows, then B rows, then (GATES) 64 fp32 per-token values.
 template <int NT, bool GATES>
 struct RingGeom {
-  static constexpr int kBInstr = 2 * NT;                     // 16 NT token rows, 8 per instruction
+  static constexpr int kBInstr = 2 * NT;  // 16 NT token rows, 8 per instruction
   static constexpr int kGateOff = kABytes + kBInstr * 1024;
   static constexpr int kBufBytes = kGateOff + (GATES ? 256 : 0);
   static constexpr int kLoadsPerStep = 8 + kBInstr + (GATES ? 1 : 0);
-  static constexpr int kWaitAhead = 2 * kLoadsPerStep;       // loads of the two steps in flight
+  static constexpr int kWaitAhead = (kRingBufs - 1) * kLoadsPerStep;  // loads of the steps in flight
 };
 
 __device__ __forceinline__ int ring_swz(int row) { return (row >> 1) & 7; }
@@ -94,6 +99,21 @@ __device__ __forceinline__ void ring_mfma(f32x4 (&acc)[4][NT], const uint8_t* bu
         acc[s][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring_bf16x8(a[s]), ring_bf16x8(b[tl]), acc[s][tl], 0,
                                                              0, 0);
   }
+}
+
+// Next item of the block's range for this wave: LDS counter, broadcast.  The
+// counter sits outside every ring buffer, so the atomic cannot race with the
+// weight DMA; it is written as assembly (with its own lgkmcnt wait, so the
+// result register is complete when the block ends) because the compiler
+// cannot prove that and would otherwise drain every in-flight DMA first.
+__device__ __forceinline__ int64_t take_item(unsigned* counter, int64_t lo, int lane) {
+  unsigned v = 0;
+  if (lane == 0) {
+    const unsigned addr = (unsigned)(uintptr_t)(lvoid_t*)counter;
+    const unsigned one = 1u;
+    asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr), "v"(one));
+  }
+  return lo + (int64_t)__builtin_amdgcn_readfirstlane(__shfl(v, 0, kWave));
 }
 
 template <int NT>

@@ -91,8 +91,12 @@ enum class Path { kGemv, kMfma, kGrouped };
 
 // Resolves `mode` to a kernel family; returns a status code.
 int resolve_mode(const blockffn_layer* ly, int32_t chunk_len, int32_t mode, Path* path, bool* dense) {
+  // The matrix-core path streams each chunk's union once for all its tokens;
+  // at chunk_len 1 its idle token columns cost nothing (the kernels are bound
+  // by weight bytes), so it is the default wherever the shapes allow it.
   const bool mfma_ok = bffn::forward_mfma_supported(ly->d, ly->d_expert, ly->dtype);
-  const bool auto_mfma = mfma_ok && chunk_len >= 8;
+  const bool auto_mfma = mfma_ok;
+  (void)chunk_len;
   *dense = false;
   switch (mode) {
     case BLOCKFFN_MODE_AUTO:
@@ -112,7 +116,7 @@ int resolve_mode(const blockffn_layer* ly, int32_t chunk_len, int32_t mode, Path
       return BLOCKFFN_OK;
     case BLOCKFFN_MODE_GROUPED:
       if (!bffn::grouped_supported(ly->d, ly->d_expert, ly->dtype))
-        return fail(BLOCKFFN_ERR_MODE, "GROUPED needs bf16 with d and d_expert multiples of 128");
+        return fail(BLOCKFFN_ERR_MODE, "GROUPED needs bf16, d a multiple of 128 and d_expert 128 or 256");
       *path = Path::kGrouped;
       return BLOCKFFN_OK;
     default:
@@ -194,6 +198,8 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, 
   if (int r = resolve_mode(layer, chunk_len, mode, &path, &dense)) return r;
   if (path == Path::kGrouped && n_layers != 1)
     return fail(BLOCKFFN_ERR_LAYERS, "GROUPED runs one batch through one layer (n_layers %d)", n_layers);
+  if (path == Path::kGrouped && n_tokens * layer->n_experts > INT32_MAX)
+    return fail(BLOCKFFN_ERR_SHAPE, "GROUPED indexes pairs with 32 bits: n_tokens x n_experts must stay below 2^31");
   if (n_tokens == 0) return BLOCKFFN_OK;
   if (!x || !gates || !y) return fail(BLOCKFFN_ERR_NULL, "x, gates and y must be non-NULL");
   if (!dense && path != Path::kGrouped && (!active_count || !active_list))

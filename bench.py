@@ -107,6 +107,7 @@ class StepRunner:
         # units per call: never more than the layer copies, so no two units of
         # one launch stream the same weights
         self.sub_units = min(C, cfg.replicas) if cfg.replicas > 1 else C
+        self.n_sub = (C + self.sub_units - 1) // self.sub_units
         sub_T = self.sub_units * L
         self.ws = {}
         for m in {mode, "dense"}:
@@ -117,9 +118,9 @@ class StepRunner:
     def step(self, mode: str, ev=None, stage_events=None):
         """route -> union -> forward -> stats, in sub-batches of at most one
         unit per layer copy.  ev: 4 torch events recorded after route, union,
-        forward and stats of the last sub-batch; stage_events: ctypes array of
-        hipEvent_t the library records around the forward's timed kernels
-        (sub-batch 0 only)."""
+        forward and stats of the last sub-batch; stage_events: one ctypes array
+        of hipEvent_t per sub-batch, which the library records around that
+        sub-batch's forward kernels."""
         B, cfg = self.B, self.cfg
         L, E = cfg.chunk_len, cfg.n_experts
         C = cfg.n_tokens // L
@@ -136,10 +137,10 @@ class StepRunner:
             B.blockffn_chunk_union(E, m, L, chunk_masks=um, active_count=cnt, active_list=lst)
             if ev is not None and last:
                 ev[1].record()
-            if stage_events is not None and b == 0:
-                self.lib.blockffn_set_stage_events(ctypes.cast(stage_events, ctypes.c_void_p), self.n_stage)
+            if stage_events is not None:
+                self.lib.blockffn_set_stage_events(ctypes.cast(stage_events[b], ctypes.c_void_p), self.n_stage)
             B.blockffn_forward(self.dl, x, L, g, cnt, lst, mode=mode, workspace=self.ws[mode], y=y)
-            if stage_events is not None and b == 0:
+            if stage_events is not None:
                 self.lib.blockffn_set_stage_events(None, 0)
             if ev is not None and last:
                 ev[2].record()
@@ -155,14 +156,16 @@ class StepRunner:
         E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
         evs = [[E() for _ in range(4)] for _ in range(steps)]
         ns = self.n_stage if mode == self.mode else 3
-        stage = [[E() for _ in range(ns)] for _ in range(steps)]
+        nb = self.n_sub
+        stage = [[[E() for _ in range(ns)] for _ in range(nb)] for _ in range(steps)]
         # record every event once so that its hipEvent exists before the
         # library is handed the raw handles
-        for row in stage:
-            for e in row:
-                e.record()
+        for per_step in stage:
+            for row in per_step:
+                for e in row:
+                    e.record()
         torch.cuda.synchronize()
-        handles = [(ctypes.c_void_p * ns)(*[e.cuda_event for e in row]) for row in stage]
+        handles = [[(ctypes.c_void_p * ns)(*[e.cuda_event for e in row]) for row in per_step] for per_step in stage]
         start, end = E(), E()
         torch.cuda.synchronize()
         start.record()
@@ -179,12 +182,12 @@ class StepRunner:
         per = {"route": [], "union": [], "up": [], "down": [], "stats": [], "forward": []}
         if ns > 3:
             per["combine"] = []
-        nb = (self.cfg.n_tokens // self.cfg.chunk_len + self.sub_units - 1) // self.sub_units
         for k in range(steps):
-            per["up"].append(stage[k][0].elapsed_time(stage[k][1]) * nb)
-            per["down"].append(stage[k][1].elapsed_time(stage[k][2]) * nb)
+            # kernel time per step: the sum over the step's sub-batch launches
+            per["up"].append(sum(r[0].elapsed_time(r[1]) for r in stage[k]))
+            per["down"].append(sum(r[1].elapsed_time(r[2]) for r in stage[k]))
             if ns > 3:
-                per["combine"].append(stage[k][2].elapsed_time(stage[k][3]) * nb)
+                per["combine"].append(sum(r[2].elapsed_time(r[3]) for r in stage[k]))
             if nb == 1:
                 per["route"].append(starts[k].elapsed_time(evs[k][0]))
                 per["union"].append(evs[k][0].elapsed_time(evs[k][1]))
@@ -212,7 +215,8 @@ class StepRunner:
         C = T // L
         W = (E + 63) // 64
         U = int(cnt.sum())
-        hid = 2 if self.mode in ("auto", "chunk_mfma") and cfg.dtype == "bf16" and L >= 8 else 4
+        mfma = cfg.dtype == "bf16" and d % 128 == 0 and de % 128 == 0  # the library's matrix-core path
+        hid = 2 if self.mode in ("auto", "chunk_mfma", "dense") and mfma else 4
         b = {
             "route": C * (E * d * es + E * 4) + T * d * es + T * E * 4 + T * W * 8,
             "union": T * W * 8 + C * (W * 8 + 4 + E * 4),
@@ -352,18 +356,23 @@ def main(argv=None) -> int:
         roofline = {"bound": "mfma", "kernel": f"grouped_{dom} ({mode})", "achieved": round(achieved, 1),
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                     "traffic": profiled_traffic(f"grouped_{dom}", cfg.name),
-                    "algorithmic_flops_per_launch": fl, "avg_launch_ms": round(avg[dom], 5)}
+                    "algorithmic_flops_per_launch": fl, "avg_launch_ms": round(avg[dom], 5), "launches_per_step": 1}
     else:
         achieved = bytes_per[dom] / (avg[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": f"{kernel_name} ({mode})", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": profiled_traffic(kernel_name, cfg.name),
-                    "algorithmic_bytes_per_launch": bytes_per[dom], "avg_launch_ms": round(avg[dom], 5)}
+                    "algorithmic_bytes_per_launch": bytes_per[dom] // runner.n_sub,
+                    "avg_launch_ms": round(avg[dom] / runner.n_sub, 5), "launches_per_step": runner.n_sub}
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, runner.layer, runner.x_host, args.cpu_seconds)
 
+    if grouped:
+        # each expert's weights are read once for the whole batch
+        fm = runner.flop_model()
+        step_alg = fm["layer_bytes"] + fm["x_bytes"] + fm["y_bytes"]
     step_gbs = step_alg / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -70,10 +70,10 @@ extern "C" {
 #define BLOCKFFN_BF16 1 /* bfloat16: the upper 16 bits of a binary32 */
 
 /* blockffn_forward modes. */
-#define BLOCKFFN_MODE_AUTO 0       /* bf16 with chunk_len >= 8 -> CHUNK_MFMA, else GEMV */
+#define BLOCKFFN_MODE_AUTO 0       /* CHUNK_MFMA where supported (bf16, d and d_expert % 128 == 0), else GEMV */
 #define BLOCKFFN_MODE_GEMV 1       /* vector-ALU streaming of the active experts (any dtype) */
 #define BLOCKFFN_MODE_CHUNK_MFMA 2 /* matrix-core tiles over each chunk's union (bf16) */
-#define BLOCKFFN_MODE_GROUPED 3    /* token-expert pairs grouped by expert (bf16, one layer) */
+#define BLOCKFFN_MODE_GROUPED 3    /* token-expert pairs grouped by expert (bf16, d % 128 == 0, d_expert 128 or 256, one layer) */
 #define BLOCKFFN_MODE_DENSE 4      /* every expert on every token (the comparison path) */
 
 /* Status codes. */
@@ -166,6 +166,8 @@ int blockffn_chunk_union(int32_t n_experts, const uint64_t* token_masks, int64_t
  * (token, expert) pair with a positive gate is grouped by expert, each
  * expert's weights are read once for all of its tokens in MFMA GEMMs, and
  * each token's per-expert partial rows are summed in ascending expert order.
+ * It needs bf16, d a multiple of 128, d_expert 128 or 256 (MODE otherwise)
+ * and n_tokens x n_experts below 2^31 (SHAPE otherwise).
  * Errors: NULL, SHAPE, DTYPE, CHUNK, WORKSPACE, MODE, ALIGN, LAYERS, HIP.
  */
 int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,

@@ -177,6 +177,7 @@ def test_forward_rejects_bad_arguments(lib):
     assert _forward(lib, _layer(), T=20) == _capi.ERR_CHUNK
     assert _forward(lib, _layer(dtype=0), mode=_capi.MODE_GROUPED) == _capi.ERR_MODE     # GROUPED needs bf16
     assert _forward(lib, _layer(d_expert=64), mode=_capi.MODE_GROUPED) == _capi.ERR_MODE
+    assert _forward(lib, _layer(d_expert=384), mode=_capi.MODE_GROUPED) == _capi.ERR_MODE   # d_expert 128 or 256
     assert _forward(lib, _layer(layer_stride=1 << 20), mode=_capi.MODE_GROUPED, n_layers=2) == _capi.ERR_LAYERS
     assert _forward(lib, _layer(), mode=_capi.MODE_GROUPED, ws_bytes=4096) == _capi.ERR_WORKSPACE
 
@@ -189,6 +190,8 @@ def test_workspace_size(lib):
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, _capi.MODE_CHUNK_MFMA) == \
         T * 64 * 128 * 2 + r256(8 * (T // 8 + 1))
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 1, _capi.MODE_AUTO) == \
+        T * 64 * 128 * 2 + r256(8 * (T + 1))
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 1, _capi.MODE_GEMV) == \
         T * 64 * 128 * 4 + r256(8 * (T + 1))
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 3, _capi.MODE_AUTO) == 0   # ragged
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, 99) == 0

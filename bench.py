@@ -48,11 +48,23 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
-def source_digest() -> str:
+# The sources each profiled kernel is built from: its counter summary stays
+# valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "expert_up": ("expert_mfma.hip", "lds_stream.h", "bffn_internal.h"),
+    "expert_down": ("expert_mfma.hip", "lds_stream.h", "bffn_internal.h"),
+    "grouped_up": ("grouped.hip", "bffn_internal.h"),
+    "grouped_down": ("grouped.hip", "bffn_internal.h"),
+}
+
+
+def source_digest(kernel: str = None) -> str:
+    """sha256 prefix of the library sources (all of them, or those of one kernel)."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode())
+    names = KERNEL_SOURCES[kernel] if kernel else [os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "*"))]
+    for name in sorted(names):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -69,7 +81,7 @@ def profiled_traffic(kernel: str, workload: str):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_digest") != source_digest():
+    if vals.get("source_digest") != source_digest(kernel):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])

@@ -1,4 +1,6 @@
-// Expert streaming on the matrix cores: the chunk path (bf16, L >= 8).
+// Expert streaming on the matrix cores: the chunk path (bf16, any chunk length;
+// at L = 1 the idle token columns cost nothing, the kernels being bound by
+// weight bytes).
 // (BlockFFN write-up, lsdiaocha.cn, §4 acceleration kernel: multiply only by
 // the experts in the union of the chunk's activations, batching the chunk's
 // tokens, then mask the irrelevant activations; §7: an outer loop over the
@@ -15,10 +17,12 @@
 // non-temporal policy through a wave-private LDS ring (lds_stream.h): full
 // 128-byte lines per load instruction, two 64-element steps in flight, the
 // step stream continuing across work items.  Both kernels are persistent
-// (one block per CU); each wave takes a contiguous, statically balanced range
+// (one block per CU); each block owns a contiguous, statically balanced range
 // of work items (equal counts for the up items, equal step totals for the
-// variable-length down items), decoded with scalar loads only, so nothing in
-// the loop waits on a returning memory operation except the weight stream.
+// variable-length down items) and its waves take items from that range
+// through an LDS counter.  Items are decoded with scalar loads only, so
+// nothing in the loop waits on a returning memory operation except the
+// weight stream.
 #include "lds_stream.h"
 
 namespace bffn {

@@ -1,4 +1,4 @@
-"""CPU oracle of the BlockFFN layer forward -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle of the BlockFFN layer (forward and backward) -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never loads it and
@@ -69,10 +69,12 @@ def _load():
             lib.oracle_forward_dense.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, vp]
             lib.oracle_union.argtypes = [i32, vp, i64, i32, vp, vp, vp]
             lib.oracle_stats.argtypes = [i32, vp, i64, i32, ctypes.POINTER(OracleStats)]
+            lib.oracle_backward.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, dbl, vp, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, vp, vp, vp, vp]
             lib.oracle_num_threads.argtypes = []
             for name in ("oracle_route", "oracle_expert", "oracle_forward_tokens",
                          "oracle_forward_chunks", "oracle_forward_dense", "oracle_union",
-                         "oracle_stats", "oracle_num_threads"):
+                         "oracle_stats", "oracle_backward", "oracle_num_threads"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -211,3 +213,32 @@ def layer_forward(layer, x, chunk_len: int):
     um, cnt, lst = chunk_union(m, layer.n_experts, chunk_len)
     y = forward_tokens(x, layer.w_in, layer.w_out, g, m)
     return dict(z=z, g=g, mask=m, umask=um, count=cnt, list=lst, y=y)
+
+
+def backward(x, w_router, b_router, rms_scale, eps, w_in, w_out, dy, expert_sel=None, token_sel=None) -> dict:
+    """Gradients of sum(y * dy) with respect to x and every parameter (float64).
+
+    Returns dx[T][d], dw_router[E][d], db[E], ds[E], dw_in[E][de][d],
+    dw_out[E][d][de], and the per-pair dz[T][E] and dg[T][E].  expert_sel /
+    token_sel (bool arrays of length E / T) restrict which dw_in / dw_out
+    blocks and which dx rows are computed; the rest stay zero.
+    """
+    x, w_router, w_in, w_out = _c(x), _c(w_router), _c(w_in), _c(w_out)
+    code = _dtype_code(x)
+    assert _dtype_code(w_router) == code and _dtype_code(w_in) == code and _dtype_code(w_out) == code
+    T, d = x.shape
+    E, de, d2 = w_in.shape
+    assert d2 == d and w_out.shape == (E, d, de) and w_router.shape == (E, d)
+    dy = _c(dy, np.float32)
+    assert dy.shape == (T, d)
+    b = _c(b_router, np.float32)
+    s = _c(rms_scale, np.float32)
+    es = None if expert_sel is None else _c(np.asarray(expert_sel, dtype=bool).astype(np.uint8))
+    ts = None if token_sel is None else _c(np.asarray(token_sel, dtype=bool).astype(np.uint8))
+    out = dict(dx=np.empty((T, d)), dw_router=np.empty((E, d)), db=np.empty(E), ds=np.empty(E),
+               dw_in=np.empty((E, de, d)), dw_out=np.empty((E, d, de)), dz=np.empty((T, E)), dg=np.empty((T, E)))
+    _check(_load().oracle_backward(d, E, de, code, _p(x), T, _p(w_router), _p(b), _p(s), float(eps), _p(w_in),
+                                   _p(w_out), _p(dy), _p(es), _p(ts), _p(out["dx"]), _p(out["dw_router"]),
+                                   _p(out["db"]), _p(out["ds"]), _p(out["dw_in"]), _p(out["dw_out"]), _p(out["dz"]),
+                                   _p(out["dg"])), "oracle_backward")
+    return out

@@ -1,5 +1,5 @@
 /*
- * blockffn_oracle.c -- plain, slow CPU oracle of the BlockFFN layer forward.
+ * blockffn_oracle.c -- plain, slow CPU oracle of the BlockFFN layer (forward and backward).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
  * load this file: only the tests, the smoke check and the CPU-baseline leg of
@@ -19,6 +19,10 @@
  *   chunk    U_c = union of the active sets of the L tokens of chunk c
  *   stats    token-level sparsity, chunk-level sparsity, experts-per-token
  *            histogram, consecutive-token expert reuse
+ *   backward the gradients of a scalar loss with respect to x and every
+ *            parameter, by the chain rule through the definitions above
+ *            (the write-up §2 calls the ReLU + RMSNorm router fully
+ *            differentiable; the abstract: differentiable, flexible routing)
  *
  * Every sum is accumulated in double, in the plain index order written
  * below, with no blocking or reordering.  Inputs are read in their stored
@@ -312,4 +316,177 @@ int oracle_stats(int32_t E, const uint64_t *mask, int64_t T, int32_t L, oracle_s
   }
   free(u);
   return 0;
+}
+
+/*
+ * Layer backward: the chain rule through the forward above, for a scalar loss
+ * whose gradient with respect to y is dy[T][d] (binary32).  Per token t, with
+ * r = (ms + eps)^(-1/2) and a_i = max(z_i, 0):
+ *
+ *   for each active i:  u = W_in[i] x,  sig = 1 / (1 + e^-u),  h = u sig,
+ *                       q = W_out[i]^T dy,  dg_i = q . h
+ *                       du = g_i q sig (1 + u (1 - sig))    (Swish' = sig (1 + u (1 - sig)))
+ *                       dW_out[i] += g_i dy h^T,  dW_in[i] += du x^T,  dx += W_in[i]^T du
+ *   ds_i += dg_i a_i r
+ *   dr    = sum_i dg_i s_i a_i,   dms = -dr r^3 / 2           (r = (ms + eps)^(-1/2))
+ *   da_i  = dg_i s_i r + dms 2 a_i / E                        (ms = sum_i a_i^2 / E)
+ *   dz_i  = da_i [z_i > 0]                                    (ReLU)
+ *   db   += dz,  dW_r += dz x^T,  dx += W_r^T dz
+ *
+ * Inactive experts have a_i = g_i = 0 and dz_i = 0: they contribute nothing,
+ * so only active pairs are visited.  The gates and pattern are recomputed
+ * here exactly as oracle_route computes them.
+ *
+ * Outputs are double and overwritten: dx[T][d], dw_router[E][d], db[E],
+ * ds[E], dw_in[E][de][d], dw_out[E][d][de], dz[T][E] and dg[T][E] (dg_i for
+ * active pairs, 0 elsewhere).  expert_sel (E bytes) and token_sel (T bytes)
+ * may restrict which dw_in / dw_out blocks and which dx rows are computed
+ * (NULL = all; unselected entries are left at 0).  Every sum over tokens runs
+ * in ascending token order and every sum over experts in ascending expert
+ * order; the per-pair quantities are recomputed where they are needed.
+ */
+/* One active pair (t, i) of the backward: u = W_in[i] x_t, h = Swish(u),
+ * q = W_out[i]^T dy_t and du = g q Swish'(u) (d_e values each). */
+static void pair_backward(int d, int de, int dtype, const void *x, int64_t t, const void *w_in,
+                          const void *w_out, int i, const float *dy, double g, double *h, double *q,
+                          double *du) {
+  for (int j = 0; j < de; ++j) {
+    double u = 0.0;
+    for (int k = 0; k < d; ++k)
+      u += widen(w_in, ((int64_t)i * de + j) * d + k, dtype) * widen(x, t * d + k, dtype);
+    double qj = 0.0;
+    for (int k = 0; k < d; ++k) qj += widen(w_out, ((int64_t)i * d + k) * de + j, dtype) * (double)dy[t * d + k];
+    const double sig = 1.0 / (1.0 + exp(-u));
+    h[j] = u * sig;
+    q[j] = qj;
+    du[j] = g * qj * sig * (1.0 + u * (1.0 - sig));
+  }
+}
+
+int oracle_backward(int32_t d, int32_t E, int32_t de, int32_t dtype, const void *x, int64_t T,
+                    const void *w_router, const float *b_router, const float *rms_scale, double eps,
+                    const void *w_in, const void *w_out, const float *dy,
+                    const uint8_t *expert_sel, const uint8_t *token_sel,
+                    double *dx, double *dw_router, double *db, double *ds, double *dw_in, double *dw_out,
+                    double *dz, double *dg) {
+  if (d <= 0 || E <= 0 || de <= 0 || T < 0) return -1;
+  const int W = mask_words(E);
+  double *z = (double *)malloc(sizeof(double) * (size_t)(T * E + 1));
+  double *g = (double *)malloc(sizeof(double) * (size_t)(T * E + 1));
+  double *dsc = (double *)malloc(sizeof(double) * (size_t)(T * E + 1));
+  uint64_t *m = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(T * W + 1));
+  if (!z || !g || !dsc || !m) {
+    free(z); free(g); free(dsc); free(m);
+    return -2;
+  }
+  oracle_route(d, E, dtype, x, T, w_router, b_router, rms_scale, eps, z, g, m);
+  int err = 0;
+
+#pragma omp parallel
+  {
+    double *h = (double *)malloc(sizeof(double) * (size_t)de);
+    double *q = (double *)malloc(sizeof(double) * (size_t)de);
+    double *du = (double *)malloc(sizeof(double) * (size_t)de);
+    const int ok = h && q && du;
+    if (!ok) {
+#pragma omp atomic write
+      err = -2;
+    }
+
+    /* 1. per token: dg for the active pairs, then the RMSNorm and ReLU backward */
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      double ms = 0.0;
+      for (int i = 0; i < E; ++i) {
+        const double a = z[t * E + i] > 0.0 ? z[t * E + i] : 0.0;
+        ms += a * a;
+      }
+      const double r = 1.0 / sqrt(ms / (double)E + eps); /* the gates' 1 / RMS */
+      double dr = 0.0;
+      for (int i = 0; i < E; ++i) {
+        double dgi = 0.0;
+        if (mask_bit(m + t * W, i) && ok) {
+          pair_backward(d, de, dtype, x, t, w_in, w_out, i, dy, g[t * E + i], h, q, du);
+          for (int j = 0; j < de; ++j) dgi += q[j] * h[j];
+        }
+        const double a = z[t * E + i] > 0.0 ? z[t * E + i] : 0.0;
+        const double s = rms_scale ? (double)rms_scale[i] : 1.0;
+        dg[t * E + i] = dgi;
+        dsc[t * E + i] = dgi * a * r;
+        dr += dgi * s * a;
+      }
+      const double dms = -0.5 * dr * r * r * r;
+      for (int i = 0; i < E; ++i) {
+        const double a = z[t * E + i] > 0.0 ? z[t * E + i] : 0.0;
+        const double s = rms_scale ? (double)rms_scale[i] : 1.0;
+        const double da = dg[t * E + i] * s * r + dms * 2.0 * a / (double)E;
+        dz[t * E + i] = z[t * E + i] > 0.0 ? da : 0.0;
+      }
+    }
+
+    /* 2. router parameter gradients: sums over tokens, ascending */
+#pragma omp for schedule(static)
+    for (int i = 0; i < E; ++i) {
+      double sb = 0.0, ss = 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        sb += dz[t * E + i];
+        ss += dsc[t * E + i];
+      }
+      db[i] = sb;
+      ds[i] = ss;
+      for (int k = 0; k < d; ++k) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t) acc += dz[t * E + i] * widen(x, t * d + k, dtype);
+        dw_router[(int64_t)i * d + k] = acc;
+      }
+    }
+
+    /* 3. expert weight gradients: per expert, sums over its active tokens, ascending */
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < E; ++i) {
+      double *gi = dw_in + (int64_t)i * de * d;
+      double *go = dw_out + (int64_t)i * d * de;
+      for (int64_t n = 0; n < (int64_t)de * d; ++n) gi[n] = go[n] = 0.0;
+      if ((expert_sel && !expert_sel[i]) || !ok) continue;
+      for (int64_t t = 0; t < T; ++t) {
+        if (!mask_bit(m + t * W, i)) continue;
+        const double gti = g[t * E + i];
+        pair_backward(d, de, dtype, x, t, w_in, w_out, i, dy, gti, h, q, du);
+        for (int k = 0; k < d; ++k)
+          for (int j = 0; j < de; ++j) go[(int64_t)k * de + j] += gti * (double)dy[t * d + k] * h[j];
+        for (int j = 0; j < de; ++j)
+          for (int k = 0; k < d; ++k) gi[(int64_t)j * d + k] += du[j] * widen(x, t * d + k, dtype);
+      }
+    }
+
+    /* 4. input gradient: per token, experts ascending, then the router term */
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      double *dxt = dx + t * d;
+      for (int k = 0; k < d; ++k) dxt[k] = 0.0;
+      if ((token_sel && !token_sel[t]) || !ok) continue;
+      for (int i = 0; i < E; ++i) {
+        if (!mask_bit(m + t * W, i)) continue;
+        pair_backward(d, de, dtype, x, t, w_in, w_out, i, dy, g[t * E + i], h, q, du);
+        for (int k = 0; k < d; ++k) {
+          double acc = 0.0;
+          for (int j = 0; j < de; ++j) acc += widen(w_in, ((int64_t)i * de + j) * d + k, dtype) * du[j];
+          dxt[k] += acc;
+        }
+      }
+      for (int k = 0; k < d; ++k) {
+        double acc = 0.0;
+        for (int i = 0; i < E; ++i) acc += dz[t * E + i] * widen(w_router, (int64_t)i * d + k, dtype);
+        dxt[k] += acc;
+      }
+    }
+    free(h);
+    free(q);
+    free(du);
+  }
+  free(z);
+  free(g);
+  free(dsc);
+  free(m);
+  return err;
 }

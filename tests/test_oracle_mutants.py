@@ -6,7 +6,10 @@ suite must fail.  The mistakes are the ones a reader of the pages could make:
 a non-strict ReLU threshold, a wrong RMS denominator, epsilon outside the
 root, a different activation, a transposed matrix, a dropped gate, AND
 instead of OR for the union, a chunk boundary off by one, a wrong bf16
-widening, a wrong reuse denominator, a flipped bias sign.
+widening, a wrong reuse denominator, a flipped bias sign; and in the backward
+a dropped or sign-flipped RMSNorm term, a wrong Swish derivative, a dropped
+gate, gradients taken through inactive pairs, a wrong scale gradient, a dropped router term of
+dx, a missing gate in dW_out.
 """
 import os
 import subprocess
@@ -35,7 +38,26 @@ MUTANTS = {
     "reuse_denominator": ("out->reuse_den += count_bits(mask + (t - 1) * W, E);",
                           "out->reuse_den += count_bits(mask + t * W, E);"),
     "bias_sign": ("if (b_router) acc += (double)b_router[i];", "if (b_router) acc -= (double)b_router[i];"),
+    # the backward
+    "bwd_rms_term_dropped": ("const double da = dg[t * E + i] * s * r + dms * 2.0 * a / (double)E;",
+                             "const double da = dg[t * E + i] * s * r;"),
+    "bwd_rms_denominator": ("const double r = 1.0 / sqrt(ms / (double)E + eps);",
+                            "const double r = 1.0 / sqrt(ms / (double)(E + 1) + eps);"),
+    "bwd_rms_term_sign": ("const double dms = -0.5 * dr * r * r * r;", "const double dms = 0.5 * dr * r * r * r;"),
+    "bwd_swish_derivative": ("du[j] = g * qj * sig * (1.0 + u * (1.0 - sig));", "du[j] = g * qj * sig;"),
+    "bwd_gate_dropped": ("du[j] = g * qj * sig * (1.0 + u * (1.0 - sig));",
+                         "du[j] = qj * sig * (1.0 + u * (1.0 - sig));"),
+    # (dropping the ReLU mask on dz alone is an equivalent change: inactive
+    # pairs have a = 0 and are never visited, so their dg and da are 0; the
+    # mistake that matters is visiting them)
+    "bwd_inactive_pairs_visited": ("if (mask_bit(m + t * W, i) && ok) {", "if (ok) {"),
+    "bwd_scale_grad_uses_gate": ("dsc[t * E + i] = dgi * a * r;", "dsc[t * E + i] = dgi * g[t * E + i];"),
+    "bwd_router_dx_dropped": ("for (int i = 0; i < E; ++i) acc += dz[t * E + i] * widen(w_router,",
+                              "for (int i = 0; i < E; ++i) acc += 0.0 * dz[t * E + i] * widen(w_router,"),
+    "bwd_w_out_grad_gate_dropped": ("go[(int64_t)k * de + j] += gti * (double)dy[t * d + k] * h[j];",
+                                    "go[(int64_t)k * de + j] += (double)dy[t * d + k] * h[j];"),
 }
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_backward_pins.py")
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -51,6 +73,6 @@ def test_pins_catch_planted_mistake(name):
                         "-o", so, c, "-lm"], check=True)
         env = dict(os.environ, BLOCKFFN_ORACLE_LIB=so)
         r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                            os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                            *[os.path.join(ROOT, "tests", f) for f in PIN_FILES]],
                            cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
         assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"

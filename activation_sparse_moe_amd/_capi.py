@@ -24,6 +24,7 @@ ERR_MODE, ERR_ALIGN, ERR_LAYERS, ERR_HIP = -6, -7, -8, -9
 
 # Every symbol include/blockffn.h declares.
 EXPORTS = ("blockffn_route", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats",
+           "blockffn_backward", "blockffn_backward_workspace_size",
            "blockffn_set_stage_events", "blockffn_workspace_size", "blockffn_status_string",
            "blockffn_last_error", "blockffn_version")
 
@@ -44,6 +45,11 @@ class BlockffnStats(ctypes.Structure):
         ("chunk_len", ctypes.c_int64), ("active_pairs", ctypes.c_int64), ("union_sum", ctypes.c_int64),
         ("reuse_num", ctypes.c_int64), ("reuse_den", ctypes.c_int64), ("hist", ctypes.c_int64 * 129),
     ]
+
+
+class BlockffnGrads(ctypes.Structure):
+    _fields_ = [("d_w_router", ctypes.c_void_p), ("d_b_router", ctypes.c_void_p), ("d_rms_scale", ctypes.c_void_p),
+                ("d_w_in", ctypes.c_void_p), ("d_w_out", ctypes.c_void_p)]
 
 
 class BlockFFNError(RuntimeError):
@@ -72,7 +78,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.blockffn_chunk_union.argtypes = [i32, vp, i64, i32, vp, vp, vp, vp]
         lib.blockffn_forward.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, i32, vp, sz, vp, vp]
         lib.blockffn_sparsity_stats.argtypes = [i32, vp, i64, i32, vp, vp]
-        for f in ("blockffn_route", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats"):
+        lib.blockffn_backward.argtypes = [lp, vp, i64, vp, vp, vp, sz, vp, ctypes.POINTER(BlockffnGrads), vp]
+        lib.blockffn_backward_workspace_size.argtypes = [lp, i64]
+        lib.blockffn_backward_workspace_size.restype = sz
+        for f in ("blockffn_route", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats",
+                  "blockffn_backward"):
             getattr(lib, f).restype = ctypes.c_int
         lib.blockffn_set_stage_events.argtypes = [vp, i32]
         lib.blockffn_set_stage_events.restype = ctypes.c_int

@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import _capi
-from ._capi import BF16, F32, MODES, BlockffnLayer, check, load
+from ._capi import BF16, F32, MODES, BlockffnGrads, BlockffnLayer, check, load
 
 _ALIGN = 256
 _STATS_WORDS = 8 + 129
@@ -207,6 +207,42 @@ def blockffn_forward(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, gates:
                                   _ptr(active_list), m, _ptr(workspace), workspace.numel(), _ptr(y),
                                   _stream(stream)), "blockffn_forward")
     return y
+
+
+def blockffn_backward_workspace_size(layer: DeviceLayer, n_tokens: int) -> int:
+    desc = layer.descriptor()
+    return int(load().blockffn_backward_workspace_size(ctypes.byref(desc), n_tokens))
+
+
+def alloc_backward_workspace(layer: DeviceLayer, n_tokens: int) -> torch.Tensor:
+    nbytes = blockffn_backward_workspace_size(layer, n_tokens)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=layer.device)
+
+
+def blockffn_backward(layer: DeviceLayer, x: torch.Tensor, preact: torch.Tensor, dy: torch.Tensor,
+                      workspace: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
+                      grads: Optional[dict] = None, stream=None) -> dict:
+    """Layer backward -> dict(dx, d_w_router, d_b_router, d_rms_scale, d_w_in, d_w_out), all fp32."""
+    T = x.shape[0]
+    E, d, de = layer.n_experts, layer.d, layer.d_expert
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if grads is None:
+        grads = dict(d_w_router=torch.empty((E, d), dtype=torch.float32, device=dev),
+                     d_b_router=torch.empty((E,), dtype=torch.float32, device=dev),
+                     d_rms_scale=torch.empty((E,), dtype=torch.float32, device=dev),
+                     d_w_in=torch.empty((E, de, d), dtype=torch.float32, device=dev),
+                     d_w_out=torch.empty((E, d, de), dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = alloc_backward_workspace(layer, T)
+    g = BlockffnGrads(*[grads[k].data_ptr() for k in ("d_w_router", "d_b_router", "d_rms_scale", "d_w_in",
+                                                       "d_w_out")])
+    desc = layer.descriptor()
+    check(load().blockffn_backward(ctypes.byref(desc), _ptr(x), T, _ptr(preact), _ptr(dy), _ptr(workspace),
+                                   workspace.numel(), _ptr(dx), ctypes.byref(g), _stream(stream)),
+          "blockffn_backward")
+    return dict(dx=dx, **grads)
 
 
 def blockffn_sparsity_stats(n_experts: int, token_masks: torch.Tensor, chunk_len: int,

@@ -1,0 +1,639 @@
+// Layer backward over one batch through one layer, grouped by expert.
+//
+// The chain rule through the forward (BlockFFN write-up, lsdiaocha.cn, §2:
+// the ReLU + RMSNorm router is differentiable end to end; non-gated Swish
+// experts), for a scalar loss with dL/dy = dy.  Per token t with
+// r = (ms + eps)^(-1/2), a = ReLU(z), g = s a r, and every active pair (z > 0):
+//
+//   u = W_in[i] x,  h = Swish(u),  q = W_out[i]^T dy,  dg_i = q . h
+//   du = g_i q Swish'(u),  Swish'(u) = sig (1 + u (1 - sig))
+//   dW_out[i] += dy (g_i h)^T,  dW_in[i] += du x^T,  dx += W_in[i]^T du
+//   ds_i += dg_i a_i r,  dr = sum_i dg_i s_i a_i,  dms = -dr r^3 / 2
+//   dz_i = dg_i s_i r + dms 2 a_i / E,  db += dz,  dW_r += dz x^T,  dx += W_r^T dz
+//
+// Active pairs are grouped by expert (the forward's pair planning, on
+// z > 0), and the per-expert products run as LDS-tiled MFMA GEMMs:
+//
+//   prep:    g and r per token (as the router computes them), dy -> bf16,
+//            W_in and W_out transposed per expert (the products that
+//            contract over a weight's row index read the transposed copy)
+//   pair:    U = X_p W_in[i]^T and Q = dY_p W_out[i] in one pass over k = d;
+//            epilogue: dU = g Q Swish'(U), HG = g Swish(U) (bf16), and the
+//            partial dg = sum over the tile's hidden units of Q Swish(U)
+//   router:  dz, ds terms per token; then db, ds by sums over tokens
+//   weights: dW_out[i] = dY_p^T HG_p, dW_in[i] = dU_p^T X_p and
+//            dW_r = dZ^T X, each a sum over pairs (tokens) in fp32 by a
+//            "transposing" grouped GEMM (the pair rows are written to LDS
+//            transposed, so the contraction runs over pairs)
+//   dx:      Part = dU W_in[i] per pair (the forward's down GEMM on the
+//            transposed W_in), then per token the sum over its active
+//            experts, ascending, of Part + dz_i W_r[i]
+//
+// No atomics: every output element has one writer and a fixed summation
+// order, so the result is bit-reproducible.
+#include "grouped_kernels.h"
+
+namespace bffn {
+namespace {
+
+constexpr int TBM = 128, TBN = 128, TBK = 32;  // transposing GEMM tile
+constexpr int kRouterPad = 128;               // dZ rows padded to 128 experts (bf16)
+
+// ---- prep: gates and 1/RMS as the router computes them; dy -> bf16 ----
+// One block per token: wave 0 does the router quantities, all threads convert dy.
+__global__ __launch_bounds__(kBlock) void bwd_prep_kernel(const float* __restrict__ z,
+                                                          const float* __restrict__ rms_scale, float eps, int64_t T,
+                                                          int E, int d, const float* __restrict__ dy,
+                                                          float* __restrict__ g_out, float* __restrict__ r_out,
+                                                          uint16_t* __restrict__ dyb, int64_t* __restrict__ all_off) {
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int lane = tid;
+    const bool v0 = lane < E, v1 = lane + 64 < E;
+    const float z0 = v0 ? z[t * E + lane] : 0.f, z1 = v1 ? z[t * E + lane + 64] : 0.f;
+    const float a0 = z0 > 0.f ? z0 : 0.f, a1 = z1 > 0.f ? z1 : 0.f;
+    const float ms = wave_sum(a0 * a0 + a1 * a1) / (float)E;
+    const float inv = 1.0f / sqrtf(ms + eps);
+    const float s0 = (v0 && rms_scale) ? rms_scale[lane] : 1.f, s1 = (v1 && rms_scale) ? rms_scale[lane + 64] : 1.f;
+    if (v0) g_out[t * E + lane] = s0 * a0 * inv;
+    if (v1) g_out[t * E + lane + 64] = s1 * a1 * inv;
+    if (lane == 0) r_out[t] = inv;
+  }
+  if (t == 0 && tid == 64) {
+    all_off[0] = 0;
+    all_off[1] = T;
+  }
+  for (int c = tid * 8; c < d; c += kBlock * 8) {
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(dy + t * d + c);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(dy + t * d + c + 4);
+    u32x4 o;
+    o[0] = f32_to_bf16(v0[0]) | (f32_to_bf16(v0[1]) << 16);
+    o[1] = f32_to_bf16(v0[2]) | (f32_to_bf16(v0[3]) << 16);
+    o[2] = f32_to_bf16(v1[0]) | (f32_to_bf16(v1[1]) << 16);
+    o[3] = f32_to_bf16(v1[2]) | (f32_to_bf16(v1[3]) << 16);
+    *reinterpret_cast<u32x4*>(dyb + t * d + c) = o;
+  }
+}
+
+// ---- transpose: out[b][c][r] = in[b][r][c], bf16, R and C multiples of 64 ----
+// grid (tiles of one matrix, batch); 64 x 64 tiles through a padded LDS tile.
+__global__ __launch_bounds__(kBlock) void transpose_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                           int R, int C) {
+  __shared__ uint16_t tile[64][66];
+  const int tid = threadIdx.x;
+  const int tiles_c = C / 64;
+  const int tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
+  const int64_t base = (int64_t)blockIdx.y * R * C;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = tid + j * kBlock, r = c >> 3, ch = c & 7;  // 64 rows x 8 chunks of 8
+    const u32x4 v = *reinterpret_cast<const u32x4*>(in + base + (int64_t)(tr * 64 + r) * C + tc * 64 + ch * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[r][ch * 8 + 2 * q] = (uint16_t)(v[q] & 0xffffu);
+      tile[r][ch * 8 + 2 * q + 1] = (uint16_t)(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = tid + j * kBlock, oc = c >> 3, ch = c & 7;  // output row oc (= input column)
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = (uint32_t)tile[ch * 8 + 2 * q][oc] | ((uint32_t)tile[ch * 8 + 2 * q + 1][oc] << 16);
+    *reinterpret_cast<u32x4*>(out + base + (int64_t)(tc * 64 + oc) * R + tr * 64 + ch * 8) = v;
+  }
+}
+
+// ---- pair: U and Q for a 64-pair x 128-hidden tile, fused epilogue ----
+struct PairArgs {
+  const uint16_t* x;        // [T][d]
+  const uint16_t* dy;       // [T][d] bf16
+  const int32_t* pair_tok;
+  const float* pair_gate;   // g of each pair
+  const uint16_t* w_in;     // [E][de][d]
+  const uint16_t* w_outT;   // [E][de][d]
+  const int64_t* pair_off;  // [E + 1]
+  const int64_t* tile_off;  // [E + 1]
+  uint16_t* du;             // [P][de] bf16
+  uint16_t* hg;             // [P][de] bf16
+  float* dgp;               // [P][de / 128]
+  int d, de, E;
+};
+
+__global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_x[2][GBM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_y[2][GBM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_wi[2][GBN * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_wo[2][GBN * 128];
+  __shared__ float dg_part[2][GBM];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int m = lane & 15, g = lane >> 4;
+  const int K = pa.d, N = pa.de, E = pa.E;
+  const int n_nt = N / GBN;
+  const int64_t total = pa.tile_off[E];
+  const int64_t nb = gridDim.x;
+  const int64_t per_xcd_blocks = nb / kXcds;
+  const int xcd = (int)(blockIdx.x % kXcds);
+  const int64_t local = blockIdx.x / kXcds;
+  const int64_t span = (total + kXcds - 1) / kXcds;
+  const int64_t t_begin = xcd * span, t_end = t_begin + span < total ? t_begin + span : total;
+
+  for (int64_t tt = t_begin + local; tt < t_end; tt += per_xcd_blocks) {
+    int lo = 0, hi = E - 1;  // last expert whose tile offset <= tt
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pa.tile_off[mid] <= tt) lo = mid; else hi = mid - 1;
+    }
+    const int i = lo;
+    const int64_t p0 = pa.pair_off[i];
+    const int n_i = (int)(pa.pair_off[i + 1] - p0);
+    const int m_tiles = (n_i + GBM - 1) / GBM;
+    const int64_t local_t = tt - pa.tile_off[i];
+    const int nt = (int)(local_t / m_tiles), mt = (int)(local_t % m_tiles);
+    const int m0 = mt * GBM, n0 = nt * GBN;
+
+    const uint16_t* x_src[2];
+    const uint16_t* y_src[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = (tid + j * kBlock) >> 3;
+      const int pr = m0 + r < n_i ? m0 + r : n_i - 1;  // rows past the group repeat a valid row
+      const int64_t tok = pa.pair_tok[p0 + pr];
+      x_src[j] = pa.x + tok * K + ((tid + j * kBlock) & 7) * 8;
+      y_src[j] = pa.dy + tok * K + ((tid + j * kBlock) & 7) * 8;
+    }
+    const uint16_t* wi_src[4];
+    const uint16_t* wo_src[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = (tid + j * kBlock) >> 3;
+      const int64_t off = ((int64_t)i * N + n0 + r) * K + ((tid + j * kBlock) & 7) * 8;
+      wi_src[j] = pa.w_in + off;
+      wo_src[j] = pa.w_outT + off;
+    }
+    u32x4 rx[2], ry[2], rwi[4], rwo[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        rx[j] = *reinterpret_cast<const u32x4*>(x_src[j] + k0);
+        ry[j] = *reinterpret_cast<const u32x4*>(y_src[j] + k0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        rwi[j] = *reinterpret_cast<const u32x4*>(wi_src[j] + k0);
+        rwo[j] = *reinterpret_cast<const u32x4*>(wo_src[j] + k0);
+      }
+    };
+    auto swrite = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tid + j * kBlock;
+        *reinterpret_cast<u32x4*>(&lds_x[buf][lds_off<128>(c >> 3, c & 7)]) = rx[j];
+        *reinterpret_cast<u32x4*>(&lds_y[buf][lds_off<128>(c >> 3, c & 7)]) = ry[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = tid + j * kBlock;
+        *reinterpret_cast<u32x4*>(&lds_wi[buf][lds_off<128>(c >> 3, c & 7)]) = rwi[j];
+        *reinterpret_cast<u32x4*>(&lds_wo[buf][lds_off<128>(c >> 3, c & 7)]) = rwo[j];
+      }
+    };
+
+    f32x4 au[4][2], aq[4][2];  // [hidden stripe b][pair group a]
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) au[b][a] = aq[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ksteps = K / GBK;
+    gload(0);
+    swrite(0);
+    __syncthreads();
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < ksteps) gload((ks + 1) * GBK);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 vx[2], vy[2], vwi[4], vwo[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int off = lds_off<128>(wm * 32 + a * 16 + m, kk * 4 + g);
+          vx[a] = *reinterpret_cast<const u32x4*>(&lds_x[cur][off]);
+          vy[a] = *reinterpret_cast<const u32x4*>(&lds_y[cur][off]);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int off = lds_off<128>(wn * 64 + b * 16 + m, kk * 4 + g);
+          vwi[b] = *reinterpret_cast<const u32x4*>(&lds_wi[cur][off]);
+          vwo[b] = *reinterpret_cast<const u32x4*>(&lds_wo[cur][off]);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            au[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vwi[b]), as_bf16x8(vx[a]), au[b][a], 0, 0, 0);
+            aq[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vwo[b]), as_bf16x8(vy[a]), aq[b][a], 0, 0, 0);
+          }
+      }
+      if (ks + 1 < ksteps) swrite(cur ^ 1);
+      __syncthreads();
+    }
+
+    // lane (m, g): pair wm*32 + a*16 + m, hidden units n0 + wn*64 + b*16 + 4g .. +3
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int row = m0 + wm * 32 + a * 16 + m;
+      const bool valid = row < n_i;
+      const float gv = valid ? pa.pair_gate[p0 + row] : 0.f;
+      float dgl = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float du4[4], hg4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float u = au[b][a][r], q = aq[b][a][r];
+          const float sig = 1.0f / (1.0f + __expf(-u));
+          const float h = u * sig;
+          dgl += q * h;
+          du4[r] = gv * q * sig * (1.0f + u * (1.0f - sig));
+          hg4[r] = gv * h;
+        }
+        if (valid) {
+          const int64_t o = (p0 + row) * N + n0 + wn * 64 + b * 16 + 4 * g;
+          *reinterpret_cast<u32x2*>(pa.du + o) = pack4_bf16(du4[0], du4[1], du4[2], du4[3]);
+          *reinterpret_cast<u32x2*>(pa.hg + o) = pack4_bf16(hg4[0], hg4[1], hg4[2], hg4[3]);
+        }
+      }
+      // the four lane groups g hold the same pair: sum them, then the two wn waves via LDS
+      dgl += __shfl_xor(dgl, 16, kWave);
+      dgl += __shfl_xor(dgl, 32, kWave);
+      if (g == 0) dg_part[wn][wm * 32 + a * 16 + m] = dgl;
+    }
+    __syncthreads();
+    if (tid < GBM && m0 + tid < n_i) pa.dgp[(p0 + m0 + tid) * n_nt + nt] = dg_part[0][tid] + dg_part[1][tid];
+    // (dg_part is next written after this tile's k loop, which has barriers)
+  }
+}
+
+// ---- router backward per token: dz (fp32 and bf16), ds terms ----
+// Wave w of a block handles token 4 blockIdx + w; lane l experts l and l + 64.
+__global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restrict__ z,
+                                                            const float* __restrict__ rms_scale,
+                                                            const float* __restrict__ r_tok,
+                                                            const int32_t* __restrict__ pair_idx,
+                                                            const float* __restrict__ dgp, int n_nt, int64_t T, int E,
+                                                            float* __restrict__ dz, uint16_t* __restrict__ dzb,
+                                                            float* __restrict__ dsc) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float r = r_tok[t];
+  float dgv[2], av[2], sv[2];
+  bool on[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    const bool v = i < E;
+    const float zi = v ? z[t * E + i] : 0.f;
+    on[h] = zi > 0.f;
+    av[h] = on[h] ? zi : 0.f;
+    sv[h] = (v && rms_scale) ? rms_scale[i] : 1.f;
+    float dg = 0.f;
+    if (on[h]) {
+      const int64_t p = pair_idx[t * E + i];
+      for (int q = 0; q < n_nt; ++q) dg += dgp[p * n_nt + q];
+    }
+    dgv[h] = dg;
+  }
+  const float dr = wave_sum(dgv[0] * sv[0] * av[0] + dgv[1] * sv[1] * av[1]);
+  const float dms = -0.5f * dr * r * r * r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    const float da = dgv[h] * sv[h] * r + dms * 2.f * av[h] / (float)E;
+    const float dzi = on[h] ? da : 0.f;
+    if (i < E) {
+      dz[t * E + i] = dzi;
+      dsc[t * E + i] = dgv[h] * av[h] * r;
+    }
+    dzb[t * kRouterPad + i] = (uint16_t)f32_to_bf16(i < E ? dzi : 0.f);
+  }
+}
+
+// ---- db[i] = sum_t dz[t][i], ds[i] = sum_t dsc[t][i]: one block per expert ----
+__global__ __launch_bounds__(kBlock) void bwd_reduce_kernel(const float* __restrict__ dz, const float* __restrict__ dsc,
+                                                            int64_t T, int E, float* __restrict__ db,
+                                                            float* __restrict__ ds) {
+  __shared__ float sb[kBlock], ss[kBlock];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  float b = 0.f, s = 0.f;
+  for (int64_t t = tid; t < T; t += kBlock) {
+    b += dz[t * E + i];
+    s += dsc[t * E + i];
+  }
+  sb[tid] = b;
+  ss[tid] = s;
+  __syncthreads();
+  for (int off = kBlock / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      sb[tid] += sb[tid + off];
+      ss[tid] += ss[tid + off];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    db[i] = sb[0];
+    ds[i] = ss[0];
+  }
+}
+
+// ---- transposing grouped GEMM: C_g[m][n] = sum over pairs p of group g of A[ra(p)][m] B[rb(p)][n] ----
+struct TGemmArgs {
+  const uint16_t* a;        // rows of M (or more) bf16 elements, row stride lda
+  int64_t lda;
+  const int32_t* a_rows;    // row of pair p (nullptr: row p)
+  const uint16_t* b;
+  int64_t ldb;
+  const int32_t* b_rows;
+  const int64_t* grp_off;   // [G + 1] pair ranges
+  float* c;                 // group g at c + g * c_stride; [M_valid][N] rows of ldc
+  int64_t ldc, c_stride;
+  int G, M, M_valid, N;
+};
+
+// LDS tile of 128 rows (m or n) x 32 pairs, 64-byte rows; 16-byte chunk
+// (8 pairs) XOR (row >> 2) & 3 so the 16 rows of an operand read hit
+// different bank groups.
+__device__ __forceinline__ int tl_off(int row, int p) {
+  return row * 64 + ((((p >> 3) ^ (row >> 2)) & 3) << 4) + (p & 7) * 2;
+}
+
+__global__ __launch_bounds__(kBlock) void tgemm_kernel(TGemmArgs ta) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][TBM * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][TBN * 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int m16 = lane & 15, g = lane >> 4;
+  const int mtn = ta.M / TBM, ntn = ta.N / TBN;
+  const int64_t total = (int64_t)ta.G * mtn * ntn;
+  const int64_t nb = gridDim.x;
+  const int64_t per_xcd_blocks = nb / kXcds;
+  const int xcd = (int)(blockIdx.x % kXcds);
+  const int64_t local = blockIdx.x / kXcds;
+  const int64_t span = (total + kXcds - 1) / kXcds;
+  const int64_t t_begin = xcd * span, t_end = t_begin + span < total ? t_begin + span : total;
+
+  for (int64_t tt = t_begin + local; tt < t_end; tt += per_xcd_blocks) {
+    const int grp = (int)(tt / (mtn * ntn));
+    const int rem = (int)(tt % (mtn * ntn));
+    const int m0 = (rem / ntn) * TBM, n0 = (rem % ntn) * TBN;
+    const int64_t p0 = ta.grp_off[grp];
+    const int64_t n_p = ta.grp_off[grp + 1] - p0;
+    const int ksteps = (int)((n_p + TBK - 1) / TBK);
+
+    // this thread's two 16-byte chunks of each operand per step: pair row
+    // c >> 4 (of 32), elements (c & 15) * 8 .. +7 of the 128-wide tile
+    u32x4 ra[2], rb[2];
+    auto gload = [&](int s) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tid + j * kBlock, pr = c >> 4, ch = c & 15;
+        const int64_t p = (int64_t)s * TBK + pr;
+        u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = u32x4{0u, 0u, 0u, 0u};
+        if (p < n_p) {  // pairs past the group contribute zero
+          const int64_t rowa = ta.a_rows ? (int64_t)ta.a_rows[p0 + p] : p0 + p;
+          const int64_t rowb = ta.b_rows ? (int64_t)ta.b_rows[p0 + p] : p0 + p;
+          va = *reinterpret_cast<const u32x4*>(ta.a + rowa * ta.lda + m0 + ch * 8);
+          vb = *reinterpret_cast<const u32x4*>(ta.b + rowb * ta.ldb + n0 + ch * 8);
+        }
+        ra[j] = va;
+        rb[j] = vb;
+      }
+    };
+    auto swrite = [&](int buf) {  // transposed: element (pair pr, row ch*8 + e) -> LDS row ch*8 + e
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tid + j * kBlock, pr = c >> 4, ch = c & 15;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          *reinterpret_cast<uint16_t*>(&lds_a[buf][tl_off(ch * 8 + 2 * q, pr)]) = (uint16_t)(ra[j][q] & 0xffffu);
+          *reinterpret_cast<uint16_t*>(&lds_a[buf][tl_off(ch * 8 + 2 * q + 1, pr)]) = (uint16_t)(ra[j][q] >> 16);
+          *reinterpret_cast<uint16_t*>(&lds_b[buf][tl_off(ch * 8 + 2 * q, pr)]) = (uint16_t)(rb[j][q] & 0xffffu);
+          *reinterpret_cast<uint16_t*>(&lds_b[buf][tl_off(ch * 8 + 2 * q + 1, pr)]) = (uint16_t)(rb[j][q] >> 16);
+        }
+      }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int sa = 0; sa < 4; ++sa)
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) acc[sa][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ksteps > 0) {
+      gload(0);
+      swrite(0);
+      __syncthreads();
+    }
+    for (int s = 0; s < ksteps; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < ksteps) gload(s + 1);
+      u32x4 av[4], bv[4];
+#pragma unroll
+      for (int sa = 0; sa < 4; ++sa)
+        av[sa] = *reinterpret_cast<const u32x4*>(&lds_a[cur][tl_off(wm * 64 + sa * 16 + m16, g * 8)]);
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+        bv[sb] = *reinterpret_cast<const u32x4*>(&lds_b[cur][tl_off(wn * 64 + sb * 16 + m16, g * 8)]);
+#pragma unroll
+      for (int sa = 0; sa < 4; ++sa)
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+          acc[sa][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[sa]), as_bf16x8(bv[sb]), acc[sa][sb], 0,
+                                                                0, 0);
+      if (s + 1 < ksteps) swrite(cur ^ 1);
+      __syncthreads();
+    }
+    // D: lane (m16, g) holds rows 4 g + r of column m16 of each 16 x 16 tile
+    float* cg = ta.c + (int64_t)grp * ta.c_stride;
+#pragma unroll
+    for (int sa = 0; sa < 4; ++sa)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mm = m0 + wm * 64 + sa * 16 + 4 * g + r;
+        if (mm >= ta.M_valid) continue;
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) cg[(int64_t)mm * ta.ldc + n0 + wn * 64 + sb * 16 + m16] = acc[sa][sb][r];
+      }
+  }
+}
+
+// ---- dx[t] = sum over active i (ascending) of Part[pair_idx[t][i]] + dz[t][i] W_r[i] ----
+__global__ __launch_bounds__(1024) void bwd_combine_kernel(const float* __restrict__ z, const float* __restrict__ dz,
+                                                           const int32_t* __restrict__ pair_idx,
+                                                           const uint16_t* __restrict__ part,
+                                                           const uint16_t* __restrict__ w_router, int64_t T, int E,
+                                                           int d, float* __restrict__ dx) {
+  __shared__ int32_t plist[128];
+  __shared__ float zlist[128];
+  __shared__ int32_t elist[128];
+  __shared__ int nlist;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const bool on0 = tid < E && z[t * E + tid] > 0.f;
+    const bool on1 = tid + 64 < E && z[t * E + tid + 64] > 0.f;
+    const uint64_t b0 = __ballot(on0), b1 = __ballot(on1);
+    const int n0 = __popcll(b0);
+    const int r0 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u));
+    const int r1 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u));
+    if (on0) {
+      plist[r0] = pair_idx[t * E + tid];
+      zlist[r0] = dz[t * E + tid];
+      elist[r0] = tid;
+    }
+    if (on1) {
+      plist[n0 + r1] = pair_idx[t * E + tid + 64];
+      zlist[n0 + r1] = dz[t * E + tid + 64];
+      elist[n0 + r1] = tid + 64;
+    }
+    if (tid == 0) nlist = n0 + __popcll(b1);
+  }
+  __syncthreads();
+  const int n = nlist;
+  for (int c0 = tid * 8; c0 < d; c0 += blockDim.x * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n; ++s) {
+      const u32x4 pv = load_part(part + (int64_t)plist[s] * d + c0);
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(w_router + (int64_t)elist[s] * d + c0);
+      const float zs = zlist[s];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_lo(pv[q]) + zs * bf16_lo(wv[q]);
+        acc[2 * q + 1] += bf16_hi(pv[q]) + zs * bf16_hi(wv[q]);
+      }
+    }
+    f32x4* o = reinterpret_cast<f32x4*>(dx + t * d + c0);
+    o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+}
+
+struct BwdLayout {
+  int32_t* blk;
+  int64_t *pair_off, *tile_up, *all_off;
+  int32_t *pair_tok, *pair_idx;
+  float *pair_gate, *g_b, *r_b, *dgp, *dz, *dsc;
+  uint16_t *dyb, *w_inT, *w_outT, *du, *hg, *dzb, *part, *trash;
+  size_t bytes;
+};
+
+BwdLayout bwd_layout(char* base, int64_t T, int E, int d, int de) {
+  const size_t P = (size_t)T * E;
+  const int rows = plan_rows(T);
+  const size_t nblk = ((size_t)T + rows - 1) / rows;
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += r256(bytes);
+    return p;
+  };
+  L.blk = reinterpret_cast<int32_t*>(take(4 * nblk * E));
+  L.pair_off = reinterpret_cast<int64_t*>(take(8 * (size_t)(E + 1)));
+  L.tile_up = reinterpret_cast<int64_t*>(take(8 * (size_t)(E + 1)));
+  L.all_off = reinterpret_cast<int64_t*>(take(16));
+  L.pair_tok = reinterpret_cast<int32_t*>(take(4 * P));
+  L.pair_gate = reinterpret_cast<float*>(take(4 * P));
+  L.pair_idx = reinterpret_cast<int32_t*>(take(4 * P));
+  L.g_b = reinterpret_cast<float*>(take(4 * P));
+  L.r_b = reinterpret_cast<float*>(take(4 * (size_t)T));
+  L.dyb = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * d));
+  L.w_inT = reinterpret_cast<uint16_t*>(take(2 * (size_t)E * d * de));
+  L.w_outT = reinterpret_cast<uint16_t*>(take(2 * (size_t)E * d * de));
+  L.du = reinterpret_cast<uint16_t*>(take(2 * P * de));
+  L.hg = reinterpret_cast<uint16_t*>(take(2 * P * de));
+  L.dgp = reinterpret_cast<float*>(take(4 * P * (de / GBN)));
+  L.dz = reinterpret_cast<float*>(take(4 * P));
+  L.dsc = reinterpret_cast<float*>(take(4 * P));
+  L.dzb = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * kRouterPad));
+  L.part = reinterpret_cast<uint16_t*>(take(2 * P * d));
+  L.trash = reinterpret_cast<uint16_t*>(take(kTrashBytes));
+  L.bytes = off;
+  return L;
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int64_t T, int E, int d, int de) { return bwd_layout(nullptr, T, E, d, de).bytes; }
+
+hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, const float* preact, const float* dy,
+                           void* workspace, float* dx, float* d_w_router, float* d_b_router, float* d_rms_scale,
+                           float* d_w_in, float* d_w_out, const StageEvents& se, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int E = la.E, d = la.d, de = la.de;
+  const BwdLayout L = bwd_layout(static_cast<char*>(workspace), T, E, d, de);
+  const int rows = plan_rows(T);
+  const int nblk = (int)((T + rows - 1) / rows);
+  const uint16_t* w_r = static_cast<const uint16_t*>(la.w_router);
+  const uint16_t* w_in = static_cast<const uint16_t*>(la.w_in);
+  const uint16_t* w_out = static_cast<const uint16_t*>(la.w_out);
+
+  se.record(0, s);
+  bwd_prep_kernel<<<dim3((unsigned)T), dim3(kBlock), 0, s>>>(preact, la.rms_scale, la.eps, T, E, d, dy, L.g_b, L.r_b,
+                                                             L.dyb, L.all_off);
+  // W_in[i] [de][d] -> [d][de];  W_out[i] [d][de] -> [de][d]
+  transpose_kernel<<<dim3((unsigned)((de / 64) * (d / 64)), (unsigned)E), dim3(kBlock), 0, s>>>(w_in, L.w_inT, de, d);
+  transpose_kernel<<<dim3((unsigned)((d / 64) * (de / 64)), (unsigned)E), dim3(kBlock), 0, s>>>(w_out, L.w_outT, d,
+                                                                                              de);
+  group_count_kernel<PairRule::kPositive><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(preact, T, E, rows,
+                                                                                              L.blk);
+  group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(L.blk, nblk, E, de / GBN, L.pair_off, L.tile_up);
+  group_fill_kernel<PairRule::kPositive><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(
+      preact, L.g_b, T, E, rows, L.blk, L.pair_tok, L.pair_gate, L.pair_idx);
+
+  const int64_t max_up_tiles = (int64_t)E * ((T + GBM - 1) / GBM) * (de / GBN);
+  int64_t grid_pair = 0, grid_t = 0, grid_dn = 0;
+  hipError_t e = persistent_grid(bwd_pair_kernel, max_up_tiles, &grid_pair);
+  if (e == hipSuccess) e = persistent_grid(tgemm_kernel, (int64_t)E * (d / TBM) * (de / TBN), &grid_t);
+  if (e == hipSuccess)
+    e = de == 128 ? persistent_grid(grouped_down_kernel<128>, (int64_t)E * (d / GBN), &grid_dn)
+                  : persistent_grid(grouped_down_kernel<256>, (int64_t)E * (d / GBN), &grid_dn);
+  if (e != hipSuccess) return e;
+
+  se.record(1, s);
+  PairArgs pa{x, L.dyb, L.pair_tok, L.pair_gate, w_in, L.w_outT, L.pair_off, L.tile_up, L.du, L.hg, L.dgp, d, de, E};
+  bwd_pair_kernel<<<dim3((unsigned)grid_pair), dim3(kBlock), 0, s>>>(pa);
+  se.record(2, s);
+  bwd_router_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(kBlock), 0, s>>>(
+      preact, la.rms_scale, L.r_b, L.pair_idx, L.dgp, de / GBN, T, E, L.dz, L.dzb, L.dsc);
+  bwd_reduce_kernel<<<dim3((unsigned)E), dim3(kBlock), 0, s>>>(L.dz, L.dsc, T, E, d_b_router, d_rms_scale);
+  // dW_out[i][k][j] = sum_p dY[t_p][k] HG[p][j]
+  TGemmArgs go{L.dyb, d, L.pair_tok, L.hg, de, nullptr, L.pair_off, d_w_out, de, (int64_t)d * de, E, d, d, de};
+  tgemm_kernel<<<dim3((unsigned)grid_t), dim3(kBlock), 0, s>>>(go);
+  // dW_in[i][j][k] = sum_p dU[p][j] X[t_p][k]
+  TGemmArgs gi{L.du, de, nullptr, x, d, L.pair_tok, L.pair_off, d_w_in, d, (int64_t)de * d, E, de, de, d};
+  tgemm_kernel<<<dim3((unsigned)grid_t), dim3(kBlock), 0, s>>>(gi);
+  // dW_r[i][k] = sum_t dZ[t][i] X[t][k]  (one group: all tokens)
+  TGemmArgs gr{L.dzb, kRouterPad, nullptr, x, d, nullptr, L.all_off, d_w_router, d, 0, 1, kRouterPad, E, d};
+  tgemm_kernel<<<dim3((unsigned)grid_t), dim3(kBlock), 0, s>>>(gr);
+  se.record(3, s);
+  // dx: per-pair dU W_in[i] rows (the forward's down GEMM on W_in^T), then the per-token sum
+  DownArgs dn{L.du, L.w_inT, L.pair_off, L.part, L.trash, d, E};
+  if (de == 128)
+    grouped_down_kernel<128><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
+  else
+    grouped_down_kernel<256><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
+  se.record(4, s);
+  int cthreads = (d / 8 + 63) / 64 * 64;
+  cthreads = cthreads < 64 ? 64 : (cthreads > 1024 ? 1024 : cthreads);
+  bwd_combine_kernel<<<dim3((unsigned)T), dim3((unsigned)cthreads), 0, s>>>(preact, L.dz, L.pair_idx, L.part, w_r, T,
+                                                                           E, d, dx);
+  se.record(5, s);
+  return hipGetLastError();
+}
+
+}  // namespace bffn

@@ -96,6 +96,11 @@ hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_
 size_t grouped_workspace_bytes(int64_t n_tokens, int E, int d, int de);
 bool grouped_supported(int d, int de, int dtype);
 
+hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, const float* preact,
+                           const float* dy, void* workspace, float* dx, float* d_w_router, float* d_b_router,
+                           float* d_rms_scale, float* d_w_in, float* d_w_out, const StageEvents& se, hipStream_t s);
+size_t backward_workspace_bytes(int64_t n_tokens, int E, int d, int de);
+
 bool route_uses_mfma(int d, int E, int chunk_len, int dtype);
 bool forward_mfma_supported(int d, int de, int dtype);
 size_t forward_mfma_plan_bytes(int64_t units);

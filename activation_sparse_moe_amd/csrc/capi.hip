@@ -240,6 +240,50 @@ BFFN_EXPORT int blockffn_sparsity_stats(int32_t n_experts, const uint64_t* token
                     "stats launch");
 }
 
+namespace {
+
+int check_backward(const blockffn_layer* layer, int64_t n_tokens) {
+  if (int r = check_layer(layer, 1)) return r;
+  if (n_tokens < 0) return fail(BLOCKFFN_ERR_SHAPE, "n_tokens %lld is negative", (long long)n_tokens);
+  if (!bffn::grouped_supported(layer->d, layer->d_expert, layer->dtype))
+    return fail(BLOCKFFN_ERR_MODE, "the backward needs bf16, d a multiple of 128 and d_expert 128 or 256");
+  if (n_tokens * layer->n_experts > INT32_MAX)
+    return fail(BLOCKFFN_ERR_SHAPE, "the backward indexes pairs with 32 bits: n_tokens x n_experts must stay below 2^31");
+  return BLOCKFFN_OK;
+}
+
+}  // namespace
+
+BFFN_EXPORT size_t blockffn_backward_workspace_size(const blockffn_layer* layer, int64_t n_tokens) {
+  if (check_backward(layer, n_tokens) != BLOCKFFN_OK) return 0;
+  return bffn::backward_workspace_bytes(n_tokens, layer->n_experts, layer->d, layer->d_expert);
+}
+
+BFFN_EXPORT int blockffn_backward(const blockffn_layer* layer, const void* x, int64_t n_tokens, const float* preact,
+                                  const float* dy, void* workspace, size_t workspace_bytes, float* dx,
+                                  const blockffn_grads* grads, hipStream_t stream) {
+  if (int r = check_backward(layer, n_tokens)) return r;
+  if (n_tokens == 0) return BLOCKFFN_OK;
+  if (!x || !preact || !dy || !dx || !grads) return fail(BLOCKFFN_ERR_NULL, "x, preact, dy, dx and grads must be non-NULL");
+  if (!grads->d_w_router || !grads->d_b_router || !grads->d_rms_scale || !grads->d_w_in || !grads->d_w_out)
+    return fail(BLOCKFFN_ERR_NULL, "every gradient pointer must be non-NULL");
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(preact, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "x, dy and dx must be 16-byte aligned, preact 4-byte aligned");
+  if (!aligned(grads->d_w_router, 16) || !aligned(grads->d_w_in, 16) || !aligned(grads->d_w_out, 16) ||
+      !aligned(grads->d_b_router, 4) || !aligned(grads->d_rms_scale, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "weight gradients must be 16-byte aligned, d_b_router / d_rms_scale 4-byte");
+  const size_t need = bffn::backward_workspace_bytes(n_tokens, layer->n_experts, layer->d, layer->d_expert);
+  if (!workspace) return fail(BLOCKFFN_ERR_NULL, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned(workspace, 256)) return fail(BLOCKFFN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  const bffn::LayerArgs la = layer_args(layer, 1);
+  return hip_status(bffn::launch_backward(la, static_cast<const uint16_t*>(x), n_tokens, preact, dy, workspace, dx,
+                                          grads->d_w_router, grads->d_b_router, grads->d_rms_scale, grads->d_w_in,
+                                          grads->d_w_out, g_stage_events, stream),
+                    "backward launch");
+}
+
 BFFN_EXPORT int blockffn_set_stage_events(hipEvent_t* events, int32_t n_events) {
   if (events != nullptr && n_events < 1) return fail(BLOCKFFN_ERR_SHAPE, "n_events %d < 1", n_events);
   g_stage_events.ev = events;

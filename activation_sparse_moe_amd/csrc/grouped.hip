@@ -1,525 +1,14 @@
-// Grouped-by-expert batch path (prefill-like batches through one layer).
+// Grouped-by-expert batch forward: the launcher (kernels in grouped_kernels.h).
 //
 // When many chunks go through the same layer, streaming each chunk's union
 // (the chunk path) would re-read the layer once per chunk.  Here every
 // (token, expert) pair with a non-zero gate is grouped by expert and each
-// expert's weights are read once for all of its tokens, in LDS-tiled MFMA
-// GEMMs (the outer loop over active experts with a batched product inside,
-// BlockFFN write-up §7, taken to the whole batch):
-//
-//   count:   per block of tokens, each expert's pair count
-//   scan:    per-expert pair offsets, up-tile offsets, and each token block's
-//            first pair slot for every expert (one block)
-//   fill:    per block of tokens, its pairs in ascending token order: token,
-//            gate, and pair_idx[t][i] for the combine
-//   up:      H'[p] = g_p * Swish(x[t_p] W_in[i]^T), bf16, grouped GEMM with
-//            gathered token rows (64 pairs x 128 hidden x 64 k tiles)
-//   down:    Part[p] = H'[p] W_out[i]^T, bf16 per-pair partial rows; a block
-//            keeps one 128-row slab of W_out[i] in LDS and runs it over all
-//            of expert i's pairs
-//   combine: y[t] = sum over the token's experts in ascending order of
-//            Part[pair_idx[t][i]], fp32 (no atomics; deterministic)
-//
-// MFMA tiles use v_mfma_f32_16x16x32_bf16 on 256 threads (2 x 2 waves of
-// 32 x 64).  Global rows are moved as 16-byte chunks and written to LDS with
-// the chunk index XOR-swizzled by row, so that the 16 rows an MFMA operand
-// read touches land in different banks.  Output tiles are staged in LDS and
-// stored as whole 16-byte chunks of each row.
-#include "bffn_internal.h"
+// expert's weights are read once for all of its tokens (the outer loop over
+// active experts with a batched product inside, BlockFFN write-up §7, taken
+// to the whole batch).
+#include "grouped_kernels.h"
 
 namespace bffn {
-namespace {
-
-constexpr int GBM = 64, GBN = 128, GBK = 64;
-constexpr int kPlanThreads = 128;     // one thread per expert (E <= 128)
-constexpr int kPlanMaxBlocks = 2048;  // token blocks of the count / fill kernels
-constexpr size_t kTrashBytes = GBM * 256;  // one staged output tile
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Byte offset of 16-byte chunk `c` of row `r` in an LDS tile of ROW_BYTES-byte
-// rows.  A 16-byte operand read serves 16 lanes (16 consecutive rows, one
-// chunk each) per 256-byte pass over the banks, so the 16 rows must land on
-// 16 different 16-byte bank groups: rows of 128 bytes alternate halves and
-// XOR by (r >> 1) & 7; rows of 256 bytes or more XOR by r & 15.
-template <int ROW_BYTES>
-__device__ __forceinline__ int lds_off(int r, int c) {
-  static_assert(ROW_BYTES == 128 || (ROW_BYTES >= 256 && ROW_BYTES % 256 == 0), "row size");
-  const int f = ROW_BYTES == 128 ? ((r >> 1) & 7) : (r & 15);
-  return r * ROW_BYTES + ((c ^ f) << 4);
-}
-
-int plan_rows(int64_t T) {
-  const int64_t r = (T + kPlanMaxBlocks - 1) / kPlanMaxBlocks;
-  return (int)(r < 8 ? 8 : r);
-}
-
-// ---- count: pairs per (token block, expert) ----
-__global__ __launch_bounds__(kPlanThreads) void group_count_kernel(const float* __restrict__ gates, int64_t T, int E,
-                                                                   int rows, int32_t* __restrict__ blk) {
-  const int i = threadIdx.x;
-  if (i >= E) return;
-  const int64_t t0 = (int64_t)blockIdx.x * rows;
-  const int64_t t1 = t0 + rows < T ? t0 + rows : T;
-  int c = 0;
-  for (int64_t t = t0; t < t1; ++t) c += gates[t * E + i] > 0.f;
-  blk[(int64_t)blockIdx.x * E + i] = c;
-}
-
-// Exclusive prefix sum over the block's 1024 threads; returns the block total
-// in *total.  `wsum` is LDS scratch of 16 entries.
-__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* wsum, int64_t* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int64_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t o = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += o;
-  }
-  if (lane == 63) wsum[w] = inc;
-  __syncthreads();
-  int64_t before = 0, all = 0;
-  for (int q = 0; q < 16; ++q) {
-    const int64_t ws = wsum[q];
-    before += q < w ? ws : 0;
-    all += ws;
-  }
-  __syncthreads();
-  *total = all;
-  return before + inc - v;
-}
-
-// ---- scan: expert offsets, up-tile offsets, per-block first slots (in place) ----
-// Thread (part, i) owns expert i's counts of token blocks [b0, b1).
-__global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ blk, int nblk, int E, int n_tiles_up,
-                                                          int64_t* __restrict__ pair_off,
-                                                          int64_t* __restrict__ tile_up) {
-  __shared__ int64_t part_sum[1024];
-  __shared__ int64_t exp_off[128];
-  __shared__ int64_t wsum[16];
-  const int tid = threadIdx.x;
-  const int nparts = 1024 / E;
-  const int part = tid / E, i = tid % E;
-  const bool act = part < nparts;
-  const int b0 = act ? (int)((int64_t)nblk * part / nparts) : 0;
-  const int b1 = act ? (int)((int64_t)nblk * (part + 1) / nparts) : 0;
-  int64_t s = 0;
-  for (int b = b0; b < b1; b += 8) {
-    int c[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? blk[(int64_t)(b + u) * E + i] : 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s += c[u];
-  }
-  part_sum[tid] = s;
-  __syncthreads();
-  // per-expert totals, then exclusive scans over experts of pairs and up tiles
-  int64_t n = 0;
-  if (tid < E)
-    for (int q = 0; q < nparts; ++q) n += part_sum[q * E + tid];
-  const int64_t tiles = (n + GBM - 1) / GBM * n_tiles_up;
-  int64_t n_all = 0, t_all = 0;
-  const int64_t p_ex = block_exclusive_scan(n, wsum, &n_all);
-  const int64_t t_ex = block_exclusive_scan(tiles, wsum, &t_all);
-  if (tid < E) {
-    pair_off[tid] = p_ex;
-    tile_up[tid] = t_ex;
-    exp_off[tid] = p_ex;
-  }
-  if (tid == 0) {
-    pair_off[E] = n_all;
-    tile_up[E] = t_all;
-  }
-  __syncthreads();
-  if (act) {
-    int64_t off = exp_off[i];
-    for (int q = 0; q < part; ++q) off += part_sum[q * E + i];
-    for (int b = b0; b < b1; b += 8) {
-      int c[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? blk[(int64_t)(b + u) * E + i] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (b + u < b1) {
-          blk[(int64_t)(b + u) * E + i] = (int32_t)off;
-          off += c[u];
-        }
-    }
-  }
-}
-
-// ---- fill: each token block writes its pairs, tokens ascending per expert ----
-__global__ __launch_bounds__(kPlanThreads) void group_fill_kernel(const float* __restrict__ gates, int64_t T, int E,
-                                                                  int rows, const int32_t* __restrict__ blk_off,
-                                                                  int32_t* __restrict__ pair_tok,
-                                                                  float* __restrict__ pair_gate,
-                                                                  int32_t* __restrict__ pair_idx) {
-  const int i = threadIdx.x;
-  if (i >= E) return;
-  const int64_t t0 = (int64_t)blockIdx.x * rows;
-  const int64_t t1 = t0 + rows < T ? t0 + rows : T;
-  int32_t p = blk_off[(int64_t)blockIdx.x * E + i];
-  for (int64_t t = t0; t < t1; ++t) {
-    const float g = gates[t * E + i];
-    if (g > 0.f) {
-      pair_tok[p] = (int32_t)t;
-      pair_gate[p] = g;
-      pair_idx[t * E + i] = p;
-      ++p;
-    }
-  }
-}
-
-// The MFMAs take the weight rows as operand A and the pair rows as operand B,
-// so D = W . X^T: lane (m, g) of a 16 x 16 tile holds outputs 4 g .. 4 g + 3
-// of pair m, four consecutive row elements that it packs into 8 bytes.
-__device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
-  return u32x2{f32_to_bf16(a) | (f32_to_bf16(b) << 16), f32_to_bf16(c) | (f32_to_bf16(d) << 16)};
-}
-
-// ---- up: H'[p][n] = g_p Swish(sum_k x[tok(p)][k] W_in[i][n][k]) ----
-struct UpArgs {
-  const uint16_t* x;          // [T][K]
-  const int32_t* pair_tok;    // token of each pair
-  const float* pair_gate;     // gate of each pair
-  const uint16_t* w;          // [E][N][K]
-  const int64_t* pair_off;    // [E + 1]
-  const int64_t* tile_off;    // [E + 1]
-  uint16_t* hid;              // [P][N]
-  int K, N, E;
-};
-
-// Tile: 64 pairs x 128 hidden units, k steps of 64; wave (wm, wn) computes
-// pairs wm*32 .. +31 against hidden units wn*64 .. +63.
-__global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][GBM * 128];  // pair (x) rows
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][GBN * 128];  // weight rows
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int m = lane & 15, g = lane >> 4;
-  const int K = ua.K, N = ua.N, E = ua.E;
-  const int64_t total = ua.tile_off[E];
-  // XCD-aware persistent striding: each XCD walks one contiguous range of
-  // tiles, so the tiles sharing an expert's weight block share an L2.
-  const int64_t nb = gridDim.x;
-  const int64_t per_xcd_blocks = nb / kXcds;
-  const int xcd = (int)(blockIdx.x % kXcds);
-  const int64_t local = blockIdx.x / kXcds;
-  const int64_t span = (total + kXcds - 1) / kXcds;
-  const int64_t t_begin = xcd * span, t_end = t_begin + span < total ? t_begin + span : total;
-
-  for (int64_t tt = t_begin + local; tt < t_end; tt += per_xcd_blocks) {
-    int lo = 0, hi = E - 1;  // last expert whose tile offset <= tt
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (ua.tile_off[mid] <= tt) lo = mid; else hi = mid - 1;
-    }
-    const int i = lo;
-    const int64_t p0 = ua.pair_off[i];
-    const int n_i = (int)(ua.pair_off[i + 1] - p0);
-    const int m_tiles = (n_i + GBM - 1) / GBM;
-    const int64_t local_t = tt - ua.tile_off[i];
-    const int nt = (int)(local_t / m_tiles), mt = (int)(local_t % m_tiles);
-    const int m0 = mt * GBM, n0 = nt * GBN;
-
-    // global source rows of this thread's load slots
-    const uint16_t* a_src[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = (tid + j * kBlock) >> 3;
-      const int pr = m0 + r < n_i ? m0 + r : n_i - 1;  // rows past the group repeat a valid row
-      a_src[j] = ua.x + (int64_t)ua.pair_tok[p0 + pr] * K + ((tid + j * kBlock) & 7) * 8;
-    }
-    const uint16_t* b_src[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = (tid + j * kBlock) >> 3;
-      b_src[j] = ua.w + ((int64_t)i * N + n0 + r) * K + ((tid + j * kBlock) & 7) * 8;
-    }
-    u32x4 ra[2], rb[4];
-    auto gload = [&](int k0) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) ra[j] = *reinterpret_cast<const u32x4*>(a_src[j] + k0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rb[j] = *reinterpret_cast<const u32x4*>(b_src[j] + k0);
-    };
-    auto swrite = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_a[buf][lds_off<128>(c >> 3, c & 7)]) = ra[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_b[buf][lds_off<128>(c >> 3, c & 7)]) = rb[j];
-      }
-    };
-
-    f32x4 acc[4][2];  // [hidden stripe b][pair group a]
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int a = 0; a < 2; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int ksteps = K / GBK;
-    gload(0);
-    swrite(0);
-    __syncthreads();
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < ksteps) gload((ks + 1) * GBK);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 av[2], bv[4];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-          av[a] = *reinterpret_cast<const u32x4*>(&lds_a[cur][lds_off<128>(wm * 32 + a * 16 + m, kk * 4 + g)]);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          bv[b] = *reinterpret_cast<const u32x4*>(&lds_b[cur][lds_off<128>(wn * 64 + b * 16 + m, kk * 4 + g)]);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-            acc[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bv[b]), as_bf16x8(av[a]), acc[b][a], 0, 0, 0);
-      }
-      if (ks + 1 < ksteps) swrite(cur ^ 1);
-      __syncthreads();
-    }
-
-    // lane (m, g): pair wm*32 + a*16 + m, hidden units n0 + wn*64 + b*16 + 4g .. +3
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int row = m0 + wm * 32 + a * 16 + m;
-      if (row >= n_i) continue;
-      const float gv = ua.pair_gate[p0 + row];
-      uint16_t* orow = ua.hid + (p0 + row) * N + n0 + wn * 64 + 4 * g;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const f32x4 v = acc[b][a];
-        *reinterpret_cast<u32x2*>(orow + b * 16) =
-            pack4_bf16(gv * swish(v[0]), gv * swish(v[1]), gv * swish(v[2]), gv * swish(v[3]));
-      }
-    }
-  }
-}
-
-// ---- down: Part[p][n] = sum_k H'[p][k] W_out[i][n][k], K = d_e in {128, 256} ----
-struct DownArgs {
-  const uint16_t* hid;        // [P][K]
-  const uint16_t* w;          // [E][N][K]
-  const int64_t* pair_off;    // [E + 1]
-  uint16_t* part;             // [P][N]
-  uint16_t* trash;            // 16 KiB that is written and never read
-  int N, E;
-};
-
-// A work item is (expert i, 128-row slab of W_out[i]); the slab sits in LDS
-// while the block runs every 64-pair tile of the expert through it, with the
-// next tile's hidden rows loaded into registers during this tile's MFMAs.
-template <int K>
-__global__ __launch_bounds__(kBlock) void grouped_down_kernel(DownArgs da) {
-  constexpr int RB = K * 2;                       // bytes per LDS row
-  constexpr int kRowChunks = K / 8;               // 16-byte chunks per row
-  constexpr int kBChunks = GBN * kRowChunks / kBlock;  // per thread
-  constexpr int kAChunks = GBM * kRowChunks / kBlock;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[GBN * RB];     // weight slab
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][GBM * RB];  // hidden rows
-  __shared__ __attribute__((aligned(16))) uint8_t lds_c[GBM * 256];    // output tile, bf16
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int m = lane & 15, g = lane >> 4;
-  const int N = da.N, E = da.E;
-  const int n_slabs = N / GBN;
-  const int64_t total = (int64_t)E * n_slabs;
-  const int64_t nb = gridDim.x;
-  const int64_t per_xcd_blocks = nb / kXcds;
-  const int xcd = (int)(blockIdx.x % kXcds);
-  const int64_t local = blockIdx.x / kXcds;
-  const int64_t span = (total + kXcds - 1) / kXcds;
-  const int64_t it_begin = xcd * span, it_end = it_begin + span < total ? it_begin + span : total;
-
-  for (int64_t it = it_begin + local; it < it_end; it += per_xcd_blocks) {
-    const int i = (int)(it / n_slabs), n0 = (int)(it % n_slabs) * GBN;
-    const int64_t p0 = da.pair_off[i];
-    const int n_i = (int)(da.pair_off[i + 1] - p0);
-    if (n_i == 0) continue;
-    const int m_tiles = (n_i + GBM - 1) / GBM;
-
-    {  // the W_out slab: rows n0 .. n0 + 127 of expert i
-      u32x4 rb[kBChunks];
-#pragma unroll
-      for (int j = 0; j < kBChunks; ++j) {
-        const int c = tid + j * kBlock, r = c / kRowChunks, ch = c % kRowChunks;
-        rb[j] = *reinterpret_cast<const u32x4*>(da.w + ((int64_t)i * N + n0 + r) * K + ch * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < kBChunks; ++j) {
-        const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_b[lds_off<RB>(c / kRowChunks, c % kRowChunks)]) = rb[j];
-      }
-    }
-    // Hidden rows of a tile travel global -> registers -> LDS.  Two register
-    // sets alternate so that the loads of tile mt + 1 are issued a whole tile
-    // before they are written to LDS, ahead of tile mt - 1's stores (a wait
-    // on them then never waits on those stores).
-    auto aload = [&](u32x4 (&regs)[kAChunks], int mt) {
-#pragma unroll
-      for (int j = 0; j < kAChunks; ++j) {
-        const int c = tid + j * kBlock, r = c / kRowChunks, ch = c % kRowChunks;
-        const int pr = mt * GBM + r < n_i ? mt * GBM + r : n_i - 1;  // rows past the group repeat a valid row
-        regs[j] = *reinterpret_cast<const u32x4*>(da.hid + (p0 + pr) * K + ch * 8);
-      }
-    };
-    auto awrite = [&](const u32x4 (&regs)[kAChunks], int buf) {
-#pragma unroll
-      for (int j = 0; j < kAChunks; ++j) {
-        const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_a[buf][lds_off<RB>(c / kRowChunks, c % kRowChunks)]) = regs[j];
-      }
-    };
-    // One tile: MFMAs on lds_a[cur]; stage; write the next tile's rows (held
-    // in `next`) to lds_a[cur ^ 1]; store the staged rows.
-    auto tile = [&](int mt, int cur, const u32x4 (&next)[kAChunks]) {
-      f32x4 acc[4][2];  // [output stripe b][pair group a]
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int a = 0; a < 2; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < K / 32; ++kk) {
-        u32x4 av[2], bv[4];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-          av[a] = *reinterpret_cast<const u32x4*>(&lds_a[cur][lds_off<RB>(wm * 32 + a * 16 + m, kk * 4 + g)]);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          bv[b] = *reinterpret_cast<const u32x4*>(&lds_b[lds_off<RB>(wn * 64 + b * 16 + m, kk * 4 + g)]);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-            acc[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bv[b]), as_bf16x8(av[a]), acc[b][a], 0, 0, 0);
-      }
-      // Stage the tile, then store whole 16-byte chunks of each pair row
-      // (measured faster than 8-byte stores straight from the accumulators).
-      // lane (m, g): pair wm*32 + a*16 + m, outputs wn*64 + b*16 + 4g .. +3.
-      // The barrier also tells every wave that lds_a[cur ^ 1] (last read by
-      // the previous tile) and the previous staged tile are free.
-      __syncthreads();
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int col = wn * 64 + b * 16 + 4 * g;
-          const f32x4 v = acc[b][a];
-          *reinterpret_cast<u32x2*>(lds_c + lds_off<256>(wm * 32 + a * 16 + m, col >> 3) + (col & 7) * 2) =
-              pack4_bf16(v[0], v[1], v[2], v[3]);
-        }
-      if (mt + 1 < m_tiles) awrite(next, cur ^ 1);
-      __syncthreads();
-      // Rows past the group go to the trash area, so every wave issues the
-      // same number of stores on every path and the waits above stay exact.
-      const int rows_left = n_i - mt * GBM;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = tid + j * kBlock, r = c >> 4, ch = c & 15;
-        uint16_t* dst = r < rows_left ? da.part + (p0 + mt * GBM + r) * N + n0 + ch * 8 : da.trash + c * 8;
-        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(lds_c + lds_off<256>(r, ch));
-      }
-    };
-
-    u32x4 ra0[kAChunks], ra1[kAChunks];
-    aload(ra0, 0);
-    aload(ra1, m_tiles > 1 ? 1 : 0);
-    awrite(ra0, 0);
-    __syncthreads();
-    // (loads past the last tile repeat it, so that their number is fixed too)
-    for (int mt = 0; mt < m_tiles; mt += 2) {
-      aload(ra0, mt + 2 < m_tiles ? mt + 2 : m_tiles - 1);
-      tile(mt, 0, ra1);
-      if (mt + 1 >= m_tiles) break;
-      aload(ra1, mt + 3 < m_tiles ? mt + 3 : m_tiles - 1);
-      tile(mt + 1, 1, ra0);
-    }
-    __syncthreads();  // slab and staged-tile reads are done before the next item's writes
-  }
-}
-
-// Partial rows are read exactly once: non-temporal loads keep them from
-// displacing anything in the caches (measured 1.3x faster than plain loads).
-__device__ __forceinline__ u32x4 load_part(const uint16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
-// ---- combine: y[t] = sum over active experts (ascending) of Part[pair_idx[t][i]] ----
-__global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ gates,
-                                                       const int32_t* __restrict__ pair_idx,
-                                                       const uint16_t* __restrict__ part, int64_t T, int E, int d,
-                                                       float* __restrict__ y) {
-  __shared__ int32_t plist[128];
-  __shared__ int nlist;
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const bool on0 = tid < E && gates[t * E + tid] > 0.f;
-    const bool on1 = tid + 64 < E && gates[t * E + tid + 64] > 0.f;
-    const uint64_t b0 = __ballot(on0), b1 = __ballot(on1);
-    const int n0 = __popcll(b0);
-    const int r0 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u));
-    const int r1 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u));
-    if (on0) plist[r0] = pair_idx[t * E + tid];
-    if (on1) plist[n0 + r1] = pair_idx[t * E + tid + 64];
-    if (tid == 0) nlist = n0 + __popcll(b1);
-  }
-  __syncthreads();
-  const int n = nlist;
-  auto add8 = [](float (&acc)[8], u32x4 v) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += bf16_lo(v[q]);
-      acc[2 * q + 1] += bf16_hi(v[q]);
-    }
-  };
-  for (int c0 = tid * 8; c0 < d; c0 += blockDim.x * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    // four partial rows in flight, added in ascending expert order
-    for (; s + 4 <= n; s += 4) {
-      u32x4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = load_part(part + (int64_t)plist[s + u] * d + c0);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) add8(acc, v[u]);
-    }
-    for (; s < n; ++s) add8(acc, load_part(part + (int64_t)plist[s] * d + c0));
-    f32x4* yo = reinterpret_cast<f32x4*>(y + t * d + c0);
-    yo[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    yo[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
-  }
-}
-
-size_t r256(size_t v) { return (v + 255) & ~size_t(255); }
-
-// A persistent grid: the resident capacity, at most the work, and a multiple
-// of the XCD count so that every XCD gets the same number of blocks.
-template <typename F>
-hipError_t persistent_grid(F kernel, int64_t n_items, int64_t* grid) {
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0);
-  if (e != hipSuccess) return e;
-  int64_t gsz = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
-  const int64_t need = xcd_grid(n_items > 0 ? n_items : 1);
-  if (gsz > need) gsz = need;
-  gsz = gsz / kXcds * kXcds;
-  *grid = gsz > 0 ? gsz : kXcds;
-  return hipSuccess;
-}
-
-}  // namespace
 
 bool grouped_supported(int d, int de, int dtype) {
   return dtype == BLOCKFFN_BF16 && d % GBN == 0 && (de == 128 || de == 256);
@@ -558,10 +47,10 @@ hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_
   uint16_t* part = reinterpret_cast<uint16_t*>(take(2 * P * d));
   uint16_t* trash = reinterpret_cast<uint16_t*>(take(kTrashBytes));
 
-  group_count_kernel<<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(gates, T, E, rows, blk);
+  group_count_kernel<PairRule::kNonZero><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(gates, T, E, rows, blk);
   group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(blk, nblk, E, de / GBN, pair_off, tile_up);
-  group_fill_kernel<<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(gates, T, E, rows, blk, pair_tok, pair_gate,
-                                                                       pair_idx);
+  group_fill_kernel<PairRule::kNonZero><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(
+      gates, gates, T, E, rows, blk, pair_tok, pair_gate, pair_idx);
   // upper bounds of the work (every pair active) cap the grids; the kernels
   // read the exact totals on the device
   const int64_t max_up_tiles = (int64_t)E * ((T + GBM - 1) / GBM) * (de / GBN);

@@ -184,15 +184,63 @@ int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, const void* 
 int blockffn_sparsity_stats(int32_t n_experts, const uint64_t* token_masks, int64_t n_tokens,
                             int32_t chunk_len, blockffn_stats* stats_dev, hipStream_t stream);
 
+/* Gradient outputs of blockffn_backward: fp32, caller-owned device buffers,
+ * fully overwritten. */
+typedef struct blockffn_grads {
+  float* d_w_router;  /* [E][d] */
+  float* d_b_router;  /* [E] */
+  float* d_rms_scale; /* [E] */
+  float* d_w_in;      /* [E][d_e][d] */
+  float* d_w_out;     /* [E][d][d_e] */
+} blockffn_grads;
+
+/*
+ * Layer backward over one batch through one layer: the gradients of a scalar
+ * loss L with respect to x and every parameter, given dy = dL/dy.  It is the
+ * chain rule through the forward defined above (write-up §2: the ReLU +
+ * RMSNorm router is differentiable end to end): for every active pair (z > 0)
+ *   u = W_in[i] x, h = Swish(u), q = W_out[i]^T dy, dg_i = q . h,
+ *   du = g_i q Swish'(u), dW_out[i] += dy (g_i h)^T, dW_in[i] += du x^T,
+ *   dx += W_in[i]^T du;
+ * and per token, with r = (ms + eps)^(-1/2) and a = ReLU(z),
+ *   ds_i += dg_i a_i r, dms = -(sum_i dg_i s_i a_i) r^3 / 2,
+ *   dz_i = [z_i > 0] (dg_i s_i r + dms 2 a_i / E), db += dz, dW_r += dz x^T,
+ *   dx += W_r^T dz.
+ * Inactive pairs contribute nothing.  Active pairs are grouped by expert and
+ * every product runs on the matrix cores from bf16 operands (dy, the hidden
+ * gradients and dz are rounded to bf16) with fp32 accumulation; no atomics,
+ * so results are bit-reproducible.
+ *   layer       one layer (bf16; d a multiple of 128; d_expert 128 or 256)
+ *   x           [n_tokens][d] bf16, the forward's input
+ *   preact      [n_tokens][E] fp32, z as written by blockffn_route
+ *   dy          [n_tokens][d] fp32, 16-byte aligned
+ *   workspace   at least blockffn_backward_workspace_size() bytes, 256-byte
+ *               aligned, no initialisation needed
+ *   dx          [n_tokens][d] fp32 out, 16-byte aligned
+ *   grads       the parameter gradients (all five pointers non-NULL)
+ * n_tokens x n_experts must stay below 2^31.  n_tokens == 0 writes nothing.
+ * Errors: NULL, SHAPE, DTYPE, WORKSPACE, MODE (unsupported shape or dtype),
+ * ALIGN, HIP.
+ */
+int blockffn_backward(const blockffn_layer* layer, const void* x, int64_t n_tokens, const float* preact,
+                      const float* dy, void* workspace, size_t workspace_bytes, float* dx,
+                      const blockffn_grads* grads, hipStream_t stream);
+
+/* Workspace bytes blockffn_backward needs (0 on invalid input). */
+size_t blockffn_backward_workspace_size(const blockffn_layer* layer, int64_t n_tokens);
+
 /*
  * Stage timing (instrumentation for profilers and benchmarks).  While set,
- * every blockffn_forward call of the calling thread records events[0] on its
- * stream before its first timed kernel and events[k] right after its k-th
- * timed kernel, for k < n_events.  The timed kernels are the expert
- * up-projection and down-projection (GEMV, CHUNK_MFMA and DENSE modes), plus
- * the per-token combine in GROUPED mode.  `events` are
- * caller-created hipEvents in caller memory that must stay valid while set;
- * pass NULL to stop.  Errors: SHAPE (n_events < 1 with non-NULL events).
+ * every blockffn_forward or blockffn_backward call of the calling thread
+ * records events[0] on its stream before its first timed kernel and events[k]
+ * right after its k-th timed stage, for k < n_events.  The timed stages of
+ * the forward are the expert up-projection and down-projection (GEMV,
+ * CHUNK_MFMA and DENSE modes), plus the per-token combine in GROUPED mode.
+ * Those of the backward are: pair planning with the weight transposes, the
+ * fused per-pair pass, the router and weight gradients, the per-pair input
+ * gradient rows, and the per-token combine.  `events` are caller-created
+ * hipEvents in caller memory that must stay valid while set; pass NULL to
+ * stop.  Errors: SHAPE (n_events < 1 with non-NULL events).
  */
 int blockffn_set_stage_events(hipEvent_t* events, int32_t n_events);
 

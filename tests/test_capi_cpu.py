@@ -15,7 +15,7 @@ import tempfile
 import pytest
 
 from activation_sparse_moe_amd import _capi
-from activation_sparse_moe_amd._capi import BlockffnLayer, BlockffnStats
+from activation_sparse_moe_amd._capi import BlockffnGrads, BlockffnLayer, BlockffnStats
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "blockffn.h")
@@ -64,6 +64,8 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu\n", sizeof(blockffn_layer), offsetof(blockffn_layer, layer_stride),
          offsetof(blockffn_layer, w_router), offsetof(blockffn_layer, w_out), sizeof(blockffn_stats));
   printf("%zu %zu\n", offsetof(blockffn_stats, active_pairs), offsetof(blockffn_stats, hist));
+  printf("%zu %zu %zu\n", sizeof(blockffn_grads), offsetof(blockffn_grads, d_rms_scale),
+         offsetof(blockffn_grads, d_w_out));
   return 0;
 }
 """
@@ -79,6 +81,8 @@ int main(void) {
     assert a == [ctypes.sizeof(BlockffnLayer), BlockffnLayer.layer_stride.offset, BlockffnLayer.w_router.offset,
                  BlockffnLayer.w_out.offset, ctypes.sizeof(BlockffnStats)]
     assert b == [BlockffnStats.active_pairs.offset, BlockffnStats.hist.offset]
+    c = [int(v) for v in lines[2].split()]
+    assert c == [ctypes.sizeof(BlockffnGrads), BlockffnGrads.d_rms_scale.offset, BlockffnGrads.d_w_out.offset]
 
 
 def test_version_and_status_strings(lib):
@@ -195,3 +199,46 @@ def test_workspace_size(lib):
         T * 64 * 128 * 4 + r256(8 * (T + 1))
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 3, _capi.MODE_AUTO) == 0   # ragged
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, 99) == 0
+
+
+def _grads(**kw):
+    f = dict(d_w_router=P, d_b_router=P, d_rms_scale=P, d_w_in=P, d_w_out=P)
+    f.update(kw)
+    return BlockffnGrads(**f)
+
+
+def _backward(lib, layer, T=16, x=P, preact=P, dy=P, ws=P, ws_bytes=1 << 40, dx=P, grads=None):
+    g = _grads() if grads is None else grads
+    return lib.blockffn_backward(ctypes.byref(layer) if layer is not None else None, x, T, preact, dy, ws, ws_bytes,
+                                 dx, ctypes.byref(g), None)
+
+
+@cpu_only
+def test_backward_validation(lib):
+    ok = _layer(d=256, n_experts=16, d_expert=128)
+    assert _backward(lib, None) == _capi.ERR_NULL
+    assert _backward(lib, _layer(dtype=0)) == _capi.ERR_MODE            # bf16 only
+    assert _backward(lib, _layer(d_expert=64)) == _capi.ERR_MODE        # d_expert 128 or 256
+    assert _backward(lib, _layer(d=192)) == _capi.ERR_MODE              # d a multiple of 128
+    assert _backward(lib, ok, T=-1) == _capi.ERR_SHAPE
+    assert _backward(lib, ok, T=1 << 27) == _capi.ERR_SHAPE             # pairs indexed with 32 bits
+    assert _backward(lib, ok, T=0, x=None, preact=None, dy=None, ws=None, dx=None) == _capi.OK
+    assert _backward(lib, ok, preact=None) == _capi.ERR_NULL
+    assert _backward(lib, ok, dx=None) == _capi.ERR_NULL
+    assert _backward(lib, ok, grads=_grads(d_w_in=None)) == _capi.ERR_NULL
+    assert _backward(lib, ok, dy=P + 4) == _capi.ERR_ALIGN
+    assert _backward(lib, ok, grads=_grads(d_w_out=P + 8)) == _capi.ERR_ALIGN
+    assert _backward(lib, ok, ws=P + 16) == _capi.ERR_ALIGN
+    assert _backward(lib, ok, ws_bytes=4096) == _capi.ERR_WORKSPACE
+    assert b"workspace" in lib.blockffn_last_error()
+
+
+def test_backward_workspace_size(lib):
+    lay = _layer(d=4096, n_experts=128, d_expert=128)
+    T = 4096
+    n = lib.blockffn_backward_workspace_size(ctypes.byref(lay), T)
+    P_ = T * 128
+    # at least: pair arrays, transposed weights, hidden gradients, partial rows
+    assert n >= 3 * 4 * P_ + 2 * (2 * 128 * 4096 * 128) + 2 * (2 * P_ * 128) + 2 * P_ * 4096
+    assert lib.blockffn_backward_workspace_size(ctypes.byref(_layer(dtype=0)), T) == 0
+    assert lib.blockffn_backward_workspace_size(ctypes.byref(lay), -1) == 0

@@ -268,3 +268,19 @@ def test_grouped_full_size_sampled():
     y_ref = oracle.forward_tokens(tok.x[tok_idx], layer.w_in, layer.w_out, g[tok_idx], m[tok_idx])
     rel = check_y(gpu["y"][tok_idx], y_ref, keep[tok_idx], cfg.dtype, cfg.name)
     say(f"  {cfg.name}: sampled {len(sample)} chunks, max|dy|/rms {rel:.2e}, band flips {len(flipped)}")
+
+
+def test_grouped_mode_signed_scales():
+    # a negative RMS scale gives active pairs negative gates; the grouped path
+    # must still include them (pairs are the non-zero gates)
+    d, E, de, L, C = 256, 16, 128, 8, 6
+    rng = np.random.default_rng(506)
+    layer = make_layer(d, E, de, "bf16", 0.3, rng)
+    layer.rms_scale = (rng.random(E) * 2.0 - 0.7).astype(np.float32)
+    x = make_tokens(d, C, L, 0.6, "bf16", rng).x
+    say(f"[gpu] grouped signed scales T={x.shape[0]}")
+    dl = B.DeviceLayer.from_workload(layer)
+    xd = B.tokens_to_device(x, BF16)
+    gpu = run_gpu(dl, xd, L, mode="grouped")
+    assert (gpu["g"] < 0).any()
+    _compare_all(layer, x, L, gpu, "grouped/signed_scales")

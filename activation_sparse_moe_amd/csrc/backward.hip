@@ -22,7 +22,8 @@
 //            partial dg = sum over the tile's hidden units of Q Swish(U)
 //   router:  dz, ds terms per token; then db, ds by sums over tokens
 //   weights: dW_out[i] = dY_p^T HG_p, dW_in[i] = dU_p^T X_p and
-//            dW_r = dZ^T X, each a sum over pairs (tokens) in fp32 by a
+//            dW_r = dZ^T X (over token ranges, then summed in order), each a
+//            sum over pairs (tokens) in fp32 by a
 //            "transposing" grouped GEMM (the pair rows are written to LDS
 //            transposed, so the contraction runs over pairs)
 //   dx:      Part = dU W_in[i] per pair (the forward's down GEMM on the
@@ -36,8 +37,9 @@
 namespace bffn {
 namespace {
 
-constexpr int TBM = 128, TBN = 128, TBK = 32;  // transposing GEMM tile
+constexpr int TBM = 128, TBN = 128, TBK = 32;  // transposing GEMM tile (TBK pairs per step)
 constexpr int kRouterPad = 128;               // dZ rows padded to 128 experts (bf16)
+constexpr int kRouterSplits = 16;             // dW_r: token range split for parallelism
 
 // ---- prep: gates and 1/RMS as the router computes them; dy -> bf16 ----
 // One block per token: wave 0 does the router quantities, all threads convert dy.
@@ -60,10 +62,8 @@ __global__ __launch_bounds__(kBlock) void bwd_prep_kernel(const float* __restric
     if (v1) g_out[t * E + lane + 64] = s1 * a1 * inv;
     if (lane == 0) r_out[t] = inv;
   }
-  if (t == 0 && tid == 64) {
-    all_off[0] = 0;
-    all_off[1] = T;
-  }
+  if (t == 0 && tid >= 64 && tid <= 64 + kRouterSplits)  // token range of each dW_r split
+    all_off[tid - 64] = T * (tid - 64) / kRouterSplits;
   for (int c = tid * 8; c < d; c += kBlock * 8) {
     const f32x4 v0 = *reinterpret_cast<const f32x4*>(dy + t * d + c);
     const f32x4 v1 = *reinterpret_cast<const f32x4*>(dy + t * d + c + 4);
@@ -351,6 +351,17 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_kernel(const float* __restr
   }
 }
 
+// ---- dW_r = sum of the split partials, in split order ----
+__global__ __launch_bounds__(kBlock) void bwd_router_sum_kernel(const float* __restrict__ part, int64_t n,
+                                                                float* __restrict__ out) {
+  const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (k >= n) return;
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < kRouterSplits; ++q) s += part[q * n + k];
+  out[k] = s;
+}
+
 // ---- transposing grouped GEMM: C_g[m][n] = sum over pairs p of group g of A[ra(p)][m] B[rb(p)][n] ----
 struct TGemmArgs {
   const uint16_t* a;        // rows of M (or more) bf16 elements, row stride lda
@@ -365,11 +376,15 @@ struct TGemmArgs {
   int G, M, M_valid, N;
 };
 
-// LDS tile of 128 rows (m or n) x 32 pairs, 64-byte rows; 16-byte chunk
-// (8 pairs) XOR (row >> 2) & 3 so the 16 rows of an operand read hit
-// different bank groups.
+// LDS tile of 128 rows (m or n) x 32 pairs, 64-byte rows.  The 16-byte chunk
+// (8 pairs) c of row r sits at position c ^ f(r), f(r) = ((r >> 2) ^ (r >> 3))
+// & 3: the 16 consecutive rows an MFMA operand read touches then hit 16
+// different bank groups, and the 8-byte transposed writes (two rows 8 apart,
+// 8 groups of 4 pairs each) collide at most 2-way.  (Steps of 64 pairs in
+// 128-byte rows measured slower: the extra prefetch registers cost a wave of
+// occupancy per SIMD, and the gathers need the latency hiding.)
 __device__ __forceinline__ int tl_off(int row, int p) {
-  return row * 64 + ((((p >> 3) ^ (row >> 2)) & 3) << 4) + (p & 7) * 2;
+  return row * 64 + (((p >> 3) ^ (row >> 2) ^ (row >> 3)) & 3) * 16 + (p & 7) * 2;
 }
 
 __global__ __launch_bounds__(kBlock) void tgemm_kernel(TGemmArgs ta) {
@@ -395,36 +410,37 @@ __global__ __launch_bounds__(kBlock) void tgemm_kernel(TGemmArgs ta) {
     const int64_t n_p = ta.grp_off[grp + 1] - p0;
     const int ksteps = (int)((n_p + TBK - 1) / TBK);
 
-    // this thread's two 16-byte chunks of each operand per step: pair row
-    // c >> 4 (of 32), elements (c & 15) * 8 .. +7 of the 128-wide tile
-    u32x4 ra[2], rb[2];
+    // Waves 0-1 stage operand A, waves 2-3 operand B.  Thread task u (of
+    // 128): pairs 4 (u & 7) .. +3 of the step, elements 8 (u >> 3) .. +7 of
+    // the 128-wide tile: four 16-byte row loads, regrouped in registers into
+    // eight 8-byte LDS writes (the 4 pairs of one element each).
+    const bool op_b = tid >= 128;
+    const int u = tid & 127, pg = u & 7, ch = u >> 3;
+    const uint16_t* src = op_b ? ta.b : ta.a;
+    const int64_t ld = op_b ? ta.ldb : ta.lda;
+    const int32_t* rows_of = op_b ? ta.b_rows : ta.a_rows;
+    const int col0 = (op_b ? n0 : m0) + ch * 8;
+    u32x4 rv[4];
     auto gload = [&](int s) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = tid + j * kBlock, pr = c >> 4, ch = c & 15;
-        const int64_t p = (int64_t)s * TBK + pr;
-        u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = u32x4{0u, 0u, 0u, 0u};
+      for (int k = 0; k < 4; ++k) {
+        const int64_t p = (int64_t)s * TBK + pg * 4 + k;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
         if (p < n_p) {  // pairs past the group contribute zero
-          const int64_t rowa = ta.a_rows ? (int64_t)ta.a_rows[p0 + p] : p0 + p;
-          const int64_t rowb = ta.b_rows ? (int64_t)ta.b_rows[p0 + p] : p0 + p;
-          va = *reinterpret_cast<const u32x4*>(ta.a + rowa * ta.lda + m0 + ch * 8);
-          vb = *reinterpret_cast<const u32x4*>(ta.b + rowb * ta.ldb + n0 + ch * 8);
+          const int64_t row = rows_of ? (int64_t)rows_of[p0 + p] : p0 + p;
+          v = *reinterpret_cast<const u32x4*>(src + row * ld + col0);
         }
-        ra[j] = va;
-        rb[j] = vb;
+        rv[k] = v;
       }
     };
-    auto swrite = [&](int buf) {  // transposed: element (pair pr, row ch*8 + e) -> LDS row ch*8 + e
+    auto swrite = [&](int buf) {  // transposed: element e of the 4 pairs -> LDS row ch*8 + e
+      uint8_t* dst = op_b ? lds_b[buf] : lds_a[buf];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = tid + j * kBlock, pr = c >> 4, ch = c & 15;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          *reinterpret_cast<uint16_t*>(&lds_a[buf][tl_off(ch * 8 + 2 * q, pr)]) = (uint16_t)(ra[j][q] & 0xffffu);
-          *reinterpret_cast<uint16_t*>(&lds_a[buf][tl_off(ch * 8 + 2 * q + 1, pr)]) = (uint16_t)(ra[j][q] >> 16);
-          *reinterpret_cast<uint16_t*>(&lds_b[buf][tl_off(ch * 8 + 2 * q, pr)]) = (uint16_t)(rb[j][q] & 0xffffu);
-          *reinterpret_cast<uint16_t*>(&lds_b[buf][tl_off(ch * 8 + 2 * q + 1, pr)]) = (uint16_t)(rb[j][q] >> 16);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 lo = u32x2{(rv[0][q] & 0xffffu) | (rv[1][q] << 16), (rv[2][q] & 0xffffu) | (rv[3][q] << 16)};
+        const u32x2 hi = u32x2{(rv[0][q] >> 16) | (rv[1][q] & 0xffff0000u), (rv[2][q] >> 16) | (rv[3][q] & 0xffff0000u)};
+        *reinterpret_cast<u32x2*>(dst + tl_off(ch * 8 + 2 * q, pg * 4)) = lo;
+        *reinterpret_cast<u32x2*>(dst + tl_off(ch * 8 + 2 * q + 1, pg * 4)) = hi;
       }
     };
 
@@ -441,19 +457,22 @@ __global__ __launch_bounds__(kBlock) void tgemm_kernel(TGemmArgs ta) {
     for (int s = 0; s < ksteps; ++s) {
       const int cur = s & 1;
       if (s + 1 < ksteps) gload(s + 1);
-      u32x4 av[4], bv[4];
 #pragma unroll
-      for (int sa = 0; sa < 4; ++sa)
-        av[sa] = *reinterpret_cast<const u32x4*>(&lds_a[cur][tl_off(wm * 64 + sa * 16 + m16, g * 8)]);
+      for (int kk = 0; kk < TBK / 32; ++kk) {
+        u32x4 av[4], bv[4];
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-        bv[sb] = *reinterpret_cast<const u32x4*>(&lds_b[cur][tl_off(wn * 64 + sb * 16 + m16, g * 8)]);
-#pragma unroll
-      for (int sa = 0; sa < 4; ++sa)
+        for (int sa = 0; sa < 4; ++sa)
+          av[sa] = *reinterpret_cast<const u32x4*>(&lds_a[cur][tl_off(wm * 64 + sa * 16 + m16, kk * 32 + g * 8)]);
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
-          acc[sa][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[sa]), as_bf16x8(bv[sb]), acc[sa][sb], 0,
-                                                                0, 0);
+          bv[sb] = *reinterpret_cast<const u32x4*>(&lds_b[cur][tl_off(wn * 64 + sb * 16 + m16, kk * 32 + g * 8)]);
+#pragma unroll
+        for (int sa = 0; sa < 4; ++sa)
+#pragma unroll
+          for (int sb = 0; sb < 4; ++sb)
+            acc[sa][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[sa]), as_bf16x8(bv[sb]), acc[sa][sb],
+                                                                  0, 0, 0);
+      }
       if (s + 1 < ksteps) swrite(cur ^ 1);
       __syncthreads();
     }
@@ -526,7 +545,7 @@ struct BwdLayout {
   int32_t* blk;
   int64_t *pair_off, *tile_up, *all_off;
   int32_t *pair_tok, *pair_idx;
-  float *pair_gate, *g_b, *r_b, *dgp, *dz, *dsc;
+  float *pair_gate, *g_b, *r_b, *dgp, *dz, *dsc, *wr_part;
   uint16_t *dyb, *w_inT, *w_outT, *du, *hg, *dzb, *part, *trash;
   size_t bytes;
 };
@@ -545,7 +564,8 @@ BwdLayout bwd_layout(char* base, int64_t T, int E, int d, int de) {
   L.blk = reinterpret_cast<int32_t*>(take(4 * nblk * E));
   L.pair_off = reinterpret_cast<int64_t*>(take(8 * (size_t)(E + 1)));
   L.tile_up = reinterpret_cast<int64_t*>(take(8 * (size_t)(E + 1)));
-  L.all_off = reinterpret_cast<int64_t*>(take(16));
+  L.all_off = reinterpret_cast<int64_t*>(take(8 * (kRouterSplits + 1)));
+  L.wr_part = reinterpret_cast<float*>(take(4 * (size_t)kRouterSplits * E * d));
   L.pair_tok = reinterpret_cast<int32_t*>(take(4 * P));
   L.pair_gate = reinterpret_cast<float*>(take(4 * P));
   L.pair_idx = reinterpret_cast<int32_t*>(take(4 * P));
@@ -617,9 +637,12 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   // dW_in[i][j][k] = sum_p dU[p][j] X[t_p][k]
   TGemmArgs gi{L.du, de, nullptr, x, d, L.pair_tok, L.pair_off, d_w_in, d, (int64_t)de * d, E, de, de, d};
   tgemm_kernel<<<dim3((unsigned)grid_t), dim3(kBlock), 0, s>>>(gi);
-  // dW_r[i][k] = sum_t dZ[t][i] X[t][k]  (one group: all tokens)
-  TGemmArgs gr{L.dzb, kRouterPad, nullptr, x, d, nullptr, L.all_off, d_w_router, d, 0, 1, kRouterPad, E, d};
+  // dW_r[i][k] = sum_t dZ[t][i] X[t][k]: kRouterSplits token ranges as groups, then their sum
+  TGemmArgs gr{L.dzb, kRouterPad, nullptr, x, d, nullptr, L.all_off, L.wr_part, d, (int64_t)E * d, kRouterSplits,
+               kRouterPad, E, d};
   tgemm_kernel<<<dim3((unsigned)grid_t), dim3(kBlock), 0, s>>>(gr);
+  bwd_router_sum_kernel<<<dim3((unsigned)(((int64_t)E * d + kBlock - 1) / kBlock)), dim3(kBlock), 0, s>>>(
+      L.wr_part, (int64_t)E * d, d_w_router);
   se.record(3, s);
   // dx: per-pair dU W_in[i] rows (the forward's down GEMM on W_in^T), then the per-token sum
   DownArgs dn{L.du, L.w_inT, L.pair_off, L.part, L.trash, d, E};

@@ -38,7 +38,8 @@ namespace {
 
 constexpr int GBM = 64, GBN = 128, GBK = 64;
 constexpr int kPlanThreads = 128;     // one thread per expert (E <= 128)
-constexpr int kPlanMaxBlocks = 2048;  // token blocks of the count / fill kernels
+constexpr int kPlanMaxBlocks = 512;   // token blocks of the count / fill kernels
+constexpr int kPlanMinRows = 32;      // tokens per block at least (short scans)
 constexpr size_t kTrashBytes = GBM * 256;  // one staged output tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -57,7 +58,7 @@ __device__ __forceinline__ int lds_off(int r, int c) {
 
 int plan_rows(int64_t T) {
   const int64_t r = (T + kPlanMaxBlocks - 1) / kPlanMaxBlocks;
-  return (int)(r < 8 ? 8 : r);
+  return (int)(r < kPlanMinRows ? kPlanMinRows : r);
 }
 
 // Which (token, expert) entries form pairs: the forward takes every pair with
@@ -81,7 +82,13 @@ __global__ __launch_bounds__(kPlanThreads) void group_count_kernel(const float* 
   const int64_t t0 = (int64_t)blockIdx.x * rows;
   const int64_t t1 = t0 + rows < T ? t0 + rows : T;
   int c = 0;
-  for (int64_t t = t0; t < t1; ++t) c += pair_selected<R>(sel[t * E + i]);
+  for (int64_t t = t0; t < t1; t += 8) {  // eight loads in flight
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = t + u < t1 ? sel[(t + u) * E + i] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c += pair_selected<R>(v[u]);
+  }
   blk[(int64_t)blockIdx.x * E + i] = c;
 }
 
@@ -181,12 +188,21 @@ __global__ __launch_bounds__(kPlanThreads) void group_fill_kernel(const float* _
   const int64_t t0 = (int64_t)blockIdx.x * rows;
   const int64_t t1 = t0 + rows < T ? t0 + rows : T;
   int32_t p = blk_off[(int64_t)blockIdx.x * E + i];
-  for (int64_t t = t0; t < t1; ++t) {
-    if (pair_selected<R>(sel[t * E + i])) {
-      pair_tok[p] = (int32_t)t;
-      pair_gate[p] = val[t * E + i];
-      pair_idx[t * E + i] = p;
-      ++p;
+  for (int64_t t = t0; t < t1; t += 8) {  // eight tokens' loads in flight, then in order
+    float sv[8], vv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sv[u] = t + u < t1 ? sel[(t + u) * E + i] : 0.f;
+      vv[u] = t + u < t1 ? val[(t + u) * E + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (pair_selected<R>(sv[u])) {  // (0 past t1: never selected)
+        pair_tok[p] = (int32_t)(t + u);
+        pair_gate[p] = vv[u];
+        pair_idx[(t + u) * E + i] = p;
+        ++p;
+      }
     }
   }
 }

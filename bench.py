@@ -42,6 +42,8 @@ def parse_args(argv=None):
     p.add_argument("--mode", default=None, help="forward mode (default: the workload's)")
     p.add_argument("--dense-steps", type=int, default=5, help="steps of the dense all-experts comparison (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--backward", action="store_true",
+                   help="also time blockffn_backward on the batch (grouped workloads: one layer)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
@@ -305,6 +307,87 @@ def torch_dense_reference_ms(runner, steps: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
+def torch_dense_backward_ms(runner, dy, steps: int) -> float:
+    """The dense all-experts layer's backward through torch autograd (hipBLASLt
+    bf16 GEMMs over the concatenated experts, gates recomputed from z): the
+    comparison for blockffn_backward on the same batch."""
+    import torch
+    t = runner.dl.tensors(0)
+    E, d, de = runner.cfg.n_experts, runner.cfg.d, runner.cfg.d_expert
+    w_in_t = t["w_in"].reshape(E * de, d).t().contiguous().requires_grad_(True)   # [d][E d_e]
+    w_out = t["w_out"].permute(0, 2, 1).reshape(E * de, d).contiguous().requires_grad_(True)
+    w_r = t["w_router"].detach().clone().float().requires_grad_(True)
+    b = t["b_router"].detach().clone().requires_grad_(True)
+    x = runner.xd.detach().clone().requires_grad_(True)
+    dyb = dy.to(torch.bfloat16)
+    eps = runner.layer.rms_eps
+
+    def step():
+        z = x.float() @ w_r.t() + b
+        a = torch.relu(z)
+        g = a / torch.sqrt((a * a).mean(dim=1, keepdim=True) + eps)
+        u = torch.matmul(x, w_in_t)
+        h = (torch.nn.functional.silu(u.float()) * g.repeat_interleave(de, dim=1)).to(torch.bfloat16)
+        y = torch.matmul(h, w_out)
+        y.backward(dyb)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def backward_measure(runner, steps: int, warmup: int, dense_steps: int) -> dict:
+    """Times blockffn_backward on the workload's batch (one layer), with the
+    library's stage events, and reports algorithmic matrix flops."""
+    import numpy as np
+    import torch
+    B, cfg = runner.B, runner.cfg
+    T, d, E, de = cfg.n_tokens, cfg.d, cfg.n_experts, cfg.d_expert
+    _, _, z = B.blockffn_route(runner.dl, runner.xd, cfg.chunk_len, n_layers=1, want_preact=True)
+    dy = torch.from_numpy(np.random.default_rng(cfg.seed + 100).standard_normal((T, d)).astype(np.float32)).cuda()
+    ws = B.alloc_backward_workspace(runner.dl, T)
+    out = B.blockffn_backward(runner.dl, runner.xd, z, dy, workspace=ws)
+    for _ in range(warmup):
+        B.blockffn_backward(runner.dl, runner.xd, z, dy, workspace=ws, dx=out["dx"],
+                            grads={k: v for k, v in out.items() if k != "dx"})
+    torch.cuda.synchronize()
+    names = ("plan", "pair", "weights", "dx_rows", "combine")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    for row in ev:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    handles = [(ctypes.c_void_p * len(row))(*[e.cuda_event for e in row]) for row in ev]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(steps):
+        runner.lib.blockffn_set_stage_events(ctypes.cast(handles[k], ctypes.c_void_p), len(names) + 1)
+        B.blockffn_backward(runner.dl, runner.xd, z, dy, workspace=ws, dx=out["dx"],
+                            grads={k2: v for k2, v in out.items() if k2 != "dx"})
+        runner.lib.blockffn_set_stage_events(None, 0)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    stage = {n: round(sum(ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(steps)) / steps, 5)
+             for j, n in enumerate(names)}
+    P = int((z > 0).sum().item())
+    flops = 10 * P * d * de + 2 * T * E * d   # U, Q, dW_in, dW_out, dx rows; dW_r
+    res = {"ms": round(ms, 5), "stage_ms": stage, "pairs": P, "algorithmic_flops": flops,
+           "tflops": round(flops / ms / 1e9, 1), "frac_of_bf16_mfma_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if dense_steps > 0:
+        dms = torch_dense_backward_ms(runner, dy, dense_steps)
+        res["torch_dense_autograd_ms"] = round(dms, 4)
+        res["speedup_vs_dense_autograd"] = round(dms / ms, 3)
+    return res
+
+
 def copy_calibration():
     """A plain device copy of 1 GiB: its FETCH_SIZE / WRITE_SIZE counters
     scale the expert kernels' counters to bytes."""
@@ -377,6 +460,10 @@ def main(argv=None) -> int:
                     "algorithmic_bytes_per_launch": bytes_per[dom] // runner.n_sub,
                     "avg_launch_ms": round(avg[dom] / runner.n_sub, 5), "launches_per_step": runner.n_sub}
 
+    backward = None
+    if args.backward:
+        backward = backward_measure(runner, args.steps, args.warmup, args.dense_steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, runner.layer, runner.x_host, args.cpu_seconds)
@@ -404,6 +491,7 @@ def main(argv=None) -> int:
                          down_tflops=round(runner.flop_model()["down_flops"] / avg["down"] / 1e9, 1))
                     if grouped else None),
         "dense": dense,
+        "backward": backward,
         "sparsity": {"tls": round(st["tls"], 4), "cls": round(st["cls"], 4), "mean_union": round(U / (T // cfg.chunk_len), 2),
                      "reuse": round(st["reuse"], 4)},
         "source_digest": source_digest(),

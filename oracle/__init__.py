@@ -69,12 +69,13 @@ def _load():
             lib.oracle_forward_dense.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, vp]
             lib.oracle_union.argtypes = [i32, vp, i64, i32, vp, vp, vp]
             lib.oracle_stats.argtypes = [i32, vp, i64, i32, ctypes.POINTER(OracleStats)]
+            lib.oracle_route_with.argtypes = [i32, i32, i32, vp, i64, vp, vp, i32, i32, vp, vp, vp]
             lib.oracle_backward.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, dbl, vp, vp, vp, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp, vp]
             lib.oracle_num_threads.argtypes = []
             for name in ("oracle_route", "oracle_expert", "oracle_forward_tokens",
                          "oracle_forward_chunks", "oracle_forward_dense", "oracle_union",
-                         "oracle_stats", "oracle_backward", "oracle_num_threads"):
+                         "oracle_stats", "oracle_backward", "oracle_route_with", "oracle_num_threads"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -126,6 +127,26 @@ def route(x, w_router, b_router=None, rms_scale=None, eps: float = 1e-6):
     m = np.empty((T, mask_words(E)), np.uint64)
     _check(_load().oracle_route(d, E, code, _p(x), T, _p(w_router), _p(b), _p(s), float(eps),
                                 _p(z), _p(g), _p(m)), "oracle_route")
+    return z, g, m
+
+
+ROUTER_TOPK_SOFTMAX, ROUTER_RELU_SUM = 1, 2
+
+
+def route_with(x, w_router, b_router, kind: int, top_k: int = 0):
+    """Baseline routers: kind 1 = top-k of a softmax, kind 2 = ReLU divided by its sum.
+    Returns (z, g, mask) like route()."""
+    x, w_router = _c(x), _c(w_router)
+    code = _dtype_code(x)
+    assert _dtype_code(w_router) == code
+    T, d = x.shape
+    E = w_router.shape[0]
+    b = _c(b_router, np.float32)
+    z = np.empty((T, E), np.float64)
+    g = np.empty((T, E), np.float64)
+    m = np.empty((T, mask_words(E)), np.uint64)
+    _check(_load().oracle_route_with(d, E, code, _p(x), T, _p(w_router), _p(b), int(kind), int(top_k), _p(z), _p(g),
+                                     _p(m)), "oracle_route_with")
     return z, g, m
 
 

@@ -117,6 +117,78 @@ int oracle_route(int32_t d, int32_t E, int32_t dtype, const void *x, int64_t T,
 }
 
 /*
+ * Baseline routers for comparison (the MoE architecture blog on
+ * intelliparadigm.com: §2.1 gives the Switch Transformer router as a
+ * softmax over x W_r with TOP-K selection, K usually 2; §5.1 gives ReMoE as
+ * G(x) = ReLU(x W_g) with the output divided by the sum of G).  Same z as
+ * oracle_route (bias included); rms_scale and eps are not used.
+ *   kind 1 (top-k softmax): p = softmax over all E of z (shifted by max z);
+ *          the k largest z are selected, lower index first among equal z;
+ *          g_i = p_i for the selected experts, 0 elsewhere; mask = selected
+ *   kind 2 (ReLU, sum-normalised): a = max(z, 0), g_i = a_i / sum_j a_j
+ *          (0 when no expert fires); mask bit i = [z_i > 0]
+ */
+int oracle_route_with(int32_t d, int32_t E, int32_t dtype, const void *x, int64_t T, const void *w_router,
+                      const float *b_router, int32_t kind, int32_t top_k, double *z_out, double *g_out,
+                      uint64_t *mask_out) {
+  if (d <= 0 || E <= 0 || T < 0 || (kind != 1 && kind != 2) || (kind == 1 && (top_k < 1 || top_k > E)))
+    return -1;
+  const int W = mask_words(E);
+  int err = 0;
+#pragma omp parallel
+  {
+    uint8_t *taken = (uint8_t *)malloc((size_t)E);
+    if (!taken) {
+#pragma omp atomic write
+      err = -2;
+    }
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      double *z = z_out + t * E;
+      double *g = g_out + t * E;
+      uint64_t *m = mask_out + t * W;
+      for (int w = 0; w < W; ++w) m[w] = 0;
+      for (int i = 0; i < E; ++i) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k)
+          acc += widen(w_router, (int64_t)i * d + k, dtype) * widen(x, t * d + k, dtype);
+        if (b_router) acc += (double)b_router[i];
+        z[i] = acc;
+        g[i] = 0.0;
+      }
+      if (!taken) continue;
+      if (kind == 1) {
+        double zmax = z[0];
+        for (int i = 1; i < E; ++i)
+          if (z[i] > zmax) zmax = z[i];
+        double sum = 0.0;
+        for (int i = 0; i < E; ++i) sum += exp(z[i] - zmax);
+        for (int i = 0; i < E; ++i) taken[i] = 0;
+        for (int r = 0; r < top_k; ++r) {
+          int best = -1;
+          for (int i = 0; i < E; ++i)
+            if (!taken[i] && (best < 0 || z[i] > z[best])) best = i;
+          taken[best] = 1;
+          g[best] = exp(z[best] - zmax) / sum;
+          m[best / 64] |= (uint64_t)1 << (best % 64);
+        }
+      } else {
+        double sum = 0.0;
+        for (int i = 0; i < E; ++i) sum += z[i] > 0.0 ? z[i] : 0.0;
+        for (int i = 0; i < E; ++i) {
+          if (z[i] > 0.0) {
+            g[i] = z[i] / sum;
+            m[i / 64] |= (uint64_t)1 << (i % 64);
+          }
+        }
+      }
+    }
+    free(taken);
+  }
+  return err;
+}
+
+/*
  * One expert on one token (write-up §2: a non-gated MLP with Swish):
  * u = W_in[i] x (d_e values), h = Swish(u), e = W_out[i] h (d values).
  * w_in_i points at W_in[i] ([d_e][d]) and w_out_i at W_out[i] ([d][d_e]);

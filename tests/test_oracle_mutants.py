@@ -9,7 +9,8 @@ instead of OR for the union, a chunk boundary off by one, a wrong bf16
 widening, a wrong reuse denominator, a flipped bias sign; and in the backward
 a dropped or sign-flipped RMSNorm term, a wrong Swish derivative, a dropped
 gate, gradients taken through inactive pairs, a wrong scale gradient, a dropped router term of
-dx, a missing gate in dW_out.
+dx, a missing gate in dW_out; and in the baseline routers a tie broken the
+other way, an unshifted softmax sum, a missing ReMoE normalisation.
 """
 import os
 import subprocess
@@ -56,8 +57,14 @@ MUTANTS = {
                               "for (int i = 0; i < E; ++i) acc += 0.0 * dz[t * E + i] * widen(w_router,"),
     "bwd_w_out_grad_gate_dropped": ("go[(int64_t)k * de + j] += gti * (double)dy[t * d + k] * h[j];",
                                     "go[(int64_t)k * de + j] += (double)dy[t * d + k] * h[j];"),
+    # the baseline routers
+    "topk_tie_to_higher_index": ("if (!taken[i] && (best < 0 || z[i] > z[best])) best = i;",
+                                 "if (!taken[i] && (best < 0 || z[i] >= z[best])) best = i;"),
+    "topk_softmax_unshifted_sum": ("for (int i = 0; i < E; ++i) sum += exp(z[i] - zmax);",
+                                   "for (int i = 0; i < E; ++i) sum += exp(z[i]);"),
+    "relu_sum_unnormalised": ("g[i] = z[i] / sum;", "g[i] = z[i];"),
 }
-PIN_FILES = ("test_oracle_pins.py", "test_oracle_backward_pins.py")
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_backward_pins.py", "test_oracle_router_pins.py")
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(PKG, "libblockffn.so")
 
 F32, BF16 = 0, 1
 MODE_AUTO, MODE_GEMV, MODE_CHUNK_MFMA, MODE_GROUPED, MODE_DENSE = 0, 1, 2, 3, 4
+ROUTER_BLOCKFFN, ROUTER_TOPK_SOFTMAX, ROUTER_RELU_SUM = 0, 1, 2
+ROUTERS = {"blockffn": ROUTER_BLOCKFFN, "topk_softmax": ROUTER_TOPK_SOFTMAX, "relu_sum": ROUTER_RELU_SUM}
 MODES = {"auto": MODE_AUTO, "gemv": MODE_GEMV, "chunk_mfma": MODE_CHUNK_MFMA, "grouped": MODE_GROUPED,
          "dense": MODE_DENSE}
 
@@ -23,7 +25,7 @@ ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_CHUNK, ERR_WORKSPACE = -1, -2, -3, -4, -5
 ERR_MODE, ERR_ALIGN, ERR_LAYERS, ERR_HIP = -6, -7, -8, -9
 
 # Every symbol include/blockffn.h declares.
-EXPORTS = ("blockffn_route", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats",
+EXPORTS = ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats",
            "blockffn_backward", "blockffn_backward_workspace_size",
            "blockffn_set_stage_events", "blockffn_workspace_size", "blockffn_status_string",
            "blockffn_last_error", "blockffn_version")
@@ -75,14 +77,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         lp = ctypes.POINTER(BlockffnLayer)
         lib.blockffn_route.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, vp]
+        lib.blockffn_route_with.argtypes = [lp, i32, vp, i64, i32, i32, i32, vp, vp, vp, vp]
         lib.blockffn_chunk_union.argtypes = [i32, vp, i64, i32, vp, vp, vp, vp]
         lib.blockffn_forward.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, i32, vp, sz, vp, vp]
         lib.blockffn_sparsity_stats.argtypes = [i32, vp, i64, i32, vp, vp]
         lib.blockffn_backward.argtypes = [lp, vp, i64, vp, vp, vp, sz, vp, ctypes.POINTER(BlockffnGrads), vp]
         lib.blockffn_backward_workspace_size.argtypes = [lp, i64]
         lib.blockffn_backward_workspace_size.restype = sz
-        for f in ("blockffn_route", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats",
-                  "blockffn_backward"):
+        for f in ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward",
+                  "blockffn_sparsity_stats", "blockffn_backward"):
             getattr(lib, f).restype = ctypes.c_int
         lib.blockffn_set_stage_events.argtypes = [vp, i32]
         lib.blockffn_set_stage_events.restype = ctypes.c_int

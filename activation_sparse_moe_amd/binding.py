@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import _capi
-from ._capi import BF16, F32, MODES, BlockffnGrads, BlockffnLayer, check, load
+from ._capi import BF16, F32, MODES, ROUTERS, BlockffnGrads, BlockffnLayer, check, load
 
 _ALIGN = 256
 _STATS_WORDS = 8 + 129
@@ -156,6 +156,27 @@ def blockffn_route(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, n_layers
     nl = layer.replicas if n_layers is None else n_layers
     check(load().blockffn_route(ctypes.byref(desc), nl, _ptr(x), T, chunk_len, _ptr(gates), _ptr(token_masks),
                                 _ptr(preact), _stream(stream)), "blockffn_route")
+    return gates, token_masks, preact
+
+
+def blockffn_route_with(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, router="blockffn", top_k: int = 0,
+                        n_layers: Optional[int] = None, gates: Optional[torch.Tensor] = None,
+                        token_masks: Optional[torch.Tensor] = None, preact: Optional[torch.Tensor] = None,
+                        want_preact: bool = False, stream=None):
+    """Router with a selectable gate function ("blockffn", "topk_softmax" with top_k, "relu_sum")."""
+    T = x.shape[0]
+    E = layer.n_experts
+    kind = ROUTERS[router] if isinstance(router, str) else int(router)
+    if gates is None:
+        gates = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    if token_masks is None:
+        token_masks = torch.empty((T, layer.mask_words), dtype=torch.int64, device=x.device)
+    if want_preact and preact is None:
+        preact = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    desc = layer.descriptor()
+    nl = layer.replicas if n_layers is None else n_layers
+    check(load().blockffn_route_with(ctypes.byref(desc), nl, _ptr(x), T, chunk_len, kind, top_k, _ptr(gates),
+                                     _ptr(token_masks), _ptr(preact), _stream(stream)), "blockffn_route_with")
     return gates, token_masks, preact
 
 

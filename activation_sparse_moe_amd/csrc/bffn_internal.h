@@ -78,8 +78,8 @@ struct StageEvents {
 };
 
 // ---- launchers (host side, enqueue only; arguments already validated) ----
-hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len, int dtype,
-                        float* gates, uint64_t* masks, float* preact, hipStream_t s);
+hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len, int dtype, int kind,
+                        int top_k, float* gates, uint64_t* masks, float* preact, hipStream_t s);
 hipError_t launch_chunk_union(int E, const uint64_t* masks, int64_t n_tokens, int chunk_len,
                               uint64_t* chunk_masks, int32_t* count, int32_t* list, hipStream_t s);
 hipError_t launch_stats(int E, const uint64_t* masks, int64_t n_tokens, int chunk_len,

@@ -159,7 +159,27 @@ BFFN_EXPORT int blockffn_route(const blockffn_layer* layer, int32_t n_layers, co
   if (!aligned(x, 16) || !aligned(gates, 4) || !aligned(token_masks, 8) || !aligned(preact, 4))
     return fail(BLOCKFFN_ERR_ALIGN, "x must be 16-byte, gates/preact 4-byte and token_masks 8-byte aligned");
   const bffn::LayerArgs la = layer_args(layer, n_layers);
-  return hip_status(bffn::launch_route(la, x, n_tokens, chunk_len, layer->dtype, gates, token_masks, preact, stream),
+  return hip_status(bffn::launch_route(la, x, n_tokens, chunk_len, layer->dtype, BLOCKFFN_ROUTER_BLOCKFFN, 0, gates,
+                                       token_masks, preact, stream),
+                    "router launch");
+}
+
+BFFN_EXPORT int blockffn_route_with(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+                                    int32_t chunk_len, int32_t router, int32_t top_k, float* gates,
+                                    uint64_t* token_masks, float* preact, hipStream_t stream) {
+  if (int r = check_layer(layer, n_layers)) return r;
+  if (int r = check_chunking(n_tokens, chunk_len)) return r;
+  if (router != BLOCKFFN_ROUTER_BLOCKFFN && router != BLOCKFFN_ROUTER_TOPK_SOFTMAX && router != BLOCKFFN_ROUTER_RELU_SUM)
+    return fail(BLOCKFFN_ERR_MODE, "unknown router %d", router);
+  if (router == BLOCKFFN_ROUTER_TOPK_SOFTMAX && (top_k < 1 || top_k > layer->n_experts))
+    return fail(BLOCKFFN_ERR_SHAPE, "top_k %d outside [1, n_experts %d]", top_k, layer->n_experts);
+  if (n_tokens == 0) return BLOCKFFN_OK;
+  if (!x || !gates || !token_masks) return fail(BLOCKFFN_ERR_NULL, "x, gates and token_masks must be non-NULL");
+  if (!aligned(x, 16) || !aligned(gates, 4) || !aligned(token_masks, 8) || !aligned(preact, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "x must be 16-byte, gates/preact 4-byte and token_masks 8-byte aligned");
+  const bffn::LayerArgs la = layer_args(layer, n_layers);
+  return hip_status(bffn::launch_route(la, x, n_tokens, chunk_len, layer->dtype, router, top_k, gates, token_masks,
+                                       preact, stream),
                     "router launch");
 }
 

@@ -19,11 +19,35 @@
 namespace bffn {
 namespace {
 
+// Wave arg-max over the experts not yet taken: larger z wins, the lower index
+// among equal z.  Every lane gets the winner's index.
+__device__ __forceinline__ int wave_argmax(float c0, float c1, int lane) {
+  float bz = c0;
+  int bi = lane;
+  if (c1 > bz) {
+    bz = c1;
+    bi = lane + 64;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float oz = __shfl_xor(bz, off, kWave);
+    const int oi = __shfl_xor(bi, off, kWave);
+    if (oz > bz || (oz == bz && oi < bi)) {
+      bz = oz;
+      bi = oi;
+    }
+  }
+  return bi;
+}
+
 // Partial sums zp[part][e][n] (n < L) in LDS -> gates, masks, optional z.
 // Wave w handles tokens n = w, w + 4, ...; lane l handles experts l, l + 64.
+// kind selects the gate function: the BlockFFN router (ReLU, then RMSNorm
+// over the E outputs) or one of the baseline routers (top-k of a softmax;
+// ReLU divided by its sum).
 __device__ void router_epilogue(const float* zp, int nparts, int E, int L, int64_t t0,
-                                const float* __restrict__ b, const float* __restrict__ s, float eps,
-                                float* __restrict__ gates, uint64_t* __restrict__ masks,
+                                const float* __restrict__ b, const float* __restrict__ s, float eps, int kind,
+                                int top_k, float* __restrict__ gates, uint64_t* __restrict__ masks,
                                 float* __restrict__ preact) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int W = (E + 63) >> 6;
@@ -38,14 +62,49 @@ __device__ void router_epilogue(const float* zp, int nparts, int E, int L, int64
     }
     z0 += b0;
     z1 += b1;
-    const bool on0 = v0 && z0 > 0.f, on1 = v1 && z1 > 0.f;
+    bool on0 = v0 && z0 > 0.f, on1 = v1 && z1 > 0.f;
     const float a0 = on0 ? z0 : 0.f, a1 = on1 ? z1 : 0.f;
-    // mean over all E outputs, inactive ones included
-    const float ms = wave_sum(a0 * a0 + a1 * a1) / (float)E;
-    const float inv = 1.0f / sqrtf(ms + eps);
+    float g0, g1;
+    if (kind == BLOCKFFN_ROUTER_TOPK_SOFTMAX) {
+      const float ninf = -__builtin_huge_valf();
+      float c0 = v0 ? z0 : ninf, c1 = v1 ? z1 : ninf;
+      float zmax = c0 > c1 ? c0 : c1;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float o = __shfl_xor(zmax, off, kWave);
+        zmax = o > zmax ? o : zmax;
+      }
+      const float e0 = v0 ? __expf(z0 - zmax) : 0.f, e1 = v1 ? __expf(z1 - zmax) : 0.f;
+      const float inv = 1.0f / wave_sum(e0 + e1);
+      on0 = on1 = false;
+      for (int r = 0; r < top_k; ++r) {
+        const int win = wave_argmax(c0, c1, lane);
+        if (win == lane) {
+          on0 = true;
+          c0 = ninf;
+        }
+        if (win == lane + 64) {
+          on1 = true;
+          c1 = ninf;
+        }
+      }
+      g0 = on0 ? e0 * inv : 0.f;
+      g1 = on1 ? e1 * inv : 0.f;
+    } else if (kind == BLOCKFFN_ROUTER_RELU_SUM) {
+      const float sum = wave_sum(a0 + a1);
+      const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+      g0 = a0 * inv;
+      g1 = a1 * inv;
+    } else {
+      // mean over all E outputs, inactive ones included
+      const float ms = wave_sum(a0 * a0 + a1 * a1) / (float)E;
+      const float inv = 1.0f / sqrtf(ms + eps);
+      g0 = s0 * a0 * inv;
+      g1 = s1 * a1 * inv;
+    }
     const int64_t t = t0 + n;
-    if (v0) gates[t * E + lane] = s0 * a0 * inv;
-    if (v1) gates[t * E + lane + 64] = s1 * a1 * inv;
+    if (v0) gates[t * E + lane] = g0;
+    if (v1) gates[t * E + lane + 64] = g1;
     if (preact) {
       if (v0) preact[t * E + lane] = z0;
       if (v1) preact[t * E + lane + 64] = z1;
@@ -83,7 +142,8 @@ __device__ __forceinline__ float dot16<uint16_t>(const uint16_t* a, const uint16
 // 16-byte vectors of the row.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const T* __restrict__ x, int L,
-                                                            int lpr, int nv, float* __restrict__ gates,
+                                                            int lpr, int nv, int kind, int top_k,
+                                                            float* __restrict__ gates,
                                                             uint64_t* __restrict__ masks,
                                                             float* __restrict__ preact) {
   extern __shared__ float zp[];  // [E][L]
@@ -114,7 +174,7 @@ __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const 
     }
   }
   __syncthreads();
-  router_epilogue(zp, 1, E, L, t0, b, s, la.eps, gates, masks, preact);
+  router_epilogue(zp, 1, E, L, t0, b, s, la.eps, kind, top_k, gates, masks, preact);
 }
 
 // MFMA router.  Wave w owns d-range [w d/4, (w+1) d/4) for every expert row,
@@ -124,7 +184,7 @@ __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const 
 // in a fixed order by the epilogue (deterministic).
 template <int NT>
 __global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
-                                                            int L, float* __restrict__ gates,
+                                                            int L, int kind, int top_k, float* __restrict__ gates,
                                                             uint64_t* __restrict__ masks,
                                                             float* __restrict__ preact) {
   extern __shared__ float zp[];  // [4][E][L]
@@ -165,7 +225,7 @@ __global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const 
     }
   }
   __syncthreads();
-  router_epilogue(zp, 4, E, L, t0, b, s, la.eps, gates, masks, preact);
+  router_epilogue(zp, 4, E, L, t0, b, s, la.eps, kind, top_k, gates, masks, preact);
 }
 
 }  // namespace
@@ -174,8 +234,8 @@ bool route_uses_mfma(int d, int E, int chunk_len, int dtype) {
   return dtype == BLOCKFFN_BF16 && chunk_len >= 8 && E % 16 == 0 && d % 512 == 0;
 }
 
-hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len, int dtype,
-                        float* gates, uint64_t* masks, float* preact, hipStream_t s) {
+hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len, int dtype, int kind,
+                        int top_k, float* gates, uint64_t* masks, float* preact, hipStream_t s) {
   const int64_t units = n_tokens / chunk_len;
   if (units == 0) return hipSuccess;
   const int L = chunk_len;
@@ -183,10 +243,10 @@ hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, in
     const size_t lds = sizeof(float) * 4 * la.E * L;
     if (L <= 16)
       route_mfma_kernel<1><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const uint16_t*>(x), L, gates, masks, preact);
+          la, static_cast<const uint16_t*>(x), L, kind, top_k, gates, masks, preact);
     else
       route_mfma_kernel<2><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const uint16_t*>(x), L, gates, masks, preact);
+          la, static_cast<const uint16_t*>(x), L, kind, top_k, gates, masks, preact);
   } else {
     const size_t lds = sizeof(float) * la.E * L;
     const int vec = dtype == BLOCKFFN_F32 ? 4 : 8;
@@ -196,10 +256,10 @@ hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, in
     const int nv = nvec / lpr;
     if (dtype == BLOCKFFN_F32)
       route_valu_kernel<float><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const float*>(x), L, lpr, nv, gates, masks, preact);
+          la, static_cast<const float*>(x), L, lpr, nv, kind, top_k, gates, masks, preact);
     else
       route_valu_kernel<uint16_t><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const uint16_t*>(x), L, lpr, nv, gates, masks, preact);
+          la, static_cast<const uint16_t*>(x), L, lpr, nv, kind, top_k, gates, masks, preact);
   }
   return hipGetLastError();
 }

@@ -42,6 +42,9 @@ def parse_args(argv=None):
     p.add_argument("--mode", default=None, help="forward mode (default: the workload's)")
     p.add_argument("--dense-steps", type=int, default=5, help="steps of the dense all-experts comparison (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--router", default="blockffn", choices=("blockffn", "topk_softmax", "relu_sum"),
+                   help="gate function: the BlockFFN router, or a baseline router for comparison")
+    p.add_argument("--top-k", type=int, default=2, help="experts per token for --router topk_softmax")
     p.add_argument("--backward", action="store_true",
                    help="also time blockffn_backward on the batch (grouped workloads: one layer)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -94,7 +97,7 @@ def profiled_traffic(kernel: str, workload: str):
 class StepRunner:
     """Holds the device buffers of one workload and runs steps on the current stream."""
 
-    def __init__(self, cfg, mode: str):
+    def __init__(self, cfg, mode: str, router: str = "blockffn", top_k: int = 0):
         import numpy as np
         import torch
         from activation_sparse_moe_amd import binding as B
@@ -102,6 +105,7 @@ class StepRunner:
 
         self.B, self.torch, self.np = B, torch, np
         self.cfg, self.mode = cfg, mode
+        self.router, self.top_k = router, top_k
         t = time.time()
         self.layer, tok = make_workload(cfg)
         self.x_host = tok.x
@@ -145,7 +149,10 @@ class StepRunner:
             last = b == nb - 1
             x, g, m, y = self.xd[t0:t1], self.gates[t0:t1], self.masks[t0:t1], self.y[t0:t1]
             cnt, lst, um = self.count[c0:c1], self.lst[c0:c1], self.umask[c0:c1]
-            B.blockffn_route(self.dl, x, L, gates=g, token_masks=m)
+            if self.router == "blockffn":
+                B.blockffn_route(self.dl, x, L, gates=g, token_masks=m)
+            else:
+                B.blockffn_route_with(self.dl, x, L, router=self.router, top_k=self.top_k, gates=g, token_masks=m)
             if ev is not None and last:
                 ev[0].record()
             B.blockffn_chunk_union(E, m, L, chunk_masks=um, active_count=cnt, active_list=lst)
@@ -420,7 +427,7 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
-    runner = StepRunner(cfg, mode)
+    runner = StepRunner(cfg, mode, args.router, args.top_k)
     ms, avg = runner.timed(mode, args.steps, args.warmup)
     from activation_sparse_moe_amd import binding as B
     st = B.stats_dict(runner.stats)
@@ -465,7 +472,7 @@ def main(argv=None) -> int:
         backward = backward_measure(runner, args.steps, args.warmup, args.dense_steps)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.router == "blockffn":
         cpu = cpu_baseline(cfg, runner.layer, runner.x_host, args.cpu_seconds)
 
     if grouped:
@@ -479,7 +486,8 @@ def main(argv=None) -> int:
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded generator shaped to the pages' sparsity)",
         "config": {"workload": cfg.name, "d": cfg.d, "n_experts": cfg.n_experts, "d_expert": cfg.d_expert,
                    "chunk_len": cfg.chunk_len, "chunks": T // cfg.chunk_len, "tokens": T,
-                   "layer_copies": cfg.replicas, "mode": mode},
+                   "layer_copies": cfg.replicas, "mode": mode,
+                   "router": args.router if args.router != "topk_softmax" else f"topk_softmax(k={args.top_k})"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "active_weight_gbs": round(step_gbs, 1),

@@ -136,6 +136,31 @@ int blockffn_route(const blockffn_layer* layer, int32_t n_layers, const void* x,
                    int32_t chunk_len, float* gates, uint64_t* token_masks, float* preact,
                    hipStream_t stream);
 
+/* Router kinds of blockffn_route_with. */
+#define BLOCKFFN_ROUTER_BLOCKFFN 0     /* ReLU, then RMSNorm over the E outputs (blockffn_route) */
+#define BLOCKFFN_ROUTER_TOPK_SOFTMAX 1 /* softmax over E; the top_k largest z keep their probability */
+#define BLOCKFFN_ROUTER_RELU_SUM 2     /* ReMoE: ReLU(z) divided by its sum over the E outputs */
+
+/*
+ * Router with a selectable gate function, for comparing routers on the same
+ * layer (the MoE architecture blog, intelliparadigm.com: §2.1 gives the
+ * Switch Transformer router, a softmax over x W_r with TOP-K selection;
+ * §5.1 gives ReMoE, ReLU gates with the output divided by their sum).  The
+ * union, forward and statistics calls take its gates and masks unchanged.
+ *   router   BLOCKFFN_ROUTER_*; BLOCKFFN_ROUTER_BLOCKFFN is blockffn_route
+ *   top_k    1 <= top_k <= E for BLOCKFFN_ROUTER_TOPK_SOFTMAX (ignored otherwise)
+ * TOPK_SOFTMAX: z as in blockffn_route (bias included); the top_k largest z
+ * are selected (the lower index first among equal z); g_i = softmax(z)_i
+ * for those, 0 elsewhere; mask bit i set iff selected.
+ * RELU_SUM: g_i = max(z_i, 0) / sum_j max(z_j, 0) (0 when none fires); mask
+ * bit i set iff z_i > 0.  rms_scale and rms_eps apply to the BlockFFN router
+ * only.  Other arguments, layout and ownership as blockffn_route.
+ * Errors: as blockffn_route, plus MODE (unknown router) and SHAPE (top_k).
+ */
+int blockffn_route_with(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+                        int32_t chunk_len, int32_t router, int32_t top_k, float* gates, uint64_t* token_masks,
+                        float* preact, hipStream_t stream);
+
 /*
  * Chunk union and compaction (write-up §4; abstract: the union of the
  * parameters several consecutive tokens activate).

@@ -242,3 +242,19 @@ def test_backward_workspace_size(lib):
     assert n >= 3 * 4 * P_ + 2 * (2 * 128 * 4096 * 128) + 2 * (2 * P_ * 128) + 2 * P_ * 4096
     assert lib.blockffn_backward_workspace_size(ctypes.byref(_layer(dtype=0)), T) == 0
     assert lib.blockffn_backward_workspace_size(ctypes.byref(lay), -1) == 0
+
+
+def _route_with(lib, layer, router=1, top_k=2, T=16, L=8, x=P, gates=P, masks=P):
+    return lib.blockffn_route_with(ctypes.byref(layer), 1, x, T, L, router, top_k, gates, masks, None, None)
+
+
+@cpu_only
+def test_route_with_validation(lib):
+    ok = _layer()
+    assert _route_with(lib, ok, router=3) == _capi.ERR_MODE
+    assert _route_with(lib, ok, router=-1) == _capi.ERR_MODE
+    assert _route_with(lib, ok, router=1, top_k=0) == _capi.ERR_SHAPE
+    assert _route_with(lib, ok, router=1, top_k=17) == _capi.ERR_SHAPE      # E = 16
+    assert _route_with(lib, ok, router=1, top_k=2, T=0, x=None, gates=None, masks=None) == _capi.OK
+    assert _route_with(lib, ok, router=2, top_k=0, x=None) == _capi.ERR_NULL   # top_k ignored for ReMoE
+    assert _route_with(lib, ok, router=1, top_k=2, gates=P + 2) == _capi.ERR_ALIGN

@@ -134,7 +134,9 @@ int oracle_route_with(int32_t d, int32_t E, int32_t dtype, const void *x, int64_
   if (d <= 0 || E <= 0 || T < 0 || (kind != 1 && kind != 2) || (kind == 1 && (top_k < 1 || top_k > E)))
     return -1;
   const int W = mask_words(E);
-  int err = 0;
+  /* z exactly as the BlockFFN router computes it; its gates are overwritten below */
+  int err = oracle_route(d, E, dtype, x, T, w_router, b_router, NULL, 0.0, z_out, g_out, mask_out);
+  if (err) return err;
 #pragma omp parallel
   {
     uint8_t *taken = (uint8_t *)malloc((size_t)E);
@@ -144,18 +146,11 @@ int oracle_route_with(int32_t d, int32_t E, int32_t dtype, const void *x, int64_
     }
 #pragma omp for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
-      double *z = z_out + t * E;
+      const double *z = z_out + t * E;
       double *g = g_out + t * E;
       uint64_t *m = mask_out + t * W;
       for (int w = 0; w < W; ++w) m[w] = 0;
-      for (int i = 0; i < E; ++i) {
-        double acc = 0.0;
-        for (int k = 0; k < d; ++k)
-          acc += widen(w_router, (int64_t)i * d + k, dtype) * widen(x, t * d + k, dtype);
-        if (b_router) acc += (double)b_router[i];
-        z[i] = acc;
-        g[i] = 0.0;
-      }
+      for (int i = 0; i < E; ++i) g[i] = 0.0;
       if (!taken) continue;
       if (kind == 1) {
         double zmax = z[0];

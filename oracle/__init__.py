@@ -70,12 +70,13 @@ def _load():
             lib.oracle_union.argtypes = [i32, vp, i64, i32, vp, vp, vp]
             lib.oracle_stats.argtypes = [i32, vp, i64, i32, ctypes.POINTER(OracleStats)]
             lib.oracle_route_with.argtypes = [i32, i32, i32, vp, i64, vp, vp, i32, i32, vp, vp, vp]
-            lib.oracle_backward.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, dbl, vp, vp, vp, vp, vp,
+            lib.oracle_backward.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, dbl, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.oracle_cls_losses.argtypes = [i32, vp, i64, i32, dbl, dbl, dbl, vp, vp]
             lib.oracle_num_threads.argtypes = []
             for name in ("oracle_route", "oracle_expert", "oracle_forward_tokens",
                          "oracle_forward_chunks", "oracle_forward_dense", "oracle_union",
-                         "oracle_stats", "oracle_backward", "oracle_route_with", "oracle_num_threads"):
+                         "oracle_stats", "oracle_backward", "oracle_route_with", "oracle_cls_losses", "oracle_num_threads"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -236,13 +237,16 @@ def layer_forward(layer, x, chunk_len: int):
     return dict(z=z, g=g, mask=m, umask=um, count=cnt, list=lst, y=y)
 
 
-def backward(x, w_router, b_router, rms_scale, eps, w_in, w_out, dy, expert_sel=None, token_sel=None) -> dict:
+def backward(x, w_router, b_router, rms_scale, eps, w_in, w_out, dy, expert_sel=None, token_sel=None,
+             dz_extra=None) -> dict:
     """Gradients of sum(y * dy) with respect to x and every parameter (float64).
 
     Returns dx[T][d], dw_router[E][d], db[E], ds[E], dw_in[E][de][d],
     dw_out[E][d][de], and the per-pair dz[T][E] and dg[T][E].  expert_sel /
     token_sel (bool arrays of length E / T) restrict which dw_in / dw_out
-    blocks and which dx rows are computed; the rest stay zero.
+    blocks and which dx rows are computed; the rest stay zero.  dz_extra
+    ([T][E]) is an extra gradient with respect to z (e.g. of the CLS-aware
+    objectives), added to every pair's dz.
     """
     x, w_router, w_in, w_out = _c(x), _c(w_router), _c(w_in), _c(w_out)
     code = _dtype_code(x)
@@ -254,12 +258,25 @@ def backward(x, w_router, b_router, rms_scale, eps, w_in, w_out, dy, expert_sel=
     assert dy.shape == (T, d)
     b = _c(b_router, np.float32)
     s = _c(rms_scale, np.float32)
+    dze = None if dz_extra is None else _c(dz_extra, np.float64)
     es = None if expert_sel is None else _c(np.asarray(expert_sel, dtype=bool).astype(np.uint8))
     ts = None if token_sel is None else _c(np.asarray(token_sel, dtype=bool).astype(np.uint8))
     out = dict(dx=np.empty((T, d)), dw_router=np.empty((E, d)), db=np.empty(E), ds=np.empty(E),
                dw_in=np.empty((E, de, d)), dw_out=np.empty((E, d, de)), dz=np.empty((T, E)), dg=np.empty((T, E)))
     _check(_load().oracle_backward(d, E, de, code, _p(x), T, _p(w_router), _p(b), _p(s), float(eps), _p(w_in),
-                                   _p(w_out), _p(dy), _p(es), _p(ts), _p(out["dx"]), _p(out["dw_router"]),
+                                   _p(w_out), _p(dy), _p(dze), _p(es), _p(ts), _p(out["dx"]), _p(out["dw_router"]),
                                    _p(out["db"]), _p(out["ds"]), _p(out["dw_in"]), _p(out["dw_out"]), _p(out["dz"]),
                                    _p(out["dg"])), "oracle_backward")
     return out
+
+
+def cls_losses(z, chunk_len: int, alpha: float, w_al: float = 1.0, w_cs: float = 1.0, want_grad: bool = True):
+    """CLS-aware objectives on pre-activations z[T][E] (float64):
+    returns (L_AL, L_CS, dz or None) with dz = w_al dL_AL/dz + w_cs dL_CS/dz."""
+    z = _c(z, np.float64)
+    T, E = z.shape
+    loss = np.empty(2, np.float64)
+    dz = np.empty((T, E), np.float64) if want_grad else None
+    _check(_load().oracle_cls_losses(E, _p(z), T, int(chunk_len), float(alpha), float(w_al), float(w_cs), _p(loss),
+                                      _p(dz)), "oracle_cls_losses")
+    return float(loss[0]), float(loss[1]), dz

@@ -404,6 +404,10 @@ int oracle_stats(int32_t E, const uint64_t *mask, int64_t T, int32_t L, oracle_s
  * so only active pairs are visited.  The gates and pattern are recomputed
  * here exactly as oracle_route computes them.
  *
+ * dz_extra ([T][E] or NULL) is a gradient with respect to z from other
+ * terms of the loss (the CLS-aware objectives below); it is added to dz for
+ * every (token, expert), active or not, before dz reaches db, dW_r and dx.
+ *
  * Outputs are double and overwritten: dx[T][d], dw_router[E][d], db[E],
  * ds[E], dw_in[E][de][d], dw_out[E][d][de], dz[T][E] and dg[T][E] (dg_i for
  * active pairs, 0 elsewhere).  expert_sel (E bytes) and token_sel (T bytes)
@@ -432,7 +436,7 @@ static void pair_backward(int d, int de, int dtype, const void *x, int64_t t, co
 
 int oracle_backward(int32_t d, int32_t E, int32_t de, int32_t dtype, const void *x, int64_t T,
                     const void *w_router, const float *b_router, const float *rms_scale, double eps,
-                    const void *w_in, const void *w_out, const float *dy,
+                    const void *w_in, const void *w_out, const float *dy, const double *dz_extra,
                     const uint8_t *expert_sel, const uint8_t *token_sel,
                     double *dx, double *dw_router, double *db, double *ds, double *dw_in, double *dw_out,
                     double *dz, double *dg) {
@@ -487,7 +491,7 @@ int oracle_backward(int32_t d, int32_t E, int32_t de, int32_t dtype, const void 
         const double a = z[t * E + i] > 0.0 ? z[t * E + i] : 0.0;
         const double s = rms_scale ? (double)rms_scale[i] : 1.0;
         const double da = dg[t * E + i] * s * r + dms * 2.0 * a / (double)E;
-        dz[t * E + i] = z[t * E + i] > 0.0 ? da : 0.0;
+        dz[t * E + i] = (z[t * E + i] > 0.0 ? da : 0.0) + (dz_extra ? dz_extra[t * E + i] : 0.0);
       }
     }
 
@@ -556,4 +560,65 @@ int oracle_backward(int32_t d, int32_t E, int32_t de, int32_t dtype, const void 
   free(dsc);
   free(m);
   return err;
+}
+
+/*
+ * CLS-aware training objectives (BlockFFN write-up §3).  With the sharp
+ * sigmoid p_{t,i} = sigma(alpha z_{t,i}) as the soft activation pattern:
+ *
+ *   activation locality: binary cross-entropy between each token's soft
+ *     pattern and the next token's activation pattern (the pattern sequence
+ *     shifted left by one token), over every consecutive pair of the stream:
+ *       L_AL = 1 / ((T - 1) E) * sum_{t < T-1} sum_i BCE(p_{t,i}, [z_{t+1,i} > 0])
+ *       BCE(p, y) = -(y log p + (1 - y) log(1 - p)) = softplus(s) - y s, s = alpha z
+ *   chunk sparsification: the probability that expert i fires for at least
+ *     one token of chunk c, averaged over chunks and experts:
+ *       L_CS = 1 / (C E) * sum_c sum_i (1 - prod_{t in c} (1 - p_{t,i}))
+ *
+ * Writes loss[0] = L_AL, loss[1] = L_CS and, when dz is non-NULL, the
+ * gradient dz = w_al dL_AL/dz + w_cs dL_CS/dz ([T][E]):
+ *   dL_AL/dz_{t,i} = alpha (p_{t,i} - y_{t,i}) / ((T - 1) E)   (t < T - 1; the target has no gradient)
+ *   dL_CS/dz_{t,i} = alpha p (1 - p) prod_{t' in c, t' != t} (1 - p_{t',i}) / (C E)
+ * z is the router pre-activation (as oracle_route writes it).
+ */
+static double softplus(double s) { return s > 0.0 ? s + log1p(exp(-s)) : log1p(exp(s)); }
+
+int oracle_cls_losses(int32_t E, const double *z, int64_t T, int32_t L, double alpha, double w_al, double w_cs,
+                      double *loss, double *dz) {
+  if (E <= 0 || L <= 0 || T < 0 || T % L != 0) return -1;
+  const int64_t C = T / L;
+  const double n_al = (double)(T - 1) * (double)E;
+  double al = 0.0, cs = 0.0;
+  for (int64_t t = 0; t + 1 < T; ++t)
+    for (int i = 0; i < E; ++i) {
+      const double s = alpha * z[t * E + i];
+      const double y = z[(t + 1) * E + i] > 0.0 ? 1.0 : 0.0;
+      al += softplus(s) - y * s;
+    }
+  for (int64_t c = 0; c < C; ++c)
+    for (int i = 0; i < E; ++i) {
+      double q = 1.0;
+      for (int64_t t = c * L; t < (c + 1) * L; ++t) q *= 1.0 - 1.0 / (1.0 + exp(-alpha * z[t * E + i]));
+      cs += 1.0 - q;
+    }
+  loss[0] = T > 1 ? al / n_al : 0.0;
+  loss[1] = C > 0 ? cs / ((double)C * (double)E) : 0.0;
+  if (!dz) return 0;
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t c = t / L;
+    for (int i = 0; i < E; ++i) {
+      const double p = 1.0 / (1.0 + exp(-alpha * z[t * E + i]));
+      double g = 0.0;
+      if (t + 1 < T) {
+        const double y = z[(t + 1) * E + i] > 0.0 ? 1.0 : 0.0;
+        g += w_al * alpha * (p - y) / n_al;
+      }
+      double others = 1.0;
+      for (int64_t u = c * L; u < (c + 1) * L; ++u)
+        if (u != t) others *= 1.0 - 1.0 / (1.0 + exp(-alpha * z[u * E + i]));
+      g += w_cs * alpha * p * (1.0 - p) * others / ((double)C * (double)E);
+      dz[t * E + i] = g;
+    }
+  }
+  return 0;
 }

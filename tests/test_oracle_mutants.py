@@ -10,7 +10,10 @@ widening, a wrong reuse denominator, a flipped bias sign; and in the backward
 a dropped or sign-flipped RMSNorm term, a wrong Swish derivative, a dropped
 gate, gradients taken through inactive pairs, a wrong scale gradient, a dropped router term of
 dx, a missing gate in dW_out; and in the baseline routers a tie broken the
-other way, an unshifted softmax sum, a missing ReMoE normalisation.
+other way, an unshifted softmax sum, a missing ReMoE normalisation; and in
+the CLS-aware objectives an unshifted locality target, the complement of the
+chunk probability, a chunk gradient that includes the token itself, and an
+extra router gradient applied to active pairs only.
 """
 import os
 import subprocess
@@ -63,8 +66,16 @@ MUTANTS = {
     "topk_softmax_unshifted_sum": ("for (int i = 0; i < E; ++i) sum += exp(z[i] - zmax);",
                                    "for (int i = 0; i < E; ++i) sum += exp(z[i]);"),
     "relu_sum_unnormalised": ("g[i] = z[i] / sum;", "g[i] = z[i];"),
+    # the CLS-aware objectives
+    "cls_locality_target_not_shifted": ("const double y = z[(t + 1) * E + i] > 0.0 ? 1.0 : 0.0;\n      al +=",
+                                        "const double y = z[t * E + i] > 0.0 ? 1.0 : 0.0;\n      al +="),
+    "cls_chunk_loss_complement": ("cs += 1.0 - q;", "cs += q;"),
+    "cls_chunk_grad_includes_self": ("if (u != t) others *= 1.0", "others *= 1.0"),
+    "bwd_extra_gradient_only_active": ("dz[t * E + i] = (z[t * E + i] > 0.0 ? da : 0.0) + (dz_extra ? dz_extra[t * E + i] : 0.0);",
+                                       "dz[t * E + i] = z[t * E + i] > 0.0 ? da + (dz_extra ? dz_extra[t * E + i] : 0.0) : 0.0;"),
 }
-PIN_FILES = ("test_oracle_pins.py", "test_oracle_backward_pins.py", "test_oracle_router_pins.py")
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_backward_pins.py", "test_oracle_router_pins.py",
+             "test_oracle_cls_pins.py")
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -242,7 +242,7 @@ def alloc_backward_workspace(layer: DeviceLayer, n_tokens: int) -> torch.Tensor:
 
 def blockffn_backward(layer: DeviceLayer, x: torch.Tensor, preact: torch.Tensor, dy: torch.Tensor,
                       workspace: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
-                      grads: Optional[dict] = None, stream=None) -> dict:
+                      grads: Optional[dict] = None, dz_extra: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Layer backward -> dict(dx, d_w_router, d_b_router, d_rms_scale, d_w_in, d_w_out), all fp32."""
     T = x.shape[0]
     E, d, de = layer.n_experts, layer.d, layer.d_expert
@@ -260,10 +260,30 @@ def blockffn_backward(layer: DeviceLayer, x: torch.Tensor, preact: torch.Tensor,
     g = BlockffnGrads(*[grads[k].data_ptr() for k in ("d_w_router", "d_b_router", "d_rms_scale", "d_w_in",
                                                        "d_w_out")])
     desc = layer.descriptor()
-    check(load().blockffn_backward(ctypes.byref(desc), _ptr(x), T, _ptr(preact), _ptr(dy), _ptr(workspace),
+    check(load().blockffn_backward(ctypes.byref(desc), _ptr(x), T, _ptr(preact), _ptr(dy), _ptr(dz_extra),
+                                   _ptr(workspace),
                                    workspace.numel(), _ptr(dx), ctypes.byref(g), _stream(stream)),
           "blockffn_backward")
     return dict(dx=dx, **grads)
+
+
+def blockffn_cls_losses(n_experts: int, preact: torch.Tensor, chunk_len: int, alpha: float, w_locality: float = 1.0,
+                        w_chunk: float = 1.0, want_grad: bool = True, losses: Optional[torch.Tensor] = None,
+                        dz: Optional[torch.Tensor] = None, stream=None):
+    """CLS-aware objectives -> (losses [2] fp32 device tensor, dz [T][E] fp32 or None)."""
+    T = preact.shape[0]
+    dev = preact.device
+    if losses is None:
+        losses = torch.empty((2,), dtype=torch.float32, device=dev)
+    if want_grad and dz is None:
+        dz = torch.empty((T, n_experts), dtype=torch.float32, device=dev)
+    lib = load()
+    nbytes = int(lib.blockffn_cls_losses_workspace_size(T, chunk_len))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    check(lib.blockffn_cls_losses(n_experts, _ptr(preact), T, chunk_len, float(alpha), float(w_locality),
+                                  float(w_chunk), _ptr(ws), ws.numel(), _ptr(losses), _ptr(dz), _stream(stream)),
+          "blockffn_cls_losses")
+    return losses, dz
 
 
 def blockffn_sparsity_stats(n_experts: int, token_masks: torch.Tensor, chunk_len: int,

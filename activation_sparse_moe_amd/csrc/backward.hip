@@ -28,7 +28,8 @@
 //            transposed, so the contraction runs over pairs)
 //   dx:      Part = dU W_in[i] per pair (the forward's down GEMM on the
 //            transposed W_in), then per token the sum over its active
-//            experts, ascending, of Part + dz_i W_r[i]
+//            experts, ascending, of Part + dz_i W_r[i] (and, with an extra
+//            router gradient, dz_i W_r[i] of the inactive experts after them)
 //
 // No atomics: every output element has one writer and a fixed summation
 // order, so the result is bit-reproducible.
@@ -286,6 +287,7 @@ __global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restr
                                                             const float* __restrict__ r_tok,
                                                             const int32_t* __restrict__ pair_idx,
                                                             const float* __restrict__ dgp, int n_nt, int64_t T, int E,
+                                                            const float* __restrict__ dz_extra,
                                                             float* __restrict__ dz, uint16_t* __restrict__ dzb,
                                                             float* __restrict__ dsc) {
   const int lane = threadIdx.x & 63;
@@ -315,7 +317,8 @@ __global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restr
   for (int h = 0; h < 2; ++h) {
     const int i = lane + 64 * h;
     const float da = dgv[h] * sv[h] * r + dms * 2.f * av[h] / (float)E;
-    const float dzi = on[h] ? da : 0.f;
+    float dzi = on[h] ? da : 0.f;
+    if (dz_extra && i < E) dzi += dz_extra[t * E + i];  // every (token, expert), active or not
     if (i < E) {
       dz[t * E + i] = dzi;
       dsc[t * E + i] = dgv[h] * av[h] * r;
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(1024) void bwd_combine_kernel(const float* __restri
                                                            const int32_t* __restrict__ pair_idx,
                                                            const uint16_t* __restrict__ part,
                                                            const uint16_t* __restrict__ w_router, int64_t T, int E,
-                                                           int d, float* __restrict__ dx) {
+                                                           int d, bool all_experts, float* __restrict__ dx) {
   __shared__ int32_t plist[128];
   __shared__ float zlist[128];
   __shared__ int32_t elist[128];
@@ -533,6 +536,19 @@ __global__ __launch_bounds__(1024) void bwd_combine_kernel(const float* __restri
       for (int q = 0; q < 4; ++q) {
         acc[2 * q] += bf16_lo(pv[q]) + zs * bf16_lo(wv[q]);
         acc[2 * q + 1] += bf16_hi(pv[q]) + zs * bf16_hi(wv[q]);
+      }
+    }
+    if (all_experts) {
+      // an extra router gradient reaches inactive experts too: their dz W_r rows, ascending
+      for (int i = 0; i < E; ++i) {
+        const float zs = dz[t * E + i];
+        if (z[t * E + i] > 0.f || zs == 0.f) continue;  // active ones were added above
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(w_router + (int64_t)i * d + c0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += zs * bf16_lo(wv[q]);
+          acc[2 * q + 1] += zs * bf16_hi(wv[q]);
+        }
       }
     }
     f32x4* o = reinterpret_cast<f32x4*>(dx + t * d + c0);
@@ -591,7 +607,7 @@ BwdLayout bwd_layout(char* base, int64_t T, int E, int d, int de) {
 size_t backward_workspace_bytes(int64_t T, int E, int d, int de) { return bwd_layout(nullptr, T, E, d, de).bytes; }
 
 hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, const float* preact, const float* dy,
-                           void* workspace, float* dx, float* d_w_router, float* d_b_router, float* d_rms_scale,
+                           const float* dz_extra, void* workspace, float* dx, float* d_w_router, float* d_b_router, float* d_rms_scale,
                            float* d_w_in, float* d_w_out, const StageEvents& se, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int E = la.E, d = la.d, de = la.de;
@@ -629,7 +645,7 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   bwd_pair_kernel<<<dim3((unsigned)grid_pair), dim3(kBlock), 0, s>>>(pa);
   se.record(2, s);
   bwd_router_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(kBlock), 0, s>>>(
-      preact, la.rms_scale, L.r_b, L.pair_idx, L.dgp, de / GBN, T, E, L.dz, L.dzb, L.dsc);
+      preact, la.rms_scale, L.r_b, L.pair_idx, L.dgp, de / GBN, T, E, dz_extra, L.dz, L.dzb, L.dsc);
   bwd_reduce_kernel<<<dim3((unsigned)E), dim3(kBlock), 0, s>>>(L.dz, L.dsc, T, E, d_b_router, d_rms_scale);
   // dW_out[i][k][j] = sum_p dY[t_p][k] HG[p][j]
   TGemmArgs go{L.dyb, d, L.pair_tok, L.hg, de, nullptr, L.pair_off, d_w_out, de, (int64_t)d * de, E, d, d, de};
@@ -654,7 +670,7 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   int cthreads = (d / 8 + 63) / 64 * 64;
   cthreads = cthreads < 64 ? 64 : (cthreads > 1024 ? 1024 : cthreads);
   bwd_combine_kernel<<<dim3((unsigned)T), dim3((unsigned)cthreads), 0, s>>>(preact, L.dz, L.pair_idx, L.part, w_r, T,
-                                                                           E, d, dx);
+                                                                           E, d, dz_extra != nullptr, dx);
   se.record(5, s);
   return hipGetLastError();
 }

@@ -97,9 +97,12 @@ size_t grouped_workspace_bytes(int64_t n_tokens, int E, int d, int de);
 bool grouped_supported(int d, int de, int dtype);
 
 hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, const float* preact,
-                           const float* dy, void* workspace, float* dx, float* d_w_router, float* d_b_router,
+                           const float* dy, const float* dz_extra, void* workspace, float* dx, float* d_w_router, float* d_b_router,
                            float* d_rms_scale, float* d_w_in, float* d_w_out, const StageEvents& se, hipStream_t s);
 size_t backward_workspace_bytes(int64_t n_tokens, int E, int d, int de);
+hipError_t launch_cls_losses(int E, const float* z, int64_t T, int L, float alpha, float w_al, float w_cs,
+                             void* workspace, float* losses, float* dz, hipStream_t s);
+size_t cls_losses_workspace_bytes(int64_t n_tokens, int chunk_len);
 
 bool route_uses_mfma(int d, int E, int chunk_len, int dtype);
 bool forward_mfma_supported(int d, int de, int dtype);

@@ -280,15 +280,15 @@ BFFN_EXPORT size_t blockffn_backward_workspace_size(const blockffn_layer* layer,
 }
 
 BFFN_EXPORT int blockffn_backward(const blockffn_layer* layer, const void* x, int64_t n_tokens, const float* preact,
-                                  const float* dy, void* workspace, size_t workspace_bytes, float* dx,
-                                  const blockffn_grads* grads, hipStream_t stream) {
+                                  const float* dy, const float* dz_extra, void* workspace, size_t workspace_bytes,
+                                  float* dx, const blockffn_grads* grads, hipStream_t stream) {
   if (int r = check_backward(layer, n_tokens)) return r;
   if (n_tokens == 0) return BLOCKFFN_OK;
   if (!x || !preact || !dy || !dx || !grads) return fail(BLOCKFFN_ERR_NULL, "x, preact, dy, dx and grads must be non-NULL");
   if (!grads->d_w_router || !grads->d_b_router || !grads->d_rms_scale || !grads->d_w_in || !grads->d_w_out)
     return fail(BLOCKFFN_ERR_NULL, "every gradient pointer must be non-NULL");
-  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(preact, 4))
-    return fail(BLOCKFFN_ERR_ALIGN, "x, dy and dx must be 16-byte aligned, preact 4-byte aligned");
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(preact, 4) || !aligned(dz_extra, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "x, dy and dx must be 16-byte aligned, preact and dz_extra 4-byte aligned");
   if (!aligned(grads->d_w_router, 16) || !aligned(grads->d_w_in, 16) || !aligned(grads->d_w_out, 16) ||
       !aligned(grads->d_b_router, 4) || !aligned(grads->d_rms_scale, 4))
     return fail(BLOCKFFN_ERR_ALIGN, "weight gradients must be 16-byte aligned, d_b_router / d_rms_scale 4-byte");
@@ -298,10 +298,36 @@ BFFN_EXPORT int blockffn_backward(const blockffn_layer* layer, const void* x, in
   if (workspace_bytes < need)
     return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   const bffn::LayerArgs la = layer_args(layer, 1);
-  return hip_status(bffn::launch_backward(la, static_cast<const uint16_t*>(x), n_tokens, preact, dy, workspace, dx,
+  return hip_status(bffn::launch_backward(la, static_cast<const uint16_t*>(x), n_tokens, preact, dy, dz_extra,
+                                          workspace, dx,
                                           grads->d_w_router, grads->d_b_router, grads->d_rms_scale, grads->d_w_in,
                                           grads->d_w_out, g_stage_events, stream),
                     "backward launch");
+}
+
+BFFN_EXPORT size_t blockffn_cls_losses_workspace_size(int64_t n_tokens, int32_t chunk_len) {
+  if (check_chunking(n_tokens, chunk_len) != BLOCKFFN_OK) return 0;
+  return bffn::cls_losses_workspace_bytes(n_tokens, chunk_len);
+}
+
+BFFN_EXPORT int blockffn_cls_losses(int32_t n_experts, const float* preact, int64_t n_tokens, int32_t chunk_len,
+                                    float alpha, float w_locality, float w_chunk, void* workspace,
+                                    size_t workspace_bytes, float* losses, float* dz, hipStream_t stream) {
+  if (int r = check_experts(n_experts)) return r;
+  if (int r = check_chunking(n_tokens, chunk_len)) return r;
+  if (!std::isfinite(alpha) || alpha <= 0.f) return fail(BLOCKFFN_ERR_SHAPE, "alpha must be finite and positive");
+  if (!std::isfinite(w_locality) || !std::isfinite(w_chunk))
+    return fail(BLOCKFFN_ERR_SHAPE, "loss weights must be finite");
+  if (!losses || !workspace || (n_tokens > 0 && !preact))
+    return fail(BLOCKFFN_ERR_NULL, "preact, workspace and losses must be non-NULL");
+  if (!aligned(preact, 4) || !aligned(losses, 4) || !aligned(dz, 4) || !aligned(workspace, 256))
+    return fail(BLOCKFFN_ERR_ALIGN, "preact, losses and dz must be 4-byte aligned, workspace 256-byte aligned");
+  const size_t need = bffn::cls_losses_workspace_bytes(n_tokens, chunk_len);
+  if (workspace_bytes < need)
+    return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  return hip_status(bffn::launch_cls_losses(n_experts, preact, n_tokens, chunk_len, alpha, w_locality, w_chunk,
+                                            workspace, losses, dz, stream),
+                    "cls-losses launch");
 }
 
 BFFN_EXPORT int blockffn_set_stage_events(hipEvent_t* events, int32_t n_events) {

@@ -239,6 +239,9 @@ typedef struct blockffn_grads {
  *   x           [n_tokens][d] bf16, the forward's input
  *   preact      [n_tokens][E] fp32, z as written by blockffn_route
  *   dy          [n_tokens][d] fp32, 16-byte aligned
+ *   dz_extra    [n_tokens][E] fp32 or NULL: a gradient with respect to z from
+ *               other terms of the loss (blockffn_cls_losses), added to dz of
+ *               every (token, expert), active or not, before db, dW_r, dx
  *   workspace   at least blockffn_backward_workspace_size() bytes, 256-byte
  *               aligned, no initialisation needed
  *   dx          [n_tokens][d] fp32 out, 16-byte aligned
@@ -248,11 +251,35 @@ typedef struct blockffn_grads {
  * ALIGN, HIP.
  */
 int blockffn_backward(const blockffn_layer* layer, const void* x, int64_t n_tokens, const float* preact,
-                      const float* dy, void* workspace, size_t workspace_bytes, float* dx,
+                      const float* dy, const float* dz_extra, void* workspace, size_t workspace_bytes, float* dx,
                       const blockffn_grads* grads, hipStream_t stream);
 
 /* Workspace bytes blockffn_backward needs (0 on invalid input). */
 size_t blockffn_backward_workspace_size(const blockffn_layer* layer, int64_t n_tokens);
+
+/*
+ * CLS-aware training objectives on the router pre-activations (write-up §3:
+ * an activation-locality loss, a binary cross-entropy between neighbouring
+ * tokens' activation patterns with a sharp sigmoid standing in for the
+ * pattern; a chunk-sparsification loss, the probability that an expert fires
+ * for at least one token of an L-token chunk).  With p = sigmoid(alpha z):
+ *   losses[0] = L_AL = mean over t < T-1 and i of BCE(p[t][i], [z[t+1][i] > 0])
+ *   losses[1] = L_CS = mean over chunks c and i of 1 - prod_{t in c} (1 - p[t][i])
+ *   dz (if non-NULL) = w_locality dL_AL/dz + w_chunk dL_CS/dz, [n_tokens][E] fp32,
+ *                      ready to pass to blockffn_backward as dz_extra
+ *   preact      [n_tokens][E] fp32, z as written by blockffn_route
+ *   losses      2 fp32 in device memory, overwritten
+ *   workspace   blockffn_cls_losses_workspace_size() bytes, 256-byte aligned
+ * The locality target takes no gradient.  Sums are fixed-order fp32
+ * (deterministic).  Errors: NULL, SHAPE (E, alpha <= 0, weights), CHUNK,
+ * WORKSPACE, ALIGN, HIP.
+ */
+int blockffn_cls_losses(int32_t n_experts, const float* preact, int64_t n_tokens, int32_t chunk_len, float alpha,
+                        float w_locality, float w_chunk, void* workspace, size_t workspace_bytes, float* losses,
+                        float* dz, hipStream_t stream);
+
+/* Workspace bytes blockffn_cls_losses needs (0 on invalid input). */
+size_t blockffn_cls_losses_workspace_size(int64_t n_tokens, int32_t chunk_len);
 
 /*
  * Stage timing (instrumentation for profilers and benchmarks).  While set,

@@ -209,8 +209,8 @@ def _grads(**kw):
 
 def _backward(lib, layer, T=16, x=P, preact=P, dy=P, ws=P, ws_bytes=1 << 40, dx=P, grads=None):
     g = _grads() if grads is None else grads
-    return lib.blockffn_backward(ctypes.byref(layer) if layer is not None else None, x, T, preact, dy, ws, ws_bytes,
-                                 dx, ctypes.byref(g), None)
+    return lib.blockffn_backward(ctypes.byref(layer) if layer is not None else None, x, T, preact, dy, None, ws,
+                                 ws_bytes, dx, ctypes.byref(g), None)
 
 
 @cpu_only
@@ -258,3 +258,21 @@ def test_route_with_validation(lib):
     assert _route_with(lib, ok, router=1, top_k=2, T=0, x=None, gates=None, masks=None) == _capi.OK
     assert _route_with(lib, ok, router=2, top_k=0, x=None) == _capi.ERR_NULL   # top_k ignored for ReMoE
     assert _route_with(lib, ok, router=1, top_k=2, gates=P + 2) == _capi.ERR_ALIGN
+
+
+@cpu_only
+def test_cls_losses_validation(lib):
+    ws_need = lib.blockffn_cls_losses_workspace_size(64, 8)
+    assert ws_need >= 8 * 2 * 4
+    assert lib.blockffn_cls_losses_workspace_size(63, 8) == 0
+    call = lambda **kw: lib.blockffn_cls_losses(*[kw.get(k, v) for k, v in (  # noqa: E731
+        ("E", 16), ("z", P), ("T", 64), ("L", 8), ("alpha", ctypes.c_float(10.0)), ("wa", ctypes.c_float(1.0)),
+        ("wc", ctypes.c_float(1.0)), ("ws", P), ("nb", 1 << 20), ("loss", P), ("dz", P), ("s", None))])
+    assert call(E=0) == _capi.ERR_SHAPE
+    assert call(L=7) == _capi.ERR_CHUNK
+    assert call(alpha=ctypes.c_float(0.0)) == _capi.ERR_SHAPE
+    assert call(wa=ctypes.c_float(float("inf"))) == _capi.ERR_SHAPE
+    assert call(loss=None) == _capi.ERR_NULL
+    assert call(z=P + 2) == _capi.ERR_ALIGN
+    assert call(ws=P + 16) == _capi.ERR_ALIGN
+    assert call(nb=8) == _capi.ERR_WORKSPACE

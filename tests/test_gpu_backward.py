@@ -158,3 +158,69 @@ def test_backward_full_size_sampled():
     assert (~band_e).sum() >= 4
     say(f"  {cfg.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rel.items()) +
         f"; band tokens {nt} of {len(tok_idx)}, router rows compared {(~band_e).sum()}")
+
+
+# ---------------------------------------------------------------- CLS-aware objectives
+CLS_ALPHA, CLS_W_AL, CLS_W_CS = 8.0, 0.5, 2.0
+E_MIN_COMPARED = 32
+
+
+def _cls_gpu(layer, x, L):
+    dl = B.DeviceLayer.from_workload(layer)
+    xd = B.tokens_to_device(x, BF16)
+    _, _, z = B.blockffn_route(dl, xd, L, want_preact=True)
+    losses, dz = B.blockffn_cls_losses(layer.w_router.shape[0], z, L, CLS_ALPHA, CLS_W_AL, CLS_W_CS)
+    torch.cuda.synchronize()
+    return dl, xd, z, losses.cpu().numpy().astype(np.float64), dz
+
+
+@pytest.mark.parametrize("name", ["d512_E64_de128_T96", "d256_E80_de256_T70", "d384_E8_de128_T40"])
+def test_cls_losses_match_oracle(name):
+    """Bars: losses within 1e-4 relative, plus the share of targets the fp32
+    and fp64 pre-activations may disagree on (pairs with |z| < 1e-3, each
+    moving L_AL by at most alpha |z_t| / ((T-1) E)); dz within 1e-4 x max|dz|
+    on tokens whose next token has no such pair."""
+    layer, x, _ = _layer_and_tokens(name)
+    L = CASES[name][4]
+    say(f"[gpu] cls losses {name} T={x.shape[0]} L={L}")
+    _, _, z, losses, dz = _cls_gpu(layer, x, L)
+    z_ref, _, _ = oracle.route(x, layer.w_router, layer.b_router, layer.rms_scale, layer.rms_eps)
+    al, cs, dz_ref = oracle.cls_losses(z_ref, L, CLS_ALPHA, CLS_W_AL, CLS_W_CS)
+    T, E = z_ref.shape
+    band_next = np.zeros(T, bool)
+    band_next[:-1] = (np.abs(z_ref[1:]) < BAND).any(axis=1)
+    slack = CLS_ALPHA * np.abs(z_ref[:-1][(np.abs(z_ref[1:]) < BAND)]).sum() / ((T - 1) * E)
+    assert abs(losses[0] - al) <= 1e-4 * abs(al) + slack, (losses[0], al, slack)
+    assert abs(losses[1] - cs) <= 1e-4 * abs(cs)
+    g = dz.cpu().numpy()
+    keep = ~band_next
+    assert np.abs(g[keep] - dz_ref[keep]).max() <= 1e-4 * np.abs(dz_ref).max()
+    say(f"  {name}: L_AL {losses[0]:.6f} (oracle {al:.6f}), L_CS {losses[1]:.6f} (oracle {cs:.6f})")
+
+
+def test_backward_with_cls_gradient_matches_oracle():
+    name = "d512_E64_de128_T96"
+    layer, x, dy = _layer_and_tokens(name)
+    L = CASES[name][4]
+    say(f"[gpu] backward + cls gradient {name}")
+    dl, xd, z, _, dz = _cls_gpu(layer, x, L)
+    out = B.blockffn_backward(dl, xd, z, torch.from_numpy(dy).cuda(), dz_extra=dz)
+    torch.cuda.synchronize()
+    gpu = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+    z_ref, _, _ = oracle.route(x, layer.w_router, layer.b_router, layer.rms_scale, layer.rms_eps)
+    _, _, dz_ref = oracle.cls_losses(z_ref, L, CLS_ALPHA, CLS_W_AL, CLS_W_CS)
+    ref = oracle.backward(x, layer.w_router, layer.b_router, layer.rms_scale, layer.rms_eps, layer.w_in,
+                          layer.w_out, dy, dz_extra=dz_ref)
+    # a target flip in the next token moves this token's extra gradient: leave those tokens out of dx
+    band_rows = (np.abs(z_ref) < BAND).any(axis=1)
+    band_rows[:-1] |= band_rows[1:]
+    rel = {"dx": _compare("dx", gpu["dx"], ref["dx"], ~band_rows)}
+    for k, r in (("d_w_in", "dw_in"), ("d_w_out", "dw_out"), ("d_rms_scale", "ds")):
+        rel[k] = _compare(k, gpu[k], ref[r])
+    # a band pair (t, i) moves dz[t][i] and the target of dz_extra[t-1][i]: both stay in expert i's router row
+    bad_e = (np.abs(z_ref) < BAND).any(axis=0)
+    assert (~bad_e).sum() >= E_MIN_COMPARED
+    rel["d_w_router"] = _compare("d_w_router", gpu["d_w_router"], ref["dw_router"], ~bad_e)
+    rel["d_b_router"] = _compare("d_b_router", gpu["d_b_router"], ref["db"], ~bad_e)
+    say("  " + ", ".join(f"{k} {v:.1e}" for k, v in rel.items()) +
+        f"; band rows {int(band_rows.sum())}, router rows compared {int((~bad_e).sum())}")

@@ -124,12 +124,16 @@ class DeviceLayer:
                                F32 if layer.dtype == "f32" else BF16, layer.rms_eps, device, replicas)
 
     def descriptor(self) -> BlockffnLayer:
+        # the buffer never moves, so the descriptor is built once
+        if getattr(self, "_desc", None) is not None:
+            return self._desc
         t = self.tensors(0)
-        return BlockffnLayer(self.d, self.n_experts, self.d_expert, self.dtype, self.rms_eps, 0,
-                             self.stride, t["w_router"].data_ptr(),
-                             t["b_router"].data_ptr() if t["b_router"] is not None else None,
-                             t["rms_scale"].data_ptr() if t["rms_scale"] is not None else None,
-                             t["w_in"].data_ptr(), t["w_out"].data_ptr())
+        self._desc = BlockffnLayer(self.d, self.n_experts, self.d_expert, self.dtype, self.rms_eps, 0,
+                                   self.stride, t["w_router"].data_ptr(),
+                                   t["b_router"].data_ptr() if t["b_router"] is not None else None,
+                                   t["rms_scale"].data_ptr() if t["rms_scale"] is not None else None,
+                                   t["w_in"].data_ptr(), t["w_out"].data_ptr())
+        return self._desc
 
     @property
     def mask_words(self) -> int:

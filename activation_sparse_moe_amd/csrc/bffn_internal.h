@@ -104,6 +104,11 @@ hipError_t launch_cls_losses(int E, const float* z, int64_t T, int L, float alph
                              void* workspace, float* losses, float* dz, hipStream_t s);
 size_t cls_losses_workspace_bytes(int64_t n_tokens, int chunk_len);
 
+// Resident blocks of `kernel` on the current device (CUs x blocks per CU at
+// `block` threads, no dynamic LDS).  Queried once per (device, kernel) and
+// cached, so persistent launches cost no runtime query after the first.
+hipError_t resident_blocks(const void* kernel, int block, int64_t* blocks);
+
 bool route_uses_mfma(int d, int E, int chunk_len, int dtype);
 bool forward_mfma_supported(int d, int de, int dtype);
 size_t forward_mfma_plan_bytes(int64_t units);

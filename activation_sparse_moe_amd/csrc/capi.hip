@@ -6,9 +6,42 @@
 #include <cstdint>
 #include <cstdio>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "bffn_internal.h"
 
 #define BFFN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace bffn {
+
+hipError_t resident_blocks(const void* kernel, int block, int64_t* blocks) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int64_t> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({dev, kernel});
+    if (it != cache.end()) {
+      *blocks = it->second;
+      return hipSuccess;
+    }
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0);
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+  std::lock_guard<std::mutex> lock(mu);
+  cache[{dev, kernel}] = n;
+  *blocks = n;
+  return hipSuccess;
+}
+
+}  // namespace bffn
 
 namespace {
 

@@ -332,15 +332,11 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
   const int rbs = la.de >> 6;
   plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, DENSE ? la.E : 0, rbs, plan);
   // persistent grids sized to the resident capacity (one block per CU at this LDS use)
-  int dev = 0, cus = 0, up_cu = 0, dn_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&up_cu, up_mfma_kernel<NT, DENSE>, kBlock, 0);
+  int64_t grid_up = 0, grid_dn = 0;
+  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&up_mfma_kernel<NT, DENSE>), kBlock, &grid_up);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&dn_cu, down_mfma_kernel<NT, DENSE>, kBlock, 0);
+    e = resident_blocks(reinterpret_cast<const void*>(&down_mfma_kernel<NT, DENSE>), kBlock, &grid_dn);
   if (e != hipSuccess) return e;
-  const int64_t grid_up = (int64_t)cus * (up_cu > 0 ? up_cu : 1);
-  const int64_t grid_dn = (int64_t)cus * (dn_cu > 0 ? dn_cu : 1);
   se.record(0, s);
   up_mfma_kernel<NT, DENSE><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list, plan,
                                                                              hbuf);

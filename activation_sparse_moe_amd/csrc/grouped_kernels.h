@@ -543,12 +543,9 @@ size_t r256(size_t v) { return (v + 255) & ~size_t(255); }
 // of the XCD count so that every XCD gets the same number of blocks.
 template <typename F>
 hipError_t persistent_grid(F kernel, int64_t n_items, int64_t* grid) {
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0);
+  int64_t gsz = 0;
+  const hipError_t e = resident_blocks(reinterpret_cast<const void*>(kernel), kBlock, &gsz);
   if (e != hipSuccess) return e;
-  int64_t gsz = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
   const int64_t need = xcd_grid(n_items > 0 ? n_items : 1);
   if (gsz > need) gsz = need;
   gsz = gsz / kXcds * kXcds;

@@ -45,9 +45,10 @@ __device__ __forceinline__ int wave_argmax(float c0, float c1, int lane) {
 // kind selects the gate function: the BlockFFN router (ReLU, then RMSNorm
 // over the E outputs) or one of the baseline routers (top-k of a softmax;
 // ReLU divided by its sum).
+template <int KIND>
 __device__ void router_epilogue(const float* zp, int nparts, int E, int L, int64_t t0,
-                                const float* __restrict__ b, const float* __restrict__ s, float eps, int kind,
-                                int top_k, float* __restrict__ gates, uint64_t* __restrict__ masks,
+                                const float* __restrict__ b, const float* __restrict__ s, float eps, int top_k,
+                                float* __restrict__ gates, uint64_t* __restrict__ masks,
                                 float* __restrict__ preact) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int W = (E + 63) >> 6;
@@ -65,7 +66,7 @@ __device__ void router_epilogue(const float* zp, int nparts, int E, int L, int64
     bool on0 = v0 && z0 > 0.f, on1 = v1 && z1 > 0.f;
     const float a0 = on0 ? z0 : 0.f, a1 = on1 ? z1 : 0.f;
     float g0, g1;
-    if (kind == BLOCKFFN_ROUTER_TOPK_SOFTMAX) {
+    if (KIND == BLOCKFFN_ROUTER_TOPK_SOFTMAX) {
       const float ninf = -__builtin_huge_valf();
       float c0 = v0 ? z0 : ninf, c1 = v1 ? z1 : ninf;
       float zmax = c0 > c1 ? c0 : c1;
@@ -90,7 +91,7 @@ __device__ void router_epilogue(const float* zp, int nparts, int E, int L, int64
       }
       g0 = on0 ? e0 * inv : 0.f;
       g1 = on1 ? e1 * inv : 0.f;
-    } else if (kind == BLOCKFFN_ROUTER_RELU_SUM) {
+    } else if (KIND == BLOCKFFN_ROUTER_RELU_SUM) {
       const float sum = wave_sum(a0 + a1);
       const float inv = sum > 0.f ? 1.0f / sum : 0.f;
       g0 = a0 * inv;
@@ -140,9 +141,9 @@ __device__ __forceinline__ float dot16<uint16_t>(const uint16_t* a, const uint16
 
 // lpr lanes per router row (a power of two dividing 64); each lane covers nv
 // 16-byte vectors of the row.
-template <typename T>
+template <typename T, int KIND>
 __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const T* __restrict__ x, int L,
-                                                            int lpr, int nv, int kind, int top_k,
+                                                            int lpr, int nv, int top_k,
                                                             float* __restrict__ gates,
                                                             uint64_t* __restrict__ masks,
                                                             float* __restrict__ preact) {
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const 
     }
   }
   __syncthreads();
-  router_epilogue(zp, 1, E, L, t0, b, s, la.eps, kind, top_k, gates, masks, preact);
+  router_epilogue<KIND>(zp, 1, E, L, t0, b, s, la.eps, top_k, gates, masks, preact);
 }
 
 // MFMA router.  Wave w owns d-range [w d/4, (w+1) d/4) for every expert row,
@@ -182,9 +183,9 @@ __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const 
 // mfma_stream.h; the last block's missing stripes repeat a valid stripe and
 // are not stored.  The four per-wave partial sums meet in LDS and are added
 // in a fixed order by the epilogue (deterministic).
-template <int NT>
+template <int NT, int KIND>
 __global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
-                                                            int L, int kind, int top_k, float* __restrict__ gates,
+                                                            int L, int top_k, float* __restrict__ gates,
                                                             uint64_t* __restrict__ masks,
                                                             float* __restrict__ preact) {
   extern __shared__ float zp[];  // [4][E][L]
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const 
     }
   }
   __syncthreads();
-  router_epilogue(zp, 4, E, L, t0, b, s, la.eps, kind, top_k, gates, masks, preact);
+  router_epilogue<KIND>(zp, 4, E, L, t0, b, s, la.eps, top_k, gates, masks, preact);
 }
 
 }  // namespace
@@ -234,19 +235,17 @@ bool route_uses_mfma(int d, int E, int chunk_len, int dtype) {
   return dtype == BLOCKFFN_BF16 && chunk_len >= 8 && E % 16 == 0 && d % 512 == 0;
 }
 
-hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len, int dtype, int kind,
-                        int top_k, float* gates, uint64_t* masks, float* preact, hipStream_t s) {
-  const int64_t units = n_tokens / chunk_len;
-  if (units == 0) return hipSuccess;
-  const int L = chunk_len;
+template <int KIND>
+hipError_t launch_route_kind(const LayerArgs& la, const void* x, int64_t units, int L, int dtype, int top_k,
+                             float* gates, uint64_t* masks, float* preact, hipStream_t s) {
   if (route_uses_mfma(la.d, la.E, L, dtype)) {
     const size_t lds = sizeof(float) * 4 * la.E * L;
     if (L <= 16)
-      route_mfma_kernel<1><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const uint16_t*>(x), L, kind, top_k, gates, masks, preact);
+      route_mfma_kernel<1, KIND><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
+          la, static_cast<const uint16_t*>(x), L, top_k, gates, masks, preact);
     else
-      route_mfma_kernel<2><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const uint16_t*>(x), L, kind, top_k, gates, masks, preact);
+      route_mfma_kernel<2, KIND><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
+          la, static_cast<const uint16_t*>(x), L, top_k, gates, masks, preact);
   } else {
     const size_t lds = sizeof(float) * la.E * L;
     const int vec = dtype == BLOCKFFN_F32 ? 4 : 8;
@@ -255,13 +254,30 @@ hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, in
     while (nvec % lpr) lpr >>= 1;
     const int nv = nvec / lpr;
     if (dtype == BLOCKFFN_F32)
-      route_valu_kernel<float><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const float*>(x), L, lpr, nv, kind, top_k, gates, masks, preact);
+      route_valu_kernel<float, KIND><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
+          la, static_cast<const float*>(x), L, lpr, nv, top_k, gates, masks, preact);
     else
-      route_valu_kernel<uint16_t><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const uint16_t*>(x), L, lpr, nv, kind, top_k, gates, masks, preact);
+      route_valu_kernel<uint16_t, KIND><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
+          la, static_cast<const uint16_t*>(x), L, lpr, nv, top_k, gates, masks, preact);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_route(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len, int dtype, int kind,
+                        int top_k, float* gates, uint64_t* masks, float* preact, hipStream_t s) {
+  const int64_t units = n_tokens / chunk_len;
+  if (units == 0) return hipSuccess;
+  switch (kind) {
+    case BLOCKFFN_ROUTER_TOPK_SOFTMAX:
+      return launch_route_kind<BLOCKFFN_ROUTER_TOPK_SOFTMAX>(la, x, units, chunk_len, dtype, top_k, gates, masks,
+                                                             preact, s);
+    case BLOCKFFN_ROUTER_RELU_SUM:
+      return launch_route_kind<BLOCKFFN_ROUTER_RELU_SUM>(la, x, units, chunk_len, dtype, top_k, gates, masks, preact,
+                                                         s);
+    default:
+      return launch_route_kind<BLOCKFFN_ROUTER_BLOCKFFN>(la, x, units, chunk_len, dtype, top_k, gates, masks, preact,
+                                                         s);
+  }
 }
 
 }  // namespace bffn

@@ -45,6 +45,8 @@ def parse_args(argv=None):
     p.add_argument("--router", default="blockffn", choices=("blockffn", "topk_softmax", "relu_sum"),
                    help="gate function: the BlockFFN router, or a baseline router for comparison")
     p.add_argument("--top-k", type=int, default=2, help="experts per token for --router topk_softmax")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step captured in a HIP graph (no host launch overhead)")
     p.add_argument("--backward", action="store_true",
                    help="also time blockffn_backward on the batch (grouped workloads: one layer)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -217,6 +219,31 @@ class StepRunner:
         avg = {k: sum(v) / len(v) for k, v in per.items() if v}
         return total_ms / steps, avg
 
+    def graph_ms(self, mode: str, steps: int, warmup: int) -> float:
+        """One whole step (every sub-batch) captured in a HIP graph and replayed:
+        the step with no host launch overhead."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(max(1, warmup)):
+                self.step(mode)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(mode)
+        for _ in range(max(1, warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
     def _step_n(self, mode, ev, handle, ns):
         n0 = self.n_stage
         self.n_stage = ns
@@ -388,6 +415,25 @@ def backward_measure(runner, steps: int, warmup: int, dense_steps: int) -> dict:
     flops = 10 * P * d * de + 2 * T * E * d   # U, Q, dW_in, dW_out, dx rows; dW_r
     res = {"ms": round(ms, 5), "stage_ms": stage, "pairs": P, "algorithmic_flops": flops,
            "tflops": round(flops / ms / 1e9, 1), "frac_of_bf16_mfma_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    # the CLS-aware objectives (alpha 8, both weights 1) and a backward that takes their dz
+    losses, dzx = B.blockffn_cls_losses(E, z, cfg.chunk_len, 8.0)
+    grads = {k2: v for k2, v in out.items() if k2 != "dx"}
+
+    def timed_ms(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    res["cls_losses_ms"] = round(timed_ms(lambda: B.blockffn_cls_losses(E, z, cfg.chunk_len, 8.0, losses=losses,
+                                                                        dz=dzx), steps), 5)
+    res["ms_with_cls_gradient"] = round(timed_ms(lambda: B.blockffn_backward(
+        runner.dl, runner.xd, z, dy, workspace=ws, dx=out["dx"], grads=grads, dz_extra=dzx), steps), 5)
     if dense_steps > 0:
         dms = torch_dense_backward_ms(runner, dy, dense_steps)
         res["torch_dense_autograd_ms"] = round(dms, 4)
@@ -467,6 +513,11 @@ def main(argv=None) -> int:
                     "algorithmic_bytes_per_launch": bytes_per[dom] // runner.n_sub,
                     "avg_launch_ms": round(avg[dom] / runner.n_sub, 5), "launches_per_step": runner.n_sub}
 
+    graph = None
+    if args.graph:
+        gms = runner.graph_ms(mode, args.steps, args.warmup)
+        graph = {"ms_per_step": round(gms, 5), "tokens_per_s": round(T / (gms / 1e3), 1)}
+
     backward = None
     if args.backward:
         backward = backward_measure(runner, args.steps, args.warmup, args.dense_steps)
@@ -499,6 +550,7 @@ def main(argv=None) -> int:
                          down_tflops=round(runner.flop_model()["down_flops"] / avg["down"] / 1e9, 1))
                     if grouped else None),
         "dense": dense,
+        "graph": graph,
         "backward": backward,
         "sparsity": {"tls": round(st["tls"], 4), "cls": round(st["cls"], 4), "mean_union": round(U / (T // cfg.chunk_len), 2),
                      "reuse": round(st["reuse"], 4)},

@@ -17,9 +17,10 @@
 // non-temporal policy through a wave-private LDS ring (lds_stream.h): full
 // 128-byte lines per load instruction, two 64-element steps in flight, the
 // step stream continuing across work items.  Both kernels are persistent
-// (one block per CU); each block owns a contiguous, statically balanced range
-// of work items (equal counts for the up items, equal step totals for the
-// variable-length down items) and its waves take items from that range
+// (one block per CU).  Each up block owns a contiguous equal share of the
+// equal-sized up items; for the variable-length down items each XCD owns a
+// range of equal step total, whose blocks take its items in turn (a chunk's
+// hidden rows then stay in the XCD's L2).  A block's waves take its items
 // through an LDS counter.  Items are decoded with scalar loads only, so
 // nothing in the loop waits on a returning memory operation except the
 // weight stream.
@@ -77,13 +78,17 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
   const int d = la.d, de = la.de, E = la.E, rbs = de >> 6;
   const int nsteps = d / kStepK;
   uint8_t* bufs = lds + w * kRingBufs * G::kBufBytes;
-  // the block's items (all of equal size): an equal share of the total
+  // the block's items (all of equal size): a contiguous equal share.  (Giving
+  // each XCD a range that its blocks take in turn keeps a chunk's token rows
+  // in L2, but then an XCD streams neighbouring weight row blocks at once, in
+  // 128-byte pieces 2 d bytes apart, and HBM efficiency drops more than the
+  // re-read token rows cost: measured 5.45 against 6.49 TB/s at d = 4096.)
   const int64_t total = prefix[n_units];
-  const int64_t blk_lo = (int64_t)blockIdx.x * total / gridDim.x;
+  const int64_t blk_lo = (int64_t)blockIdx.x * total / gridDim.x, stride = 1;
   const int64_t item_end = ((int64_t)blockIdx.x + 1) * total / gridDim.x;
   if (threadIdx.x == 0) taken = 0;
   __syncthreads();
-  int64_t item = take_item(&taken, blk_lo, lane);
+  int64_t item = take_item(&taken, blk_lo, stride, lane);
   if (item >= item_end) return;
 
   auto decode = [&](int64_t it_idx) {
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
   for (int t = 0;; ++t) {
     // issue the step two ahead, or repeat a valid one past the end of the range
     if (!iss_done && k_iss == nsteps) {
-      item = take_item(&taken, blk_lo, lane);
+      item = take_item(&taken, blk_lo, stride, lane);
       if (item < item_end) {
         nxt = decode(item);
         has_next = true;
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
 }
 
 // ---- down-projection: Y[unit][kb .. kb + 64) = sum over slots of H'[unit][slot] W_out[i]^T ----
-// Items (chunk, 64 output rows) take count[chunk] * d_e / 64 steps; each wave
+// Items (chunk, 64 output rows) take count[chunk] * d_e / 64 steps; each XCD
 // gets the items whose first step falls in its equal share of all steps.
 template <int NT, bool DENSE>
 __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t n_units, int L,
@@ -223,12 +228,14 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
     while (item_start(lo, kb) < s) ++kb;  // stops before kbs
     return lo * kbs + kb;
   };
-  // the block's items: those whose first step falls in its equal share of all
-  // steps (the last block also takes items starting at the very end)
+  // the block's items: its turns in its XCD's range, the items whose first
+  // step falls in an equal share of all steps (the last range also takes
+  // items starting at the very end)
   const int64_t S = prefix[n_units] / rbs * kbs * spe;
-  const int64_t blk_lo = first_item_at((int64_t)blockIdx.x * S / gridDim.x);
-  const int64_t item_end = blockIdx.x + 1 == gridDim.x ? n_units * kbs
-                                                        : first_item_at(((int64_t)blockIdx.x + 1) * S / gridDim.x);
+  const XcdShare share = xcd_share([&](int k) {
+    return k == kXcds ? n_units * kbs : first_item_at((int64_t)k * S / kXcds);
+  });
+  const int64_t blk_lo = share.lo, stride = share.stride, item_end = share.end;
   if (threadIdx.x == 0) taken = 0;
   __syncthreads();
 
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   // empty union get y = 0 here
   auto next_item = [&](DownItem& it) -> bool {
     for (;;) {
-      const int64_t item = take_item(&taken, blk_lo, lane);
+      const int64_t item = take_item(&taken, blk_lo, stride, lane);
       if (item >= item_end) return false;
       it.unit = item / kbs;
       it.kb = (int)(item % kbs);
@@ -337,6 +344,9 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
   if (e == hipSuccess)
     e = resident_blocks(reinterpret_cast<const void*>(&down_mfma_kernel<NT, DENSE>), kBlock, &grid_dn);
   if (e != hipSuccess) return e;
+  // the item shares assume the grid is a multiple of the XCD count
+  grid_up = grid_up / kXcds * kXcds > 0 ? grid_up / kXcds * kXcds : kXcds;
+  grid_dn = grid_dn / kXcds * kXcds > 0 ? grid_dn / kXcds * kXcds : kXcds;
   se.record(0, s);
   up_mfma_kernel<NT, DENSE><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list, plan,
                                                                              hbuf);

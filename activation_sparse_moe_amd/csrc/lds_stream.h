@@ -12,10 +12,11 @@
 // Two steps are always in flight ahead of the one being multiplied, so the
 // wait before a step is a constant vmcnt.
 //
-// Work items are shared out in two levels: each block owns a contiguous,
-// statically balanced range of items, and the block's waves take items from
-// that range through an LDS counter (an LDS atomic waits on lgkmcnt, not on
-// vmcnt, so taking work never drains the weight stream).
+// Work items are shared out in two levels: each block gets a statically
+// balanced share of the items (a contiguous range, or its turns in its XCD's
+// range), and the block's waves take items from that share through an LDS
+// counter (an LDS atomic waits on lgkmcnt, not on vmcnt, so taking work never
+// drains the weight stream).
 //
 // Operand layout (v_mfma_f32_16x16x32_bf16, checked on gfx950): lane l
 // supplies row l % 16 of A and column l % 16 of B with k elements
@@ -101,19 +102,38 @@ __device__ __forceinline__ void ring_mfma(f32x4 (&acc)[4][NT], const uint8_t* bu
   }
 }
 
-// Next item of the block's range for this wave: LDS counter, broadcast.  The
-// counter sits outside every ring buffer, so the atomic cannot race with the
-// weight DMA; it is written as assembly (with its own lgkmcnt wait, so the
-// result register is complete when the block ends) because the compiler
-// cannot prove that and would otherwise drain every in-flight DMA first.
-__device__ __forceinline__ int64_t take_item(unsigned* counter, int64_t lo, int lane) {
+// Next item of the block's share for this wave: LDS counter k, broadcast,
+// item lo + stride k.  The counter sits outside every ring buffer, so the
+// atomic cannot race with the weight DMA; it is written as assembly (with its
+// own lgkmcnt wait, so the result register is complete when the block ends)
+// because the compiler cannot prove that and would otherwise drain every
+// in-flight DMA first.
+__device__ __forceinline__ int64_t take_item(unsigned* counter, int64_t lo, int64_t stride, int lane) {
   unsigned v = 0;
   if (lane == 0) {
     const unsigned addr = (unsigned)(uintptr_t)(lvoid_t*)counter;
     const unsigned one = 1u;
     asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr), "v"(one));
   }
-  return lo + (int64_t)__builtin_amdgcn_readfirstlane(__shfl(v, 0, kWave));
+  return lo + stride * (int64_t)__builtin_amdgcn_readfirstlane(__shfl(v, 0, kWave));
+}
+
+// A block's share of the items [0, n) of a persistent launch: the items are
+// split into one contiguous range per XCD (by `split`, which maps a fraction
+// k / kXcds of the work to an item index), and the blocks of an XCD take
+// that range's items in turn (block j of the XCD: range start + j, + per_xcd,
+// ...).  The XCD's waves then work on neighbouring items at any time: items
+// of one chunk share that chunk's token rows, which stay in the XCD's L2.
+struct XcdShare {
+  int64_t lo, stride, end;
+};
+template <typename Split>
+__device__ __forceinline__ XcdShare xcd_share(Split split) {
+  const int64_t per_xcd = gridDim.x / kXcds;  // the grid is a multiple of kXcds
+  const int xcd = (int)(blockIdx.x % kXcds);
+  const int64_t j = blockIdx.x / kXcds;
+  const int64_t lo = split(xcd), hi = split(xcd + 1);
+  return XcdShare{lo + j, per_xcd, hi};
 }
 
 template <int NT>

@@ -45,8 +45,8 @@ def parse_args(argv=None):
     p.add_argument("--router", default="blockffn", choices=("blockffn", "topk_softmax", "relu_sum"),
                    help="gate function: the BlockFFN router, or a baseline router for comparison")
     p.add_argument("--top-k", type=int, default=2, help="experts per token for --router topk_softmax")
-    p.add_argument("--graph", action="store_true",
-                   help="also time the step captured in a HIP graph (no host launch overhead)")
+    p.add_argument("--eager", action="store_true",
+                   help="time eager launches (default: each step replayed from a HIP graph)")
     p.add_argument("--backward", action="store_true",
                    help="also time blockffn_backward on the batch (grouped workloads: one layer)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -474,7 +474,11 @@ def main(argv=None) -> int:
     if args.copy_calibration:
         copy_calibration()
     runner = StepRunner(cfg, mode, args.router, args.top_k)
-    ms, avg = runner.timed(mode, args.steps, args.warmup)
+    # eager steps, instrumented: per-kernel times for the roofline
+    eager_ms, avg = runner.timed(mode, args.steps, args.warmup)
+    # the timed steps: each whole step (every sub-batch) replayed from a HIP
+    # graph, so host launch overhead is not in the figure (--eager: eager)
+    ms = eager_ms if args.eager else runner.graph_ms(mode, args.steps, args.warmup)
     from activation_sparse_moe_amd import binding as B
     st = B.stats_dict(runner.stats)
     bytes_per, U, active_weight, step_alg = runner.byte_model()
@@ -489,6 +493,8 @@ def main(argv=None) -> int:
                  "speedup_forward": round(dfwd / avg["forward"], 3) if "forward" in avg else None}
     elif args.dense_steps > 0:
         dms, davg = runner.timed("dense", args.dense_steps, 1)
+        if not args.eager:
+            dms = runner.graph_ms("dense", args.dense_steps, 1)
         dense = {"kind": "same kernels, every expert (BLOCKFFN_MODE_DENSE)", "ms_per_step": round(dms, 4),
                  "speedup_step": round(dms / ms, 3)}
         if "forward" in davg and "forward" in avg:
@@ -513,10 +519,6 @@ def main(argv=None) -> int:
                     "algorithmic_bytes_per_launch": bytes_per[dom] // runner.n_sub,
                     "avg_launch_ms": round(avg[dom] / runner.n_sub, 5), "launches_per_step": runner.n_sub}
 
-    graph = None
-    if args.graph:
-        gms = runner.graph_ms(mode, args.steps, args.warmup)
-        graph = {"ms_per_step": round(gms, 5), "tokens_per_s": round(T / (gms / 1e3), 1)}
 
     backward = None
     if args.backward:
@@ -550,7 +552,9 @@ def main(argv=None) -> int:
                          down_tflops=round(runner.flop_model()["down_flops"] / avg["down"] / 1e9, 1))
                     if grouped else None),
         "dense": dense,
-        "graph": graph,
+        "timing": {"steps": "eager launches" if args.eager else "HIP graph replay of each whole step",
+                   "eager_ms_per_step": round(eager_ms, 5),
+                   "kernel_ms": "eager steps with HIP events around each launch"},
         "backward": backward,
         "sparsity": {"tls": round(st["tls"], 4), "cls": round(st["cls"], 4), "mean_union": round(U / (T // cfg.chunk_len), 2),
                      "reuse": round(st["reuse"], 4)},

@@ -1,12 +1,13 @@
-"""CPU oracle of the BlockFFN layer (forward and backward) -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle of the BlockFFN layer (forward and backward) and of the FFF tree
+layer -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never loads it and
 shares no code with it.
 
-The arithmetic lives in ``blockffn_oracle.c`` (plain C, double accumulation,
-OpenMP over tokens); this module only builds it with gcc and marshals numpy
-arrays.  Arrays are float32 (an fp32 layer) or uint16 bfloat16 bit patterns
+The arithmetic lives in ``blockffn_oracle.c`` and ``fff_oracle.c`` (plain C,
+double accumulation, OpenMP over tokens); this module only builds them with
+gcc and marshals numpy arrays.  Arrays are float32 (an fp32 layer) or uint16 bfloat16 bit patterns
 (a bf16 layer); the C code widens them itself.
 """
 from __future__ import annotations
@@ -19,7 +20,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "blockffn_oracle.c")
+SOURCES = (os.path.join(_HERE, "blockffn_oracle.c"), os.path.join(_HERE, "fff_oracle.c"))
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -40,11 +41,11 @@ class OracleStats(ctypes.Structure):
 
 def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc (plain -O2, no fast-math, no FMA contraction)."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+    if not force and os.path.exists(_LIB) and all(os.path.getmtime(_LIB) >= os.path.getmtime(s) for s in SOURCES):
         return _LIB
     tmp = _LIB + f".tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-           "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+           "-shared", "-fPIC", "-o", tmp, *SOURCES, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -73,10 +74,12 @@ def _load():
             lib.oracle_backward.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, dbl, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp, vp]
             lib.oracle_cls_losses.argtypes = [i32, vp, i64, i32, dbl, dbl, dbl, vp, vp]
+            lib.oracle_fff_forward.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp]
             lib.oracle_num_threads.argtypes = []
             for name in ("oracle_route", "oracle_expert", "oracle_forward_tokens",
                          "oracle_forward_chunks", "oracle_forward_dense", "oracle_union",
-                         "oracle_stats", "oracle_backward", "oracle_route_with", "oracle_cls_losses", "oracle_num_threads"):
+                         "oracle_stats", "oracle_backward", "oracle_route_with", "oracle_cls_losses", "oracle_fff_forward",
+                         "oracle_num_threads"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -280,3 +283,31 @@ def cls_losses(z, chunk_len: int, alpha: float, w_al: float = 1.0, w_cs: float =
     _check(_load().oracle_cls_losses(E, _p(z), T, int(chunk_len), float(alpha), float(w_al), float(w_cs), _p(loss),
                                       _p(dz)), "oracle_cls_losses")
     return float(loss[0]), float(loss[1]), dz
+
+
+def fff_nodes(depth: int) -> int:
+    """Nodes of one perfect binary tree of depth D (levels 0..D)."""
+    return (1 << (depth + 1)) - 1
+
+
+def fff_forward(x, w_node, b_node, w_out, post: bool = False, dense: bool = False, want_paths: bool = True):
+    """FFF tree layer.  x[T][d]; w_node, w_out [P][N][d] with N = 2^(D+1) - 1; b_node [P][N] or None.
+
+    Returns (paths, preact, y): paths [T][P][D+1] int32 node ids (None when dense or not wanted),
+    preact [T][P][D+1] float64 ([T][P][N] when dense), y [T][d] float64."""
+    x, w_node, w_out = _c(x), _c(w_node), _c(w_out)
+    code = _dtype_code(x)
+    assert _dtype_code(w_node) == code and _dtype_code(w_out) == code, "x and the node rows must share a dtype"
+    T, d = x.shape
+    P, N, d2 = w_node.shape
+    D = int(N + 1).bit_length() - 2
+    assert d2 == d and fff_nodes(D) == N and w_out.shape == (P, N, d)
+    b = _c(b_node, np.float32)
+    assert b is None or b.shape == (P, N)
+    V = N if dense else D + 1
+    paths = np.empty((T, P, V), np.int32) if (want_paths and not dense) else None
+    preact = np.empty((T, P, V), np.float64)
+    y = np.empty((T, d), np.float64)
+    _check(_load().oracle_fff_forward(d, P, D, code, int(bool(post)), int(bool(dense)), _p(x), T, _p(w_node), _p(b),
+                                      _p(w_out), _p(paths), _p(preact), _p(y)), "oracle_fff_forward")
+    return paths, preact, y

@@ -13,7 +13,11 @@ dx, a missing gate in dW_out; and in the baseline routers a tie broken the
 other way, an unshifted softmax sum, a missing ReMoE normalisation; and in
 the CLS-aware objectives an unshifted locality target, the complement of the
 chunk probability, a chunk gradient that includes the token itself, and an
-extra router gradient applied to active pairs only.
+extra router gradient applied to active pairs only; and in the FFF tree layer
+a turn taken at c >= 0, swapped children, one level too few, the tanh
+approximation of GELU, a dropped node bias, GELU kept at the nodes in the
+post variant, a dense evaluation that skips the leaves, and the output taken
+from the input row.
 """
 import os
 import subprocess
@@ -23,7 +27,8 @@ import tempfile
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "oracle", "blockffn_oracle.c")
+ORACLE_DIR = os.path.join(ROOT, "oracle")
+SOURCES = ("blockffn_oracle.c", "fff_oracle.c")
 
 MUTANTS = {
     "relu_not_strict": ("if (acc > 0.0) m[i / 64]", "if (acc >= 0.0) m[i / 64]"),
@@ -77,20 +82,51 @@ MUTANTS = {
 PIN_FILES = ("test_oracle_pins.py", "test_oracle_backward_pins.py", "test_oracle_router_pins.py",
              "test_oracle_cls_pins.py")
 
+# mistakes in the FFF tree layer (fff_oracle.c), caught by its own pins
+FFF_MUTANTS = {
+    "fff_turn_not_strict": ("n = 2 * n + 1 + (c > 0.0 ? 1 : 0);", "n = 2 * n + 1 + (c >= 0.0 ? 1 : 0);"),
+    "fff_children_swapped": ("n = 2 * n + 1 + (c > 0.0 ? 1 : 0);", "n = 2 * n + 1 + (c > 0.0 ? 0 : 1);"),
+    "fff_one_level_short": ("const int64_t V = dense ? N : (int64_t)D + 1;", "const int64_t V = dense ? N : (int64_t)D;"),
+    "fff_gelu_tanh": ("return 0.5 * c * (1.0 + erf(c / sqrt(2.0)));",
+                      "return 0.5 * c * (1.0 + tanh(0.7978845608028654 * (c + 0.044715 * c * c * c)));"),
+    "fff_bias_dropped": ("if (b_node) c += (double)b_node[row];", ""),
+    "fff_post_gelu_at_nodes": ("const double a = post ? c : fff_gelu(c);", "const double a = fff_gelu(c);"),
+    "fff_dense_skips_leaves": ("const int64_t V = dense ? N : (int64_t)D + 1;",
+                               "const int64_t V = dense ? (N - 1) / 2 : (int64_t)D + 1;"),
+    "fff_output_from_input_row": ("yt[k] += a * fff_widen(w_out, row * d + k, dtype);",
+                                  "yt[k] += a * fff_widen(w_node, row * d + k, dtype);"),
+}
+FFF_PIN_FILES = ("test_oracle_fff_pins.py",)
+
+
+def _run_mutant(name, target, old, new, pin_files):
+    path = os.path.join(ORACLE_DIR, target)
+    src = open(path).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as tmp:
+        files = []
+        for f in SOURCES:
+            c = os.path.join(tmp, f)
+            text = open(os.path.join(ORACLE_DIR, f)).read()
+            open(c, "w").write(src.replace(old, new) if f == target else text)
+            files.append(c)
+        so = os.path.join(tmp, "libmutant.so")
+        subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
+                        "-o", so, *files, "-lm"], check=True)
+        env = dict(os.environ, BLOCKFFN_ORACLE_LIB=so)
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            *[os.path.join(ROOT, "tests", f) for f in pin_files]],
+                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+        assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name):
     old, new = MUTANTS[name]
-    src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
-    with tempfile.TemporaryDirectory() as tmp:
-        c = os.path.join(tmp, "mutant.c")
-        so = os.path.join(tmp, "libmutant.so")
-        open(c, "w").write(src.replace(old, new))
-        subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
-                        "-o", so, c, "-lm"], check=True)
-        env = dict(os.environ, BLOCKFFN_ORACLE_LIB=so)
-        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                            *[os.path.join(ROOT, "tests", f) for f in PIN_FILES]],
-                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
-        assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+    _run_mutant(name, "blockffn_oracle.c", old, new, PIN_FILES)
+
+
+@pytest.mark.parametrize("name", sorted(FFF_MUTANTS))
+def test_fff_pins_catch_planted_mistake(name):
+    old, new = FFF_MUTANTS[name]
+    _run_mutant(name, "fff_oracle.c", old, new, FFF_PIN_FILES)

@@ -24,10 +24,13 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_CHUNK, ERR_WORKSPACE = -1, -2, -3, -4, -5
 ERR_MODE, ERR_ALIGN, ERR_LAYERS, ERR_HIP = -6, -7, -8, -9
 
+FFF_GELU_NODES, FFF_GELU_OUTPUT = 0, 1
+FFF_SPARSE, FFF_DENSE = 0, 1
+
 # Every symbol include/blockffn.h declares.
 EXPORTS = ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats",
            "blockffn_backward", "blockffn_backward_workspace_size",
-           "blockffn_cls_losses", "blockffn_cls_losses_workspace_size",
+           "blockffn_cls_losses", "blockffn_cls_losses_workspace_size", "blockffn_fff_forward",
            "blockffn_set_stage_events", "blockffn_workspace_size", "blockffn_status_string",
            "blockffn_last_error", "blockffn_version")
 
@@ -39,6 +42,14 @@ class BlockffnLayer(ctypes.Structure):
         ("layer_stride", ctypes.c_int64),
         ("w_router", ctypes.c_void_p), ("b_router", ctypes.c_void_p), ("rms_scale", ctypes.c_void_p),
         ("w_in", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
+    ]
+
+
+class BlockffnFffLayer(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int32), ("n_trees", ctypes.c_int32), ("depth", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("activation", ctypes.c_int32), ("reserved", ctypes.c_int32), ("layer_stride", ctypes.c_int64),
+        ("w_node", ctypes.c_void_p), ("b_node", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
     ]
 
 
@@ -85,12 +96,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.blockffn_backward.argtypes = [lp, vp, i64, vp, vp, vp, vp, sz, vp, ctypes.POINTER(BlockffnGrads), vp]
         flt = ctypes.c_float
         lib.blockffn_cls_losses.argtypes = [i32, vp, i64, i32, flt, flt, flt, vp, sz, vp, vp, vp]
+        lib.blockffn_fff_forward.argtypes = [ctypes.POINTER(BlockffnFffLayer), i32, vp, i64, i32, vp, vp, vp, vp]
         lib.blockffn_cls_losses_workspace_size.argtypes = [i64, i32]
         lib.blockffn_cls_losses_workspace_size.restype = sz
         lib.blockffn_backward_workspace_size.argtypes = [lp, i64]
         lib.blockffn_backward_workspace_size.restype = sz
         for f in ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward",
-                  "blockffn_sparsity_stats", "blockffn_backward", "blockffn_cls_losses"):
+                  "blockffn_sparsity_stats", "blockffn_backward", "blockffn_cls_losses", "blockffn_fff_forward"):
             getattr(lib, f).restype = ctypes.c_int
         lib.blockffn_set_stage_events.argtypes = [vp, i32]
         lib.blockffn_set_stage_events.restype = ctypes.c_int

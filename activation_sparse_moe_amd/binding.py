@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import _capi
-from ._capi import BF16, F32, MODES, ROUTERS, BlockffnGrads, BlockffnLayer, check, load
+from ._capi import BF16, F32, MODES, ROUTERS, BlockffnFffLayer, BlockffnGrads, BlockffnLayer, check, load
 
 _ALIGN = 256
 _STATS_WORDS = 8 + 129
@@ -316,3 +316,87 @@ def stats_dict(stats_dev: torch.Tensor) -> dict:
 
 def masks_to_u64(token_masks: torch.Tensor) -> np.ndarray:
     return token_masks.cpu().numpy().view(np.uint64)
+
+
+class DeviceFffLayer:
+    """`replicas` copies of one FFF tree layer in a single device buffer.
+
+    Copy r holds w_node [P][N][d], b_node [P][N] (fp32, optional) and
+    w_out [P][N][d] at replica 0's offsets plus r * stride bytes: the
+    stacked-layer convention of blockffn_fff_forward (token t uses copy
+    t % n_layers)."""
+
+    def __init__(self, d: int, n_trees: int, depth: int, dtype: int, post: bool = False, device="cuda",
+                 replicas: int = 1, has_bias: bool = True):
+        assert dtype in (F32, BF16)
+        self.d, self.n_trees, self.depth, self.dtype = d, n_trees, depth, dtype
+        self.post, self.replicas, self.device = bool(post), int(replicas), torch.device(device)
+        self.nodes = (1 << (depth + 1)) - 1
+        rows = n_trees * self.nodes
+        es = _elem(dtype)
+        sizes = [("w_node", rows * d * es), ("b_node", 4 * rows if has_bias else 0), ("w_out", rows * d * es)]
+        self._off = {}
+        off = 0
+        for name, nbytes in sizes:
+            self._off[name] = (off, nbytes) if nbytes else None
+            off = _round(off + nbytes)
+        self.stride = _round(off, 4096)
+        self.buffer = torch.empty(self.stride * self.replicas, dtype=torch.uint8, device=self.device)
+        self._desc = None
+
+    def tensors(self, r: int = 0) -> dict:
+        td = _torch_dtype(self.dtype)
+        P, N, d = self.n_trees, self.nodes, self.d
+
+        def view(name, shape, dt):
+            slot = self._off[name]
+            if slot is None:
+                return None
+            off, nbytes = slot
+            base = r * self.stride + off
+            return self.buffer[base:base + nbytes].view(dt).view(*shape)
+
+        return dict(w_node=view("w_node", (P, N, d), td), b_node=view("b_node", (P, N), torch.float32),
+                    w_out=view("w_out", (P, N, d), td))
+
+    @classmethod
+    def from_workload(cls, layer, post: bool = False, device="cuda", replicas: int = 1) -> "DeviceFffLayer":
+        dtype = F32 if layer.dtype == "f32" else BF16
+        self = cls(layer.d, layer.n_trees, layer.depth, dtype, post, device, replicas,
+                   has_bias=layer.b_node is not None)
+        t = self.tensors(0)
+        t["w_node"].copy_(_to_device(layer.w_node, dtype, self.device))
+        t["w_out"].copy_(_to_device(layer.w_out, dtype, self.device))
+        if layer.b_node is not None:
+            t["b_node"].copy_(torch.as_tensor(np.asarray(layer.b_node, np.float32)).to(self.device))
+        for r in range(1, self.replicas):
+            self.buffer[r * self.stride:(r + 1) * self.stride].copy_(self.buffer[:self.stride])
+        return self
+
+    def descriptor(self) -> BlockffnFffLayer:
+        if self._desc is None:
+            t = self.tensors(0)
+            self._desc = BlockffnFffLayer(self.d, self.n_trees, self.depth, self.dtype,
+                                          _capi.FFF_GELU_OUTPUT if self.post else _capi.FFF_GELU_NODES, 0,
+                                          self.stride, t["w_node"].data_ptr(),
+                                          t["b_node"].data_ptr() if t["b_node"] is not None else None,
+                                          t["w_out"].data_ptr())
+        return self._desc
+
+
+def blockffn_fff_forward(layer: DeviceFffLayer, x: torch.Tensor, mode: str = "sparse", want_paths: bool = False,
+                         y: Optional[torch.Tensor] = None, paths: Optional[torch.Tensor] = None,
+                         node_preact: Optional[torch.Tensor] = None, n_layers: Optional[int] = None, stream=None):
+    """FFF tree layer -> (y [T][d] f32, paths [T][P][D+1] i32 or None, node_preact [T][P][D+1] f32 or None)."""
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device)
+    if want_paths and paths is None:
+        paths = torch.empty((T, layer.n_trees, layer.depth + 1), dtype=torch.int32, device=x.device)
+    if want_paths and node_preact is None:
+        node_preact = torch.empty((T, layer.n_trees, layer.depth + 1), dtype=torch.float32, device=x.device)
+    m = {"sparse": _capi.FFF_SPARSE, "dense": _capi.FFF_DENSE}[mode]
+    nl = layer.replicas if n_layers is None else n_layers
+    check(load().blockffn_fff_forward(ctypes.byref(layer.descriptor()), nl, _ptr(x), T, m, _ptr(paths),
+                                      _ptr(node_preact), _ptr(y), _stream(stream)), "blockffn_fff_forward")
+    return y, paths, node_preact

@@ -104,6 +104,12 @@ hipError_t launch_cls_losses(int E, const float* z, int64_t T, int L, float alph
                              void* workspace, float* losses, float* dz, hipStream_t s);
 size_t cls_losses_workspace_bytes(int64_t n_tokens, int chunk_len);
 
+// FFF tree layer: rows of d elements are 1..kFffMaxPieces pieces of 1 KiB.
+constexpr int kFffMaxPieces = 8;
+bool fff_width_supported(int d, int dtype);
+hipError_t launch_fff_forward(const blockffn_fff_layer& ly, int n_layers, const void* x, int64_t n_tokens, bool dense,
+                              int32_t* paths, float* preact, float* y, hipStream_t s);
+
 // Resident blocks of `kernel` on the current device (CUs x blocks per CU at
 // `block` threads, no dynamic LDS).  Queried once per (device, kernel) and
 // cached, so persistent launches cost no runtime query after the first.

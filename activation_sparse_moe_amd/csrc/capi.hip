@@ -363,6 +363,41 @@ BFFN_EXPORT int blockffn_cls_losses(int32_t n_experts, const float* preact, int6
                     "cls-losses launch");
 }
 
+BFFN_EXPORT int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_layers, const void* x,
+                                     int64_t n_tokens, int32_t mode, int32_t* paths, float* node_preact, float* y,
+                                     hipStream_t stream) {
+  if (!layer) return fail(BLOCKFFN_ERR_NULL, "layer descriptor is NULL");
+  const blockffn_fff_layer& ly = *layer;
+  if (ly.dtype != BLOCKFFN_F32 && ly.dtype != BLOCKFFN_BF16) return fail(BLOCKFFN_ERR_DTYPE, "unknown dtype %d", ly.dtype);
+  if (!bffn::fff_width_supported(ly.d, ly.dtype))
+    return fail(BLOCKFFN_ERR_SHAPE, "d %d: bf16 needs a multiple of 512 up to 4096, f32 a multiple of 256 up to 2048",
+                ly.d);
+  if (ly.n_trees < 1 || ly.n_trees > (1 << 16)) return fail(BLOCKFFN_ERR_SHAPE, "n_trees %d outside [1, 65536]", ly.n_trees);
+  if (ly.depth < 0 || ly.depth > 15) return fail(BLOCKFFN_ERR_SHAPE, "depth %d outside [0, 15]", ly.depth);
+  if (ly.activation != BLOCKFFN_FFF_GELU_NODES && ly.activation != BLOCKFFN_FFF_GELU_OUTPUT)
+    return fail(BLOCKFFN_ERR_SHAPE, "unknown activation placement %d", ly.activation);
+  if (ly.reserved != 0) return fail(BLOCKFFN_ERR_SHAPE, "reserved field must be 0");
+  if (mode != BLOCKFFN_FFF_SPARSE && mode != BLOCKFFN_FFF_DENSE) return fail(BLOCKFFN_ERR_MODE, "unknown mode %d", mode);
+  if (mode == BLOCKFFN_FFF_DENSE && (paths || node_preact))
+    return fail(BLOCKFFN_ERR_MODE, "paths and node_preact must be NULL in dense mode");
+  if (n_layers < 1) return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d < 1", n_layers);
+  if (n_layers > 1 && ly.layer_stride <= 0)
+    return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d > 1 needs a positive layer_stride", n_layers);
+  if (n_layers > 1 && ly.layer_stride % 256 != 0)
+    return fail(BLOCKFFN_ERR_ALIGN, "layer_stride %lld is not a multiple of 256", (long long)ly.layer_stride);
+  if (n_tokens < 0 || n_tokens > INT32_MAX)
+    return fail(BLOCKFFN_ERR_SHAPE, "n_tokens %lld outside [0, 2^31)", (long long)n_tokens);
+  if (!ly.w_node || !ly.w_out) return fail(BLOCKFFN_ERR_NULL, "w_node and w_out must be non-NULL");
+  if (n_tokens > 0 && (!x || !y)) return fail(BLOCKFFN_ERR_NULL, "x and y must be non-NULL");
+  if (!aligned(ly.w_node, 16) || !aligned(ly.w_out, 16) || !aligned(x, 16) || !aligned(y, 16))
+    return fail(BLOCKFFN_ERR_ALIGN, "w_node, w_out, x and y must be 16-byte aligned");
+  if (!aligned(ly.b_node, 4) || !aligned(paths, 4) || !aligned(node_preact, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "b_node, paths and node_preact must be 4-byte aligned");
+  return hip_status(bffn::launch_fff_forward(ly, n_layers, x, n_tokens, mode == BLOCKFFN_FFF_DENSE, paths,
+                                             node_preact, y, stream),
+                    "fff forward launch");
+}
+
 BFFN_EXPORT int blockffn_set_stage_events(hipEvent_t* events, int32_t n_events) {
   if (events != nullptr && n_events < 1) return fail(BLOCKFFN_ERR_SHAPE, "n_events %d < 1", n_events);
   g_stage_events.ev = events;

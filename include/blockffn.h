@@ -282,6 +282,60 @@ int blockffn_cls_losses(int32_t n_experts, const float* preact, int64_t n_tokens
 size_t blockffn_cls_losses_workspace_size(int64_t n_tokens, int32_t chunk_len);
 
 /*
+ * ---- FFF tree layer (a second activation-sparse feed-forward block) ----
+ *
+ * Source: "Dynamic sparsity in tree-structured feed-forward layers at
+ * scale", write-up on gist.science, §2 methodology (architecture design, key
+ * mechanisms) and §4 (efficiency).  The layer is P parallel perfect binary
+ * trees of depth D.  Tree p has N = 2^(D+1) - 1 nodes in heap order (root 0,
+ * children of node n at 2n + 1 = left and 2n + 2 = right); node n holds an
+ * input row w_node[p][n][0..d), a bias b_node[p][n] and an output row
+ * w_out[p][n][0..d).  For a token x, every tree routes hard from the root:
+ * at level l = 0..D the current node computes c = w_node[p][n] . x + b[p][n]
+ * and the walk continues right iff c > 0, so D + 1 of the N nodes run.
+ *   GELU_NODES  (FFF)      y = sum_p sum_l GELU(c_{p,l}) w_out[p][n_{p,l}]
+ *   GELU_OUTPUT (FFFpost)  y = GELU(sum_p sum_l c_{p,l} w_out[p][n_{p,l}])
+ * with the exact GELU(c) = c Phi(c).  Sums are fp32; the dot products are
+ * reduced in a fixed order, so results are bit-reproducible.
+ *
+ * With n_layers > 1, layer l's arrays live at (char*)ptr + l * layer_stride
+ * for every pointer (NULL stays NULL) and token t uses layer t % n_layers.
+ */
+#define BLOCKFFN_FFF_GELU_NODES 0  /* GELU on every visited node's pre-activation */
+#define BLOCKFFN_FFF_GELU_OUTPUT 1 /* visited nodes linear, GELU on the summed output */
+
+#define BLOCKFFN_FFF_SPARSE 0 /* one root-to-leaf walk per tree */
+#define BLOCKFFN_FFF_DENSE 1  /* every node of every tree: the dense block of width P N (the comparison path) */
+
+typedef struct blockffn_fff_layer {
+  int32_t d;            /* model width: bf16 a multiple of 512 up to 4096, f32 a multiple of 256 up to 2048 */
+  int32_t n_trees;      /* P, 1 .. 65536 */
+  int32_t depth;        /* D, 0 .. 15 */
+  int32_t dtype;        /* BLOCKFFN_F32 or BLOCKFFN_BF16, for x, w_node and w_out */
+  int32_t activation;   /* BLOCKFFN_FFF_GELU_NODES or BLOCKFFN_FFF_GELU_OUTPUT */
+  int32_t reserved;     /* must be 0 */
+  int64_t layer_stride; /* bytes between consecutive layers (multiple of 256) */
+  const void* w_node;   /* [P][N][d], dtype, 16-byte aligned */
+  const float* b_node;  /* [P][N] fp32, or NULL for no bias */
+  const void* w_out;    /* [P][N][d], dtype, 16-byte aligned */
+} blockffn_fff_layer;
+
+/*
+ * FFF layer forward.
+ *   x            [n_tokens][d] in the layer's dtype, 16-byte aligned
+ *   mode         BLOCKFFN_FFF_SPARSE or BLOCKFFN_FFF_DENSE
+ *   paths        [n_tokens][P][D+1] i32 out: the node visited at each level,
+ *                or NULL (must be NULL in DENSE mode)
+ *   node_preact  [n_tokens][P][D+1] fp32 out: c at each visited node, or
+ *                NULL (must be NULL in DENSE mode)
+ *   y            [n_tokens][d] fp32 out, overwritten, 16-byte aligned
+ * n_tokens below 2^31; n_tokens == 0 enqueues nothing.  No workspace.
+ * Errors: NULL, SHAPE, DTYPE, MODE, ALIGN, LAYERS, HIP.
+ */
+int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+                         int32_t mode, int32_t* paths, float* node_preact, float* y, hipStream_t stream);
+
+/*
  * Stage timing (instrumentation for profilers and benchmarks).  While set,
  * every blockffn_forward or blockffn_backward call of the calling thread
  * records events[0] on its stream before its first timed kernel and events[k]

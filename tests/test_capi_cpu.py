@@ -15,7 +15,7 @@ import tempfile
 import pytest
 
 from activation_sparse_moe_amd import _capi
-from activation_sparse_moe_amd._capi import BlockffnGrads, BlockffnLayer, BlockffnStats
+from activation_sparse_moe_amd._capi import BlockffnFffLayer, BlockffnGrads, BlockffnLayer, BlockffnStats
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "blockffn.h")
@@ -66,6 +66,9 @@ int main(void) {
   printf("%zu %zu\n", offsetof(blockffn_stats, active_pairs), offsetof(blockffn_stats, hist));
   printf("%zu %zu %zu\n", sizeof(blockffn_grads), offsetof(blockffn_grads, d_rms_scale),
          offsetof(blockffn_grads, d_w_out));
+  printf("%zu %zu %zu %zu %zu\n", sizeof(blockffn_fff_layer), offsetof(blockffn_fff_layer, activation),
+         offsetof(blockffn_fff_layer, layer_stride), offsetof(blockffn_fff_layer, b_node),
+         offsetof(blockffn_fff_layer, w_out));
   return 0;
 }
 """
@@ -83,6 +86,9 @@ int main(void) {
     assert b == [BlockffnStats.active_pairs.offset, BlockffnStats.hist.offset]
     c = [int(v) for v in lines[2].split()]
     assert c == [ctypes.sizeof(BlockffnGrads), BlockffnGrads.d_rms_scale.offset, BlockffnGrads.d_w_out.offset]
+    f = [int(v) for v in lines[3].split()]
+    assert f == [ctypes.sizeof(BlockffnFffLayer), BlockffnFffLayer.activation.offset,
+                 BlockffnFffLayer.layer_stride.offset, BlockffnFffLayer.b_node.offset, BlockffnFffLayer.w_out.offset]
 
 
 def test_version_and_status_strings(lib):
@@ -276,3 +282,47 @@ def test_cls_losses_validation(lib):
     assert call(z=P + 2) == _capi.ERR_ALIGN
     assert call(ws=P + 16) == _capi.ERR_ALIGN
     assert call(nb=8) == _capi.ERR_WORKSPACE
+
+
+def _fff_layer(**kw):
+    v = dict(d=2048, n_trees=64, depth=6, dtype=_capi.BF16, activation=0, reserved=0, layer_stride=0,
+             w_node=P, b_node=P, w_out=P)
+    v.update(kw)
+    return BlockffnFffLayer(**v)
+
+
+@cpu_only
+def test_fff_forward_validation(lib):
+    def call(layer=None, n_layers=1, x=P, T=4, mode=0, paths=None, pre=None, y=P):
+        ly = _fff_layer() if layer is None else layer
+        return lib.blockffn_fff_forward(ctypes.byref(ly), n_layers, x, T, mode, paths, pre, y, None)
+
+    assert lib.blockffn_fff_forward(None, 1, P, 4, 0, None, None, P, None) == _capi.ERR_NULL
+    assert call(_fff_layer(dtype=2)) == _capi.ERR_DTYPE
+    for d in (0, 256, 2048 + 64, 4608):       # bf16: multiples of 512 up to 4096
+        assert call(_fff_layer(d=d)) == _capi.ERR_SHAPE, d
+    assert call(_fff_layer(d=256, dtype=_capi.F32), T=0, x=None, y=None) == _capi.OK
+    assert call(_fff_layer(d=4096, dtype=_capi.F32)) == _capi.ERR_SHAPE   # f32: up to 2048
+    assert call(_fff_layer(n_trees=0)) == _capi.ERR_SHAPE
+    assert call(_fff_layer(depth=-1)) == _capi.ERR_SHAPE
+    assert call(_fff_layer(depth=16)) == _capi.ERR_SHAPE
+    assert call(_fff_layer(activation=2)) == _capi.ERR_SHAPE
+    assert call(_fff_layer(reserved=1)) == _capi.ERR_SHAPE
+    assert call(mode=2) == _capi.ERR_MODE
+    assert call(mode=1, paths=P) == _capi.ERR_MODE
+    assert call(mode=1, pre=P) == _capi.ERR_MODE
+    assert call(n_layers=0) == _capi.ERR_LAYERS
+    assert call(n_layers=2) == _capi.ERR_LAYERS                       # no stride
+    assert call(_fff_layer(layer_stride=1000), n_layers=2) == _capi.ERR_ALIGN
+    assert call(T=-1) == _capi.ERR_SHAPE
+    assert call(T=1 << 31) == _capi.ERR_SHAPE
+    assert call(_fff_layer(w_node=None)) == _capi.ERR_NULL
+    assert call(x=None) == _capi.ERR_NULL
+    assert call(y=None) == _capi.ERR_NULL
+    assert call(x=P + 8) == _capi.ERR_ALIGN
+    assert call(_fff_layer(w_out=P + 8)) == _capi.ERR_ALIGN
+    assert call(_fff_layer(b_node=P + 2)) == _capi.ERR_ALIGN
+    assert call(paths=P + 2) == _capi.ERR_ALIGN
+    # a valid call with no tokens enqueues nothing
+    assert call(T=0, x=None, y=None) == _capi.OK
+    assert call(T=0, x=None, y=None, mode=1) == _capi.OK

@@ -10,6 +10,10 @@ streaming its own copy of the layer so that no weight byte is served from a
 cache.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+With --workload fff_D6_P64_d2048 it measures the FFF tree layer instead (64
+trees of depth 6, d = 2048, bf16, 4096 independent tokens, each through its
+own copy of the layer): one step is one blockffn_fff_forward over the batch.
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "chunk-8 BlockFFN layer tokens/s + active-weight HBM GB/s (% of peak)"
+FFF_METRIC = "FFF tree layer tokens/s + visited-node HBM GB/s (% of peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 DEFAULT_WORKLOAD = "chunk8_d2048_E64"
@@ -62,6 +67,7 @@ KERNEL_SOURCES = {
     "expert_down": ("expert_mfma.hip", "lds_stream.h", "bffn_internal.h"),
     "grouped_up": ("grouped.hip", "grouped_kernels.h", "bffn_internal.h"),
     "grouped_down": ("grouped.hip", "grouped_kernels.h", "bffn_internal.h"),
+    "fff_walk": ("fff.hip", "bffn_internal.h"),
 }
 
 
@@ -457,6 +463,186 @@ def copy_calibration():
     torch.cuda.empty_cache()
 
 
+def fff_byte_model(cfg) -> dict:
+    """Algorithmic HBM bytes of one FFF forward over the batch: every visited
+    node's two rows, each token's x, and its fp32 output row."""
+    per_token_nodes = cfg.n_trees * (cfg.depth + 1) * cfg.node_bytes
+    io = cfg.d * cfg.elt_bytes + 4 * cfg.d
+    return {"per_token": per_token_nodes + io, "node_bytes_per_token": per_token_nodes,
+            "step": cfg.tokens * (per_token_nodes + io),
+            "dense_per_token": cfg.n_trees * cfg.nodes * cfg.node_bytes + io}
+
+
+def fff_cpu_baseline(cfg, layer, x_host, target_s: float):
+    """The FFF oracle as it stands, on the host cores, on a bounded sample of tokens."""
+    import oracle
+
+    def run(n):
+        t = time.perf_counter()
+        oracle.fff_forward(x_host[:n], layer.w_node, layer.b_node, layer.w_out, want_paths=False)
+        return time.perf_counter() - t
+
+    n = 64
+    dt = run(n)
+    if dt < target_s and n < cfg.tokens:
+        n = int(min(cfg.tokens, max(n + 1, n * target_s / max(dt, 1e-3))))
+        dt = run(n)
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {cfg.tokens} tokens of this workload, layer copy 0: the tree walk and output sum, "
+                      f"fp64 C oracle, {dt:.1f} s"}
+
+
+def torch_dense_fff_ms(dl, xd, n: int, reps: int) -> float:
+    """The dense feed-forward block the tree layer replaces (every node of
+    every tree, GELU, output projection), for n tokens each through its own
+    layer copy, as two batched vendor GEMMs (torch.bmm -> hipBLASLt)."""
+    import torch
+    t0 = dl.tensors(0)
+    rows = dl.n_trees * dl.nodes
+    es = t0["w_node"].element_size()
+    step = dl.stride // es
+    w_node = t0["w_node"].reshape(-1).as_strided((n, rows, dl.d), (step, dl.d, 1))
+    w_out = t0["w_out"].reshape(-1).as_strided((n, rows, dl.d), (step, dl.d, 1))
+    b = t0["b_node"].reshape(-1).as_strided((n, rows, 1), (dl.stride // 4, 1, 1)) if t0["b_node"] is not None \
+        else None
+    x = xd[:n].unsqueeze(2).contiguous()                                      # [n][d][1]
+
+    def fwd():
+        c = torch.bmm(w_node, x).float()                                      # [n][rows][1]
+        if b is not None:
+            c = c + b
+        a = torch.nn.functional.gelu(c).to(xd.dtype).reshape(n, 1, rows)
+        return torch.bmm(a, w_out)                                            # [n][1][d]
+
+    fwd()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fwd()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def fff_main(args, cfg) -> int:
+    import torch
+    from activation_sparse_moe_amd import binding as B
+    from activation_sparse_moe_amd._capi import BF16, F32
+    from workload import make_fff_workload
+
+    mode = args.mode or "sparse"
+    if mode not in ("sparse", "dense"):
+        print(f"FFF workloads take --mode sparse or dense, not {mode!r}", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+    layer, x = make_fff_workload(cfg)
+    dl = B.DeviceFffLayer.from_workload(layer, replicas=cfg.replicas)
+    xd = B.tokens_to_device(x, F32 if cfg.dtype == "f32" else BF16)
+    T = cfg.tokens
+    y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+    fwd = lambda: B.blockffn_fff_forward(dl, xd, mode=mode, y=y)  # noqa: E731
+
+    # eager launches, each bracketed by events on the launch stream: the
+    # kernel's average duration for the roofline
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for a, b in ev:
+        a.record()
+        fwd()
+        b.record()
+    t_end.record()
+    torch.cuda.synchronize()
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    eager_ms = t_start.elapsed_time(t_end) / args.steps
+    ms = eager_ms
+    if not args.eager:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fwd()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fwd()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+
+    bm = fff_byte_model(cfg)
+    step_bytes = bm["step"] if mode == "sparse" else T * bm["dense_per_token"]
+    achieved = step_bytes / (kernel_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": f"fff_walk ({mode})", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": profiled_traffic("fff_walk", cfg.name) if mode == "sparse" else None,
+                "algorithmic_bytes_per_launch": step_bytes, "avg_launch_ms": round(kernel_ms, 5),
+                "launches_per_step": 1}
+
+    dense = None
+    if args.dense_steps > 0 and mode == "sparse":
+        n = min(256, T, cfg.replicas)
+        yd = torch.empty((n, cfg.d), dtype=torch.float32, device="cuda")
+        B.blockffn_fff_forward(dl, xd[:n], mode="dense", y=yd)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.dense_steps):
+            B.blockffn_fff_forward(dl, xd[:n], mode="dense", y=yd)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / args.dense_steps
+        tms = torch_dense_fff_ms(dl, xd, n, args.dense_steps)
+        dense_tps, torch_tps = n / (dms * 1e-3), n / (tms * 1e-3)
+        dense = {"kind": "every node of every tree (the dense block of width P N) on the first "
+                         f"{n} tokens, each through its own layer copy",
+                 "same_kernel_tokens_per_s": round(dense_tps, 1),
+                 "same_kernel_gbs": round(n * bm["dense_per_token"] / (dms * 1e-3) / 1e9, 1),
+                 "torch_bmm_tokens_per_s": round(torch_tps, 1),
+                 "speedup_vs_same_kernel": round(T / (ms * 1e-3) / dense_tps, 2),
+                 "speedup_vs_torch_bmm": round(T / (ms * 1e-3) / torch_tps, 2),
+                 "ideal_byte_ratio": round(bm["dense_per_token"] / bm["per_token"], 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = fff_cpu_baseline(cfg, layer, x, args.cpu_seconds)
+    step_gbs = step_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": FFF_METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0, 1/d) node rows and N(0, I) tokens)",
+        "config": {"workload": cfg.name, "d": cfg.d, "n_trees": cfg.n_trees, "depth": cfg.depth,
+                   "nodes_per_tree": cfg.nodes, "tokens": T, "layer_copies": cfg.replicas, "mode": mode,
+                   "activation": "gelu_nodes"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "visited_node_gbs": round(step_gbs, 1),
+        "visited_node_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+        "sparsity": {"nodes_visited_per_token": cfg.n_trees * (cfg.depth + 1),
+                     "fraction_idle": round(1 - (cfg.depth + 1) / cfg.nodes, 4)},
+        "dense": dense,
+        "timing": {"steps": "eager launches" if args.eager else "HIP graph replay of the forward",
+                   "eager_ms_per_step": round(eager_ms, 5), "kernel_ms": round(kernel_ms, 5)},
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -466,8 +652,10 @@ def main(argv=None) -> int:
         return 2
 
     import torch
-    from workload import get_config
+    from workload import FFF_CONFIGS, get_config
 
+    if args.workload in FFF_CONFIGS:
+        return fff_main(args, FFF_CONFIGS[args.workload])
     cfg = get_config(args.workload)
     mode = args.mode or cfg.mode
     torch.cuda.set_device(0)

@@ -321,66 +321,83 @@ def masks_to_u64(token_masks: torch.Tensor) -> np.ndarray:
 class DeviceFffLayer:
     """`replicas` copies of one FFF tree layer in a single device buffer.
 
-    Copy r holds w_node [P][N][d], b_node [P][N] (fp32, optional) and
-    w_out [P][N][d] at replica 0's offsets plus r * stride bytes: the
-    stacked-layer convention of blockffn_fff_forward (token t uses copy
-    t % n_layers)."""
+    Copy r holds the node rows, then b_node [P][N] (fp32, optional), at
+    replica 0's offsets plus r * stride bytes: the stacked-layer convention
+    of blockffn_fff_forward (token t uses copy t % n_layers).  With
+    `interleave` (the default) each node's input and output rows sit next to
+    each other, [P][N][2][d], so a visited node is one contiguous read;
+    otherwise w_node [P][N][d] and w_out [P][N][d] are separate arrays."""
 
     def __init__(self, d: int, n_trees: int, depth: int, dtype: int, post: bool = False, device="cuda",
-                 replicas: int = 1, has_bias: bool = True):
+                 replicas: int = 1, has_bias: bool = True, interleave: bool = True):
         assert dtype in (F32, BF16)
         self.d, self.n_trees, self.depth, self.dtype = d, n_trees, depth, dtype
         self.post, self.replicas, self.device = bool(post), int(replicas), torch.device(device)
+        self.interleave = bool(interleave)
         self.nodes = (1 << (depth + 1)) - 1
-        rows = n_trees * self.nodes
-        es = _elem(dtype)
-        sizes = [("w_node", rows * d * es), ("b_node", 4 * rows if has_bias else 0), ("w_out", rows * d * es)]
-        self._off = {}
-        off = 0
-        for name, nbytes in sizes:
-            self._off[name] = (off, nbytes) if nbytes else None
-            off = _round(off + nbytes)
+        self.rows = n_trees * self.nodes
+        self.row_bytes = d * _elem(dtype)
+        self.node_stride = 2 * self.row_bytes if self.interleave else self.row_bytes
+        nb = self.rows * self.row_bytes
+        if self.interleave:
+            self._w_node_off, self._w_out_off = 0, self.row_bytes
+            off = _round(2 * nb)
+        else:
+            self._w_node_off, self._w_out_off = 0, _round(nb)
+            off = _round(self._w_out_off + nb)
+        self._b_off = off if has_bias else None
+        off = _round(off + (4 * self.rows if has_bias else 0))
         self.stride = _round(off, 4096)
         self.buffer = torch.empty(self.stride * self.replicas, dtype=torch.uint8, device=self.device)
         self._desc = None
 
-    def tensors(self, r: int = 0) -> dict:
+    def rows_view(self, which: str, r: int = 0, n_copies: int = 1) -> torch.Tensor:
+        """[n_copies][P N][d] view of the input ("w_node") or output ("w_out") rows of copies r.."""
         td = _torch_dtype(self.dtype)
+        es = _elem(self.dtype)
+        flat = self.buffer.view(td)
+        off = r * self.stride + (self._w_node_off if which == "w_node" else self._w_out_off)
+        return flat.as_strided((n_copies, self.rows, self.d), (self.stride // es, self.node_stride // es, 1), off // es)
+
+    def tensors(self, r: int = 0) -> dict:
         P, N, d = self.n_trees, self.nodes, self.d
-
-        def view(name, shape, dt):
-            slot = self._off[name]
-            if slot is None:
-                return None
-            off, nbytes = slot
-            base = r * self.stride + off
-            return self.buffer[base:base + nbytes].view(dt).view(*shape)
-
-        return dict(w_node=view("w_node", (P, N, d), td), b_node=view("b_node", (P, N), torch.float32),
-                    w_out=view("w_out", (P, N, d), td))
+        b = None
+        if self._b_off is not None:
+            base = r * self.stride + self._b_off
+            b = self.buffer[base:base + 4 * self.rows].view(torch.float32).view(P, N)
+        return dict(w_node=self.rows_view("w_node", r)[0].view(P, N, d) if not self.interleave
+                    else self.rows_view("w_node", r)[0].unflatten(0, (P, N)),
+                    b_node=b,
+                    w_out=self.rows_view("w_out", r)[0].view(P, N, d) if not self.interleave
+                    else self.rows_view("w_out", r)[0].unflatten(0, (P, N)))
 
     @classmethod
-    def from_workload(cls, layer, post: bool = False, device="cuda", replicas: int = 1) -> "DeviceFffLayer":
+    def from_workload(cls, layer, post: bool = False, device="cuda", replicas: int = 1,
+                      interleave: bool = True) -> "DeviceFffLayer":
         dtype = F32 if layer.dtype == "f32" else BF16
         self = cls(layer.d, layer.n_trees, layer.depth, dtype, post, device, replicas,
-                   has_bias=layer.b_node is not None)
-        t = self.tensors(0)
-        t["w_node"].copy_(_to_device(layer.w_node, dtype, self.device))
-        t["w_out"].copy_(_to_device(layer.w_out, dtype, self.device))
-        if layer.b_node is not None:
-            t["b_node"].copy_(torch.as_tensor(np.asarray(layer.b_node, np.float32)).to(self.device))
+                   has_bias=layer.b_node is not None, interleave=interleave)
+        self.fill(0, layer)
         for r in range(1, self.replicas):
             self.buffer[r * self.stride:(r + 1) * self.stride].copy_(self.buffer[:self.stride])
         return self
 
+    def fill(self, r: int, layer) -> None:
+        """Write a host layer (workload.FffLayer) into copy r."""
+        t = self.tensors(r)
+        t["w_node"].copy_(_to_device(layer.w_node, self.dtype, self.device))
+        t["w_out"].copy_(_to_device(layer.w_out, self.dtype, self.device))
+        if layer.b_node is not None:
+            t["b_node"].copy_(torch.as_tensor(np.asarray(layer.b_node, np.float32)).to(self.device))
+
     def descriptor(self) -> BlockffnFffLayer:
         if self._desc is None:
-            t = self.tensors(0)
+            base = self.buffer.data_ptr()
             self._desc = BlockffnFffLayer(self.d, self.n_trees, self.depth, self.dtype,
-                                          _capi.FFF_GELU_OUTPUT if self.post else _capi.FFF_GELU_NODES, 0,
-                                          self.stride, t["w_node"].data_ptr(),
-                                          t["b_node"].data_ptr() if t["b_node"] is not None else None,
-                                          t["w_out"].data_ptr())
+                                          _capi.FFF_GELU_OUTPUT if self.post else _capi.FFF_GELU_NODES,
+                                          self.node_stride, self.stride, base + self._w_node_off,
+                                          base + self._b_off if self._b_off is not None else None,
+                                          base + self._w_out_off)
         return self._desc
 
 

@@ -376,7 +376,10 @@ BFFN_EXPORT int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_
   if (ly.depth < 0 || ly.depth > 15) return fail(BLOCKFFN_ERR_SHAPE, "depth %d outside [0, 15]", ly.depth);
   if (ly.activation != BLOCKFFN_FFF_GELU_NODES && ly.activation != BLOCKFFN_FFF_GELU_OUTPUT)
     return fail(BLOCKFFN_ERR_SHAPE, "unknown activation placement %d", ly.activation);
-  if (ly.reserved != 0) return fail(BLOCKFFN_ERR_SHAPE, "reserved field must be 0");
+  const int64_t row_bytes = (int64_t)ly.d * (ly.dtype == BLOCKFFN_BF16 ? 2 : 4);
+  if (ly.node_stride != 0 && (ly.node_stride < row_bytes || ly.node_stride % 16 != 0))
+    return fail(BLOCKFFN_ERR_SHAPE, "node_stride %d must be 0 or a multiple of 16 of at least %lld", ly.node_stride,
+                (long long)row_bytes);
   if (mode != BLOCKFFN_FFF_SPARSE && mode != BLOCKFFN_FFF_DENSE) return fail(BLOCKFFN_ERR_MODE, "unknown mode %d", mode);
   if (mode == BLOCKFFN_FFF_DENSE && (paths || node_preact))
     return fail(BLOCKFFN_ERR_MODE, "paths and node_preact must be NULL in dense mode");

@@ -497,12 +497,10 @@ def torch_dense_fff_ms(dl, xd, n: int, reps: int) -> float:
     every tree, GELU, output projection), for n tokens each through its own
     layer copy, as two batched vendor GEMMs (torch.bmm -> hipBLASLt)."""
     import torch
+    rows = dl.rows
+    w_node = dl.rows_view("w_node", 0, n)                                    # [n][rows][d], row stride node_stride
+    w_out = dl.rows_view("w_out", 0, n)
     t0 = dl.tensors(0)
-    rows = dl.n_trees * dl.nodes
-    es = t0["w_node"].element_size()
-    step = dl.stride // es
-    w_node = t0["w_node"].reshape(-1).as_strided((n, rows, dl.d), (step, dl.d, 1))
-    w_out = t0["w_out"].reshape(-1).as_strided((n, rows, dl.d), (step, dl.d, 1))
     b = t0["b_node"].reshape(-1).as_strided((n, rows, 1), (dl.stride // 4, 1, 1)) if t0["b_node"] is not None \
         else None
     x = xd[:n].unsqueeze(2).contiguous()                                      # [n][d][1]

@@ -298,6 +298,14 @@ size_t blockffn_cls_losses_workspace_size(int64_t n_tokens, int32_t chunk_len);
  * with the exact GELU(c) = c Phi(c).  Sums are fp32; the dot products are
  * reduced in a fixed order, so results are bit-reproducible.
  *
+ * Node rows: node n of tree p has its input row at
+ * (char*)w_node + (p N + n) * node_stride and its output row at
+ * (char*)w_out + (p N + n) * node_stride.  node_stride = 0 means separate
+ * dense arrays (d * element size).  A node's two rows may be interleaved in
+ * one array, [P][N][2][d] with w_out = w_node + d * element size and
+ * node_stride = 2 d * element size: a visited node is then one contiguous
+ * read, which streams faster.
+ *
  * With n_layers > 1, layer l's arrays live at (char*)ptr + l * layer_stride
  * for every pointer (NULL stays NULL) and token t uses layer t % n_layers.
  */
@@ -313,11 +321,12 @@ typedef struct blockffn_fff_layer {
   int32_t depth;        /* D, 0 .. 15 */
   int32_t dtype;        /* BLOCKFFN_F32 or BLOCKFFN_BF16, for x, w_node and w_out */
   int32_t activation;   /* BLOCKFFN_FFF_GELU_NODES or BLOCKFFN_FFF_GELU_OUTPUT */
-  int32_t reserved;     /* must be 0 */
+  int32_t node_stride;  /* bytes between consecutive nodes' rows: 0 (= d * element size) or a
+                           multiple of 16 of at least d * element size */
   int64_t layer_stride; /* bytes between consecutive layers (multiple of 256) */
-  const void* w_node;   /* [P][N][d], dtype, 16-byte aligned */
+  const void* w_node;   /* input rows, dtype, 16-byte aligned */
   const float* b_node;  /* [P][N] fp32, or NULL for no bias */
-  const void* w_out;    /* [P][N][d], dtype, 16-byte aligned */
+  const void* w_out;    /* output rows, dtype, 16-byte aligned */
 } blockffn_fff_layer;
 
 /*

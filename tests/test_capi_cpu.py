@@ -285,7 +285,7 @@ def test_cls_losses_validation(lib):
 
 
 def _fff_layer(**kw):
-    v = dict(d=2048, n_trees=64, depth=6, dtype=_capi.BF16, activation=0, reserved=0, layer_stride=0,
+    v = dict(d=2048, n_trees=64, depth=6, dtype=_capi.BF16, activation=0, node_stride=0, layer_stride=0,
              w_node=P, b_node=P, w_out=P)
     v.update(kw)
     return BlockffnFffLayer(**v)
@@ -307,7 +307,9 @@ def test_fff_forward_validation(lib):
     assert call(_fff_layer(depth=-1)) == _capi.ERR_SHAPE
     assert call(_fff_layer(depth=16)) == _capi.ERR_SHAPE
     assert call(_fff_layer(activation=2)) == _capi.ERR_SHAPE
-    assert call(_fff_layer(reserved=1)) == _capi.ERR_SHAPE
+    assert call(_fff_layer(node_stride=2048)) == _capi.ERR_SHAPE         # shorter than a bf16 row of 2048
+    assert call(_fff_layer(node_stride=4096 + 8)) == _capi.ERR_SHAPE     # not a multiple of 16
+    assert call(_fff_layer(node_stride=8192), T=0, x=None, y=None) == _capi.OK   # interleaved rows
     assert call(mode=2) == _capi.ERR_MODE
     assert call(mode=1, paths=P) == _capi.ERR_MODE
     assert call(mode=1, pre=P) == _capi.ERR_MODE

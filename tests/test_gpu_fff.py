@@ -33,17 +33,11 @@ PRE_TOL = 1e-4
 Y_TOL = 1e-5
 
 
-def _dev_layer(layers, post=False):
+def _dev_layer(layers, post=False, interleave=True):
     """One device layer stack from a list of host layers (copy r = layers[r])."""
-    l0 = layers[0]
-    dl = B.DeviceFffLayer.from_workload(l0, post=post, replicas=len(layers))
-    dt = F32 if l0.dtype == "f32" else BF16
+    dl = B.DeviceFffLayer.from_workload(layers[0], post=post, replicas=len(layers), interleave=interleave)
     for r, lr in enumerate(layers[1:], start=1):
-        t = dl.tensors(r)
-        t["w_node"].copy_(B._to_device(lr.w_node, dt, "cuda"))
-        t["w_out"].copy_(B._to_device(lr.w_out, dt, "cuda"))
-        if lr.b_node is not None:
-            t["b_node"].copy_(torch.as_tensor(lr.b_node).cuda())
+        dl.fill(r, lr)
     return dl
 
 
@@ -95,13 +89,13 @@ def _compare(paths_g, pre_g, y_g, paths_o, pre_o, y_o, where):
     return len(flipped)
 
 
-def _case(d, P, D, dtype, T, seed, post=False, dense=False, n_layers=1, bias=True):
+def _case(d, P, D, dtype, T, seed, post=False, dense=False, n_layers=1, bias=True, interleave=True):
     rng = np.random.default_rng(seed)
     layers = [make_fff_layer(d, P, D, dtype, rng, bias=bias) for _ in range(n_layers)]
     x = make_fff_tokens(d, T, dtype, rng)
-    where = f"d={d} P={P} D={D} {dtype} T={T} post={post} dense={dense} layers={n_layers}"
+    where = f"d={d} P={P} D={D} {dtype} T={T} post={post} dense={dense} layers={n_layers} interleave={interleave}"
     say(f"[gpu] fff {where}")
-    dl = _dev_layer(layers, post)
+    dl = _dev_layer(layers, post, interleave)
     xd = B.tokens_to_device(x, F32 if dtype == "f32" else BF16)
     y, paths, pre = B.blockffn_fff_forward(dl, xd, mode="dense" if dense else "sparse", want_paths=not dense)
     torch.cuda.synchronize()
@@ -138,6 +132,12 @@ def test_fff_dense_matches_oracle(d, P, D, dtype, T, post):
 
 def test_fff_without_bias():
     _case(512, 6, 4, "bf16", 11, 961, bias=False)
+
+
+@pytest.mark.parametrize("dense", [False, True])
+def test_fff_separate_row_arrays(dense):
+    # node_stride 0: w_node and w_out as two dense [P][N][d] arrays
+    _case(1024, 7, 3, "bf16", 13, 965, dense=dense, n_layers=2, interleave=False)
 
 
 def test_fff_zero_tokens_and_determinism():

@@ -30,7 +30,7 @@ FFF_SPARSE, FFF_DENSE = 0, 1
 # Every symbol include/blockffn.h declares.
 EXPORTS = ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats",
            "blockffn_backward", "blockffn_backward_workspace_size",
-           "blockffn_cls_losses", "blockffn_cls_losses_workspace_size", "blockffn_fff_forward",
+           "blockffn_cls_losses", "blockffn_cls_losses_workspace_size", "blockffn_fff_forward", "blockffn_fff_workspace_size", "blockffn_read_probe",
            "blockffn_set_stage_events", "blockffn_workspace_size", "blockffn_status_string",
            "blockffn_last_error", "blockffn_version")
 
@@ -96,13 +96,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.blockffn_backward.argtypes = [lp, vp, i64, vp, vp, vp, vp, sz, vp, ctypes.POINTER(BlockffnGrads), vp]
         flt = ctypes.c_float
         lib.blockffn_cls_losses.argtypes = [i32, vp, i64, i32, flt, flt, flt, vp, sz, vp, vp, vp]
-        lib.blockffn_fff_forward.argtypes = [ctypes.POINTER(BlockffnFffLayer), i32, vp, i64, i32, vp, vp, vp, vp]
+        lib.blockffn_fff_forward.argtypes = [ctypes.POINTER(BlockffnFffLayer), i32, vp, i64, i32, i32, vp, vp, vp, sz,
+                                             vp, vp]
+        lib.blockffn_fff_workspace_size.argtypes = [ctypes.POINTER(BlockffnFffLayer), i64, i32]
+        lib.blockffn_fff_workspace_size.restype = sz
+        lib.blockffn_read_probe.argtypes = [vp, sz, i32, vp, vp]
         lib.blockffn_cls_losses_workspace_size.argtypes = [i64, i32]
         lib.blockffn_cls_losses_workspace_size.restype = sz
         lib.blockffn_backward_workspace_size.argtypes = [lp, i64]
         lib.blockffn_backward_workspace_size.restype = sz
         for f in ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward",
-                  "blockffn_sparsity_stats", "blockffn_backward", "blockffn_cls_losses", "blockffn_fff_forward"):
+                  "blockffn_sparsity_stats", "blockffn_backward", "blockffn_cls_losses", "blockffn_fff_forward",
+                  "blockffn_read_probe"):
             getattr(lib, f).restype = ctypes.c_int
         lib.blockffn_set_stage_events.argtypes = [vp, i32]
         lib.blockffn_set_stage_events.restype = ctypes.c_int

@@ -139,6 +139,19 @@ class DeviceLayer:
     def mask_words(self) -> int:
         return (self.n_experts + 63) // 64
 
+    def single_copy(self, r: int) -> "DeviceLayer":
+        """A view of copy r alone (n_layers 1), sharing this buffer: for calls that
+        should read one particular copy."""
+        import copy as _copy
+        v = _copy.copy(self)
+        base = self.descriptor()
+        off = r * self.stride
+        v._desc = BlockffnLayer(self.d, self.n_experts, self.d_expert, self.dtype, self.rms_eps, 0, self.stride,
+                                base.w_router + off, base.b_router + off if base.b_router else None,
+                                base.rms_scale + off if base.rms_scale else None, base.w_in + off, base.w_out + off)
+        v.replicas = 1
+        return v
+
 
 def tokens_to_device(x, dtype: int, device="cuda") -> torch.Tensor:
     return _to_device(x, dtype, device)
@@ -349,6 +362,7 @@ class DeviceFffLayer:
         off = _round(off + (4 * self.rows if has_bias else 0))
         self.stride = _round(off, 4096)
         self.buffer = torch.empty(self.stride * self.replicas, dtype=torch.uint8, device=self.device)
+        self._base = 0  # byte offset of copy 0 in the buffer (non-zero for single_copy views)
         self._desc = None
 
     def rows_view(self, which: str, r: int = 0, n_copies: int = 1) -> torch.Tensor:
@@ -356,14 +370,14 @@ class DeviceFffLayer:
         td = _torch_dtype(self.dtype)
         es = _elem(self.dtype)
         flat = self.buffer.view(td)
-        off = r * self.stride + (self._w_node_off if which == "w_node" else self._w_out_off)
+        off = self._base + r * self.stride + (self._w_node_off if which == "w_node" else self._w_out_off)
         return flat.as_strided((n_copies, self.rows, self.d), (self.stride // es, self.node_stride // es, 1), off // es)
 
     def tensors(self, r: int = 0) -> dict:
         P, N, d = self.n_trees, self.nodes, self.d
         b = None
         if self._b_off is not None:
-            base = r * self.stride + self._b_off
+            base = self._base + r * self.stride + self._b_off
             b = self.buffer[base:base + 4 * self.rows].view(torch.float32).view(P, N)
         return dict(w_node=self.rows_view("w_node", r)[0].view(P, N, d) if not self.interleave
                     else self.rows_view("w_node", r)[0].unflatten(0, (P, N)),
@@ -390,9 +404,18 @@ class DeviceFffLayer:
         if layer.b_node is not None:
             t["b_node"].copy_(torch.as_tensor(np.asarray(layer.b_node, np.float32)).to(self.device))
 
+    def single_copy(self, r: int) -> "DeviceFffLayer":
+        """A view of copy r alone (n_layers 1), sharing this buffer."""
+        import copy as _copy
+        v = _copy.copy(self)
+        v._desc = None
+        v._base = self._base + r * self.stride
+        v.replicas = 1
+        return v
+
     def descriptor(self) -> BlockffnFffLayer:
         if self._desc is None:
-            base = self.buffer.data_ptr()
+            base = self.buffer.data_ptr() + self._base
             self._desc = BlockffnFffLayer(self.d, self.n_trees, self.depth, self.dtype,
                                           _capi.FFF_GELU_OUTPUT if self.post else _capi.FFF_GELU_NODES,
                                           self.node_stride, self.stride, base + self._w_node_off,
@@ -401,10 +424,21 @@ class DeviceFffLayer:
         return self._desc
 
 
+def blockffn_fff_workspace_size(layer: DeviceFffLayer, n_tokens: int, split: int = 0) -> int:
+    return int(load().blockffn_fff_workspace_size(ctypes.byref(layer.descriptor()), n_tokens, int(split)))
+
+
+def alloc_fff_workspace(layer: DeviceFffLayer, n_tokens: int, split: int = 0) -> Optional[torch.Tensor]:
+    nbytes = blockffn_fff_workspace_size(layer, n_tokens, split)
+    return torch.empty(nbytes, dtype=torch.uint8, device=layer.device) if nbytes else None
+
+
 def blockffn_fff_forward(layer: DeviceFffLayer, x: torch.Tensor, mode: str = "sparse", want_paths: bool = False,
-                         y: Optional[torch.Tensor] = None, paths: Optional[torch.Tensor] = None,
-                         node_preact: Optional[torch.Tensor] = None, n_layers: Optional[int] = None, stream=None):
-    """FFF tree layer -> (y [T][d] f32, paths [T][P][D+1] i32 or None, node_preact [T][P][D+1] f32 or None)."""
+                         split: int = 0, workspace: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                         paths: Optional[torch.Tensor] = None, node_preact: Optional[torch.Tensor] = None,
+                         n_layers: Optional[int] = None, stream=None):
+    """FFF tree layer -> (y [T][d] f32, paths [T][P][D+1] i32 or None, node_preact [T][P][D+1] f32 or None).
+    A workspace is allocated here when the call needs one and none is given."""
     T = x.shape[0]
     if y is None:
         y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device)
@@ -412,8 +446,18 @@ def blockffn_fff_forward(layer: DeviceFffLayer, x: torch.Tensor, mode: str = "sp
         paths = torch.empty((T, layer.n_trees, layer.depth + 1), dtype=torch.int32, device=x.device)
     if want_paths and node_preact is None:
         node_preact = torch.empty((T, layer.n_trees, layer.depth + 1), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_fff_workspace(layer, T, split)
     m = {"sparse": _capi.FFF_SPARSE, "dense": _capi.FFF_DENSE}[mode]
     nl = layer.replicas if n_layers is None else n_layers
-    check(load().blockffn_fff_forward(ctypes.byref(layer.descriptor()), nl, _ptr(x), T, m, _ptr(paths),
-                                      _ptr(node_preact), _ptr(y), _stream(stream)), "blockffn_fff_forward")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().blockffn_fff_forward(ctypes.byref(layer.descriptor()), nl, _ptr(x), T, m, int(split), _ptr(paths),
+                                      _ptr(node_preact), _ptr(workspace), ws_bytes, _ptr(y), _stream(stream)),
+          "blockffn_fff_forward")
     return y, paths, node_preact
+
+
+def blockffn_read_probe(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 0, stream=None) -> None:
+    """One streaming read of `buf` (the HBM read-ceiling probe)."""
+    check(load().blockffn_read_probe(_ptr(buf), buf.numel() * buf.element_size(), int(blocks), _ptr(sink),
+                                     _stream(stream)), "blockffn_read_probe")

@@ -363,9 +363,9 @@ BFFN_EXPORT int blockffn_cls_losses(int32_t n_experts, const float* preact, int6
                     "cls-losses launch");
 }
 
-BFFN_EXPORT int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_layers, const void* x,
-                                     int64_t n_tokens, int32_t mode, int32_t* paths, float* node_preact, float* y,
-                                     hipStream_t stream) {
+namespace {
+
+int check_fff_layer(const blockffn_fff_layer* layer, int32_t n_layers) {
   if (!layer) return fail(BLOCKFFN_ERR_NULL, "layer descriptor is NULL");
   const blockffn_fff_layer& ly = *layer;
   if (ly.dtype != BLOCKFFN_F32 && ly.dtype != BLOCKFFN_BF16) return fail(BLOCKFFN_ERR_DTYPE, "unknown dtype %d", ly.dtype);
@@ -380,25 +380,67 @@ BFFN_EXPORT int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_
   if (ly.node_stride != 0 && (ly.node_stride < row_bytes || ly.node_stride % 16 != 0))
     return fail(BLOCKFFN_ERR_SHAPE, "node_stride %d must be 0 or a multiple of 16 of at least %lld", ly.node_stride,
                 (long long)row_bytes);
-  if (mode != BLOCKFFN_FFF_SPARSE && mode != BLOCKFFN_FFF_DENSE) return fail(BLOCKFFN_ERR_MODE, "unknown mode %d", mode);
-  if (mode == BLOCKFFN_FFF_DENSE && (paths || node_preact))
-    return fail(BLOCKFFN_ERR_MODE, "paths and node_preact must be NULL in dense mode");
   if (n_layers < 1) return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d < 1", n_layers);
   if (n_layers > 1 && ly.layer_stride <= 0)
     return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d > 1 needs a positive layer_stride", n_layers);
   if (n_layers > 1 && ly.layer_stride % 256 != 0)
     return fail(BLOCKFFN_ERR_ALIGN, "layer_stride %lld is not a multiple of 256", (long long)ly.layer_stride);
+  if (!ly.w_node || !ly.w_out) return fail(BLOCKFFN_ERR_NULL, "w_node and w_out must be non-NULL");
+  if (!aligned(ly.w_node, 16) || !aligned(ly.w_out, 16))
+    return fail(BLOCKFFN_ERR_ALIGN, "w_node and w_out must be 16-byte aligned");
+  if (!aligned(ly.b_node, 4)) return fail(BLOCKFFN_ERR_ALIGN, "b_node must be 4-byte aligned");
+  return BLOCKFFN_OK;
+}
+
+int check_fff_split(const blockffn_fff_layer& ly, int64_t n_tokens, int32_t split) {
   if (n_tokens < 0 || n_tokens > INT32_MAX)
     return fail(BLOCKFFN_ERR_SHAPE, "n_tokens %lld outside [0, 2^31)", (long long)n_tokens);
-  if (!ly.w_node || !ly.w_out) return fail(BLOCKFFN_ERR_NULL, "w_node and w_out must be non-NULL");
+  const int gmax = bffn::fff_max_split(ly.n_trees);
+  if (split < 0 || split > gmax)
+    return fail(BLOCKFFN_ERR_SHAPE, "split %d outside [0, %d] (0 = automatic)", split, gmax);
+  if (n_tokens * bffn::fff_split(ly.n_trees, n_tokens, split) > INT32_MAX)
+    return fail(BLOCKFFN_ERR_SHAPE, "n_tokens x blocks per token must stay below 2^31");
+  return BLOCKFFN_OK;
+}
+
+}  // namespace
+
+BFFN_EXPORT size_t blockffn_fff_workspace_size(const blockffn_fff_layer* layer, int64_t n_tokens, int32_t split) {
+  if (check_fff_layer(layer, 1) != BLOCKFFN_OK || check_fff_split(*layer, n_tokens, split) != BLOCKFFN_OK) return 0;
+  return bffn::fff_workspace_bytes(layer->d, layer->n_trees, n_tokens, split);
+}
+
+BFFN_EXPORT int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_layers, const void* x,
+                                     int64_t n_tokens, int32_t mode, int32_t split, int32_t* paths,
+                                     float* node_preact, void* workspace, size_t workspace_bytes, float* y,
+                                     hipStream_t stream) {
+  if (int r = check_fff_layer(layer, n_layers)) return r;
+  const blockffn_fff_layer& ly = *layer;
+  if (mode != BLOCKFFN_FFF_SPARSE && mode != BLOCKFFN_FFF_DENSE) return fail(BLOCKFFN_ERR_MODE, "unknown mode %d", mode);
+  if (mode == BLOCKFFN_FFF_DENSE && (paths || node_preact))
+    return fail(BLOCKFFN_ERR_MODE, "paths and node_preact must be NULL in dense mode");
+  if (int r = check_fff_split(ly, n_tokens, split)) return r;
   if (n_tokens > 0 && (!x || !y)) return fail(BLOCKFFN_ERR_NULL, "x and y must be non-NULL");
-  if (!aligned(ly.w_node, 16) || !aligned(ly.w_out, 16) || !aligned(x, 16) || !aligned(y, 16))
-    return fail(BLOCKFFN_ERR_ALIGN, "w_node, w_out, x and y must be 16-byte aligned");
-  if (!aligned(ly.b_node, 4) || !aligned(paths, 4) || !aligned(node_preact, 4))
-    return fail(BLOCKFFN_ERR_ALIGN, "b_node, paths and node_preact must be 4-byte aligned");
-  return hip_status(bffn::launch_fff_forward(ly, n_layers, x, n_tokens, mode == BLOCKFFN_FFF_DENSE, paths,
-                                             node_preact, y, stream),
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 16))
+    return fail(BLOCKFFN_ERR_ALIGN, "x, y and workspace must be 16-byte aligned");
+  if (!aligned(paths, 4) || !aligned(node_preact, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "paths and node_preact must be 4-byte aligned");
+  const size_t need = bffn::fff_workspace_bytes(ly.d, ly.n_trees, n_tokens, split);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
+  return hip_status(bffn::launch_fff_forward(ly, n_layers, x, n_tokens, mode == BLOCKFFN_FFF_DENSE, split, paths,
+                                             node_preact, workspace, y, stream),
                     "fff forward launch");
+}
+
+BFFN_EXPORT int blockffn_read_probe(const void* buf, size_t bytes, int32_t blocks, uint32_t* sink,
+                                    hipStream_t stream) {
+  if (!sink || (bytes > 0 && !buf)) return fail(BLOCKFFN_ERR_NULL, "buf and sink must be non-NULL");
+  if (!aligned(buf, 16) || bytes % 16 != 0 || !aligned(sink, 4))
+    return fail(BLOCKFFN_ERR_ALIGN, "buf must be 16-byte aligned, bytes a multiple of 16, sink 4-byte aligned");
+  if (blocks < 0) return fail(BLOCKFFN_ERR_SHAPE, "blocks %d < 0", blocks);
+  if (bytes == 0) return BLOCKFFN_OK;
+  return hip_status(bffn::launch_read_probe(buf, bytes, blocks, sink, stream), "read probe launch");
 }
 
 BFFN_EXPORT int blockffn_set_stage_events(hipEvent_t* events, int32_t n_events) {

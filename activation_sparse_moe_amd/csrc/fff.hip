@@ -29,6 +29,12 @@
 //    the turn is wave-uniform and the node index stays scalar.
 //  * The waves' partial outputs are added in LDS in a fixed order (wave 0,
 //    then 1, 2, 3), so the output is deterministic.
+//  * Few tokens cannot fill the GPU one block each, and a lone token would
+//    walk its trees a pair at a time.  A token's trees are then split into
+//    G groups, one block each; the blocks write fp32 partial outputs to a
+//    workspace and a second kernel adds the G partials in group order (and
+//    applies the post-aggregation GELU).  G is chosen from the token count
+//    alone, so a given call is reproducible.
 #include "bffn_internal.h"
 
 namespace bffn {
@@ -50,6 +56,9 @@ struct FffArgs {
   float* y;
   int32_t* paths;
   float* preact;
+  int32_t G;          // blocks per token
+  int32_t per_group;  // trees per block
+  float* partial;     // [T][G][d] when G > 1
 };
 
 // exact GELU, c Phi(c)
@@ -148,7 +157,8 @@ __global__ __launch_bounds__(kFffWaves * kWave) void fff_kernel(FffArgs a) {
   using W = Walker<NCH, BF16>;
   extern __shared__ __attribute__((aligned(16))) float part[];  // [kFffWaves - 1][d]
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t t = blockIdx.x;
+  const int64_t t = (int64_t)(blockIdx.x / (unsigned)a.G);
+  const int g = (int)(blockIdx.x % (unsigned)a.G);
   const int64_t layer = a.n_layers > 1 ? t % a.n_layers : 0;
   W wk{a,
        a.w_node + layer * a.stride,
@@ -166,9 +176,11 @@ __global__ __launch_bounds__(kFffWaves * kWave) void fff_kernel(FffArgs a) {
 #pragma unroll
   for (int e = 0; e < W::kEL; ++e) wk.acc[e] = 0.f;
 
-  int p = w;
-  for (; p + kFffWaves * (kTreePar - 1) < a.P; p += kFffWaves * kTreePar) wk.template walk<kTreePar>(p);
-  for (; p < a.P; p += kFffWaves) wk.template walk<1>(p);
+  const int p_lo = g * a.per_group;
+  const int p_hi = p_lo + a.per_group < a.P ? p_lo + a.per_group : a.P;
+  int p = p_lo + w;
+  for (; p + kFffWaves * (kTreePar - 1) < p_hi; p += kFffWaves * kTreePar) wk.template walk<kTreePar>(p);
+  for (; p < p_hi; p += kFffWaves) wk.template walk<1>(p);
 
   // fixed-order sum of the four waves' partial outputs
   const int d = NCH * 1024 / (BF16 ? 2 : 4);
@@ -184,7 +196,8 @@ __global__ __launch_bounds__(kFffWaves * kWave) void fff_kernel(FffArgs a) {
   }
   __syncthreads();
   if (w == 0) {
-    float* yr = a.y + t * d;
+    const bool whole = a.G == 1;  // else a partial output for the combine
+    float* yr = whole ? a.y + t * d : a.partial + ((int64_t)t * a.G + g) * d;
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
 #pragma unroll
@@ -194,17 +207,36 @@ __global__ __launch_bounds__(kFffWaves * kWave) void fff_kernel(FffArgs a) {
                 wk.acc[j * W::kEP + i + 3]};
 #pragma unroll
         for (int r = 0; r < kFffWaves - 1; ++r) v += *reinterpret_cast<const f32x4*>(part + r * d + e);
-        if (a.post) v = f32x4{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
+        if (whole && a.post) v = f32x4{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
         *reinterpret_cast<f32x4*>(yr + e) = v;
       }
   }
+}
+
+// y[t] = sum over g = 0..G-1, in order, of partial[t][g] (then GELU in the
+// post variant).  Block b covers 1024 elements of one token's row.
+__global__ __launch_bounds__(kBlock) void fff_combine_kernel(const float* __restrict__ partial, int G, int d,
+                                                             int chunks, int post, float* __restrict__ y) {
+  const int64_t t = blockIdx.x / (unsigned)chunks;
+  const int e = (int)(blockIdx.x % (unsigned)chunks) * 1024 + threadIdx.x * 4;
+  if (e >= d) return;
+  const float* src = partial + t * G * (int64_t)d + e;
+  f32x4 v = *reinterpret_cast<const f32x4*>(src);
+  for (int g = 1; g < G; ++g) v += *reinterpret_cast<const f32x4*>(src + (int64_t)g * d);
+  if (post) v = f32x4{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
+  *reinterpret_cast<f32x4*>(y + t * d + e) = v;
 }
 
 template <int NCH, bool BF16>
 hipError_t launch_nch(const FffArgs& a, int64_t n_tokens, hipStream_t s) {
   const int d = NCH * 1024 / (BF16 ? 2 : 4);
   const size_t lds = sizeof(float) * (kFffWaves - 1) * d;
-  fff_kernel<NCH, BF16><<<dim3((unsigned)n_tokens), dim3(kFffWaves * kWave), lds, s>>>(a);
+  fff_kernel<NCH, BF16><<<dim3((unsigned)(n_tokens * a.G)), dim3(kFffWaves * kWave), lds, s>>>(a);
+  if (a.G > 1) {
+    const int chunks = (d + 1023) / 1024;
+    fff_combine_kernel<<<dim3((unsigned)(n_tokens * chunks)), dim3(kBlock), 0, s>>>(a.partial, a.G, d, chunks,
+                                                                                 a.post, a.y);
+  }
   return hipGetLastError();
 }
 
@@ -225,13 +257,28 @@ hipError_t launch_dtype(const FffArgs& a, int nch, int64_t n_tokens, hipStream_t
 
 }  // namespace
 
+int fff_max_split(int n_trees) { return (n_trees + kFffWaves - 1) / kFffWaves; }
+
+int fff_split(int n_trees, int64_t n_tokens, int requested) {
+  const int gmax = fff_max_split(n_trees);
+  if (requested > 0) return requested < gmax ? requested : gmax;
+  if (n_tokens <= 0 || n_tokens >= kFffTargetBlocks) return 1;
+  const int64_t g = (kFffTargetBlocks + n_tokens - 1) / n_tokens;
+  return (int)(g < gmax ? g : gmax);
+}
+
+size_t fff_workspace_bytes(int d, int n_trees, int64_t n_tokens, int requested) {
+  const int G = fff_split(n_trees, n_tokens, requested);
+  return G > 1 ? (size_t)n_tokens * G * d * sizeof(float) : 0;
+}
+
 bool fff_width_supported(int d, int dtype) {
   const int esz = dtype == BLOCKFFN_BF16 ? 2 : 4;
   return d > 0 && (d * esz) % 1024 == 0 && d * esz / 1024 <= kFffMaxPieces;
 }
 
 hipError_t launch_fff_forward(const blockffn_fff_layer& ly, int n_layers, const void* x, int64_t n_tokens, bool dense,
-                              int32_t* paths, float* preact, float* y, hipStream_t s) {
+                              int split, int32_t* paths, float* preact, void* workspace, float* y, hipStream_t s) {
   if (n_tokens == 0) return hipSuccess;
   FffArgs a;
   a.w_node = static_cast<const uint8_t*>(ly.w_node);
@@ -248,6 +295,9 @@ hipError_t launch_fff_forward(const blockffn_fff_layer& ly, int n_layers, const 
   a.y = y;
   a.paths = paths;
   a.preact = preact;
+  a.G = fff_split(ly.n_trees, n_tokens, split);
+  a.per_group = (ly.n_trees + a.G - 1) / a.G;
+  a.partial = static_cast<float*>(workspace);
   const bool bf16 = ly.dtype == BLOCKFFN_BF16;
   const int nch = ly.d * (bf16 ? 2 : 4) / 1024;
   return bf16 ? launch_dtype<true>(a, nch, n_tokens, s) : launch_dtype<false>(a, nch, n_tokens, s);

@@ -55,6 +55,12 @@ def parse_args(argv=None):
     p.add_argument("--backward", action="store_true",
                    help="also time blockffn_backward on the batch (grouped workloads: one layer)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--latency-units", type=int, default=64,
+                   help="latency mode: units run one after another, one graph per chain of this many (0: skip)")
+    p.add_argument("--fff-split", type=int, default=0,
+                   help="FFF workloads: blocks per token (0: the library's choice)")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured ceilings (HBM read probe, hipBLASLt bf16 GEMM)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
     return p.parse_args(argv)
@@ -447,6 +453,97 @@ def backward_measure(runner, steps: int, warmup: int, dense_steps: int) -> dict:
     return res
 
 
+def measure_ceilings(gemm: bool) -> dict:
+    """Measured ceilings the achieved figures are also set against: the HBM
+    streaming-read probe (blockffn_read_probe over 8 GiB, best over grid
+    sizes) and, for matrix-core workloads, a large bf16 GEMM through
+    torch.matmul (hipBLASLt)."""
+    import torch
+    from activation_sparse_moe_amd import binding as B
+    n = 8 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    best, best_blocks = 0.0, 0
+    for blocks in (0, 2048, 4096, 8192, 16384):
+        B.blockffn_read_probe(buf, sink, blocks)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            B.blockffn_read_probe(buf, sink, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = n / (e0.elapsed_time(e1) / 3 * 1e-3) / 1e9
+        if gbs > best:
+            best, best_blocks = gbs, blocks
+    del buf
+    out = {"hbm_read_gbs": round(best, 1), "hbm_read_probe": f"blockffn_read_probe, 8 GiB, {best_blocks or 'resident'} blocks"}
+    if gemm:
+        m = 8192
+        a = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+        b = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+        torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        out["bf16_gemm_tflops"] = round(2 * m ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12, 1)
+        out["bf16_gemm"] = f"torch.matmul (hipBLASLt) {m} x {m} x {m} bf16"
+        del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def latency_measure(runner, units: int, mode: str) -> dict:
+    """Latency mode: `units` units run one after another (route -> union ->
+    forward -> stats for one unit, each unit through its own layer copy), the
+    chain captured in one HIP graph and replayed; per-unit latency = replay
+    time / units."""
+    import torch
+    B, cfg = runner.B, runner.cfg
+    L, E = cfg.chunk_len, cfg.n_experts
+    C = cfg.n_tokens // L
+    units = min(units, C)
+    views = [runner.dl.single_copy(u % max(1, cfg.replicas)) for u in range(units)]
+    ws = B.alloc_workspace(views[0], L, L, mode)
+
+    def chain():
+        for u in range(units):
+            t0, t1 = u * L, (u + 1) * L
+            x, g, m = runner.xd[t0:t1], runner.gates[t0:t1], runner.masks[t0:t1]
+            cnt, lst, um = runner.count[u:u + 1], runner.lst[u:u + 1], runner.umask[u:u + 1]
+            B.blockffn_route(views[u], x, L, gates=g, token_masks=m)
+            B.blockffn_chunk_union(E, m, L, chunk_masks=um, active_count=cnt, active_list=lst)
+            B.blockffn_forward(views[u], x, L, g, cnt, lst, mode=mode, workspace=ws, y=runner.y[t0:t1])
+            B.blockffn_sparsity_stats(E, m, L, stats_dev=runner.stats)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chain()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps / units * 1e3
+    return {"us_per_unit": round(us, 2), "units_chained": units, "tokens_per_unit": L,
+            "kind": "units one after another, each through its own layer copy, one HIP graph per chain"}
+
+
 def copy_calibration():
     """A plain device copy of 1 GiB: its FETCH_SIZE / WRITE_SIZE counters
     scale the expert kernels' counters to bytes."""
@@ -523,6 +620,67 @@ def torch_dense_fff_ms(dl, xd, n: int, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def fff_latency(dl, xd, units: int) -> dict:
+    """Latency mode: single tokens one after another, each through its own
+    layer copy, the chain captured in one HIP graph (per-token latency =
+    replay time / units); beside it the dense block for one token as two
+    torch.bmm calls, chained the same way."""
+    import torch
+    from activation_sparse_moe_amd import binding as B
+    views = [dl.single_copy(u) for u in range(units)]
+    ws = B.alloc_fff_workspace(views[0], 1)
+    y = torch.empty((units, dl.d), dtype=torch.float32, device="cuda")
+    rows = dl.rows
+    wn = [v.rows_view("w_node") for v in views]
+    wo = [v.rows_view("w_out") for v in views]
+    bias = [v.tensors(0)["b_node"] for v in views]
+    xs = [xd[u:u + 1].unsqueeze(2).contiguous() for u in range(units)]
+
+    def sparse_chain():
+        for u in range(units):
+            B.blockffn_fff_forward(views[u], xd[u:u + 1], y=y[u:u + 1], workspace=ws)
+
+    def dense_chain():
+        for u in range(units):
+            c = torch.bmm(wn[u], xs[u]).float()
+            if bias[u] is not None:
+                c = c + bias[u].reshape(1, rows, 1)
+            a = torch.nn.functional.gelu(c).to(xd.dtype).reshape(1, 1, rows)
+            torch.bmm(a, wo[u])
+
+    out = {}
+    for name, chain in (("us_per_token", sparse_chain), ("dense_torch_bmm_us_per_token", dense_chain)):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            chain()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            chain()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / 3 / units * 1e3, 2)
+    out["speedup_vs_dense"] = round(out["dense_torch_bmm_us_per_token"] / out["us_per_token"], 2)
+    out.update({"tokens_chained": units, "blocks_per_token": _fff_split(views[0], 1),
+                "kind": "tokens one after another, each through its own layer copy, one HIP graph per chain"})
+    return out
+
+
+def _fff_split(layer, n_tokens: int) -> int:
+    """Blocks per token the library uses (workspace bytes / (T d 4), at least 1)."""
+    from activation_sparse_moe_amd import binding as B
+    nb = B.blockffn_fff_workspace_size(layer, n_tokens, 0)
+    return max(1, nb // (n_tokens * layer.d * 4))
+
+
 def fff_main(args, cfg) -> int:
     import torch
     from activation_sparse_moe_amd import binding as B
@@ -541,7 +699,8 @@ def fff_main(args, cfg) -> int:
     xd = B.tokens_to_device(x, F32 if cfg.dtype == "f32" else BF16)
     T = cfg.tokens
     y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
-    fwd = lambda: B.blockffn_fff_forward(dl, xd, mode=mode, y=y)  # noqa: E731
+    ws = B.alloc_fff_workspace(dl, T, args.fff_split)
+    fwd = lambda: B.blockffn_fff_forward(dl, xd, mode=mode, y=y, split=args.fff_split, workspace=ws)  # noqa: E731
 
     # eager launches, each bracketed by events on the launch stream: the
     # kernel's average duration for the roofline
@@ -614,6 +773,15 @@ def fff_main(args, cfg) -> int:
                  "speedup_vs_torch_bmm": round(T / (ms * 1e-3) / torch_tps, 2),
                  "ideal_byte_ratio": round(bm["dense_per_token"] / bm["per_token"], 2)}
 
+    latency = None
+    if args.latency_units > 0 and mode == "sparse":
+        latency = fff_latency(dl, xd, min(args.latency_units, T, cfg.replicas))
+    ceilings = None
+    if not args.no_ceilings:
+        del dl
+        torch.cuda.empty_cache()
+        ceilings = measure_ceilings(gemm=False)
+        roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / ceilings["hbm_read_gbs"], 4)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = fff_cpu_baseline(cfg, layer, x, args.cpu_seconds)
@@ -633,6 +801,8 @@ def fff_main(args, cfg) -> int:
         "sparsity": {"nodes_visited_per_token": cfg.n_trees * (cfg.depth + 1),
                      "fraction_idle": round(1 - (cfg.depth + 1) / cfg.nodes, 4)},
         "dense": dense,
+        "latency": latency,
+        "ceilings": ceilings,
         "timing": {"steps": "eager launches" if args.eager else "HIP graph replay of the forward",
                    "eager_ms_per_step": round(eager_ms, 5), "kernel_ms": round(kernel_ms, 5)},
         "source_digest": source_digest(),
@@ -710,6 +880,17 @@ def main(argv=None) -> int:
     if args.backward:
         backward = backward_measure(runner, args.steps, args.warmup, args.dense_steps)
 
+    latency = None
+    if args.latency_units > 0 and not grouped:
+        latency = latency_measure(runner, args.latency_units, mode)
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(gemm=grouped)
+        if grouped and "bf16_gemm_tflops" in ceilings:
+            roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / ceilings["bf16_gemm_tflops"], 4)
+        elif not grouped:
+            roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / ceilings["hbm_read_gbs"], 4)
+
     cpu = None
     if not args.no_cpu_baseline and args.router == "blockffn":
         cpu = cpu_baseline(cfg, runner.layer, runner.x_host, args.cpu_seconds)
@@ -742,6 +923,8 @@ def main(argv=None) -> int:
                    "eager_ms_per_step": round(eager_ms, 5),
                    "kernel_ms": "eager steps with HIP events around each launch"},
         "backward": backward,
+        "latency": latency,
+        "ceilings": ceilings,
         "sparsity": {"tls": round(st["tls"], 4), "cls": round(st["cls"], 4), "mean_union": round(U / (T // cfg.chunk_len), 2),
                      "reuse": round(st["reuse"], 4)},
         "source_digest": source_digest(),

@@ -333,16 +333,31 @@ typedef struct blockffn_fff_layer {
  * FFF layer forward.
  *   x            [n_tokens][d] in the layer's dtype, 16-byte aligned
  *   mode         BLOCKFFN_FFF_SPARSE or BLOCKFFN_FFF_DENSE
+ *   split        blocks per token: 0 lets the library choose from n_tokens
+ *                (one block per token for large batches, a token's trees
+ *                spread over several blocks for small ones); k >= 1 asks for
+ *                k (at most ceil(P / 4)).  With more than one block per token
+ *                each block sums its own trees and a second kernel adds the
+ *                blocks' partial outputs in order, so results depend on the
+ *                split in the last bits but are reproducible for a given one
  *   paths        [n_tokens][P][D+1] i32 out: the node visited at each level,
  *                or NULL (must be NULL in DENSE mode)
  *   node_preact  [n_tokens][P][D+1] fp32 out: c at each visited node, or
  *                NULL (must be NULL in DENSE mode)
+ *   workspace    blockffn_fff_workspace_size() bytes, 16-byte aligned (NULL
+ *                when that size is 0); no initialisation needed
  *   y            [n_tokens][d] fp32 out, overwritten, 16-byte aligned
- * n_tokens below 2^31; n_tokens == 0 enqueues nothing.  No workspace.
- * Errors: NULL, SHAPE, DTYPE, MODE, ALIGN, LAYERS, HIP.
+ * n_tokens below 2^31, and n_tokens x blocks per token too; n_tokens == 0
+ * enqueues nothing.
+ * Errors: NULL, SHAPE, DTYPE, MODE, WORKSPACE, ALIGN, LAYERS, HIP.
  */
 int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
-                         int32_t mode, int32_t* paths, float* node_preact, float* y, hipStream_t stream);
+                         int32_t mode, int32_t split, int32_t* paths, float* node_preact, void* workspace,
+                         size_t workspace_bytes, float* y, hipStream_t stream);
+
+/* Workspace bytes blockffn_fff_forward needs for these arguments (0 when it
+ * runs one block per token, or on invalid input). */
+size_t blockffn_fff_workspace_size(const blockffn_fff_layer* layer, int64_t n_tokens, int32_t split);
 
 /*
  * Stage timing (instrumentation for profilers and benchmarks).  While set,
@@ -358,6 +373,19 @@ int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_layers, cons
  * stop.  Errors: SHAPE (n_events < 1 with non-NULL events).
  */
 int blockffn_set_stage_events(hipEvent_t* events, int32_t n_events);
+
+/*
+ * HBM streaming-read ceiling probe (instrumentation for benchmarks): reads
+ * `bytes` from `buf` once with 16-byte non-temporal loads, eight in flight
+ * per thread, in a grid-stride sweep of `blocks` blocks of 256 threads
+ * (0 = every block the device holds at once).  The time of the call is the
+ * measured ceiling the layer kernels' bandwidth is compared with.
+ *   buf    device memory, 16-byte aligned; bytes a multiple of 16
+ *   sink   one u32 of device memory; written only if the XOR of all the data
+ *          read equals a fixed constant, so that the loads stay live
+ * Errors: NULL, ALIGN (buf or bytes), SHAPE (blocks < 0), HIP.
+ */
+int blockffn_read_probe(const void* buf, size_t bytes, int32_t blocks, uint32_t* sink, hipStream_t stream);
 
 /* Workspace bytes blockffn_forward needs for these arguments (0 on invalid input). */
 size_t blockffn_workspace_size(const blockffn_layer* layer, int64_t n_tokens, int32_t chunk_len,

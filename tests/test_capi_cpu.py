@@ -293,11 +293,11 @@ def _fff_layer(**kw):
 
 @cpu_only
 def test_fff_forward_validation(lib):
-    def call(layer=None, n_layers=1, x=P, T=4, mode=0, paths=None, pre=None, y=P):
+    def call(layer=None, n_layers=1, x=P, T=4, mode=0, split=1, paths=None, pre=None, ws=None, nb=0, y=P):
         ly = _fff_layer() if layer is None else layer
-        return lib.blockffn_fff_forward(ctypes.byref(ly), n_layers, x, T, mode, paths, pre, y, None)
+        return lib.blockffn_fff_forward(ctypes.byref(ly), n_layers, x, T, mode, split, paths, pre, ws, nb, y, None)
 
-    assert lib.blockffn_fff_forward(None, 1, P, 4, 0, None, None, P, None) == _capi.ERR_NULL
+    assert lib.blockffn_fff_forward(None, 1, P, 4, 0, 1, None, None, None, 0, P, None) == _capi.ERR_NULL
     assert call(_fff_layer(dtype=2)) == _capi.ERR_DTYPE
     for d in (0, 256, 2048 + 64, 4608):       # bf16: multiples of 512 up to 4096
         assert call(_fff_layer(d=d)) == _capi.ERR_SHAPE, d
@@ -325,6 +325,36 @@ def test_fff_forward_validation(lib):
     assert call(_fff_layer(w_out=P + 8)) == _capi.ERR_ALIGN
     assert call(_fff_layer(b_node=P + 2)) == _capi.ERR_ALIGN
     assert call(paths=P + 2) == _capi.ERR_ALIGN
+    # blocks per token: 0 (automatic) .. ceil(P / 4) = 16
+    assert call(split=-1) == _capi.ERR_SHAPE
+    assert call(split=17) == _capi.ERR_SHAPE
+    need = 4 * 2 * 2048 * 4                                              # T x G x d fp32 partials
+    assert call(split=2) == _capi.ERR_WORKSPACE
+    assert call(split=2, ws=P, nb=need - 16) == _capi.ERR_WORKSPACE
+    assert call(split=2, ws=P + 8, nb=need) == _capi.ERR_ALIGN
     # a valid call with no tokens enqueues nothing
     assert call(T=0, x=None, y=None) == _capi.OK
     assert call(T=0, x=None, y=None, mode=1) == _capi.OK
+    assert call(T=0, x=None, y=None, split=0) == _capi.OK
+
+
+def test_fff_workspace_size(lib):
+    ly = _fff_layer()
+    size = lambda T, split: lib.blockffn_fff_workspace_size(ctypes.byref(ly), T, split)  # noqa: E731
+    assert size(4096, 0) == 0                       # enough tokens: one block per token
+    assert size(64, 1) == 0
+    assert size(64, 0) == 64 * 16 * 2048 * 4        # a token's 64 trees over 16 blocks
+    assert size(1000, 0) == 1000 * 4 * 2048 * 4     # ceil(3072 / 1000) = 4 blocks per token
+    assert size(64, 3) == 64 * 3 * 2048 * 4
+    assert size(64, 17) == 0                        # invalid split
+    assert lib.blockffn_fff_workspace_size(ctypes.byref(_fff_layer(d=100)), 64, 0) == 0
+
+
+@cpu_only
+def test_read_probe_validation(lib):
+    assert lib.blockffn_read_probe(P, 1 << 20, 0, None, None) == _capi.ERR_NULL
+    assert lib.blockffn_read_probe(None, 1 << 20, 0, P, None) == _capi.ERR_NULL
+    assert lib.blockffn_read_probe(P + 8, 1 << 20, 0, P, None) == _capi.ERR_ALIGN
+    assert lib.blockffn_read_probe(P, (1 << 20) + 4, 0, P, None) == _capi.ERR_ALIGN
+    assert lib.blockffn_read_probe(P, 1 << 20, -1, P, None) == _capi.ERR_SHAPE
+    assert lib.blockffn_read_probe(P, 0, 0, P, None) == _capi.OK     # nothing to read

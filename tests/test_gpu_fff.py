@@ -89,15 +89,17 @@ def _compare(paths_g, pre_g, y_g, paths_o, pre_o, y_o, where):
     return len(flipped)
 
 
-def _case(d, P, D, dtype, T, seed, post=False, dense=False, n_layers=1, bias=True, interleave=True):
+def _case(d, P, D, dtype, T, seed, post=False, dense=False, n_layers=1, bias=True, interleave=True, split=0):
     rng = np.random.default_rng(seed)
     layers = [make_fff_layer(d, P, D, dtype, rng, bias=bias) for _ in range(n_layers)]
     x = make_fff_tokens(d, T, dtype, rng)
-    where = f"d={d} P={P} D={D} {dtype} T={T} post={post} dense={dense} layers={n_layers} interleave={interleave}"
+    where = (f"d={d} P={P} D={D} {dtype} T={T} post={post} dense={dense} layers={n_layers} "
+             f"interleave={interleave} split={split}")
     say(f"[gpu] fff {where}")
     dl = _dev_layer(layers, post, interleave)
     xd = B.tokens_to_device(x, F32 if dtype == "f32" else BF16)
-    y, paths, pre = B.blockffn_fff_forward(dl, xd, mode="dense" if dense else "sparse", want_paths=not dense)
+    y, paths, pre = B.blockffn_fff_forward(dl, xd, mode="dense" if dense else "sparse", want_paths=not dense,
+                                           split=split)
     torch.cuda.synchronize()
     po, co, yo = _oracle(layers, x, post, dense)
     flips = _compare(None if dense else paths.cpu().numpy(), None if dense else pre.cpu().numpy(),
@@ -130,6 +132,16 @@ def test_fff_dense_matches_oracle(d, P, D, dtype, T, post):
     _case(d, P, D, dtype, T, 950 + d + P + D, post=post, dense=True)
 
 
+@pytest.mark.parametrize("split", [1, 2, 3, 0])
+@pytest.mark.parametrize("d,P,D,dtype,T,post", [
+    (2048, 64, 6, "bf16", 7, False),        # 64 trees over 1, 2, 3 or (automatically) 16 blocks per token
+    (512, 13, 4, "bf16", 5, True),          # uneven groups, GELU after the combine
+    (256, 9, 3, "f32", 3, False),
+])
+def test_fff_blocks_per_token(d, P, D, dtype, T, post, split):
+    _case(d, P, D, dtype, T, 970 + P + split, post=post, split=split)
+
+
 def test_fff_without_bias():
     _case(512, 6, 4, "bf16", 11, 961, bias=False)
 
@@ -159,20 +171,22 @@ def test_fff_graph_replays_match_eager():
     say("[gpu] fff graph replay")
     dl = B.DeviceFffLayer.from_workload(layer)
     xd = B.tokens_to_device(x, BF16)
-    y, paths, pre = B.blockffn_fff_forward(dl, xd, want_paths=True)
+    ws = B.alloc_fff_workspace(dl, 24)                      # 24 tokens: several blocks per token
+    assert ws is not None
+    y, paths, pre = B.blockffn_fff_forward(dl, xd, want_paths=True, workspace=ws)
     torch.cuda.synchronize()
     eager = [v.clone() for v in (y, paths, pre)]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        B.blockffn_fff_forward(dl, xd, y=y, paths=paths, node_preact=pre)
+        B.blockffn_fff_forward(dl, xd, y=y, paths=paths, node_preact=pre, workspace=ws)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        B.blockffn_fff_forward(dl, xd, y=y, paths=paths, node_preact=pre)
+        B.blockffn_fff_forward(dl, xd, y=y, paths=paths, node_preact=pre, workspace=ws)
     for rep in range(3):
-        for v in (y, paths, pre):
+        for v in (y, paths, pre, ws):
             v.zero_()
         noise = torch.randn(1 << 20, device="cuda").sum()
         torch.cuda.synchronize()

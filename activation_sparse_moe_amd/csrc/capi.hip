@@ -11,6 +11,7 @@
 #include <utility>
 
 #include "bffn_internal.h"
+#include "fff_probe_launch.h"
 
 #define BFFN_EXPORT extern "C" __attribute__((visibility("default")))
 

@@ -35,7 +35,7 @@
 //    workspace and a second kernel adds the G partials in group order (and
 //    applies the post-aggregation GELU).  G is chosen from the token count
 //    alone, so a given call is reproducible.
-#include "bffn_internal.h"
+#include "fff_probe_launch.h"
 
 namespace bffn {
 namespace {

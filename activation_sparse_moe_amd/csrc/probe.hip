@@ -4,7 +4,7 @@
 // A grid-stride sweep of 16-byte non-temporal loads, eight in flight per
 // thread.  The XOR of everything read decides one store that practically
 // never happens, so the loads cannot be removed and nothing is written.
-#include "bffn_internal.h"
+#include "fff_probe_launch.h"
 
 namespace bffn {
 namespace {

@@ -73,7 +73,7 @@ KERNEL_SOURCES = {
     "expert_down": ("expert_mfma.hip", "lds_stream.h", "bffn_internal.h"),
     "grouped_up": ("grouped.hip", "grouped_kernels.h", "bffn_internal.h"),
     "grouped_down": ("grouped.hip", "grouped_kernels.h", "bffn_internal.h"),
-    "fff_walk": ("fff.hip", "bffn_internal.h"),
+    "fff_walk": ("fff.hip", "fff_probe_launch.h", "bffn_internal.h"),
 }
 
 

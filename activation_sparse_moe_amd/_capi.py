@@ -14,10 +14,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libblockffn.so")
 
 F32, BF16 = 0, 1
-MODE_AUTO, MODE_GEMV, MODE_CHUNK_MFMA, MODE_GROUPED, MODE_DENSE = 0, 1, 2, 3, 4
+MODE_AUTO, MODE_GEMV, MODE_CHUNK_MFMA, MODE_GROUPED, MODE_DENSE, MODE_CHUNK_SPLIT = 0, 1, 2, 3, 4, 5
 ROUTER_BLOCKFFN, ROUTER_TOPK_SOFTMAX, ROUTER_RELU_SUM = 0, 1, 2
 ROUTERS = {"blockffn": ROUTER_BLOCKFFN, "topk_softmax": ROUTER_TOPK_SOFTMAX, "relu_sum": ROUTER_RELU_SUM}
-MODES = {"auto": MODE_AUTO, "gemv": MODE_GEMV, "chunk_mfma": MODE_CHUNK_MFMA, "grouped": MODE_GROUPED,
+MODES = {"auto": MODE_AUTO, "gemv": MODE_GEMV, "chunk_mfma": MODE_CHUNK_MFMA, "chunk_split": MODE_CHUNK_SPLIT,
+         "grouped": MODE_GROUPED,
          "dense": MODE_DENSE}
 
 OK = 0

@@ -87,9 +87,22 @@ hipError_t launch_stats(int E, const uint64_t* masks, int64_t n_tokens, int chun
 hipError_t launch_forward_gemv(const LayerArgs& la, const void* x, int64_t n_tokens, int chunk_len,
                                int dtype, const float* gates, const int32_t* count, const int32_t* list,
                                bool dense, float* hbuf, float* y, const StageEvents& se, hipStream_t s);
+// The chunk path split for a few units: up items cut into ks k-ranges, down
+// items into sp ranges of the union's slots, with fp32 partial tiles in
+// up_part / down_part.  ks == 0: no split.
+struct ChunkSplit {
+  int ks = 0, sp = 0;
+  float* up_part = nullptr;
+  float* down_part = nullptr;
+};
+constexpr int64_t kChunkSplitMaxUnits = 16;  // AUTO splits launches of at most this many units
+bool chunk_split_factors(int d, int de, int64_t units, bool force, int* ks, int* sp);
+size_t chunk_split_part_bytes(int d, int de, int E, int64_t units, int chunk_len, int ks, int sp,
+                              size_t* down_offset);
 hipError_t launch_forward_mfma(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len,
                                const float* gates, const int32_t* count, const int32_t* list, bool dense,
-                               uint16_t* hbuf, int64_t* plan, float* y, const StageEvents& se, hipStream_t s);
+                               uint16_t* hbuf, int64_t* plan, const ChunkSplit& sp, float* y, const StageEvents& se,
+                               hipStream_t s);
 
 hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, const float* gates,
                                   void* workspace, float* y, const StageEvents& se, hipStream_t s);

@@ -121,20 +121,28 @@ bffn::LayerArgs layer_args(const blockffn_layer* ly, int32_t n_layers) {
   return la;
 }
 
-enum class Path { kGemv, kMfma, kGrouped };
+enum class Path { kGemv, kMfma, kMfmaSplit, kGrouped };
 
 // Resolves `mode` to a kernel family; returns a status code.
-int resolve_mode(const blockffn_layer* ly, int32_t chunk_len, int32_t mode, Path* path, bool* dense) {
+int resolve_mode(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, int32_t mode, Path* path,
+                 bool* dense) {
   // The matrix-core path streams each chunk's union once for all its tokens;
   // at chunk_len 1 its idle token columns cost nothing (the kernels are bound
-  // by weight bytes), so it is the default wherever the shapes allow it.
+  // by weight bytes), so it is the default wherever the shapes allow it.  A
+  // launch of a few units cuts each unit's work finer to fill the GPU.
   const bool mfma_ok = bffn::forward_mfma_supported(ly->d, ly->d_expert, ly->dtype);
   const bool auto_mfma = mfma_ok;
-  (void)chunk_len;
+  int ks = 0, sp = 0;
+  const bool few = bffn::chunk_split_factors(ly->d, ly->d_expert, n_tokens / chunk_len, false, &ks, &sp);
   *dense = false;
   switch (mode) {
     case BLOCKFFN_MODE_AUTO:
-      *path = auto_mfma ? Path::kMfma : Path::kGemv;
+      *path = auto_mfma ? (few ? Path::kMfmaSplit : Path::kMfma) : Path::kGemv;
+      return BLOCKFFN_OK;
+    case BLOCKFFN_MODE_CHUNK_SPLIT:
+      if (!mfma_ok)
+        return fail(BLOCKFFN_ERR_MODE, "CHUNK_SPLIT needs bf16 with d and d_expert multiples of 128");
+      *path = Path::kMfmaSplit;
       return BLOCKFFN_OK;
     case BLOCKFFN_MODE_GEMV:
       *path = Path::kGemv;
@@ -161,7 +169,7 @@ int resolve_mode(const blockffn_layer* ly, int32_t chunk_len, int32_t mode, Path
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 size_t hbuf_bytes(const blockffn_layer* ly, int64_t n_tokens, Path path) {
-  const size_t elem = path == Path::kMfma ? 2 : 4;
+  const size_t elem = path == Path::kMfma || path == Path::kMfmaSplit ? 2 : 4;
   return round256((size_t)n_tokens * (size_t)ly->n_experts * (size_t)ly->d_expert * elem);
 }
 
@@ -171,9 +179,22 @@ size_t plan_bytes(int64_t n_tokens, int32_t chunk_len) {
   return round256(bffn::forward_mfma_plan_bytes(n_tokens / chunk_len));
 }
 
+// The split chunk path's partial tiles, after the plan.
+size_t split_bytes(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, bffn::ChunkSplit* sp) {
+  int ks = 0, s = 0;
+  bffn::chunk_split_factors(ly->d, ly->d_expert, n_tokens / chunk_len, true, &ks, &s);
+  if (sp) {
+    sp->ks = ks;
+    sp->sp = s;
+  }
+  return bffn::chunk_split_part_bytes(ly->d, ly->d_expert, ly->n_experts, n_tokens / chunk_len, chunk_len, ks, s,
+                                      nullptr);
+}
+
 size_t workspace_bytes_for(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, Path path) {
   if (path == Path::kGrouped) return bffn::grouped_workspace_bytes(n_tokens, ly->n_experts, ly->d, ly->d_expert);
-  return hbuf_bytes(ly, n_tokens, path) + plan_bytes(n_tokens, chunk_len);
+  const size_t base = hbuf_bytes(ly, n_tokens, path) + plan_bytes(n_tokens, chunk_len);
+  return path == Path::kMfmaSplit ? base + split_bytes(ly, n_tokens, chunk_len, nullptr) : base;
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -237,7 +258,7 @@ BFFN_EXPORT size_t blockffn_workspace_size(const blockffn_layer* layer, int64_t 
   if (check_layer(layer, 1) != BLOCKFFN_OK || check_chunking(n_tokens, chunk_len) != BLOCKFFN_OK) return 0;
   Path path;
   bool dense;
-  if (resolve_mode(layer, chunk_len, mode, &path, &dense) != BLOCKFFN_OK) return 0;
+  if (resolve_mode(layer, n_tokens, chunk_len, mode, &path, &dense) != BLOCKFFN_OK) return 0;
   return workspace_bytes_for(layer, n_tokens, chunk_len, path);
 }
 
@@ -249,7 +270,7 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, 
   if (int r = check_chunking(n_tokens, chunk_len)) return r;
   Path path;
   bool dense;
-  if (int r = resolve_mode(layer, chunk_len, mode, &path, &dense)) return r;
+  if (int r = resolve_mode(layer, n_tokens, chunk_len, mode, &path, &dense)) return r;
   if (path == Path::kGrouped && n_layers != 1)
     return fail(BLOCKFFN_ERR_LAYERS, "GROUPED runs one batch through one layer (n_layers %d)", n_layers);
   if (path == Path::kGrouped && n_tokens * layer->n_experts > INT32_MAX)
@@ -271,12 +292,22 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, 
   if (path == Path::kGrouped)
     e = bffn::launch_forward_grouped(la, static_cast<const uint16_t*>(x), n_tokens, gates, workspace, y,
                                      g_stage_events, stream);
-  else if (path == Path::kMfma)
-    e = bffn::launch_forward_mfma(
-        la, static_cast<const uint16_t*>(x), n_tokens, chunk_len, gates, active_count, active_list, dense,
-        static_cast<uint16_t*>(workspace),
-        reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + hbuf_bytes(layer, n_tokens, path)), y,
-        g_stage_events, stream);
+  else if (path == Path::kMfma || path == Path::kMfmaSplit) {
+    char* ws = static_cast<char*>(workspace);
+    const size_t hb = hbuf_bytes(layer, n_tokens, path), pb = plan_bytes(n_tokens, chunk_len);
+    bffn::ChunkSplit sp;
+    if (path == Path::kMfmaSplit) {
+      split_bytes(layer, n_tokens, chunk_len, &sp);
+      size_t down_off = 0;
+      bffn::chunk_split_part_bytes(layer->d, layer->d_expert, layer->n_experts, n_tokens / chunk_len, chunk_len,
+                                   sp.ks, sp.sp, &down_off);
+      sp.up_part = reinterpret_cast<float*>(ws + hb + pb);
+      sp.down_part = reinterpret_cast<float*>(ws + hb + pb + down_off);
+    }
+    e = bffn::launch_forward_mfma(la, static_cast<const uint16_t*>(x), n_tokens, chunk_len, gates, active_count,
+                                  active_list, dense, static_cast<uint16_t*>(workspace),
+                                  reinterpret_cast<int64_t*>(ws + hb), sp, y, g_stage_events, stream);
+  }
   else
     e = bffn::launch_forward_gemv(la, x, n_tokens, chunk_len, layer->dtype, gates, active_count, active_list, dense,
                                   static_cast<float*>(workspace), y, g_stage_events, stream);

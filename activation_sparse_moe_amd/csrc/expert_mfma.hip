@@ -24,6 +24,14 @@
 // through an LDS counter.  Items are decoded with scalar loads only, so
 // nothing in the loop waits on a returning memory operation except the
 // weight stream.
+//
+// A few units cannot fill the GPU this way: one chunk of 8 tokens has about
+// 38 up and 32 down items.  The SPLIT instantiations cut every up item into
+// ks k-ranges and every down item into sp ranges of the union's slots; the
+// items write fp32 partial tiles, and two small kernels add the partials in
+// range order (then apply g * Swish, or store y).  The summation order
+// differs from the unsplit kernels only in the last bits, and it is fixed
+// for a given split, so results stay reproducible.
 #include "lds_stream.h"
 
 namespace bffn {
@@ -59,24 +67,26 @@ __global__ __launch_bounds__(1024) void plan_items_kernel(const int32_t* __restr
 
 struct UpItem {
   int64_t unit;
-  int slot, rb, i;
+  int slot, rb, i, kp;
 };
 
 // ---- up-projection: H'[unit][slot] = g * Swish(X W_in[i]^T), items of 64 rows ----
-template <int NT, bool DENSE>
+template <int NT, bool DENSE, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
                                                          int64_t n_units, int L, const float* __restrict__ gates,
                                                          const int32_t* __restrict__ list,
                                                          const int64_t* __restrict__ prefix,
-                                                         uint16_t* __restrict__ hbuf) {
-  using G = RingGeom<NT, true>;
+                                                         uint16_t* __restrict__ hbuf, int ks,
+                                                         float* __restrict__ part) {
+  using G = RingGeom<NT, !SPLIT>;  // split items leave the gates to their epilogue
   // one LDS object: the four waves' rings, then the block's work counter
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRingBufs * G::kBufBytes + 16];
   unsigned& taken = *reinterpret_cast<unsigned*>(lds + 4 * kRingBufs * G::kBufBytes);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int d = la.d, de = la.de, E = la.E, rbs = de >> 6;
-  const int nsteps = d / kStepK;
+  const int nsteps = d / kStepK / (SPLIT ? ks : 1);  // steps per item
+  const int per_slot = SPLIT ? rbs * ks : rbs;       // items per union slot
   uint8_t* bufs = lds + w * kRingBufs * G::kBufBytes;
   // the block's items (all of equal size): a contiguous equal share.  (Giving
   // each XCD a range that its blocks take in turn keeps a chunk's token rows
@@ -100,8 +110,10 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
     UpItem it;
     it.unit = lo;
     const int r = (int)(it_idx - prefix[lo]);
-    it.slot = r / rbs;
-    it.rb = r % rbs;
+    it.slot = r / per_slot;
+    const int rem = r % per_slot;
+    it.rb = SPLIT ? rem / ks : rem;
+    it.kp = SPLIT ? rem % ks : 0;
     it.i = DENSE ? it.slot : list[lo * E + it.slot];
     return it;
   };
@@ -111,15 +123,16 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
   const float* g_src;
   auto point = [&](const UpItem& it) {
     const uint16_t* wi = layer_ptr(static_cast<const uint16_t*>(la.w_in), la.stride, it.unit, la.n_layers);
+    const int k0 = it.kp * nsteps * kStepK;  // first k of the item's range
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int R = 8 * j + (lane >> 3);
-      a_src[j] = wi + ((int64_t)it.i * de + it.rb * 64 + R) * d + dma_chunk_elems(R, lane);
+      a_src[j] = wi + ((int64_t)it.i * de + it.rb * 64 + R) * d + k0 + dma_chunk_elems(R, lane);
     }
 #pragma unroll
     for (int j = 0; j < G::kBInstr; ++j) {
       const int n = 8 * j + (lane >> 3);
-      b_src[j] = x + (it.unit * L + n % L) * d + dma_chunk_elems(n, lane);
+      b_src[j] = x + (it.unit * L + n % L) * d + k0 + dma_chunk_elems(n, lane);
     }
     g_src = gates + (it.unit * L + lane % L) * E + it.i;
   };
@@ -129,7 +142,7 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
     for (int j = 0; j < 8; ++j) dma16<kPolicyStream>(a_src[j] + k * kStepK, buf + j * 1024);
 #pragma unroll
     for (int j = 0; j < G::kBInstr; ++j) dma16<kPolicyReuse>(b_src[j] + k * kStepK, buf + kABytes + j * 1024);
-    dma4(g_src, buf + G::kGateOff);
+    if constexpr (!SPLIT) dma4(g_src, buf + G::kGateOff);
   };
 
   UpItem cmp = decode(item), nxt = cmp;
@@ -163,6 +176,23 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
     ring_mfma<NT>(acc, buf, m, g);
     __builtin_amdgcn_sched_barrier(0);
     if (++k_cmp < nsteps) continue;
+    if constexpr (SPLIT) {
+      // item complete: its fp32 partial tile [token][64 rows]
+      float* pb = part + ((((cmp.unit * E + cmp.slot) * rbs + cmp.rb) * (int64_t)ks + cmp.kp) * L) * 64;
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl) {
+        const int n = m + 16 * tl;
+        if (n >= L) continue;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4*>(pb + n * 64 + 16 * s + 4 * g) = acc[s][tl];
+      }
+      if (!has_next) break;
+      cmp = nxt;
+      has_next = false;
+      k_cmp = 0;
+      ring_zero<NT>(acc);
+      continue;
+    }
     // item complete: g * Swish, bf16, to the hidden buffer (gates from this step's buffer)
     const int64_t t0 = cmp.unit * L;
     const float* gv_lds = reinterpret_cast<const float*>(buf + G::kGateOff);
@@ -192,13 +222,14 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
 // ---- down-projection: Y[unit][kb .. kb + 64) = sum over slots of H'[unit][slot] W_out[i]^T ----
 // Items (chunk, 64 output rows) take count[chunk] * d_e / 64 steps; each XCD
 // gets the items whose first step falls in its equal share of all steps.
-template <int NT, bool DENSE>
+template <int NT, bool DENSE, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t n_units, int L,
                                                            const int32_t* __restrict__ count,
                                                            const int32_t* __restrict__ list,
                                                            const int64_t* __restrict__ prefix,
                                                            const uint16_t* __restrict__ hbuf,
-                                                           float* __restrict__ y) {
+                                                           float* __restrict__ y, int sp,
+                                                           float* __restrict__ part) {
   using G = RingGeom<NT, false>;
   // one LDS object: the four waves' rings, then the block's work counter
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRingBufs * G::kBufBytes + 16];
@@ -230,20 +261,42 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   };
   // the block's items: its turns in its XCD's range, the items whose first
   // step falls in an equal share of all steps (the last range also takes
-  // items starting at the very end)
-  const int64_t S = prefix[n_units] / rbs * kbs * spe;
-  const XcdShare share = xcd_share([&](int k) {
-    return k == kXcds ? n_units * kbs : first_item_at((int64_t)k * S / kXcds);
-  });
-  const int64_t blk_lo = share.lo, stride = share.stride, item_end = share.end;
+  // items starting at the very end).  Split items (few units) are shared
+  // out in contiguous ranges.
+  int64_t blk_lo, stride, item_end;
+  if constexpr (SPLIT) {
+    const int64_t total = n_units * kbs * sp;
+    blk_lo = (int64_t)blockIdx.x * total / gridDim.x;
+    stride = 1;
+    item_end = ((int64_t)blockIdx.x + 1) * total / gridDim.x;
+  } else {
+    const int64_t S = prefix[n_units] / rbs * kbs * spe;
+    const XcdShare share = xcd_share([&](int k) {
+      return k == kXcds ? n_units * kbs : first_item_at((int64_t)k * S / kXcds);
+    });
+    blk_lo = share.lo;
+    stride = share.stride;
+    item_end = share.end;
+  }
   if (threadIdx.x == 0) taken = 0;
   __syncthreads();
 
   struct DownItem {
-    int64_t unit;
-    int kb, nsteps;
+    int64_t unit, idx;
+    int kb, nsteps, s0;
   };
   auto store_y = [&](const DownItem& it, const f32x4 (&acc)[4][NT]) {
+    if constexpr (SPLIT) {  // the item's fp32 partial tile [token][64 rows]
+      float* pb = part + it.idx * L * 64;
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl) {
+        const int n = m + 16 * tl;
+        if (n >= L) continue;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4*>(pb + n * 64 + 16 * s + 4 * g) = acc[s][tl];
+      }
+      return;
+    }
 #pragma unroll
     for (int tl = 0; tl < NT; ++tl) {
       const int n = m + 16 * tl;
@@ -259,9 +312,23 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
     for (;;) {
       const int64_t item = take_item(&taken, blk_lo, stride, lane);
       if (item >= item_end) return false;
-      it.unit = item / kbs;
-      it.kb = (int)(item % kbs);
-      it.nsteps = (int)nact(it.unit) * spe;
+      it.idx = item;
+      if constexpr (SPLIT) {  // (unit, kb, a range of the union's slots)
+        it.unit = item / ((int64_t)kbs * sp);
+        const int rem = (int)(item % ((int64_t)kbs * sp));
+        it.kb = rem / sp;
+        const int spi = rem % sp;
+        const int S = (int)nact(it.unit), per = (S + sp - 1) / sp;
+        const int s0 = spi * per < S ? spi * per : S;
+        const int s1 = s0 + per < S ? s0 + per : S;
+        it.s0 = s0;
+        it.nsteps = (s1 - s0) * spe;
+      } else {
+        it.unit = item / kbs;
+        it.kb = (int)(item % kbs);
+        it.s0 = 0;
+        it.nsteps = (int)nact(it.unit) * spe;
+      }
       if (it.nsteps > 0) return true;
       f32x4 z[4][NT];
       ring_zero<NT>(z);
@@ -270,7 +337,7 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
     return false;
   };
   auto issue = [&](int slot_buf, const DownItem& it, int k) {
-    const int sl = k / spe, j0 = (k % spe) * kStepK;
+    const int sl = it.s0 + k / spe, j0 = (k % spe) * kStepK;
     const int i = DENSE ? sl : list[it.unit * E + sl];
     const uint16_t* wo = layer_ptr(static_cast<const uint16_t*>(la.w_out), la.stride, it.unit, la.n_layers);
     const uint16_t* wbase = wo + ((int64_t)i * d + it.kb * 64) * de + j0;
@@ -332,27 +399,75 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   wait_vmcnt<0>();  // no LDS write may outlive the wave
 }
 
-template <int NT, bool DENSE>
+// h'[unit][slot][token][64 rb + r] = g * Swish(sum over k-ranges, in order, of
+// the up items' partial tiles), bf16; one block per (unit, slot, row block).
+__global__ __launch_bounds__(kBlock) void up_split_epilogue_kernel(const float* __restrict__ part,
+                                                                   const float* __restrict__ gates,
+                                                                   const int32_t* __restrict__ count,
+                                                                   const int32_t* __restrict__ list, int L, int E,
+                                                                   int de, int ks, uint16_t* __restrict__ hbuf) {
+  const int rbs = de >> 6;
+  const int64_t b = blockIdx.x;
+  const int rb = (int)(b % rbs);
+  const int slot = (int)((b / rbs) % E);
+  const int64_t u = b / ((int64_t)rbs * E);
+  if (slot >= count[u]) return;
+  const int i = list[u * E + slot];
+  const float* pb = part + (((u * E + slot) * rbs + rb) * (int64_t)ks) * L * 64;
+  for (int idx = threadIdx.x; idx < L * 64; idx += kBlock) {
+    const int n = idx >> 6, r = idx & 63;
+    float v = pb[idx];
+    for (int kp = 1; kp < ks; ++kp) v += pb[(int64_t)kp * L * 64 + idx];
+    const float gv = gates[(u * L + n) * E + i];
+    hbuf[((u * E + slot) * L + n) * (int64_t)de + rb * 64 + r] = (uint16_t)f32_to_bf16(gv * swish(v));
+  }
+}
+
+// y[unit L + token][64 kb + r] = sum over slot ranges, in order, of the down
+// items' partial tiles; one block per (unit, row block).
+__global__ __launch_bounds__(kBlock) void down_split_combine_kernel(const float* __restrict__ part, int L, int d,
+                                                                    int sp, float* __restrict__ y) {
+  const int kbs = d >> 6;
+  const int64_t b = blockIdx.x;
+  const int kb = (int)(b % kbs);
+  const int64_t u = b / kbs;
+  const float* pb = part + b * sp * (int64_t)L * 64;
+  for (int idx = threadIdx.x; idx < L * 64; idx += kBlock) {
+    float v = pb[idx];
+    for (int j = 1; j < sp; ++j) v += pb[(int64_t)j * L * 64 + idx];
+    y[(u * L + (idx >> 6)) * (int64_t)d + kb * 64 + (idx & 63)] = v;
+  }
+}
+
+template <int NT, bool DENSE, bool SPLIT>
 hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int L, const float* gates,
                      const int32_t* count, const int32_t* list, uint16_t* hbuf, int64_t* plan, float* y,
-                     const StageEvents& se, hipStream_t s) {
+                     const ChunkSplit& sp, const StageEvents& se, hipStream_t s) {
   const int rbs = la.de >> 6;
-  plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, DENSE ? la.E : 0, rbs, plan);
+  const int ks = SPLIT ? sp.ks : 1;
+  plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, DENSE ? la.E : 0, rbs * ks, plan);
   // persistent grids sized to the resident capacity (one block per CU at this LDS use)
   int64_t grid_up = 0, grid_dn = 0;
-  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&up_mfma_kernel<NT, DENSE>), kBlock, &grid_up);
+  hipError_t e =
+      resident_blocks(reinterpret_cast<const void*>(&up_mfma_kernel<NT, DENSE, SPLIT>), kBlock, &grid_up);
   if (e == hipSuccess)
-    e = resident_blocks(reinterpret_cast<const void*>(&down_mfma_kernel<NT, DENSE>), kBlock, &grid_dn);
+    e = resident_blocks(reinterpret_cast<const void*>(&down_mfma_kernel<NT, DENSE, SPLIT>), kBlock, &grid_dn);
   if (e != hipSuccess) return e;
   // the item shares assume the grid is a multiple of the XCD count
   grid_up = grid_up / kXcds * kXcds > 0 ? grid_up / kXcds * kXcds : kXcds;
   grid_dn = grid_dn / kXcds * kXcds > 0 ? grid_dn / kXcds * kXcds : kXcds;
   se.record(0, s);
-  up_mfma_kernel<NT, DENSE><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list, plan,
-                                                                             hbuf);
+  up_mfma_kernel<NT, DENSE, SPLIT><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list,
+                                                                                    plan, hbuf, ks, sp.up_part);
+  if (SPLIT)
+    up_split_epilogue_kernel<<<dim3((unsigned)(units * la.E * rbs)), dim3(kBlock), 0, s>>>(
+        sp.up_part, gates, count, list, L, la.E, la.de, ks, hbuf);
   se.record(1, s);
-  down_mfma_kernel<NT, DENSE><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(la, units, L, count, list, plan,
-                                                                               hbuf, y);
+  down_mfma_kernel<NT, DENSE, SPLIT><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(
+      la, units, L, count, list, plan, hbuf, y, SPLIT ? sp.sp : 1, sp.down_part);
+  if (SPLIT)
+    down_split_combine_kernel<<<dim3((unsigned)(units * (la.d >> 6))), dim3(kBlock), 0, s>>>(sp.down_part, L, la.d,
+                                                                                          sp.sp, y);
   se.record(2, s);
   return hipGetLastError();
 }
@@ -365,17 +480,46 @@ bool forward_mfma_supported(int d, int de, int dtype) {
 
 size_t forward_mfma_plan_bytes(int64_t units) { return sizeof(int64_t) * (size_t)(units + 1); }
 
+bool chunk_split_factors(int d, int de, int64_t units, bool force, int* ks, int* sp) {
+  (void)de;
+  *ks = 1;
+  *sp = 1;
+  if (!force && (units < 1 || units > kChunkSplitMaxUnits)) return false;
+  // k-ranges of at least 4 steps (the ring keeps two steps in flight), up to 8
+  const int nsteps = d / kStepK;
+  while (*ks < 8 && nsteps % (2 * *ks) == 0 && nsteps / (2 * *ks) >= 4) *ks *= 2;
+  *sp = 8;
+  return true;
+}
+
+size_t chunk_split_part_bytes(int d, int de, int E, int64_t units, int chunk_len, int ks, int sp,
+                              size_t* down_offset) {
+  const size_t up = (size_t)units * E * (de >> 6) * ks * chunk_len * 64 * sizeof(float);
+  const size_t up_rounded = (up + 255) & ~size_t(255);
+  const size_t down = (size_t)units * (d >> 6) * sp * chunk_len * 64 * sizeof(float);
+  if (down_offset) *down_offset = up_rounded;
+  return up_rounded + ((down + 255) & ~size_t(255));
+}
+
 hipError_t launch_forward_mfma(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len,
                                const float* gates, const int32_t* count, const int32_t* list, bool dense,
-                               uint16_t* hbuf, int64_t* plan, float* y, const StageEvents& se, hipStream_t s) {
+                               uint16_t* hbuf, int64_t* plan, const ChunkSplit& sp, float* y,
+                               const StageEvents& se, hipStream_t s) {
   const int64_t units = n_tokens / chunk_len;
   if (units == 0) return hipSuccess;
   if (dense) {
-    if (chunk_len <= 16) return launch_nt<1, true>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, se, s);
-    return launch_nt<2, true>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, se, s);
+    if (chunk_len <= 16)
+      return launch_nt<1, true, false>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, sp, se, s);
+    return launch_nt<2, true, false>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, sp, se, s);
   }
-  if (chunk_len <= 16) return launch_nt<1, false>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, se, s);
-  return launch_nt<2, false>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, se, s);
+  if (sp.ks > 0) {
+    if (chunk_len <= 16)
+      return launch_nt<1, false, true>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, sp, se, s);
+    return launch_nt<2, false, true>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, sp, se, s);
+  }
+  if (chunk_len <= 16)
+    return launch_nt<1, false, false>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, sp, se, s);
+  return launch_nt<2, false, false>(la, x, units, chunk_len, gates, count, list, hbuf, plan, y, sp, se, s);
 }
 
 }  // namespace bffn

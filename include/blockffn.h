@@ -70,11 +70,13 @@ extern "C" {
 #define BLOCKFFN_BF16 1 /* bfloat16: the upper 16 bits of a binary32 */
 
 /* blockffn_forward modes. */
-#define BLOCKFFN_MODE_AUTO 0       /* CHUNK_MFMA where supported (bf16, d and d_expert % 128 == 0), else GEMV */
+#define BLOCKFFN_MODE_AUTO 0       /* CHUNK_SPLIT for at most 16 units, else CHUNK_MFMA, where supported (bf16, d and d_expert % 128 == 0); else GEMV */
 #define BLOCKFFN_MODE_GEMV 1       /* vector-ALU streaming of the active experts (any dtype) */
 #define BLOCKFFN_MODE_CHUNK_MFMA 2 /* matrix-core tiles over each chunk's union (bf16) */
 #define BLOCKFFN_MODE_GROUPED 3    /* token-expert pairs grouped by expert (bf16, d % 128 == 0, d_expert 128 or 256, one layer) */
 #define BLOCKFFN_MODE_DENSE 4      /* every expert on every token (the comparison path) */
+#define BLOCKFFN_MODE_CHUNK_SPLIT 5 /* CHUNK_MFMA with each unit's work cut finer (k ranges, union-slot ranges) and
+                                       summed in fixed order: a few units (latency) fill the GPU (bf16) */
 
 /* Status codes. */
 #define BLOCKFFN_OK 0

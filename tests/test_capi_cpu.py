@@ -205,6 +205,21 @@ def test_workspace_size(lib):
         T * 64 * 128 * 4 + r256(8 * (T + 1))
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 3, _capi.MODE_AUTO) == 0   # ragged
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, 99) == 0
+    # a few units: AUTO splits each unit's work (8 k-ranges of 4 steps, 8 slot ranges) and adds the
+    # fp32 partial tiles of the up items [C][E][d_e/64][8][L][64] and the down items [C][d/64][8][L][64]
+    C, L = 2, 8
+    split_ws = C * L * 64 * 128 * 2 + r256(8 * (C + 1)) + r256(C * 64 * 2 * 8 * L * 64 * 4) + \
+        r256(C * 32 * 8 * L * 64 * 4)
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_AUTO) == split_ws
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_CHUNK_SPLIT) == split_ws
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_CHUNK_MFMA) == \
+        C * L * 64 * 128 * 2 + r256(8 * (C + 1))
+    # 17 units: AUTO no longer splits
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), 17 * L, L, _capi.MODE_AUTO) == \
+        17 * L * 64 * 128 * 2 + r256(8 * 18)
+    # CHUNK_SPLIT needs the matrix-core shapes
+    f32 = _layer(d=2048, n_experts=64, d_expert=128, dtype=_capi.F32)
+    assert lib.blockffn_workspace_size(ctypes.byref(f32), C * L, L, _capi.MODE_CHUNK_SPLIT) == 0
 
 
 def _grads(**kw):

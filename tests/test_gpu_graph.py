@@ -39,7 +39,7 @@ def _snapshot(b):
     return {k: v.detach().cpu().clone() for k, v in b.items() if k != "ws"}
 
 
-@pytest.mark.parametrize("mode", ["auto", "grouped", "gemv"])
+@pytest.mark.parametrize("mode", ["auto", "grouped", "gemv", "chunk_split"])
 def test_forward_step_replays_match_eager(mode):
     d, E, de, L, C = 512, 64, 128, 8, 24
     rng = np.random.default_rng(801)

@@ -72,7 +72,7 @@ def test_every_mode_matches_oracle(name):
     xd = B.tokens_to_device(x, dl.dtype)
     modes = ["gemv", "dense"]
     if layer.dtype == "bf16" and layer.d % 128 == 0 and layer.d_expert % 128 == 0:
-        modes.append("chunk_mfma")
+        modes += ["chunk_mfma", "chunk_split"]
     z, g, m, um, cnt, lst = oracle_full(layer, x, L)
     y_ref = oracle.forward_dense(x, layer.w_in, layer.w_out, g)
     for mode in modes:

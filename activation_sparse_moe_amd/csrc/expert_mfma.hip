@@ -39,9 +39,15 @@ namespace {
 
 // Exclusive prefix over chunks of the up-projection item counts
 // (union size x row blocks, or E x row blocks in dense mode):
-// prefix[u] = items of chunks < u, prefix[n_units] = total.  One block.
+// prefix[u] = items of chunks < u, prefix[n_units] = total.  Then the down
+// kernel's XCD ranges: the down items (chunk, 64 output rows) in chunk-major
+// order start at step (U_u kbs + kb c_u) spe, with U_u the union sizes of
+// the chunks before u; bounds[k] = the number of items starting before step
+// k S / kXcds (S = all steps), the first item of XCD k's range.  One block.
 __global__ __launch_bounds__(1024) void plan_items_kernel(const int32_t* __restrict__ count, int64_t n_units,
-                                                          int dense_E, int per_slot, int64_t* __restrict__ prefix) {
+                                                          int dense_E, int per_slot, int kbs, int spe,
+                                                          int64_t* __restrict__ prefix,
+                                                          int64_t* __restrict__ bounds) {
   __shared__ int64_t part[1024];
   const int tid = threadIdx.x;
   const int64_t per = (n_units + 1023) / 1024;
@@ -57,11 +63,48 @@ __global__ __launch_bounds__(1024) void plan_items_kernel(const int32_t* __restr
     __syncthreads();
   }
   int64_t run = part[tid] - sum;
+  const int64_t total = part[1023];
   for (int64_t u = b; u < e; ++u) {
     prefix[u] = run * per_slot;
     run += dense_E ? dense_E : count[u];
   }
-  if (tid == 1023) prefix[n_units] = part[1023] * per_slot;
+  if (tid == 1023) prefix[n_units] = total * per_slot;
+  // XCD ranges of the down items
+  const int64_t S = total * kbs * spe;
+  int64_t below[kXcds - 1];  // items of this thread's chunks starting before step k S / kXcds
+#pragma unroll
+  for (int k = 0; k < kXcds - 1; ++k) below[k] = 0;
+  run = part[tid] - sum;
+  for (int64_t u = b; u < e; ++u) {
+    const int64_t c = dense_E ? dense_E : count[u];
+    const int64_t first = run * kbs * spe;  // step where chunk u's first item starts
+#pragma unroll
+    for (int k = 0; k < kXcds - 1; ++k) {
+      const int64_t q = (int64_t)(k + 1) * S / kXcds - first;
+      if (q <= 0) continue;
+      if (c == 0) {
+        below[k] += kbs;
+      } else {
+        const int64_t n = (q + c * spe - 1) / (c * spe);
+        below[k] += n < kbs ? n : kbs;
+      }
+    }
+    run += c;
+  }
+  for (int k = 0; k < kXcds - 1; ++k) {  // block sums in a fixed order
+    __syncthreads();
+    part[tid] = below[k];
+    __syncthreads();
+    for (int off = 512; off > 0; off >>= 1) {
+      if (tid < off) part[tid] += part[tid + off];
+      __syncthreads();
+    }
+    if (tid == 0) bounds[k + 1] = part[0];
+  }
+  if (tid == 0) {
+    bounds[0] = 0;
+    bounds[kXcds] = n_units * kbs;
+  }
 }
 
 
@@ -239,26 +282,9 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   const int d = la.d, de = la.de, E = la.E;
   const int spe = de / kStepK;   // steps per expert
   const int kbs = d >> 6;        // 64-row blocks per chunk
-  const int rbs = de >> 6;       // prefix[] counts union size x rbs
   uint8_t* bufs = lds + w * kRingBufs * G::kBufBytes;
 
-  // step index where item (u, kb) starts; union sizes before u are prefix[u] / rbs
   auto nact = [&](int64_t u) { return (int64_t)(DENSE ? E : count[u]); };
-  auto item_start = [&](int64_t u, int kb) { return (prefix[u] / rbs * kbs + kb * nact(u)) * spe; };
-  // first item (chunk-major order) whose start step is >= s: it lies in the
-  // first chunk whose last item starts at or after s (starts never decrease;
-  // chunks with an empty union share their start step)
-  auto first_item_at = [&](int64_t s) -> int64_t {
-    int64_t lo = 0, hi = n_units;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (item_start(mid, kbs - 1) >= s) hi = mid; else lo = mid + 1;
-    }
-    if (lo == n_units) return n_units * kbs;
-    int kb = 0;
-    while (item_start(lo, kb) < s) ++kb;  // stops before kbs
-    return lo * kbs + kb;
-  };
   // the block's items: its turns in its XCD's range, the items whose first
   // step falls in an equal share of all steps (the last range also takes
   // items starting at the very end).  Split items (few units) are shared
@@ -270,10 +296,8 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
     stride = 1;
     item_end = ((int64_t)blockIdx.x + 1) * total / gridDim.x;
   } else {
-    const int64_t S = prefix[n_units] / rbs * kbs * spe;
-    const XcdShare share = xcd_share([&](int k) {
-      return k == kXcds ? n_units * kbs : first_item_at((int64_t)k * S / kXcds);
-    });
+    const int64_t* bounds = prefix + n_units + 1;  // written by the plan kernel
+    const XcdShare share = xcd_share([&](int k) { return bounds[k]; });
     blk_lo = share.lo;
     stride = share.stride;
     item_end = share.end;
@@ -445,7 +469,8 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
                      const ChunkSplit& sp, const StageEvents& se, hipStream_t s) {
   const int rbs = la.de >> 6;
   const int ks = SPLIT ? sp.ks : 1;
-  plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, DENSE ? la.E : 0, rbs * ks, plan);
+  plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, DENSE ? la.E : 0, rbs * ks, la.d >> 6, rbs, plan,
+                                                   plan + units + 1);
   // persistent grids sized to the resident capacity (one block per CU at this LDS use)
   int64_t grid_up = 0, grid_dn = 0;
   hipError_t e =
@@ -478,7 +503,7 @@ bool forward_mfma_supported(int d, int de, int dtype) {
   return dtype == BLOCKFFN_BF16 && d % 128 == 0 && de % 128 == 0;
 }
 
-size_t forward_mfma_plan_bytes(int64_t units) { return sizeof(int64_t) * (size_t)(units + 1); }
+size_t forward_mfma_plan_bytes(int64_t units) { return sizeof(int64_t) * (size_t)(units + 1 + kXcds + 1); }
 
 bool chunk_split_factors(int d, int de, int64_t units, bool force, int* ks, int* sp) {
   (void)de;

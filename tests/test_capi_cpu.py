@@ -196,27 +196,28 @@ def test_workspace_size(lib):
     lay = _layer(d=2048, n_experts=64, d_expert=128)
     T = 4096
     r256 = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    # hidden activations (bf16 on the chunk path, fp32 on the GEMV path) + one int64 plan entry per chunk
+    # hidden activations (bf16 on the chunk path, fp32 on the GEMV path) + the plan: one int64 per
+    # chunk plus a total, and the down kernel's 8 + 1 XCD range bounds
+    plan = lambda C: r256(8 * (C + 1) + 8 * 9)  # noqa: E731
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, _capi.MODE_CHUNK_MFMA) == \
-        T * 64 * 128 * 2 + r256(8 * (T // 8 + 1))
+        T * 64 * 128 * 2 + plan(T // 8)
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 1, _capi.MODE_AUTO) == \
-        T * 64 * 128 * 2 + r256(8 * (T + 1))
+        T * 64 * 128 * 2 + plan(T)
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 1, _capi.MODE_GEMV) == \
-        T * 64 * 128 * 4 + r256(8 * (T + 1))
+        T * 64 * 128 * 4 + plan(T)
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 3, _capi.MODE_AUTO) == 0   # ragged
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, 99) == 0
     # a few units: AUTO splits each unit's work (8 k-ranges of 4 steps, 8 slot ranges) and adds the
     # fp32 partial tiles of the up items [C][E][d_e/64][8][L][64] and the down items [C][d/64][8][L][64]
     C, L = 2, 8
-    split_ws = C * L * 64 * 128 * 2 + r256(8 * (C + 1)) + r256(C * 64 * 2 * 8 * L * 64 * 4) + \
-        r256(C * 32 * 8 * L * 64 * 4)
+    split_ws = C * L * 64 * 128 * 2 + plan(C) + r256(C * 64 * 2 * 8 * L * 64 * 4) + r256(C * 32 * 8 * L * 64 * 4)
     assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_AUTO) == split_ws
     assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_CHUNK_SPLIT) == split_ws
     assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_CHUNK_MFMA) == \
-        C * L * 64 * 128 * 2 + r256(8 * (C + 1))
+        C * L * 64 * 128 * 2 + plan(C)
     # 17 units: AUTO no longer splits
     assert lib.blockffn_workspace_size(ctypes.byref(lay), 17 * L, L, _capi.MODE_AUTO) == \
-        17 * L * 64 * 128 * 2 + r256(8 * 18)
+        17 * L * 64 * 128 * 2 + plan(17)
     # CHUNK_SPLIT needs the matrix-core shapes
     f32 = _layer(d=2048, n_experts=64, d_expert=128, dtype=_capi.F32)
     assert lib.blockffn_workspace_size(ctypes.byref(f32), C * L, L, _capi.MODE_CHUNK_SPLIT) == 0

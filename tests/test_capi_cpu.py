@@ -197,8 +197,8 @@ def test_workspace_size(lib):
     T = 4096
     r256 = lambda v: (v + 255) // 256 * 256  # noqa: E731
     # hidden activations (bf16 on the chunk path, fp32 on the GEMV path) + the plan: one int64 per
-    # chunk plus a total, and the down kernel's 8 + 1 XCD range bounds
-    plan = lambda C: r256(8 * (C + 1) + 8 * 9)  # noqa: E731
+    # chunk plus a total, the down kernel's 8 + 1 XCD range bounds, and 1 + 8 u32 pool counters
+    plan = lambda C: r256(8 * (C + 1) + 8 * 9 + 4 * 9)  # noqa: E731
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, _capi.MODE_CHUNK_MFMA) == \
         T * 64 * 128 * 2 + plan(T // 8)
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 1, _capi.MODE_AUTO) == \

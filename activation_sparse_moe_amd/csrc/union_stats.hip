@@ -70,17 +70,20 @@ __global__ __launch_bounds__(kBlock) void chunk_union_kernel(int E, const uint64
   for (int p = n + lane; p < E; p += 64) lc[p] = -1;
 }
 
-__global__ __launch_bounds__(kBlock) void stats_kernel(int E, const uint64_t* __restrict__ masks, int64_t T,
-                                                       int L, blockffn_stats* __restrict__ out) {
+constexpr int kStatsThreads = 1024;  // one block; more threads = fewer dependent rounds of loads
+
+__global__ __launch_bounds__(kStatsThreads) void stats_kernel(int E, const uint64_t* __restrict__ masks, int64_t T,
+                                                              int L, blockffn_stats* __restrict__ out) {
+  constexpr int kWaves = kStatsThreads / kWave;
   __shared__ unsigned long long hist[129];
-  __shared__ unsigned long long part[4][4];
+  __shared__ unsigned long long part[kWaves][4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int W = (E + 63) >> 6;
   const uint64_t vb0 = valid_bits(E, 0), vb1 = valid_bits(E, 1);
-  for (int k = tid; k < 129; k += kBlock) hist[k] = 0;
+  for (int k = tid; k < 129; k += kStatsThreads) hist[k] = 0;
   __syncthreads();
   unsigned long long pairs = 0, rnum = 0, rden = 0, usum = 0;
-  for (int64_t t = tid; t < T; t += kBlock) {
+  for (int64_t t = tid; t < T; t += kStatsThreads) {
     const uint64_t a0 = masks[t * W] & vb0, a1 = W > 1 ? (masks[t * W + 1] & vb1) : 0ull;
     const int n = __popcll(a0) + __popcll(a1);
     pairs += n;
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(int E, const uint64_t* __
     }
   }
   const int64_t C = T / L;
-  for (int64_t c = tid; c < C; c += kBlock) {
+  for (int64_t c = tid; c < C; c += kStatsThreads) {
     uint64_t u0 = 0, u1 = 0;
     for (int64_t t = c * L; t < (c + 1) * L; ++t) {
       u0 |= masks[t * W];
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(int E, const uint64_t* __
   __syncthreads();
   if (tid == 0) {
     unsigned long long tot[4] = {0, 0, 0, 0};
-    for (int ww = 0; ww < 4; ++ww)
+    for (int ww = 0; ww < kWaves; ++ww)
       for (int q = 0; q < 4; ++q) tot[q] += part[ww][q];
     out->n_tokens = T;
     out->n_chunks = C;
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(int E, const uint64_t* __
     out->reuse_den = (int64_t)tot[2];
     out->union_sum = (int64_t)tot[3];
   }
-  for (int k = tid; k < 129; k += kBlock) out->hist[k] = (int64_t)hist[k];
+  for (int k = tid; k < 129; k += kStatsThreads) out->hist[k] = (int64_t)hist[k];
 }
 
 }  // namespace
@@ -141,7 +144,7 @@ hipError_t launch_chunk_union(int E, const uint64_t* masks, int64_t n_tokens, in
 
 hipError_t launch_stats(int E, const uint64_t* masks, int64_t n_tokens, int chunk_len, blockffn_stats* out,
                         hipStream_t s) {
-  stats_kernel<<<dim3(1), dim3(kBlock), 0, s>>>(E, masks, n_tokens, chunk_len, out);
+  stats_kernel<<<dim3(1), dim3(kStatsThreads), 0, s>>>(E, masks, n_tokens, chunk_len, out);
   return hipGetLastError();
 }
 

@@ -333,7 +333,9 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
     blk_lo = (int64_t)blockIdx.x * total / gridDim.x;
     stride = 1;
     item_end = ((int64_t)blockIdx.x + 1) * total / gridDim.x;
-  } else {  // the static part of the XCD's range, before its pool
+  } else {  // the static part of the XCD's range, before its pool: block j of the XCD takes
+            // the range's items j, j + (blocks per XCD), ..., so the XCD's waves work on
+            // neighbouring items, whose chunks' hidden rows stay in its L2
     const int64_t lo = bounds[xcd], hi = bounds[xcd + 1];
     blk_lo = lo + (int64_t)blockIdx.x / kXcds;
     stride = gridDim.x / kXcds;  // the grid is a multiple of kXcds

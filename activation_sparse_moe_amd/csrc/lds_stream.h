@@ -118,24 +118,6 @@ __device__ __forceinline__ int64_t take_item(unsigned* counter, int64_t lo, int6
   return lo + stride * (int64_t)__builtin_amdgcn_readfirstlane(__shfl(v, 0, kWave));
 }
 
-// A block's share of the items [0, n) of a persistent launch: the items are
-// split into one contiguous range per XCD (by `split`, which maps a fraction
-// k / kXcds of the work to an item index), and the blocks of an XCD take
-// that range's items in turn (block j of the XCD: range start + j, + per_xcd,
-// ...).  The XCD's waves then work on neighbouring items at any time: items
-// of one chunk share that chunk's token rows, which stay in the XCD's L2.
-struct XcdShare {
-  int64_t lo, stride, end;
-};
-template <typename Split>
-__device__ __forceinline__ XcdShare xcd_share(Split split) {
-  const int64_t per_xcd = gridDim.x / kXcds;  // the grid is a multiple of kXcds
-  const int xcd = (int)(blockIdx.x % kXcds);
-  const int64_t j = blockIdx.x / kXcds;
-  const int64_t lo = split(xcd), hi = split(xcd + 1);
-  return XcdShare{lo + j, per_xcd, hi};
-}
-
 template <int NT>
 __device__ __forceinline__ void ring_zero(f32x4 (&acc)[4][NT]) {
 #pragma unroll

@@ -46,50 +46,81 @@
 namespace bffn {
 namespace {
 
+// 64-bit wave shuffles, as two 32-bit halves.
+__device__ __forceinline__ int64_t shfl_up64(int64_t v, int off) {
+  const uint32_t lo = __shfl_up((uint32_t)v, off, kWave), hi = __shfl_up((uint32_t)((uint64_t)v >> 32), off, kWave);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)((uint64_t)v >> 32), off, kWave);
+    v += (int64_t)(((uint64_t)hi << 32) | lo);
+  }
+  return v;
+}
+
+constexpr int kPlanMaxThreads = 1024;
+
 // Exclusive prefix over chunks of the up-projection item counts
 // (union size x row blocks, or E x row blocks in dense mode):
 // prefix[u] = items of chunks < u, prefix[n_units] = total.  Then the down
 // kernel's XCD ranges: the down items (chunk, 64 output rows) in chunk-major
 // order start at step (U_u kbs + kb c_u) spe, with U_u the union sizes of
 // the chunks before u; bounds[k] = the number of items starting before step
-// k S / kXcds (S = all steps), the first item of XCD k's range.  One block.
-__global__ __launch_bounds__(1024) void plan_items_kernel(const int32_t* __restrict__ count, int64_t n_units,
-                                                          int dense_E, int per_slot, int kbs, int spe,
-                                                          int64_t* __restrict__ prefix,
-                                                          int64_t* __restrict__ bounds) {
-  __shared__ int64_t part[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = (n_units + 1023) / 1024;
+// k S / kXcds (S = all steps), the first item of XCD k's range.  One block of
+// 64 to 1024 threads; each thread owns a run of consecutive chunks.  Scans
+// and sums go through wave shuffles and one LDS exchange each, so the block
+// meets at two barriers (this is on a single chunk's critical path).
+__global__ __launch_bounds__(kPlanMaxThreads) void plan_items_kernel(const int32_t* __restrict__ count,
+                                                                     int64_t n_units, int dense_E, int per_slot,
+                                                                     int kbs, int spe,
+                                                                     int64_t* __restrict__ prefix,
+                                                                     int64_t* __restrict__ bounds) {
+  constexpr int kMaxWaves = kPlanMaxThreads / kWave;
+  __shared__ int64_t wave_tot[kMaxWaves];
+  __shared__ int64_t wave_below[kXcds - 1][kMaxWaves];
+  const int nth = blockDim.x, waves = nth / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int64_t per = (n_units + nth - 1) / nth;
   const int64_t b = tid * per, e = b + per < n_units ? b + per : n_units;
   int64_t sum = 0;
   for (int64_t u = b; u < e; ++u) sum += dense_E ? dense_E : count[u];
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-    const int64_t v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // inclusive scan in the wave, then the totals of the waves before this one
+  int64_t inc = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int64_t v = shfl_up64(inc, off);
+    if (lane >= off) inc += v;
   }
-  int64_t run = part[tid] - sum;
-  const int64_t total = part[1023];
+  if (lane == kWave - 1) wave_tot[w] = inc;
+  __syncthreads();
+  int64_t first = inc - sum, total = 0;
+  for (int j = 0; j < waves; ++j) {
+    const int64_t t = wave_tot[j];
+    if (j < w) first += t;
+    total += t;
+  }
+  int64_t run = first;
   for (int64_t u = b; u < e; ++u) {
     prefix[u] = run * per_slot;
     run += dense_E ? dense_E : count[u];
   }
-  if (tid == 1023) prefix[n_units] = total * per_slot;
+  if (tid == 0) prefix[n_units] = total * per_slot;
   // XCD ranges of the down items
   const int64_t S = total * kbs * spe;
   int64_t below[kXcds - 1];  // items of this thread's chunks starting before step k S / kXcds
 #pragma unroll
   for (int k = 0; k < kXcds - 1; ++k) below[k] = 0;
-  run = part[tid] - sum;
+  run = first;
   for (int64_t u = b; u < e; ++u) {
     const int64_t c = dense_E ? dense_E : count[u];
-    const int64_t first = run * kbs * spe;  // step where chunk u's first item starts
+    const int64_t first_step = run * kbs * spe;  // step where chunk u's first item starts
 #pragma unroll
     for (int k = 0; k < kXcds - 1; ++k) {
-      const int64_t q = (int64_t)(k + 1) * S / kXcds - first;
+      const int64_t q = (int64_t)(k + 1) * S / kXcds - first_step;
       if (q <= 0) continue;
       if (c == 0) {
         below[k] += kbs;
@@ -100,15 +131,16 @@ __global__ __launch_bounds__(1024) void plan_items_kernel(const int32_t* __restr
     }
     run += c;
   }
-  for (int k = 0; k < kXcds - 1; ++k) {  // block sums in a fixed order
-    __syncthreads();
-    part[tid] = below[k];
-    __syncthreads();
-    for (int off = 512; off > 0; off >>= 1) {
-      if (tid < off) part[tid] += part[tid + off];
-      __syncthreads();
-    }
-    if (tid == 0) bounds[k + 1] = part[0];
+#pragma unroll
+  for (int k = 0; k < kXcds - 1; ++k) {
+    const int64_t v = wave_sum64(below[k]);
+    if (lane == 0) wave_below[k][w] = v;
+  }
+  __syncthreads();
+  if (tid < kXcds - 1) {
+    int64_t v = 0;
+    for (int j = 0; j < waves; ++j) v += wave_below[tid][j];
+    bounds[tid + 1] = v;
   }
   if (tid == 0) {
     bounds[0] = 0;
@@ -522,8 +554,10 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
                      const ChunkSplit& sp, const StageEvents& se, hipStream_t s) {
   const int rbs = la.de >> 6;
   const int ks = SPLIT ? sp.ks : 1;
-  plan_items_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, units, DENSE ? la.E : 0, rbs * ks, la.d >> 6, rbs, plan,
-                                                   plan + units + 1);
+  // one thread per chunk up to the block's maximum (whole waves)
+  const int plan_threads = units < kPlanMaxThreads ? (int)((units + kWave - 1) / kWave * kWave) : kPlanMaxThreads;
+  plan_items_kernel<<<dim3(1), dim3((unsigned)plan_threads), 0, s>>>(count, units, DENSE ? la.E : 0, rbs * ks,
+                                                                     la.d >> 6, rbs, plan, plan + units + 1);
   // persistent grids sized to the resident capacity (one block per CU at this LDS use)
   int64_t grid_up = 0, grid_dn = 0;
   hipError_t e =

@@ -70,36 +70,67 @@ __global__ __launch_bounds__(kBlock) void chunk_union_kernel(int E, const uint64
   for (int p = n + lane; p < E; p += 64) lc[p] = -1;
 }
 
-constexpr int kStatsThreads = 1024;  // one block; more threads = fewer dependent rounds of loads
+constexpr int kStatsMaxThreads = 1024;
+constexpr int kStatsTokensPerRound = 4;  // tokens per thread and round, their loads issued together
+constexpr int kStatsChunkBatch = 8;      // a chunk's token words loaded together
 
-__global__ __launch_bounds__(kStatsThreads) void stats_kernel(int E, const uint64_t* __restrict__ masks, int64_t T,
-                                                              int L, blockffn_stats* __restrict__ out) {
-  constexpr int kWaves = kStatsThreads / kWave;
+// One block of 64 to 1024 threads (sized to the tokens).  Every round issues
+// all its loads before using any, so a thread waits for memory once per
+// round instead of once per token.
+__global__ __launch_bounds__(kStatsMaxThreads) void stats_kernel(int E, const uint64_t* __restrict__ masks,
+                                                                 int64_t T, int L,
+                                                                 blockffn_stats* __restrict__ out) {
+  constexpr int kMaxWaves = kStatsMaxThreads / kWave;
   __shared__ unsigned long long hist[129];
-  __shared__ unsigned long long part[kWaves][4];
+  __shared__ unsigned long long part[kMaxWaves][4];
+  const int nth = blockDim.x, waves = nth / kWave;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int W = (E + 63) >> 6;
+  const int hw = W - 1;  // the high word; with one word it repeats word 0, which vb1 = 0 masks out
   const uint64_t vb0 = valid_bits(E, 0), vb1 = valid_bits(E, 1);
-  for (int k = tid; k < 129; k += kStatsThreads) hist[k] = 0;
+  for (int k = tid; k < 129; k += nth) hist[k] = 0;
   __syncthreads();
   unsigned long long pairs = 0, rnum = 0, rden = 0, usum = 0;
-  for (int64_t t = tid; t < T; t += kStatsThreads) {
-    const uint64_t a0 = masks[t * W] & vb0, a1 = W > 1 ? (masks[t * W + 1] & vb1) : 0ull;
-    const int n = __popcll(a0) + __popcll(a1);
-    pairs += n;
-    atomicAdd(&hist[n], 1ull);
-    if (t >= 1) {
-      const uint64_t p0 = masks[(t - 1) * W] & vb0, p1 = W > 1 ? (masks[(t - 1) * W + 1] & vb1) : 0ull;
-      rnum += __popcll(a0 & p0) + __popcll(a1 & p1);
-      rden += __popcll(p0) + __popcll(p1);
+  for (int64_t t0 = tid; t0 < T; t0 += (int64_t)kStatsTokensPerRound * nth) {
+    uint64_t a0[kStatsTokensPerRound], a1[kStatsTokensPerRound], p0[kStatsTokensPerRound],
+        p1[kStatsTokensPerRound];
+#pragma unroll
+    for (int j = 0; j < kStatsTokensPerRound; ++j) {
+      const int64_t t = t0 + (int64_t)j * nth;
+      const bool v = t < T, vp = v && t >= 1;
+      a0[j] = v ? masks[t * W] : 0ull;
+      a1[j] = v ? masks[t * W + hw] : 0ull;
+      p0[j] = vp ? masks[(t - 1) * W] : 0ull;  // no previous token for t = 0: no reuse terms
+      p1[j] = vp ? masks[(t - 1) * W + hw] : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kStatsTokensPerRound; ++j) {
+      if (t0 + (int64_t)j * nth >= T) continue;
+      const uint64_t x0 = a0[j] & vb0, x1 = a1[j] & vb1, q0 = p0[j] & vb0, q1 = p1[j] & vb1;
+      const int n = __popcll(x0) + __popcll(x1);
+      pairs += n;
+      atomicAdd(&hist[n], 1ull);
+      rnum += __popcll(x0 & q0) + __popcll(x1 & q1);
+      rden += __popcll(q0) + __popcll(q1);
     }
   }
   const int64_t C = T / L;
-  for (int64_t c = tid; c < C; c += kStatsThreads) {
+  for (int64_t c = tid; c < C; c += nth) {
     uint64_t u0 = 0, u1 = 0;
-    for (int64_t t = c * L; t < (c + 1) * L; ++t) {
-      u0 |= masks[t * W];
-      if (W > 1) u1 |= masks[t * W + 1];
+    const uint64_t* mc = masks + c * L * W;
+    for (int i0 = 0; i0 < L; i0 += kStatsChunkBatch) {
+      uint64_t m0[kStatsChunkBatch], m1[kStatsChunkBatch];
+#pragma unroll
+      for (int j = 0; j < kStatsChunkBatch; ++j) {
+        const bool v = i0 + j < L;
+        m0[j] = v ? mc[(int64_t)(i0 + j) * W] : 0ull;
+        m1[j] = v ? mc[(int64_t)(i0 + j) * W + hw] : 0ull;
+      }
+#pragma unroll
+      for (int j = 0; j < kStatsChunkBatch; ++j) {
+        u0 |= m0[j];
+        u1 |= m1[j];
+      }
     }
     usum += __popcll(u0 & vb0) + __popcll(u1 & vb1);
   }
@@ -117,7 +148,7 @@ __global__ __launch_bounds__(kStatsThreads) void stats_kernel(int E, const uint6
   __syncthreads();
   if (tid == 0) {
     unsigned long long tot[4] = {0, 0, 0, 0};
-    for (int ww = 0; ww < kWaves; ++ww)
+    for (int ww = 0; ww < waves; ++ww)
       for (int q = 0; q < 4; ++q) tot[q] += part[ww][q];
     out->n_tokens = T;
     out->n_chunks = C;
@@ -128,7 +159,7 @@ __global__ __launch_bounds__(kStatsThreads) void stats_kernel(int E, const uint6
     out->reuse_den = (int64_t)tot[2];
     out->union_sum = (int64_t)tot[3];
   }
-  for (int k = tid; k < 129; k += kStatsThreads) out->hist[k] = (int64_t)hist[k];
+  for (int k = tid; k < 129; k += nth) out->hist[k] = (int64_t)hist[k];
 }
 
 }  // namespace
@@ -144,7 +175,10 @@ hipError_t launch_chunk_union(int E, const uint64_t* masks, int64_t n_tokens, in
 
 hipError_t launch_stats(int E, const uint64_t* masks, int64_t n_tokens, int chunk_len, blockffn_stats* out,
                         hipStream_t s) {
-  stats_kernel<<<dim3(1), dim3(kStatsThreads), 0, s>>>(E, masks, n_tokens, chunk_len, out);
+  // a thread per kStatsTokensPerRound tokens, whole waves, 64 to 1024 threads
+  const int64_t waves = (n_tokens + kStatsTokensPerRound * kWave - 1) / (kStatsTokensPerRound * kWave);
+  const int threads = waves >= kStatsMaxThreads / kWave ? kStatsMaxThreads : waves < 1 ? kWave : (int)waves * kWave;
+  stats_kernel<<<dim3(1), dim3((unsigned)threads), 0, s>>>(E, masks, n_tokens, chunk_len, out);
   return hipGetLastError();
 }
 

@@ -69,10 +69,10 @@ __global__ __launch_bounds__(kBlock) void bwd_prep_kernel(const float* __restric
     const f32x4 v0 = *reinterpret_cast<const f32x4*>(dy + t * d + c);
     const f32x4 v1 = *reinterpret_cast<const f32x4*>(dy + t * d + c + 4);
     u32x4 o;
-    o[0] = f32_to_bf16(v0[0]) | (f32_to_bf16(v0[1]) << 16);
-    o[1] = f32_to_bf16(v0[2]) | (f32_to_bf16(v0[3]) << 16);
-    o[2] = f32_to_bf16(v1[0]) | (f32_to_bf16(v1[1]) << 16);
-    o[3] = f32_to_bf16(v1[2]) | (f32_to_bf16(v1[3]) << 16);
+    o[0] = pack2_bf16(v0[0], v0[1]);
+    o[1] = pack2_bf16(v0[2], v0[3]);
+    o[2] = pack2_bf16(v1[0], v1[1]);
+    o[3] = pack2_bf16(v1[2], v1[3]);
     *reinterpret_cast<u32x4*>(dyb + t * d + c) = o;
   }
 }
@@ -562,7 +562,7 @@ struct BwdLayout {
   int64_t *pair_off, *tile_up, *all_off;
   int32_t *pair_tok, *pair_idx;
   float *pair_gate, *g_b, *r_b, *dgp, *dz, *dsc, *wr_part;
-  uint16_t *dyb, *w_inT, *w_outT, *du, *hg, *dzb, *part, *trash;
+  uint16_t *dyb, *w_inT, *w_outT, *du, *hg, *dzb, *part;
   size_t bytes;
 };
 
@@ -597,7 +597,6 @@ BwdLayout bwd_layout(char* base, int64_t T, int E, int d, int de) {
   L.dsc = reinterpret_cast<float*>(take(4 * P));
   L.dzb = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * kRouterPad));
   L.part = reinterpret_cast<uint16_t*>(take(2 * P * d));
-  L.trash = reinterpret_cast<uint16_t*>(take(kTrashBytes));
   L.bytes = off;
   return L;
 }
@@ -636,8 +635,8 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   hipError_t e = persistent_grid(bwd_pair_kernel, max_up_tiles, &grid_pair);
   if (e == hipSuccess) e = persistent_grid(tgemm_kernel, (int64_t)E * (d / TBM) * (de / TBN), &grid_t);
   if (e == hipSuccess)
-    e = de == 128 ? persistent_grid(grouped_down_kernel<128>, (int64_t)E * (d / GBN), &grid_dn)
-                  : persistent_grid(grouped_down_kernel<256>, (int64_t)E * (d / GBN), &grid_dn);
+    e = de == 128 ? persistent_grid(grouped_down_kernel<128>, down_blocks(E, d, de), &grid_dn)
+                  : persistent_grid(grouped_down_kernel<256>, down_blocks(E, d, de), &grid_dn);
   if (e != hipSuccess) return e;
 
   se.record(1, s);
@@ -661,7 +660,7 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
       L.wr_part, (int64_t)E * d, d_w_router);
   se.record(3, s);
   // dx: per-pair dU W_in[i] rows (the forward's down GEMM on W_in^T), then the per-token sum
-  DownArgs dn{L.du, L.w_inT, L.pair_off, L.part, L.trash, d, E};
+  DownArgs dn{L.du, L.w_inT, L.pair_off, L.part, d, E};
   if (de == 128)
     grouped_down_kernel<128><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
   else

@@ -9,6 +9,8 @@
 namespace bffn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -40,13 +42,15 @@ __device__ __forceinline__ P layer_ptr(P p, int64_t stride, int64_t unit, int n_
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// fp32 -> bf16 through gfx950's packed conversion (v_cvt_pk_bf16_f32):
+// round to nearest even, denormals kept, NaN stays NaN.  One instruction
+// per pair instead of a rounding sequence per value, which matters in MFMA
+// epilogues.  pack2_bf16 puts `lo` in bits 0-15.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack2_bf16(f, 0.f) & 0xffffu; }
 
 // Swish with beta = 1 (SiLU): u * logistic(u).
 __device__ __forceinline__ float swish(float u) { return u / (1.0f + __expf(-u)); }

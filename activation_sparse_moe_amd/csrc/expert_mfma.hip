@@ -316,8 +316,8 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const f32x4 v = acc[s][tl];
-        const uint32_t lo = f32_to_bf16(gv * swish(v[0])) | (f32_to_bf16(gv * swish(v[1])) << 16);
-        const uint32_t hi = f32_to_bf16(gv * swish(v[2])) | (f32_to_bf16(gv * swish(v[3])) << 16);
+        const uint32_t lo = pack2_bf16(gv * swish(v[0]), gv * swish(v[1]));
+        const uint32_t hi = pack2_bf16(gv * swish(v[2]), gv * swish(v[3]));
         *reinterpret_cast<u32x2*>(hrow + s * 16) = u32x2{lo, hi};
       }
     }

@@ -15,13 +15,13 @@ bool grouped_supported(int d, int de, int dtype) {
 }
 
 // Workspace: per-block slots, offsets, pair arrays (capacity T*E pairs),
-// pair_idx, hidden and partial rows, and the down kernel's trash area.
+// pair_idx, hidden and partial rows.
 size_t grouped_workspace_bytes(int64_t T, int E, int d, int de) {
   const size_t P = (size_t)T * E;
   const size_t rows = (size_t)plan_rows(T);
   const size_t nblk = ((size_t)T + rows - 1) / rows;
   return r256(4 * nblk * E) + 2 * r256(sizeof(int64_t) * (E + 1)) + r256(4 * P) + r256(4 * P) + r256(4 * P) +
-         r256(2 * P * de) + r256(2 * P * d) + kTrashBytes;
+         r256(2 * P * de) + r256(2 * P * d);
 }
 
 hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_t T, const float* gates,
@@ -45,7 +45,6 @@ hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_
   int32_t* pair_idx = reinterpret_cast<int32_t*>(take(4 * P));
   uint16_t* hid = reinterpret_cast<uint16_t*>(take(2 * P * de));
   uint16_t* part = reinterpret_cast<uint16_t*>(take(2 * P * d));
-  uint16_t* trash = reinterpret_cast<uint16_t*>(take(kTrashBytes));
 
   group_count_kernel<PairRule::kNonZero><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(gates, T, E, rows, blk);
   group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(blk, nblk, E, de / GBN, pair_off, tile_up);
@@ -54,19 +53,18 @@ hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_
   // upper bounds of the work (every pair active) cap the grids; the kernels
   // read the exact totals on the device
   const int64_t max_up_tiles = (int64_t)E * ((T + GBM - 1) / GBM) * (de / GBN);
-  const int64_t down_items = (int64_t)E * (d / GBN);
   int64_t grid_up = 0, grid_dn = 0;
   hipError_t e = persistent_grid(grouped_up_kernel, max_up_tiles, &grid_up);
   if (e == hipSuccess)
-    e = de == 128 ? persistent_grid(grouped_down_kernel<128>, down_items, &grid_dn)
-                  : persistent_grid(grouped_down_kernel<256>, down_items, &grid_dn);
+    e = de == 128 ? persistent_grid(grouped_down_kernel<128>, down_blocks(E, d, de), &grid_dn)
+                  : persistent_grid(grouped_down_kernel<256>, down_blocks(E, d, de), &grid_dn);
   if (e != hipSuccess) return e;
 
   se.record(0, s);
   UpArgs up{x, pair_tok, pair_gate, static_cast<const uint16_t*>(la.w_in), pair_off, tile_up, hid, d, de, E};
   grouped_up_kernel<<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(up);
   se.record(1, s);
-  DownArgs dn{hid, static_cast<const uint16_t*>(la.w_out), pair_off, part, trash, d, E};
+  DownArgs dn{hid, static_cast<const uint16_t*>(la.w_out), pair_off, part, d, E};
   if (de == 128)
     grouped_down_kernel<128><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
   else

@@ -18,16 +18,17 @@
 //            every non-zero gate; the backward every active pair)
 //   up:      H'[p] = g_p * Swish(x[t_p] W_in[i]^T), bf16, grouped GEMM with
 //            gathered token rows (64 pairs x 128 hidden x 64 k tiles)
-//   down:    Part[p] = H'[p] W_out[i]^T, bf16 per-pair partial rows; a block
-//            keeps one 128-row slab of W_out[i] in LDS and runs it over all
-//            of expert i's pairs
+//   down:    Part[p] = H'[p] W_out[i]^T, bf16 per-pair partial rows; each
+//            wave keeps one 64-row slab of W_out[i] in registers and runs it
+//            over all of expert i's pairs, read from block-shared LDS tiles
 //   combine: y[t] = sum over the token's experts in ascending order of
 //            Part[pair_idx[t][i]], fp32 (no atomics; deterministic)
 //
-// MFMA tiles use v_mfma_f32_16x16x32_bf16 on 256 threads (2 x 2 waves of
-// 32 x 64).  Global rows are moved as 16-byte chunks and written to LDS with
-// the chunk index XOR-swizzled by row, so that the 16 rows an MFMA operand
-// read touches land in different banks.  Output tiles are staged in LDS and
+// The up GEMM's MFMA tiles (v_mfma_f32_16x16x32_bf16) use 256 threads as
+// 2 x 2 waves of 32 x 64; its global rows are moved as 16-byte chunks and
+// written to LDS with the chunk index XOR-swizzled by row, so that the 16
+// rows an MFMA operand read touches land in different banks (the down GEMM
+// stages its hidden rows the same way).  Output tiles are staged in LDS and
 // stored as whole 16-byte chunks of each row.
 #pragma once
 
@@ -40,7 +41,6 @@ constexpr int GBM = 64, GBN = 128, GBK = 64;
 constexpr int kPlanThreads = 128;     // one thread per expert (E <= 128)
 constexpr int kPlanMaxBlocks = 512;   // token blocks of the count / fill kernels
 constexpr int kPlanMinRows = 32;      // tokens per block at least (short scans)
-constexpr size_t kTrashBytes = GBM * 256;  // one staged output tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kPlanThreads) void group_fill_kernel(const float* _
 // so D = W . X^T: lane (m, g) of a 16 x 16 tile holds outputs 4 g .. 4 g + 3
 // of pair m, four consecutive row elements that it packs into 8 bytes.
 __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
-  return u32x2{f32_to_bf16(a) | (f32_to_bf16(b) << 16), f32_to_bf16(c) | (f32_to_bf16(d) << 16)};
+  return u32x2{pack2_bf16(a, b), pack2_bf16(c, d)};
 }
 
 // ---- up: H'[p][n] = g_p Swish(sum_k x[tok(p)][k] W_in[i][n][k]) ----
@@ -348,139 +348,171 @@ struct DownArgs {
   const uint16_t* w;          // [E][N][K]
   const int64_t* pair_off;    // [E + 1]
   uint16_t* part;             // [P][N]
-  uint16_t* trash;            // 16 KiB that is written and never read
   int N, E;
 };
 
-// A work item is (expert i, 128-row slab of W_out[i]); the slab sits in LDS
-// while the block runs every 64-pair tile of the expert through it, with the
-// next tile's hidden rows loaded into registers during this tile's MFMAs.
+// Output columns of one wave in the down GEMM: its slab of W (SN rows x K)
+// lives in 64 VGPRs per lane for the whole work item.
+template <int K>
+constexpr int down_slab() {
+  return K == 128 ? 64 : 32;
+}
+constexpr int kDownPairs = 32;  // pairs per tile: two 16-pair MFMA groups
+constexpr int kDownWaves = kBlock / kWave;
+
+// Blocks that cover every down item once (the last group of an expert may
+// be partial: N is a multiple of 128 only).
+int64_t down_blocks(int E, int N, int K) {
+  const int cols = kDownWaves * (K == 128 ? down_slab<128>() : down_slab<256>());
+  return (int64_t)E * ((N + cols - 1) / cols);
+}
+
+// Byte offset of 16-byte chunk c of row r in a wave's staged output tile of
+// RB-byte rows: the XOR spreads the 16 rows that one MFMA group writes over
+// distinct bank groups (two rows per 256 bytes at RB = 128, four at RB = 64).
+template <int RB>
+__device__ __forceinline__ int stage_off(int r, int c) {
+  static_assert(RB == 128 || RB == 64, "staged row size");
+  const int f = RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+  return r * RB + ((c ^ f) << 4);
+}
+
+// A work item is (expert i, kDownWaves slabs of SN columns of W[i]); wave w
+// takes slab w and holds it in the MFMA A-operand layout for all of expert
+// i's pairs.  Each 32-pair tile of hidden rows is loaded once by the block
+// with whole-row (coalesced) loads into a double-buffered LDS tile, the
+// next tile's loads in flight during this tile's MFMAs; every wave reads the
+// B operands from there.  Each wave writes its output through a private LDS
+// stage as whole row segments (plain stores: the L2 acknowledges them sooner
+// than non-temporal ones, and later waits include them).  Past the end of a
+// group, hidden loads and output stores repeat the group's last pair (the
+// same bytes again), so every path issues the same number of memory
+// operations and the compiler's waits stay partial.
 template <int K>
 __global__ __launch_bounds__(kBlock) void grouped_down_kernel(DownArgs da) {
-  constexpr int RB = K * 2;                       // bytes per LDS row
-  constexpr int kRowChunks = K / 8;               // 16-byte chunks per row
-  constexpr int kBChunks = GBN * kRowChunks / kBlock;  // per thread
-  constexpr int kAChunks = GBM * kRowChunks / kBlock;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[GBN * RB];     // weight slab
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][GBM * RB];  // hidden rows
-  __shared__ __attribute__((aligned(16))) uint8_t lds_c[GBM * 256];    // output tile, bf16
+  constexpr int SN = down_slab<K>();
+  constexpr int NB = SN / 16;                       // 16-column MFMA stripes
+  constexpr int KK = K / 32;                        // 32-deep MFMA steps
+  constexpr int RB = SN * 2;                        // bytes per staged output row
+  constexpr int CPR = RB / 16;                      // 16-byte chunks per staged row
+  constexpr int RPI = kWave / CPR;                  // staged rows per store instruction
+  constexpr int HB = K * 2;                         // bytes per hidden row
+  constexpr int HC = HB / 16;                       // 16-byte chunks per hidden row
+  constexpr int HL = kDownPairs * HC / kBlock;      // hidden-tile loads per thread
+  __shared__ __attribute__((aligned(16))) uint8_t htile[2][kDownPairs * HB];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kDownWaves][kDownPairs * RB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
   const int m = lane & 15, g = lane >> 4;
   const int N = da.N, E = da.E;
-  const int n_slabs = N / GBN;
-  const int64_t total = (int64_t)E * n_slabs;
-  const int64_t nb = gridDim.x;
-  const int64_t per_xcd_blocks = nb / kXcds;
+  const int groups = (N + SN * kDownWaves - 1) / (SN * kDownWaves);
+  const int64_t total = (int64_t)E * groups;
+  // XCD-aware: XCD k walks one contiguous range of items (expert-major), so
+  // the blocks reading an expert's hidden rows share an L2.
+  const int64_t per_xcd_blocks = gridDim.x / kXcds;
   const int xcd = (int)(blockIdx.x % kXcds);
   const int64_t local = blockIdx.x / kXcds;
   const int64_t span = (total + kXcds - 1) / kXcds;
   const int64_t it_begin = xcd * span, it_end = it_begin + span < total ? it_begin + span : total;
+  uint8_t* st = stage[w];
 
   for (int64_t it = it_begin + local; it < it_end; it += per_xcd_blocks) {
-    const int i = (int)(it / n_slabs), n0 = (int)(it % n_slabs) * GBN;
+    const int i = (int)(it / groups), grp = (int)(it % groups);
+    const int n0 = (grp * kDownWaves + w) * SN;
+    const bool has_slab = n0 < N;  // false only for waves past the end of a partial group
     const int64_t p0 = da.pair_off[i];
     const int n_i = (int)(da.pair_off[i + 1] - p0);
-    if (n_i == 0) continue;
-    const int m_tiles = (n_i + GBM - 1) / GBM;
-
-    {  // the W_out slab: rows n0 .. n0 + 127 of expert i
-      u32x4 rb[kBChunks];
+    if (n_i == 0) continue;  // (uniform over the block)
+    const int tiles = (n_i + kDownPairs - 1) / kDownPairs;
+    // The expert's blocks run at the same time; each starts at its own tile
+    // (and wraps), so they do not all read the same hidden rows at once.
+    const int rot = (int)((int64_t)grp * tiles / groups);
+    auto phys = [&](int t) { return t + rot < tiles ? t + rot : t + rot - tiles; };
+    // the slab: lane (m, g) holds row n0 + 16 b + m, elements 32 kk + 8 g .. +7
+    u32x4 wa[NB][KK];
 #pragma unroll
-      for (int j = 0; j < kBChunks; ++j) {
-        const int c = tid + j * kBlock, r = c / kRowChunks, ch = c % kRowChunks;
-        rb[j] = *reinterpret_cast<const u32x4*>(da.w + ((int64_t)i * N + n0 + r) * K + ch * 8);
-      }
+    for (int b = 0; b < NB; ++b) {
+      const uint16_t* src = da.w + ((int64_t)i * N + (has_slab ? n0 : 0) + 16 * b + m) * K + 8 * g;
 #pragma unroll
-      for (int j = 0; j < kBChunks; ++j) {
-        const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_b[lds_off<RB>(c / kRowChunks, c % kRowChunks)]) = rb[j];
-      }
+      for (int kk = 0; kk < KK; ++kk) wa[b][kk] = *reinterpret_cast<const u32x4*>(src + 32 * kk);
     }
-    // Hidden rows of a tile travel global -> registers -> LDS.  Two register
-    // sets alternate so that the loads of tile mt + 1 are issued a whole tile
-    // before they are written to LDS, ahead of tile mt - 1's stores (a wait
-    // on them then never waits on those stores).
-    auto aload = [&](u32x4 (&regs)[kAChunks], int mt) {
+    // hidden tile pt: thread chunk c = tid + j kBlock is row c / HC, chunk c % HC
+    u32x4 hr[HL];
+    auto hload = [&](int pt) {
 #pragma unroll
-      for (int j = 0; j < kAChunks; ++j) {
-        const int c = tid + j * kBlock, r = c / kRowChunks, ch = c % kRowChunks;
-        const int pr = mt * GBM + r < n_i ? mt * GBM + r : n_i - 1;  // rows past the group repeat a valid row
-        regs[j] = *reinterpret_cast<const u32x4*>(da.hid + (p0 + pr) * K + ch * 8);
+      for (int j = 0; j < HL; ++j) {
+        const int c = tid + j * kBlock, r = c / HC;
+        const int pr = pt * kDownPairs + r < n_i ? pt * kDownPairs + r : n_i - 1;
+        hr[j] = *reinterpret_cast<const u32x4*>(da.hid + (p0 + pr) * K + (c % HC) * 8);
       }
     };
-    auto awrite = [&](const u32x4 (&regs)[kAChunks], int buf) {
+    auto hwrite = [&](int buf) {
 #pragma unroll
-      for (int j = 0; j < kAChunks; ++j) {
+      for (int j = 0; j < HL; ++j) {
         const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_a[buf][lds_off<RB>(c / kRowChunks, c % kRowChunks)]) = regs[j];
+        *reinterpret_cast<u32x4*>(&htile[buf][lds_off<HB>(c / HC, c % HC)]) = hr[j];
       }
     };
-    // One tile: MFMAs on lds_a[cur]; stage; write the next tile's rows (held
-    // in `next`) to lds_a[cur ^ 1]; store the staged rows.
-    auto tile = [&](int mt, int cur, const u32x4 (&next)[kAChunks]) {
-      f32x4 acc[4][2];  // [output stripe b][pair group a]
+    auto tile = [&](int buf, int pt) {
+      if (!has_slab) return;  // (such a wave still loads and meets the barriers)
+      f32x4 acc[NB][2];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int a = 0; a < 2; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < K / 32; ++kk) {
-        u32x4 av[2], bv[4];
+      for (int kk = 0; kk < KK; ++kk) {
+        u32x4 hb[2];  // lane (m, g): pair 16 a + m, elements 32 kk + 8 g .. +7
 #pragma unroll
         for (int a = 0; a < 2; ++a)
-          av[a] = *reinterpret_cast<const u32x4*>(&lds_a[cur][lds_off<RB>(wm * 32 + a * 16 + m, kk * 4 + g)]);
+          hb[a] = *reinterpret_cast<const u32x4*>(&htile[buf][lds_off<HB>(16 * a + m, 4 * kk + g)]);
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          bv[b] = *reinterpret_cast<const u32x4*>(&lds_b[lds_off<RB>(wn * 64 + b * 16 + m, kk * 4 + g)]);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int a = 0; a < 2; ++a)
-            acc[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bv[b]), as_bf16x8(av[a]), acc[b][a], 0, 0, 0);
+            acc[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[b][kk]), as_bf16x8(hb[a]), acc[b][a],
+                                                               0, 0, 0);
       }
-      // Stage the tile, then store whole 16-byte chunks of each pair row
-      // (measured faster than 8-byte stores straight from the accumulators).
-      // lane (m, g): pair wm*32 + a*16 + m, outputs wn*64 + b*16 + 4g .. +3.
-      // The barrier also tells every wave that lds_a[cur ^ 1] (last read by
-      // the previous tile) and the previous staged tile are free.
-      __syncthreads();
+      // lane (m, g): outputs 16 b + 4 g .. +3 of the tile's pair 16 a + m
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int col = wn * 64 + b * 16 + 4 * g;
+        for (int b = 0; b < NB; ++b) {
+          const int col = 16 * b + 4 * g;
           const f32x4 v = acc[b][a];
-          *reinterpret_cast<u32x2*>(lds_c + lds_off<256>(wm * 32 + a * 16 + m, col >> 3) + (col & 7) * 2) =
+          *reinterpret_cast<u32x2*>(st + stage_off<RB>(16 * a + m, col >> 3) + (col & 7) * 2) =
               pack4_bf16(v[0], v[1], v[2], v[3]);
         }
-      if (mt + 1 < m_tiles) awrite(next, cur ^ 1);
-      __syncthreads();
-      // Rows past the group go to the trash area, so every wave issues the
-      // same number of stores on every path and the waits above stay exact.
-      const int rows_left = n_i - mt * GBM;
+      // A wave's LDS operations complete in issue order, so the reads below
+      // see the writes above (and the next tile's writes follow these reads);
+      // the empty asm keeps the compiler from moving LDS accesses across.
+      asm volatile("" ::: "memory");
+      const int last = n_i - 1 - pt * kDownPairs;  // the group's last row in this tile
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = tid + j * kBlock, r = c >> 4, ch = c & 15;
-        uint16_t* dst = r < rows_left ? da.part + (p0 + mt * GBM + r) * N + n0 + ch * 8 : da.trash + c * 8;
-        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(lds_c + lds_off<256>(r, ch));
+      for (int q = 0; q < kDownPairs / RPI; ++q) {
+        const int r = q * RPI + lane / CPR, c = lane % CPR;
+        const int rr = r < last ? r : last;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + stage_off<RB>(rr, c));
+        *reinterpret_cast<u32x4*>(da.part + (p0 + pt * kDownPairs + rr) * N + n0 + c * 8) = v;
       }
+      asm volatile("" ::: "memory");
     };
 
-    u32x4 ra0[kAChunks], ra1[kAChunks];
-    aload(ra0, 0);
-    aload(ra1, m_tiles > 1 ? 1 : 0);
-    awrite(ra0, 0);
+    // htile[t & 1] holds tile t.  Tile t + 1's rows, loaded during tile
+    // t - 1, go to the other buffer (last read by tile t - 1, before the
+    // barrier) before tile t's MFMAs, and tile t + 2's loads are issued
+    // ahead of tile t's stores: stores count in the same in-order counter as
+    // loads, so a wait for those rows never waits for the latest stores.
+    // Loads past the last tile repeat it.
+    hload(phys(0));
+    hwrite(0);
+    hload(phys(tiles > 1 ? 1 : 0));
     __syncthreads();
-    // (loads past the last tile repeat it, so that their number is fixed too)
-    for (int mt = 0; mt < m_tiles; mt += 2) {
-      aload(ra0, mt + 2 < m_tiles ? mt + 2 : m_tiles - 1);
-      tile(mt, 0, ra1);
-      if (mt + 1 >= m_tiles) break;
-      aload(ra1, mt + 3 < m_tiles ? mt + 3 : m_tiles - 1);
-      tile(mt + 1, 1, ra0);
+    for (int t = 0; t < tiles; ++t) {
+      if (t + 1 < tiles) hwrite((t + 1) & 1);  // (uniform over the block)
+      hload(phys(t + 2 < tiles ? t + 2 : tiles - 1));
+      tile(t & 1, phys(t));
+      __syncthreads();
     }
-    __syncthreads();  // slab and staged-tile reads are done before the next item's writes
   }
 }
 
@@ -491,6 +523,8 @@ __device__ __forceinline__ u32x4 load_part(const uint16_t* p) {
 }
 
 // ---- combine: y[t] = sum over active experts (ascending) of Part[pair_idx[t][i]] ----
+constexpr int kCombineInFlight = 8;  // partial-row loads per thread in flight
+
 __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ gates,
                                                        const int32_t* __restrict__ pair_idx,
                                                        const uint16_t* __restrict__ part, int64_t T, int E, int d,
@@ -500,14 +534,16 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   if (tid < 64) {
-    const bool on0 = tid < E && gates[t * E + tid] != 0.f;
-    const bool on1 = tid + 64 < E && gates[t * E + tid + 64] != 0.f;
+    // gates and pair slots load together (a slot is used only where its gate is non-zero)
+    const float g0 = tid < E ? gates[t * E + tid] : 0.f, g1 = tid + 64 < E ? gates[t * E + tid + 64] : 0.f;
+    const int32_t q0 = tid < E ? pair_idx[t * E + tid] : 0, q1 = tid + 64 < E ? pair_idx[t * E + tid + 64] : 0;
+    const bool on0 = g0 != 0.f, on1 = g1 != 0.f;
     const uint64_t b0 = __ballot(on0), b1 = __ballot(on1);
     const int n0 = __popcll(b0);
     const int r0 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u));
     const int r1 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u));
-    if (on0) plist[r0] = pair_idx[t * E + tid];
-    if (on1) plist[n0 + r1] = pair_idx[t * E + tid + 64];
+    if (on0) plist[r0] = q0;
+    if (on1) plist[n0 + r1] = q1;
     if (tid == 0) nlist = n0 + __popcll(b1);
   }
   __syncthreads();
@@ -521,16 +557,16 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
   };
   for (int c0 = tid * 8; c0 < d; c0 += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    // four partial rows in flight, added in ascending expert order
-    for (; s + 4 <= n; s += 4) {
-      u32x4 v[4];
+    // eight partial rows in flight, added in ascending expert order
+    for (int s = 0; s < n; s += kCombineInFlight) {
+      u32x4 v[kCombineInFlight];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = load_part(part + (int64_t)plist[s + u] * d + c0);
+      for (int u = 0; u < kCombineInFlight; ++u)
+        v[u] = s + u < n ? load_part(part + (int64_t)plist[s + u] * d + c0) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) add8(acc, v[u]);
+      for (int u = 0; u < kCombineInFlight; ++u)
+        if (s + u < n) add8(acc, v[u]);
     }
-    for (; s < n; ++s) add8(acc, load_part(part + (int64_t)plist[s] * d + c0));
     f32x4* yo = reinterpret_cast<f32x4*>(y + t * d + c0);
     yo[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
     yo[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};

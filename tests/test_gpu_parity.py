@@ -231,6 +231,7 @@ GROUPED_CASES = {
     "d768_E80_de256_L4_C33": (768, 80, 256, 4, 33, 0.9, 0.7, 502),       # E not a multiple of 16, 2 hidden tiles
     "d1024_E128_de128_L1_C300": (1024, 128, 128, 1, 300, 1.6, 0.0, 503),  # rarely-active experts, some empty
     "d256_E8_de128_L8_C16": (256, 8, 128, 8, 16, -1.0, 0.5, 504),        # most pairs active, long groups
+    "d384_E24_de128_L8_C12": (384, 24, 128, 8, 12, 0.8, 0.6, 505),       # d not a multiple of a down block's 256 columns
 }
 
 

@@ -4,16 +4,19 @@
 // RMSNorm, which separates the activation pattern from its strength; BlockFFN
 // abstract, arXiv 2507.08771: a router integrating ReLU and RMSNorm.)
 //
-// One workgroup per unit (a chunk of L tokens, or one token when L == 1)
-// computes the unit's E x L pre-activations into LDS, then a fused epilogue
-// applies ReLU + RMSNorm and builds the 64-bit activation words with wave64
-// ballots.  Two producers of the pre-activations:
-//   * route_mfma_kernel (bf16, L >= 8): the router is a genuine E x d x L
-//     contraction; each wave streams a quarter of d for every expert row
-//     through v_mfma_f32_16x16x32_bf16 (pipelined as in mfma_stream.h) and
-//     the four partial sums are added in a fixed order in the epilogue.
-//   * route_valu_kernel (fp32, or L < 8): a bandwidth-bound GEMV; lane groups
-//     stride over d with 16-byte loads and reduce with cross-lane shuffles.
+// One workgroup per unit (a chunk of L tokens, or one token when L == 1),
+// or per 16-token tile when all units share one layer, computes the tokens'
+// E pre-activations into LDS, then a fused epilogue applies ReLU + RMSNorm
+// and builds the 64-bit activation words with wave64 ballots.  Two
+// producers of the pre-activations:
+//   * route_mfma_kernel (bf16, L >= 8 or one layer for all tokens): the
+//     router is a genuine E x d x tokens contraction; each wave streams a
+//     quarter of d for every expert row through v_mfma_f32_16x16x32_bf16
+//     (pipelined as in mfma_stream.h) and the four partial sums are added in
+//     a fixed order in the epilogue.
+//   * route_valu_kernel (fp32, or L < 8 with a layer copy per unit): a
+//     bandwidth-bound GEMV; lane groups stride over d with 16-byte loads and
+//     reduce with cross-lane shuffles.
 #include "mfma_stream.h"
 
 namespace bffn {
@@ -183,13 +186,24 @@ __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const 
 // mfma_stream.h; the last block's missing stripes repeat a valid stripe and
 // are not stored.  The four per-wave partial sums meet in LDS and are added
 // in a fixed order by the epilogue (deterministic).
+//
+// A block takes tokens [t0, t0 + tb): one unit (tb = L, the unit's own layer
+// copy), or, when every unit uses the same layer, a whole token tile of 16 NT
+// tokens across units, so that the shared router is streamed once per tile
+// rather than once per unit.  Blocks that share the router start at
+// different stripe groups, which spreads their simultaneous reads of it.
+// Each output column depends only on its own token, so the grouping does not
+// change any result bit.
 template <int NT, int KIND>
 __global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
-                                                            int L, int top_k, float* __restrict__ gates,
+                                                            int64_t T, int L, int tb, int top_k,
+                                                            float* __restrict__ gates,
                                                             uint64_t* __restrict__ masks,
                                                             float* __restrict__ preact) {
-  extern __shared__ float zp[];  // [4][E][L]
-  const int64_t unit = blockIdx.x;
+  extern __shared__ float zp[];  // [4][E][Lb]
+  const int64_t t0 = (int64_t)blockIdx.x * tb;
+  const int Lb = T - t0 < tb ? (int)(T - t0) : tb;  // tokens of this block
+  const int64_t unit = t0 / L;
   const uint16_t* wr = layer_ptr(static_cast<const uint16_t*>(la.w_router), la.stride, unit, la.n_layers);
   const float* b = layer_ptr(la.b_router, la.stride, unit, la.n_layers);
   const float* s = layer_ptr(la.rms_scale, la.stride, unit, la.n_layers);
@@ -197,12 +211,13 @@ __global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const 
   const int m = lane & 15, g = lane >> 4;
   const int d = la.d, E = la.E;
   const int kw = d >> 2;
-  const int64_t t0 = unit * L;
   const int nstripes = E >> 4;
+  const int ngroups = (nstripes + 3) >> 2;
   const uint16_t* b_row[NT];
 #pragma unroll
-  for (int tl = 0; tl < NT; ++tl) b_row[tl] = x + (t0 + (m + 16 * tl) % L) * d;
-  for (int sb = 0; sb < nstripes; sb += 4) {
+  for (int tl = 0; tl < NT; ++tl) b_row[tl] = x + (t0 + (m + 16 * tl) % Lb) * d;
+  for (int q = 0; q < ngroups; ++q) {
+    const int sb = (int)((q + blockIdx.x) % ngroups) * 4;
     const uint16_t* a_row[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -219,14 +234,14 @@ __global__ __launch_bounds__(kBlock) void route_mfma_kernel(LayerArgs la, const 
 #pragma unroll
       for (int tl = 0; tl < NT; ++tl) {
         const int n = m + 16 * tl;
-        if (n >= L) continue;
+        if (n >= Lb) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) zp[(w * E + (sb + st) * 16 + 4 * g + r) * L + n] = acc[st][tl][r];
+        for (int r = 0; r < 4; ++r) zp[(w * E + (sb + st) * 16 + 4 * g + r) * Lb + n] = acc[st][tl][r];
       }
     }
   }
   __syncthreads();
-  router_epilogue<KIND>(zp, 4, E, L, t0, b, s, la.eps, top_k, gates, masks, preact);
+  router_epilogue<KIND>(zp, 4, E, Lb, t0, b, s, la.eps, top_k, gates, masks, preact);
 }
 
 }  // namespace
@@ -238,14 +253,19 @@ bool route_uses_mfma(int d, int E, int chunk_len, int dtype) {
 template <int KIND>
 hipError_t launch_route_kind(const LayerArgs& la, const void* x, int64_t units, int L, int dtype, int top_k,
                              float* gates, uint64_t* masks, float* preact, hipStream_t s) {
-  if (route_uses_mfma(la.d, la.E, L, dtype)) {
-    const size_t lds = sizeof(float) * 4 * la.E * L;
-    if (L <= 16)
-      route_mfma_kernel<1, KIND><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const uint16_t*>(x), L, top_k, gates, masks, preact);
+  const int64_t T = units * L;
+  const bool shared = la.n_layers == 1 && route_uses_mfma(la.d, la.E, 16, dtype);
+  if (shared || route_uses_mfma(la.d, la.E, L, dtype)) {
+    // one layer for all tokens: 16-token tiles; else one unit per block
+    const int tb = shared ? 16 : L;
+    const int64_t blocks = (T + tb - 1) / tb;
+    const size_t lds = sizeof(float) * 4 * la.E * tb;
+    if (tb <= 16)
+      route_mfma_kernel<1, KIND><<<dim3((unsigned)blocks), dim3(kBlock), lds, s>>>(
+          la, static_cast<const uint16_t*>(x), T, L, tb, top_k, gates, masks, preact);
     else
-      route_mfma_kernel<2, KIND><<<dim3((unsigned)units), dim3(kBlock), lds, s>>>(
-          la, static_cast<const uint16_t*>(x), L, top_k, gates, masks, preact);
+      route_mfma_kernel<2, KIND><<<dim3((unsigned)blocks), dim3(kBlock), lds, s>>>(
+          la, static_cast<const uint16_t*>(x), T, L, tb, top_k, gates, masks, preact);
   } else {
     const size_t lds = sizeof(float) * la.E * L;
     const int vec = dtype == BLOCKFFN_F32 ? 4 : 8;

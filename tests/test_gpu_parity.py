@@ -42,7 +42,7 @@ def _case(name):
 def _compare_all(layer, x, L, gpu, name, check_stats=True):
     E, dt = layer.n_experts, layer.dtype
     z, g, m, um, cnt, lst = oracle_full(layer, x, L)
-    flipped, keep = check_route(gpu, z, g, m, E, dt)
+    flipped, keep = check_route(gpu, z, g, m, E, dt, layer=layer)
     nflip_u = check_union(gpu, um, z, E, L)
     y_ref = oracle.forward_tokens(x, layer.w_in, layer.w_out, g, m)
     rel = check_y(gpu["y"], y_ref, keep, dt, name)
@@ -78,7 +78,7 @@ def test_every_mode_matches_oracle(name):
     for mode in modes:
         say(f"[gpu] mode {mode} {name}")
         gpu = run_gpu(dl, xd, L, mode=mode, stats=False)
-        flipped, keep = check_route(gpu, z, g, m, layer.n_experts, layer.dtype)
+        flipped, keep = check_route(gpu, z, g, m, layer.n_experts, layer.dtype, layer=layer)
         check_y(gpu["y"], y_ref, keep, layer.dtype, f"{name}/{mode}")
 
 
@@ -103,7 +103,7 @@ def test_stacked_distinct_layers():
             tok = (chunks[:, None] * L + np.arange(L)[None, :]).ravel()
             ly = layers[r]
             z, g, m = oracle.route(x[tok], ly.w_router, ly.b_router, None, ly.rms_eps)
-            flipped, keep = check_route(gpu, z, g, m, E, "bf16", t_idx=tok)
+            flipped, keep = check_route(gpu, z, g, m, E, "bf16", t_idx=tok, layer=ly)
             y_ref = oracle.forward_tokens(x[tok], ly.w_in, ly.w_out, g, m)
             check_y(gpu["y"][tok], y_ref, keep, "bf16", f"stacked layer {r}/{mode}")
 
@@ -142,12 +142,32 @@ def test_edge_cases_empty_none_and_all_active():
             _compare_all(layer, x, L, gpu, f"{name}/{mode}")
 
 
+def test_many_chunks():
+    # more than 1024 chunks: each thread of the plan kernel owns several chunks,
+    # and the stats kernel takes several rounds of tokens per thread
+    d, E, de, L, C = 256, 16, 128, 8, 1300
+    rng = np.random.default_rng(520)
+    layer = make_layer(d, E, de, "bf16", 0.9, rng)
+    x = make_tokens(d, C, L, 0.7, "bf16", rng).x
+    dl = B.DeviceLayer.from_workload(layer)
+    xd = B.tokens_to_device(x, BF16)
+    say(f"[gpu] many chunks C={C} T={x.shape[0]}")
+    gpu = run_gpu(dl, xd, L, mode="chunk_mfma")
+    _compare_all(layer, x, L, gpu, "many_chunks/chunk_mfma")
+    z, g, m, um, cnt, lst = oracle_full(layer, x, L)
+    y_ref = oracle.forward_dense(x, layer.w_in, layer.w_out, g)
+    dense = run_gpu(dl, xd, L, mode="dense", stats=False)
+    flipped, keep = check_route(dense, z, g, m, E, "bf16", layer=layer)
+    check_y(dense["y"], y_ref, keep, "bf16", "many_chunks/dense")
+
+
 def test_union_and_stats_kernels_on_seeded_masks():
     # masks straight from a seeded generator (not from the router), so the
     # union and statistics kernels are compared bit for bit
     rng = np.random.default_rng(400)
     for E, L, C, p in ((8, 4, 16, 0.2), (64, 8, 512, 0.19), (70, 3, 33, 0.3), (128, 32, 20, 0.15),
-                       (128, 1, 100, 0.5), (1, 2, 7, 0.5)):
+                       (128, 1, 100, 0.5), (1, 2, 7, 0.5),
+                       (16, 8, 1100, 0.25), (32, 1, 9000, 0.3)):  # several rounds per stats thread
         say(f"[gpu] union/stats E={E} L={L} C={C}")
         T = L * C
         act = rng.random((T, E)) < p
@@ -206,7 +226,7 @@ def test_full_size_sampled(name):
     del dl, xd
     torch.cuda.empty_cache()
     z, g, m, um, cnt, lst = oracle_full(layer, tok.x, L)
-    flipped, keep = check_route(gpu, z, g, m, E, cfg.dtype)
+    flipped, keep = check_route(gpu, z, g, m, E, cfg.dtype, layer=layer)
     nflip_u = check_union(gpu, um, z, E, L)
     if not flipped:
         st = oracle.stats(m, E, L)
@@ -262,7 +282,7 @@ def test_grouped_full_size_sampled():
     del dl, xd
     torch.cuda.empty_cache()
     z, g, m, um, cnt, lst = oracle_full(layer, tok.x, L)
-    flipped, keep = check_route(gpu, z, g, m, E, cfg.dtype)
+    flipped, keep = check_route(gpu, z, g, m, E, cfg.dtype, layer=layer)
     C = cfg.units
     sample = np.unique(np.r_[np.linspace(0, C - 1, 8).astype(int), 1, C - 2])
     tok_idx = (sample[:, None] * L + np.arange(L)[None, :]).ravel()

@@ -423,21 +423,36 @@ __global__ __launch_bounds__(kBlock) void tgemm_kernel(TGemmArgs ta) {
     const int64_t ld = op_b ? ta.ldb : ta.lda;
     const int32_t* rows_of = op_b ? ta.b_rows : ta.a_rows;
     const int col0 = (op_b ? n0 : m0) + ch * 8;
+    // A gathered row needs its index first, so the indices of step s + 2 are
+    // loaded during step s and the rows of step s + 1 come from indices that
+    // have already arrived.  Pairs past the group load the group's last pair
+    // (no branches around the loads) and are zeroed when written to LDS.
+    // (The index loads are unconditional, from a valid word when the operand
+    // has no row array, and the choice is made only when the row is used, so
+    // that nothing waits for an index before it is needed.)
     u32x4 rv[4];
+    int32_t ridx[4];
+    const int32_t* idx_base = rows_of ? rows_of + p0 : reinterpret_cast<const int32_t*>(ta.grp_off);
+    auto pair_of = [&](int s, int k) {
+      const int64_t p = (int64_t)s * TBK + pg * 4 + k;
+      return p < n_p ? p : n_p - 1;
+    };
+    auto iload = [&](int s) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ridx[k] = idx_base[rows_of ? pair_of(s, k) : 0];
+    };
     auto gload = [&](int s) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int64_t p = (int64_t)s * TBK + pg * 4 + k;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (p < n_p) {  // pairs past the group contribute zero
-          const int64_t row = rows_of ? (int64_t)rows_of[p0 + p] : p0 + p;
-          v = *reinterpret_cast<const u32x4*>(src + row * ld + col0);
-        }
-        rv[k] = v;
+        const int64_t row = rows_of ? (int64_t)ridx[k] : p0 + pair_of(s, k);
+        rv[k] = *reinterpret_cast<const u32x4*>(src + row * ld + col0);
       }
     };
-    auto swrite = [&](int buf) {  // transposed: element e of the 4 pairs -> LDS row ch*8 + e
+    auto swrite = [&](int buf, int s) {  // transposed: element e of the 4 pairs -> LDS row ch*8 + e
       uint8_t* dst = op_b ? lds_b[buf] : lds_a[buf];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)  // pairs past the group contribute zero
+        if ((int64_t)s * TBK + pg * 4 + k >= n_p) rv[k] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const u32x2 lo = u32x2{(rv[0][q] & 0xffffu) | (rv[1][q] << 16), (rv[2][q] & 0xffffu) | (rv[3][q] << 16)};
@@ -453,13 +468,18 @@ __global__ __launch_bounds__(kBlock) void tgemm_kernel(TGemmArgs ta) {
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) acc[sa][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ksteps > 0) {
+      iload(0);
       gload(0);
-      swrite(0);
+      iload(ksteps > 1 ? 1 : 0);
+      swrite(0, 0);
       __syncthreads();
     }
     for (int s = 0; s < ksteps; ++s) {
       const int cur = s & 1;
-      if (s + 1 < ksteps) gload(s + 1);
+      if (s + 1 < ksteps) {  // (uniform)
+        gload(s + 1);                                // indices loaded a step ago
+        iload(s + 2 < ksteps ? s + 2 : ksteps - 1);  // step s + 2's indices
+      }
 #pragma unroll
       for (int kk = 0; kk < TBK / 32; ++kk) {
         u32x4 av[4], bv[4];
@@ -476,7 +496,7 @@ __global__ __launch_bounds__(kBlock) void tgemm_kernel(TGemmArgs ta) {
             acc[sa][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[sa]), as_bf16x8(bv[sb]), acc[sa][sb],
                                                                   0, 0, 0);
       }
-      if (s + 1 < ksteps) swrite(cur ^ 1);
+      if (s + 1 < ksteps) swrite(cur ^ 1, s + 1);
       __syncthreads();
     }
     // D: lane (m16, g) holds rows 4 g + r of column m16 of each 16 x 16 tile

@@ -190,9 +190,10 @@ int blockffn_chunk_union(int32_t n_experts, const uint64_t* token_masks, int64_t
  *   workspace  device scratch of at least blockffn_workspace_size() bytes,
  *              256-byte aligned; its contents need no initialisation
  * GROUPED mode (one batch through one layer, n_layers == 1): every
- * (token, expert) pair with a positive gate is grouped by expert, each
- * expert's weights are read once for all of its tokens in MFMA GEMMs, and
- * each token's per-expert partial rows are summed in ascending expert order.
+ * (token, expert) pair with a non-zero gate (negative where the RMS scale
+ * is negative) is grouped by expert, each expert's weights are read once
+ * for all of its tokens in MFMA GEMMs, and each token's per-expert partial
+ * rows are summed in ascending expert order.
  * It needs bf16, d a multiple of 128, d_expert 128 or 256 (MODE otherwise)
  * and n_tokens x n_experts below 2^31 (SHAPE otherwise).
  * Errors: NULL, SHAPE, DTYPE, CHUNK, WORKSPACE, MODE, ALIGN, LAYERS, HIP.

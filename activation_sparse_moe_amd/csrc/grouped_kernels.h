@@ -41,6 +41,7 @@ constexpr int GBM = 64, GBN = 128, GBK = 64;
 constexpr int kPlanThreads = 128;     // one thread per expert (E <= 128)
 constexpr int kPlanMaxBlocks = 512;   // token blocks of the count / fill kernels
 constexpr int kPlanMinRows = 32;      // tokens per block at least (short scans)
+constexpr int kPlanInFlight = 32;     // tokens whose gate loads a count / fill thread issues together
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -82,12 +83,14 @@ __global__ __launch_bounds__(kPlanThreads) void group_count_kernel(const float* 
   const int64_t t0 = (int64_t)blockIdx.x * rows;
   const int64_t t1 = t0 + rows < T ? t0 + rows : T;
   int c = 0;
-  for (int64_t t = t0; t < t1; t += 8) {  // eight loads in flight
-    float v[8];
+  for (int64_t t = t0; t < t1; t += kPlanInFlight) {  // (one round at the minimum block size)
+    // (loads past t1 repeat token t1 - 1 and are not counted: no branch
+    // around a load, so all of them are in flight together)
+    float v[kPlanInFlight];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = t + u < t1 ? sel[(t + u) * E + i] : 0.f;
+    for (int u = 0; u < kPlanInFlight; ++u) v[u] = sel[(t + u < t1 ? t + u : t1 - 1) * E + i];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) c += pair_selected<R>(v[u]);
+    for (int u = 0; u < kPlanInFlight; ++u) c += t + u < t1 && pair_selected<R>(v[u]);
   }
   blk[(int64_t)blockIdx.x * E + i] = c;
 }
@@ -129,13 +132,15 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ 
   const bool act = part < nparts;
   const int b0 = act ? (int)((int64_t)nblk * part / nparts) : 0;
   const int b1 = act ? (int)((int64_t)nblk * (part + 1) / nparts) : 0;
+  // (loads past b1 repeat block b1 - 1 and are not used: no branch around a
+  // load, so each round's loads are in flight together)
   int64_t s = 0;
   for (int b = b0; b < b1; b += 8) {
     int c[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? blk[(int64_t)(b + u) * E + i] : 0;
+    for (int u = 0; u < 8; ++u) c[u] = blk[(int64_t)(b + u < b1 ? b + u : b1 - 1) * E + i];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += c[u];
+    for (int u = 0; u < 8; ++u) s += b + u < b1 ? c[u] : 0;
   }
   part_sum[tid] = s;
   __syncthreads();
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ 
     for (int b = b0; b < b1; b += 8) {
       int c[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? blk[(int64_t)(b + u) * E + i] : 0;
+      for (int u = 0; u < 8; ++u) c[u] = blk[(int64_t)(b + u < b1 ? b + u : b1 - 1) * E + i];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (b + u < b1) {
@@ -188,16 +193,17 @@ __global__ __launch_bounds__(kPlanThreads) void group_fill_kernel(const float* _
   const int64_t t0 = (int64_t)blockIdx.x * rows;
   const int64_t t1 = t0 + rows < T ? t0 + rows : T;
   int32_t p = blk_off[(int64_t)blockIdx.x * E + i];
-  for (int64_t t = t0; t < t1; t += 8) {  // eight tokens' loads in flight, then in order
-    float sv[8], vv[8];
+  for (int64_t t = t0; t < t1; t += kPlanInFlight) {  // a round of tokens' loads in flight, then in order
+    float sv[kPlanInFlight], vv[kPlanInFlight];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      sv[u] = t + u < t1 ? sel[(t + u) * E + i] : 0.f;
-      vv[u] = t + u < t1 ? val[(t + u) * E + i] : 0.f;
+    for (int u = 0; u < kPlanInFlight; ++u) {  // (as in the count: clamped, unconditional loads)
+      const int64_t tt = t + u < t1 ? t + u : t1 - 1;
+      sv[u] = sel[tt * E + i];
+      vv[u] = val[tt * E + i];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (pair_selected<R>(sv[u])) {  // (0 past t1: never selected)
+    for (int u = 0; u < kPlanInFlight; ++u) {
+      if (t + u < t1 && pair_selected<R>(sv[u])) {
         pair_tok[p] = (int32_t)(t + u);
         pair_gate[p] = vv[u];
         pair_idx[(t + u) * E + i] = p;

@@ -17,7 +17,8 @@
 //            gate, and pair_idx[t][i] for the combine (the forward pairs
 //            every non-zero gate; the backward every active pair)
 //   up:      H'[p] = g_p * Swish(x[t_p] W_in[i]^T), bf16, grouped GEMM with
-//            gathered token rows (64 pairs x 128 hidden x 64 k tiles)
+//            gathered token rows (64 pairs x 128 hidden x 64 k tiles), both
+//            operands DMA'd into a block-shared LDS ring
 //   down:    Part[p] = H'[p] W_out[i]^T, bf16 per-pair partial rows; each
 //            wave keeps one 64-row slab of W_out[i] in registers and runs it
 //            over all of expert i's pairs, read from block-shared LDS tiles
@@ -25,14 +26,15 @@
 //            Part[pair_idx[t][i]], fp32 (no atomics; deterministic)
 //
 // The up GEMM's MFMA tiles (v_mfma_f32_16x16x32_bf16) use 256 threads as
-// 2 x 2 waves of 32 x 64; its global rows are moved as 16-byte chunks and
-// written to LDS with the chunk index XOR-swizzled by row, so that the 16
-// rows an MFMA operand read touches land in different banks (the down GEMM
-// stages its hidden rows the same way).  Output tiles are staged in LDS and
-// stored as whole 16-byte chunks of each row.
+// 2 x 2 waves of 32 x 64.  LDS tiles hold 16-byte chunks XOR-swizzled by
+// row, so that the 16 rows an MFMA operand read touches land in different
+// banks (the up GEMM's DMA applies the swizzle on the source side; the down
+// GEMM stages its hidden rows through registers).  Output tiles are staged
+// in LDS and stored as whole 16-byte chunks of each row.
 #pragma once
 
 #include "bffn_internal.h"
+#include "lds_stream.h"
 
 namespace bffn {
 namespace {
@@ -232,12 +234,36 @@ struct UpArgs {
   int K, N, E;
 };
 
-// Tile: 64 pairs x 128 hidden units, k steps of 64; wave (wm, wn) computes
-// pairs wm*32 .. +31 against hidden units wn*64 .. +63.
+// Tile: 64 pairs x 128 hidden units over k in steps of 64; wave (wm, wn)
+// computes pairs wm*32 .. +31 against hidden units wn*64 .. +63.  Both
+// operands reach LDS by DMA (global_load_lds: 16 bytes per lane, each
+// 128-byte row piece read whole; the gathered token rows too, every lane
+// with its own row) into a block-shared ring of kUpRing buffers, with the
+// two steps after the one being multiplied in flight.  A step's 24 DMA
+// instructions are split over the four waves.  Each wave waits for its own
+// share with a constant vmcnt, and one barrier per step tells every wave
+// that the step has landed and that the buffer about to be refilled has
+// been read by all of them.  The 16-byte chunks are swizzled on the source
+// side (lane slot c of row r holds chunk c ^ ((r >> 1) & 7)), the layout the
+// operand reads below expect.
+constexpr int kUpRing = 3;
+constexpr int kUpABytes = GBM * 128;                             // 64 pair rows x 128 bytes
+constexpr int kUpBufBytes = kUpABytes + GBN * 128;               // + 128 weight rows: 24 KiB
+constexpr int kUpDmaPerWave = (GBM + GBN) / 8 / (kBlock / kWave);  // 1 KiB instructions per wave and step
+
+// Block barrier for data that DMA has already delivered to LDS: no fence,
+// so the DMA of later steps stays in flight (__syncthreads would drain it).
+__device__ __forceinline__ void block_barrier_no_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][GBM * 128];  // pair (x) rows
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][GBN * 128];  // weight rows
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  static_assert(GBK == kStepK && kUpDmaPerWave * (kBlock / kWave) * 8 == GBM + GBN, "ring geometry");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kUpRing][kUpBufBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
   const int m = lane & 15, g = lane >> 4;
   const int K = ua.K, N = ua.N, E = ua.E;
@@ -265,38 +291,30 @@ __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
     const int nt = (int)(local_t / m_tiles), mt = (int)(local_t % m_tiles);
     const int m0 = mt * GBM, n0 = nt * GBN;
 
-    // global source rows of this thread's load slots
-    const uint16_t* a_src[2];
+    // this wave's DMA instructions j = w kUpDmaPerWave + q of a step: j < 8
+    // moves pair rows 8 j .. +7 (gathered token rows; rows past the group
+    // repeat a valid row), j >= 8 weight rows 8 (j - 8) .. +7
+    const uint16_t* src[kUpDmaPerWave];
+    int dst[kUpDmaPerWave];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = (tid + j * kBlock) >> 3;
-      const int pr = m0 + r < n_i ? m0 + r : n_i - 1;  // rows past the group repeat a valid row
-      a_src[j] = ua.x + (int64_t)ua.pair_tok[p0 + pr] * K + ((tid + j * kBlock) & 7) * 8;
-    }
-    const uint16_t* b_src[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = (tid + j * kBlock) >> 3;
-      b_src[j] = ua.w + ((int64_t)i * N + n0 + r) * K + ((tid + j * kBlock) & 7) * 8;
-    }
-    u32x4 ra[2], rb[4];
-    auto gload = [&](int k0) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) ra[j] = *reinterpret_cast<const u32x4*>(a_src[j] + k0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rb[j] = *reinterpret_cast<const u32x4*>(b_src[j] + k0);
-    };
-    auto swrite = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_a[buf][lds_off<128>(c >> 3, c & 7)]) = ra[j];
+    for (int q = 0; q < kUpDmaPerWave; ++q) {
+      const int j = w * kUpDmaPerWave + q;
+      if (j < GBM / 8) {
+        const int R = 8 * j + (lane >> 3);
+        const int pr = m0 + R < n_i ? m0 + R : n_i - 1;
+        src[q] = ua.x + (int64_t)ua.pair_tok[p0 + pr] * K + dma_chunk_elems(R, lane);
+        dst[q] = j * 1024;
+      } else {
+        const int R = 8 * (j - GBM / 8) + (lane >> 3);
+        src[q] = ua.w + ((int64_t)i * N + n0 + R) * K + dma_chunk_elems(R, lane);
+        dst[q] = kUpABytes + (j - GBM / 8) * 1024;
       }
+    }
+    const int ksteps = K / GBK;
+    auto issue = [&](int slot, int step) {  // steps past the last repeat it (constant vmcnt)
+      const int st = step < ksteps ? step : ksteps - 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_b[buf][lds_off<128>(c >> 3, c & 7)]) = rb[j];
-      }
+      for (int q = 0; q < kUpDmaPerWave; ++q) dma16<kPolicyReuse>(src[q] + st * GBK, &ring[slot][0] + dst[q]);
     };
 
     f32x4 acc[4][2];  // [hidden stripe b][pair group a]
@@ -305,30 +323,29 @@ __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
 #pragma unroll
       for (int a = 0; a < 2; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int ksteps = K / GBK;
-    gload(0);
-    swrite(0);
-    __syncthreads();
+    issue(0, 0);
+    issue(1, 1);
     for (int ks = 0; ks < ksteps; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < ksteps) gload((ks + 1) * GBK);
+      wait_vmcnt<kUpDmaPerWave>();  // this wave's share of step ks has landed
+      block_barrier_no_fence();     // ... and everyone's; step ks - 1's buffer is free
+      issue((ks + 2) % kUpRing, ks + 2);
+      const uint8_t* buf = &ring[ks % kUpRing][0];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         u32x4 av[2], bv[4];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
-          av[a] = *reinterpret_cast<const u32x4*>(&lds_a[cur][lds_off<128>(wm * 32 + a * 16 + m, kk * 4 + g)]);
+          av[a] = *reinterpret_cast<const u32x4*>(buf + lds_off<128>(wm * 32 + a * 16 + m, kk * 4 + g));
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          bv[b] = *reinterpret_cast<const u32x4*>(&lds_b[cur][lds_off<128>(wn * 64 + b * 16 + m, kk * 4 + g)]);
+          bv[b] = *reinterpret_cast<const u32x4*>(buf + kUpABytes + lds_off<128>(wn * 64 + b * 16 + m, kk * 4 + g));
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
           for (int a = 0; a < 2; ++a)
             acc[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bv[b]), as_bf16x8(av[a]), acc[b][a], 0, 0, 0);
       }
-      if (ks + 1 < ksteps) swrite(cur ^ 1);
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // lane (m, g): pair wm*32 + a*16 + m, hidden units n0 + wn*64 + b*16 + 4g .. +3
@@ -345,6 +362,10 @@ __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
             pack4_bf16(gv * swish(v[0]), gv * swish(v[1]), gv * swish(v[2]), gv * swish(v[3]));
       }
     }
+    // the tile's last DMAs (repeats) land and every wave is done with the
+    // ring before the next tile refills it
+    wait_vmcnt<0>();
+    __syncthreads();
   }
 }
 

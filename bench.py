@@ -72,8 +72,8 @@ def parse_args(argv=None):
 KERNEL_SOURCES = {
     "expert_up": ("expert_mfma.hip", "lds_stream.h", "bffn_internal.h"),
     "expert_down": ("expert_mfma.hip", "lds_stream.h", "bffn_internal.h"),
-    "grouped_up": ("grouped.hip", "grouped_kernels.h", "bffn_internal.h"),
-    "grouped_down": ("grouped.hip", "grouped_kernels.h", "bffn_internal.h"),
+    "grouped_up": ("grouped.hip", "grouped_kernels.h", "lds_stream.h", "bffn_internal.h"),
+    "grouped_down": ("grouped.hip", "grouped_kernels.h", "lds_stream.h", "bffn_internal.h"),
     "fff_walk": ("fff.hip", "fff_probe_launch.h", "bffn_internal.h"),
 }
 

@@ -170,6 +170,7 @@ struct UpItem {
 template <int NT, bool DENSE, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uint16_t* __restrict__ x,
                                                          int64_t n_units, int L, const float* __restrict__ gates,
+                                                         const int32_t* __restrict__ count,
                                                          const int32_t* __restrict__ list,
                                                          const int64_t* __restrict__ prefix,
                                                          uint16_t* __restrict__ hbuf, int ks,
@@ -184,6 +185,25 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
   const int nsteps = d / kStepK / (SPLIT ? ks : 1);  // steps per item
   const int per_slot = SPLIT ? rbs * ks : rbs;       // items per union slot
   uint8_t* bufs = lds + w * kRingBufs * G::kBufBytes;
+  // A split launch of at most kChunkSplitMaxUnits units gets no plan
+  // (prefix == nullptr, which saves a launch on the single-chunk path): wave
+  // 0 scans the chunks' item counts itself, lane u holding chunk u.
+  __shared__ int64_t own_prefix[kChunkSplitMaxUnits + 1];
+  if (SPLIT && prefix == nullptr) {  // (uniform)
+    if (threadIdx.x < kWave) {
+      const int u = threadIdx.x;
+      int64_t c = u < n_units ? (int64_t)(DENSE ? E : count[u]) * per_slot : 0;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int64_t v = shfl_up64(c, off);
+        if (u >= off) c += v;
+      }
+      if (u < n_units) own_prefix[u + 1] = c;
+      if (u == 0) own_prefix[0] = 0;
+    }
+    __syncthreads();
+    prefix = own_prefix;
+  }
   // the block's items (all of equal size): a contiguous equal share.  (Giving
   // each XCD a range that its blocks take in turn keeps a chunk's token rows
   // in L2, but then an XCD streams neighbouring weight row blocks at once, in
@@ -554,10 +574,16 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
                      const ChunkSplit& sp, const StageEvents& se, hipStream_t s) {
   const int rbs = la.de >> 6;
   const int ks = SPLIT ? sp.ks : 1;
-  // one thread per chunk up to the block's maximum (whole waves)
-  const int plan_threads = units < kPlanMaxThreads ? (int)((units + kWave - 1) / kWave * kWave) : kPlanMaxThreads;
-  plan_items_kernel<<<dim3(1), dim3((unsigned)plan_threads), 0, s>>>(count, units, DENSE ? la.E : 0, rbs * ks,
-                                                                     la.d >> 6, rbs, plan, plan + units + 1);
+  // A split launch of few units needs only the item prefix, which its up
+  // kernel computes itself; every other launch gets the plan kernel (one
+  // thread per chunk up to the block's maximum, whole waves).
+  const bool own_prefix = SPLIT && units <= kChunkSplitMaxUnits;
+  if (!own_prefix) {
+    const int plan_threads =
+        units < kPlanMaxThreads ? (int)((units + kWave - 1) / kWave * kWave) : kPlanMaxThreads;
+    plan_items_kernel<<<dim3(1), dim3((unsigned)plan_threads), 0, s>>>(count, units, DENSE ? la.E : 0, rbs * ks,
+                                                                       la.d >> 6, rbs, plan, plan + units + 1);
+  }
   // persistent grids sized to the resident capacity (one block per CU at this LDS use)
   int64_t grid_up = 0, grid_dn = 0;
   hipError_t e =
@@ -571,8 +597,8 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
   se.record(0, s);
   // the pool counters follow the prefix and the XCD bounds in the plan
   unsigned* pool = reinterpret_cast<unsigned*>(plan + units + 1 + kXcds + 1);
-  up_mfma_kernel<NT, DENSE, SPLIT><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(la, x, units, L, gates, list,
-                                                                                    plan, hbuf, ks, sp.up_part, pool);
+  up_mfma_kernel<NT, DENSE, SPLIT><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(
+      la, x, units, L, gates, count, list, own_prefix ? nullptr : plan, hbuf, ks, sp.up_part, pool);
   if (SPLIT)
     up_split_epilogue_kernel<<<dim3((unsigned)(units * la.E * rbs)), dim3(kBlock), 0, s>>>(
         sp.up_part, gates, count, list, L, la.E, la.de, ks, hbuf);

@@ -125,10 +125,10 @@ struct PairArgs {
 };
 
 __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_x[2][GBM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_y[2][GBM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_wi[2][GBN * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_wo[2][GBN * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_x[GBM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_y[GBM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_wi[GBN * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_wo[GBN * 128];
   __shared__ float dg_part[2][GBM];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -189,18 +189,18 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
         rwo[j] = *reinterpret_cast<const u32x4*>(wo_src[j] + k0);
       }
     };
-    auto swrite = [&](int buf) {
+    auto swrite = [&]() {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_x[buf][lds_off<128>(c >> 3, c & 7)]) = rx[j];
-        *reinterpret_cast<u32x4*>(&lds_y[buf][lds_off<128>(c >> 3, c & 7)]) = ry[j];
+        *reinterpret_cast<u32x4*>(&lds_x[lds_off<128>(c >> 3, c & 7)]) = rx[j];
+        *reinterpret_cast<u32x4*>(&lds_y[lds_off<128>(c >> 3, c & 7)]) = ry[j];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = tid + j * kBlock;
-        *reinterpret_cast<u32x4*>(&lds_wi[buf][lds_off<128>(c >> 3, c & 7)]) = rwi[j];
-        *reinterpret_cast<u32x4*>(&lds_wo[buf][lds_off<128>(c >> 3, c & 7)]) = rwo[j];
+        *reinterpret_cast<u32x4*>(&lds_wi[lds_off<128>(c >> 3, c & 7)]) = rwi[j];
+        *reinterpret_cast<u32x4*>(&lds_wo[lds_off<128>(c >> 3, c & 7)]) = rwo[j];
       }
     };
 
@@ -211,11 +211,13 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
       for (int a = 0; a < 2; ++a) au[b][a] = aq[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int ksteps = K / GBK;
+    // one LDS buffer (two blocks fit on a CU): the registers hold step ks + 1
+    // while step ks is multiplied; a fence-free barrier after the products
+    // frees the buffer without waiting for those loads
     gload(0);
-    swrite(0);
-    __syncthreads();
     for (int ks = 0; ks < ksteps; ++ks) {
-      const int cur = ks & 1;
+      swrite();
+      __syncthreads();
       if (ks + 1 < ksteps) gload((ks + 1) * GBK);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -223,14 +225,14 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
           const int off = lds_off<128>(wm * 32 + a * 16 + m, kk * 4 + g);
-          vx[a] = *reinterpret_cast<const u32x4*>(&lds_x[cur][off]);
-          vy[a] = *reinterpret_cast<const u32x4*>(&lds_y[cur][off]);
+          vx[a] = *reinterpret_cast<const u32x4*>(&lds_x[off]);
+          vy[a] = *reinterpret_cast<const u32x4*>(&lds_y[off]);
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int off = lds_off<128>(wn * 64 + b * 16 + m, kk * 4 + g);
-          vwi[b] = *reinterpret_cast<const u32x4*>(&lds_wi[cur][off]);
-          vwo[b] = *reinterpret_cast<const u32x4*>(&lds_wo[cur][off]);
+          vwi[b] = *reinterpret_cast<const u32x4*>(&lds_wi[off]);
+          vwo[b] = *reinterpret_cast<const u32x4*>(&lds_wo[off]);
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -240,8 +242,7 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
             aq[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vwo[b]), as_bf16x8(vy[a]), aq[b][a], 0, 0, 0);
           }
       }
-      if (ks + 1 < ksteps) swrite(cur ^ 1);
-      __syncthreads();
+      block_barrier_no_fence();
     }
 
     // lane (m, g): pair wm*32 + a*16 + m, hidden units n0 + wn*64 + b*16 + 4g .. +3

@@ -391,7 +391,9 @@ __device__ __forceinline__ int tl_off(int row, int p) {
   return row * 64 + (((p >> 3) ^ (row >> 2) ^ (row >> 3)) & 3) * 16 + (p & 7) * 2;
 }
 
-__global__ __launch_bounds__(kBlock) void tgemm_kernel(TGemmArgs ta) {
+// Three waves per SIMD (a 168-register cap; the compiler spills a few
+// registers of the set-up) hide the gathers better than two.
+__global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][TBM * 64];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][TBN * 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;

@@ -380,25 +380,92 @@ struct TGemmArgs {
   int G, M, M_valid, N;
 };
 
-// LDS tile of 128 rows (m or n) x 32 pairs, 64-byte rows.  The 16-byte chunk
-// (8 pairs) c of row r sits at position c ^ f(r), f(r) = ((r >> 2) ^ (r >> 3))
-// & 3: the 16 consecutive rows an MFMA operand read touches then hit 16
-// different bank groups, and the 8-byte transposed writes (two rows 8 apart,
-// 8 groups of 4 pairs each) collide at most 2-way.  (Steps of 64 pairs in
-// 128-byte rows measured slower: the extra prefetch registers cost a wave of
-// occupancy per SIMD, and the gathers need the latency hiding.)
-__device__ __forceinline__ int tl_off(int row, int p) {
-  return row * 64 + (((p >> 3) ^ (row >> 2) ^ (row >> 3)) & 3) * 16 + (p & 7) * 2;
+// The operands lie in memory pair-major (a pair's 128 elements of m, or of n,
+// are one 256-byte row piece), and the contraction runs over pairs.  A step of
+// TBK = 32 pairs reaches LDS untouched, by DMA (global_load_lds, 16 bytes per
+// lane; the gathered rows too, every lane with its own row), into a
+// block-shared ring of kTgRing slots, kTgDepth steps ahead of the one being
+// multiplied.  The MFMA operands (8 consecutive pairs of one m or n per lane)
+// are then read with the LDS transpose load ds_read_b64_tr_b16: within each
+// 16-lane group, lane L names 4 elements (8 bytes) and lane i receives
+// element i % 4 of lanes 4 j + i / 4, j = 0..3 (checked on gfx950); so lanes
+// naming row k0 + L / 4 at column c0 + 4 (L % 4) deliver rows k0 .. k0 + 3 of
+// column c0 + i to lane i.
+//
+// The row indices of a gathered operand come by DMA too, each wave its own
+// 16 per step into its own index ring, issued kTgDepth steps before the rows
+// that use them; the in-order vmcnt wait for a step's rows therefore also
+// covers the indices of the step kTgDepth later, and every wait is a constant.
+// Pairs past the group read a row of zeros.
+constexpr int kTgDepth = 2;
+constexpr int kTgRing = kTgDepth + 1;
+constexpr int kTgIdxSlots = 4;                        // > kTgDepth: indices in flight + the one being read
+constexpr int kTgOpBytes = TBK * TBM * 2;             // 32 rows of 256 bytes
+constexpr int kTgSlotBytes = 2 * kTgOpBytes;          // A rows, then B rows
+constexpr int kTgDmaPerWave = kTgOpBytes / 1024 / 2;  // two waves per operand
+constexpr int kTgLoadsPerStep = kTgDmaPerWave + 1;    // + the index DMA
+
+__device__ __attribute__((aligned(256))) const uint16_t kTgZeroRow[TBM] = {};
+
+// 16-byte chunk position of chunk c in LDS row r (an XOR with an even value:
+// the two chunks a 16-lane transpose read touches in a row stay adjacent, and
+// the rows read together land on different bank groups).
+__device__ __forceinline__ int tg_swz(int r) { return ((r & 3) | ((r >> 1) & 4)) << 1; }
+
+typedef short tg_v4i16 __attribute__((ext_vector_type(4)));
+
+// The four MFMA operands of 16 columns c0 + 16 j .. +15 (m or n), j < 4, from
+// one operand's rows: eight transpose reads.  They are written as one asm
+// block that also waits for them (lgkmcnt), because the compiler's builtin for
+// this load makes it wait for every LDS DMA in flight first (vmcnt 0), which
+// would drain the ring.
+__device__ __forceinline__ void tg_operands(const uint8_t* rows, int c0, int lane, u32x4 (&v)[4]) {
+  const int L = lane & 15, k0 = 8 * (lane >> 4) + (L >> 2);
+  unsigned a[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = c0 + 16 * j + 4 * (L & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + 4 * h;
+      a[2 * j + h] = (unsigned)(uintptr_t)(lvoid_t*)(rows + k * 256 + (((c >> 3) ^ tg_swz(k)) << 4) + (c & 7) * 2);
+    }
+  }
+  tg_v4i16 o[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x2 l2 = __builtin_bit_cast(u32x2, o[2 * j]), h2 = __builtin_bit_cast(u32x2, o[2 * j + 1]);
+    v[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
 }
 
-// Three waves per SIMD (a 168-register cap; the compiler spills a few
-// registers of the set-up) hide the gathers better than two.
 __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][TBM * 64];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][TBN * 64];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  static_assert(TBM == 128 && TBN == 128 && TBK == 32, "tile geometry");
+  static_assert(kTgDmaPerWave * 2 * 1024 == kTgOpBytes && kTgIdxSlots > kTgDepth, "ring geometry");
+  // one LDS object: the step ring, then each wave's index ring
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kTgRing * kTgSlotBytes + (kBlock / kWave) * kTgIdxSlots * 256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;  // compute: 64 x 64 of the 128 x 128 tile
   const int m16 = lane & 15, g = lane >> 4;
+  const int op = w >> 1, wl = w & 1;  // DMA: waves 0-1 move A rows, waves 2-3 B rows (16 rows each)
+  const uint16_t* src = op ? ta.b : ta.a;
+  const int64_t ld = op ? ta.ldb : ta.lda;
+  const int32_t* rows_of = op ? ta.b_rows : ta.a_rows;
+  uint8_t* my_idx = lds + kTgRing * kTgSlotBytes + w * kTgIdxSlots * 256;
   const int mtn = ta.M / TBM, ntn = ta.N / TBN;
   const int64_t total = (int64_t)ta.G * mtn * ntn;
   const int64_t nb = gridDim.x;
@@ -415,53 +482,33 @@ __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
     const int64_t p0 = ta.grp_off[grp];
     const int64_t n_p = ta.grp_off[grp + 1] - p0;
     const int ksteps = (int)((n_p + TBK - 1) / TBK);
+    const int col0 = op ? n0 : m0;
 
-    // Waves 0-1 stage operand A, waves 2-3 operand B.  Thread task u (of
-    // 128): pairs 4 (u & 7) .. +3 of the step, elements 8 (u >> 3) .. +7 of
-    // the 128-wide tile: four 16-byte row loads, regrouped in registers into
-    // eight 8-byte LDS writes (the 4 pairs of one element each).
-    const bool op_b = tid >= 128;
-    const int u = tid & 127, pg = u & 7, ch = u >> 3;
-    const uint16_t* src = op_b ? ta.b : ta.a;
-    const int64_t ld = op_b ? ta.ldb : ta.lda;
-    const int32_t* rows_of = op_b ? ta.b_rows : ta.a_rows;
-    const int col0 = (op_b ? n0 : m0) + ch * 8;
-    // A gathered row needs its index first, so the indices of step s + 2 are
-    // loaded during step s and the rows of step s + 1 come from indices that
-    // have already arrived.  Pairs past the group load the group's last pair
-    // (no branches around the loads) and are zeroed when written to LDS.
-    // (The index loads are unconditional, from a valid word when the operand
-    // has no row array, and the choice is made only when the row is used, so
-    // that nothing waits for an index before it is needed.)
-    u32x4 rv[4];
-    int32_t ridx[4];
-    const int32_t* idx_base = rows_of ? rows_of + p0 : reinterpret_cast<const int32_t*>(ta.grp_off);
-    auto pair_of = [&](int s, int k) {
-      const int64_t p = (int64_t)s * TBK + pg * 4 + k;
-      return p < n_p ? p : n_p - 1;
+    // index DMA of a step: lane l fetches the index of the wave's pair l % 16
+    // (an operand without a row array fetches a valid dummy word)
+    auto issue_idx = [&](int step) {
+      const int st = step < ksteps ? step : ksteps - 1;
+      int64_t p = (int64_t)st * TBK + wl * 16 + (lane & 15);
+      p = p < n_p ? p : n_p - 1;
+      const int32_t* s = rows_of ? rows_of + p0 + p : reinterpret_cast<const int32_t*>(ta.grp_off);
+      dma4(reinterpret_cast<const float*>(s), my_idx + (step % kTgIdxSlots) * 256);
     };
-    auto iload = [&](int s) {
+    // row DMA of a step: instruction q moves LDS rows wl 16 + 4 q .. +3; LDS
+    // row wl 16 + 4 q + i holds pair wl 16 + 4 i + q, so a lane's four pairs
+    // are consecutive and their indices one 16-byte LDS read (the k order is
+    // the same for both operands, which is all the product needs)
+    auto issue_rows = [&](int step) {
+      const int st = step < ksteps ? step : ksteps - 1;
+      uint8_t* dst = lds + (step % kTgRing) * kTgSlotBytes + op * kTgOpBytes + wl * 4 * 1024;
+      const u32x4 rid = *reinterpret_cast<const u32x4*>(my_idx + (step % kTgIdxSlots) * 256 + 16 * g);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) ridx[k] = idx_base[rows_of ? pair_of(s, k) : 0];
-    };
-    auto gload = [&](int s) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int64_t row = rows_of ? (int64_t)ridx[k] : p0 + pair_of(s, k);
-        rv[k] = *reinterpret_cast<const u32x4*>(src + row * ld + col0);
-      }
-    };
-    auto swrite = [&](int buf, int s) {  // transposed: element e of the 4 pairs -> LDS row ch*8 + e
-      uint8_t* dst = op_b ? lds_b[buf] : lds_a[buf];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)  // pairs past the group contribute zero
-        if ((int64_t)s * TBK + pg * 4 + k >= n_p) rv[k] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x2 lo = u32x2{(rv[0][q] & 0xffffu) | (rv[1][q] << 16), (rv[2][q] & 0xffffu) | (rv[3][q] << 16)};
-        const u32x2 hi = u32x2{(rv[0][q] >> 16) | (rv[1][q] & 0xffff0000u), (rv[2][q] >> 16) | (rv[3][q] & 0xffff0000u)};
-        *reinterpret_cast<u32x2*>(dst + tl_off(ch * 8 + 2 * q, pg * 4)) = lo;
-        *reinterpret_cast<u32x2*>(dst + tl_off(ch * 8 + 2 * q + 1, pg * 4)) = hi;
+      for (int q = 0; q < kTgDmaPerWave; ++q) {
+        const int r = wl * 16 + 4 * q + g;
+        const int64_t p = (int64_t)st * TBK + wl * 16 + 4 * g + q;
+        const int gc = (lane & 15) ^ tg_swz(r);
+        const int64_t row = rows_of ? (int64_t)(int32_t)rid[q] : p0 + p;
+        const uint16_t* a = p < n_p ? src + row * ld + col0 + gc * 8 : kTgZeroRow + gc * 8;
+        dma16<kPolicyReuse>(a, dst + q * 1024);
       }
     };
 
@@ -470,38 +517,39 @@ __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
     for (int sa = 0; sa < 4; ++sa)
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) acc[sa][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (ksteps > 0) {
-      iload(0);
-      gload(0);
-      iload(ksteps > 1 ? 1 : 0);
-      swrite(0, 0);
-      __syncthreads();
+    if (ksteps > 0) {  // (uniform)
+      // indices of the first kTgDepth steps, then kTgDepth steps issued as
+      // the loop issues them: indices kTgDepth steps ahead of their rows
+#pragma unroll
+      for (int s = 0; s < kTgDepth; ++s) issue_idx(s);
+      wait_vmcnt<0>();
+#pragma unroll
+      for (int s = 0; s < kTgDepth; ++s) {
+        issue_idx(s + kTgDepth);
+        issue_rows(s);
+      }
     }
     for (int s = 0; s < ksteps; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < ksteps) {  // (uniform)
-        gload(s + 1);                                // indices loaded a step ago
-        iload(s + 2 < ksteps ? s + 2 : ksteps - 1);  // step s + 2's indices
-      }
+      wait_vmcnt<kTgLoadsPerStep * (kTgDepth - 1)>();  // this wave's rows of step s (and older indices)
+      block_barrier_no_fence();                        // ... everyone's; step s - 1's slot is free
+      issue_idx(s + 2 * kTgDepth);
+      issue_rows(s + kTgDepth);
+      const uint8_t* buf = lds + (s % kTgRing) * kTgSlotBytes;
+      u32x4 av[4], bv[4];
+      tg_operands(buf, wm * 64, lane, av);
+      tg_operands(buf + kTgOpBytes, wn * 64, lane, bv);
 #pragma unroll
-      for (int kk = 0; kk < TBK / 32; ++kk) {
-        u32x4 av[4], bv[4];
-#pragma unroll
-        for (int sa = 0; sa < 4; ++sa)
-          av[sa] = *reinterpret_cast<const u32x4*>(&lds_a[cur][tl_off(wm * 64 + sa * 16 + m16, kk * 32 + g * 8)]);
+      for (int sa = 0; sa < 4; ++sa)
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
-          bv[sb] = *reinterpret_cast<const u32x4*>(&lds_b[cur][tl_off(wn * 64 + sb * 16 + m16, kk * 32 + g * 8)]);
-#pragma unroll
-        for (int sa = 0; sa < 4; ++sa)
-#pragma unroll
-          for (int sb = 0; sb < 4; ++sb)
-            acc[sa][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[sa]), as_bf16x8(bv[sb]), acc[sa][sb],
-                                                                  0, 0, 0);
-      }
-      if (s + 1 < ksteps) swrite(cur ^ 1, s + 1);
-      __syncthreads();
+          acc[sa][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[sa]), as_bf16x8(bv[sb]), acc[sa][sb], 0,
+                                                                0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the tile's last DMAs (repeats) land and every wave is done with both
+    // rings before the next tile refills them
+    wait_vmcnt<0>();
+    __syncthreads();
     // D: lane (m16, g) holds rows 4 g + r of column m16 of each 16 x 16 tile
     float* cg = ta.c + (int64_t)grp * ta.c_stride;
 #pragma unroll

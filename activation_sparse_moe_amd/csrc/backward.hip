@@ -14,20 +14,20 @@
 // Active pairs are grouped by expert (the forward's pair planning, on
 // z > 0), and the per-expert products run as LDS-tiled MFMA GEMMs:
 //
-//   prep:    g and r per token (as the router computes them), dy -> bf16,
-//            W_in and W_out transposed per expert (the products that
-//            contract over a weight's row index read the transposed copy)
+//   prep:    g and r per token (as the router computes them), dy -> bf16
+//            (the products that contract over a weight's row index, dY W_out
+//            and dU W_in, read the weight as it lies, by LDS transpose loads)
 //   pair:    U = X_p W_in[i]^T and Q = dY_p W_out[i] in one pass over k = d;
 //            epilogue: dU = g Q Swish'(U), HG = g Swish(U) (bf16), and the
 //            partial dg = sum over the tile's hidden units of Q Swish(U)
 //   router:  dz, ds terms per token; then db, ds by sums over tokens
 //   weights: dW_out[i] = dY_p^T HG_p, dW_in[i] = dU_p^T X_p and
 //            dW_r = dZ^T X (over token ranges, then summed in order), each a
-//            sum over pairs (tokens) in fp32 by a
-//            "transposing" grouped GEMM (the pair rows are written to LDS
-//            transposed, so the contraction runs over pairs)
-//   dx:      Part = dU W_in[i] per pair (the forward's down GEMM on the
-//            transposed W_in), then per token the sum over its active
+//            sum over pairs (tokens) in fp32 by a grouped GEMM that
+//            contracts over pairs (pair-major rows in LDS, MFMA operands by
+//            transpose loads)
+//   dx:      Part = dU W_in[i] per pair (the forward's down GEMM, reading
+//            W_in k-major), then per token the sum over its active
 //            experts, ascending, of Part + dz_i W_r[i] (and, with an extra
 //            router gradient, dz_i W_r[i] of the inactive experts after them)
 //
@@ -77,37 +77,6 @@ __global__ __launch_bounds__(kBlock) void bwd_prep_kernel(const float* __restric
   }
 }
 
-// ---- transpose: out[b][c][r] = in[b][r][c], bf16, R and C multiples of 64 ----
-// grid (tiles of one matrix, batch); 64 x 64 tiles through a padded LDS tile.
-__global__ __launch_bounds__(kBlock) void transpose_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
-                                                           int R, int C) {
-  __shared__ uint16_t tile[64][66];
-  const int tid = threadIdx.x;
-  const int tiles_c = C / 64;
-  const int tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
-  const int64_t base = (int64_t)blockIdx.y * R * C;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = tid + j * kBlock, r = c >> 3, ch = c & 7;  // 64 rows x 8 chunks of 8
-    const u32x4 v = *reinterpret_cast<const u32x4*>(in + base + (int64_t)(tr * 64 + r) * C + tc * 64 + ch * 8);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[r][ch * 8 + 2 * q] = (uint16_t)(v[q] & 0xffffu);
-      tile[r][ch * 8 + 2 * q + 1] = (uint16_t)(v[q] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = tid + j * kBlock, oc = c >> 3, ch = c & 7;  // output row oc (= input column)
-    u32x4 v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      v[q] = (uint32_t)tile[ch * 8 + 2 * q][oc] | ((uint32_t)tile[ch * 8 + 2 * q + 1][oc] << 16);
-    *reinterpret_cast<u32x4*>(out + base + (int64_t)(tc * 64 + oc) * R + tr * 64 + ch * 8) = v;
-  }
-}
-
 // ---- pair: U and Q for a 64-pair x 128-hidden tile, fused epilogue ----
 struct PairArgs {
   const uint16_t* x;        // [T][d]
@@ -115,7 +84,7 @@ struct PairArgs {
   const int32_t* pair_tok;
   const float* pair_gate;   // g of each pair
   const uint16_t* w_in;     // [E][de][d]
-  const uint16_t* w_outT;   // [E][de][d]
+  const uint16_t* w_out;    // [E][d][de]
   const int64_t* pair_off;  // [E + 1]
   const int64_t* tile_off;  // [E + 1]
   uint16_t* du;             // [P][de] bf16
@@ -128,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[GBM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t lds_y[GBM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t lds_wi[GBN * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_wo[GBN * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_wo[GBK * GBN * 2];  // k-major: 64 rows of 128 hidden units
   __shared__ float dg_part[2][GBM];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -168,13 +137,12 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
       y_src[j] = pa.dy + tok * K + ((tid + j * kBlock) & 7) * 8;
     }
     const uint16_t* wi_src[4];
-    const uint16_t* wo_src[4];
+    const uint16_t* wo_src[4];  // W_out[i] rows k (d) of the tile's 128 hidden units: 16 chunks per row
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = (tid + j * kBlock) >> 3;
-      const int64_t off = ((int64_t)i * N + n0 + r) * K + ((tid + j * kBlock) & 7) * 8;
-      wi_src[j] = pa.w_in + off;
-      wo_src[j] = pa.w_outT + off;
+      const int c = tid + j * kBlock;
+      wi_src[j] = pa.w_in + ((int64_t)i * N + n0 + (c >> 3)) * K + (c & 7) * 8;
+      wo_src[j] = pa.w_out + ((int64_t)i * K + (c >> 4)) * N + n0 + (c & 15) * 8;
     }
     u32x4 rx[2], ry[2], rwi[4], rwo[4];
     auto gload = [&](int k0) {
@@ -186,7 +154,7 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         rwi[j] = *reinterpret_cast<const u32x4*>(wi_src[j] + k0);
-        rwo[j] = *reinterpret_cast<const u32x4*>(wo_src[j] + k0);
+        rwo[j] = *reinterpret_cast<const u32x4*>(wo_src[j] + (int64_t)k0 * N);
       }
     };
     auto swrite = [&]() {
@@ -200,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
       for (int j = 0; j < 4; ++j) {
         const int c = tid + j * kBlock;
         *reinterpret_cast<u32x4*>(&lds_wi[lds_off<128>(c >> 3, c & 7)]) = rwi[j];
-        *reinterpret_cast<u32x4*>(&lds_wo[lds_off<128>(c >> 3, c & 7)]) = rwo[j];
+        *reinterpret_cast<u32x4*>(&lds_wo[tg_off(c >> 4, c & 15)]) = rwo[j];
       }
     };
 
@@ -222,6 +190,7 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         u32x4 vx[2], vy[2], vwi[4], vwo[4];
+        tg_operands(lds_wo + kk * 32 * 256, wn * 64, lane, vwo);
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
           const int off = lds_off<128>(wm * 32 + a * 16 + m, kk * 4 + g);
@@ -232,7 +201,6 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
         for (int b = 0; b < 4; ++b) {
           const int off = lds_off<128>(wn * 64 + b * 16 + m, kk * 4 + g);
           vwi[b] = *reinterpret_cast<const u32x4*>(&lds_wi[off]);
-          vwo[b] = *reinterpret_cast<const u32x4*>(&lds_wo[off]);
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -386,11 +354,7 @@ struct TGemmArgs {
 // lane; the gathered rows too, every lane with its own row), into a
 // block-shared ring of kTgRing slots, kTgDepth steps ahead of the one being
 // multiplied.  The MFMA operands (8 consecutive pairs of one m or n per lane)
-// are then read with the LDS transpose load ds_read_b64_tr_b16: within each
-// 16-lane group, lane L names 4 elements (8 bytes) and lane i receives
-// element i % 4 of lanes 4 j + i / 4, j = 0..3 (checked on gfx950); so lanes
-// naming row k0 + L / 4 at column c0 + 4 (L % 4) deliver rows k0 .. k0 + 3 of
-// column c0 + i to lane i.
+// are then read with transpose loads (tg_operands).
 //
 // The row indices of a gathered operand come by DMA too, each wave its own
 // 16 per step into its own index ring, issued kTgDepth steps before the rows
@@ -406,51 +370,6 @@ constexpr int kTgDmaPerWave = kTgOpBytes / 1024 / 2;  // two waves per operand
 constexpr int kTgLoadsPerStep = kTgDmaPerWave + 1;    // + the index DMA
 
 __device__ __attribute__((aligned(256))) const uint16_t kTgZeroRow[TBM] = {};
-
-// 16-byte chunk position of chunk c in LDS row r (an XOR with an even value:
-// the two chunks a 16-lane transpose read touches in a row stay adjacent, and
-// the rows read together land on different bank groups).
-__device__ __forceinline__ int tg_swz(int r) { return ((r & 3) | ((r >> 1) & 4)) << 1; }
-
-typedef short tg_v4i16 __attribute__((ext_vector_type(4)));
-
-// The four MFMA operands of 16 columns c0 + 16 j .. +15 (m or n), j < 4, from
-// one operand's rows: eight transpose reads.  They are written as one asm
-// block that also waits for them (lgkmcnt), because the compiler's builtin for
-// this load makes it wait for every LDS DMA in flight first (vmcnt 0), which
-// would drain the ring.
-__device__ __forceinline__ void tg_operands(const uint8_t* rows, int c0, int lane, u32x4 (&v)[4]) {
-  const int L = lane & 15, k0 = 8 * (lane >> 4) + (L >> 2);
-  unsigned a[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = c0 + 16 * j + 4 * (L & 3);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = k0 + 4 * h;
-      a[2 * j + h] = (unsigned)(uintptr_t)(lvoid_t*)(rows + k * 256 + (((c >> 3) ^ tg_swz(k)) << 4) + (c & 7) * 2);
-    }
-  }
-  tg_v4i16 o[8];
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u32x2 l2 = __builtin_bit_cast(u32x2, o[2 * j]), h2 = __builtin_bit_cast(u32x2, o[2 * j + 1]);
-    v[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-  }
-}
 
 __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
   static_assert(TBM == 128 && TBN == 128 && TBK == 32, "tile geometry");
@@ -633,7 +552,7 @@ struct BwdLayout {
   int64_t *pair_off, *tile_up, *all_off;
   int32_t *pair_tok, *pair_idx;
   float *pair_gate, *g_b, *r_b, *dgp, *dz, *dsc, *wr_part;
-  uint16_t *dyb, *w_inT, *w_outT, *du, *hg, *dzb, *part;
+  uint16_t *dyb, *du, *hg, *dzb, *part;
   size_t bytes;
 };
 
@@ -659,8 +578,6 @@ BwdLayout bwd_layout(char* base, int64_t T, int E, int d, int de) {
   L.g_b = reinterpret_cast<float*>(take(4 * P));
   L.r_b = reinterpret_cast<float*>(take(4 * (size_t)T));
   L.dyb = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * d));
-  L.w_inT = reinterpret_cast<uint16_t*>(take(2 * (size_t)E * d * de));
-  L.w_outT = reinterpret_cast<uint16_t*>(take(2 * (size_t)E * d * de));
   L.du = reinterpret_cast<uint16_t*>(take(2 * P * de));
   L.hg = reinterpret_cast<uint16_t*>(take(2 * P * de));
   L.dgp = reinterpret_cast<float*>(take(4 * P * (de / GBN)));
@@ -691,10 +608,6 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   se.record(0, s);
   bwd_prep_kernel<<<dim3((unsigned)T), dim3(kBlock), 0, s>>>(preact, la.rms_scale, la.eps, T, E, d, dy, L.g_b, L.r_b,
                                                              L.dyb, L.all_off);
-  // W_in[i] [de][d] -> [d][de];  W_out[i] [d][de] -> [de][d]
-  transpose_kernel<<<dim3((unsigned)((de / 64) * (d / 64)), (unsigned)E), dim3(kBlock), 0, s>>>(w_in, L.w_inT, de, d);
-  transpose_kernel<<<dim3((unsigned)((d / 64) * (de / 64)), (unsigned)E), dim3(kBlock), 0, s>>>(w_out, L.w_outT, d,
-                                                                                              de);
   group_count_kernel<PairRule::kPositive><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(preact, T, E, rows,
                                                                                               L.blk);
   group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(L.blk, nblk, E, de / GBN, L.pair_off, L.tile_up);
@@ -706,12 +619,12 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   hipError_t e = persistent_grid(bwd_pair_kernel, max_up_tiles, &grid_pair);
   if (e == hipSuccess) e = persistent_grid(tgemm_kernel, (int64_t)E * (d / TBM) * (de / TBN), &grid_t);
   if (e == hipSuccess)
-    e = de == 128 ? persistent_grid(grouped_down_kernel<128>, down_blocks(E, d, de), &grid_dn)
-                  : persistent_grid(grouped_down_kernel<256>, down_blocks(E, d, de), &grid_dn);
+    e = de == 128 ? persistent_grid(grouped_down_kernel<128, true>, down_blocks(E, d, de), &grid_dn)
+                  : persistent_grid(grouped_down_kernel<256, true>, down_blocks(E, d, de), &grid_dn);
   if (e != hipSuccess) return e;
 
   se.record(1, s);
-  PairArgs pa{x, L.dyb, L.pair_tok, L.pair_gate, w_in, L.w_outT, L.pair_off, L.tile_up, L.du, L.hg, L.dgp, d, de, E};
+  PairArgs pa{x, L.dyb, L.pair_tok, L.pair_gate, w_in, w_out, L.pair_off, L.tile_up, L.du, L.hg, L.dgp, d, de, E};
   bwd_pair_kernel<<<dim3((unsigned)grid_pair), dim3(kBlock), 0, s>>>(pa);
   se.record(2, s);
   bwd_router_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(kBlock), 0, s>>>(
@@ -730,12 +643,12 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   bwd_router_sum_kernel<<<dim3((unsigned)(((int64_t)E * d + kBlock - 1) / kBlock)), dim3(kBlock), 0, s>>>(
       L.wr_part, (int64_t)E * d, d_w_router);
   se.record(3, s);
-  // dx: per-pair dU W_in[i] rows (the forward's down GEMM on W_in^T), then the per-token sum
-  DownArgs dn{L.du, L.w_inT, L.pair_off, L.part, d, E};
+  // dx: per-pair dU W_in[i] rows (the forward's down GEMM, reading W_in k-major), then the per-token sum
+  DownArgs dn{L.du, w_in, L.pair_off, L.part, d, E};
   if (de == 128)
-    grouped_down_kernel<128><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
+    grouped_down_kernel<128, true><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
   else
-    grouped_down_kernel<256><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
+    grouped_down_kernel<256, true><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
   se.record(4, s);
   int cthreads = (d / 8 + 63) / 64 * 64;
   cthreads = cthreads < 64 ? 64 : (cthreads > 1024 ? 1024 : cthreads);

@@ -369,10 +369,79 @@ __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
   }
 }
 
+// ---- MFMA operands from k-major LDS rows by transpose loads ----
+// LDS rows of 128 bf16 (256 bytes), row k holding element j of contraction
+// index k.  An MFMA operand needs 8 consecutive k of one j per lane; the LDS
+// transpose load ds_read_b64_tr_b16 delivers that: within each 16-lane group,
+// lane L names 4 elements (8 bytes) and lane i receives element i % 4 of
+// lanes 4 j + i / 4, j = 0..3 (checked on gfx950), so lanes naming row
+// k0 + L / 4 at column c0 + 4 (L % 4) deliver rows k0 .. k0 + 3 of column
+// c0 + i to lane i.
+//
+// 16-byte chunk position of chunk c in LDS row r (an XOR with an even value:
+// the two chunks a 16-lane transpose read touches in a row stay adjacent, and
+// the rows read together land on different bank groups).
+__device__ __forceinline__ int tg_swz(int r) { return ((r & 3) | ((r >> 1) & 4)) << 1; }
+
+// Byte offset of 16-byte chunk c of k-major row r.
+__device__ __forceinline__ int tg_off(int r, int c) { return r * 256 + ((c ^ tg_swz(r)) << 4); }
+
+typedef short tg_v4i16 __attribute__((ext_vector_type(4)));
+
+// NS (4 or 2) MFMA operands of 16 columns c0 + 16 j .. +15, j < NS, over
+// rows 0..31: 2 NS transpose reads.  They are written as one asm block that
+// also waits for them (lgkmcnt), because the compiler's builtin for this load
+// makes it wait for every LDS DMA in flight first (vmcnt 0), which would
+// drain a DMA ring.
+template <int NS>
+__device__ __forceinline__ void tg_operands(const uint8_t* rows, int c0, int lane, u32x4 (&v)[NS]) {
+  static_assert(NS == 4 || NS == 2, "stripes");
+  const int L = lane & 15, k0 = 8 * (lane >> 4) + (L >> 2);
+  unsigned a[2 * NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int c = c0 + 16 * j + 4 * (L & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      a[2 * j + h] = (unsigned)(uintptr_t)(lvoid_t*)(rows + tg_off(k0 + 4 * h, c >> 3) + (c & 7) * 2);
+  }
+  tg_v4i16 o[2 * NS];
+  if constexpr (NS == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %6\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const u32x2 l2 = __builtin_bit_cast(u32x2, o[2 * j]), h2 = __builtin_bit_cast(u32x2, o[2 * j + 1]);
+    v[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+}
+
 // ---- down: Part[p][n] = sum_k H'[p][k] W_out[i][n][k], K = d_e in {128, 256} ----
 struct DownArgs {
   const uint16_t* hid;        // [P][K]
-  const uint16_t* w;          // [E][N][K]
+  const uint16_t* w;          // [E][N][K], or [E][K][N] (KMAJOR)
   const int64_t* pair_off;    // [E + 1]
   uint16_t* part;             // [P][N]
   int N, E;
@@ -415,7 +484,13 @@ __device__ __forceinline__ int stage_off(int r, int c) {
 // group, hidden loads and output stores repeat the group's last pair (the
 // same bytes again), so every path issues the same number of memory
 // operations and the compiler's waits stay partial.
-template <int K>
+//
+// KMAJOR: W[i] lies k-major ([K][N], the layout of W_in when the backward
+// multiplies by it).  The block then loads its slabs (K rows of the item's
+// kDownWaves SN columns) with whole-row loads, all in flight at once, and
+// turns them into the A-operand layout 32 k rows at a time: written to the
+// hidden-tile buffers as k-major 256-byte rows, read back by transpose loads.
+template <int K, bool KMAJOR = false>
 __global__ __launch_bounds__(kBlock) void grouped_down_kernel(DownArgs da) {
   constexpr int SN = down_slab<K>();
   constexpr int NB = SN / 16;                       // 16-column MFMA stripes
@@ -456,11 +531,46 @@ __global__ __launch_bounds__(kBlock) void grouped_down_kernel(DownArgs da) {
     auto phys = [&](int t) { return t + rot < tiles ? t + rot : t + rot - tiles; };
     // the slab: lane (m, g) holds row n0 + 16 b + m, elements 32 kk + 8 g .. +7
     u32x4 wa[NB][KK];
+    if constexpr (!KMAJOR) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const uint16_t* src = da.w + ((int64_t)i * N + (has_slab ? n0 : 0) + 16 * b + m) * K + 8 * g;
+      for (int b = 0; b < NB; ++b) {
+        const uint16_t* src = da.w + ((int64_t)i * N + (has_slab ? n0 : 0) + 16 * b + m) * K + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) wa[b][kk] = *reinterpret_cast<const u32x4*>(src + 32 * kk);
+        for (int kk = 0; kk < KK; ++kk) wa[b][kk] = *reinterpret_cast<const u32x4*>(src + 32 * kk);
+      }
+    } else {
+      constexpr int COLS = SN * kDownWaves;       // the item's columns: 256 (K = 128) or 128 (K = 256)
+      constexpr int CPK = COLS / 8;               // 16-byte chunks per k row
+      constexpr int RL = 32 * CPK / kBlock;       // chunks per thread per 32 k rows
+      static_assert(COLS % 128 == 0 && RL * kBlock == 32 * CPK && COLS / 128 * 32 * 256 <= 2 * kDownPairs * HB,
+                    "k-major staging geometry");
+      // thread chunk c = tid + j kBlock of each 32-row round: k row c / CPK,
+      // columns 8 (c % CPK) .. +7 of the item (past N: column 0, unused)
+      u32x4 raw[KK][RL];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int j = 0; j < RL; ++j) {
+          const int c = tid + j * kBlock;
+          const int col = grp * COLS + (c % CPK) * 8;
+          raw[kk][j] = *reinterpret_cast<const u32x4*>(da.w + ((int64_t)i * K + 32 * kk + c / CPK) * N +
+                                                       (col < N ? col : 0));
+        }
+      uint8_t* sbuf = &htile[0][0];  // COLS / 128 planes of 32 rows x 256 bytes
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int j = 0; j < RL; ++j) {
+          const int c = tid + j * kBlock, cc = c % CPK;
+          *reinterpret_cast<u32x4*>(sbuf + (cc >> 4) * (32 * 256) + tg_off(c / CPK, cc & 15)) = raw[kk][j];
+        }
+        __syncthreads();
+        u32x4 v[NB];
+        tg_operands(sbuf + ((w * SN) >> 7) * (32 * 256), (w * SN) & 127, lane, v);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wa[b][kk] = v[b];
+        __syncthreads();
+      }
     }
     // hidden tile pt: thread chunk c = tid + j kBlock is row c / HC, chunk c % HC
     u32x4 hr[HL];

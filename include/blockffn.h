@@ -369,7 +369,7 @@ size_t blockffn_fff_workspace_size(const blockffn_fff_layer* layer, int64_t n_to
  * right after its k-th timed stage, for k < n_events.  The timed stages of
  * the forward are the expert up-projection and down-projection (GEMV,
  * CHUNK_MFMA and DENSE modes), plus the per-token combine in GROUPED mode.
- * Those of the backward are: pair planning with the weight transposes, the
+ * Those of the backward are: the router quantities and pair planning, the
  * fused per-pair pass, the router and weight gradients, the per-pair input
  * gradient rows, and the per-token combine.  `events` are caller-created
  * hipEvents in caller memory that must stay valid while set; pass NULL to

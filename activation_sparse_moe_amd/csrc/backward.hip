@@ -78,6 +78,11 @@ __global__ __launch_bounds__(kBlock) void bwd_prep_kernel(const float* __restric
 }
 
 // ---- pair: U and Q for a 64-pair x 128-hidden tile, fused epilogue ----
+// A 64-wide k step stages 64 gathered x rows, 64 gathered dy rows and 128
+// W_in rows (128 bytes each, chunk-swizzled), and 64 k-major W_out rows of the
+// tile's 128 hidden units (256 bytes each), read back by transpose loads.  One
+// LDS buffer (48 KiB) lets two blocks share a CU; the registers hold the next
+// step while this one is multiplied.
 struct PairArgs {
   const uint16_t* x;        // [T][d]
   const uint16_t* dy;       // [T][d] bf16

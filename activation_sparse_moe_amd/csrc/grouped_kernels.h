@@ -490,8 +490,10 @@ __device__ __forceinline__ int stage_off(int r, int c) {
 // kDownWaves SN columns) with whole-row loads, all in flight at once, and
 // turns them into the A-operand layout 32 k rows at a time: written to the
 // hidden-tile buffers as k-major 256-byte rows, read back by transpose loads.
+// The staging registers live only while an item starts, so that variant is
+// capped for three waves per SIMD, which it meets without spilling.
 template <int K, bool KMAJOR = false>
-__global__ __launch_bounds__(kBlock) void grouped_down_kernel(DownArgs da) {
+__global__ __launch_bounds__(kBlock, KMAJOR ? 3 : 1) void grouped_down_kernel(DownArgs da) {
   constexpr int SN = down_slab<K>();
   constexpr int NB = SN / 16;                       // 16-column MFMA stripes
   constexpr int KK = K / 32;                        // 32-deep MFMA steps

@@ -376,10 +376,13 @@ constexpr int kTgLoadsPerStep = kTgDmaPerWave + 1;    // + the index DMA
 
 __device__ __attribute__((aligned(256))) const uint16_t kTgZeroRow[TBM] = {};
 
+// 52 KiB of LDS and at most 168 registers: three blocks (waves per SIMD) per CU.
 __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
   static_assert(TBM == 128 && TBN == 128 && TBK == 32, "tile geometry");
   static_assert(kTgDmaPerWave * 2 * 1024 == kTgOpBytes && kTgIdxSlots > kTgDepth, "ring geometry");
-  // one LDS object: the step ring, then each wave's index ring
+  // one LDS object, the step ring then each wave's index ring (with the
+  // index ring a separate object, the compiler waits for every DMA in flight
+  // before reading it)
   __shared__ __attribute__((aligned(16))) uint8_t lds[kTgRing * kTgSlotBytes + (kBlock / kWave) * kTgIdxSlots * 256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -17,6 +17,7 @@
 //   * route_valu_kernel (fp32, or L < 8 with a layer copy per unit): a
 //     bandwidth-bound GEMV; lane groups stride over d with 16-byte loads and
 //     reduce with cross-lane shuffles.
+#include "lds_stream.h"
 #include "mfma_stream.h"
 
 namespace bffn {
@@ -187,13 +188,10 @@ __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const 
 // are not stored.  The four per-wave partial sums meet in LDS and are added
 // in a fixed order by the epilogue (deterministic).
 //
-// A block takes tokens [t0, t0 + tb): one unit (tb = L, the unit's own layer
-// copy), or, when every unit uses the same layer, a whole token tile of 16 NT
-// tokens across units, so that the shared router is streamed once per tile
-// rather than once per unit.  Blocks that share the router start at
-// different stripe groups, which spreads their simultaneous reads of it.
-// Each output column depends only on its own token, so the grouping does not
-// change any result bit.
+// A block takes tokens [t0, t0 + tb); the launch gives it one unit (tb = L,
+// the unit's own layer copy).  (A router shared by every token goes to
+// route_ring_kernel.)  Blocks start at different stripe groups, which spreads
+// simultaneous reads of a router they share.
 // With one token tile the registers are capped for two waves per SIMD (two
 // blocks per CU): 30.8 us instead of 33.9 us for 512 chunk-8 units.
 template <int NT, int KIND>
@@ -247,6 +245,86 @@ __global__ __launch_bounds__(kBlock, NT == 1 ? 2 : 1) void route_mfma_kernel(Lay
   router_epilogue<KIND>(zp, 4, E, Lb, t0, b, s, la.eps, top_k, gates, masks, preact);
 }
 
+// Router shared by every token (one layer), one 16-token tile per block, by
+// DMA.  Streaming the router into registers in the MFMA layout makes every
+// load instruction touch 16 rows at 64 bytes each (half lines); there the
+// vector-memory pipeline of the CU, not L2, set the pace (measured: the
+// texture addresser busy 57% of the time at ~56 cycles per load, L2 hits at
+// ~260 cycles).  Here each wave streams its quarter of d through a private
+// ring of the chunk path's geometry (lds_stream.h): a step is 64 router rows
+// (one group of four stripes) and the tile's 16 token rows, 128 bytes each,
+// so every DMA instruction reads 8 whole lines.  Groups follow one another
+// (rotated per block, as in route_mfma_kernel); the partial sums of each
+// group go to LDS and the common epilogue adds them in a fixed order.
+constexpr int kRouteRingMaxE = 128;
+
+template <int KIND>
+__global__ __launch_bounds__(kBlock) void route_ring_kernel(LayerArgs la, const uint16_t* __restrict__ x, int64_t T,
+                                                           int top_k, float* __restrict__ gates,
+                                                           uint64_t* __restrict__ masks,
+                                                           float* __restrict__ preact) {
+  using G = RingGeom<1, false>;
+  constexpr int kRings = (kBlock / kWave) * kRingBufs * G::kBufBytes;
+  // one LDS object: the four waves' rings, then the partial sums [4][E][Lb]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kRings + 4 * kRouteRingMaxE * 16 * 4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int d = la.d, E = la.E;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int Lb = T - t0 < 16 ? (int)(T - t0) : 16;
+  uint8_t* bufs = lds + w * (kRingBufs * G::kBufBytes);
+  float* zp = reinterpret_cast<float*>(lds + kRings);
+  const uint16_t* wr = static_cast<const uint16_t*>(la.w_router);
+  const int kw = d >> 2;  // this wave's range of d
+  const int S = kw / kStepK;
+  const int nstripes = E >> 4, ngroups = (nstripes + 3) >> 2;
+  const int total = ngroups * S;
+  auto group_base = [&](int q) { return (int)((q + blockIdx.x) % ngroups) * 4; };
+  // step t: group t / S, k step t % S (past the end: the last step again)
+  auto issue = [&](int slot, int t) {
+    const int tc = t < total ? t : total - 1;
+    const int sb = group_base(tc / S);
+    const int k0 = w * kw + (tc % S) * kStepK;
+    uint8_t* buf = bufs + slot * G::kBufBytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int R = 8 * j + (lane >> 3);
+      const int st = sb + (R >> 4) < nstripes ? sb + (R >> 4) : nstripes - 1;  // missing stripes repeat one
+      dma16<kPolicyReuse>(wr + (int64_t)(st * 16 + (R & 15)) * d + k0 + dma_chunk_elems(R, lane), buf + j * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < G::kBInstr; ++j) {
+      const int n = 8 * j + (lane >> 3);  // tokens past the tile repeat one
+      dma16<kPolicyReuse>(x + (t0 + n % Lb) * d + k0 + dma_chunk_elems(n, lane), buf + kABytes + j * 1024);
+    }
+  };
+
+  issue(0, 0);
+  issue(1, 1);
+  f32x4 acc[4][1];
+  ring_zero<1>(acc);
+  for (int t = 0; t < total; ++t) {
+    issue((t + kRingBufs - 1) % kRingBufs, t + kRingBufs - 1);
+    wait_vmcnt<G::kWaitAhead>();
+    ring_mfma<1>(acc, bufs + (t % kRingBufs) * G::kBufBytes, m, g);
+    __builtin_amdgcn_sched_barrier(0);
+    if ((t + 1) % S == 0) {  // (uniform) group done: lane (m, g) holds rows 4 g + r of token m
+      const int sb = group_base(t / S);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (sb + st >= nstripes || m >= Lb) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zp[(w * E + (sb + st) * 16 + 4 * g + r) * Lb + m] = acc[st][0][r];
+      }
+      ring_zero<1>(acc);
+    }
+  }
+  wait_vmcnt<0>();  // the repeats land before the LDS is read or given up
+  __syncthreads();
+  router_epilogue<KIND>(zp, 4, E, Lb, t0, la.b_router, la.rms_scale, la.eps, top_k, gates, masks, preact);
+}
+
 }  // namespace
 
 bool route_uses_mfma(int d, int E, int chunk_len, int dtype) {
@@ -258,9 +336,12 @@ hipError_t launch_route_kind(const LayerArgs& la, const void* x, int64_t units, 
                              float* gates, uint64_t* masks, float* preact, hipStream_t s) {
   const int64_t T = units * L;
   const bool shared = la.n_layers == 1 && route_uses_mfma(la.d, la.E, 16, dtype);
-  if (shared || route_uses_mfma(la.d, la.E, L, dtype)) {
-    // one layer for all tokens: 16-token tiles; else one unit per block
-    const int tb = shared ? 16 : L;
+  if (shared && la.E <= kRouteRingMaxE) {  // (E never exceeds it: the layer check caps E at 128)
+    route_ring_kernel<KIND><<<dim3((unsigned)((T + 15) / 16)), dim3(kBlock), 0, s>>>(
+        la, static_cast<const uint16_t*>(x), T, top_k, gates, masks, preact);
+  } else if (route_uses_mfma(la.d, la.E, L, dtype)) {
+    // one unit per block, through the unit's own layer copy
+    const int tb = L;
     const int64_t blocks = (T + tb - 1) / tb;
     const size_t lds = sizeof(float) * 4 * la.E * tb;
     if (tb <= 16)

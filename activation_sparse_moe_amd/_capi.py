@@ -40,7 +40,6 @@ class BlockffnLayer(ctypes.Structure):
     _fields_ = [
         ("d", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("d_expert", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("reserved", ctypes.c_int32),
-        ("layer_stride", ctypes.c_int64),
         ("w_router", ctypes.c_void_p), ("b_router", ctypes.c_void_p), ("rms_scale", ctypes.c_void_p),
         ("w_in", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
     ]
@@ -49,7 +48,7 @@ class BlockffnLayer(ctypes.Structure):
 class BlockffnFffLayer(ctypes.Structure):
     _fields_ = [
         ("d", ctypes.c_int32), ("n_trees", ctypes.c_int32), ("depth", ctypes.c_int32), ("dtype", ctypes.c_int32),
-        ("activation", ctypes.c_int32), ("node_stride", ctypes.c_int32), ("layer_stride", ctypes.c_int64),
+        ("activation", ctypes.c_int32), ("node_stride", ctypes.c_int32),
         ("w_node", ctypes.c_void_p), ("b_node", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
     ]
 

@@ -58,10 +58,12 @@ class DeviceLayer:
     """`replicas` copies of one BlockFFN layer in a single device buffer.
 
     Every copy has the same internal layout, so copy r's tensors sit at
-    replica 0's addresses plus r * stride bytes, which is the stacked-layer
-    convention of the C ABI (chunk c uses copy c % n_layers).  The copies are
-    distinct memory, so a stack of them streams from HBM like a stack of
-    distinct layers.
+    replica 0's addresses plus r * stride bytes.  Passed to a call, the
+    copies become an array of layer descriptors (chunk c uses copy
+    c % n_layers), which the library recognises as evenly spaced.  The copies
+    are distinct memory, so a stack of them streams from HBM like a stack of
+    distinct layers.  A list of DeviceLayer objects (each in its own
+    allocation) may be passed wherever one DeviceLayer is accepted.
     """
 
     def __init__(self, d: int, n_experts: int, d_expert: int, dtype: int, rms_eps: float = 1e-6,
@@ -91,6 +93,9 @@ class DeviceLayer:
         return self.buffer[base:base + nbytes].view(dtype).view(*shape)
 
     def tensors(self, r: int = 0) -> dict:
+        if getattr(self, "_own", None) is not None:  # a layer made from the caller's tensors
+            assert r == 0, "a layer made from separate tensors has one copy"
+            return dict(self._own)
         td = _torch_dtype(self.dtype)
         E, d, de = self.n_experts, self.d, self.d_expert
         return dict(w_router=self._view("w_router", r, (E, d), td),
@@ -119,6 +124,26 @@ class DeviceLayer:
         return self
 
     @classmethod
+    def from_tensors(cls, w_router: torch.Tensor, w_in: torch.Tensor, w_out: torch.Tensor,
+                     b_router: Optional[torch.Tensor] = None, rms_scale: Optional[torch.Tensor] = None,
+                     rms_eps: float = 1e-6) -> "DeviceLayer":
+        """A layer over existing device tensors (each may be its own allocation, as a model's
+        parameters are); nothing is copied and the tensors must outlive the layer's use."""
+        E, d = w_router.shape
+        de = w_in.shape[1]
+        assert w_router.dtype == w_in.dtype == w_out.dtype and w_router.dtype in (torch.float32, torch.bfloat16)
+        assert w_in.shape == (E, de, d) and w_out.shape == (E, d, de)
+        for t in (w_router, w_in, w_out, b_router, rms_scale):
+            assert t is None or (t.is_contiguous() and t.device == w_router.device)
+        self = cls.__new__(cls)
+        self.d, self.n_experts, self.d_expert = d, E, de
+        self.dtype = F32 if w_router.dtype == torch.float32 else BF16
+        self.rms_eps, self.replicas, self.device = float(rms_eps), 1, w_router.device
+        self.stride, self.buffer, self._off = 0, None, None
+        self._own = dict(w_router=w_router, b_router=b_router, rms_scale=rms_scale, w_in=w_in, w_out=w_out)
+        return self
+
+    @classmethod
     def from_workload(cls, layer, device="cuda", replicas: int = 1) -> "DeviceLayer":
         return cls.from_arrays(layer.w_router, layer.b_router, layer.rms_scale, layer.w_in, layer.w_out,
                                F32 if layer.dtype == "f32" else BF16, layer.rms_eps, device, replicas)
@@ -129,11 +154,26 @@ class DeviceLayer:
             return self._desc
         t = self.tensors(0)
         self._desc = BlockffnLayer(self.d, self.n_experts, self.d_expert, self.dtype, self.rms_eps, 0,
-                                   self.stride, t["w_router"].data_ptr(),
+                                   t["w_router"].data_ptr(),
                                    t["b_router"].data_ptr() if t["b_router"] is not None else None,
                                    t["rms_scale"].data_ptr() if t["rms_scale"] is not None else None,
                                    t["w_in"].data_ptr(), t["w_out"].data_ptr())
         return self._desc
+
+    def descriptors(self, n: int):
+        """ctypes array of n descriptors: copy l % replicas for l < n (built once per n)."""
+        cache = self.__dict__.setdefault("_descs", {})
+        if n not in cache:
+            base = self.descriptor()
+            arr = (BlockffnLayer * n)()
+            for l in range(n):
+                off = (l % self.replicas) * self.stride
+                arr[l] = BlockffnLayer(self.d, self.n_experts, self.d_expert, self.dtype, self.rms_eps, 0,
+                                       base.w_router + off, base.b_router + off if base.b_router else None,
+                                       base.rms_scale + off if base.rms_scale else None, base.w_in + off,
+                                       base.w_out + off)
+            cache[n] = arr
+        return cache[n]
 
     @property
     def mask_words(self) -> int:
@@ -144,9 +184,10 @@ class DeviceLayer:
         should read one particular copy."""
         import copy as _copy
         v = _copy.copy(self)
+        v.__dict__.pop("_descs", None)
         base = self.descriptor()
         off = r * self.stride
-        v._desc = BlockffnLayer(self.d, self.n_experts, self.d_expert, self.dtype, self.rms_eps, 0, self.stride,
+        v._desc = BlockffnLayer(self.d, self.n_experts, self.d_expert, self.dtype, self.rms_eps, 0,
                                 base.w_router + off, base.b_router + off if base.b_router else None,
                                 base.rms_scale + off if base.rms_scale else None, base.w_in + off, base.w_out + off)
         v.replicas = 1
@@ -157,11 +198,25 @@ def tokens_to_device(x, dtype: int, device="cuda") -> torch.Tensor:
     return _to_device(x, dtype, device)
 
 
+def _layers(layer, n_layers: Optional[int]):
+    """(first DeviceLayer, ctypes descriptor array, count) for a call: a DeviceLayer's copies (all of them
+    unless n_layers says how many), or one descriptor per DeviceLayer of a sequence (each its copy 0)."""
+    if isinstance(layer, (list, tuple)):
+        assert n_layers is None or n_layers == len(layer), "n_layers must match the sequence length"
+        arr = (BlockffnLayer * len(layer))(*[ly.descriptor() for ly in layer])
+        return layer[0], arr, len(layer)
+    n = layer.replicas if n_layers is None else int(n_layers)
+    if n < 1:  # passed through so that the library reports it
+        return layer, ctypes.pointer(layer.descriptor()), n
+    return layer, layer.descriptors(n), n
+
+
 def blockffn_route(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, n_layers: Optional[int] = None,
                    gates: Optional[torch.Tensor] = None, token_masks: Optional[torch.Tensor] = None,
                    preact: Optional[torch.Tensor] = None, want_preact: bool = False, stream=None):
     """Router (ReLU + RMSNorm) -> (gates [T][E] f32, token_masks [T][W] int64 bit patterns, preact or None)."""
     T = x.shape[0]
+    layer, descs, nl = _layers(layer, n_layers)
     E = layer.n_experts
     if gates is None:
         gates = torch.empty((T, E), dtype=torch.float32, device=x.device)
@@ -169,9 +224,7 @@ def blockffn_route(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, n_layers
         token_masks = torch.empty((T, layer.mask_words), dtype=torch.int64, device=x.device)
     if want_preact and preact is None:
         preact = torch.empty((T, E), dtype=torch.float32, device=x.device)
-    desc = layer.descriptor()
-    nl = layer.replicas if n_layers is None else n_layers
-    check(load().blockffn_route(ctypes.byref(desc), nl, _ptr(x), T, chunk_len, _ptr(gates), _ptr(token_masks),
+    check(load().blockffn_route(descs, nl, _ptr(x), T, chunk_len, _ptr(gates), _ptr(token_masks),
                                 _ptr(preact), _stream(stream)), "blockffn_route")
     return gates, token_masks, preact
 
@@ -182,6 +235,7 @@ def blockffn_route_with(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, rou
                         want_preact: bool = False, stream=None):
     """Router with a selectable gate function ("blockffn", "topk_softmax" with top_k, "relu_sum")."""
     T = x.shape[0]
+    layer, descs, nl = _layers(layer, n_layers)
     E = layer.n_experts
     kind = ROUTERS[router] if isinstance(router, str) else int(router)
     if gates is None:
@@ -190,9 +244,7 @@ def blockffn_route_with(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, rou
         token_masks = torch.empty((T, layer.mask_words), dtype=torch.int64, device=x.device)
     if want_preact and preact is None:
         preact = torch.empty((T, E), dtype=torch.float32, device=x.device)
-    desc = layer.descriptor()
-    nl = layer.replicas if n_layers is None else n_layers
-    check(load().blockffn_route_with(ctypes.byref(desc), nl, _ptr(x), T, chunk_len, kind, top_k, _ptr(gates),
+    check(load().blockffn_route_with(descs, nl, _ptr(x), T, chunk_len, kind, top_k, _ptr(gates),
                                      _ptr(token_masks), _ptr(preact), _stream(stream)), "blockffn_route_with")
     return gates, token_masks, preact
 
@@ -218,11 +270,15 @@ def blockffn_chunk_union(n_experts: int, token_masks: torch.Tensor, chunk_len: i
 
 def blockffn_workspace_size(layer: DeviceLayer, n_tokens: int, chunk_len: int, mode="auto") -> int:
     m = MODES[mode] if isinstance(mode, str) else int(mode)
+    if isinstance(layer, (list, tuple)):
+        layer = layer[0]
     desc = layer.descriptor()
     return int(load().blockffn_workspace_size(ctypes.byref(desc), n_tokens, chunk_len, m))
 
 
 def alloc_workspace(layer: DeviceLayer, n_tokens: int, chunk_len: int, mode="auto") -> torch.Tensor:
+    if isinstance(layer, (list, tuple)):
+        layer = layer[0]
     nbytes = blockffn_workspace_size(layer, n_tokens, chunk_len, mode)
     # torch's caching allocator returns 256-byte aligned blocks
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=layer.device)
@@ -235,13 +291,12 @@ def blockffn_forward(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, gates:
     """Expert evaluation over each chunk's union -> y [T][d] fp32."""
     m = MODES[mode] if isinstance(mode, str) else int(mode)
     T = x.shape[0]
+    layer, descs, nl = _layers(layer, n_layers)
     if y is None:
         y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(layer, T, chunk_len, m)
-    desc = layer.descriptor()
-    nl = layer.replicas if n_layers is None else n_layers
-    check(load().blockffn_forward(ctypes.byref(desc), nl, _ptr(x), T, chunk_len, _ptr(gates), _ptr(active_count),
+    check(load().blockffn_forward(descs, nl, _ptr(x), T, chunk_len, _ptr(gates), _ptr(active_count),
                                   _ptr(active_list), m, _ptr(workspace), workspace.numel(), _ptr(y),
                                   _stream(stream)), "blockffn_forward")
     return y
@@ -335,8 +390,9 @@ class DeviceFffLayer:
     """`replicas` copies of one FFF tree layer in a single device buffer.
 
     Copy r holds the node rows, then b_node [P][N] (fp32, optional), at
-    replica 0's offsets plus r * stride bytes: the stacked-layer convention
-    of blockffn_fff_forward (token t uses copy t % n_layers).  With
+    replica 0's offsets plus r * stride bytes.  Passed to a call, the copies
+    become an array of descriptors (token t uses copy t % n_layers), which
+    the library recognises as evenly spaced.  With
     `interleave` (the default) each node's input and output rows sit next to
     each other, [P][N][2][d], so a visited node is one contiguous read;
     otherwise w_node [P][N][d] and w_out [P][N][d] are separate arrays."""
@@ -409,6 +465,7 @@ class DeviceFffLayer:
         import copy as _copy
         v = _copy.copy(self)
         v._desc = None
+        v.__dict__.pop("_descs", None)
         v._base = self._base + r * self.stride
         v.replicas = 1
         return v
@@ -418,10 +475,23 @@ class DeviceFffLayer:
             base = self.buffer.data_ptr() + self._base
             self._desc = BlockffnFffLayer(self.d, self.n_trees, self.depth, self.dtype,
                                           _capi.FFF_GELU_OUTPUT if self.post else _capi.FFF_GELU_NODES,
-                                          self.node_stride, self.stride, base + self._w_node_off,
+                                          self.node_stride, base + self._w_node_off,
                                           base + self._b_off if self._b_off is not None else None,
                                           base + self._w_out_off)
         return self._desc
+
+    def descriptors(self, n: int):
+        """ctypes array of n descriptors: copy l % replicas for l < n (built once per n)."""
+        cache = self.__dict__.setdefault("_descs", {})
+        if n not in cache:
+            b = self.descriptor()
+            arr = (BlockffnFffLayer * n)()
+            for l in range(n):
+                off = (l % self.replicas) * self.stride
+                arr[l] = BlockffnFffLayer(b.d, b.n_trees, b.depth, b.dtype, b.activation, b.node_stride,
+                                          b.w_node + off, b.b_node + off if b.b_node else None, b.w_out + off)
+            cache[n] = arr
+        return cache[n]
 
 
 def blockffn_fff_workspace_size(layer: DeviceFffLayer, n_tokens: int, split: int = 0) -> int:
@@ -440,6 +510,13 @@ def blockffn_fff_forward(layer: DeviceFffLayer, x: torch.Tensor, mode: str = "sp
     """FFF tree layer -> (y [T][d] f32, paths [T][P][D+1] i32 or None, node_preact [T][P][D+1] f32 or None).
     A workspace is allocated here when the call needs one and none is given."""
     T = x.shape[0]
+    if isinstance(layer, (list, tuple)):
+        assert n_layers is None or n_layers == len(layer), "n_layers must match the sequence length"
+        descs, nl = (BlockffnFffLayer * len(layer))(*[ly.descriptor() for ly in layer]), len(layer)
+        layer = layer[0]
+    else:
+        nl = layer.replicas if n_layers is None else int(n_layers)
+        descs = layer.descriptors(nl) if nl >= 1 else ctypes.pointer(layer.descriptor())
     if y is None:
         y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device)
     if want_paths and paths is None:
@@ -449,9 +526,8 @@ def blockffn_fff_forward(layer: DeviceFffLayer, x: torch.Tensor, mode: str = "sp
     if workspace is None:
         workspace = alloc_fff_workspace(layer, T, split)
     m = {"sparse": _capi.FFF_SPARSE, "dense": _capi.FFF_DENSE}[mode]
-    nl = layer.replicas if n_layers is None else n_layers
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check(load().blockffn_fff_forward(ctypes.byref(layer.descriptor()), nl, _ptr(x), T, m, int(split), _ptr(paths),
+    check(load().blockffn_fff_forward(descs, nl, _ptr(x), T, m, int(split), _ptr(paths),
                                       _ptr(node_preact), _ptr(workspace), ws_bytes, _ptr(y), _stream(stream)),
           "blockffn_fff_forward")
     return y, paths, node_preact

@@ -19,8 +19,16 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;  // four waves
 constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, each with its own L2
 
-// Kernel-side view of a (stack of) layer(s).  Layer l's tensors sit at
-// ptr + l * stride bytes; chunk c uses layer c % n_layers.
+// Kernel-side view of the layers a call's units cycle through: unit u uses
+// layer u % n_layers.  The named pointers are layer 0's.  Either the layers
+// lie evenly spaced in memory (layer l's tensors at ptr + l * stride bytes;
+// the host finds this out, and a single layer has stride 0), or listed == 1
+// and layer l's pointers are tab[tensor][l], at most kMaxListedLayers of
+// them.  The table is a kernel argument: a lookup is one scalar load from
+// the kernel-argument segment.
+constexpr int kMaxListedLayers = 32;
+enum LayerTensor { kTWRouter = 0, kTBRouter = 1, kTScale = 2, kTWIn = 3, kTWOut = 4, kLayerTensors = 5 };
+
 struct LayerArgs {
   const void* w_router;
   const float* b_router;
@@ -29,14 +37,20 @@ struct LayerArgs {
   const void* w_out;
   int64_t stride;
   int32_t n_layers;
+  int32_t listed;
   int32_t d, E, de;
   float eps;
+  const void* tab[kLayerTensors][kMaxListedLayers];
 };
 
-template <typename P>
-__device__ __forceinline__ P layer_ptr(P p, int64_t stride, int64_t unit, int n_layers) {
-  if (p == nullptr || n_layers == 1) return p;
-  return reinterpret_cast<P>(reinterpret_cast<const char*>(p) + stride * (unit % n_layers));
+// Tensor K of the layer that unit `unit` uses; p0 is layer 0's pointer.
+template <int K, typename P>
+__device__ __forceinline__ P layer_ptr(const LayerArgs& la, P p0, int64_t unit) {
+  if (la.n_layers == 1) return p0;
+  const int64_t l = unit % la.n_layers;
+  if (la.listed) return reinterpret_cast<P>(la.tab[K][l]);
+  if (p0 == nullptr) return p0;
+  return reinterpret_cast<P>(reinterpret_cast<const char*>(p0) + la.stride * l);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }

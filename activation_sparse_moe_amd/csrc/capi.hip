@@ -79,7 +79,7 @@ int check_experts(int32_t E) {
   return BLOCKFFN_OK;
 }
 
-int check_layer(const blockffn_layer* ly, int32_t n_layers) {
+int check_layer(const blockffn_layer* ly) {
   if (!ly) return fail(BLOCKFFN_ERR_NULL, "layer descriptor is NULL");
   if (ly->dtype != BLOCKFFN_F32 && ly->dtype != BLOCKFFN_BF16)
     return fail(BLOCKFFN_ERR_DTYPE, "unknown dtype %d", ly->dtype);
@@ -91,11 +91,6 @@ int check_layer(const blockffn_layer* ly, int32_t n_layers) {
   if (!std::isfinite(ly->rms_eps) || ly->rms_eps < 0.f)
     return fail(BLOCKFFN_ERR_SHAPE, "rms_eps must be finite and >= 0");
   if (ly->reserved != 0) return fail(BLOCKFFN_ERR_SHAPE, "reserved field must be 0");
-  if (n_layers < 1) return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d < 1", n_layers);
-  if (n_layers > 1 && ly->layer_stride <= 0)
-    return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d > 1 needs a positive layer_stride", n_layers);
-  if (n_layers > 1 && ly->layer_stride % 256 != 0)
-    return fail(BLOCKFFN_ERR_ALIGN, "layer_stride %lld is not a multiple of 256", (long long)ly->layer_stride);
   if (!ly->w_router || !ly->w_in || !ly->w_out)
     return fail(BLOCKFFN_ERR_NULL, "w_router, w_in and w_out must all be non-NULL");
   if (!aligned(ly->w_router, 16) || !aligned(ly->w_in, 16) || !aligned(ly->w_out, 16))
@@ -105,20 +100,110 @@ int check_layer(const blockffn_layer* ly, int32_t n_layers) {
   return BLOCKFFN_OK;
 }
 
-bffn::LayerArgs layer_args(const blockffn_layer* ly, int32_t n_layers) {
-  bffn::LayerArgs la;
-  la.w_router = ly->w_router;
-  la.b_router = ly->b_router;
-  la.rms_scale = ly->rms_scale;
-  la.w_in = ly->w_in;
-  la.w_out = ly->w_out;
-  la.stride = n_layers > 1 ? ly->layer_stride : 0;
-  la.n_layers = n_layers;
-  la.d = ly->d;
-  la.E = ly->n_experts;
-  la.de = ly->d_expert;
-  la.eps = ly->rms_eps;
-  return la;
+// The pointers of descriptor l, in bffn::LayerTensor order.
+void layer_ptrs(const blockffn_layer& ly, const void* p[bffn::kLayerTensors]) {
+  p[bffn::kTWRouter] = ly.w_router;
+  p[bffn::kTBRouter] = ly.b_router;
+  p[bffn::kTScale] = ly.rms_scale;
+  p[bffn::kTWIn] = ly.w_in;
+  p[bffn::kTWOut] = ly.w_out;
+}
+
+// Reduces an array of per-unit layers to what the kernels index: the
+// shortest period p (layers[l] == layers[l % p] for every l, p dividing n),
+// then either an even spacing of that many layers (every pointer of layer
+// l + 1 the same number of bytes past layer l's, NULL pointers NULL in
+// every layer) or a table of at most kMaxListedLayers.  Host only.
+template <int K, typename Desc, typename Ptrs>
+int reduce_layers(const Desc* layers, int32_t n, Ptrs get_ptrs, int32_t* n_eff, int64_t* stride, bool* listed,
+                  const void* tab[K][bffn::kMaxListedLayers]) {
+  auto ptrs = [&](int l, const void* p[K]) { get_ptrs(layers[l], p); };
+  auto same = [&](int a, int b) {
+    const void *pa[K], *pb[K];
+    ptrs(a, pa);
+    ptrs(b, pb);
+    for (int k = 0; k < K; ++k)
+      if (pa[k] != pb[k]) return false;
+    return true;
+  };
+  int32_t p = n;
+  for (int32_t q = 1; q < n; ++q) {
+    if (n % q != 0) continue;
+    bool periodic = true;
+    for (int32_t l = q; l < n && periodic; ++l) periodic = same(l, l % q);
+    if (periodic) {
+      p = q;
+      break;
+    }
+  }
+  *n_eff = p;
+  *stride = 0;
+  *listed = false;
+  if (p == 1) return BLOCKFFN_OK;
+  const void *p0[K], *p1[K];
+  ptrs(0, p0);
+  ptrs(1, p1);
+  const int64_t s = (int64_t)(reinterpret_cast<uintptr_t>(p1[0]) - reinterpret_cast<uintptr_t>(p0[0]));
+  bool even = true;
+  for (int32_t l = 1; l < p && even; ++l) {
+    const void* pl[K];
+    ptrs(l, pl);
+    for (int k = 0; k < K && even; ++k) {
+      if ((p0[k] == nullptr) != (pl[k] == nullptr)) even = false;
+      else if (p0[k] && (int64_t)(reinterpret_cast<uintptr_t>(pl[k]) - reinterpret_cast<uintptr_t>(p0[k])) != s * l)
+        even = false;
+    }
+  }
+  if (even) {
+    *stride = s;
+    return BLOCKFFN_OK;
+  }
+  if (p > bffn::kMaxListedLayers)
+    return fail(BLOCKFFN_ERR_LAYERS,
+                "%d distinct layers that are not evenly spaced in memory exceed the %d one call can list; "
+                "split the call or place the layers at a fixed spacing", p, bffn::kMaxListedLayers);
+  *listed = true;
+  for (int32_t l = 0; l < p; ++l) {
+    const void* pl[K];
+    ptrs(l, pl);
+    for (int k = 0; k < K; ++k) tab[k][l] = pl[k];
+  }
+  return BLOCKFFN_OK;
+}
+
+// Validates an array of n_layers descriptors (each one, and that they share
+// one shape) and builds the kernels' view of it.  Host only: nothing is
+// enqueued, so a failure leaves the stream untouched.
+int layer_args(const blockffn_layer* layers, int32_t n_layers, bffn::LayerArgs* la) {
+  if (!layers) return fail(BLOCKFFN_ERR_NULL, "layer descriptor array is NULL");
+  if (n_layers < 1) return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d < 1", n_layers);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const blockffn_layer& a = layers[0];
+    const blockffn_layer& b = layers[l];
+    if (int r = check_layer(&b)) return r;
+    if (b.d != a.d || b.n_experts != a.n_experts || b.d_expert != a.d_expert || b.dtype != a.dtype ||
+        b.rms_eps != a.rms_eps)
+      return fail(BLOCKFFN_ERR_LAYERS, "layer %d differs from layer 0 in d, n_experts, d_expert, dtype or rms_eps", l);
+  }
+  const blockffn_layer* ly = &layers[0];
+  *la = bffn::LayerArgs{};
+  la->w_router = ly->w_router;
+  la->b_router = ly->b_router;
+  la->rms_scale = ly->rms_scale;
+  la->w_in = ly->w_in;
+  la->w_out = ly->w_out;
+  la->d = ly->d;
+  la->E = ly->n_experts;
+  la->de = ly->d_expert;
+  la->eps = ly->rms_eps;
+  bool listed = false;
+  int32_t n_eff = 1;
+  if (int r = reduce_layers<bffn::kLayerTensors>(layers, n_layers, layer_ptrs, &n_eff, &la->stride, &listed,
+                                                 la->tab))
+    return r;
+  la->n_layers = n_eff;
+  la->listed = listed ? 1 : 0;
+  return BLOCKFFN_OK;
 }
 
 enum class Path { kGemv, kMfma, kMfmaSplit, kGrouped };
@@ -204,36 +289,36 @@ int hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
-BFFN_EXPORT int blockffn_route(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+BFFN_EXPORT int blockffn_route(const blockffn_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
                                int32_t chunk_len, float* gates, uint64_t* token_masks, float* preact,
                                hipStream_t stream) {
-  if (int r = check_layer(layer, n_layers)) return r;
+  bffn::LayerArgs la;
+  if (int r = layer_args(layers, n_layers, &la)) return r;
   if (int r = check_chunking(n_tokens, chunk_len)) return r;
   if (n_tokens == 0) return BLOCKFFN_OK;  // nothing is read or written; buffers may be NULL
   if (!x || !gates || !token_masks) return fail(BLOCKFFN_ERR_NULL, "x, gates and token_masks must be non-NULL");
   if (!aligned(x, 16) || !aligned(gates, 4) || !aligned(token_masks, 8) || !aligned(preact, 4))
     return fail(BLOCKFFN_ERR_ALIGN, "x must be 16-byte, gates/preact 4-byte and token_masks 8-byte aligned");
-  const bffn::LayerArgs la = layer_args(layer, n_layers);
-  return hip_status(bffn::launch_route(la, x, n_tokens, chunk_len, layer->dtype, BLOCKFFN_ROUTER_BLOCKFFN, 0, gates,
+  return hip_status(bffn::launch_route(la, x, n_tokens, chunk_len, layers->dtype, BLOCKFFN_ROUTER_BLOCKFFN, 0, gates,
                                        token_masks, preact, stream),
                     "router launch");
 }
 
-BFFN_EXPORT int blockffn_route_with(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+BFFN_EXPORT int blockffn_route_with(const blockffn_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
                                     int32_t chunk_len, int32_t router, int32_t top_k, float* gates,
                                     uint64_t* token_masks, float* preact, hipStream_t stream) {
-  if (int r = check_layer(layer, n_layers)) return r;
+  bffn::LayerArgs la;
+  if (int r = layer_args(layers, n_layers, &la)) return r;
   if (int r = check_chunking(n_tokens, chunk_len)) return r;
   if (router != BLOCKFFN_ROUTER_BLOCKFFN && router != BLOCKFFN_ROUTER_TOPK_SOFTMAX && router != BLOCKFFN_ROUTER_RELU_SUM)
     return fail(BLOCKFFN_ERR_MODE, "unknown router %d", router);
-  if (router == BLOCKFFN_ROUTER_TOPK_SOFTMAX && (top_k < 1 || top_k > layer->n_experts))
-    return fail(BLOCKFFN_ERR_SHAPE, "top_k %d outside [1, n_experts %d]", top_k, layer->n_experts);
+  if (router == BLOCKFFN_ROUTER_TOPK_SOFTMAX && (top_k < 1 || top_k > layers->n_experts))
+    return fail(BLOCKFFN_ERR_SHAPE, "top_k %d outside [1, n_experts %d]", top_k, layers->n_experts);
   if (n_tokens == 0) return BLOCKFFN_OK;
   if (!x || !gates || !token_masks) return fail(BLOCKFFN_ERR_NULL, "x, gates and token_masks must be non-NULL");
   if (!aligned(x, 16) || !aligned(gates, 4) || !aligned(token_masks, 8) || !aligned(preact, 4))
     return fail(BLOCKFFN_ERR_ALIGN, "x must be 16-byte, gates/preact 4-byte and token_masks 8-byte aligned");
-  const bffn::LayerArgs la = layer_args(layer, n_layers);
-  return hip_status(bffn::launch_route(la, x, n_tokens, chunk_len, layer->dtype, router, top_k, gates, token_masks,
+  return hip_status(bffn::launch_route(la, x, n_tokens, chunk_len, layers->dtype, router, top_k, gates, token_masks,
                                        preact, stream),
                     "router launch");
 }
@@ -255,24 +340,27 @@ BFFN_EXPORT int blockffn_chunk_union(int32_t n_experts, const uint64_t* token_ma
 
 BFFN_EXPORT size_t blockffn_workspace_size(const blockffn_layer* layer, int64_t n_tokens, int32_t chunk_len,
                                            int32_t mode) {
-  if (check_layer(layer, 1) != BLOCKFFN_OK || check_chunking(n_tokens, chunk_len) != BLOCKFFN_OK) return 0;
+  if (check_layer(layer) != BLOCKFFN_OK || check_chunking(n_tokens, chunk_len) != BLOCKFFN_OK) return 0;
   Path path;
   bool dense;
   if (resolve_mode(layer, n_tokens, chunk_len, mode, &path, &dense) != BLOCKFFN_OK) return 0;
   return workspace_bytes_for(layer, n_tokens, chunk_len, path);
 }
 
-BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+BFFN_EXPORT int blockffn_forward(const blockffn_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
                                  int32_t chunk_len, const float* gates, const int32_t* active_count,
                                  const int32_t* active_list, int32_t mode, void* workspace, size_t workspace_bytes,
                                  float* y, hipStream_t stream) {
-  if (int r = check_layer(layer, n_layers)) return r;
+  bffn::LayerArgs la;
+  if (int r = layer_args(layers, n_layers, &la)) return r;
+  const blockffn_layer* layer = layers;
   if (int r = check_chunking(n_tokens, chunk_len)) return r;
   Path path;
   bool dense;
   if (int r = resolve_mode(layer, n_tokens, chunk_len, mode, &path, &dense)) return r;
-  if (path == Path::kGrouped && n_layers != 1)
-    return fail(BLOCKFFN_ERR_LAYERS, "GROUPED runs one batch through one layer (n_layers %d)", n_layers);
+  if (path == Path::kGrouped && la.n_layers != 1)
+    return fail(BLOCKFFN_ERR_LAYERS, "GROUPED runs one batch through one layer (%d distinct layers given)",
+                la.n_layers);
   if (path == Path::kGrouped && n_tokens * layer->n_experts > INT32_MAX)
     return fail(BLOCKFFN_ERR_SHAPE, "GROUPED indexes pairs with 32 bits: n_tokens x n_experts must stay below 2^31");
   if (n_tokens == 0) return BLOCKFFN_OK;
@@ -287,7 +375,6 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, 
   if (!aligned(workspace, 256)) return fail(BLOCKFFN_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (workspace_bytes < need)
     return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  const bffn::LayerArgs la = layer_args(layer, n_layers);
   hipError_t e;
   if (path == Path::kGrouped)
     e = bffn::launch_forward_grouped(la, static_cast<const uint16_t*>(x), n_tokens, gates, workspace, y,
@@ -328,7 +415,7 @@ BFFN_EXPORT int blockffn_sparsity_stats(int32_t n_experts, const uint64_t* token
 namespace {
 
 int check_backward(const blockffn_layer* layer, int64_t n_tokens) {
-  if (int r = check_layer(layer, 1)) return r;
+  if (int r = check_layer(layer)) return r;
   if (n_tokens < 0) return fail(BLOCKFFN_ERR_SHAPE, "n_tokens %lld is negative", (long long)n_tokens);
   if (!bffn::grouped_supported(layer->d, layer->d_expert, layer->dtype))
     return fail(BLOCKFFN_ERR_MODE, "the backward needs bf16, d a multiple of 128 and d_expert 128 or 256");
@@ -362,7 +449,8 @@ BFFN_EXPORT int blockffn_backward(const blockffn_layer* layer, const void* x, in
   if (!aligned(workspace, 256)) return fail(BLOCKFFN_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (workspace_bytes < need)
     return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  const bffn::LayerArgs la = layer_args(layer, 1);
+  bffn::LayerArgs la;
+  if (int r = layer_args(layer, 1, &la)) return r;
   return hip_status(bffn::launch_backward(la, static_cast<const uint16_t*>(x), n_tokens, preact, dy, dz_extra,
                                           workspace, dx,
                                           grads->d_w_router, grads->d_b_router, grads->d_rms_scale, grads->d_w_in,
@@ -397,7 +485,7 @@ BFFN_EXPORT int blockffn_cls_losses(int32_t n_experts, const float* preact, int6
 
 namespace {
 
-int check_fff_layer(const blockffn_fff_layer* layer, int32_t n_layers) {
+int check_fff_layer(const blockffn_fff_layer* layer) {
   if (!layer) return fail(BLOCKFFN_ERR_NULL, "layer descriptor is NULL");
   const blockffn_fff_layer& ly = *layer;
   if (ly.dtype != BLOCKFFN_F32 && ly.dtype != BLOCKFFN_BF16) return fail(BLOCKFFN_ERR_DTYPE, "unknown dtype %d", ly.dtype);
@@ -412,15 +500,39 @@ int check_fff_layer(const blockffn_fff_layer* layer, int32_t n_layers) {
   if (ly.node_stride != 0 && (ly.node_stride < row_bytes || ly.node_stride % 16 != 0))
     return fail(BLOCKFFN_ERR_SHAPE, "node_stride %d must be 0 or a multiple of 16 of at least %lld", ly.node_stride,
                 (long long)row_bytes);
-  if (n_layers < 1) return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d < 1", n_layers);
-  if (n_layers > 1 && ly.layer_stride <= 0)
-    return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d > 1 needs a positive layer_stride", n_layers);
-  if (n_layers > 1 && ly.layer_stride % 256 != 0)
-    return fail(BLOCKFFN_ERR_ALIGN, "layer_stride %lld is not a multiple of 256", (long long)ly.layer_stride);
   if (!ly.w_node || !ly.w_out) return fail(BLOCKFFN_ERR_NULL, "w_node and w_out must be non-NULL");
   if (!aligned(ly.w_node, 16) || !aligned(ly.w_out, 16))
     return fail(BLOCKFFN_ERR_ALIGN, "w_node and w_out must be 16-byte aligned");
   if (!aligned(ly.b_node, 4)) return fail(BLOCKFFN_ERR_ALIGN, "b_node must be 4-byte aligned");
+  return BLOCKFFN_OK;
+}
+
+void fff_ptrs(const blockffn_fff_layer& ly, const void* p[3]) {
+  p[0] = ly.w_node;
+  p[1] = ly.b_node;
+  p[2] = ly.w_out;
+}
+
+// Validates an array of FFF layer descriptors of one shape and reduces it
+// as layer_args does.  Host only.
+int fff_layer_set(const blockffn_fff_layer* layers, int32_t n_layers, bffn::FffLayerSet* set) {
+  if (!layers) return fail(BLOCKFFN_ERR_NULL, "layer descriptor array is NULL");
+  if (n_layers < 1) return fail(BLOCKFFN_ERR_LAYERS, "n_layers %d < 1", n_layers);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const blockffn_fff_layer& a = layers[0];
+    const blockffn_fff_layer& b = layers[l];
+    if (int r = check_fff_layer(&b)) return r;
+    if (b.d != a.d || b.n_trees != a.n_trees || b.depth != a.depth || b.dtype != a.dtype ||
+        b.activation != a.activation || b.node_stride != a.node_stride)
+      return fail(BLOCKFFN_ERR_LAYERS,
+                  "layer %d differs from layer 0 in d, n_trees, depth, dtype, activation or node_stride", l);
+  }
+  *set = bffn::FffLayerSet{};
+  bool listed = false;
+  int32_t n_eff = 1;
+  if (int r = reduce_layers<3>(layers, n_layers, fff_ptrs, &n_eff, &set->stride, &listed, set->tab)) return r;
+  set->n_layers = n_eff;
+  set->listed = listed ? 1 : 0;
   return BLOCKFFN_OK;
 }
 
@@ -438,16 +550,17 @@ int check_fff_split(const blockffn_fff_layer& ly, int64_t n_tokens, int32_t spli
 }  // namespace
 
 BFFN_EXPORT size_t blockffn_fff_workspace_size(const blockffn_fff_layer* layer, int64_t n_tokens, int32_t split) {
-  if (check_fff_layer(layer, 1) != BLOCKFFN_OK || check_fff_split(*layer, n_tokens, split) != BLOCKFFN_OK) return 0;
+  if (check_fff_layer(layer) != BLOCKFFN_OK || check_fff_split(*layer, n_tokens, split) != BLOCKFFN_OK) return 0;
   return bffn::fff_workspace_bytes(layer->d, layer->n_trees, n_tokens, split);
 }
 
-BFFN_EXPORT int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_layers, const void* x,
+BFFN_EXPORT int blockffn_fff_forward(const blockffn_fff_layer* layers, int32_t n_layers, const void* x,
                                      int64_t n_tokens, int32_t mode, int32_t split, int32_t* paths,
                                      float* node_preact, void* workspace, size_t workspace_bytes, float* y,
                                      hipStream_t stream) {
-  if (int r = check_fff_layer(layer, n_layers)) return r;
-  const blockffn_fff_layer& ly = *layer;
+  bffn::FffLayerSet set;
+  if (int r = fff_layer_set(layers, n_layers, &set)) return r;
+  const blockffn_fff_layer& ly = *layers;
   if (mode != BLOCKFFN_FFF_SPARSE && mode != BLOCKFFN_FFF_DENSE) return fail(BLOCKFFN_ERR_MODE, "unknown mode %d", mode);
   if (mode == BLOCKFFN_FFF_DENSE && (paths || node_preact))
     return fail(BLOCKFFN_ERR_MODE, "paths and node_preact must be NULL in dense mode");
@@ -460,7 +573,7 @@ BFFN_EXPORT int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_
   const size_t need = bffn::fff_workspace_bytes(ly.d, ly.n_trees, n_tokens, split);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
-  return hip_status(bffn::launch_fff_forward(ly, n_layers, x, n_tokens, mode == BLOCKFFN_FFF_DENSE, split, paths,
+  return hip_status(bffn::launch_fff_forward(ly, set, x, n_tokens, mode == BLOCKFFN_FFF_DENSE, split, paths,
                                              node_preact, workspace, y, stream),
                     "fff forward launch");
 }

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kBlock) void up_valu_kernel(LayerArgs la, const T* 
   const int n_active = DENSE ? E : count[unit];
   if (slot >= n_active) return;
   const int i = DENSE ? slot : list[unit * E + slot];
-  const T* wi = layer_ptr(static_cast<const T*>(la.w_in), la.stride, unit, la.n_layers) + (int64_t)i * de * d;
+  const T* wi = layer_ptr<kTWIn>(la, static_cast<const T*>(la.w_in), unit) + (int64_t)i * de * d;
   constexpr int VEC = Vec16<T>::kElems;
   const int rpp = 64 / lpr, lg = lane / lpr, li = lane % lpr;
   const int64_t t0 = unit * L;
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kBlock) void down_valu_kernel(LayerArgs la, int64_t
   if (k0 >= d) return;
   const int k_end = min(d, k0 + rows_per_wave);
   const int n_active = DENSE ? E : count[unit];
-  const T* wo_base = layer_ptr(static_cast<const T*>(la.w_out), la.stride, unit, la.n_layers);
+  const T* wo_base = layer_ptr<kTWOut>(la, static_cast<const T*>(la.w_out), unit);
   constexpr int VEC = Vec16<T>::kElems;
   const int rpp = 64 / lpr, lg = lane / lpr, li = lane % lpr;
   const int64_t t0 = unit * L;

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
   const uint16_t* b_src[G::kBInstr];
   const float* g_src;
   auto point = [&](const UpItem& it) {
-    const uint16_t* wi = layer_ptr(static_cast<const uint16_t*>(la.w_in), la.stride, it.unit, la.n_layers);
+    const uint16_t* wi = layer_ptr<kTWIn>(la, static_cast<const uint16_t*>(la.w_in), it.unit);
     const int k0 = it.kp * nsteps * kStepK;  // first k of the item's range
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kBlock) void down_mfma_kernel(LayerArgs la, int64_t
   auto issue = [&](int slot_buf, const DownItem& it, int k) {
     const int sl = it.s0 + k / spe, j0 = (k % spe) * kStepK;
     const int i = DENSE ? sl : list[it.unit * E + sl];
-    const uint16_t* wo = layer_ptr(static_cast<const uint16_t*>(la.w_out), la.stride, it.unit, la.n_layers);
+    const uint16_t* wo = layer_ptr<kTWOut>(la, static_cast<const uint16_t*>(la.w_out), it.unit);
     const uint16_t* wbase = wo + ((int64_t)i * d + it.kb * 64) * de + j0;
     const uint16_t* hb = hbuf + ((it.unit * E + sl) * L) * (int64_t)de + j0;
     uint8_t* buf = bufs + slot_buf * G::kBufBytes;

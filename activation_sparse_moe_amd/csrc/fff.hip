@@ -50,6 +50,7 @@ struct FffArgs {
   int64_t stride;       // bytes between consecutive layers (0 with one layer)
   int64_t node_stride;  // bytes between consecutive nodes' rows
   int32_t n_layers;
+  int32_t listed;       // 1: layer l's pointers are tab[*][l]
   int32_t P, D;
   int32_t post, dense;
   const uint8_t* x;
@@ -59,6 +60,7 @@ struct FffArgs {
   int32_t G;          // blocks per token
   int32_t per_group;  // trees per block
   float* partial;     // [T][G][d] when G > 1
+  const void* tab[3][kMaxListedLayers];  // w_node, b_node, w_out of each listed layer
 };
 
 // exact GELU, c Phi(c)
@@ -160,11 +162,13 @@ __global__ __launch_bounds__(kFffWaves * kWave) void fff_kernel(FffArgs a) {
   const int64_t t = (int64_t)(blockIdx.x / (unsigned)a.G);
   const int g = (int)(blockIdx.x % (unsigned)a.G);
   const int64_t layer = a.n_layers > 1 ? t % a.n_layers : 0;
+  const bool listed = a.listed && a.n_layers > 1;
   W wk{a,
-       a.w_node + layer * a.stride,
-       a.w_out + layer * a.stride,
-       a.b_node ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.b_node) + layer * a.stride)
-                : nullptr,
+       listed ? static_cast<const uint8_t*>(a.tab[0][layer]) : a.w_node + layer * a.stride,
+       listed ? static_cast<const uint8_t*>(a.tab[2][layer]) : a.w_out + layer * a.stride,
+       listed   ? static_cast<const float*>(a.tab[1][layer])
+       : a.b_node ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.b_node) + layer * a.stride)
+                  : nullptr,
        t,
        (int64_t(1) << (a.D + 1)) - 1,
        (int)(threadIdx.x & 63),
@@ -277,16 +281,20 @@ bool fff_width_supported(int d, int dtype) {
   return d > 0 && (d * esz) % 1024 == 0 && d * esz / 1024 <= kFffMaxPieces;
 }
 
-hipError_t launch_fff_forward(const blockffn_fff_layer& ly, int n_layers, const void* x, int64_t n_tokens, bool dense,
-                              int split, int32_t* paths, float* preact, void* workspace, float* y, hipStream_t s) {
+hipError_t launch_fff_forward(const blockffn_fff_layer& ly, const FffLayerSet& set, const void* x, int64_t n_tokens,
+                              bool dense, int split, int32_t* paths, float* preact, void* workspace, float* y,
+                              hipStream_t s) {
   if (n_tokens == 0) return hipSuccess;
   FffArgs a;
   a.w_node = static_cast<const uint8_t*>(ly.w_node);
   a.b_node = ly.b_node;
   a.w_out = static_cast<const uint8_t*>(ly.w_out);
-  a.stride = n_layers > 1 ? ly.layer_stride : 0;
+  a.stride = set.n_layers > 1 ? set.stride : 0;
   a.node_stride = ly.node_stride ? ly.node_stride : (int64_t)ly.d * (ly.dtype == BLOCKFFN_BF16 ? 2 : 4);
-  a.n_layers = n_layers;
+  a.n_layers = set.n_layers;
+  a.listed = set.listed;
+  for (int k = 0; k < 3; ++k)
+    for (int l = 0; l < kMaxListedLayers; ++l) a.tab[k][l] = set.tab[k][l];
   a.P = ly.n_trees;
   a.D = ly.depth;
   a.post = ly.activation == BLOCKFFN_FFF_GELU_OUTPUT;

@@ -153,9 +153,9 @@ __global__ __launch_bounds__(kBlock) void route_valu_kernel(LayerArgs la, const 
                                                             float* __restrict__ preact) {
   extern __shared__ float zp[];  // [E][L]
   const int64_t unit = blockIdx.x;
-  const T* wr = layer_ptr(static_cast<const T*>(la.w_router), la.stride, unit, la.n_layers);
-  const float* b = layer_ptr(la.b_router, la.stride, unit, la.n_layers);
-  const float* s = layer_ptr(la.rms_scale, la.stride, unit, la.n_layers);
+  const T* wr = layer_ptr<kTWRouter>(la, static_cast<const T*>(la.w_router), unit);
+  const float* b = layer_ptr<kTBRouter>(la, la.b_router, unit);
+  const float* s = layer_ptr<kTScale>(la, la.rms_scale, unit);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int d = la.d, E = la.E;
   constexpr int VEC = 16 / sizeof(T);
@@ -205,9 +205,9 @@ __global__ __launch_bounds__(kBlock, NT == 1 ? 2 : 1) void route_mfma_kernel(Lay
   const int64_t t0 = (int64_t)blockIdx.x * tb;
   const int Lb = T - t0 < tb ? (int)(T - t0) : tb;  // tokens of this block
   const int64_t unit = t0 / L;
-  const uint16_t* wr = layer_ptr(static_cast<const uint16_t*>(la.w_router), la.stride, unit, la.n_layers);
-  const float* b = layer_ptr(la.b_router, la.stride, unit, la.n_layers);
-  const float* s = layer_ptr(la.rms_scale, la.stride, unit, la.n_layers);
+  const uint16_t* wr = layer_ptr<kTWRouter>(la, static_cast<const uint16_t*>(la.w_router), unit);
+  const float* b = layer_ptr<kTBRouter>(la, la.b_router, unit);
+  const float* s = layer_ptr<kTScale>(la, la.rms_scale, unit);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int m = lane & 15, g = lane >> 4;
   const int d = la.d, E = la.E;

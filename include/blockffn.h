@@ -22,9 +22,10 @@
  *
  * General rules for every entry point:
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
- *     the `layer` descriptor itself, which is a host struct read during the
- *     call.  Buffers must stay valid until the queued work has completed;
- *     the library keeps no reference after the call returns.
+ *     the layer descriptors themselves (and blockffn_grads), which are host
+ *     structs read during the call.  Buffers must stay valid until the
+ *     queued work has completed; the library keeps no reference after the
+ *     call returns.
  *   - No entry point allocates memory.  Scratch space for blockffn_forward is
  *     a caller-provided workspace of at least blockffn_workspace_size() bytes.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream); no
@@ -63,7 +64,7 @@
 extern "C" {
 #endif
 
-#define BLOCKFFN_VERSION 1
+#define BLOCKFFN_VERSION 2
 
 /* Element type of x and of every weight matrix. */
 #define BLOCKFFN_F32 0  /* IEEE binary32 */
@@ -86,17 +87,28 @@ extern "C" {
 #define BLOCKFFN_ERR_CHUNK (-4)     /* chunk_len out of range or n_tokens % chunk_len != 0 */
 #define BLOCKFFN_ERR_WORKSPACE (-5) /* workspace smaller than blockffn_workspace_size() */
 #define BLOCKFFN_ERR_MODE (-6)      /* unknown mode, or a mode the layer's dtype/shape cannot use */
-#define BLOCKFFN_ERR_ALIGN (-7)     /* a pointer or the layer stride is misaligned */
-#define BLOCKFFN_ERR_LAYERS (-8)    /* n_layers < 1, or n_layers > 1 without a layer stride */
+#define BLOCKFFN_ERR_ALIGN (-7)     /* a pointer is misaligned */
+#define BLOCKFFN_ERR_LAYERS (-8)    /* n_layers < 1, layers of different shapes, or too many scattered layers */
 #define BLOCKFFN_ERR_HIP (-9)       /* a HIP launch failed (see blockffn_last_error) */
 
 /*
  * One BlockFFN layer (plain data; the library takes no ownership).
  *
- * With n_layers > 1 the entry points see a stack of layers of identical
- * shape: layer l's tensors live at (char*)ptr + l * layer_stride for every
- * pointer below (NULL pointers stay NULL), and chunk c uses layer
- * c % n_layers.  layer_stride is ignored when n_layers == 1.
+ * Layer arrays.  blockffn_route, blockffn_route_with and blockffn_forward
+ * take `layers`, a host array of n_layers >= 1 descriptors, and unit u
+ * (chunk u of chunk_len tokens) uses layers[u % n_layers]: a call can send
+ * consecutive chunks through different layers, as the verify step of
+ * speculative decoding sends one chunk of candidate tokens through each
+ * layer of the model in turn (BlockFFN write-up §4 acceleration kernel,
+ * §6 real speed-up).  The descriptors must agree in d, n_experts, d_expert,
+ * dtype and rms_eps (ERR_LAYERS otherwise); their tensors may live anywhere,
+ * each layer in its own allocations.  The array is read during the call
+ * only.  The library reduces it before launching: a repeating array counts
+ * once per period (n copies of one descriptor are one layer); layers whose
+ * every pointer lies a fixed number of bytes past the previous layer's (one
+ * strided allocation; NULL pointers NULL in every layer) are indexed by
+ * that spacing, in any number; otherwise at most 32 distinct layers are
+ * passed to the kernels by address, and more return ERR_LAYERS.
  */
 typedef struct blockffn_layer {
   int32_t d;          /* hidden size */
@@ -105,7 +117,6 @@ typedef struct blockffn_layer {
   int32_t dtype;      /* BLOCKFFN_F32 or BLOCKFFN_BF16, for x and every weight */
   float rms_eps;      /* RMSNorm epsilon, inside the square root (1e-6 typical) */
   int32_t reserved;   /* must be 0 */
-  int64_t layer_stride;     /* bytes between consecutive layers (multiple of 256) */
   const void* w_router;     /* [E][d], dtype */
   const float* b_router;    /* [E] fp32 router bias, or NULL for none */
   const float* rms_scale;   /* [E] fp32 RMSNorm scale, or NULL for ones */
@@ -126,6 +137,7 @@ typedef struct blockffn_stats {
 /*
  * Router: pre-activations, ReLU, RMSNorm over the E outputs, activation
  * pattern (write-up §2; abstract).
+ *   layers       n_layers descriptors; chunk c uses layers[c % n_layers]
  *   x            [n_tokens][d] in the layer's dtype
  *   gates        [n_tokens][E] fp32 out: g = s * ReLU(z) / sqrt(mean_E(ReLU(z)^2) + eps),
  *                exactly 0 for inactive experts
@@ -134,7 +146,7 @@ typedef struct blockffn_stats {
  *   chunk_len    maps tokens to chunks, and so to layers when n_layers > 1
  * z is accumulated in fp32.  Errors: NULL, SHAPE, DTYPE, CHUNK, ALIGN, LAYERS, HIP.
  */
-int blockffn_route(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+int blockffn_route(const blockffn_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
                    int32_t chunk_len, float* gates, uint64_t* token_masks, float* preact,
                    hipStream_t stream);
 
@@ -159,7 +171,7 @@ int blockffn_route(const blockffn_layer* layer, int32_t n_layers, const void* x,
  * only.  Other arguments, layout and ownership as blockffn_route.
  * Errors: as blockffn_route, plus MODE (unknown router) and SHAPE (top_k).
  */
-int blockffn_route_with(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+int blockffn_route_with(const blockffn_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
                         int32_t chunk_len, int32_t router, int32_t top_k, float* gates, uint64_t* token_masks,
                         float* preact, hipStream_t stream);
 
@@ -182,6 +194,7 @@ int blockffn_chunk_union(int32_t n_experts, const uint64_t* token_masks, int64_t
  * kernel: multiply only by the union's experts, batch the chunk's tokens,
  * mask the irrelevant activations with the gates; §7: outer loop over the
  * active experts).
+ *   layers     n_layers descriptors; chunk c uses layers[c % n_layers]
  *   gates, active_count, active_list   as written by the two calls above
  *                                      (active_* are ignored, and may be NULL,
  *                                      in DENSE and GROUPED modes)
@@ -189,7 +202,7 @@ int blockffn_chunk_union(int32_t n_experts, const uint64_t* token_masks, int64_t
  *              y_t = sum over i in the chunk's union of g[t][i] E_i(x_t)
  *   workspace  device scratch of at least blockffn_workspace_size() bytes,
  *              256-byte aligned; its contents need no initialisation
- * GROUPED mode (one batch through one layer, n_layers == 1): every
+ * GROUPED mode (one batch through one layer: every descriptor the same): every
  * (token, expert) pair with a non-zero gate (negative where the RMS scale
  * is negative) is grouped by expert, each expert's weights are read once
  * for all of its tokens in MFMA GEMMs, and each token's per-expert partial
@@ -198,7 +211,7 @@ int blockffn_chunk_union(int32_t n_experts, const uint64_t* token_masks, int64_t
  * and n_tokens x n_experts below 2^31 (SHAPE otherwise).
  * Errors: NULL, SHAPE, DTYPE, CHUNK, WORKSPACE, MODE, ALIGN, LAYERS, HIP.
  */
-int blockffn_forward(const blockffn_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+int blockffn_forward(const blockffn_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
                      int32_t chunk_len, const float* gates, const int32_t* active_count,
                      const int32_t* active_list, int32_t mode, void* workspace,
                      size_t workspace_bytes, float* y, hipStream_t stream);
@@ -309,8 +322,11 @@ size_t blockffn_cls_losses_workspace_size(int64_t n_tokens, int32_t chunk_len);
  * node_stride = 2 d * element size: a visited node is then one contiguous
  * read, which streams faster.
  *
- * With n_layers > 1, layer l's arrays live at (char*)ptr + l * layer_stride
- * for every pointer (NULL stays NULL) and token t uses layer t % n_layers.
+ * blockffn_fff_forward takes a host array of n_layers descriptors and
+ * token t uses layers[t % n_layers], with the rules of BlockFFN layer
+ * arrays: the descriptors agree in everything but their three pointers,
+ * and a repeating array counts once per period; evenly spaced layers are
+ * taken in any number, at most 32 scattered ones (ERR_LAYERS otherwise).
  */
 #define BLOCKFFN_FFF_GELU_NODES 0  /* GELU on every visited node's pre-activation */
 #define BLOCKFFN_FFF_GELU_OUTPUT 1 /* visited nodes linear, GELU on the summed output */
@@ -326,7 +342,6 @@ typedef struct blockffn_fff_layer {
   int32_t activation;   /* BLOCKFFN_FFF_GELU_NODES or BLOCKFFN_FFF_GELU_OUTPUT */
   int32_t node_stride;  /* bytes between consecutive nodes' rows: 0 (= d * element size) or a
                            multiple of 16 of at least d * element size */
-  int64_t layer_stride; /* bytes between consecutive layers (multiple of 256) */
   const void* w_node;   /* input rows, dtype, 16-byte aligned */
   const float* b_node;  /* [P][N] fp32, or NULL for no bias */
   const void* w_out;    /* output rows, dtype, 16-byte aligned */
@@ -354,7 +369,7 @@ typedef struct blockffn_fff_layer {
  * enqueues nothing.
  * Errors: NULL, SHAPE, DTYPE, MODE, WORKSPACE, ALIGN, LAYERS, HIP.
  */
-int blockffn_fff_forward(const blockffn_fff_layer* layer, int32_t n_layers, const void* x, int64_t n_tokens,
+int blockffn_fff_forward(const blockffn_fff_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
                          int32_t mode, int32_t split, int32_t* paths, float* node_preact, void* workspace,
                          size_t workspace_bytes, float* y, hipStream_t stream);
 

@@ -53,7 +53,7 @@ def bits(m_u64: np.ndarray, E: int) -> np.ndarray:
 def run_gpu(dev_layer: B.DeviceLayer, x_dev: torch.Tensor, L: int, mode="auto", n_layers=None,
             want_preact=True, stats=True):
     """route -> chunk_union -> forward (-> stats) on the current stream; numpy results."""
-    E = dev_layer.n_experts
+    E = (dev_layer[0] if isinstance(dev_layer, (list, tuple)) else dev_layer).n_experts
     g, m, z = B.blockffn_route(dev_layer, x_dev, L, n_layers=n_layers, want_preact=want_preact)
     um, cnt, lst = B.blockffn_chunk_union(E, m, L)
     y = B.blockffn_forward(dev_layer, x_dev, L, g, cnt, lst, mode=mode, n_layers=n_layers)

@@ -61,13 +61,13 @@ def test_struct_layout_matches_header():
 #include <stdio.h>
 #include "blockffn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu\n", sizeof(blockffn_layer), offsetof(blockffn_layer, layer_stride),
+  printf("%zu %zu %zu %zu %zu\n", sizeof(blockffn_layer), offsetof(blockffn_layer, reserved),
          offsetof(blockffn_layer, w_router), offsetof(blockffn_layer, w_out), sizeof(blockffn_stats));
   printf("%zu %zu\n", offsetof(blockffn_stats, active_pairs), offsetof(blockffn_stats, hist));
   printf("%zu %zu %zu\n", sizeof(blockffn_grads), offsetof(blockffn_grads, d_rms_scale),
          offsetof(blockffn_grads, d_w_out));
   printf("%zu %zu %zu %zu %zu\n", sizeof(blockffn_fff_layer), offsetof(blockffn_fff_layer, activation),
-         offsetof(blockffn_fff_layer, layer_stride), offsetof(blockffn_fff_layer, b_node),
+         offsetof(blockffn_fff_layer, w_node), offsetof(blockffn_fff_layer, b_node),
          offsetof(blockffn_fff_layer, w_out));
   return 0;
 }
@@ -81,18 +81,18 @@ int main(void) {
         lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     a = [int(v) for v in lines[0].split()]
     b = [int(v) for v in lines[1].split()]
-    assert a == [ctypes.sizeof(BlockffnLayer), BlockffnLayer.layer_stride.offset, BlockffnLayer.w_router.offset,
+    assert a == [ctypes.sizeof(BlockffnLayer), BlockffnLayer.reserved.offset, BlockffnLayer.w_router.offset,
                  BlockffnLayer.w_out.offset, ctypes.sizeof(BlockffnStats)]
     assert b == [BlockffnStats.active_pairs.offset, BlockffnStats.hist.offset]
     c = [int(v) for v in lines[2].split()]
     assert c == [ctypes.sizeof(BlockffnGrads), BlockffnGrads.d_rms_scale.offset, BlockffnGrads.d_w_out.offset]
     f = [int(v) for v in lines[3].split()]
     assert f == [ctypes.sizeof(BlockffnFffLayer), BlockffnFffLayer.activation.offset,
-                 BlockffnFffLayer.layer_stride.offset, BlockffnFffLayer.b_node.offset, BlockffnFffLayer.w_out.offset]
+                 BlockffnFffLayer.w_node.offset, BlockffnFffLayer.b_node.offset, BlockffnFffLayer.w_out.offset]
 
 
 def test_version_and_status_strings(lib):
-    assert lib.blockffn_version() == 1
+    assert lib.blockffn_version() == 2
     assert lib.blockffn_status_string(0) == b"ok"
     for code in range(-9, 0):
         s = lib.blockffn_status_string(code)
@@ -104,15 +104,19 @@ P = 0x10000  # placeholder, 64 KiB aligned; never dereferenced (every call fails
 
 
 def _layer(**kw):
-    f = dict(d=256, n_experts=16, d_expert=128, dtype=1, rms_eps=1e-6, reserved=0, layer_stride=0,
+    f = dict(d=256, n_experts=16, d_expert=128, dtype=1, rms_eps=1e-6, reserved=0,
              w_router=P, b_router=P, rms_scale=None, w_in=P, w_out=P)
     f.update(kw)
     return BlockffnLayer(**f)
 
 
+def _arr(layers):
+    return (BlockffnLayer * len(layers))(*layers)
+
+
 def _route(lib, layer, n_layers=1, x=P, T=16, L=8, gates=P, masks=P, preact=None):
-    return lib.blockffn_route(ctypes.byref(layer) if layer is not None else None, n_layers, x, T, L, gates, masks,
-                              preact, None)
+    ref = None if layer is None else ctypes.byref(layer) if isinstance(layer, BlockffnLayer) else layer
+    return lib.blockffn_route(ref, n_layers, x, T, L, gates, masks, preact, None)
 
 
 @cpu_only
@@ -140,8 +144,7 @@ def test_route_rejects_bad_layer(lib, kw, code):
 def test_route_rejects_bad_arguments(lib):
     assert _route(lib, None) == _capi.ERR_NULL
     assert _route(lib, _layer(), n_layers=0) == _capi.ERR_LAYERS
-    assert _route(lib, _layer(), n_layers=2) == _capi.ERR_LAYERS            # no stride
-    assert _route(lib, _layer(layer_stride=1000), n_layers=2) == _capi.ERR_ALIGN
+    assert _route(lib, _layer(), n_layers=-3) == _capi.ERR_LAYERS
     assert _route(lib, _layer(), L=0) == _capi.ERR_CHUNK
     assert _route(lib, _layer(), L=33) == _capi.ERR_CHUNK
     assert _route(lib, _layer(), T=12, L=8) == _capi.ERR_CHUNK             # ragged tail
@@ -152,6 +155,46 @@ def test_route_rejects_bad_arguments(lib):
     assert _route(lib, _layer(), masks=P + 4) == _capi.ERR_ALIGN
     assert b"multiple of chunk_len" in (lib.blockffn_route(ctypes.byref(_layer()), 1, P, 12, 8, P, P, None, None)
                                         and lib.blockffn_last_error())
+
+
+@cpu_only
+def test_layer_arrays_are_validated(lib):
+    """Every descriptor of a layer array is checked, and they must share one shape."""
+    M = 1 << 24
+    ok2 = _arr([_layer(), _layer(w_router=P + M, b_router=P + 2 * M, w_in=P + 3 * M, w_out=P + 4 * M)])
+    # a valid array passes validation and then fails on the NULL x (nothing is launched)
+    assert _route(lib, ok2, n_layers=2, x=None) == _capi.ERR_NULL
+    bad = [
+        (_arr([_layer(), _layer(d=512)]), _capi.ERR_LAYERS),            # shapes differ
+        (_arr([_layer(), _layer(n_experts=32)]), _capi.ERR_LAYERS),
+        (_arr([_layer(), _layer(d_expert=256)]), _capi.ERR_LAYERS),
+        (_arr([_layer(), _layer(dtype=0)]), _capi.ERR_LAYERS),
+        (_arr([_layer(), _layer(rms_eps=1e-5)]), _capi.ERR_LAYERS),
+        (_arr([_layer(), _layer(w_in=None)]), _capi.ERR_NULL),          # a later descriptor is checked too
+        (_arr([_layer(), _layer(w_out=P + 8)]), _capi.ERR_ALIGN),
+        (_arr([_layer(), _layer(reserved=3)]), _capi.ERR_SHAPE),
+        (_arr([_layer(), _layer(dtype=9)]), _capi.ERR_DTYPE),
+    ]
+    for arr, code in bad:
+        assert _route(lib, arr, n_layers=2) == code, lib.blockffn_last_error()
+        assert _forward(lib, arr, n_layers=2) == code
+    # more than 32 scattered layers cannot be listed; evenly spaced ones can be any number, and so can
+    # repeats of a few layers
+    def scattered(n):
+        return _arr([_layer(w_router=P + M * (l * l + 1), w_in=P + M * (l * l + 2), w_out=P + M * (l * l + 3))
+                     for l in range(n)])
+    assert _route(lib, scattered(32), n_layers=32, x=None) == _capi.ERR_NULL
+    assert _route(lib, scattered(33), n_layers=33, x=None) == _capi.ERR_LAYERS
+    assert b"evenly spaced" in lib.blockffn_last_error()
+    even = _arr([_layer(w_router=P + l * M, b_router=P + l * M + 4096, w_in=P + l * M + 8192,
+                        w_out=P + l * M + 16384) for l in range(600)])
+    assert _route(lib, even, n_layers=600, x=None) == _capi.ERR_NULL
+    # evenly spaced except that one layer's bias is NULL: 40 such layers must be listed, which is too many
+    uneven = list(even)[:40]
+    uneven[7] = _layer(w_router=P + 7 * M, b_router=None, w_in=P + 7 * M + 8192, w_out=P + 7 * M + 16384)
+    assert _route(lib, _arr(uneven), n_layers=40, x=None) == _capi.ERR_LAYERS
+    periodic = _arr(list(scattered(2)) * 40)                           # 80 entries, 2 distinct layers
+    assert _route(lib, periodic, n_layers=80, x=None) == _capi.ERR_NULL
 
 
 @cpu_only
@@ -171,7 +214,8 @@ def test_union_and_stats_reject_bad_arguments(lib):
 
 
 def _forward(lib, layer, mode=0, T=16, L=8, ws=P, ws_bytes=1 << 40, y=P, count=P, lst=P, n_layers=1):
-    return lib.blockffn_forward(ctypes.byref(layer), n_layers, P, T, L, P, count, lst, mode, ws, ws_bytes, y, None)
+    ref = ctypes.byref(layer) if isinstance(layer, BlockffnLayer) else layer
+    return lib.blockffn_forward(ref, n_layers, P, T, L, P, count, lst, mode, ws, ws_bytes, y, None)
 
 
 @cpu_only
@@ -188,7 +232,8 @@ def test_forward_rejects_bad_arguments(lib):
     assert _forward(lib, _layer(dtype=0), mode=_capi.MODE_GROUPED) == _capi.ERR_MODE     # GROUPED needs bf16
     assert _forward(lib, _layer(d_expert=64), mode=_capi.MODE_GROUPED) == _capi.ERR_MODE
     assert _forward(lib, _layer(d_expert=384), mode=_capi.MODE_GROUPED) == _capi.ERR_MODE   # d_expert 128 or 256
-    assert _forward(lib, _layer(layer_stride=1 << 20), mode=_capi.MODE_GROUPED, n_layers=2) == _capi.ERR_LAYERS
+    two = _arr([_layer(), _layer(w_router=P + (1 << 20), w_in=P + (1 << 20), w_out=P + (1 << 20))])
+    assert _forward(lib, two, mode=_capi.MODE_GROUPED, n_layers=2) == _capi.ERR_LAYERS  # one layer only
     assert _forward(lib, _layer(), mode=_capi.MODE_GROUPED, ws_bytes=4096) == _capi.ERR_WORKSPACE
 
 
@@ -304,7 +349,7 @@ def test_cls_losses_validation(lib):
 
 
 def _fff_layer(**kw):
-    v = dict(d=2048, n_trees=64, depth=6, dtype=_capi.BF16, activation=0, node_stride=0, layer_stride=0,
+    v = dict(d=2048, n_trees=64, depth=6, dtype=_capi.BF16, activation=0, node_stride=0,
              w_node=P, b_node=P, w_out=P)
     v.update(kw)
     return BlockffnFffLayer(**v)
@@ -314,7 +359,8 @@ def _fff_layer(**kw):
 def test_fff_forward_validation(lib):
     def call(layer=None, n_layers=1, x=P, T=4, mode=0, split=1, paths=None, pre=None, ws=None, nb=0, y=P):
         ly = _fff_layer() if layer is None else layer
-        return lib.blockffn_fff_forward(ctypes.byref(ly), n_layers, x, T, mode, split, paths, pre, ws, nb, y, None)
+        ref = ctypes.byref(ly) if isinstance(ly, BlockffnFffLayer) else ly
+        return lib.blockffn_fff_forward(ref, n_layers, x, T, mode, split, paths, pre, ws, nb, y, None)
 
     assert lib.blockffn_fff_forward(None, 1, P, 4, 0, 1, None, None, None, 0, P, None) == _capi.ERR_NULL
     assert call(_fff_layer(dtype=2)) == _capi.ERR_DTYPE
@@ -333,8 +379,16 @@ def test_fff_forward_validation(lib):
     assert call(mode=1, paths=P) == _capi.ERR_MODE
     assert call(mode=1, pre=P) == _capi.ERR_MODE
     assert call(n_layers=0) == _capi.ERR_LAYERS
-    assert call(n_layers=2) == _capi.ERR_LAYERS                       # no stride
-    assert call(_fff_layer(layer_stride=1000), n_layers=2) == _capi.ERR_ALIGN
+    arr = lambda *ls: (BlockffnFffLayer * len(ls))(*ls)  # noqa: E731
+    M = 1 << 26
+    assert call(arr(_fff_layer(), _fff_layer(w_node=P + M, b_node=P + M, w_out=P + M)), n_layers=2,
+                x=None) == _capi.ERR_NULL                             # a valid array
+    assert call(arr(_fff_layer(), _fff_layer(depth=5)), n_layers=2) == _capi.ERR_LAYERS
+    assert call(arr(_fff_layer(), _fff_layer(node_stride=8192)), n_layers=2) == _capi.ERR_LAYERS
+    assert call(arr(_fff_layer(), _fff_layer(activation=1)), n_layers=2) == _capi.ERR_LAYERS
+    assert call(arr(_fff_layer(), _fff_layer(w_out=P + 8)), n_layers=2) == _capi.ERR_ALIGN
+    many = arr(*[_fff_layer(w_node=P + M * (l * l + 1), w_out=P + M * (l * l + 2)) for l in range(33)])
+    assert call(many, n_layers=33) == _capi.ERR_LAYERS                 # 33 scattered layers
     assert call(T=-1) == _capi.ERR_SHAPE
     assert call(T=1 << 31) == _capi.ERR_SHAPE
     assert call(_fff_layer(w_node=None)) == _capi.ERR_NULL

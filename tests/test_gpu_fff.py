@@ -33,8 +33,11 @@ PRE_TOL = 1e-4
 Y_TOL = 1e-5
 
 
-def _dev_layer(layers, post=False, interleave=True):
-    """One device layer stack from a list of host layers (copy r = layers[r])."""
+def _dev_layer(layers, post=False, interleave=True, separate=False):
+    """One device layer stack from a list of host layers (copy r = layers[r]), or with `separate` a list of
+    device layers, each in its own allocation."""
+    if separate:
+        return [B.DeviceFffLayer.from_workload(lr, post=post, interleave=interleave) for lr in layers]
     dl = B.DeviceFffLayer.from_workload(layers[0], post=post, replicas=len(layers), interleave=interleave)
     for r, lr in enumerate(layers[1:], start=1):
         dl.fill(r, lr)
@@ -89,14 +92,15 @@ def _compare(paths_g, pre_g, y_g, paths_o, pre_o, y_o, where):
     return len(flipped)
 
 
-def _case(d, P, D, dtype, T, seed, post=False, dense=False, n_layers=1, bias=True, interleave=True, split=0):
+def _case(d, P, D, dtype, T, seed, post=False, dense=False, n_layers=1, bias=True, interleave=True, split=0,
+          separate=False):
     rng = np.random.default_rng(seed)
     layers = [make_fff_layer(d, P, D, dtype, rng, bias=bias) for _ in range(n_layers)]
     x = make_fff_tokens(d, T, dtype, rng)
     where = (f"d={d} P={P} D={D} {dtype} T={T} post={post} dense={dense} layers={n_layers} "
-             f"interleave={interleave} split={split}")
+             f"interleave={interleave} split={split} separate={separate}")
     say(f"[gpu] fff {where}")
-    dl = _dev_layer(layers, post, interleave)
+    dl = _dev_layer(layers, post, interleave, separate)
     xd = B.tokens_to_device(x, F32 if dtype == "f32" else BF16)
     y, paths, pre = B.blockffn_fff_forward(dl, xd, mode="dense" if dense else "sparse", want_paths=not dense,
                                            split=split)
@@ -140,6 +144,12 @@ def test_fff_dense_matches_oracle(d, P, D, dtype, T, post):
 ])
 def test_fff_blocks_per_token(d, P, D, dtype, T, post, split):
     _case(d, P, D, dtype, T, 970 + P + split, post=post, split=split)
+
+
+@pytest.mark.parametrize("dense", [False, True])
+def test_fff_separately_allocated_layers(dense):
+    # token t uses layers[t % 3], each layer in its own allocation: the kernel gets each layer's addresses
+    _case(1024, 6, 3, "bf16", 14, 966, dense=dense, n_layers=3, separate=True)
 
 
 def test_fff_without_bias():

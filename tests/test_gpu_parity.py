@@ -82,22 +82,36 @@ def test_every_mode_matches_oracle(name):
         check_y(gpu["y"], y_ref, keep, layer.dtype, f"{name}/{mode}")
 
 
-def test_stacked_distinct_layers():
-    # chunk c must use layer c % n_layers: three different layers in one call
+def _separate_layer(ly):
+    """A layer whose five tensors are each their own torch allocation, as a model's parameters are."""
+    dev = torch.device("cuda")
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return B.DeviceLayer.from_tensors(bf(ly.w_router), bf(ly.w_in), bf(ly.w_out),
+                                      b_router=torch.from_numpy(ly.b_router).to(dev), rms_eps=ly.rms_eps)
+
+
+@pytest.mark.parametrize("alloc", ["separate", "strided"])
+def test_distinct_layers_per_chunk(alloc):
+    # chunk c must use layers[c % n_layers]: three different layers in one call, either each in its own
+    # allocations (the kernels get their addresses) or as evenly spaced copies in one buffer
     d, E, de, L, C = 512, 64, 128, 8, 9
     rngs = [np.random.default_rng(200 + r) for r in range(3)]
     layers = [make_layer(d, E, de, "bf16", 0.9, rg) for rg in rngs]
     x = make_tokens(d, C, L, 0.8, "bf16", np.random.default_rng(210)).x
-    dl = B.DeviceLayer.from_workload(layers[0], replicas=3)
-    for r in (1, 2):
-        t = dl.tensors(r)
-        src = B.DeviceLayer.from_workload(layers[r]).tensors(0)
-        for key in ("w_router", "b_router", "w_in", "w_out"):
-            t[key].copy_(src[key])
+    if alloc == "separate":
+        dl = [_separate_layer(ly) for ly in layers]
+    else:
+        dl = B.DeviceLayer.from_workload(layers[0], replicas=3)
+        for r in (1, 2):
+            t = dl.tensors(r)
+            src = B.DeviceLayer.from_workload(layers[r]).tensors(0)
+            for key in ("w_router", "b_router", "w_in", "w_out"):
+                t[key].copy_(src[key])
     xd = B.tokens_to_device(x, BF16)
-    for mode in ("auto", "gemv"):
-        say(f"[gpu] stacked layers mode {mode}")
-        gpu = run_gpu(dl, xd, L, mode=mode, n_layers=3)
+    for mode in ("auto", "chunk_mfma", "gemv", "dense"):
+        say(f"[gpu] {alloc} layers mode {mode}")
+        gpu = run_gpu(dl, xd, L, mode=mode, n_layers=3 if alloc == "strided" else None)
         for r in range(3):
             chunks = np.arange(r, C, 3)
             tok = (chunks[:, None] * L + np.arange(L)[None, :]).ravel()
@@ -105,7 +119,26 @@ def test_stacked_distinct_layers():
             z, g, m = oracle.route(x[tok], ly.w_router, ly.b_router, None, ly.rms_eps)
             flipped, keep = check_route(gpu, z, g, m, E, "bf16", t_idx=tok, layer=ly)
             y_ref = oracle.forward_tokens(x[tok], ly.w_in, ly.w_out, g, m)
-            check_y(gpu["y"][tok], y_ref, keep, "bf16", f"stacked layer {r}/{mode}")
+            check_y(gpu["y"][tok], y_ref, keep, "bf16", f"{alloc} layer {r}/{mode}")
+
+
+def test_single_token_units_through_separate_layers():
+    # chunk_len 1 (decode): token t uses layers[t % 3]; the router and experts take the GEMV-sized path
+    d, E, de, T = 1024, 64, 128, 12
+    layers = [make_layer(d, E, de, "bf16", 0.887, np.random.default_rng(220 + r)) for r in range(3)]
+    x = make_tokens(d, T, 1, 0.0, "bf16", np.random.default_rng(230)).x
+    dl = [_separate_layer(ly) for ly in layers]
+    xd = B.tokens_to_device(x, BF16)
+    for mode in ("auto", "gemv"):
+        say(f"[gpu] decode through separate layers mode {mode}")
+        gpu = run_gpu(dl, xd, 1, mode=mode)
+        for r in range(3):
+            tok = np.arange(r, T, 3)
+            ly = layers[r]
+            z, g, m = oracle.route(x[tok], ly.w_router, ly.b_router, None, ly.rms_eps)
+            flipped, keep = check_route(gpu, z, g, m, E, "bf16", t_idx=tok, layer=ly)
+            y_ref = oracle.forward_tokens(x[tok], ly.w_in, ly.w_out, g, m)
+            check_y(gpu["y"][tok], y_ref, keep, "bf16", f"decode layer {r}/{mode}")
 
 
 def test_edge_cases_empty_none_and_all_active():

@@ -33,7 +33,7 @@ EXPORTS = ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blo
            "blockffn_backward", "blockffn_backward_workspace_size",
            "blockffn_cls_losses", "blockffn_cls_losses_workspace_size", "blockffn_fff_forward", "blockffn_fff_workspace_size", "blockffn_read_probe",
            "blockffn_set_stage_events", "blockffn_workspace_size", "blockffn_status_string",
-           "blockffn_last_error", "blockffn_version")
+           "blockffn_last_error", "blockffn_version", "blockffn_build_digest")
 
 
 class BlockffnLayer(ctypes.Structure):
@@ -85,6 +85,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with `python -m activation_sparse_moe_amd.build` "
                                "(the BlockFFN path has no fallback)")
+        # torch brings its own HIP runtime, which its libraries load under the name "libamdhip64.so"; the
+        # library links "libamdhip64.so.7", which that runtime also answers to once it is loaded.  Loaded
+        # first, the library would pull in the system runtime, torch would then load its own beside it, and
+        # the two runtimes in one process disagree (calls fail with "no ROCm-capable device").  Importing
+        # torch first leaves one runtime, shared by torch and the library.
+        import torch  # noqa: F401
         lib = ctypes.CDLL(path)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         lp = ctypes.POINTER(BlockffnLayer)
@@ -119,8 +125,27 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.blockffn_last_error.restype = ctypes.c_char_p
         lib.blockffn_version.argtypes = []
         lib.blockffn_version.restype = ctypes.c_int
+        lib.blockffn_build_digest.argtypes = []
+        lib.blockffn_build_digest.restype = ctypes.c_char_p
+        _check_digest(lib, path)
         _lib = lib
         return lib
+
+
+def _check_digest(lib, path: str) -> None:
+    """Refuse a library built from other sources than those beside it (a stale build)."""
+    from . import build as _build
+    if os.path.abspath(path) != os.path.abspath(LIB_PATH) or not os.path.isdir(_build.CSRC):
+        return  # not the in-tree build, or no sources to compare with
+    have = lib.blockffn_build_digest().decode()
+    want = _build.library_digest()
+    if have != want:
+        raise RuntimeError(f"{path} was built from sources with digest {have}, but the sources here have digest "
+                           f"{want}: rebuild it with `python -m activation_sparse_moe_amd.build`")
+
+
+def build_digest() -> str:
+    return load().blockffn_build_digest().decode()
 
 
 def check(status: int, where: str) -> None:

@@ -5,10 +5,16 @@
 Compiles every ``csrc/*.hip`` to an object under ``_build/`` and links them
 into ``activation_sparse_moe_amd/libblockffn.so``.  Every HIP source is built
 with packed-fp32 code generation disabled.
+
+The library carries a digest of the sources it was built from
+(``blockffn_build_digest()``); the binding refuses a library whose digest
+differs from that of the sources beside it, so a stale build cannot be
+tested or timed by mistake.
 """
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -37,9 +43,27 @@ COMPILE_FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def library_sources() -> list:
+    """Every file the library is built from: csrc/* and include/blockffn.h."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")) +
+                  [os.path.join(ROOT, "include", "blockffn.h")])
+
+
+def library_digest() -> str:
+    """sha256 prefix over the library's sources (relative name, then contents, in name order)."""
+    h = hashlib.sha256()
+    for path in library_sources():
+        h.update(os.path.relpath(path, ROOT).encode())
+        h.update(b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMPILE_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMPILE_FLAGS, f'-DBLOCKFFN_BUILD_DIGEST="{digest}"', "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -49,8 +73,9 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    digest = library_digest()
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda src: _compile(src, digest), srcs))
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,7 +83,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources, digest {digest}")
     return LIB
 
 

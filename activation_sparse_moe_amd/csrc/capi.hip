@@ -614,3 +614,8 @@ BFFN_EXPORT const char* blockffn_status_string(int status) {
 BFFN_EXPORT const char* blockffn_last_error(void) { return g_err; }
 
 BFFN_EXPORT int blockffn_version(void) { return BLOCKFFN_VERSION; }
+
+#ifndef BLOCKFFN_BUILD_DIGEST
+#define BLOCKFFN_BUILD_DIGEST "unknown"
+#endif
+BFFN_EXPORT const char* blockffn_build_digest(void) { return BLOCKFFN_BUILD_DIGEST; }

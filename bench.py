@@ -89,6 +89,12 @@ def source_digest(kernel: str = None) -> str:
     return h.hexdigest()[:16]
 
 
+def _build_digest() -> str:
+    """Digest of the sources the loaded library was built from (loading refuses a stale build)."""
+    from activation_sparse_moe_amd import _capi
+    return _capi.build_digest()
+
+
 def profiled_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None if there is none or the kernels changed since it was taken."""
@@ -818,6 +824,7 @@ def fff_main(args, cfg) -> int:
         "timing": {"steps": "eager launches" if args.eager else "HIP graph replay of the forward",
                    "eager_ms_per_step": round(eager_ms, 5), "kernel_ms": round(kernel_ms, 5)},
         "source_digest": source_digest(),
+        "build_digest": _build_digest(),
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -940,6 +947,7 @@ def main(argv=None) -> int:
         "sparsity": {"tls": round(st["tls"], 4), "cls": round(st["cls"], 4), "mean_union": round(U / (T // cfg.chunk_len), 2),
                      "reuse": round(st["reuse"], 4)},
         "source_digest": source_digest(),
+        "build_digest": _build_digest(),
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -418,6 +418,12 @@ const char* blockffn_last_error(void);
 /* BLOCKFFN_VERSION of the built library. */
 int blockffn_version(void);
 
+/* Digest of the sources the library was built from (16 hex digits: a
+ * sha256 prefix over every HIP source and header, by relative name and
+ * contents, in name order), or "unknown" for a build that did not set it.
+ * Lets a caller check that the library it loaded matches its sources. */
+const char* blockffn_build_digest(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -132,7 +132,9 @@ def test_backward_is_reproducible_and_zero_tokens_is_a_no_op():
 
 def test_backward_full_size_sampled():
     """The batched workload (4096 tokens, d 4096, 128 experts) in one call, as
-    the benchmark runs it; the oracle checks sampled tokens and experts."""
+    the benchmark runs it; the oracle checks 288 tokens' dx, 32 experts'
+    weight gradients (over every token that activates them) and the router
+    gradients over all tokens."""
     cfg = CONFIGS["batched_L8_d4096_E128"]
     layer, tok = make_workload(cfg)
     x = tok.x
@@ -140,8 +142,9 @@ def test_backward_full_size_sampled():
     dy = np.random.default_rng(cfg.seed + 100).standard_normal((T, d)).astype(np.float32)
     say(f"[gpu] backward full size {cfg.name} T={T}")
     gpu = _gpu_backward(layer, x, dy)
-    tok_idx = np.unique(np.r_[np.linspace(0, T - 1, 24).astype(int), 1, T - 2])
-    experts = [0, 37, 90, 127]
+    tok_idx = np.unique(np.r_[np.linspace(0, T - 1, 256).astype(int), np.arange(1, 17), np.arange(T - 16, T)])
+    experts = sorted(set(np.linspace(0, cfg.n_experts - 1, 32).astype(int).tolist()))
+    assert len(experts) == 32 and len(tok_idx) >= 256
     tsel = np.zeros(T, bool)
     tsel[tok_idx] = True
     esel = np.zeros(cfg.n_experts, bool)

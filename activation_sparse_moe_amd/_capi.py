@@ -25,11 +25,14 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_CHUNK, ERR_WORKSPACE = -1, -2, -3, -4, -5
 ERR_MODE, ERR_ALIGN, ERR_LAYERS, ERR_HIP = -6, -7, -8, -9
 
+NOALLOC_SCRATCH_BYTES = 32 << 20  # BLOCKFFN_NOALLOC_SCRATCH_BYTES
+
 FFF_GELU_NODES, FFF_GELU_OUTPUT = 0, 1
 FFF_SPARSE, FFF_DENSE = 0, 1
 
 # Every symbol include/blockffn.h declares.
-EXPORTS = ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward", "blockffn_sparsity_stats",
+EXPORTS = ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward",
+           "blockffn_forward_noalloc", "blockffn_sparsity_stats",
            "blockffn_backward", "blockffn_backward_workspace_size",
            "blockffn_cls_losses", "blockffn_cls_losses_workspace_size", "blockffn_fff_forward", "blockffn_fff_workspace_size", "blockffn_read_probe",
            "blockffn_set_stage_events", "blockffn_workspace_size", "blockffn_status_string",
@@ -98,6 +101,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.blockffn_route_with.argtypes = [lp, i32, vp, i64, i32, i32, i32, vp, vp, vp, vp]
         lib.blockffn_chunk_union.argtypes = [i32, vp, i64, i32, vp, vp, vp, vp]
         lib.blockffn_forward.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, i32, vp, sz, vp, vp]
+        lib.blockffn_forward_noalloc.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, i32, vp, vp]
         lib.blockffn_sparsity_stats.argtypes = [i32, vp, i64, i32, vp, vp]
         lib.blockffn_backward.argtypes = [lp, vp, i64, vp, vp, vp, vp, sz, vp, ctypes.POINTER(BlockffnGrads), vp]
         flt = ctypes.c_float
@@ -112,6 +116,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.blockffn_backward_workspace_size.argtypes = [lp, i64]
         lib.blockffn_backward_workspace_size.restype = sz
         for f in ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward",
+                  "blockffn_forward_noalloc",
                   "blockffn_sparsity_stats", "blockffn_backward", "blockffn_cls_losses", "blockffn_fff_forward",
                   "blockffn_read_probe"):
             getattr(lib, f).restype = ctypes.c_int

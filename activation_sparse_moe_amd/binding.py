@@ -302,6 +302,23 @@ def blockffn_forward(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, gates:
     return y
 
 
+def blockffn_forward_noalloc(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, gates: torch.Tensor,
+                             active_count: Optional[torch.Tensor], active_list: Optional[torch.Tensor], mode="auto",
+                             n_layers: Optional[int] = None, y: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """blockffn_forward with the library's static scratch array instead of a workspace -> y [T][d] fp32.
+    Allocates y here only when none is given."""
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    T = x.shape[0]
+    layer, descs, nl = _layers(layer, n_layers)
+    if y is None:
+        y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device)
+    check(load().blockffn_forward_noalloc(descs, nl, _ptr(x), T, chunk_len, _ptr(gates), _ptr(active_count),
+                                          _ptr(active_list), m, _ptr(y), _stream(stream)),
+          "blockffn_forward_noalloc")
+    return y
+
+
 def blockffn_backward_workspace_size(layer: DeviceLayer, n_tokens: int) -> int:
     desc = layer.descriptor()
     return int(load().blockffn_backward_workspace_size(ctypes.byref(desc), n_tokens))

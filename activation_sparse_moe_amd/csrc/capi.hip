@@ -401,6 +401,68 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layers, int32_t n_layers,
   return hip_status(e, "forward launch");
 }
 
+// ---- blockffn_forward_noalloc: the forward with a static scratch array ----
+
+namespace {
+
+// Scratch of blockffn_forward_noalloc: one array per GPU, in the library's
+// code object, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device array: kernels and copies get the
+// device address from hipGetSymbolAddress (static_scratch_ptr), never the
+// name.
+constexpr size_t kStaticScratchBytes = size_t(BLOCKFFN_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.  Returns a status code.
+int static_scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  if (int r = hip_status(hipGetDevice(&dev), "hipGetDevice")) return r;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BLOCKFFN_ERR_HIP, "device %d is beyond the %d devices the static scratch table covers", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (int r = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) return r;
+    if (p == nullptr || !aligned(p, 256)) return fail(BLOCKFFN_ERR_HIP, "static scratch has no usable address");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return BLOCKFFN_OK;
+}
+
+}  // namespace
+
+BFFN_EXPORT int blockffn_forward_noalloc(const blockffn_layer* layers, int32_t n_layers, const void* x,
+                                         int64_t n_tokens, int32_t chunk_len, const float* gates,
+                                         const int32_t* active_count, const int32_t* active_list, int32_t mode,
+                                         float* y, hipStream_t stream) {
+  // everything blockffn_forward checks that does not depend on the workspace, and the size it needs
+  bffn::LayerArgs la;
+  if (int r = layer_args(layers, n_layers, &la)) return r;
+  if (int r = check_chunking(n_tokens, chunk_len)) return r;
+  Path path;
+  bool dense;
+  if (int r = resolve_mode(layers, n_tokens, chunk_len, mode, &path, &dense)) return r;
+  const size_t need = workspace_bytes_for(layers, n_tokens, chunk_len, path);
+  if (need > kStaticScratchBytes)
+    return fail(BLOCKFFN_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch, beyond the %zu of the static array; split the call or use "
+                "blockffn_forward with a workspace", need, kStaticScratchBytes);
+  if (n_tokens == 0)  // validated as blockffn_forward would, and nothing to enqueue
+    return blockffn_forward(layers, n_layers, x, n_tokens, chunk_len, gates, active_count, active_list, mode,
+                            nullptr, 0, y, stream);
+  void* ws = nullptr;
+  if (int r = static_scratch_ptr(&ws)) return r;
+  return blockffn_forward(layers, n_layers, x, n_tokens, chunk_len, gates, active_count, active_list, mode, ws,
+                          kStaticScratchBytes, y, stream);
+}
+
 BFFN_EXPORT int blockffn_sparsity_stats(int32_t n_experts, const uint64_t* token_masks, int64_t n_tokens,
                                         int32_t chunk_len, blockffn_stats* stats_dev, hipStream_t stream) {
   if (int r = check_experts(n_experts)) return r;

@@ -217,6 +217,29 @@ int blockffn_forward(const blockffn_layer* layers, int32_t n_layers, const void*
                      size_t workspace_bytes, float* y, hipStream_t stream);
 
 /*
+ * blockffn_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  It takes no workspace: its scratch space is a static device
+ * array of BLOCKFFN_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held
+ * from the first call on that GPU until the process ends.  The call itself
+ * allocates nothing.  Arguments, modes, results and errors are those of
+ * blockffn_forward, plus:
+ *   - WORKSPACE when blockffn_workspace_size() for these arguments exceeds
+ *     BLOCKFFN_NOALLOC_SCRATCH_BYTES (split the call; at d_expert 128 and
+ *     64 experts the chunk path fits about 2000 tokens per call);
+ *   - HIP when the array's device address cannot be obtained.
+ * Every call on one GPU uses that GPU's one array, which keeps the previous
+ * call's contents (the kernels read nothing a call has not written itself).
+ * Calls that overlap in time on one GPU (on different streams, or from
+ * threads whose calls are not ordered on one stream) race on the array and
+ * give wrong results; calls on one stream are ordered and safe.
+ */
+#define BLOCKFFN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int blockffn_forward_noalloc(const blockffn_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
+                             int32_t chunk_len, const float* gates, const int32_t* active_count,
+                             const int32_t* active_list, int32_t mode, float* y, hipStream_t stream);
+
+/*
  * Sparsity statistics of a mask stream (abstract: TLS and 8-token CLS;
  * write-up §5: consecutive-token expert reuse, experts-per-token histogram).
  *   stats_dev  one blockffn_stats in device memory, fully overwritten

@@ -237,6 +237,19 @@ def test_forward_rejects_bad_arguments(lib):
     assert _forward(lib, _layer(), mode=_capi.MODE_GROUPED, ws_bytes=4096) == _capi.ERR_WORKSPACE
 
 
+@cpu_only
+def test_forward_noalloc_rejects_calls_beyond_its_array(lib):
+    f = lib.blockffn_forward_noalloc
+    lay = _layer(d=2048, n_experts=64, d_expert=128)
+    # 4096 chunk-8 tokens need 64 MiB of scratch: more than the static array holds
+    assert f(ctypes.byref(lay), 1, P, 4096, 8, P, P, P, 0, P, None) == _capi.ERR_WORKSPACE
+    assert b"static array" in lib.blockffn_last_error()
+    assert f(ctypes.byref(lay), 1, P, 20, 8, P, P, P, 0, P, None) == _capi.ERR_CHUNK   # validated like the forward
+    assert f(ctypes.byref(lay), 1, P, 16, 8, P, P, P, 9, P, None) == _capi.ERR_MODE
+    assert f(ctypes.byref(lay), 0, P, 16, 8, P, P, P, 0, P, None) == _capi.ERR_LAYERS
+    assert f(ctypes.byref(lay), 1, None, 0, 8, None, None, None, 0, None, None) == _capi.OK  # no tokens: nothing to do
+
+
 def test_workspace_size(lib):
     lay = _layer(d=2048, n_experts=64, d_expert=128)
     T = 4096

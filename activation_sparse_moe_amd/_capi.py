@@ -79,12 +79,15 @@ _lock = threading.Lock()
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libblockffn.so (built by `python -m activation_sparse_moe_amd.build`)."""
+def load(path: str = None) -> ctypes.CDLL:
+    """Load libblockffn.so (built by `python -m activation_sparse_moe_amd.build`), or the build that
+    BLOCKFFN_LIB names (the host-sanitizer build of the CPU tests)."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
+        if path is None:
+            path = os.environ.get("BLOCKFFN_LIB") or LIB_PATH
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with `python -m activation_sparse_moe_amd.build` "
                                "(the BlockFFN path has no fallback)")
@@ -140,8 +143,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 def _check_digest(lib, path: str) -> None:
     """Refuse a library built from other sources than those beside it (a stale build)."""
     from . import build as _build
-    if os.path.abspath(path) != os.path.abspath(LIB_PATH) or not os.path.isdir(_build.CSRC):
-        return  # not the in-tree build, or no sources to compare with
+    if os.path.dirname(os.path.abspath(path)) != PKG or not os.path.isdir(_build.CSRC):
+        return  # not an in-tree build, or no sources to compare with
     have = lib.blockffn_build_digest().decode()
     want = _build.library_digest()
     if have != want:

@@ -87,6 +87,44 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+HOSTSAN_LIB = os.path.join(PKG, "libblockffn_hostsan.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (the C ABI's validation and
+# launch set-up); the gfx950 code is built as usual.  Each -fsanitize= goes right after -Xarch_host.
+HOSTSAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libblockffn_hostsan.so: the library with ASan + UBSan in its host code, for CPU tests of the C ABI
+    (load it with the compiler's ASan runtime preloaded).  Same sources, same digest."""
+    san_dir = os.path.join(BUILD, "hostsan")
+    os.makedirs(san_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    digest = library_digest()
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(san_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *COMPILE_FLAGS, *HOSTSAN_FLAGS, f'-DBLOCKFFN_BUILD_DIGEST="{digest}"', "-I",
+               os.path.join(ROOT, "include"), "-I", CSRC, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    tmp = HOSTSAN_LIB + f".tmp{os.getpid()}"
+    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, HOSTSAN_LIB)
+    if verbose:
+        print(f"built {HOSTSAN_LIB}")
+    return HOSTSAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -51,7 +51,9 @@ struct Vec16<uint16_t> {
 
 // Rows are split over lane groups of `lpr` lanes (a power of two); a group
 // covers its row with `nv` 16-byte vectors per lane.  Four rows per group are
-// in flight per iteration.
+// in flight per iteration, against up to kTokGroup tokens of the unit.
+constexpr int kTokGroup = 4;
+
 template <typename T, bool DENSE>
 __global__ __launch_bounds__(kBlock) void up_valu_kernel(LayerArgs la, const T* __restrict__ x, int64_t n_units,
                                                          int L, const float* __restrict__ gates,
@@ -75,28 +77,37 @@ __global__ __launch_bounds__(kBlock) void up_valu_kernel(LayerArgs la, const T* 
   const int rpp = 64 / lpr, lg = lane / lpr, li = lane % lpr;
   const int64_t t0 = unit * L;
   const int r_end = (rb + 1) * rows_per_wave;
-  for (int n = 0; n < L; ++n) {
-    const T* xr = x + (t0 + n) * d;
-    const float gate = gates[(t0 + n) * E + i];
-    float* hrow = hbuf + ((unit * E + slot) * L + n) * (int64_t)de;
+  // tokens kTokGroup at a time: each weight vector is loaded once per group
+  // and meets every token of it (the per-(row, token) sums keep their order)
+  for (int n0 = 0; n0 < L; n0 += kTokGroup) {
     for (int r0 = rb * rows_per_wave; r0 < r_end; r0 += 4 * rpp) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      float acc[4][kTokGroup] = {};
       for (int mm = 0; mm < nv; ++mm) {
         const int k = (li + mm * lpr) * VEC;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = r0 + q * rpp + lg;
-          if (r < r_end) acc[q] += Vec16<T>::dot_same(wi + (int64_t)r * d + k, xr + k);
+          if (r >= r_end) continue;
+          const T* wrow = wi + (int64_t)r * d + k;
+#pragma unroll
+          for (int j = 0; j < kTokGroup; ++j)
+            if (n0 + j < L) acc[q][j] += Vec16<T>::dot_same(wrow, x + (t0 + n0 + j) * d + k);
         }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        for (int off = lpr >> 1; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off, kWave);
-      if (li == 0) {
+      for (int j = 0; j < kTokGroup; ++j) {
+        if (n0 + j >= L) break;
+        const float gate = gates[(t0 + n0 + j) * E + i];
+        float* hrow = hbuf + ((unit * E + slot) * L + n0 + j) * (int64_t)de;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = r0 + q * rpp + lg;
-          if (r < r_end) hrow[r] = gate * swish(acc[q]);
+        for (int q = 0; q < 4; ++q)
+          for (int off = lpr >> 1; off > 0; off >>= 1) acc[q][j] += __shfl_xor(acc[q][j], off, kWave);
+        if (li == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = r0 + q * rpp + lg;
+            if (r < r_end) hrow[r] = gate * swish(acc[q][j]);
+          }
         }
       }
     }
@@ -124,30 +135,38 @@ __global__ __launch_bounds__(kBlock) void down_valu_kernel(LayerArgs la, int64_t
   constexpr int VEC = Vec16<T>::kElems;
   const int rpp = 64 / lpr, lg = lane / lpr, li = lane % lpr;
   const int64_t t0 = unit * L;
-  for (int n = 0; n < L; ++n) {
+  for (int n0 = 0; n0 < L; n0 += kTokGroup) {
     for (int r0 = k0; r0 < k_end; r0 += 4 * rpp) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      float acc[4][kTokGroup] = {};
       for (int s = 0; s < n_active; ++s) {
         const int i = DENSE ? s : list[unit * E + s];
         const T* wo = wo_base + (int64_t)i * d * de;
-        const float* hrow = hbuf + ((unit * E + s) * L + n) * (int64_t)de;
+        const float* hbase = hbuf + ((unit * E + s) * L + n0) * (int64_t)de;
         for (int mm = 0; mm < nv; ++mm) {
-          const int j = (li + mm * lpr) * VEC;
+          const int j0 = (li + mm * lpr) * VEC;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int r = r0 + q * rpp + lg;
-            if (r < k_end) acc[q] += Vec16<T>::dot_f32(wo + (int64_t)r * de + j, hrow + j);
+            if (r >= k_end) continue;
+            const T* wrow = wo + (int64_t)r * de + j0;
+#pragma unroll
+            for (int j = 0; j < kTokGroup; ++j)
+              if (n0 + j < L) acc[q][j] += Vec16<T>::dot_f32(wrow, hbase + (int64_t)j * de + j0);
           }
         }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        for (int off = lpr >> 1; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off, kWave);
-      if (li == 0) {
+      for (int j = 0; j < kTokGroup; ++j) {
+        if (n0 + j >= L) break;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = r0 + q * rpp + lg;
-          if (r < k_end) y[(t0 + n) * d + r] = acc[q];
+        for (int q = 0; q < 4; ++q)
+          for (int off = lpr >> 1; off > 0; off >>= 1) acc[q][j] += __shfl_xor(acc[q][j], off, kWave);
+        if (li == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = r0 + q * rpp + lg;
+            if (r < k_end) y[(t0 + n0 + j) * d + r] = acc[q][j];
+          }
         }
       }
     }

@@ -39,24 +39,33 @@ class OracleStats(ctypes.Structure):
     ]
 
 
-def build(force: bool = True) -> str:
-    """Compile liboracle.so with gcc (plain -O2, no fast-math, no FMA contraction)."""
-    if not force and os.path.exists(_LIB) and all(os.path.getmtime(_LIB) >= os.path.getmtime(s) for s in SOURCES):
-        return _LIB
-    tmp = _LIB + f".tmp{os.getpid()}"
+SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer (host code only; any report aborts the process)
+SAN_FLAGS = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile liboracle.so with gcc (plain -O2, no fast-math, no FMA contraction); with `sanitize`,
+    liboracle_san.so, the same code under ASan + UBSan (load it with gcc's libasan preloaded)."""
+    lib = SAN_LIB if sanitize else _LIB
+    if not force and os.path.exists(lib) and all(os.path.getmtime(lib) >= os.path.getmtime(s) for s in SOURCES):
+        return lib
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-           "-shared", "-fPIC", "-o", tmp, *SOURCES, "-lm"]
+           *(SAN_FLAGS if sanitize else []), "-shared", "-fPIC", "-o", tmp, *SOURCES, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            # BLOCKFFN_ORACLE_LIB points the tests at a deliberately broken
-            # copy of the oracle (mutation tests); normally it is unset.
+            # BLOCKFFN_ORACLE_LIB points the tests at another build of the
+            # oracle: a deliberately broken copy (mutation tests) or the
+            # sanitizer build; normally it is unset.
             path = os.environ.get("BLOCKFFN_ORACLE_LIB")
             if not path:
                 build(force=False)

@@ -33,6 +33,7 @@ FFF_SPARSE, FFF_DENSE = 0, 1
 # Every symbol include/blockffn.h declares.
 EXPORTS = ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward",
            "blockffn_forward_noalloc", "blockffn_sparsity_stats",
+           "blockffn_layer_forward", "blockffn_layer_forward_workspace_size",
            "blockffn_backward", "blockffn_backward_workspace_size",
            "blockffn_cls_losses", "blockffn_cls_losses_workspace_size", "blockffn_fff_forward", "blockffn_fff_workspace_size", "blockffn_read_probe",
            "blockffn_set_stage_events", "blockffn_workspace_size", "blockffn_status_string",
@@ -106,6 +107,9 @@ def load(path: str = None) -> ctypes.CDLL:
         lib.blockffn_forward.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, i32, vp, sz, vp, vp]
         lib.blockffn_forward_noalloc.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, i32, vp, vp]
         lib.blockffn_sparsity_stats.argtypes = [i32, vp, i64, i32, vp, vp]
+        lib.blockffn_layer_forward.argtypes = [lp, i32, vp, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        lib.blockffn_layer_forward_workspace_size.argtypes = [lp, i64, i32]
+        lib.blockffn_layer_forward_workspace_size.restype = sz
         lib.blockffn_backward.argtypes = [lp, vp, i64, vp, vp, vp, vp, sz, vp, ctypes.POINTER(BlockffnGrads), vp]
         flt = ctypes.c_float
         lib.blockffn_cls_losses.argtypes = [i32, vp, i64, i32, flt, flt, flt, vp, sz, vp, vp, vp]
@@ -119,7 +123,7 @@ def load(path: str = None) -> ctypes.CDLL:
         lib.blockffn_backward_workspace_size.argtypes = [lp, i64]
         lib.blockffn_backward_workspace_size.restype = sz
         for f in ("blockffn_route", "blockffn_route_with", "blockffn_chunk_union", "blockffn_forward",
-                  "blockffn_forward_noalloc",
+                  "blockffn_forward_noalloc", "blockffn_layer_forward",
                   "blockffn_sparsity_stats", "blockffn_backward", "blockffn_cls_losses", "blockffn_fff_forward",
                   "blockffn_read_probe"):
             getattr(lib, f).restype = ctypes.c_int

@@ -319,6 +319,52 @@ def blockffn_forward_noalloc(layer: DeviceLayer, x: torch.Tensor, chunk_len: int
     return y
 
 
+def blockffn_layer_forward_workspace_size(layer: DeviceLayer, n_tokens: int, chunk_len: int) -> int:
+    if isinstance(layer, (list, tuple)):
+        layer = layer[0]
+    desc = layer.descriptor()
+    return int(load().blockffn_layer_forward_workspace_size(ctypes.byref(desc), n_tokens, chunk_len))
+
+
+def alloc_layer_forward(layer: DeviceLayer, n_tokens: int, chunk_len: int, want_preact: bool = False,
+                        want_stats: bool = True, device=None) -> dict:
+    """Output buffers and workspace of blockffn_layer_forward, for reuse across calls."""
+    if isinstance(layer, (list, tuple)):
+        layer = layer[0]
+    dev = layer.device if device is None else device
+    T, E, W = n_tokens, layer.n_experts, layer.mask_words
+    C = T // chunk_len if chunk_len > 0 else 0
+    nbytes = blockffn_layer_forward_workspace_size(layer, T, chunk_len)
+    return {
+        "gates": torch.empty((T, E), dtype=torch.float32, device=dev),
+        "token_masks": torch.empty((T, W), dtype=torch.int64, device=dev),
+        "preact": torch.empty((T, E), dtype=torch.float32, device=dev) if want_preact else None,
+        "chunk_masks": torch.empty((C, W), dtype=torch.int64, device=dev),
+        "active_count": torch.empty((C,), dtype=torch.int32, device=dev),
+        "active_list": torch.empty((C, E), dtype=torch.int32, device=dev),
+        "stats": torch.empty((_STATS_WORDS,), dtype=torch.int64, device=dev) if want_stats else None,
+        "workspace": torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev),
+        "y": torch.empty((T, layer.d), dtype=torch.float32, device=dev),
+    }
+
+
+def blockffn_layer_forward(layer: DeviceLayer, x: torch.Tensor, chunk_len: int, n_layers: Optional[int] = None,
+                           out: Optional[dict] = None, want_preact: bool = False, want_stats: bool = True,
+                           stream=None) -> dict:
+    """Router, chunk union, forward and statistics in one call -> the dict of alloc_layer_forward, filled."""
+    T = x.shape[0]
+    layer, descs, nl = _layers(layer, n_layers)
+    if out is None:
+        out = alloc_layer_forward(layer, T, chunk_len, want_preact, want_stats, x.device)
+    ws = out["workspace"]
+    check(load().blockffn_layer_forward(descs, nl, _ptr(x), T, chunk_len, _ptr(out["gates"]),
+                                        _ptr(out["token_masks"]), _ptr(out["preact"]), _ptr(out["chunk_masks"]),
+                                        _ptr(out["active_count"]), _ptr(out["active_list"]), _ptr(out["stats"]),
+                                        _ptr(ws), ws.numel(), _ptr(out["y"]), _stream(stream)),
+          "blockffn_layer_forward")
+    return out
+
+
 def blockffn_backward_workspace_size(layer: DeviceLayer, n_tokens: int) -> int:
     desc = layer.descriptor()
     return int(load().blockffn_backward_workspace_size(ctypes.byref(desc), n_tokens))

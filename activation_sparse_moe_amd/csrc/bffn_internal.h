@@ -75,6 +75,37 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// 64-bit activation-mask helpers.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Number of set bits of v in lane positions below this lane.
+__device__ __forceinline__ int rank_below(uint64_t v) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(v >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)v, 0u));
+}
+
+__device__ __forceinline__ uint64_t valid_bits(int E, int word) {
+  const int nb = E - 64 * word;
+  if (nb >= 64) return ~0ull;
+  if (nb <= 0) return 0ull;
+  return (1ull << nb) - 1ull;
+}
+
+// Lane l gets lane l - 1's value (lane 0 its own).
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v) {
+  const uint32_t lo = __shfl_up((uint32_t)v, 1, kWave), hi = __shfl_up((uint32_t)(v >> 32), 1, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += shfl_xor_u64(v, off);
+  return v;
+}
+
 // Blocks of one launch are handed to the 8 XCDs round-robin.  Renumber them
 // so that each XCD works through one contiguous range of logical blocks:
 // blocks of the same unit then share that XCD's L2 for their common operand.
@@ -134,6 +165,20 @@ size_t backward_workspace_bytes(int64_t n_tokens, int E, int d, int de);
 hipError_t launch_cls_losses(int E, const float* z, int64_t T, int L, float alpha, float w_al, float w_cs,
                              void* workspace, float* losses, float* dz, hipStream_t s);
 size_t cls_losses_workspace_bytes(int64_t n_tokens, int chunk_len);
+
+// One layer step (router, union, statistics, forward) of a short call in
+// three launches (layer_step.hip): bf16, E a multiple of 16, d and d_e
+// multiples of 128 with d <= 4096, at most kStepMaxUnits units and
+// kStepMaxTokens tokens.  Its workspace: the router's partial
+// pre-activations (fp32), then Swish(W_in x) (bf16).
+constexpr int64_t kStepMaxTokens = 64;
+constexpr int64_t kStepMaxUnits = 16;
+bool layer_step_fused(int d, int E, int de, int dtype, int64_t n_tokens, int chunk_len);
+size_t layer_step_zpart_bytes(int d, int E, int64_t n_tokens);
+size_t layer_step_hs_bytes(int E, int de, int64_t n_tokens);
+hipError_t launch_layer_step(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len, float* gates,
+                             uint64_t* masks, float* preact, uint64_t* chunk_masks, int32_t* count, int32_t* list,
+                             blockffn_stats* stats, float* zpart, uint16_t* hs, float* y, hipStream_t s);
 
 // Resident blocks of `kernel` on the current device (CUs x blocks per CU at
 // `block` threads, no dynamic LDS).  Queried once per (device, kernel) and

@@ -347,6 +347,13 @@ BFFN_EXPORT size_t blockffn_workspace_size(const blockffn_layer* layer, int64_t 
   return workspace_bytes_for(layer, n_tokens, chunk_len, path);
 }
 
+namespace {
+hipError_t launch_forward_path(const bffn::LayerArgs& la, const blockffn_layer* layer, Path path, bool dense,
+                               const void* x, int64_t n_tokens, int32_t chunk_len, const float* gates,
+                               const int32_t* active_count, const int32_t* active_list, void* workspace, float* y,
+                               hipStream_t stream);
+}  // namespace
+
 BFFN_EXPORT int blockffn_forward(const blockffn_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
                                  int32_t chunk_len, const float* gates, const int32_t* active_count,
                                  const int32_t* active_list, int32_t mode, void* workspace, size_t workspace_bytes,
@@ -375,6 +382,18 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layers, int32_t n_layers,
   if (!aligned(workspace, 256)) return fail(BLOCKFFN_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (workspace_bytes < need)
     return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  return hip_status(launch_forward_path(la, layer, path, dense, x, n_tokens, chunk_len, gates, active_count,
+                                        active_list, workspace, y, stream),
+                    "forward launch");
+}
+
+namespace {
+
+// Enqueues the forward on an already validated path and workspace.
+hipError_t launch_forward_path(const bffn::LayerArgs& la, const blockffn_layer* layer, Path path, bool dense,
+                               const void* x, int64_t n_tokens, int32_t chunk_len, const float* gates,
+                               const int32_t* active_count, const int32_t* active_list, void* workspace, float* y,
+                               hipStream_t stream) {
   hipError_t e;
   if (path == Path::kGrouped)
     e = bffn::launch_forward_grouped(la, static_cast<const uint16_t*>(x), n_tokens, gates, workspace, y,
@@ -398,8 +417,10 @@ BFFN_EXPORT int blockffn_forward(const blockffn_layer* layers, int32_t n_layers,
   else
     e = bffn::launch_forward_gemv(la, x, n_tokens, chunk_len, layer->dtype, gates, active_count, active_list, dense,
                                   static_cast<float*>(workspace), y, g_stage_events, stream);
-  return hip_status(e, "forward launch");
+  return e;
 }
+
+}  // namespace
 
 // ---- blockffn_forward_noalloc: the forward with a static scratch array ----
 
@@ -472,6 +493,83 @@ BFFN_EXPORT int blockffn_sparsity_stats(int32_t n_experts, const uint64_t* token
     return fail(BLOCKFFN_ERR_ALIGN, "token_masks and stats_dev must be 8-byte aligned");
   return hip_status(bffn::launch_stats(n_experts, token_masks, n_tokens, chunk_len, stats_dev, stream),
                     "stats launch");
+}
+
+// ---- blockffn_layer_forward: router, union, forward and statistics in one call ----
+
+namespace {
+
+// Workspace of the three-kernel step: the router's partial pre-activations [token][E][d/128] fp32, then
+// Swish(W_in x) [chunk][expert][token][d_e] bf16.
+size_t step_zpart_bytes(const blockffn_layer* ly, int64_t n_tokens) {
+  return round256(bffn::layer_step_zpart_bytes(ly->d, ly->n_experts, n_tokens));
+}
+
+size_t step_workspace(const blockffn_layer* ly, int64_t n_tokens) {
+  return step_zpart_bytes(ly, n_tokens) + round256(bffn::layer_step_hs_bytes(ly->n_experts, ly->d_expert, n_tokens));
+}
+
+bool step_fused(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len) {
+  return bffn::layer_step_fused(ly->d, ly->n_experts, ly->d_expert, ly->dtype, n_tokens, chunk_len);
+}
+
+}  // namespace
+
+BFFN_EXPORT size_t blockffn_layer_forward_workspace_size(const blockffn_layer* layer, int64_t n_tokens,
+                                                         int32_t chunk_len) {
+  if (check_layer(layer) != BLOCKFFN_OK || check_chunking(n_tokens, chunk_len) != BLOCKFFN_OK) return 0;
+  if (step_fused(layer, n_tokens, chunk_len)) return step_workspace(layer, n_tokens);
+  Path path;
+  bool dense;
+  if (resolve_mode(layer, n_tokens, chunk_len, BLOCKFFN_MODE_AUTO, &path, &dense) != BLOCKFFN_OK) return 0;
+  return workspace_bytes_for(layer, n_tokens, chunk_len, path);
+}
+
+BFFN_EXPORT int blockffn_layer_forward(const blockffn_layer* layers, int32_t n_layers, const void* x,
+                                       int64_t n_tokens, int32_t chunk_len, float* gates, uint64_t* token_masks,
+                                       float* preact, uint64_t* chunk_masks, int32_t* active_count,
+                                       int32_t* active_list, blockffn_stats* stats_dev, void* workspace,
+                                       size_t workspace_bytes, float* y, hipStream_t stream) {
+  bffn::LayerArgs la;
+  if (int r = layer_args(layers, n_layers, &la)) return r;
+  if (int r = check_chunking(n_tokens, chunk_len)) return r;
+  if (n_tokens == 0) return BLOCKFFN_OK;  // nothing is read or written; buffers may be NULL
+  if (!x || !gates || !token_masks || !chunk_masks || !active_count || !active_list || !y)
+    return fail(BLOCKFFN_ERR_NULL, "x, gates, token_masks, chunk_masks, active_count, active_list and y must be "
+                                   "non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(gates, 4) || !aligned(preact, 4) || !aligned(token_masks, 8) ||
+      !aligned(chunk_masks, 8) || !aligned(active_count, 4) || !aligned(active_list, 4) || !aligned(stats_dev, 8))
+    return fail(BLOCKFFN_ERR_ALIGN, "x and y must be 16-byte, masks and stats 8-byte, the rest 4-byte aligned");
+  const blockffn_layer* layer = layers;
+  const bool fused = step_fused(layer, n_tokens, chunk_len);
+  Path path = Path::kMfmaSplit;
+  bool dense = false;
+  if (!fused)
+    if (int r = resolve_mode(layer, n_tokens, chunk_len, BLOCKFFN_MODE_AUTO, &path, &dense)) return r;
+  const size_t need = fused ? step_workspace(layer, n_tokens) : workspace_bytes_for(layer, n_tokens, chunk_len, path);
+  if (need > 0 && !workspace) return fail(BLOCKFFN_ERR_NULL, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned(workspace, 256)) return fail(BLOCKFFN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(BLOCKFFN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  hipError_t e;
+  if (fused) {
+    char* ws = static_cast<char*>(workspace);
+    e = bffn::launch_layer_step(la, static_cast<const uint16_t*>(x), n_tokens, chunk_len, gates, token_masks, preact,
+                                chunk_masks, active_count, active_list, stats_dev, reinterpret_cast<float*>(ws),
+                                reinterpret_cast<uint16_t*>(ws + step_zpart_bytes(layer, n_tokens)), y, stream);
+  } else {
+    e = bffn::launch_route(la, x, n_tokens, chunk_len, layer->dtype, BLOCKFFN_ROUTER_BLOCKFFN, 0, gates, token_masks,
+                           preact, stream);
+    if (e == hipSuccess)
+      e = bffn::launch_chunk_union(la.E, token_masks, n_tokens, chunk_len, chunk_masks, active_count, active_list,
+                                   stream);
+    if (e == hipSuccess)
+      e = launch_forward_path(la, layer, path, dense, x, n_tokens, chunk_len, gates, active_count, active_list,
+                              workspace, y, stream);
+    if (e == hipSuccess && stats_dev)
+      e = bffn::launch_stats(la.E, token_masks, n_tokens, chunk_len, stats_dev, stream);
+  }
+  return hip_status(e, "layer forward launch");
 }
 
 namespace {

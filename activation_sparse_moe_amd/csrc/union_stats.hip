@@ -17,24 +17,6 @@
 namespace bffn {
 namespace {
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Number of set bits of v in lane positions below this lane.
-__device__ __forceinline__ int rank_below(uint64_t v) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(v >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)v, 0u));
-}
-
-__device__ __forceinline__ uint64_t valid_bits(int E, int word) {
-  const int nb = E - 64 * word;
-  if (nb >= 64) return ~0ull;
-  if (nb <= 0) return 0ull;
-  return (1ull << nb) - 1ull;
-}
-
 __global__ __launch_bounds__(kBlock) void chunk_union_kernel(int E, const uint64_t* __restrict__ masks,
                                                              int64_t n_chunks, int L,
                                                              uint64_t* __restrict__ chunk_masks,

@@ -512,10 +512,11 @@ def measure_ceilings(gemm: bool) -> dict:
 
 
 def latency_measure(runner, units: int, mode: str) -> dict:
-    """Latency mode: `units` units run one after another (route -> union ->
-    forward -> stats for one unit, each unit through its own layer copy), the
-    chain captured in one HIP graph and replayed; per-unit latency = replay
-    time / units."""
+    """Latency mode: `units` units run one after another, each unit through
+    its own layer copy, the chain captured in one HIP graph and replayed;
+    per-unit latency = replay time / units.  Two chains: one
+    blockffn_layer_forward call per unit (router, union, forward and
+    statistics in one call), and the four separate calls per unit."""
     import torch
     B, cfg = runner.B, runner.cfg
     L, E = cfg.chunk_len, cfg.n_experts
@@ -523,8 +524,10 @@ def latency_measure(runner, units: int, mode: str) -> dict:
     units = min(units, C)
     views = [runner.dl.single_copy(u % max(1, cfg.replicas)) for u in range(units)]
     ws = B.alloc_workspace(views[0], L, L, mode)
+    step_ws = torch.empty(max(B.blockffn_layer_forward_workspace_size(views[0], L, L), 256), dtype=torch.uint8,
+                          device="cuda")
 
-    def chain():
+    def separate():
         for u in range(units):
             t0, t1 = u * L, (u + 1) * L
             x, g, m = runner.xd[t0:t1], runner.gates[t0:t1], runner.masks[t0:t1]
@@ -534,27 +537,50 @@ def latency_measure(runner, units: int, mode: str) -> dict:
             B.blockffn_forward(views[u], x, L, g, cnt, lst, mode=mode, workspace=ws, y=runner.y[t0:t1])
             B.blockffn_sparsity_stats(E, m, L, stats_dev=runner.stats)
 
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        chain()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        chain()
-    graph.replay()
-    torch.cuda.synchronize()
-    reps = 5
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    outs = []
+    for u in range(units):
+        t0, t1 = u * L, (u + 1) * L
+        outs.append({"gates": runner.gates[t0:t1], "token_masks": runner.masks[t0:t1], "preact": None,
+                     "chunk_masks": runner.umask[u:u + 1], "active_count": runner.count[u:u + 1],
+                     "active_list": runner.lst[u:u + 1], "stats": runner.stats, "workspace": step_ws,
+                     "y": runner.y[t0:t1]})
+
+    def one_call():
+        for u in range(units):
+            B.blockffn_layer_forward(views[u], runner.xd[u * L:(u + 1) * L], L, out=outs[u])
+
+    def per_unit_us(chain):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            chain()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            chain()
         graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / reps / units * 1e3
-    return {"us_per_unit": round(us, 2), "units_chained": units, "tokens_per_unit": L,
-            "kind": "units one after another, each through its own layer copy, one HIP graph per chain"}
+        torch.cuda.synchronize()
+        reps = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del graph
+        return e0.elapsed_time(e1) / reps / units * 1e3
+
+    us_sep = per_unit_us(separate)
+    us_one = per_unit_us(one_call)
+    # the four-kernel step adds its counters and router partials to the split forward's workspace
+    fused = B.blockffn_layer_forward_workspace_size(views[0], L, L) != B.blockffn_workspace_size(views[0], L, L)
+    return {"us_per_unit": round(us_one, 2), "us_per_unit_separate_calls": round(us_sep, 2),
+            "units_chained": units, "tokens_per_unit": L,
+            "kernels_per_unit": 3 if fused else None,
+            "kind": "units one after another, each through its own layer copy, one HIP graph per chain; "
+                    "us_per_unit: one blockffn_layer_forward call per unit; separate: route, union, forward "
+                    f"({mode}), stats"}
 
 
 def copy_calibration():

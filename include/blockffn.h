@@ -248,6 +248,46 @@ int blockffn_forward_noalloc(const blockffn_layer* layers, int32_t n_layers, con
 int blockffn_sparsity_stats(int32_t n_experts, const uint64_t* token_masks, int64_t n_tokens,
                             int32_t chunk_len, blockffn_stats* stats_dev, hipStream_t stream);
 
+/*
+ * One layer step: blockffn_route, blockffn_chunk_union, blockffn_forward
+ * (AUTO) and blockffn_sparsity_stats in a single call (write-up §4 and §6:
+ * the chunk of draft tokens that speculative decoding verifies goes through
+ * each layer in turn, so a step of one or a few chunks is latency bound and
+ * every launch counts).
+ *   layers, x, chunk_len     as blockffn_route
+ *   gates, token_masks, preact (or NULL)            as blockffn_route
+ *   chunk_masks, active_count, active_list          as blockffn_chunk_union
+ *   stats_dev                as blockffn_sparsity_stats, or NULL
+ *   y                        as blockffn_forward
+ *   workspace                at least blockffn_layer_forward_workspace_size()
+ *                            bytes, 256-byte aligned, contents need no
+ *                            initialisation
+ * For calls of at most 64 tokens and 16 chunks with bf16, E a multiple of 16,
+ * d and d_expert multiples of 128 (d <= 4096) and chunk_len <= 32, the step
+ * runs as three kernels: the router's product over d-ranges of 128; the
+ * up-projection of every expert in a chunk's union (each block adds its
+ * expert's partials and skips the expert unless a token activates it), with
+ * one more block per chunk for the gates, patterns and union; and the
+ * down-projection, with one more block for the statistics.  Each block's
+ * waves split the contraction and add their parts in a fixed order, so
+ * results are reproducible bit for bit; they differ from the separate calls'
+ * in the last bits (another summation order), so a pattern bit whose z lies
+ * within rounding of 0 may differ.  The down-projection there scales each
+ * expert's product with Swish(W_in x) (bf16) by the token's gate in fp32
+ * instead of rounding g * Swish to bf16 first.  The workspace then holds the
+ * router's partial pre-activations (n_tokens x E x d/128 fp32) and
+ * Swish(W_in x) (n_tokens x E x d_expert bf16).  Other calls run the four
+ * separate calls.
+ * Errors: NULL, SHAPE, DTYPE, CHUNK, WORKSPACE, MODE, ALIGN, LAYERS, HIP.
+ */
+int blockffn_layer_forward(const blockffn_layer* layers, int32_t n_layers, const void* x, int64_t n_tokens,
+                           int32_t chunk_len, float* gates, uint64_t* token_masks, float* preact,
+                           uint64_t* chunk_masks, int32_t* active_count, int32_t* active_list,
+                           blockffn_stats* stats_dev, void* workspace, size_t workspace_bytes, float* y,
+                           hipStream_t stream);
+/* Workspace bytes of blockffn_layer_forward (0 for invalid arguments). */
+size_t blockffn_layer_forward_workspace_size(const blockffn_layer* layer, int64_t n_tokens, int32_t chunk_len);
+
 /* Gradient outputs of blockffn_backward: fp32, caller-owned device buffers,
  * fully overwritten. */
 typedef struct blockffn_grads {

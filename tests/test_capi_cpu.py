@@ -281,6 +281,55 @@ def test_workspace_size(lib):
     assert lib.blockffn_workspace_size(ctypes.byref(f32), C * L, L, _capi.MODE_CHUNK_SPLIT) == 0
 
 
+def _layer_forward(lib, layer, T=16, L=8, x=P, gates=P, masks=P, preact=None, um=P, count=P, lst=P, stats=P,
+                   ws=P, ws_bytes=1 << 40, y=P, n_layers=1):
+    ref = ctypes.byref(layer) if isinstance(layer, BlockffnLayer) else layer
+    return lib.blockffn_layer_forward(ref, n_layers, x, T, L, gates, masks, preact, um, count, lst, stats, ws,
+                                      ws_bytes, y, None)
+
+
+@cpu_only
+def test_layer_forward_rejects_bad_arguments(lib):
+    lay = _layer(d=2048, n_experts=64, d_expert=128)
+    assert _layer_forward(lib, None) == _capi.ERR_NULL
+    assert _layer_forward(lib, lay, n_layers=0) == _capi.ERR_LAYERS
+    assert _layer_forward(lib, lay, L=0) == _capi.ERR_CHUNK
+    assert _layer_forward(lib, lay, T=12) == _capi.ERR_CHUNK
+    for kw in ("x", "gates", "masks", "um", "count", "lst", "y"):
+        assert _layer_forward(lib, lay, **{kw: None}) == _capi.ERR_NULL, kw
+    assert _layer_forward(lib, lay, ws=None) == _capi.ERR_NULL
+    assert _layer_forward(lib, lay, ws=P + 64) == _capi.ERR_ALIGN
+    assert _layer_forward(lib, lay, ws_bytes=4096) == _capi.ERR_WORKSPACE
+    assert _layer_forward(lib, lay, T=4096, ws_bytes=4096) == _capi.ERR_WORKSPACE   # the separate-call regime
+    assert _layer_forward(lib, lay, stats=P + 4) == _capi.ERR_ALIGN
+    assert _layer_forward(lib, lay, preact=P + 2) == _capi.ERR_ALIGN
+    assert _layer_forward(lib, lay, x=P + 4) == _capi.ERR_ALIGN
+    assert _layer_forward(lib, _arr([lay, _layer(d=1024, n_experts=64, d_expert=128)]), n_layers=2) == \
+        _capi.ERR_LAYERS
+    # no tokens: nothing is read or written
+    assert _layer_forward(lib, lay, T=0, x=None, gates=None, masks=None, um=None, count=None, lst=None, stats=None,
+                          ws=None, y=None) == _capi.OK
+
+
+def test_layer_forward_workspace_size(lib):
+    lay = _layer(d=2048, n_experts=64, d_expert=128)
+    r256 = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    # the three-kernel step (at most 64 tokens and 16 chunks, d <= 4096): the router's partial
+    # pre-activations [T][E][d/128] fp32, then Swish(W_in x) [T][E][d_e] bf16
+    for C, L in ((1, 8), (2, 8), (16, 1), (2, 32)):
+        T = C * L
+        want = r256(16 * T * 64 * 4) + r256(T * 64 * 128 * 2)
+        assert lib.blockffn_layer_forward_workspace_size(ctypes.byref(lay), T, L) == want, (C, L)
+    # more tokens, or another shape: the separate calls' AUTO forward workspace
+    for T, L, ly in ((4096, 8, lay), (72, 8, lay), (16, 8, _layer(d=2048, n_experts=64, d_expert=128, dtype=0)),
+                     (16, 8, _layer(d=2048, n_experts=72, d_expert=128)),
+                     (16, 8, _layer(d=8192, n_experts=64, d_expert=128))):
+        assert lib.blockffn_layer_forward_workspace_size(ctypes.byref(ly), T, L) == \
+            lib.blockffn_workspace_size(ctypes.byref(ly), T, L, _capi.MODE_AUTO), (T, L)
+    assert lib.blockffn_layer_forward_workspace_size(ctypes.byref(lay), 12, 8) == 0        # ragged
+    assert lib.blockffn_layer_forward_workspace_size(ctypes.byref(_layer(d=100)), 16, 8) == 0
+
+
 def _grads(**kw):
     f = dict(d_w_router=P, d_b_router=P, d_rms_scale=P, d_w_in=P, d_w_out=P)
     f.update(kw)

@@ -153,6 +153,7 @@ __global__ __launch_bounds__(kPlanMaxThreads) void plan_items_kernel(const int32
 
 
 constexpr int kPoolShift = 3;  // the pool is the last 1/8 of the items
+constexpr int kUpShare = 4;    // blocks of one XCD that share an item range at two token tiles
 
 // One ticket of a global work counter (agent scope), broadcast to the wave.
 __device__ __forceinline__ int64_t take_global(unsigned* counter, int lane) {
@@ -204,15 +205,31 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
     __syncthreads();
     prefix = own_prefix;
   }
-  // the block's items (all of equal size): a contiguous equal share.  (Giving
-  // each XCD a range that its blocks take in turn keeps a chunk's token rows
-  // in L2, but then an XCD streams neighbouring weight row blocks at once, in
+  // the block's items (all of equal size): a contiguous equal share.  With
+  // two token tiles (a chunk's rows are 2 KiB x L, up to 256 KiB), kUpShare
+  // blocks of one XCD take the union of their shares in turn, so that they
+  // work on one chunk at a time and its token rows stay in that XCD's L2 (32
+  // resident blocks each on its own chunk need 8 MB there).  (Giving all of
+  // an XCD's blocks one range taken in turn keeps the rows in L2 too, but
+  // then the XCD streams 32 neighbouring weight row blocks at once, in
   // 128-byte pieces 2 d bytes apart, and HBM efficiency drops more than the
   // re-read token rows cost: measured 5.45 against 6.49 TB/s at d = 4096.)
   const int64_t total = prefix[n_units];
   const int64_t pool_lo = SPLIT ? total : total - (total >> kPoolShift);
-  const int64_t blk_lo = (int64_t)blockIdx.x * pool_lo / gridDim.x, stride = 1;
-  const int64_t item_end = ((int64_t)blockIdx.x + 1) * pool_lo / gridDim.x;
+  constexpr int kShare = (NT == 2 && !SPLIT) ? kUpShare : 1;
+  int64_t blk_lo, stride, item_end;
+  if constexpr (kShare > 1) {  // the grid is a multiple of kXcds * kShare
+    const int64_t per_xcd = gridDim.x / kXcds;
+    const int64_t lb = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;  // XCD-contiguous
+    const int64_t grp = lb / kShare, groups = gridDim.x / kShare;
+    blk_lo = grp * pool_lo / groups + lb % kShare;
+    stride = kShare;
+    item_end = (grp + 1) * pool_lo / groups;
+  } else {
+    blk_lo = (int64_t)blockIdx.x * pool_lo / gridDim.x;
+    stride = 1;
+    item_end = ((int64_t)blockIdx.x + 1) * pool_lo / gridDim.x;
+  }
   bool in_pool = false;
   auto take = [&]() -> int64_t {  // an item index, or total when none is left
     if (!in_pool) {
@@ -592,7 +609,8 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
     e = resident_blocks(reinterpret_cast<const void*>(&down_mfma_kernel<NT, DENSE, SPLIT>), kBlock, &grid_dn);
   if (e != hipSuccess) return e;
   // the item shares assume the grid is a multiple of the XCD count
-  grid_up = grid_up / kXcds * kXcds > 0 ? grid_up / kXcds * kXcds : kXcds;
+  const int64_t up_mult = (NT == 2 && !SPLIT) ? kXcds * kUpShare : kXcds;  // see the up kernel's item shares
+  grid_up = grid_up / up_mult * up_mult > 0 ? grid_up / up_mult * up_mult : up_mult;
   grid_dn = grid_dn / kXcds * kXcds > 0 ? grid_dn / kXcds * kXcds : kXcds;
   se.record(0, s);
   // the pool counters follow the prefix and the XCD bounds in the plan

@@ -179,6 +179,12 @@ size_t layer_step_hs_bytes(int E, int de, int64_t n_tokens);
 hipError_t launch_layer_step(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len, float* gates,
                              uint64_t* masks, float* preact, uint64_t* chunk_masks, int32_t* count, int32_t* list,
                              blockffn_stats* stats, float* zpart, uint16_t* hs, float* y, hipStream_t s);
+// The step's up and down kernels as the forward of at most kStepMaxUnits units with a given union
+// (workspace: layer_step_hs_bytes).
+bool forward_few_supported(int d, int de, int dtype, int64_t units, int chunk_len);
+hipError_t launch_forward_few(const LayerArgs& la, const uint16_t* x, int64_t n_tokens, int chunk_len,
+                              const float* gates, const int32_t* count, const int32_t* list, uint16_t* hs, float* y,
+                              const StageEvents& se, hipStream_t s);
 
 // Resident blocks of `kernel` on the current device (CUs x blocks per CU at
 // `block` threads, no dynamic LDS).  Queried once per (device, kernel) and

@@ -206,7 +206,7 @@ int layer_args(const blockffn_layer* layers, int32_t n_layers, bffn::LayerArgs* 
   return BLOCKFFN_OK;
 }
 
-enum class Path { kGemv, kMfma, kMfmaSplit, kGrouped };
+enum class Path { kGemv, kMfma, kMfmaSplit, kFew, kGrouped };
 
 // Resolves `mode` to a kernel family; returns a status code.
 int resolve_mode(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, int32_t mode, Path* path,
@@ -214,7 +214,11 @@ int resolve_mode(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, 
   // The matrix-core path streams each chunk's union once for all its tokens;
   // at chunk_len 1 its idle token columns cost nothing (the kernels are bound
   // by weight bytes), so it is the default wherever the shapes allow it.  A
-  // launch of a few units cuts each unit's work finer to fill the GPU.
+  // launch of a few units cuts each unit's work finer to fill the GPU: into
+  // blocks of 16 rows whose waves split the contraction and add their parts
+  // in LDS (kFew; without a step between blocks, so two kernels), or, for
+  // shapes those kernels do not take, into k- and slot-ranges added by two
+  // more kernels (kMfmaSplit).
   const bool mfma_ok = bffn::forward_mfma_supported(ly->d, ly->d_expert, ly->dtype);
   const bool auto_mfma = mfma_ok;
   int ks = 0, sp = 0;
@@ -222,7 +226,14 @@ int resolve_mode(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, 
   *dense = false;
   switch (mode) {
     case BLOCKFFN_MODE_AUTO:
-      *path = auto_mfma ? (few ? Path::kMfmaSplit : Path::kMfma) : Path::kGemv;
+      if (!auto_mfma)
+        *path = Path::kGemv;
+      else if (!few)
+        *path = Path::kMfma;
+      else
+        *path = bffn::forward_few_supported(ly->d, ly->d_expert, ly->dtype, n_tokens / chunk_len, chunk_len)
+                    ? Path::kFew
+                    : Path::kMfmaSplit;
       return BLOCKFFN_OK;
     case BLOCKFFN_MODE_CHUNK_SPLIT:
       if (!mfma_ok)
@@ -278,6 +289,7 @@ size_t split_bytes(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len
 
 size_t workspace_bytes_for(const blockffn_layer* ly, int64_t n_tokens, int32_t chunk_len, Path path) {
   if (path == Path::kGrouped) return bffn::grouped_workspace_bytes(n_tokens, ly->n_experts, ly->d, ly->d_expert);
+  if (path == Path::kFew) return round256(bffn::layer_step_hs_bytes(ly->n_experts, ly->d_expert, n_tokens));
   const size_t base = hbuf_bytes(ly, n_tokens, path) + plan_bytes(n_tokens, chunk_len);
   return path == Path::kMfmaSplit ? base + split_bytes(ly, n_tokens, chunk_len, nullptr) : base;
 }
@@ -398,6 +410,9 @@ hipError_t launch_forward_path(const bffn::LayerArgs& la, const blockffn_layer* 
   if (path == Path::kGrouped)
     e = bffn::launch_forward_grouped(la, static_cast<const uint16_t*>(x), n_tokens, gates, workspace, y,
                                      g_stage_events, stream);
+  else if (path == Path::kFew)
+    e = bffn::launch_forward_few(la, static_cast<const uint16_t*>(x), n_tokens, chunk_len, gates, active_count,
+                                 active_list, static_cast<uint16_t*>(workspace), y, g_stage_events, stream);
   else if (path == Path::kMfma || path == Path::kMfmaSplit) {
     char* ws = static_cast<char*>(workspace);
     const size_t hb = hbuf_bytes(layer, n_tokens, path), pb = plan_bytes(n_tokens, chunk_len);

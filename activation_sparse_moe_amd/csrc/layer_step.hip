@@ -31,6 +31,10 @@
 //      activate the expert) and added, y = the sum, fp32.  One more block
 //      computes the call's statistics.
 // Every sum has a fixed order, so the results are reproducible.
+//
+// The last two kernels, with the up blocks taking their experts from a given
+// union (count / list) instead, are also the forward of a few chunks whose
+// union is already known (blockffn_forward's AUTO mode).
 #include "bffn_internal.h"
 #include "router_epilogue.h"
 
@@ -212,7 +216,9 @@ __device__ __forceinline__ void route_finish(const LayerArgs& la, int64_t u, int
 
 // ---- 2. up-projection: block (chunk, expert, 16 hidden rows); one more block per chunk: router epilogue ----
 // hs[chunk][expert][token][d_e] = Swish(W_in[expert] x), bf16, for the experts in the chunk's union.
-template <int NT>
+// With ZTEST false (a forward whose union is given) block (chunk, slot, 16 hidden rows) takes the slot's
+// expert from count / list and there are no router blocks.
+template <int NT, bool ZTEST>
 __global__ __launch_bounds__(kStepThreads) void step_up_kernel(LayerArgs la, const uint16_t* __restrict__ x,
                                                                int64_t units, int L, int S,
                                                                const float* __restrict__ zpart,
@@ -230,23 +236,31 @@ __global__ __launch_bounds__(kStepThreads) void step_up_kernel(LayerArgs la, con
   const int m = lane & 15, g = lane >> 4;
   const int d = la.d, E = la.E, de = la.de, R = de >> 4;
   const int64_t b = blockIdx.x, nb = units * E * R;
-  if (b >= nb) {
+  if (ZTEST && b >= nb) {
     route_finish(la, b - nb, L, S, zpart, gates, masks, preact, chunk_masks, count, list, zl, ml, bs);
     return;
   }
   const int64_t u = b / (E * R);
-  const int rem = (int)(b % (E * R)), e = rem / R, r16 = rem % R;
-  // is expert e in the chunk's union?  z of token `lane` as the router epilogue forms it
-  bool on = false;
-  if (lane < L) {
-    const float* bias = layer_ptr<kTBRouter>(la, la.b_router, u);
-    const float be = bias ? bias[e] : 0.f;  // (loaded before the partials)
-    float z = 0.f;
-    z += zpart_sum(zpart + ((u * L + lane) * E + e) * S, S);
-    z += be;
-    on = z > 0.f;
+  const int rem = (int)(b % (E * R)), r16 = rem % R;
+  int e;
+  if constexpr (ZTEST) {
+    // is expert e in the chunk's union?  z of token `lane` as the router epilogue forms it
+    e = rem / R;
+    bool on = false;
+    if (lane < L) {
+      const float* bias = layer_ptr<kTBRouter>(la, la.b_router, u);
+      const float be = bias ? bias[e] : 0.f;  // (loaded before the partials)
+      float z = 0.f;
+      z += zpart_sum(zpart + ((u * L + lane) * E + e) * S, S);
+      z += be;
+      on = z > 0.f;
+    }
+    if (__ballot(on) == 0ull) return;  // (every wave computes the same: the whole block)
+  } else {
+    const int slot = rem / R;
+    if (slot >= count[u]) return;  // (the whole block)
+    e = list[u * E + slot];
   }
-  if (__ballot(on) == 0ull) return;  // (every wave computes the same: the whole block)
   const uint16_t* arow = layer_ptr<kTWIn>(la, static_cast<const uint16_t*>(la.w_in), u) +
                          ((int64_t)e * de + r16 * 16 + m) * d + 8 * g;
   const uint16_t* brow[NT];
@@ -391,6 +405,23 @@ __global__ __launch_bounds__(kStepThreads) void step_down_kernel(LayerArgs la, i
 }
 
 template <int NT>
+hipError_t launch_few_nt(const LayerArgs& la, const uint16_t* x, int64_t T, int L, const float* gates,
+                         const int32_t* count, const int32_t* list, uint16_t* hs, float* y, const StageEvents& se,
+                         hipStream_t s) {
+  const int64_t units = T / L;
+  se.record(0, s);
+  step_up_kernel<NT, false><<<dim3((unsigned)(units * la.E * (la.de >> 4))), dim3(kStepThreads), 0, s>>>(
+      la, x, units, L, 0, nullptr, hs, nullptr, nullptr, nullptr, nullptr, const_cast<int32_t*>(count),
+      const_cast<int32_t*>(list));
+  se.record(1, s);
+  const int64_t down_blocks = units * (la.d >> 4) + 1;
+  step_down_kernel<NT><<<dim3((unsigned)down_blocks), dim3(kStepThreads), 0, s>>>(la, units, L, gates, count, list,
+                                                                                  hs, y, nullptr, nullptr);
+  se.record(2, s);
+  return hipGetLastError();
+}
+
+template <int NT>
 hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t T, int L, float* gates, uint64_t* masks,
                      float* preact, uint64_t* chunk_masks, int32_t* count, int32_t* list, blockffn_stats* stats,
                      float* zpart, uint16_t* hs, float* y, hipStream_t s) {
@@ -398,8 +429,8 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t T, int L, f
   const int S = la.d / kRouteSplitK;
   route_split_kernel<NT><<<dim3((unsigned)(units * S)), dim3(kBlock), 0, s>>>(la, x, L, S, zpart);
   const int64_t up_blocks = units * la.E * (la.de >> 4) + units;
-  step_up_kernel<NT><<<dim3((unsigned)up_blocks), dim3(kStepThreads), 0, s>>>(la, x, units, L, S, zpart, hs, gates,
-                                                                              masks, preact, chunk_masks, count, list);
+  step_up_kernel<NT, true><<<dim3((unsigned)up_blocks), dim3(kStepThreads), 0, s>>>(
+      la, x, units, L, S, zpart, hs, gates, masks, preact, chunk_masks, count, list);
   const int64_t down_blocks = units * (la.d >> 4) + 1;
   step_down_kernel<NT><<<dim3((unsigned)down_blocks), dim3(kStepThreads), 0, s>>>(la, units, L, gates, count, list,
                                                                                   hs, y, masks, stats);
@@ -412,6 +443,18 @@ bool layer_step_fused(int d, int E, int de, int dtype, int64_t n_tokens, int chu
   const int64_t units = chunk_len > 0 ? n_tokens / chunk_len : 0;
   return forward_mfma_supported(d, de, dtype) && E % 16 == 0 && d <= kStepMaxD && units >= 1 &&
          units <= kStepMaxUnits && n_tokens <= kStepMaxTokens && chunk_len <= kStepMaxL;
+}
+
+bool forward_few_supported(int d, int de, int dtype, int64_t units, int chunk_len) {
+  return forward_mfma_supported(d, de, dtype) && d <= kStepMaxD && units >= 1 && units <= kStepMaxUnits &&
+         chunk_len <= kStepMaxL;
+}
+
+hipError_t launch_forward_few(const LayerArgs& la, const uint16_t* x, int64_t T, int L, const float* gates,
+                              const int32_t* count, const int32_t* list, uint16_t* hs, float* y,
+                              const StageEvents& se, hipStream_t s) {
+  if (L <= 16) return launch_few_nt<1>(la, x, T, L, gates, count, list, hs, y, se, s);
+  return launch_few_nt<2>(la, x, T, L, gates, count, list, hs, y, se, s);
 }
 
 size_t layer_step_zpart_bytes(int d, int E, int64_t n_tokens) {

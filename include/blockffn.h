@@ -71,7 +71,11 @@ extern "C" {
 #define BLOCKFFN_BF16 1 /* bfloat16: the upper 16 bits of a binary32 */
 
 /* blockffn_forward modes. */
-#define BLOCKFFN_MODE_AUTO 0       /* CHUNK_SPLIT for at most 16 units, else CHUNK_MFMA, where supported (bf16, d and d_expert % 128 == 0); else GEMV */
+/* AUTO: where the matrix-core shapes hold (bf16, d and d_expert % 128 == 0), CHUNK_MFMA, except for at most 16
+   units, which run as blocks of 16 rows whose waves split the contraction and add their parts in a fixed order
+   (d <= 4096; y scales each expert's product with Swish(W_in x), bf16, by the gate in fp32), or else
+   CHUNK_SPLIT; otherwise GEMV */
+#define BLOCKFFN_MODE_AUTO 0
 #define BLOCKFFN_MODE_GEMV 1       /* vector-ALU streaming of the active experts (any dtype) */
 #define BLOCKFFN_MODE_CHUNK_MFMA 2 /* matrix-core tiles over each chunk's union (bf16) */
 #define BLOCKFFN_MODE_GROUPED 3    /* token-expert pairs grouped by expert (bf16, d % 128 == 0, d_expert 128 or 256, one layer) */

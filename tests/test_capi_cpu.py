@@ -265,12 +265,18 @@ def test_workspace_size(lib):
         T * 64 * 128 * 4 + plan(T)
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 3, _capi.MODE_AUTO) == 0   # ragged
     assert lib.blockffn_workspace_size(ctypes.byref(lay), T, 8, 99) == 0
-    # a few units: AUTO splits each unit's work (8 k-ranges of 4 steps, 8 slot ranges) and adds the
-    # fp32 partial tiles of the up items [C][E][d_e/64][8][L][64] and the down items [C][d/64][8][L][64]
+    # a few units: AUTO runs blocks of 16 rows over a given union, whose workspace is Swish(W_in x)
+    # [C][E][L][d_e] bf16; CHUNK_SPLIT splits each unit's work (8 k-ranges of 4 steps, 8 slot ranges)
+    # and adds the fp32 partial tiles of the up items [C][E][d_e/64][8][L][64] and the down items
+    # [C][d/64][8][L][64]
     C, L = 2, 8
     split_ws = C * L * 64 * 128 * 2 + plan(C) + r256(C * 64 * 2 * 8 * L * 64 * 4) + r256(C * 32 * 8 * L * 64 * 4)
-    assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_AUTO) == split_ws
+    assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_AUTO) == r256(C * L * 64 * 128 * 2)
     assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_CHUNK_SPLIT) == split_ws
+    # d above 4096: AUTO splits
+    big = _layer(d=8192, n_experts=64, d_expert=128)
+    assert lib.blockffn_workspace_size(ctypes.byref(big), C * L, L, _capi.MODE_AUTO) == \
+        lib.blockffn_workspace_size(ctypes.byref(big), C * L, L, _capi.MODE_CHUNK_SPLIT)
     assert lib.blockffn_workspace_size(ctypes.byref(lay), C * L, L, _capi.MODE_CHUNK_MFMA) == \
         C * L * 64 * 128 * 2 + plan(C)
     # 17 units: AUTO no longer splits

@@ -7,13 +7,17 @@
 // One workgroup per unit (a chunk of L tokens, or one token when L == 1),
 // or per 16-token tile when all units share one layer, computes the tokens'
 // E pre-activations into LDS, then a fused epilogue applies ReLU + RMSNorm
-// and builds the 64-bit activation words with wave64 ballots.  Two
+// and builds the 64-bit activation words with wave64 ballots.  Three
 // producers of the pre-activations:
-//   * route_mfma_kernel (bf16, L >= 8 or one layer for all tokens): the
-//     router is a genuine E x d x tokens contraction; each wave streams a
-//     quarter of d for every expert row through v_mfma_f32_16x16x32_bf16
-//     (pipelined as in mfma_stream.h) and the four partial sums are added in
-//     a fixed order in the epilogue.
+//   * route_ring_kernel (bf16, every unit through one layer, any L): one
+//     block per 16-token tile; each wave streams its quarter of d through a
+//     private 3-slot DMA ring of whole 128-byte lines (lds_stream.h), and
+//     the four partial sums are added in a fixed order in the epilogue.
+//   * route_mfma_kernel (bf16, L >= 8, one unit per block through the unit's
+//     own layer copy): the router is a genuine E x d x tokens contraction;
+//     each wave streams a quarter of d for every expert row through
+//     v_mfma_f32_16x16x32_bf16 (pipelined as in mfma_stream.h), partial sums
+//     added in a fixed order.
 //   * route_valu_kernel (fp32, or L < 8 with a layer copy per unit): a
 //     bandwidth-bound GEMV; lane groups stride over d with 16-byte loads and
 //     reduce with cross-lane shuffles.

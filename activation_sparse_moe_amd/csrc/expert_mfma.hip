@@ -367,6 +367,235 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
   wait_vmcnt<0>();  // no LDS write may outlive the wave
 }
 
+// ---- up-projection at two token tiles, the block's four waves in lockstep ----
+// At chunk lengths 17-32 a wave's ring slot (8 KiB of weights + 4 KiB of
+// token rows) fills the LDS at three slots per wave, so each wave keeps two
+// steps in flight.  Here the block takes groups of four consecutive items of
+// one chunk, one per wave, which share the chunk's token rows: a slot holds
+// the four waves' weight rows, the 32 token rows once, and the four waves'
+// gates (37 KiB), and four slots keep three steps in flight per wave.  Each
+// step a wave DMAs its 64 weight rows, 8 of the 32 token rows and its gates
+// (10 instructions, so the wait is a constant), then meets the others at a
+// barrier: past it every wave's loads for the step have landed and every
+// wave has finished the step before, whose slot is refilled.  Items of a
+// chunk are counted up to a multiple of four; a wave whose group position is
+// past the chunk's items streams the group's first item (served from L2)
+// and stores nothing.
+constexpr int kLockBufs = 4;
+constexpr int kLockA = 4 * kABytes;                // the four waves' weight rows
+constexpr int kLockB = 32 * kRowBytes;             // the chunk's 32 token rows
+constexpr int kLockGate = kLockA + kLockB;         // then 64 fp32 gates per wave
+constexpr int kLockSlot = kLockGate + 4 * 256;
+constexpr int kLockLoads = 8 + 1 + 1;              // DMA instructions per wave and step
+constexpr int64_t kLockMaxUnits = 1024;            // group prefix kept in LDS
+constexpr int kLockShare = 4;                      // blocks of one XCD that share a group range
+
+__device__ __forceinline__ unsigned lds_addr(const uint8_t* p) { return (unsigned)(uintptr_t)(const lvoid_t*)p; }
+
+// Six 16-byte LDS reads and their wait in one assembly block.  Written as C,
+// the reads would be ordered after every LDS DMA in flight (the compiler
+// cannot tell the ring's slots apart, and waits for vmcnt 0), which would
+// drain the three steps this kernel keeps in flight; the slot read here was
+// completed by the step's wait and barrier.
+__device__ __forceinline__ void lds_read6(const unsigned (&ad)[6], u32x4 (&v)[6]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b128 %4, %10\n\t"
+      "ds_read_b128 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5])
+      : "memory");
+}
+
+// Two 4-byte LDS reads (the gates of a lane's two tokens) and their wait, for the same reason.
+__device__ __forceinline__ void lds_read2f(unsigned a0, unsigned a1, float (&v)[2]) {
+  asm volatile(
+      "ds_read_b32 %0, %2\n\t"
+      "ds_read_b32 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1])
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
+__global__ __launch_bounds__(kBlock) void up_lock_kernel(LayerArgs la, const uint16_t* __restrict__ x,
+                                                         int64_t n_units, int L, const float* __restrict__ gates,
+                                                         const int32_t* __restrict__ count,
+                                                         const int32_t* __restrict__ list,
+                                                         uint16_t* __restrict__ hbuf) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLockBufs * kLockSlot];
+  __shared__ int64_t gpre[kLockMaxUnits + 1];
+  __shared__ int64_t wave_tot[kBlock / kWave];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int d = la.d, de = la.de, E = la.E, rbs = de >> 6;
+  const int nsteps = d / kStepK;
+  // gpre[u] = groups of the chunks before u (a chunk's count x rbs items, rounded up to a multiple of 4)
+  {
+    const int64_t per = (n_units + kBlock - 1) / kBlock;
+    const int64_t b = tid * per, e = b + per < n_units ? b + per : n_units;
+    int64_t sum = 0;
+    for (int64_t u = b; u < e; ++u) sum += ((int64_t)count[u] * rbs + 3) >> 2;
+    int64_t inc = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int64_t v = shfl_up64(inc, off);
+      if (lane >= off) inc += v;
+    }
+    if (lane == kWave - 1) wave_tot[w] = inc;
+    __syncthreads();
+    int64_t run = inc - sum, total = 0;
+    for (int j = 0; j < kBlock / kWave; ++j) {
+      if (j < w) run += wave_tot[j];
+      total += wave_tot[j];
+    }
+    for (int64_t u = b; u < e; ++u) {
+      gpre[u] = run;
+      run += ((int64_t)count[u] * rbs + 3) >> 2;
+    }
+    if (tid == 0) gpre[n_units] = total;
+    __syncthreads();
+  }
+  const int64_t total = gpre[n_units];
+  // the block's groups: kLockShare blocks of one XCD take the union of their equal shares in turn
+  const int64_t per_xcd = gridDim.x / kXcds;  // the grid is a multiple of kXcds * kLockShare
+  const int64_t lb = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int64_t grp = lb / kLockShare, groups = gridDim.x / kLockShare;
+  const int64_t g_first = grp * total / groups + lb % kLockShare, g_end = (grp + 1) * total / groups;
+  if (g_first >= g_end) return;  // (the whole block)
+
+  struct LockItem {
+    int64_t unit;
+    int slot, rb, i;
+    bool store;
+  };
+  auto decode = [&](int64_t gi) {
+    int64_t lo = 0, hi = n_units - 1;  // last chunk whose group prefix <= gi
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (gpre[mid] <= gi) lo = mid; else hi = mid - 1;
+    }
+    LockItem it;
+    it.unit = lo;
+    const int first = (int)((gi - gpre[lo]) * 4);  // the group's first item in the chunk (always one of its items)
+    int r = first + w;
+    it.store = r < count[lo] * rbs;
+    if (!it.store) r = first;
+    it.slot = r / rbs;
+    it.rb = r % rbs;
+    it.i = list[lo * E + it.slot];
+    return it;
+  };
+  const uint16_t* a_src[8];
+  const uint16_t* b_src;
+  const float* g_src;
+  auto point = [&](const LockItem& it) {
+    const uint16_t* wi = layer_ptr<kTWIn>(la, static_cast<const uint16_t*>(la.w_in), it.unit);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int R = 8 * j + (lane >> 3);
+      a_src[j] = wi + ((int64_t)it.i * de + it.rb * 64 + R) * d + dma_chunk_elems(R, lane);
+    }
+    const int n = 8 * w + (lane >> 3);  // this wave's 8 of the 32 token rows
+    b_src = x + (it.unit * L + n % L) * d + dma_chunk_elems(n, lane);
+    g_src = gates + (it.unit * L + lane % L) * E + it.i;
+  };
+  auto issue = [&](int slot_i, int k) {
+    uint8_t* buf = lds + slot_i * kLockSlot;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16<kPolicyStream>(a_src[j] + k * kStepK, buf + w * kABytes + j * 1024);
+    dma16<kPolicyReuse>(b_src + k * kStepK, buf + kLockA + w * 1024);
+    dma4(g_src, buf + kLockGate + w * 256);
+  };
+
+  int64_t g_iss = g_first, g_cmp = g_first;
+  LockItem cmp = decode(g_cmp);
+  point(cmp);
+  int k_iss = 0, k_last = 0;
+  bool iss_done = false;
+  for (int b = 0; b < kLockBufs - 1; ++b) {  // nsteps >= kLockBufs - 1 (d >= 192)
+    issue(b, k_iss);
+    k_last = k_iss++;
+  }
+  f32x4 acc[4][2];
+  ring_zero<2>(acc);
+  int k_cmp = 0;
+  for (int t = 0;; ++t) {
+    wait_vmcnt<(kLockBufs - 2) * kLockLoads>();  // this wave's loads of step t have landed
+    block_barrier_no_fence();  // ... and every wave's; every wave is done with step t - 1
+    // issue three steps ahead into step t - 1's slot, or repeat a valid one past the end
+    if (!iss_done && k_iss == nsteps) {
+      g_iss += kLockShare;
+      if (g_iss < g_end) {
+        point(decode(g_iss));
+        k_iss = 0;
+      } else {
+        iss_done = true;
+      }
+    }
+    if (!iss_done) k_last = k_iss++;
+    issue((t + kLockBufs - 1) % kLockBufs, k_last);
+    // step t: this wave's 64 rows x the 32 shared token rows
+    const uint8_t* buf = lds + (t % kLockBufs) * kLockSlot;
+    const uint8_t* abuf = buf + w * kABytes;
+    const uint8_t* bbuf = buf + kLockA;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      unsigned ad[6];  // LDS addresses: rows 16 s + m of A (s < 4), rows 16 tl + m of B
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int R = 16 * s + m;
+        ad[s] = lds_addr(abuf + R * kRowBytes + (((4 * q + g) ^ ring_swz(R)) << 4));
+      }
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl) {
+        const int n = 16 * tl + m;
+        ad[4 + tl] = lds_addr(bbuf + n * kRowBytes + (((4 * q + g) ^ ring_swz(n)) << 4));
+      }
+      u32x4 v[6];
+      lds_read6(ad, v);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+          acc[s][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring_bf16x8(v[s]), ring_bf16x8(v[4 + tl]), acc[s][tl],
+                                                               0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (++k_cmp < nsteps) continue;
+    // item complete: g * Swish, bf16, to the hidden buffer (gates from this step's slot)
+    if (cmp.store) {
+      const uint8_t* gv_lds = buf + kLockGate + w * 256;
+      float gvs[2];
+      lds_read2f(lds_addr(gv_lds + 4 * m), lds_addr(gv_lds + 4 * (m + 16)), gvs);
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl) {
+        const int n = m + 16 * tl;
+        if (n >= L) continue;
+        const float gv = gvs[tl];
+        uint16_t* hrow = hbuf + ((cmp.unit * E + cmp.slot) * L + n) * (int64_t)de + cmp.rb * 64 + 4 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f32x4 v = acc[s][tl];
+          const uint32_t lo = pack2_bf16(gv * swish(v[0]), gv * swish(v[1]));
+          const uint32_t hi = pack2_bf16(gv * swish(v[2]), gv * swish(v[3]));
+          *reinterpret_cast<u32x2*>(hrow + s * 16) = u32x2{lo, hi};
+        }
+      }
+    }
+    g_cmp += kLockShare;
+    if (g_cmp >= g_end) break;
+    cmp = decode(g_cmp);
+    k_cmp = 0;
+    ring_zero<2>(acc);
+  }
+  wait_vmcnt<0>();  // no LDS write may outlive the wave
+}
+
 // ---- down-projection: Y[unit][kb .. kb + 64) = sum over slots of H'[unit][slot] W_out[i]^T ----
 // Items (chunk, 64 output rows) take count[chunk] * d_e / 64 steps; each XCD
 // gets the items whose first step falls in its equal share of all steps.
@@ -612,11 +841,23 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
   const int64_t up_mult = (NT == 2 && !SPLIT) ? kXcds * kUpShare : kXcds;  // see the up kernel's item shares
   grid_up = grid_up / up_mult * up_mult > 0 ? grid_up / up_mult * up_mult : up_mult;
   grid_dn = grid_dn / kXcds * kXcds > 0 ? grid_dn / kXcds * kXcds : kXcds;
+  // two token tiles: the lockstep up kernel (its group prefix lives in LDS; it needs three steps of d)
+  const bool lock = NT == 2 && !DENSE && !SPLIT && units <= kLockMaxUnits && la.d / kStepK >= kLockBufs - 1;
+  int64_t grid_lock = 0;
+  if (lock) {
+    e = resident_blocks(reinterpret_cast<const void*>(&up_lock_kernel), kBlock, &grid_lock);
+    if (e != hipSuccess) return e;
+    const int64_t mult = kXcds * kLockShare;  // see the kernel's group shares
+    grid_lock = grid_lock / mult * mult > 0 ? grid_lock / mult * mult : mult;
+  }
   se.record(0, s);
   // the pool counters follow the prefix and the XCD bounds in the plan
   unsigned* pool = reinterpret_cast<unsigned*>(plan + units + 1 + kXcds + 1);
-  up_mfma_kernel<NT, DENSE, SPLIT><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(
-      la, x, units, L, gates, count, list, own_prefix ? nullptr : plan, hbuf, ks, sp.up_part, pool);
+  if (lock)
+    up_lock_kernel<<<dim3((unsigned)grid_lock), dim3(kBlock), 0, s>>>(la, x, units, L, gates, count, list, hbuf);
+  else
+    up_mfma_kernel<NT, DENSE, SPLIT><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(
+        la, x, units, L, gates, count, list, own_prefix ? nullptr : plan, hbuf, ks, sp.up_part, pool);
   if (SPLIT)
     up_split_epilogue_kernel<<<dim3((unsigned)(units * la.E * rbs)), dim3(kBlock), 0, s>>>(
         sp.up_part, gates, count, list, L, la.E, la.de, ks, hbuf);

@@ -251,14 +251,6 @@ constexpr int kUpABytes = GBM * 128;                             // 64 pair rows
 constexpr int kUpBufBytes = kUpABytes + GBN * 128;               // + 128 weight rows: 24 KiB
 constexpr int kUpDmaPerWave = (GBM + GBN) / 8 / (kBlock / kWave);  // 1 KiB instructions per wave and step
 
-// Block barrier for data that DMA has already delivered to LDS: no fence,
-// so the DMA of later steps stays in flight (__syncthreads would drain it).
-__device__ __forceinline__ void block_barrier_no_fence() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
   static_assert(GBK == kStepK && kUpDmaPerWave * (kBlock / kWave) * 8 == GBM + GBN, "ring geometry");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kUpRing][kUpBufBytes];

@@ -62,6 +62,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Block barrier for data that DMA has already delivered to LDS: no fence,
+// so the DMA of later steps stays in flight (__syncthreads would drain it).
+__device__ __forceinline__ void block_barrier_no_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // One DMA instruction: this lane's 16 bytes from src to LDS dst + 16 lane.
 template <unsigned POLICY>
 __device__ __forceinline__ void dma16(const uint16_t* src, uint8_t* dst_instr_base) {

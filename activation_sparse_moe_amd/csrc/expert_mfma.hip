@@ -426,10 +426,11 @@ __global__ __launch_bounds__(kBlock) void up_lock_kernel(LayerArgs la, const uin
                                                          int64_t n_units, int L, const float* __restrict__ gates,
                                                          const int32_t* __restrict__ count,
                                                          const int32_t* __restrict__ list,
-                                                         uint16_t* __restrict__ hbuf) {
+                                                         uint16_t* __restrict__ hbuf, unsigned* pool_ctr) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLockBufs * kLockSlot];
   __shared__ int64_t gpre[kLockMaxUnits + 1];
   __shared__ int64_t wave_tot[kBlock / kWave];
+  __shared__ unsigned pool_take;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
   const int d = la.d, de = la.de, E = la.E, rbs = de >> 6;
@@ -461,12 +462,34 @@ __global__ __launch_bounds__(kBlock) void up_lock_kernel(LayerArgs la, const uin
     __syncthreads();
   }
   const int64_t total = gpre[n_units];
-  // the block's groups: kLockShare blocks of one XCD take the union of their equal shares in turn
+  // the block's groups: of the first 7/8, kLockShare blocks of one XCD take the union of their equal
+  // shares in turn; then the block takes groups of the last 1/8 through the pool counter, one take per
+  // block, broadcast through LDS (the take waits for wave 0's loads in flight, so it is kept to the tail)
+  const int64_t pool_lo = total - (total >> kPoolShift);
   const int64_t per_xcd = gridDim.x / kXcds;  // the grid is a multiple of kXcds * kLockShare
   const int64_t lb = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   const int64_t grp = lb / kLockShare, groups = gridDim.x / kLockShare;
-  const int64_t g_first = grp * total / groups + lb % kLockShare, g_end = (grp + 1) * total / groups;
-  if (g_first >= g_end) return;  // (the whole block)
+  const int64_t g_end = (grp + 1) * pool_lo / groups;
+  int64_t g_static = grp * pool_lo / groups + lb % kLockShare;
+  bool in_pool = false;
+  auto next_group = [&]() -> int64_t {  // block-uniform: the next group, or -1
+    if (!in_pool) {
+      const int64_t gs = g_static;
+      g_static += kLockShare;
+      if (gs < g_end) return gs;
+      in_pool = true;
+    }
+    if (threadIdx.x == 0) {
+      pool_take = __hip_atomic_fetch_add(pool_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS write lands before the barrier (no fence there)
+    }
+    block_barrier_no_fence();
+    const int64_t gp = pool_lo + (int64_t)__builtin_amdgcn_readfirstlane(pool_take);
+    block_barrier_no_fence();  // every wave has read pool_take before a later take writes it
+    return gp < total ? gp : -1;
+  };
+  const int64_t g_first = next_group();
+  if (g_first < 0) return;  // (the whole block)
 
   struct LockItem {
     int64_t unit;
@@ -512,9 +535,9 @@ __global__ __launch_bounds__(kBlock) void up_lock_kernel(LayerArgs la, const uin
     dma4(g_src, buf + kLockGate + w * 256);
   };
 
-  int64_t g_iss = g_first, g_cmp = g_first;
-  LockItem cmp = decode(g_cmp);
+  LockItem cmp = decode(g_first);
   point(cmp);
+  int64_t g_pend = -1;  // the group the issue side has moved on to, not yet multiplied
   int k_iss = 0, k_last = 0;
   bool iss_done = false;
   for (int b = 0; b < kLockBufs - 1; ++b) {  // nsteps >= kLockBufs - 1 (d >= 192)
@@ -529,9 +552,10 @@ __global__ __launch_bounds__(kBlock) void up_lock_kernel(LayerArgs la, const uin
     block_barrier_no_fence();  // ... and every wave's; every wave is done with step t - 1
     // issue three steps ahead into step t - 1's slot, or repeat a valid one past the end
     if (!iss_done && k_iss == nsteps) {
-      g_iss += kLockShare;
-      if (g_iss < g_end) {
-        point(decode(g_iss));
+      const int64_t gn = next_group();
+      if (gn >= 0) {
+        g_pend = gn;
+        point(decode(gn));
         k_iss = 0;
       } else {
         iss_done = true;
@@ -587,9 +611,9 @@ __global__ __launch_bounds__(kBlock) void up_lock_kernel(LayerArgs la, const uin
         }
       }
     }
-    g_cmp += kLockShare;
-    if (g_cmp >= g_end) break;
-    cmp = decode(g_cmp);
+    if (g_pend < 0) break;
+    cmp = decode(g_pend);
+    g_pend = -1;
     k_cmp = 0;
     ring_zero<2>(acc);
   }
@@ -854,7 +878,8 @@ hipError_t launch_nt(const LayerArgs& la, const uint16_t* x, int64_t units, int 
   // the pool counters follow the prefix and the XCD bounds in the plan
   unsigned* pool = reinterpret_cast<unsigned*>(plan + units + 1 + kXcds + 1);
   if (lock)
-    up_lock_kernel<<<dim3((unsigned)grid_lock), dim3(kBlock), 0, s>>>(la, x, units, L, gates, count, list, hbuf);
+    up_lock_kernel<<<dim3((unsigned)grid_lock), dim3(kBlock), 0, s>>>(la, x, units, L, gates, count, list, hbuf,
+                                                                      pool);
   else
     up_mfma_kernel<NT, DENSE, SPLIT><<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(
         la, x, units, L, gates, count, list, own_prefix ? nullptr : plan, hbuf, ks, sp.up_part, pool);

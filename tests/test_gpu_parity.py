@@ -162,7 +162,7 @@ def test_edge_cases_empty_none_and_all_active():
         t["b_router"].fill_(bias)
         layer.b_router = np.full(E, bias, np.float32)
         xd = B.tokens_to_device(x, BF16)
-        for mode in ("auto", "gemv"):
+        for mode in ("auto", "gemv", "chunk_mfma", "chunk_split"):
             gpu = run_gpu(dl, xd, L, mode=mode)
             if bias < 0:
                 assert (gpu["mask"] == 0).all() and (gpu["g"] == 0).all()
@@ -173,6 +173,28 @@ def test_edge_cases_empty_none_and_all_active():
                 assert (gpu["count"] == E).all()
                 np.testing.assert_array_equal(gpu["list"], np.tile(np.arange(E), (4, 1)))
             _compare_all(layer, x, L, gpu, f"{name}/{mode}")
+
+
+@pytest.mark.parametrize("L", [8, 32])
+def test_empty_unions_among_busy_chunks(L):
+    """Chunks whose tokens are all zero activate nothing (z = b < 0): their y must be exactly zero
+    while their neighbours' are right, on the batched chunk path (more than 16 chunks)."""
+    d, E, de, C = 1024, 64, 128, 40
+    rng = np.random.default_rng(310 + L)
+    layer = make_layer(d, E, de, "bf16", 0.9, rng)
+    x = make_tokens(d, C, L, 0.8, "bf16", rng).x.copy()
+    empty = [0, 3, 4, 17, 39]
+    for c in empty:
+        x[c * L:(c + 1) * L] = 0
+    say(f"[gpu] empty unions among {C} chunks, L={L}")
+    dl = B.DeviceLayer.from_workload(layer)
+    xd = B.tokens_to_device(x, BF16)
+    gpu = run_gpu(dl, xd, L)
+    assert all(gpu["count"][c] == 0 for c in empty)
+    assert (gpu["count"][[c for c in range(C) if c not in empty]] > 0).all()
+    for c in empty:
+        assert (gpu["y"][c * L:(c + 1) * L] == 0).all()
+    _compare_all(layer, x, L, gpu, f"empty unions L={L}")
 
 
 def test_many_chunks():

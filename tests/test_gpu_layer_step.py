@@ -2,7 +2,7 @@
 chunk union, expert forward and statistics).
 
 Short calls (at most 64 tokens and 16 chunks, bf16, E a multiple of 16)
-run the four-kernel step; the rest run the separate calls.  Every output is
+run the three-kernel step; the rest run the separate calls.  Every output is
 compared with the oracle element by element (bars in gpu_parity_util), and
 with the separate calls where those are bit-for-bit comparable.  The step
 must also be reproducible bit for bit, across calls and under graph replay.
@@ -27,6 +27,8 @@ CASES = {
     "d1024_E128_L32_x2": (1024, 128, 128, "bf16", 32, 2, 1.0, 0.65, 904),        # two token tiles, E = 128
     "d640_E48_L17_x3": (640, 48, 128, "bf16", 17, 3, 0.9, 0.7, 905),             # padded tile (d/128 = 5)
     "d256_E16_de128_L5_x3": (256, 16, 128, "bf16", 5, 3, 0.5, 0.6, 906),         # few experts
+    "d4096_E128_L32_x2": (4096, 128, 128, "bf16", 32, 2, 1.0364, 0.647, 910),     # the largest d, 64 tokens
+    "d4096_E128_de256_L8_x1": (4096, 128, 256, "bf16", 8, 1, 1.0364, 0.647, 911), # d_e 256
     # the separate-call regime: too many tokens; fp32; E not a multiple of 16
     "d512_E64_L8_x12_separate": (512, 64, 128, "bf16", 8, 12, 0.9, 0.8, 907),
     "f32_d128_E24_de32_L8_separate": (128, 24, 32, "f32", 8, 4, 0.8, 0.7, 908),

@@ -366,6 +366,62 @@ def torch_dense_reference_ms(runner, steps: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
+def torch_dense_chunks_reference(runner, steps: int) -> dict:
+    """Dense all-experts forward of every unit through its own layer copy as
+    vendor GEMMs (torch.bmm -> hipBLASLt): per sub-batch, one batched product
+    of each unit's tokens with its copy's concatenated W_in rows, SiLU times
+    the gates, and one batched product with the concatenated W_out rows.  The
+    transposed, concatenated weights of every copy are laid out once before
+    the timed steps (not timed).  Same inputs and gates as the sparse step;
+    the comparison for the chunk workloads.  Returns the forward time and the
+    largest difference from the DENSE mode's y of the same kernels on the
+    first sub-batch (run just before), relative to its RMS."""
+    import torch
+    cfg, dl = runner.cfg, runner.dl
+    E, d, de, L = cfg.n_experts, cfg.d, cfg.d_expert, cfg.chunk_len
+    U = runner.sub_units
+    copies = max(1, cfg.replicas)
+    w_in_t = torch.empty((U, d, E * de), dtype=torch.bfloat16, device="cuda")   # [copy][d][E d_e]
+    w_out_t = torch.empty((U, E * de, d), dtype=torch.bfloat16, device="cuda")  # [copy][E d_e][d]
+    for r in range(U):
+        t = dl.tensors(r % copies)
+        w_in_t[r].copy_(t["w_in"].reshape(E * de, d).t())
+        w_out_t[r].copy_(t["w_out"].permute(0, 2, 1).reshape(E * de, d))
+    C = cfg.n_tokens // L
+    subs = []
+    for b in range(runner.n_sub):
+        c0, c1 = b * U, min(C, (b + 1) * U)
+        n = c1 - c0
+        x = runner.xd[c0 * L:c1 * L].view(n, L, d)
+        g = runner.gates[c0 * L:c1 * L].view(n, L, E).repeat_interleave(de, dim=2)
+        subs.append((x, g, n))
+    y_ref = runner.y[:subs[0][2] * L].clone()  # the DENSE mode's y of the first sub-batch
+    outs = [None] * len(subs)
+
+    def fwd():
+        for k, (x, g, n) in enumerate(subs):
+            h = torch.bmm(x, w_in_t[:n])
+            h = (torch.nn.functional.silu(h.float()) * g).to(torch.bfloat16)
+            outs[k] = torch.bmm(h, w_out_t[:n])
+
+    for _ in range(2):
+        fwd()
+    torch.cuda.synchronize()
+    y0 = outs[0].reshape(-1, d).float()
+    rms = float(y_ref.pow(2).mean().sqrt())
+    diff = float((y0 - y_ref).abs().max()) / rms if rms > 0 else 0.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fwd()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del w_in_t, w_out_t, subs, outs
+    torch.cuda.empty_cache()
+    return {"forward_ms": ms, "max_rel_diff_vs_dense_mode": diff}
+
+
 def torch_dense_backward_ms(runner, dy, steps: int) -> float:
     """The dense all-experts layer's backward through torch autograd (hipBLASLt
     bf16 GEMMs over the concatenated experts, gates recomputed from z): the
@@ -901,6 +957,14 @@ def main(argv=None) -> int:
         if "forward" in davg and "forward" in avg:
             dense.update({"forward_ms": round(davg["forward"], 4),
                           "speedup_forward": round(davg["forward"] / avg["forward"], 3)})
+        if cfg.dtype == "bf16":
+            vend = torch_dense_chunks_reference(runner, args.dense_steps)
+            sparse_fwd = avg.get("forward", sum(avg[k] for k in ("up", "down") if k in avg))
+            dense["vendor"] = {
+                "kind": "torch.bmm (hipBLASLt) per sub-batch over each unit's layer copy, concatenated experts",
+                "forward_ms": round(vend["forward_ms"], 4),
+                "speedup_forward": round(vend["forward_ms"] / sparse_fwd, 3),
+                "max_rel_diff_vs_dense_mode": round(vend["max_rel_diff_vs_dense_mode"], 5)}
 
     dom = "up" if avg["up"] >= avg["down"] else "down"
     kernel_name = {"up": "expert_up", "down": "expert_down"}[dom]

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
   }
 }
 
-// ---- router backward per token: dz (fp32 and bf16), ds terms ----
+// ---- router backward per token: dz (fp32 and bf16, and per pair for the dx rows), ds terms ----
 // Wave w of a block handles token 4 blockIdx + w; lane l experts l and l + 64.
 __global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restrict__ z,
                                                             const float* __restrict__ rms_scale,
@@ -263,13 +263,14 @@ __global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restr
                                                             const float* __restrict__ dgp, int n_nt, int64_t T, int E,
                                                             const float* __restrict__ dz_extra,
                                                             float* __restrict__ dz, uint16_t* __restrict__ dzb,
-                                                            float* __restrict__ dsc) {
+                                                            float* __restrict__ dsc, float* __restrict__ pair_dz) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float r = r_tok[t];
   float dgv[2], av[2], sv[2];
   bool on[2];
+  int64_t pv[2] = {0, 0};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int i = lane + 64 * h;
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restr
     float dg = 0.f;
     if (on[h]) {
       const int64_t p = pair_idx[t * E + i];
+      pv[h] = p;
       for (int q = 0; q < n_nt; ++q) dg += dgp[p * n_nt + q];
     }
     dgv[h] = dg;
@@ -297,6 +299,7 @@ __global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restr
       dz[t * E + i] = dzi;
       dsc[t * E + i] = dgv[h] * av[h] * r;
     }
+    if (on[h]) pair_dz[pv[h]] = dzi;
     dzb[t * kRouterPad + i] = (uint16_t)f32_to_bf16(i < E ? dzi : 0.f);
   }
 }
@@ -491,56 +494,54 @@ __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
   }
 }
 
-// ---- dx[t] = sum over active i (ascending) of Part[pair_idx[t][i]] + dz[t][i] W_r[i] ----
+// ---- dx[t] = sum over active i (ascending) of Part[pair_idx[t][i]] (each row already holds its
+// dz[t][i] W_r[i]); with an extra router gradient, then the inactive experts' dz[t][i] W_r[i] ----
 __global__ __launch_bounds__(1024) void bwd_combine_kernel(const float* __restrict__ z, const float* __restrict__ dz,
                                                            const int32_t* __restrict__ pair_idx,
                                                            const uint16_t* __restrict__ part,
                                                            const uint16_t* __restrict__ w_router, int64_t T, int E,
                                                            int d, bool all_experts, float* __restrict__ dx) {
   __shared__ int32_t plist[128];
-  __shared__ float zlist[128];
-  __shared__ int32_t elist[128];
   __shared__ int nlist;
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   if (tid < 64) {
-    const bool on0 = tid < E && z[t * E + tid] > 0.f;
-    const bool on1 = tid + 64 < E && z[t * E + tid + 64] > 0.f;
+    // pre-activations and pair slots load together (a slot is used only where z > 0)
+    const float z0 = tid < E ? z[t * E + tid] : 0.f, z1 = tid + 64 < E ? z[t * E + tid + 64] : 0.f;
+    const int32_t q0 = tid < E ? pair_idx[t * E + tid] : 0, q1 = tid + 64 < E ? pair_idx[t * E + tid + 64] : 0;
+    const bool on0 = z0 > 0.f, on1 = z1 > 0.f;
     const uint64_t b0 = __ballot(on0), b1 = __ballot(on1);
     const int n0 = __popcll(b0);
     const int r0 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u));
     const int r1 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u));
-    if (on0) {
-      plist[r0] = pair_idx[t * E + tid];
-      zlist[r0] = dz[t * E + tid];
-      elist[r0] = tid;
-    }
-    if (on1) {
-      plist[n0 + r1] = pair_idx[t * E + tid + 64];
-      zlist[n0 + r1] = dz[t * E + tid + 64];
-      elist[n0 + r1] = tid + 64;
-    }
+    if (on0) plist[r0] = q0;
+    if (on1) plist[n0 + r1] = q1;
     if (tid == 0) nlist = n0 + __popcll(b1);
   }
   __syncthreads();
   const int n = nlist;
   for (int c0 = tid * 8; c0 < d; c0 += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n; ++s) {
-      const u32x4 pv = load_part(part + (int64_t)plist[s] * d + c0);
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(w_router + (int64_t)elist[s] * d + c0);
-      const float zs = zlist[s];
+    // kCombineInFlight partial rows in flight, added in ascending expert order
+    for (int s = 0; s < n; s += kCombineInFlight) {
+      u32x4 v[kCombineInFlight];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += bf16_lo(pv[q]) + zs * bf16_lo(wv[q]);
-        acc[2 * q + 1] += bf16_hi(pv[q]) + zs * bf16_hi(wv[q]);
-      }
+      for (int u = 0; u < kCombineInFlight; ++u)
+        v[u] = s + u < n ? load_part(part + (int64_t)plist[s + u] * d + c0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < kCombineInFlight; ++u)
+        if (s + u < n)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += bf16_lo(v[u][q]);
+            acc[2 * q + 1] += bf16_hi(v[u][q]);
+          }
     }
     if (all_experts) {
       // an extra router gradient reaches inactive experts too: their dz W_r rows, ascending
       for (int i = 0; i < E; ++i) {
         const float zs = dz[t * E + i];
-        if (z[t * E + i] > 0.f || zs == 0.f) continue;  // active ones were added above
+        if (z[t * E + i] > 0.f || zs == 0.f) continue;  // active ones are in their pair rows
         const u32x4 wv = *reinterpret_cast<const u32x4*>(w_router + (int64_t)i * d + c0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -559,7 +560,7 @@ struct BwdLayout {
   int32_t* blk;
   int64_t *pair_off, *tile_up, *all_off;
   int32_t *pair_tok, *pair_idx;
-  float *pair_gate, *g_b, *r_b, *dgp, *dz, *dsc, *wr_part;
+  float *pair_gate, *g_b, *r_b, *dgp, *dz, *dsc, *wr_part, *pair_dz;
   uint16_t *dyb, *du, *hg, *dzb, *part;
   size_t bytes;
 };
@@ -591,6 +592,7 @@ BwdLayout bwd_layout(char* base, int64_t T, int E, int d, int de) {
   L.dgp = reinterpret_cast<float*>(take(4 * P * (de / GBN)));
   L.dz = reinterpret_cast<float*>(take(4 * P));
   L.dsc = reinterpret_cast<float*>(take(4 * P));
+  L.pair_dz = reinterpret_cast<float*>(take(4 * P));
   L.dzb = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * kRouterPad));
   L.part = reinterpret_cast<uint16_t*>(take(2 * P * d));
   L.bytes = off;
@@ -636,7 +638,7 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   bwd_pair_kernel<<<dim3((unsigned)grid_pair), dim3(kBlock), 0, s>>>(pa);
   se.record(2, s);
   bwd_router_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(kBlock), 0, s>>>(
-      preact, la.rms_scale, L.r_b, L.pair_idx, L.dgp, de / GBN, T, E, dz_extra, L.dz, L.dzb, L.dsc);
+      preact, la.rms_scale, L.r_b, L.pair_idx, L.dgp, de / GBN, T, E, dz_extra, L.dz, L.dzb, L.dsc, L.pair_dz);
   bwd_reduce_kernel<<<dim3((unsigned)E), dim3(kBlock), 0, s>>>(L.dz, L.dsc, T, E, d_b_router, d_rms_scale);
   // dW_out[i][k][j] = sum_p dY[t_p][k] HG[p][j]
   TGemmArgs go{L.dyb, d, L.pair_tok, L.hg, de, nullptr, L.pair_off, d_w_out, de, (int64_t)d * de, E, d, d, de};
@@ -651,8 +653,9 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   bwd_router_sum_kernel<<<dim3((unsigned)(((int64_t)E * d + kBlock - 1) / kBlock)), dim3(kBlock), 0, s>>>(
       L.wr_part, (int64_t)E * d, d_w_router);
   se.record(3, s);
-  // dx: per-pair dU W_in[i] rows (the forward's down GEMM, reading W_in k-major), then the per-token sum
-  DownArgs dn{L.du, w_in, L.pair_off, L.part, d, E};
+  // dx: per-pair rows dU W_in[i] + dz W_r[i] (the forward's down GEMM, reading W_in k-major), then the
+  // per-token sum
+  DownArgs dn{L.du, w_in, L.pair_off, L.part, d, E, L.pair_dz, w_r};
   if (de == 128)
     grouped_down_kernel<128, true><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
   else

@@ -437,6 +437,10 @@ struct DownArgs {
   const int64_t* pair_off;    // [E + 1]
   uint16_t* part;             // [P][N]
   int N, E;
+  // KMAJOR only (required there): each pair's row also gets pair_dz[p] * w_add[i] added before it is
+  // rounded (the router's share of dx: dz times the expert's router row)
+  const float* pair_dz;       // [P]
+  const uint16_t* w_add;      // [E][N]
 };
 
 // Output columns of one wave in the down GEMM: its slab of W (SN rows x K)
@@ -483,7 +487,11 @@ __device__ __forceinline__ int stage_off(int r, int c) {
 // turns them into the A-operand layout 32 k rows at a time: written to the
 // hidden-tile buffers as k-major 256-byte rows, read back by transpose loads.
 // The staging registers live only while an item starts, so that variant is
-// capped for three waves per SIMD, which it meets without spilling.
+// capped for three waves per SIMD, which it meets without spilling.  It also
+// adds dz_p W_add[i] to each pair's row in fp32 before the row is rounded (the
+// products start from it): the tile's 32 dz values travel with its hidden
+// rows (loaded with them, staged in LDS beside them), and the item's slice of
+// W_add[i] sits in LDS.
 template <int K, bool KMAJOR = false>
 __global__ __launch_bounds__(kBlock, KMAJOR ? 3 : 1) void grouped_down_kernel(DownArgs da) {
   constexpr int SN = down_slab<K>();
@@ -497,6 +505,9 @@ __global__ __launch_bounds__(kBlock, KMAJOR ? 3 : 1) void grouped_down_kernel(Do
   constexpr int HL = kDownPairs * HC / kBlock;      // hidden-tile loads per thread
   __shared__ __attribute__((aligned(16))) uint8_t htile[2][kDownPairs * HB];
   __shared__ __attribute__((aligned(16))) uint8_t stage[kDownWaves][kDownPairs * RB];
+  constexpr int kAddCols = KMAJOR ? SN * kDownWaves : 1;  // the item's columns of W_add[i]
+  __shared__ __attribute__((aligned(16))) uint16_t wadd[kAddCols];
+  __shared__ float hdz[2][KMAJOR ? kDownPairs : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
   const int N = da.N, E = da.E;
@@ -567,13 +578,19 @@ __global__ __launch_bounds__(kBlock, KMAJOR ? 3 : 1) void grouped_down_kernel(Do
       }
     }
     // hidden tile pt: thread chunk c = tid + j kBlock is row c / HC, chunk c % HC
+    // (KMAJOR: every lane also loads the dz of the tile's pair lane % 32, so all waves issue the same loads)
     u32x4 hr[HL];
+    float hz = 0.f;
     auto hload = [&](int pt) {
 #pragma unroll
       for (int j = 0; j < HL; ++j) {
         const int c = tid + j * kBlock, r = c / HC;
         const int pr = pt * kDownPairs + r < n_i ? pt * kDownPairs + r : n_i - 1;
         hr[j] = *reinterpret_cast<const u32x4*>(da.hid + (p0 + pr) * K + (c % HC) * 8);
+      }
+      if constexpr (KMAJOR) {
+        const int r = lane & (kDownPairs - 1);
+        hz = da.pair_dz[p0 + (pt * kDownPairs + r < n_i ? pt * kDownPairs + r : n_i - 1)];
       }
     };
     auto hwrite = [&](int buf) {
@@ -582,14 +599,32 @@ __global__ __launch_bounds__(kBlock, KMAJOR ? 3 : 1) void grouped_down_kernel(Do
         const int c = tid + j * kBlock;
         *reinterpret_cast<u32x4*>(&htile[buf][lds_off<HB>(c / HC, c % HC)]) = hr[j];
       }
+      if constexpr (KMAJOR)
+        if (tid < kDownPairs) hdz[buf][tid] = hz;
     };
     auto tile = [&](int buf, int pt) {
       if (!has_slab) return;  // (such a wave still loads and meets the barriers)
       f32x4 acc[NB][2];
+      if constexpr (KMAJOR) {
+        // each product starts from dz_p W_add[i] at its four columns (lane (m, g): columns
+        // 16 b + 4 g .. +3 of pair 16 a + m, as the MFMA leaves them)
+        float z[2];
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+        for (int a = 0; a < 2; ++a) z[a] = hdz[buf][16 * a + m];
 #pragma unroll
-        for (int a = 0; a < 2; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < NB; ++b) {
+          const u32x2 wv = *reinterpret_cast<const u32x2*>(&wadd[w * SN + 16 * b + 4 * g]);
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+            acc[b][a] = f32x4{z[a] * bf16_lo(wv[0]), z[a] * bf16_hi(wv[0]), z[a] * bf16_lo(wv[1]),
+                              z[a] * bf16_hi(wv[1])};
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         u32x4 hb[2];  // lane (m, g): pair 16 a + m, elements 32 kk + 8 g .. +7
@@ -635,7 +670,16 @@ __global__ __launch_bounds__(kBlock, KMAJOR ? 3 : 1) void grouped_down_kernel(Do
     // loads, so a wait for those rows never waits for the latest stores.
     // Loads past the last tile repeat it.
     hload(phys(0));
-    hwrite(0);
+    if constexpr (KMAJOR) {
+      // the item's W_add[i] columns (past N: column 0, unused), loaded by every thread (the same
+      // loads in every wave), stored by the first kAddCols / 8; published by the barrier below
+      const int c8 = tid % (kAddCols / 8), col = grp * kAddCols + c8 * 8;
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(da.w_add + (int64_t)i * N + (col < N ? col : 0));
+      hwrite(0);
+      if (tid < kAddCols / 8) *reinterpret_cast<u32x4*>(&wadd[c8 * 8]) = wv;
+    } else {
+      hwrite(0);
+    }
     hload(phys(tiles > 1 ? 1 : 0));
     __syncthreads();
     for (int t = 0; t < tiles; ++t) {

@@ -254,7 +254,8 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
   }
 }
 
-// ---- router backward per token: dz (fp32 and bf16, and per pair for the dx rows), ds terms ----
+// ---- router backward per token: dz (fp32 and bf16, and per pair for the dx rows), ds terms;
+// with an extra router gradient also the inactive experts' dz (bf16, active ones 0) ----
 // Wave w of a block handles token 4 blockIdx + w; lane l experts l and l + 64.
 __global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restrict__ z,
                                                             const float* __restrict__ rms_scale,
@@ -263,7 +264,8 @@ __global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restr
                                                             const float* __restrict__ dgp, int n_nt, int64_t T, int E,
                                                             const float* __restrict__ dz_extra,
                                                             float* __restrict__ dz, uint16_t* __restrict__ dzb,
-                                                            float* __restrict__ dsc, float* __restrict__ pair_dz) {
+                                                            float* __restrict__ dsc, float* __restrict__ pair_dz,
+                                                            uint16_t* __restrict__ dz_off) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -301,6 +303,7 @@ __global__ __launch_bounds__(kBlock) void bwd_router_kernel(const float* __restr
     }
     if (on[h]) pair_dz[pv[h]] = dzi;
     dzb[t * kRouterPad + i] = (uint16_t)f32_to_bf16(i < E ? dzi : 0.f);
+    if (dz_off) dz_off[t * kRouterPad + i] = (uint16_t)f32_to_bf16(i < E && !on[h] ? dzi : 0.f);
   }
 }
 
@@ -494,13 +497,60 @@ __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
   }
 }
 
+// ---- dx[t][n] = sum over the inactive experts i of dz[t][i] W_r[i][n] (an extra router gradient
+// reaches every expert; the active ones are in their pair rows) ----
+// Block: 128 columns x 64 tokens.  The block's slice of W_r (every expert's 128 columns) sits in
+// LDS as k-major rows and reaches the MFMA as operand A (16 columns) through transpose loads; the
+// tokens' inactive dz rows (bf16, padded to kRouterPad with zeros) are operand B.  Wave w takes
+// tokens 16 w .. +15 of the block's 64.
+__global__ __launch_bounds__(kBlock) void bwd_router_dx_kernel(const uint16_t* __restrict__ w_r, int E,
+                                                               const uint16_t* __restrict__ dz_off, int64_t T,
+                                                               int d, float* __restrict__ dx) {
+  constexpr int kSteps = kRouterPad / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t rows[kRouterPad * 256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 128;
+  const int64_t t0 = (int64_t)blockIdx.y * 64 + 16 * w;
+  const int64_t tb = t0 + m < T ? t0 + m : T - 1;  // (a repeated token's column is not stored)
+  const int ksteps = (E + 31) / 32;
+  u32x4 b[kSteps];
+#pragma unroll
+  for (int kk = 0; kk < kSteps; ++kk)
+    b[kk] = *reinterpret_cast<const u32x4*>(dz_off + tb * kRouterPad + 32 * kk + 8 * g);
+  // row i of the slice: W_r[i][n0 .. n0 + 127] (rows past E: zeros), 16-byte chunk q % 16 of row q / 16
+#pragma unroll
+  for (int j = 0; j < kRouterPad * 16 / kBlock; ++j) {
+    const int q = tid + j * kBlock, r = q >> 4, c = q & 15;
+    const u32x4 v = r < E ? *reinterpret_cast<const u32x4*>(w_r + (int64_t)r * d + n0 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(rows + tg_off(r, c)) = v;
+  }
+  __syncthreads();
+  f32x4 acc[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < ksteps; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 a[4];
+      tg_operands<4>(rows + kk * 32 * 256, 64 * h, lane, a);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[4 * h + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j]), as_bf16x8(b[kk]), acc[4 * h + j],
+                                                                 0, 0, 0);
+    }
+  // lane (m, g): columns n0 + 16 s + 4 g .. +3 of token t0 + m
+  if (t0 + m >= T) return;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) *reinterpret_cast<f32x4*>(dx + (t0 + m) * d + n0 + 16 * s + 4 * g) = acc[s];
+}
+
 // ---- dx[t] = sum over active i (ascending) of Part[pair_idx[t][i]] (each row already holds its
-// dz[t][i] W_r[i]); with an extra router gradient, then the inactive experts' dz[t][i] W_r[i] ----
-__global__ __launch_bounds__(1024) void bwd_combine_kernel(const float* __restrict__ z, const float* __restrict__ dz,
+// dz[t][i] W_r[i]), added onto the inactive experts' router term in dx when `accumulate` ----
+__global__ __launch_bounds__(1024) void bwd_combine_kernel(const float* __restrict__ z,
                                                            const int32_t* __restrict__ pair_idx,
-                                                           const uint16_t* __restrict__ part,
-                                                           const uint16_t* __restrict__ w_router, int64_t T, int E,
-                                                           int d, bool all_experts, float* __restrict__ dx) {
+                                                           const uint16_t* __restrict__ part, int64_t T, int E,
+                                                           int d, bool accumulate, float* __restrict__ dx) {
   __shared__ int32_t plist[128];
   __shared__ int nlist;
   const int64_t t = blockIdx.x;
@@ -521,7 +571,16 @@ __global__ __launch_bounds__(1024) void bwd_combine_kernel(const float* __restri
   __syncthreads();
   const int n = nlist;
   for (int c0 = tid * 8; c0 < d; c0 += blockDim.x * 8) {
+    f32x4* o = reinterpret_cast<f32x4*>(dx + t * d + c0);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (accumulate) {
+      const f32x4 r0 = o[0], r1 = o[1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q] = r0[q];
+        acc[4 + q] = r1[q];
+      }
+    }
     // kCombineInFlight partial rows in flight, added in ascending expert order
     for (int s = 0; s < n; s += kCombineInFlight) {
       u32x4 v[kCombineInFlight];
@@ -537,20 +596,6 @@ __global__ __launch_bounds__(1024) void bwd_combine_kernel(const float* __restri
             acc[2 * q + 1] += bf16_hi(v[u][q]);
           }
     }
-    if (all_experts) {
-      // an extra router gradient reaches inactive experts too: their dz W_r rows, ascending
-      for (int i = 0; i < E; ++i) {
-        const float zs = dz[t * E + i];
-        if (z[t * E + i] > 0.f || zs == 0.f) continue;  // active ones are in their pair rows
-        const u32x4 wv = *reinterpret_cast<const u32x4*>(w_router + (int64_t)i * d + c0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += zs * bf16_lo(wv[q]);
-          acc[2 * q + 1] += zs * bf16_hi(wv[q]);
-        }
-      }
-    }
-    f32x4* o = reinterpret_cast<f32x4*>(dx + t * d + c0);
     o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
     o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
@@ -561,7 +606,7 @@ struct BwdLayout {
   int64_t *pair_off, *tile_up, *all_off;
   int32_t *pair_tok, *pair_idx;
   float *pair_gate, *g_b, *r_b, *dgp, *dz, *dsc, *wr_part, *pair_dz;
-  uint16_t *dyb, *du, *hg, *dzb, *part;
+  uint16_t *dyb, *du, *hg, *dzb, *dz_off, *part;
   size_t bytes;
 };
 
@@ -594,6 +639,7 @@ BwdLayout bwd_layout(char* base, int64_t T, int E, int d, int de) {
   L.dsc = reinterpret_cast<float*>(take(4 * P));
   L.pair_dz = reinterpret_cast<float*>(take(4 * P));
   L.dzb = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * kRouterPad));
+  L.dz_off = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * kRouterPad));
   L.part = reinterpret_cast<uint16_t*>(take(2 * P * d));
   L.bytes = off;
   return L;
@@ -638,7 +684,8 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   bwd_pair_kernel<<<dim3((unsigned)grid_pair), dim3(kBlock), 0, s>>>(pa);
   se.record(2, s);
   bwd_router_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(kBlock), 0, s>>>(
-      preact, la.rms_scale, L.r_b, L.pair_idx, L.dgp, de / GBN, T, E, dz_extra, L.dz, L.dzb, L.dsc, L.pair_dz);
+      preact, la.rms_scale, L.r_b, L.pair_idx, L.dgp, de / GBN, T, E, dz_extra, L.dz, L.dzb, L.dsc, L.pair_dz,
+      dz_extra != nullptr ? L.dz_off : nullptr);
   bwd_reduce_kernel<<<dim3((unsigned)E), dim3(kBlock), 0, s>>>(L.dz, L.dsc, T, E, d_b_router, d_rms_scale);
   // dW_out[i][k][j] = sum_p dY[t_p][k] HG[p][j]
   TGemmArgs go{L.dyb, d, L.pair_tok, L.hg, de, nullptr, L.pair_off, d_w_out, de, (int64_t)d * de, E, d, d, de};
@@ -661,10 +708,13 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   else
     grouped_down_kernel<256, true><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
   se.record(4, s);
+  if (dz_extra != nullptr)  // the inactive experts' router term goes into dx first
+    bwd_router_dx_kernel<<<dim3((unsigned)(d / 128), (unsigned)((T + 63) / 64)), dim3(kBlock), 0, s>>>(
+        w_r, E, L.dz_off, T, d, dx);
   int cthreads = (d / 8 + 63) / 64 * 64;
   cthreads = cthreads < 64 ? 64 : (cthreads > 1024 ? 1024 : cthreads);
-  bwd_combine_kernel<<<dim3((unsigned)T), dim3((unsigned)cthreads), 0, s>>>(preact, L.dz, L.pair_idx, L.part, w_r, T,
-                                                                           E, d, dz_extra != nullptr, dx);
+  bwd_combine_kernel<<<dim3((unsigned)T), dim3((unsigned)cthreads), 0, s>>>(preact, L.pair_idx, L.part, T, E, d,
+                                                                           dz_extra != nullptr, dx);
   se.record(5, s);
   return hipGetLastError();
 }

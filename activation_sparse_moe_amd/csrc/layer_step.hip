@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kBlock) void route_split_kernel(LayerArgs la, const
                                                              int S, float* __restrict__ zpart) {
   const int64_t u = blockIdx.x / S;
   const int s = (int)(blockIdx.x % S);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int d = la.d, E = la.E;
   const uint16_t* wr = layer_ptr<kTWRouter>(la, static_cast<const uint16_t*>(la.w_router), u);
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kStepThreads) void step_up_kernel(LayerArgs la, con
   __shared__ float zl[128 * kStepMaxL];
   __shared__ uint64_t ml[kStepMaxL * 2];
   __shared__ float bs[256];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int d = la.d, E = la.E, de = la.de, R = de >> 4;
   const int64_t b = blockIdx.x, nb = units * E * R;
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kStepThreads) void step_down_kernel(LayerArgs la, i
   constexpr int DB = NT == 1 ? kBatch : kBatch / 2;  // steps whose loads are issued together
   __shared__ f32x4 red[kStepWaves - 1][NT][kWave];
   __shared__ unsigned hist[129];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int d = la.d, E = la.E, de = la.de;
   const int rbs = d >> 4;

@@ -201,8 +201,10 @@ def test_cls_losses_match_oracle(name):
     say(f"  {name}: L_AL {losses[0]:.6f} (oracle {al:.6f}), L_CS {losses[1]:.6f} (oracle {cs:.6f})")
 
 
-def test_backward_with_cls_gradient_matches_oracle():
-    name = "d512_E64_de128_T96"
+# E = 80: the router term's contraction runs over expert rows padded to 96 with zeros; T = 70 and 96:
+# token tiles of 64 with a ragged tail
+@pytest.mark.parametrize("name", ["d512_E64_de128_T96", "d256_E80_de256_T70"])
+def test_backward_with_cls_gradient_matches_oracle(name):
     layer, x, dy = _layer_and_tokens(name)
     L = CASES[name][4]
     say(f"[gpu] backward + cls gradient {name}")

@@ -238,20 +238,22 @@ class StepRunner:
         avg = {k: sum(v) / len(v) for k, v in per.items() if v}
         return total_ms / steps, avg
 
-    def graph_ms(self, mode: str, steps: int, warmup: int) -> float:
+    def graph_ms(self, mode: str, steps: int, warmup: int, forward_only: bool = False) -> float:
         """One whole step (every sub-batch) captured in a HIP graph and replayed:
-        the step with no host launch overhead."""
+        the step with no host launch overhead.  forward_only: the forward calls
+        alone (every sub-batch; route and union results from earlier steps)."""
         torch = self.torch
+        run = (lambda: self.forward_calls(mode)) if forward_only else (lambda: self.step(mode))
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for _ in range(max(1, warmup)):
-                self.step(mode)
+                run()
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.step(mode)
+            run()
         for _ in range(max(1, warmup)):
             g.replay()
         torch.cuda.synchronize()
@@ -259,6 +261,32 @@ class StepRunner:
         a.record()
         for _ in range(steps):
             g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def forward_calls(self, mode: str):
+        """blockffn_forward of every sub-batch, on the gates and unions already in the buffers."""
+        B, cfg = self.B, self.cfg
+        L = cfg.chunk_len
+        C = cfg.n_tokens // L
+        for b in range(self.n_sub):
+            c0, c1 = b * self.sub_units, min(C, (b + 1) * self.sub_units)
+            t0, t1 = c0 * L, c1 * L
+            B.blockffn_forward(self.dl, self.xd[t0:t1], L, self.gates[t0:t1], self.count[c0:c1], self.lst[c0:c1],
+                               mode=mode, workspace=self.ws[mode], y=self.y[t0:t1])
+
+    def eager_ms(self, mode: str, steps: int, warmup: int) -> float:
+        """Eager steps with no events inside the timed loop (instrumented steps
+        leave the GPU idle between launches on the larger layers)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(mode)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            self.step(mode)
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
@@ -932,10 +960,14 @@ def main(argv=None) -> int:
         copy_calibration()
     runner = StepRunner(cfg, mode, args.router, args.top_k)
     # eager steps, instrumented: per-kernel times for the roofline
-    eager_ms, avg = runner.timed(mode, args.steps, args.warmup)
+    _, avg = runner.timed(mode, args.steps, args.warmup)
+    eager_ms = runner.eager_ms(mode, args.steps, args.warmup)
     # the timed steps: each whole step (every sub-batch) replayed from a HIP
     # graph, so host launch overhead is not in the figure (--eager: eager)
     ms = eager_ms if args.eager else runner.graph_ms(mode, args.steps, args.warmup)
+    # the forward alone (planning and expert kernels of every sub-batch), replayed from a graph: the
+    # figure the dense comparisons divide by
+    avg["forward"] = runner.graph_ms(mode, args.steps, args.warmup, forward_only=True)
     from activation_sparse_moe_amd import binding as B
     st = B.stats_dict(runner.stats)
     bytes_per, U, active_weight, step_alg = runner.byte_model()
@@ -949,9 +981,8 @@ def main(argv=None) -> int:
         dense = {"kind": "torch.matmul (hipBLASLt) dense GEMMs over all experts", "forward_ms": round(dfwd, 4),
                  "speedup_forward": round(dfwd / avg["forward"], 3) if "forward" in avg else None}
     elif args.dense_steps > 0:
-        dms, davg = runner.timed("dense", args.dense_steps, 1)
-        if not args.eager:
-            dms = runner.graph_ms("dense", args.dense_steps, 1)
+        dms = runner.eager_ms("dense", args.dense_steps, 1) if args.eager else runner.graph_ms("dense", args.dense_steps, 1)
+        davg = {"forward": runner.graph_ms("dense", args.dense_steps, 1, forward_only=True)}
         dense = {"kind": "same kernels, every expert (BLOCKFFN_MODE_DENSE)", "ms_per_step": round(dms, 4),
                  "speedup_step": round(dms / ms, 3)}
         if "forward" in davg and "forward" in avg:
@@ -1030,7 +1061,8 @@ def main(argv=None) -> int:
         "dense": dense,
         "timing": {"steps": "eager launches" if args.eager else "HIP graph replay of each whole step",
                    "eager_ms_per_step": round(eager_ms, 5),
-                   "kernel_ms": "eager steps with HIP events around each launch"},
+                   "kernel_ms": "eager steps with HIP events around each launch; forward: the forward calls alone "
+                                "(planning and expert kernels, every sub-batch) replayed from a HIP graph"},
         "backward": backward,
         "latency": latency,
         "ceilings": ceilings,

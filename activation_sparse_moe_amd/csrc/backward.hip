@@ -666,7 +666,7 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
                                                              L.dyb, L.all_off);
   group_count_kernel<PairRule::kPositive><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(preact, T, E, rows,
                                                                                               L.blk);
-  group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(L.blk, nblk, E, de / GBN, L.pair_off, L.tile_up);
+  group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(L.blk, nblk, E, de / GBN, GBM, L.pair_off, L.tile_up);
   group_fill_kernel<PairRule::kPositive><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(
       preact, L.g_b, T, E, rows, L.blk, L.pair_tok, L.pair_gate, L.pair_idx);
 

@@ -47,12 +47,12 @@ hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_
   uint16_t* part = reinterpret_cast<uint16_t*>(take(2 * P * d));
 
   group_count_kernel<PairRule::kNonZero><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(gates, T, E, rows, blk);
-  group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(blk, nblk, E, de / GBN, pair_off, tile_up);
+  group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(blk, nblk, E, de / GBN, kUpRows, pair_off, tile_up);
   group_fill_kernel<PairRule::kNonZero><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(
       gates, gates, T, E, rows, blk, pair_tok, pair_gate, pair_idx);
   // upper bounds of the work (every pair active) cap the grids; the kernels
   // read the exact totals on the device
-  const int64_t max_up_tiles = (int64_t)E * ((T + GBM - 1) / GBM) * (de / GBN);
+  const int64_t max_up_tiles = (int64_t)E * ((T + kUpRows - 1) / kUpRows) * (de / GBN);
   int64_t grid_up = 0, grid_dn = 0;
   hipError_t e = persistent_grid(grouped_up_kernel, max_up_tiles, &grid_up);
   if (e == hipSuccess)

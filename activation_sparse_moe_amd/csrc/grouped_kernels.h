@@ -120,10 +120,10 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* wsum
   return before + inc - v;
 }
 
-// ---- scan: expert offsets, up-tile offsets, per-block first slots (in place) ----
+// ---- scan: expert offsets, up-tile offsets (tiles of tile_rows pairs), per-block first slots (in place) ----
 // Thread (part, i) owns expert i's counts of token blocks [b0, b1).
 __global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ blk, int nblk, int E, int n_tiles_up,
-                                                          int64_t* __restrict__ pair_off,
+                                                          int tile_rows, int64_t* __restrict__ pair_off,
                                                           int64_t* __restrict__ tile_up) {
   __shared__ int64_t part_sum[1024];
   __shared__ int64_t exp_off[128];
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ 
   int64_t n = 0;
   if (tid < E)
     for (int q = 0; q < nparts; ++q) n += part_sum[q * E + tid];
-  const int64_t tiles = (n + GBM - 1) / GBM * n_tiles_up;
+  const int64_t tiles = (n + tile_rows - 1) / tile_rows * n_tiles_up;
   int64_t n_all = 0, t_all = 0;
   const int64_t p_ex = block_exclusive_scan(n, wsum, &n_all);
   const int64_t t_ex = block_exclusive_scan(tiles, wsum, &t_all);
@@ -234,25 +234,26 @@ struct UpArgs {
   int K, N, E;
 };
 
-// Tile: 64 pairs x 128 hidden units over k in steps of 64; wave (wm, wn)
-// computes pairs wm*32 .. +31 against hidden units wn*64 .. +63.  Both
+// Tile: kUpRows (128) pairs x 128 hidden units over k in steps of 64; wave
+// (wm, wn) computes pairs wm*64 .. +63 against hidden units wn*64 .. +63.  Both
 // operands reach LDS by DMA (global_load_lds: 16 bytes per lane, each
 // 128-byte row piece read whole; the gathered token rows too, every lane
 // with its own row) into a block-shared ring of kUpRing buffers, with the
-// two steps after the one being multiplied in flight.  A step's 24 DMA
+// three steps after the one being multiplied in flight.  A step's 32 DMA
 // instructions are split over the four waves.  Each wave waits for its own
 // share with a constant vmcnt, and one barrier per step tells every wave
 // that the step has landed and that the buffer about to be refilled has
 // been read by all of them.  The 16-byte chunks are swizzled on the source
 // side (lane slot c of row r holds chunk c ^ ((r >> 1) & 7)), the layout the
 // operand reads below expect.
-constexpr int kUpRing = 3;
-constexpr int kUpABytes = GBM * 128;                             // 64 pair rows x 128 bytes
-constexpr int kUpBufBytes = kUpABytes + GBN * 128;               // + 128 weight rows: 24 KiB
-constexpr int kUpDmaPerWave = (GBM + GBN) / 8 / (kBlock / kWave);  // 1 KiB instructions per wave and step
+constexpr int kUpRing = 4;
+constexpr int kUpRows = 128;                                        // pairs per up tile
+constexpr int kUpABytes = kUpRows * 128;                            // 128 pair rows x 128 bytes
+constexpr int kUpBufBytes = kUpABytes + GBN * 128;                  // + 128 weight rows: 32 KiB
+constexpr int kUpDmaPerWave = (kUpRows + GBN) / 8 / (kBlock / kWave);  // 1 KiB instructions per wave and step
 
 __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
-  static_assert(GBK == kStepK && kUpDmaPerWave * (kBlock / kWave) * 8 == GBM + GBN, "ring geometry");
+  static_assert(GBK == kStepK && kUpDmaPerWave * (kBlock / kWave) * 8 == kUpRows + GBN, "ring geometry");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kUpRing][kUpBufBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -278,10 +279,10 @@ __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
     const int i = lo;
     const int64_t p0 = ua.pair_off[i];
     const int n_i = (int)(ua.pair_off[i + 1] - p0);
-    const int m_tiles = (n_i + GBM - 1) / GBM;
+    const int m_tiles = (n_i + kUpRows - 1) / kUpRows;
     const int64_t local_t = tt - ua.tile_off[i];
     const int nt = (int)(local_t / m_tiles), mt = (int)(local_t % m_tiles);
-    const int m0 = mt * GBM, n0 = nt * GBN;
+    const int m0 = mt * kUpRows, n0 = nt * GBN;
 
     // this wave's DMA instructions j = w kUpDmaPerWave + q of a step: j < 8
     // moves pair rows 8 j .. +7 (gathered token rows; rows past the group
@@ -291,15 +292,15 @@ __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
 #pragma unroll
     for (int q = 0; q < kUpDmaPerWave; ++q) {
       const int j = w * kUpDmaPerWave + q;
-      if (j < GBM / 8) {
+      if (j < kUpRows / 8) {
         const int R = 8 * j + (lane >> 3);
         const int pr = m0 + R < n_i ? m0 + R : n_i - 1;
         src[q] = ua.x + (int64_t)ua.pair_tok[p0 + pr] * K + dma_chunk_elems(R, lane);
         dst[q] = j * 1024;
       } else {
-        const int R = 8 * (j - GBM / 8) + (lane >> 3);
+        const int R = 8 * (j - kUpRows / 8) + (lane >> 3);
         src[q] = ua.w + ((int64_t)i * N + n0 + R) * K + dma_chunk_elems(R, lane);
-        dst[q] = kUpABytes + (j - GBM / 8) * 1024;
+        dst[q] = kUpABytes + (j - kUpRows / 8) * 1024;
       }
     }
     const int ksteps = K / GBK;
@@ -309,41 +310,42 @@ __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
       for (int q = 0; q < kUpDmaPerWave; ++q) dma16<kPolicyReuse>(src[q] + st * GBK, &ring[slot][0] + dst[q]);
     };
 
-    f32x4 acc[4][2];  // [hidden stripe b][pair group a]
+    f32x4 acc[4][4];  // [hidden stripe b][pair group a]
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int a = 0; a < 2; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int a = 0; a < 4; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     issue(0, 0);
     issue(1, 1);
+    issue(2, 2);
     for (int ks = 0; ks < ksteps; ++ks) {
-      wait_vmcnt<kUpDmaPerWave>();  // this wave's share of step ks has landed
+      wait_vmcnt<2 * kUpDmaPerWave>();  // this wave's share of step ks has landed
       block_barrier_no_fence();     // ... and everyone's; step ks - 1's buffer is free
-      issue((ks + 2) % kUpRing, ks + 2);
+      issue((ks + 3) % kUpRing, ks + 3);
       const uint8_t* buf = &ring[ks % kUpRing][0];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        u32x4 av[2], bv[4];
+        u32x4 av[4], bv[4];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-          av[a] = *reinterpret_cast<const u32x4*>(buf + lds_off<128>(wm * 32 + a * 16 + m, kk * 4 + g));
+        for (int a = 0; a < 4; ++a)
+          av[a] = *reinterpret_cast<const u32x4*>(buf + lds_off<128>(wm * 64 + a * 16 + m, kk * 4 + g));
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           bv[b] = *reinterpret_cast<const u32x4*>(buf + kUpABytes + lds_off<128>(wn * 64 + b * 16 + m, kk * 4 + g));
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-          for (int a = 0; a < 2; ++a)
+          for (int a = 0; a < 4; ++a)
             acc[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bv[b]), as_bf16x8(av[a]), acc[b][a], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // lane (m, g): pair wm*32 + a*16 + m, hidden units n0 + wn*64 + b*16 + 4g .. +3
+    // lane (m, g): pair wm*64 + a*16 + m, hidden units n0 + wn*64 + b*16 + 4g .. +3
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int row = m0 + wm * 32 + a * 16 + m;
+    for (int a = 0; a < 4; ++a) {
+      const int row = m0 + wm * 64 + a * 16 + m;
       if (row >= n_i) continue;
       const float gv = ua.pair_gate[p0 + row];
       uint16_t* orow = ua.hid + (p0 + row) * N + n0 + wn * 64 + 4 * g;

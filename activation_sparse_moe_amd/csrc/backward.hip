@@ -77,12 +77,15 @@ __global__ __launch_bounds__(kBlock) void bwd_prep_kernel(const float* __restric
   }
 }
 
-// ---- pair: U and Q for a 64-pair x 128-hidden tile, fused epilogue ----
-// A 64-wide k step stages 64 gathered x rows, 64 gathered dy rows and 128
+// ---- pair: U and Q for a kPairRows (96)-pair x 128-hidden tile, fused epilogue ----
+// A 64-wide k step stages 96 gathered x rows, 96 gathered dy rows and 128
 // W_in rows (128 bytes each, chunk-swizzled), and 64 k-major W_out rows of the
 // tile's 128 hidden units (256 bytes each), read back by transpose loads.  One
-// LDS buffer (48 KiB) lets two blocks share a CU; the registers hold the next
-// step while this one is multiplied.
+// LDS buffer (56 KiB) lets two blocks share a CU, with the registers capped for
+// two waves per SIMD (a few spill; one block per CU without spills measured
+// 30% slower); the registers hold the next step while this one is multiplied.
+constexpr int kPairRows = 96;                     // pairs per tile: each wave 48 (three 16-pair groups)
+constexpr int kPairStage = kPairRows * 8 / kBlock;  // 16-byte x (and dy) chunks per thread and step
 struct PairArgs {
   const uint16_t* x;        // [T][d]
   const uint16_t* dy;       // [T][d] bf16
@@ -98,12 +101,13 @@ struct PairArgs {
   int d, de, E;
 };
 
-__global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_x[GBM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_y[GBM * 128];
+__global__ __launch_bounds__(kBlock, 2) void bwd_pair_kernel(PairArgs pa) {
+  static_assert(kPairStage * kBlock == kPairRows * 8 && kPairRows % 32 == 0, "pair tile staging");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_x[kPairRows * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_y[kPairRows * 128];
   __shared__ __attribute__((aligned(16))) uint8_t lds_wi[GBN * 128];
   __shared__ __attribute__((aligned(16))) uint8_t lds_wo[GBK * GBN * 2];  // k-major: 64 rows of 128 hidden units
-  __shared__ float dg_part[2][GBM];
+  __shared__ float dg_part[2][kPairRows];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int m = lane & 15, g = lane >> 4;
@@ -126,15 +130,15 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
     const int i = lo;
     const int64_t p0 = pa.pair_off[i];
     const int n_i = (int)(pa.pair_off[i + 1] - p0);
-    const int m_tiles = (n_i + GBM - 1) / GBM;
+    const int m_tiles = (n_i + kPairRows - 1) / kPairRows;
     const int64_t local_t = tt - pa.tile_off[i];
     const int nt = (int)(local_t / m_tiles), mt = (int)(local_t % m_tiles);
-    const int m0 = mt * GBM, n0 = nt * GBN;
+    const int m0 = mt * kPairRows, n0 = nt * GBN;
 
-    const uint16_t* x_src[2];
-    const uint16_t* y_src[2];
+    const uint16_t* x_src[kPairStage];
+    const uint16_t* y_src[kPairStage];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kPairStage; ++j) {
       const int r = (tid + j * kBlock) >> 3;
       const int pr = m0 + r < n_i ? m0 + r : n_i - 1;  // rows past the group repeat a valid row
       const int64_t tok = pa.pair_tok[p0 + pr];
@@ -149,10 +153,10 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
       wi_src[j] = pa.w_in + ((int64_t)i * N + n0 + (c >> 3)) * K + (c & 7) * 8;
       wo_src[j] = pa.w_out + ((int64_t)i * K + (c >> 4)) * N + n0 + (c & 15) * 8;
     }
-    u32x4 rx[2], ry[2], rwi[4], rwo[4];
+    u32x4 rx[kPairStage], ry[kPairStage], rwi[4], rwo[4];
     auto gload = [&](int k0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kPairStage; ++j) {
         rx[j] = *reinterpret_cast<const u32x4*>(x_src[j] + k0);
         ry[j] = *reinterpret_cast<const u32x4*>(y_src[j] + k0);
       }
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
     };
     auto swrite = [&]() {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kPairStage; ++j) {
         const int c = tid + j * kBlock;
         *reinterpret_cast<u32x4*>(&lds_x[lds_off<128>(c >> 3, c & 7)]) = rx[j];
         *reinterpret_cast<u32x4*>(&lds_y[lds_off<128>(c >> 3, c & 7)]) = ry[j];
@@ -177,11 +181,12 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
       }
     };
 
-    f32x4 au[4][2], aq[4][2];  // [hidden stripe b][pair group a]
+    constexpr int PA = kPairRows / 32;  // 16-pair groups per wave
+    f32x4 au[4][PA], aq[4][PA];       // [hidden stripe b][pair group a]
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int a = 0; a < 2; ++a) au[b][a] = aq[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int a = 0; a < PA; ++a) au[b][a] = aq[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int ksteps = K / GBK;
     // one LDS buffer (two blocks fit on a CU): the registers hold step ks + 1
@@ -194,11 +199,11 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
       if (ks + 1 < ksteps) gload((ks + 1) * GBK);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        u32x4 vx[2], vy[2], vwi[4], vwo[4];
+        u32x4 vx[PA], vy[PA], vwi[4], vwo[4];
         tg_operands(lds_wo + kk * 32 * 256, wn * 64, lane, vwo);
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int off = lds_off<128>(wm * 32 + a * 16 + m, kk * 4 + g);
+        for (int a = 0; a < PA; ++a) {
+          const int off = lds_off<128>(wm * (16 * PA) + a * 16 + m, kk * 4 + g);
           vx[a] = *reinterpret_cast<const u32x4*>(&lds_x[off]);
           vy[a] = *reinterpret_cast<const u32x4*>(&lds_y[off]);
         }
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-          for (int a = 0; a < 2; ++a) {
+          for (int a = 0; a < PA; ++a) {
             au[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vwi[b]), as_bf16x8(vx[a]), au[b][a], 0, 0, 0);
             aq[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vwo[b]), as_bf16x8(vy[a]), aq[b][a], 0, 0, 0);
           }
@@ -218,10 +223,10 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
       block_barrier_no_fence();
     }
 
-    // lane (m, g): pair wm*32 + a*16 + m, hidden units n0 + wn*64 + b*16 + 4g .. +3
+    // lane (m, g): pair wm*16 PA + a*16 + m, hidden units n0 + wn*64 + b*16 + 4g .. +3
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int row = m0 + wm * 32 + a * 16 + m;
+    for (int a = 0; a < PA; ++a) {
+      const int row = m0 + wm * (16 * PA) + a * 16 + m;
       const bool valid = row < n_i;
       const float gv = valid ? pa.pair_gate[p0 + row] : 0.f;
       float dgl = 0.f;
@@ -246,10 +251,10 @@ __global__ __launch_bounds__(kBlock) void bwd_pair_kernel(PairArgs pa) {
       // the four lane groups g hold the same pair: sum them, then the two wn waves via LDS
       dgl += __shfl_xor(dgl, 16, kWave);
       dgl += __shfl_xor(dgl, 32, kWave);
-      if (g == 0) dg_part[wn][wm * 32 + a * 16 + m] = dgl;
+      if (g == 0) dg_part[wn][wm * (16 * PA) + a * 16 + m] = dgl;
     }
     __syncthreads();
-    if (tid < GBM && m0 + tid < n_i) pa.dgp[(p0 + m0 + tid) * n_nt + nt] = dg_part[0][tid] + dg_part[1][tid];
+    if (tid < kPairRows && m0 + tid < n_i) pa.dgp[(p0 + m0 + tid) * n_nt + nt] = dg_part[0][tid] + dg_part[1][tid];
     // (dg_part is next written after this tile's k loop, which has barriers)
   }
 }
@@ -666,11 +671,11 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
                                                              L.dyb, L.all_off);
   group_count_kernel<PairRule::kPositive><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(preact, T, E, rows,
                                                                                               L.blk);
-  group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(L.blk, nblk, E, de / GBN, GBM, L.pair_off, L.tile_up);
+  group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(L.blk, nblk, E, de / GBN, kPairRows, L.pair_off, L.tile_up);
   group_fill_kernel<PairRule::kPositive><<<dim3((unsigned)nblk), dim3(kPlanThreads), 0, s>>>(
       preact, L.g_b, T, E, rows, L.blk, L.pair_tok, L.pair_gate, L.pair_idx);
 
-  const int64_t max_up_tiles = (int64_t)E * ((T + GBM - 1) / GBM) * (de / GBN);
+  const int64_t max_up_tiles = (int64_t)E * ((T + kPairRows - 1) / kPairRows) * (de / GBN);
   int64_t grid_pair = 0, grid_t = 0, grid_dn = 0;
   hipError_t e = persistent_grid(bwd_pair_kernel, max_up_tiles, &grid_pair);
   if (e == hipSuccess) e = persistent_grid(tgemm_kernel, (int64_t)E * (d / TBM) * (de / TBN), &grid_t);

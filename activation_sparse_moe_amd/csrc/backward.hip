@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kBlock) void bwd_router_dx_kernel(const uint16_t* _
 // dz[t][i] W_r[i]), added onto the inactive experts' router term in dx when `accumulate` ----
 __global__ __launch_bounds__(1024) void bwd_combine_kernel(const float* __restrict__ z,
                                                            const int32_t* __restrict__ pair_idx,
-                                                           const uint16_t* __restrict__ part, int64_t T, int E,
+                                                           const uint16_t* __restrict__ part, int E,
                                                            int d, bool accumulate, float* __restrict__ dx) {
   __shared__ int32_t plist[128];
   __shared__ int nlist;
@@ -718,7 +718,7 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
         w_r, E, L.dz_off, T, d, dx);
   int cthreads = (d / 8 + 63) / 64 * 64;
   cthreads = cthreads < 64 ? 64 : (cthreads > 1024 ? 1024 : cthreads);
-  bwd_combine_kernel<<<dim3((unsigned)T), dim3((unsigned)cthreads), 0, s>>>(preact, L.pair_idx, L.part, T, E, d,
+  bwd_combine_kernel<<<dim3((unsigned)T), dim3((unsigned)cthreads), 0, s>>>(preact, L.pair_idx, L.part, E, d,
                                                                            dz_extra != nullptr, dx);
   se.record(5, s);
   return hipGetLastError();

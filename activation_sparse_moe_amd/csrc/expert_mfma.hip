@@ -342,7 +342,6 @@ __global__ __launch_bounds__(kBlock) void up_mfma_kernel(LayerArgs la, const uin
       continue;
     }
     // item complete: g * Swish, bf16, to the hidden buffer (gates from this step's buffer)
-    const int64_t t0 = cmp.unit * L;
     const float* gv_lds = reinterpret_cast<const float*>(buf + G::kGateOff);
 #pragma unroll
     for (int tl = 0; tl < NT; ++tl) {

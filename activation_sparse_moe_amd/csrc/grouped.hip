@@ -64,7 +64,7 @@ hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_
   UpArgs up{x, pair_tok, pair_gate, static_cast<const uint16_t*>(la.w_in), pair_off, tile_up, hid, d, de, E};
   grouped_up_kernel<<<dim3((unsigned)grid_up), dim3(kBlock), 0, s>>>(up);
   se.record(1, s);
-  DownArgs dn{hid, static_cast<const uint16_t*>(la.w_out), pair_off, part, d, E};
+  DownArgs dn{hid, static_cast<const uint16_t*>(la.w_out), pair_off, part, d, E, nullptr, nullptr};
   if (de == 128)
     grouped_down_kernel<128><<<dim3((unsigned)grid_dn), dim3(kBlock), 0, s>>>(dn);
   else
@@ -72,7 +72,7 @@ hipError_t launch_forward_grouped(const LayerArgs& la, const uint16_t* x, int64_
   se.record(2, s);
   int cthreads = (d / 8 + 63) / 64 * 64;
   cthreads = cthreads < 64 ? 64 : (cthreads > 1024 ? 1024 : cthreads);
-  combine_kernel<<<dim3((unsigned)T), dim3((unsigned)cthreads), 0, s>>>(gates, pair_idx, part, T, E, d, y);
+  combine_kernel<<<dim3((unsigned)T), dim3((unsigned)cthreads), 0, s>>>(gates, pair_idx, part, E, d, y);
   se.record(3, s);
   return hipGetLastError();
 }

@@ -17,7 +17,7 @@
 //            gate, and pair_idx[t][i] for the combine (the forward pairs
 //            every non-zero gate; the backward every active pair)
 //   up:      H'[p] = g_p * Swish(x[t_p] W_in[i]^T), bf16, grouped GEMM with
-//            gathered token rows (64 pairs x 128 hidden x 64 k tiles), both
+//            gathered token rows (192 pairs x 128 hidden x 64 k tiles), both
 //            operands DMA'd into a block-shared LDS ring
 //   down:    Part[p] = H'[p] W_out[i]^T, bf16 per-pair partial rows; each
 //            wave keeps one 64-row slab of W_out[i] in registers and runs it
@@ -234,26 +234,37 @@ struct UpArgs {
   int K, N, E;
 };
 
-// Tile: kUpRows (128) pairs x 128 hidden units over k in steps of 64; wave
-// (wm, wn) computes pairs wm*64 .. +63 against hidden units wn*64 .. +63.  Both
+// Tile: kUpRows (192) pairs x 128 hidden units over k in steps of 64; wave
+// (wm, wn) computes pairs wm*96 .. +95 against hidden units wn*64 .. +63.  Both
 // operands reach LDS by DMA (global_load_lds: 16 bytes per lane, each
 // 128-byte row piece read whole; the gathered token rows too, every lane
 // with its own row) into a block-shared ring of kUpRing buffers, with the
-// three steps after the one being multiplied in flight.  A step's 32 DMA
+// three steps after the one being multiplied in flight.  A step's 40 DMA
 // instructions are split over the four waves.  Each wave waits for its own
 // share with a constant vmcnt, and one barrier per step tells every wave
 // that the step has landed and that the buffer about to be refilled has
 // been read by all of them.  The 16-byte chunks are swizzled on the source
 // side (lane slot c of row r holds chunk c ^ ((r >> 1) & 7)), the layout the
 // operand reads below expect.
+//
+// The kernel is bound by the cache lines a CU can have outstanding, so its
+// time follows the lines the busiest CU requests: the weight rows are shared
+// by a tile's pairs, while every pair brings its own token row.  At about 612
+// pairs per expert, 192-pair tiles take 320 lines a step and at most two
+// tiles per CU (640 per step of k); 128-pair tiles take 256 lines and up to
+// three tiles (768), and 256-pair tiles 384 lines and up to two (768).
 constexpr int kUpRing = 4;
-constexpr int kUpRows = 128;                                        // pairs per up tile
-constexpr int kUpABytes = kUpRows * 128;                            // 128 pair rows x 128 bytes
-constexpr int kUpBufBytes = kUpABytes + GBN * 128;                  // + 128 weight rows: 32 KiB
+constexpr int kUpAhead = kUpRing - 1;                               // steps in flight behind the one multiplied
+constexpr int kUpRows = 192;                                        // pairs per up tile
+constexpr int kUpWaveRows = kUpRows / 2;                            // pairs per wave
+constexpr int kUpA = kUpWaveRows / 16;                              // 16-pair MFMA groups per wave
+constexpr int kUpABytes = kUpRows * 128;                            // pair rows of 128 bytes
+constexpr int kUpBufBytes = kUpABytes + GBN * 128;                  // + 128 weight rows: 40 KiB
 constexpr int kUpDmaPerWave = (kUpRows + GBN) / 8 / (kBlock / kWave);  // 1 KiB instructions per wave and step
 
 __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
   static_assert(GBK == kStepK && kUpDmaPerWave * (kBlock / kWave) * 8 == kUpRows + GBN, "ring geometry");
+  static_assert(kUpRows % 32 == 0 && kUpRing * kUpBufBytes <= 160 * 1024, "tile and ring fit LDS");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kUpRing][kUpBufBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -310,33 +321,32 @@ __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
       for (int q = 0; q < kUpDmaPerWave; ++q) dma16<kPolicyReuse>(src[q] + st * GBK, &ring[slot][0] + dst[q]);
     };
 
-    f32x4 acc[4][4];  // [hidden stripe b][pair group a]
+    f32x4 acc[4][kUpA];  // [hidden stripe b][pair group a]
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int a = 0; a < kUpA; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
+#pragma unroll
+    for (int s = 0; s < kUpAhead; ++s) issue(s, s);
     for (int ks = 0; ks < ksteps; ++ks) {
-      wait_vmcnt<2 * kUpDmaPerWave>();  // this wave's share of step ks has landed
+      wait_vmcnt<(kUpAhead - 1) * kUpDmaPerWave>();  // this wave's share of step ks has landed
       block_barrier_no_fence();     // ... and everyone's; step ks - 1's buffer is free
-      issue((ks + 3) % kUpRing, ks + 3);
+      issue((ks + kUpAhead) % kUpRing, ks + kUpAhead);
       const uint8_t* buf = &ring[ks % kUpRing][0];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        u32x4 av[4], bv[4];
+        u32x4 av[kUpA], bv[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-          av[a] = *reinterpret_cast<const u32x4*>(buf + lds_off<128>(wm * 64 + a * 16 + m, kk * 4 + g));
+        for (int a = 0; a < kUpA; ++a)
+          av[a] = *reinterpret_cast<const u32x4*>(buf + lds_off<128>(wm * kUpWaveRows + a * 16 + m, kk * 4 + g));
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           bv[b] = *reinterpret_cast<const u32x4*>(buf + kUpABytes + lds_off<128>(wn * 64 + b * 16 + m, kk * 4 + g));
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < kUpA; ++a)
             acc[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bv[b]), as_bf16x8(av[a]), acc[b][a], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -344,8 +354,8 @@ __global__ __launch_bounds__(kBlock) void grouped_up_kernel(UpArgs ua) {
 
     // lane (m, g): pair wm*64 + a*16 + m, hidden units n0 + wn*64 + b*16 + 4g .. +3
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int row = m0 + wm * 64 + a * 16 + m;
+    for (int a = 0; a < kUpA; ++a) {
+      const int row = m0 + wm * kUpWaveRows + a * 16 + m;
       if (row >= n_i) continue;
       const float gv = ua.pair_gate[p0 + row];
       uint16_t* orow = ua.hid + (p0 + row) * N + n0 + wn * 64 + 4 * g;
@@ -704,7 +714,7 @@ constexpr int kCombineInFlight = 8;  // partial-row loads per thread in flight
 
 __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ gates,
                                                        const int32_t* __restrict__ pair_idx,
-                                                       const uint16_t* __restrict__ part, int64_t T, int E, int d,
+                                                       const uint16_t* __restrict__ part, int E, int d,
                                                        float* __restrict__ y) {
   __shared__ int32_t plist[128];
   __shared__ int nlist;

@@ -38,7 +38,7 @@
 namespace bffn {
 namespace {
 
-constexpr int TBM = 128, TBN = 128, TBK = 32;  // transposing GEMM tile (TBK pairs per step)
+constexpr int TBM = 128, TBN = 256, TBK = 32;  // transposing GEMM tile (TBK pairs per step)
 constexpr int kRouterPad = 128;               // dZ rows padded to 128 experts (bf16)
 constexpr int kRouterSplits = 16;             // dW_r: token range split for parallelism
 
@@ -350,61 +350,67 @@ __global__ __launch_bounds__(kBlock) void bwd_router_sum_kernel(const float* __r
   out[k] = s;
 }
 
-// ---- transposing grouped GEMM: C_g[m][n] = sum over pairs p of group g of A[ra(p)][m] B[rb(p)][n] ----
+// ---- transposing grouped GEMM: C_g[m][n] = sum over pairs p of group g of A[p0 + p][m] B[rb(p)][n] ----
 struct TGemmArgs {
-  const uint16_t* a;        // rows of M (or more) bf16 elements, row stride lda
+  const uint16_t* a;        // pair rows of M (or more) bf16 elements, row stride lda: pair p is row p0 + p
   int64_t lda;
-  const int32_t* a_rows;    // row of pair p (nullptr: row p)
-  const uint16_t* b;
+  const uint16_t* b;        // rows of N (or more) bf16 elements, row stride ldb
   int64_t ldb;
-  const int32_t* b_rows;
-  const int64_t* grp_off;   // [G + 1] pair ranges
-  float* c;                 // group g at c + g * c_stride; [M_valid][N] rows of ldc
+  const int32_t* b_rows;    // B row of pair p (nullptr: row p0 + p)
+  const int64_t* grp_off;   // [G + 1] pair ranges (p0 = grp_off[g])
+  float* c;                 // group g at c + g * c_stride: C[m][n] at m * ldc + n, or at n * ldc + m (c_nm)
   int64_t ldc, c_stride;
-  int G, M, M_valid, N;
+  int G, M, M_valid, N;     // M a multiple of TBM, N of 128
+  bool c_nm;
 };
 
-// The operands lie in memory pair-major (a pair's 128 elements of m, or of n,
-// are one 256-byte row piece), and the contraction runs over pairs.  A step of
-// TBK = 32 pairs reaches LDS untouched, by DMA (global_load_lds, 16 bytes per
-// lane; the gathered rows too, every lane with its own row), into a
-// block-shared ring of kTgRing slots, kTgDepth steps ahead of the one being
-// multiplied.  The MFMA operands (8 consecutive pairs of one m or n per lane)
-// are then read with transpose loads (tg_operands).
+// A tile is 128 rows of A's side by 256 columns of B's side, the gathered
+// operand, so that every gathered B row piece (512 bytes) serves 128 rows and
+// every A piece 256 columns.  The kernel is bound by the cache lines a CU keeps
+// in flight: this tile requests 0.75 of the lines per product that a 128 x
+// 128 tile does.
 //
-// The row indices of a gathered operand come by DMA too, each wave its own
-// 16 per step into its own index ring, issued kTgDepth steps before the rows
-// that use them; the in-order vmcnt wait for a step's rows therefore also
-// covers the indices of the step kTgDepth later, and every wait is a constant.
-// Pairs past the group read a row of zeros.
+// The operands lie in memory pair-major (a pair's elements of m, or of n, are
+// one row piece), and the contraction runs over pairs.  A step of TBK = 32
+// pairs reaches LDS untouched, by DMA (global_load_lds, 16 bytes per lane; the
+// gathered rows too, every lane with its own row), into a block-shared ring of
+// kTgRing slots, kTgDepth steps ahead of the one being multiplied.  A slot
+// holds the step's 32 A rows, then B's two 128-column halves as 32 rows each,
+// all rows of 256 bytes; LDS row r holds pair r of the step.  Each wave moves
+// the rows of 8 pairs.  The MFMA operands (8 consecutive pairs of one m or n
+// per lane) are read with transpose loads (tg_operands).
+//
+// The B row indices come by DMA too, each wave its own 8 per step into its
+// own index ring, issued kTgDepth steps before the rows that use them; the
+// in-order vmcnt wait for a step's rows therefore also covers the indices of
+// the step kTgDepth later, and every wait is a constant.  Pairs past the group
+// read a row of zeros; a tile whose second column half lies past N loads the
+// first half again there and stores only the first.
 constexpr int kTgDepth = 2;
 constexpr int kTgRing = kTgDepth + 1;
 constexpr int kTgIdxSlots = 4;                        // > kTgDepth: indices in flight + the one being read
-constexpr int kTgOpBytes = TBK * TBM * 2;             // 32 rows of 256 bytes
-constexpr int kTgSlotBytes = 2 * kTgOpBytes;          // A rows, then B rows
-constexpr int kTgDmaPerWave = kTgOpBytes / 1024 / 2;  // two waves per operand
+constexpr int kTgHalfBytes = TBK * 256;               // 32 rows of 128 bf16
+constexpr int kTgSlotBytes = 3 * kTgHalfBytes;        // A rows, B columns 0..127, B columns 128..255
+constexpr int kTgDmaPerWave = 6;                      // per step: 8 pairs x (1 A + 2 B) row pieces of 256 bytes
 constexpr int kTgLoadsPerStep = kTgDmaPerWave + 1;    // + the index DMA
 
-__device__ __attribute__((aligned(256))) const uint16_t kTgZeroRow[TBM] = {};
+__device__ __attribute__((aligned(256))) const uint16_t kTgZeroRow[128] = {};
 
-// 52 KiB of LDS and at most 168 registers: three blocks (waves per SIMD) per CU.
-__global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
-  static_assert(TBM == 128 && TBN == 128 && TBK == 32, "tile geometry");
-  static_assert(kTgDmaPerWave * 2 * 1024 == kTgOpBytes && kTgIdxSlots > kTgDepth, "ring geometry");
+// 76 KiB of LDS and at most 256 registers: two blocks (waves per SIMD) per CU.
+__global__ __launch_bounds__(kBlock, 2) void tgemm_kernel(TGemmArgs ta) {
+  static_assert(TBM == 128 && TBN == 256 && TBK == 32, "tile geometry");
+  static_assert((kBlock / kWave) * 8 == TBK && kTgDmaPerWave * 1024 == 8 * 3 * 256 && kTgIdxSlots > kTgDepth,
+                "ring geometry");
   // one LDS object, the step ring then each wave's index ring (with the
   // index ring a separate object, the compiler waits for every DMA in flight
   // before reading it)
   __shared__ __attribute__((aligned(16))) uint8_t lds[kTgRing * kTgSlotBytes + (kBlock / kWave) * kTgIdxSlots * 256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;  // compute: 64 x 64 of the 128 x 128 tile
+  const int wm = w >> 1, wn = w & 1;  // compute: rows wm*64 .. +63 against B's column half wn
   const int m16 = lane & 15, g = lane >> 4;
-  const int op = w >> 1, wl = w & 1;  // DMA: waves 0-1 move A rows, waves 2-3 B rows (16 rows each)
-  const uint16_t* src = op ? ta.b : ta.a;
-  const int64_t ld = op ? ta.ldb : ta.lda;
-  const int32_t* rows_of = op ? ta.b_rows : ta.a_rows;
   uint8_t* my_idx = lds + kTgRing * kTgSlotBytes + w * kTgIdxSlots * 256;
-  const int mtn = ta.M / TBM, ntn = ta.N / TBN;
+  const int mtn = ta.M / TBM, ntn = (ta.N + TBN - 1) / TBN;
   const int64_t total = (int64_t)ta.G * mtn * ntn;
   const int64_t nb = gridDim.x;
   const int64_t per_xcd_blocks = nb / kXcds;
@@ -420,41 +426,45 @@ __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
     const int64_t p0 = ta.grp_off[grp];
     const int64_t n_p = ta.grp_off[grp + 1] - p0;
     const int ksteps = (int)((n_p + TBK - 1) / TBK);
-    const int col0 = op ? n0 : m0;
+    const bool hi_ok = n0 + 128 < ta.N;  // the tile's second column half exists
 
-    // index DMA of a step: lane l fetches the index of the wave's pair l % 16
-    // (an operand without a row array fetches a valid dummy word)
+    // index DMA of a step: lane l fetches the B row of pair 8 w + ((l >> 1) & 3) + 4 (l & 1), so that
+    // the two pairs of lane group g (8 w + g, 8 w + 4 + g) are words 2 g and 2 g + 1 (an operand
+    // without a row array fetches a valid dummy word)
     auto issue_idx = [&](int step) {
       const int st = step < ksteps ? step : ksteps - 1;
-      int64_t p = (int64_t)st * TBK + wl * 16 + (lane & 15);
+      int64_t p = (int64_t)st * TBK + 8 * w + ((lane >> 1) & 3) + 4 * (lane & 1);
       p = p < n_p ? p : n_p - 1;
-      const int32_t* s = rows_of ? rows_of + p0 + p : reinterpret_cast<const int32_t*>(ta.grp_off);
+      const int32_t* s = ta.b_rows ? ta.b_rows + p0 + p : reinterpret_cast<const int32_t*>(ta.grp_off);
       dma4(reinterpret_cast<const float*>(s), my_idx + (step % kTgIdxSlots) * 256);
     };
-    // row DMA of a step: instruction q moves LDS rows wl 16 + 4 q .. +3; LDS
-    // row wl 16 + 4 q + i holds pair wl 16 + 4 i + q, so a lane's four pairs
-    // are consecutive and their indices one 16-byte LDS read (the k order is
-    // the same for both operands, which is all the product needs)
+    // row DMA of a step: instruction q of each part moves LDS rows 8 w + 4 q .. +3 (pairs 8 w + 4 q + g)
     auto issue_rows = [&](int step) {
       const int st = step < ksteps ? step : ksteps - 1;
-      uint8_t* dst = lds + (step % kTgRing) * kTgSlotBytes + op * kTgOpBytes + wl * 4 * 1024;
-      const u32x4 rid = *reinterpret_cast<const u32x4*>(my_idx + (step % kTgIdxSlots) * 256 + 16 * g);
+      uint8_t* dst = lds + (step % kTgRing) * kTgSlotBytes + (8 * w) * 256;
+      const u32x2 rid = *reinterpret_cast<const u32x2*>(my_idx + (step % kTgIdxSlots) * 256 + 8 * g);
 #pragma unroll
-      for (int q = 0; q < kTgDmaPerWave; ++q) {
-        const int r = wl * 16 + 4 * q + g;
-        const int64_t p = (int64_t)st * TBK + wl * 16 + 4 * g + q;
+      for (int q = 0; q < 2; ++q) {
+        const int r = 8 * w + 4 * q + g;
+        const int64_t p = (int64_t)st * TBK + r;
         const int gc = (lane & 15) ^ tg_swz(r);
-        const int64_t row = rows_of ? (int64_t)(int32_t)rid[q] : p0 + p;
-        const uint16_t* a = p < n_p ? src + row * ld + col0 + gc * 8 : kTgZeroRow + gc * 8;
-        dma16<kPolicyReuse>(a, dst + q * 1024);
+        const bool in = p < n_p;
+        dma16<kPolicyReuse>(in ? ta.a + (p0 + p) * ta.lda + m0 + gc * 8 : kTgZeroRow + gc * 8, dst + q * 1024);
+        const int64_t row = ta.b_rows ? (int64_t)(int32_t)rid[q] : p0 + p;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = n0 + (h && hi_ok ? 128 : 0) + gc * 8;
+          dma16<kPolicyReuse>(in ? ta.b + row * ta.ldb + col : kTgZeroRow + gc * 8,
+                              dst + (1 + h) * kTgHalfBytes + q * 1024);
+        }
       }
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[4][8];  // [A stripe sa][B stripe sb]
 #pragma unroll
     for (int sa = 0; sa < 4; ++sa)
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) acc[sa][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int sb = 0; sb < 8; ++sb) acc[sa][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ksteps > 0) {  // (uniform)
       // indices of the first kTgDepth steps, then kTgDepth steps issued as
       // the loop issues them: indices kTgDepth steps ahead of their rows
@@ -473,15 +483,19 @@ __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
       issue_idx(s + 2 * kTgDepth);
       issue_rows(s + kTgDepth);
       const uint8_t* buf = lds + (s % kTgRing) * kTgSlotBytes;
-      u32x4 av[4], bv[4];
+      u32x4 av[4], bv0[4], bv1[4];
       tg_operands(buf, wm * 64, lane, av);
-      tg_operands(buf + kTgOpBytes, wn * 64, lane, bv);
+      tg_operands(buf + (1 + wn) * kTgHalfBytes, 0, lane, bv0);
+      tg_operands(buf + (1 + wn) * kTgHalfBytes, 64, lane, bv1);
 #pragma unroll
       for (int sa = 0; sa < 4; ++sa)
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb)
-          acc[sa][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[sa]), as_bf16x8(bv[sb]), acc[sa][sb], 0,
+        for (int sb = 0; sb < 4; ++sb) {
+          acc[sa][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[sa]), as_bf16x8(bv0[sb]), acc[sa][sb], 0,
                                                                 0, 0);
+          acc[sa][4 + sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[sa]), as_bf16x8(bv1[sb]),
+                                                                    acc[sa][4 + sb], 0, 0, 0);
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
     // the tile's last DMAs (repeats) land and every wave is done with both
@@ -489,16 +503,29 @@ __global__ __launch_bounds__(kBlock, 3) void tgemm_kernel(TGemmArgs ta) {
     wait_vmcnt<0>();
     __syncthreads();
     // D: lane (m16, g) holds rows 4 g + r of column m16 of each 16 x 16 tile
+    if (wn == 1 && !hi_ok) continue;  // (uniform per wave; no barrier follows before the next tile's)
     float* cg = ta.c + (int64_t)grp * ta.c_stride;
+    const int nb0 = n0 + wn * 128;
+    if (ta.c_nm) {  // C[m][n] at n * ldc + m: a lane's four rows are one 16-byte store
 #pragma unroll
-    for (int sa = 0; sa < 4; ++sa)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int mm = m0 + wm * 64 + sa * 16 + 4 * g + r;
+      for (int sa = 0; sa < 4; ++sa) {
+        const int mm = m0 + wm * 64 + sa * 16 + 4 * g;
         if (mm >= ta.M_valid) continue;
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) cg[(int64_t)mm * ta.ldc + n0 + wn * 64 + sb * 16 + m16] = acc[sa][sb][r];
+        for (int sb = 0; sb < 8; ++sb)
+          *reinterpret_cast<f32x4*>(cg + (int64_t)(nb0 + sb * 16 + m16) * ta.ldc + mm) = acc[sa][sb];
       }
+    } else {
+#pragma unroll
+      for (int sa = 0; sa < 4; ++sa)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int mm = m0 + wm * 64 + sa * 16 + 4 * g + r;
+          if (mm >= ta.M_valid) continue;
+#pragma unroll
+          for (int sb = 0; sb < 8; ++sb) cg[(int64_t)mm * ta.ldc + nb0 + sb * 16 + m16] = acc[sa][sb][r];
+        }
+    }
   }
 }
 
@@ -678,7 +705,7 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
   const int64_t max_up_tiles = (int64_t)E * ((T + kPairRows - 1) / kPairRows) * (de / GBN);
   int64_t grid_pair = 0, grid_t = 0, grid_dn = 0;
   hipError_t e = persistent_grid(bwd_pair_kernel, max_up_tiles, &grid_pair);
-  if (e == hipSuccess) e = persistent_grid(tgemm_kernel, (int64_t)E * (d / TBM) * (de / TBN), &grid_t);
+  if (e == hipSuccess) e = persistent_grid(tgemm_kernel, (int64_t)E * (de / TBM) * ((d + TBN - 1) / TBN), &grid_t);
   if (e == hipSuccess)
     e = de == 128 ? persistent_grid(grouped_down_kernel<128, true>, down_blocks(E, d, de), &grid_dn)
                   : persistent_grid(grouped_down_kernel<256, true>, down_blocks(E, d, de), &grid_dn);
@@ -692,15 +719,15 @@ hipError_t launch_backward(const LayerArgs& la, const uint16_t* x, int64_t T, co
       preact, la.rms_scale, L.r_b, L.pair_idx, L.dgp, de / GBN, T, E, dz_extra, L.dz, L.dzb, L.dsc, L.pair_dz,
       dz_extra != nullptr ? L.dz_off : nullptr);
   bwd_reduce_kernel<<<dim3((unsigned)E), dim3(kBlock), 0, s>>>(L.dz, L.dsc, T, E, d_b_router, d_rms_scale);
-  // dW_out[i][k][j] = sum_p dY[t_p][k] HG[p][j]
-  TGemmArgs go{L.dyb, d, L.pair_tok, L.hg, de, nullptr, L.pair_off, d_w_out, de, (int64_t)d * de, E, d, d, de};
+  // dW_out[i][k][j] = sum_p HG[p][j] dY[t_p][k], stored transposed (the gathered dY rows on the wide side)
+  TGemmArgs go{L.hg, de, L.dyb, d, L.pair_tok, L.pair_off, d_w_out, de, (int64_t)d * de, E, de, de, d, true};
   tgemm_kernel<<<dim3((unsigned)grid_t), dim3(kBlock), 0, s>>>(go);
   // dW_in[i][j][k] = sum_p dU[p][j] X[t_p][k]
-  TGemmArgs gi{L.du, de, nullptr, x, d, L.pair_tok, L.pair_off, d_w_in, d, (int64_t)de * d, E, de, de, d};
+  TGemmArgs gi{L.du, de, x, d, L.pair_tok, L.pair_off, d_w_in, d, (int64_t)de * d, E, de, de, d, false};
   tgemm_kernel<<<dim3((unsigned)grid_t), dim3(kBlock), 0, s>>>(gi);
   // dW_r[i][k] = sum_t dZ[t][i] X[t][k]: kRouterSplits token ranges as groups, then their sum
-  TGemmArgs gr{L.dzb, kRouterPad, nullptr, x, d, nullptr, L.all_off, L.wr_part, d, (int64_t)E * d, kRouterSplits,
-               kRouterPad, E, d};
+  TGemmArgs gr{L.dzb, kRouterPad, x, d, nullptr, L.all_off, L.wr_part, d, (int64_t)E * d, kRouterSplits,
+               kRouterPad, E, d, false};
   tgemm_kernel<<<dim3((unsigned)grid_t), dim3(kBlock), 0, s>>>(gr);
   bwd_router_sum_kernel<<<dim3((unsigned)(((int64_t)E * d + kBlock - 1) / kBlock)), dim3(kBlock), 0, s>>>(
       L.wr_part, (int64_t)E * d, d_w_router);

@@ -23,11 +23,10 @@ import torch
 import oracle
 from activation_sparse_moe_amd import binding as B
 from activation_sparse_moe_amd._capi import BF16
-from gpu_parity_util import BAND, say
+from gpu_parity_util import BAND, check_backward as _check, check_grad as _compare, say
 from workload import CONFIGS, make_layer, make_tokens, make_workload
 
 pytestmark = pytest.mark.gpu
-TOL = 1e-2
 
 # name: (d, E, d_e, T-chunks, L, bias_k, alpha, seed, scale)   scale: None | "pos" | "signed"
 CASES = {
@@ -61,43 +60,6 @@ def _gpu_backward(layer, x, dy):
     res = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
     res["z"] = z.cpu().numpy()
     return res
-
-
-def _compare(name, got, ref, rows=None):
-    """Returns the norm-wise relative error after checking both bars."""
-    if rows is not None:
-        got, ref = got[rows], ref[rows]
-    if ref.size == 0:
-        return 0.0
-    top = np.abs(ref).max()
-    if top == 0:
-        assert np.all(got == 0), f"{name}: expected zeros, max |got| {np.abs(got).max():.3e}"
-        return 0.0
-    err = np.abs(got - ref).max()
-    fro = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    assert fro <= TOL, f"{name}: norm-wise relative error {fro:.3e} > {TOL}"
-    assert err <= TOL * top, f"{name}: max |err| {err:.3e} > {TOL} x max |G| {top:.3e}"
-    return fro
-
-
-def _check(gpu, ref, gz, z_ref, dx_gpu, dx_ref, experts=None, router=True):
-    """Compare every gradient.  gz / z_ref are the pre-activations of the
-    tokens whose dx rows are compared; experts restricts the expert blocks;
-    router=False leaves dW_r and db to the caller."""
-    band = np.abs(z_ref) < BAND
-    flips = (gz > 0) != (z_ref > 0)
-    assert not (flips & ~band).any(), "activation pattern differs outside the band"
-    bad_tok = band.any(axis=1)
-    bad_exp = band.any(axis=0)
-    rel = {"dx": _compare("dx", dx_gpu, dx_ref, ~bad_tok)}
-    ex = np.arange(z_ref.shape[1]) if experts is None else np.asarray(experts)
-    rel["d_w_in"] = _compare("d_w_in", gpu["d_w_in"][ex], ref["dw_in"][ex])
-    rel["d_w_out"] = _compare("d_w_out", gpu["d_w_out"][ex], ref["dw_out"][ex])
-    rel["d_rms_scale"] = _compare("d_rms_scale", gpu["d_rms_scale"], ref["ds"])
-    if router:
-        rel["d_w_router"] = _compare("d_w_router", gpu["d_w_router"], ref["dw_router"], ~bad_exp)
-        rel["d_b_router"] = _compare("d_b_router", gpu["d_b_router"], ref["db"], ~bad_exp)
-    return rel, int(bad_tok.sum()), int(bad_exp.sum())
 
 
 @pytest.mark.parametrize("name", sorted(CASES))

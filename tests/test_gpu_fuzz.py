@@ -1,0 +1,122 @@
+"""GPU parity on seeded, drawn shapes: every forward mode a shape allows, the
+one-call layer step and (for matrix-core shapes) the backward, each against
+the CPU oracle with the bars of gpu_parity_util.
+
+The fixed cases elsewhere pick shapes for the tiles and tails they exercise;
+these draw d, E, d_e, chunk length, chunk count, dtype, bias and token
+correlation from the whole supported range (1 <= E <= 128, d a multiple of 64,
+d_e a multiple of 16, chunks of 1..32 tokens), so that combinations nobody
+chose are covered too.  Each draw is a pure function of its seed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_moe_amd import binding as B
+from activation_sparse_moe_amd._capi import BF16
+from gpu_parity_util import (check_backward, check_route, check_union, check_y, conditioned_tols, oracle_full,
+                              run_gpu, say)
+from workload import make_layer, make_tokens
+from workload.gen import bf16_bits_to_f32, bf16_round_bits
+
+pytestmark = pytest.mark.gpu
+
+FORWARD_SEEDS = range(40)
+BACKWARD_SEEDS = range(10)
+
+
+def _draw_forward(seed: int):
+    r = np.random.default_rng(7000 + seed)
+    dt = "f32" if r.random() < 0.2 else "bf16"
+    if dt == "bf16" and r.random() < 0.7:  # matrix-core shapes
+        d = 128 * int(r.integers(1, 9))
+        de = int(r.choice([128, 256]))
+    else:
+        d = 64 * int(r.integers(1, 17))
+        de = 16 * int(r.integers(1, 17))
+    E = int(r.choice([1, 2, 7, 16, 24, 33, 48, 64, 65, 80, 100, 127, 128]))
+    L = int(r.choice([1, 2, 3, 5, 8, 9, 13, 16, 17, 24, 31, 32]))
+    C = int(r.integers(1, 25))
+    return d, E, de, dt, L, C, float(r.uniform(-0.3, 1.6)), float(r.uniform(0.0, 0.9))
+
+
+def _draw_backward(seed: int):
+    r = np.random.default_rng(8000 + seed)
+    d = 128 * int(r.integers(1, 9))
+    de = int(r.choice([128, 256]))
+    E = int(r.choice([1, 3, 8, 17, 40, 64, 96, 128]))
+    T = int(r.integers(1, 200))
+    return d, E, de, T, float(r.uniform(-0.3, 1.6)), float(r.uniform(0.0, 0.9)), int(r.integers(0, 3))
+
+
+def _checks(layer, x, L, gpu, z, g, m, um, y_ref, st, what):
+    E, dt = layer.n_experts, layer.dtype
+    flipped, keep = check_route(gpu, z, g, m, E, dt, layer=layer)
+    check_union(gpu, um, z, E, L)
+    check_y(gpu["y"], y_ref, keep, dt, what)
+    if gpu.get("stats") is not None and not flipped:
+        for key in ("active_pairs", "union_sum", "reuse_num", "reuse_den"):
+            assert gpu["stats"][key] == st[key], f"{what}: {key}"
+        np.testing.assert_array_equal(gpu["stats"]["hist"], st["hist"])
+
+
+@pytest.mark.parametrize("seed", FORWARD_SEEDS)
+def test_forward_on_drawn_shapes(seed):
+    d, E, de, dt, L, C, k, a = _draw_forward(seed)
+    say(f"[gpu] drawn forward {seed}: d={d} E={E} d_e={de} {dt} L={L} chunks={C}")
+    rng = np.random.default_rng(9000 + seed)
+    layer = make_layer(d, E, de, dt, k, rng)
+    x = make_tokens(d, C, L, a, dt, rng).x
+    dl = B.DeviceLayer.from_workload(layer)
+    xd = B.tokens_to_device(x, dl.dtype)
+    z, g, m, um, _, _ = oracle_full(layer, x, L)
+    y_ref = oracle.forward_tokens(x, layer.w_in, layer.w_out, g, m)
+    st = oracle.stats(m, E, L)
+    modes = ["auto", "gemv", "dense"]
+    if dt == "bf16" and d % 128 == 0 and de % 128 == 0:
+        modes += ["chunk_mfma", "chunk_split"]
+    if dt == "bf16" and d % 128 == 0 and de in (128, 256):
+        modes.append("grouped")
+    for mode in modes:
+        say(f"  mode {mode}")
+        gpu = run_gpu(dl, xd, L, mode=mode)
+        _checks(layer, x, L, gpu, z, g, m, um, y_ref, st, f"seed {seed}/{mode}")
+    say("  one-call layer step")
+    out = B.blockffn_layer_forward(dl, xd, L, want_preact=True)
+    torch.cuda.synchronize()
+    gpu = dict(g=out["gates"].cpu().numpy(), mask=B.masks_to_u64(out["token_masks"]),
+               umask=B.masks_to_u64(out["chunk_masks"]), count=out["active_count"].cpu().numpy(),
+               list=out["active_list"].cpu().numpy(), y=out["y"].cpu().numpy(), z=out["preact"].cpu().numpy(),
+               stats=B.stats_dict(out["stats"]))
+    _checks(layer, x, L, gpu, z, g, m, um, y_ref, st, f"seed {seed}/layer step")
+
+
+@pytest.mark.parametrize("seed", BACKWARD_SEEDS)
+def test_backward_on_drawn_shapes(seed):
+    d, E, de, T, k, a, scale = _draw_backward(seed)
+    say(f"[gpu] drawn backward {seed}: d={d} E={E} d_e={de} T={T} scale={scale}")
+    rng = np.random.default_rng(9500 + seed)
+    layer = make_layer(d, E, de, "bf16", k, rng)
+    if scale == 1:
+        layer.rms_scale = (0.5 + rng.random(E)).astype(np.float32)
+    elif scale == 2:
+        layer.rms_scale = (rng.random(E) * 2.0 - 0.7).astype(np.float32)
+    x = make_tokens(d, T, 1, a, "bf16", rng).x
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    dl = B.DeviceLayer.from_workload(layer)
+    xd = B.tokens_to_device(x, BF16)
+    _, _, zd = B.blockffn_route(dl, xd, 1, want_preact=True)
+    out = B.blockffn_backward(dl, xd, zd, torch.from_numpy(dy).cuda())
+    torch.cuda.synchronize()
+    gpu = {key: v.cpu().numpy().astype(np.float64) for key, v in out.items()}
+    gz = zd.cpu().numpy()
+    args = (x, layer.w_router, layer.b_router, layer.rms_scale, layer.rms_eps, layer.w_in, layer.w_out)
+    ref = oracle.backward(*args, dy)
+    # drawn shapes include ill-conditioned ones (few tokens, one active expert of three): the bars
+    # follow how far the oracle's own gradients move when dy is rounded as the kernels round it
+    tols = conditioned_tols(ref, oracle.backward(*args, bf16_bits_to_f32(bf16_round_bits(dy))))
+    z_ref, _, _ = oracle.route(x, layer.w_router, layer.b_router, layer.rms_scale, layer.rms_eps)
+    rel, nt, ne = check_backward(gpu, ref, gz, z_ref, gpu["dx"], ref["dx"], tols=tols)
+    say("  " + ", ".join(f"{key} {v:.1e} (bar {tols[key][0]:.1e})" for key, v in rel.items())
+        + f"; band tokens {nt}, experts {ne}")

@@ -21,15 +21,16 @@
 //            epilogue: dU = g Q Swish'(U), HG = g Swish(U) (bf16), and the
 //            partial dg = sum over the tile's hidden units of Q Swish(U)
 //   router:  dz, ds terms per token; then db, ds by sums over tokens
-//   weights: dW_out[i] = dY_p^T HG_p, dW_in[i] = dU_p^T X_p and
-//            dW_r = dZ^T X (over token ranges, then summed in order), each a
-//            sum over pairs (tokens) in fp32 by a grouped GEMM that
-//            contracts over pairs (pair-major rows in LDS, MFMA operands by
-//            transpose loads)
-//   dx:      Part = dU W_in[i] per pair (the forward's down GEMM, reading
-//            W_in k-major), then per token the sum over its active
-//            experts, ascending, of Part + dz_i W_r[i] (and, with an extra
-//            router gradient, dz_i W_r[i] of the inactive experts after them)
+//   weights: dW_out[i] = dY_p^T HG_p (computed as HG_p^T dY_p, stored
+//            transposed), dW_in[i] = dU_p^T X_p and dW_r = dZ^T X (over token
+//            ranges, then summed in order), each a sum over pairs (tokens) in
+//            fp32 by a grouped GEMM that contracts over pairs (pair-major rows
+//            in LDS, MFMA operands by transpose loads)
+//   dx:      Part = dU W_in[i] + dz_i W_r[i] per pair (the forward's down
+//            GEMM, reading W_in k-major, its products starting from the
+//            router term), then per token the sum over its active experts,
+//            ascending; with an extra router gradient, the inactive experts'
+//            dz_i W_r[i] first, as one product, and the sum added onto it
 //
 // No atomics: every output element has one writer and a fixed summation
 // order, so the result is bit-reproducible.

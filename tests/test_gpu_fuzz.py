@@ -6,7 +6,9 @@ The fixed cases elsewhere pick shapes for the tiles and tails they exercise;
 these draw d, E, d_e, chunk length, chunk count, dtype, bias and token
 correlation from the whole supported range (1 <= E <= 128, d a multiple of 64,
 d_e a multiple of 16, chunks of 1..32 tokens), so that combinations nobody
-chose are covered too.  Each draw is a pure function of its seed.
+chose are covered too, and do the same for the baseline routers (top-k
+softmax with k drawn from 1..E, and the ReLU-sum router).  Each draw is a pure
+function of its seed.
 """
 import numpy as np
 import pytest
@@ -15,14 +17,15 @@ import torch
 import oracle
 from activation_sparse_moe_amd import binding as B
 from activation_sparse_moe_amd._capi import BF16
-from gpu_parity_util import (check_backward, check_route, check_union, check_y, conditioned_tols, oracle_full,
-                              run_gpu, say)
+from gpu_parity_util import (check_backward, check_baseline_router, check_route, check_union, check_y,
+                              conditioned_tols, oracle_full, run_gpu, say)
 from workload import make_layer, make_tokens
 from workload.gen import bf16_bits_to_f32, bf16_round_bits
 
 pytestmark = pytest.mark.gpu
 
 FORWARD_SEEDS = range(40)
+ROUTER_SEEDS = range(16)
 BACKWARD_SEEDS = range(10)
 
 
@@ -90,6 +93,19 @@ def test_forward_on_drawn_shapes(seed):
                list=out["active_list"].cpu().numpy(), y=out["y"].cpu().numpy(), z=out["preact"].cpu().numpy(),
                stats=B.stats_dict(out["stats"]))
     _checks(layer, x, L, gpu, z, g, m, um, y_ref, st, f"seed {seed}/layer step")
+
+
+@pytest.mark.parametrize("seed", ROUTER_SEEDS)
+def test_baseline_routers_on_drawn_shapes(seed):
+    d, E, de, dt, L, C, k, a = _draw_forward(100 + seed)
+    r = np.random.default_rng(7500 + seed)
+    router = "relu_sum" if seed % 3 == 2 else "topk_softmax"
+    top_k = int(r.integers(1, E + 1)) if router == "topk_softmax" else 0
+    say(f"[gpu] drawn router {seed}: {router}{top_k} d={d} E={E} d_e={de} {dt} L={L} chunks={C}")
+    rng = np.random.default_rng(9200 + seed)
+    layer = make_layer(d, E, de, dt, k, rng)
+    x = make_tokens(d, C, L, a, dt, rng).x
+    check_baseline_router(layer, x, L, router, top_k, f"seed {seed}")
 
 
 @pytest.mark.parametrize("seed", BACKWARD_SEEDS)

@@ -10,12 +10,8 @@ within 1e-4 (bf16) / 1e-5 (fp32) x RMS of the oracle's; y within 2e-2 (bf16)
 """
 import numpy as np
 import pytest
-import torch
 
-import oracle
-from activation_sparse_moe_amd import binding as B
-from activation_sparse_moe_amd._capi import BF16, F32
-from gpu_parity_util import BAND, GATE_TOL, Y_TOL, bits, say
+from gpu_parity_util import check_baseline_router, say
 from workload import make_layer, make_tokens
 
 pytestmark = pytest.mark.gpu
@@ -29,13 +25,6 @@ SHAPES = {
 ROUTERS = [("topk_softmax", 1), ("topk_softmax", 2), ("topk_softmax", 8), ("relu_sum", 0)]
 
 
-def _band_tokens(z, kind, k):
-    if kind == "relu_sum":
-        return (np.abs(z) < BAND).any(axis=1)
-    zs = -np.sort(-z, axis=1)
-    return (zs[:, k - 1] - zs[:, k]) < BAND if k < z.shape[1] else np.zeros(z.shape[0], bool)
-
-
 @pytest.mark.parametrize("router,k", ROUTERS, ids=[f"{r}{k}" for r, k in ROUTERS])
 @pytest.mark.parametrize("shape", sorted(SHAPES))
 def test_router_matches_oracle(shape, router, k):
@@ -44,29 +33,4 @@ def test_router_matches_oracle(shape, router, k):
     layer = make_layer(d, E, de, dt, bias_k, rng)
     x = make_tokens(d, C, L, a, dt, rng).x
     say(f"[gpu] router {router}{k} {shape} T={x.shape[0]}")
-    dl = B.DeviceLayer.from_workload(layer)
-    xd = B.tokens_to_device(x, F32 if dt == "f32" else BF16)
-    g, m, z = B.blockffn_route_with(dl, xd, L, router=router, top_k=k, want_preact=True)
-    um, cnt, lst = B.blockffn_chunk_union(E, m, L)
-    y = B.blockffn_forward(dl, xd, L, g, cnt, lst)
-    torch.cuda.synchronize()
-    kind = oracle.ROUTER_TOPK_SOFTMAX if router == "topk_softmax" else oracle.ROUTER_RELU_SUM
-    z_ref, g_ref, m_ref = oracle.route_with(x, layer.w_router, layer.b_router, kind, k)
-    gz, gg, gm = z.cpu().numpy(), g.cpu().numpy(), B.masks_to_u64(m)
-    scale = np.sqrt((z_ref ** 2).mean())
-    assert np.abs(gz - z_ref).max() <= (1e-5 if dt == "f32" else 1e-4) * scale
-    band = _band_tokens(z_ref, router, k)
-    ob, gb = bits(m_ref, E), bits(gm, E)
-    diff = (ob != gb).any(axis=1)
-    assert not (diff & ~band).any(), f"mask mismatch outside the band at tokens {np.nonzero(diff & ~band)[0][:8]}"
-    keep = ~band
-    if router == "topk_softmax":
-        assert np.all(gb.sum(axis=1) == k)
-    rms = np.sqrt((g_ref[keep] ** 2).mean())
-    assert np.abs(gg[keep] - g_ref[keep]).max() <= GATE_TOL[dt] * rms
-    y_ref = oracle.forward_tokens(x, layer.w_in, layer.w_out, g_ref, m_ref)
-    yr = y.cpu().numpy()
-    yrms = np.sqrt((y_ref[keep] ** 2).mean())
-    err = np.abs(yr[keep] - y_ref[keep]).max()
-    assert err <= Y_TOL[dt] * yrms, f"y error {err:.3e} > {Y_TOL[dt]} x RMS {yrms:.3e}"
-    say(f"  {router}{k} {shape}: max|dy|/rms {err / yrms:.2e}, band tokens {int(band.sum())}")
+    check_baseline_router(layer, x, L, router, k, shape)

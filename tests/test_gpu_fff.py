@@ -223,3 +223,25 @@ def test_fff_timed_configuration_every_output():
     _compare(paths.cpu().numpy(), pre.cpu().numpy(), y.cpu().numpy(), po, co, yo, cfg.name)
     del dl
     torch.cuda.empty_cache()
+
+
+def _draw(seed: int):
+    """A seeded shape from the supported range: dtype, d, trees, depth, tokens, layer copies, bias,
+    node layout, blocks per token (at most ceil(P / 4)) and, at small depth, the dense mode."""
+    r = np.random.default_rng(6000 + seed)
+    dtype = "f32" if r.random() < 0.3 else "bf16"
+    d = (256 if dtype == "f32" else 512) * int(r.integers(1, 9))
+    P = int(r.choice([1, 2, 3, 7, 13, 16, 33, 64]))
+    D = int(r.integers(0, 9))
+    dense = D <= 6 and r.random() < 0.25
+    split = int(r.integers(0, (P + 3) // 4 + 1))  # 0: the library's choice
+    return dict(d=d, P=P, D=D, dtype=dtype, T=int(r.integers(1, 65)), dense=bool(dense),
+                n_layers=int(r.integers(1, 4)), bias=bool(r.random() < 0.7), interleave=bool(r.random() < 0.5),
+                split=split)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_fff_drawn_shapes(seed):
+    s = _draw(seed)
+    _case(s["d"], s["P"], s["D"], s["dtype"], s["T"], 990 + seed, dense=s["dense"], n_layers=s["n_layers"],
+          bias=s["bias"], interleave=s["interleave"], split=s["split"])

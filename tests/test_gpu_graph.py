@@ -39,13 +39,16 @@ def _snapshot(b):
     return {k: v.detach().cpu().clone() for k, v in b.items() if k != "ws"}
 
 
-@pytest.mark.parametrize("mode", ["auto", "grouped", "gemv", "chunk_split"])
-def test_forward_step_replays_match_eager(mode):
-    d, E, de, L, C = 512, 64, 128, 8, 24
+# (mode, chunk length, chunks): 24 chunks of 8 take the chunk kernels under AUTO, 8 chunks the
+# few-unit kernels, 20 chunks of 32 the lockstep two-tile kernels
+@pytest.mark.parametrize("mode,L,C", [("auto", 8, 24), ("grouped", 8, 24), ("gemv", 8, 24), ("chunk_split", 8, 24),
+                                      ("auto", 8, 8), ("auto", 32, 20)])
+def test_forward_step_replays_match_eager(mode, L, C):
+    d, E, de = 512, 64, 128
     rng = np.random.default_rng(801)
     layer = make_layer(d, E, de, "bf16", 0.9, rng)
     x = make_tokens(d, C, L, 0.8, "bf16", rng).x
-    say(f"[gpu] graph replay, forward mode {mode}")
+    say(f"[gpu] graph replay, forward mode {mode}, {C} chunks of {L}")
     dl = B.DeviceLayer.from_workload(layer)
     xd = B.tokens_to_device(x, BF16)
     b = _bufs(dl, x.shape[0], L, mode)

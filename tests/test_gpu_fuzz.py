@@ -7,8 +7,8 @@ these draw d, E, d_e, chunk length, chunk count, dtype, bias and token
 correlation from the whole supported range (1 <= E <= 128, d a multiple of 64,
 d_e a multiple of 16, chunks of 1..32 tokens), so that combinations nobody
 chose are covered too, and do the same for the baseline routers (top-k
-softmax with k drawn from 1..E, and the ReLU-sum router).  Each draw is a pure
-function of its seed.
+softmax with k drawn from 1..E, and the ReLU-sum router) and the CLS-aware
+objectives.  Each draw is a pure function of its seed.
 """
 import numpy as np
 import pytest
@@ -136,3 +136,26 @@ def test_backward_on_drawn_shapes(seed):
     rel, nt, ne = check_backward(gpu, ref, gz, z_ref, gpu["dx"], ref["dx"], tols=tols)
     say("  " + ", ".join(f"{key} {v:.1e} (bar {tols[key][0]:.1e})" for key, v in rel.items())
         + f"; band tokens {nt}, experts {ne}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_cls_losses_on_drawn_inputs(seed):
+    """The CLS-aware objectives on drawn pre-activations (E, chunk length, chunks, scale, shift,
+    alpha, weights).  Both sides take the same fp32 z, so every target [z > 0] agrees: the losses
+    must match within 1e-4 relative and dz within 1e-4 x max |dz| (fp32 against fp64 arithmetic)."""
+    r = np.random.default_rng(7700 + seed)
+    E = int(r.choice([1, 2, 7, 16, 33, 64, 100, 128]))
+    L = int(r.choice([1, 2, 5, 8, 16, 17, 32]))
+    C = int(r.integers(1, 41))
+    alpha = float(r.uniform(1.0, 16.0))
+    w_al, w_cs = float(r.uniform(0.0, 2.0)), float(r.uniform(0.0, 2.0))
+    z = (r.standard_normal((C * L, E)) * r.uniform(0.1, 3.0) + r.uniform(-2.0, 1.0)).astype(np.float32)
+    say(f"[gpu] drawn cls losses {seed}: E={E} L={L} chunks={C} alpha={alpha:.2f} w=({w_al:.2f}, {w_cs:.2f})")
+    losses, dz = B.blockffn_cls_losses(E, torch.from_numpy(z).cuda(), L, alpha, w_al, w_cs)
+    torch.cuda.synchronize()
+    al, cs, dz_ref = oracle.cls_losses(z, L, alpha, w_al, w_cs)
+    got = losses.cpu().numpy()
+    assert abs(got[0] - al) <= 1e-4 * abs(al) + 1e-7, (got[0], al)
+    assert abs(got[1] - cs) <= 1e-4 * abs(cs) + 1e-7, (got[1], cs)
+    top = np.abs(dz_ref).max()
+    assert np.abs(dz.cpu().numpy() - dz_ref).max() <= 1e-4 * top + 1e-12
